@@ -1,0 +1,9 @@
+"""fp64 CPU oracle of the DeltaKV hot path (test infrastructure only; see
+deltakv_oracle for the statement of what it computes)."""
+from .deltakv_oracle import *  # noqa: F401,F403
+from .deltakv_oracle import (  # noqa: F401
+    rnd, n_refs, ref_positions, nonref_positions, idx_bytes_for, stream_bytes,
+    cache_array_bytes, cache_bytes, dense_kv_bytes, decode_effective_bytes,
+    shared_component, center, cosines, search, encode, compress_stream, compress,
+    reconstruct_stream, attend, decode, ELEM_BYTES, ALIGN,
+)

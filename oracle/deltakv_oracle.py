@@ -1,0 +1,315 @@
+"""DeltaKV oracle: a plain, slow, fp64 CPU statement of what the hot path computes.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module; only the test suite, the smoke check of the package
+entry file and the CPU-baseline leg of the benchmark use it.  It shares no
+code with the HIP library: it has its own rounding, its own layout
+arithmetic and its own search, written from the method's description.
+
+Sources.  Every step cites the DeltaKV explainer pages on gist.science
+("DeltaKV: Residual-Based KV Cache Compression via Long-Range Similarity",
+arXiv 2602.08005), in the language editions they were published in:
+  [en]  gist.science/paper/2602.08005      Technical Summary §1-§6
+  [fr]  gist.science/fr/paper/2602.08005   Résumé Technique §1-§5
+  [de]  gist.science/de/paper/2602.08005   Technische Zusammenfassung §1-§5
+  [pt]  gist.science/pt/paper/2602.08005   Resumo Técnico §1-§5
+  [es]  gist.science/es/paper/2602.08005   Resumen Técnico §1-§5
+
+The pages fix the method only as an idea (strided references, removal of a
+shared component, a residual against a retrieved reference, a linear or MLP
+code, reconstruction as decompressed code plus reference).  The concrete,
+seedable instance computed here is:
+
+  compress, per stream (one (sequence, KV head) of K, and separately of V):
+    O2  mu      = rnd( (1/T) * sum_t k_t )                   fp64 sum
+    O3  x~_t    = rnd( k_t - mu )                            every t
+    O4  refs[r] = x~_{r*s},  r = 0 .. ceil(T/s)-1
+    O5  ref(t)  = argmax_{r : r*s < t} cos(x~_t, x~_{r*s}), lowest r on ties,
+                  cos := 0 when either norm is 0            non-ref t only
+    O6  c_t     = rnd( W_down @ ((k_t - mu) - x~_{ref(t)*s}) )
+  decode, per query head g of KV head h = g // G:
+    O7  k^_t = mu + x~_{ref(t)*s} + W_up @ c_t   (non-ref t)
+        k^_t = mu + x~_t                         (ref t)        same for V
+    O8  out_g = softmax_t(<q_g, k^_t> * scale) @ V^   over all T tokens
+
+``rnd`` rounds to the storage dtype (nearest, ties to even).  Storage
+"f64" makes rnd the identity; the pins use it to test the mathematics
+exactly.
+
+Readings of points the pages leave open (each listed with its reason in the
+design notes of the repository):
+  * the shared component is the per-stream mean (O2);
+  * similarity is cosine, top-1, among strictly earlier references (O5);
+  * the residual uses the unrounded centred token against the stored
+    reference (O6), which for a linear, bias-free compressor equals the
+    code-space difference the [en] page writes;
+  * K and V search independently, each with its own mean and references.
+
+Parity status.  Every function here is pinned by a CPU test against
+something other than itself (brute force on tiny inputs, exact
+reconstruction when d_c = d, dense attention when s = 1, closed forms and
+invariants).  No function is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+ELEM_BYTES = {"f32": 4, "bf16": 2, "f64": 8}
+ALIGN = 256  # byte alignment of each cache array in the carved layout
+
+
+# ---------------------------------------------------------------------------
+# Rounding to the storage dtype.
+# ---------------------------------------------------------------------------
+
+def rnd(x, storage: str) -> np.ndarray:
+    """Round float64 values to the storage dtype, nearest with ties to even.
+
+    bf16 keeps 8 significant bits and fp32's exponent range.  Written from
+    the definition: for x = m * 2**e with 0.5 <= |m| < 1 the spacing of
+    representable numbers near x is 2**(e - 8) (clamped at the subnormal
+    spacing 2**-133), and numpy's rint rounds half to even.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if storage == "f64":
+        return x.copy()
+    if storage == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    if storage == "bf16":
+        _, e = np.frexp(x)
+        q = np.maximum(e, -125) - 8
+        y = np.ldexp(np.rint(np.ldexp(x, -q)), q)
+        big = (2.0 - 2.0 ** -7) * 2.0 ** 127
+        return np.where(np.abs(y) > big, np.copysign(np.inf, x), y)
+    raise ValueError(storage)
+
+
+# ---------------------------------------------------------------------------
+# Layout arithmetic ([en] §3 "Strided Reference Selection": references at a
+# fixed interval s; [fr] §2 "Architecture de compression": a d_c-dimensional
+# code per token).
+# ---------------------------------------------------------------------------
+
+def n_refs(T: int, s: int) -> int:
+    """Number of references: positions 0, s, 2s, ... below T."""
+    return -(-T // s) if T > 0 else 0
+
+
+def ref_positions(T: int, s: int) -> np.ndarray:
+    return np.arange(n_refs(T, s), dtype=np.int64) * s
+
+
+def nonref_positions(T: int, s: int) -> np.ndarray:
+    t = np.arange(T, dtype=np.int64)
+    return t[t % s != 0]
+
+
+def idx_bytes_for(R: int) -> int:
+    """A reference ordinal fits 16 bits while R <= 65536, else 32 bits."""
+    return 2 if R <= 65536 else 4
+
+
+def stream_bytes(T: int, s: int, d: int, dc: int, storage: str) -> int:
+    """Bytes one compressed stream occupies: references, codes, indices, mean."""
+    e = ELEM_BYTES[storage]
+    R = n_refs(T, s)
+    N = T - R
+    return R * d * e + N * (dc * e + idx_bytes_for(R)) + d * e
+
+
+def cache_array_bytes(B: int, H: int, T: int, s: int, d: int, dc: int, storage: str) -> dict:
+    """Unpadded size of each cache array over B sequences x H heads x {K, V}."""
+    e = ELEM_BYTES[storage]
+    R = n_refs(T, s)
+    N = T - R
+    n = B * H * 2
+    return {
+        "refs": n * R * d * e,
+        "codes": n * N * dc * e,
+        "idx": n * N * idx_bytes_for(R),
+        "mu": n * d * e,
+    }
+
+
+def cache_bytes(B, H, T, s, d, dc, storage, align: int = ALIGN) -> int:
+    """Total carved cache size: each array padded to ``align`` bytes."""
+    return sum(-(-v // align) * align for v in cache_array_bytes(B, H, T, s, d, dc, storage).values())
+
+
+def dense_kv_bytes(n_layers, n_kv_heads, head_dim, seq_len, batch, elem_bytes=2) -> int:
+    """Bytes of an uncompressed K+V cache: 2 tensors x L x H x d x e per token."""
+    return 2 * n_layers * n_kv_heads * head_dim * elem_bytes * seq_len * batch
+
+
+def decode_effective_bytes(B, H, Hq, T, s, d, dc, storage) -> int:
+    """Bytes one decode step must move at least once: both tensors' references,
+    codes and indices, V's mean, W_up of K and V, the query and the fp32
+    output.  K's mean is never needed (it shifts every score equally)."""
+    e = ELEM_BYTES[storage]
+    a = cache_array_bytes(B, H, T, s, d, dc, storage)
+    mu_v = B * H * d * e
+    return a["refs"] + a["codes"] + a["idx"] + mu_v + 2 * d * dc * e + B * Hq * d * e + B * Hq * d * 4
+
+
+# ---------------------------------------------------------------------------
+# Compression.
+# ---------------------------------------------------------------------------
+
+def shared_component(k: np.ndarray, storage: str) -> np.ndarray:
+    """O2.  The component every token shares, read as the mean over the
+    prefill ([en] §2 "Highly Shared Latent Components": a few high-norm
+    directions common to all tokens are removed before compression)."""
+    T = k.shape[0]
+    return rnd(k.sum(axis=0, dtype=np.float64) / T, storage)
+
+
+def center(k: np.ndarray, mu: np.ndarray, storage: str) -> np.ndarray:
+    """O3.  Centred tokens in storage precision: these are what is stored for
+    references and what the similarity search compares."""
+    return rnd(k - mu, storage)
+
+
+def cosines(xt: np.ndarray, tok: np.ndarray, ref: np.ndarray, s: int) -> np.ndarray:
+    """cos(x~_t, x~_{r*s}) for paired arrays of token positions and reference
+    ordinals; 0 where either vector has zero norm."""
+    a = xt[tok]
+    b = xt[ref * s]
+    dot = np.einsum("ij,ij->i", a, b)
+    den = np.sqrt(np.einsum("ij,ij->i", a, a)) * np.sqrt(np.einsum("ij,ij->i", b, b))
+    return np.where(den > 0, dot / np.where(den > 0, den, 1.0), 0.0)
+
+
+def search(xt: np.ndarray, s: int, block: int = 2048):
+    """O5.  For every non-reference token, the earlier reference of highest
+    cosine similarity ([en] §3 "Strided Reference Selection": each new token
+    retrieves its nearest references from the strided set only; [de] §2: the
+    most similar references).  Ties go to the lowest ordinal (np.argmax
+    returns the first maximum).
+
+    Returns (idx, top1, margin) over non-reference tokens in position order;
+    margin = best minus second-best cosine (inf with a single candidate).
+    Each cosine is one fp64 dot product divided by the two fp64 norms; the
+    blocking over tokens only bounds memory.
+    """
+    T, _ = xt.shape
+    R = n_refs(T, s)
+    toks = nonref_positions(T, s)
+    refs = xt[ref_positions(T, s)]
+    nr = np.sqrt((refs * refs).sum(axis=1))
+    idx = np.empty(len(toks), np.int64)
+    top1 = np.empty(len(toks))
+    margin = np.empty(len(toks))
+    r_pos = np.arange(R, dtype=np.int64) * s
+    for a in range(0, len(toks), block):
+        tb = toks[a:a + block]
+        X = xt[tb]
+        nt = np.sqrt((X * X).sum(axis=1))
+        dots = X @ refs.T
+        den = nt[:, None] * nr[None, :]
+        cos = np.where(den > 0, dots / np.where(den > 0, den, 1.0), 0.0)
+        cos = np.where(r_pos[None, :] < tb[:, None], cos, -np.inf)
+        i1 = np.argmax(cos, axis=1)
+        rows = np.arange(len(tb))
+        t1 = cos[rows, i1]
+        cos[rows, i1] = -np.inf
+        t2 = cos.max(axis=1)
+        idx[a:a + block] = i1
+        top1[a:a + block] = t1
+        margin[a:a + block] = np.where(np.isfinite(t2), t1 - t2, np.inf)
+    return idx, top1, margin
+
+
+def encode(k, mu, xt, s, idx, w_down, storage):
+    """O6.  Residual of each non-reference token against its reference,
+    projected to d_c dimensions and rounded to storage ([en] §3 "Residual
+    Encoding": z = f_c(KV) - f_c(KV^R), which for a linear bias-free f_c is
+    f_c applied to the difference; [fr] §2: a light linear projection to a
+    d_c-dimensional code)."""
+    T = k.shape[0]
+    toks = nonref_positions(T, s)
+    delta = (k[toks] - mu) - xt[np.asarray(idx, np.int64) * s]
+    return rnd(delta @ w_down.T, storage)
+
+
+def compress_stream(k, s, w_down, storage, mu_in=None, force_idx=None) -> dict:
+    """One stream, steps O2-O6.  ``k`` holds storage-dtype values as float64.
+    ``force_idx`` re-encodes with given references (used where several
+    references are equally correct within the search tolerance)."""
+    k = np.asarray(k, np.float64)
+    T = k.shape[0]
+    mu = shared_component(k, storage) if mu_in is None else np.asarray(mu_in, np.float64)
+    xt = center(k, mu, storage)
+    refs = xt[ref_positions(T, s)]
+    idx, top1, margin = search(xt, s)
+    if force_idx is not None:
+        idx = np.asarray(force_idx, np.int64)
+    codes = encode(k, mu, xt, s, idx, w_down, storage)
+    return {"mu": mu, "refs": refs, "idx": idx, "codes": codes,
+            "top1": top1, "margin": margin, "xt": xt}
+
+
+def compress(k, v, s, w_down_k, w_down_v, storage) -> dict:
+    """All streams of one layer: k, v are [B][H][T][d].  Returns arrays shaped
+    [B][H][2][...] with index 0 = K and 1 = V."""
+    B, H, T, d = k.shape
+    out = {n: [] for n in ("mu", "refs", "idx", "codes", "top1", "margin")}
+    for b in range(B):
+        row = {n: [] for n in out}
+        for h in range(H):
+            pair = [compress_stream(k[b, h], s, w_down_k, storage),
+                    compress_stream(v[b, h], s, w_down_v, storage)]
+            for n in out:
+                row[n].append(np.stack([p[n] for p in pair]))
+        for n in out:
+            out[n].append(np.stack(row[n]))
+    return {n: np.stack(a) for n, a in out.items()}
+
+
+# ---------------------------------------------------------------------------
+# Decode.
+# ---------------------------------------------------------------------------
+
+def reconstruct_stream(mu, refs, idx, codes, w_up, s, T) -> np.ndarray:
+    """O7.  KV^ = f_d(z) + KV^R ([en] §3 "Reconstruction"; [fr] §2
+    "Architecture de compression"), with the shared component added back.
+    Reference tokens are stored whole: their reconstruction is mu + x~."""
+    d = refs.shape[1]
+    out = np.empty((T, d))
+    out[ref_positions(T, s)] = mu + refs
+    toks = nonref_positions(T, s)
+    out[toks] = mu + refs[np.asarray(idx, np.int64)] + codes @ w_up.T
+    return out
+
+
+def attend(q, khat, vhat, scale) -> np.ndarray:
+    """O8.  GQA decode attention over every reconstructed token: query head g
+    reads KV head g // G.  q [Hq][d], khat/vhat [H][T][d]."""
+    Hq = q.shape[0]
+    H = khat.shape[0]
+    G = Hq // H
+    out = np.empty((Hq, vhat.shape[2]))
+    for g in range(Hq):
+        h = g // G
+        sc = (khat[h] @ q[g]) * scale
+        p = np.exp(sc - sc.max())
+        out[g] = (p @ vhat[h]) / p.sum()
+    return out
+
+
+def decode(cache: dict, q, w_up_k, w_up_v, s, T, scale=None) -> np.ndarray:
+    """Decode one query per sequence over a compressed layer cache
+    (arrays [B][H][2][...]) by literal reconstruction, then attention.
+    q is [B][Hq][d]; returns [B][Hq][d] in float64."""
+    B, H = cache["mu"].shape[:2]
+    d = cache["mu"].shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    out = []
+    for b in range(B):
+        kh = np.stack([reconstruct_stream(cache["mu"][b, h, 0], cache["refs"][b, h, 0], cache["idx"][b, h, 0],
+                                          cache["codes"][b, h, 0], w_up_k, s, T) for h in range(H)])
+        vh = np.stack([reconstruct_stream(cache["mu"][b, h, 1], cache["refs"][b, h, 1], cache["idx"][b, h, 1],
+                                          cache["codes"][b, h, 1], w_up_v, s, T) for h in range(H)])
+        out.append(attend(np.asarray(q[b], np.float64), kh, vh, scale))
+    return np.stack(out)

@@ -1,0 +1,190 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins
+catch each of them.  This guards the pins themselves: a pin suite that a
+dropped term or a transposed operand slips through would not be pinning
+anything."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.deltakv_oracle as OD
+import tests.test_oracle_pins as P
+
+_ORIG = {"reconstruct": OD.reconstruct_stream, "attend": OD.attend, "rnd": OD.rnd}
+
+PINS = [
+    P.test_search_matches_brute_force_real_data,
+    P.test_search_handmade_cases,
+    P.test_stride_one_is_dense_attention,
+    lambda: P.test_full_rank_code_reconstructs_exactly(5),
+    P.test_shift_invariance,
+    P.test_output_ignores_key_mean,
+    P.test_zero_query_averages_values,
+    P.test_mean_is_arithmetic_mean,
+    P.test_hand_worked_example,
+    P.test_bf16_encode_rounds_each_code,
+    P.test_rnd_bf16_ties_and_double_rounding,
+    P.test_rnd_bf16_matches_bit_level_conversion,
+    P.test_bytes_identity_matches_arrays,
+    P.test_stored_values_are_representable,
+    lambda: P.test_search_matches_brute_force_integer_data(97, 5, 6, 6),
+]
+
+
+def _search_factory(*, see_next=False, last_tie=False, raw_dot=False):
+    def search(xt, s, block=2048):
+        T, _ = xt.shape
+        R = OD.n_refs(T, s)
+        toks = OD.nonref_positions(T, s)
+        refs = xt[OD.ref_positions(T, s)]
+        nr = np.sqrt((refs * refs).sum(1))
+        X = xt[toks]
+        nt = np.sqrt((X * X).sum(1))
+        dots = X @ refs.T
+        den = nt[:, None] * nr[None, :]
+        cos = dots if raw_dot else np.where(den > 0, dots / np.where(den > 0, den, 1.0), 0.0)
+        rp = np.arange(R) * s
+        ok = rp[None, :] < toks[:, None] + (s if see_next else 0)
+        cos = np.where(ok, cos, -np.inf)
+        if last_tie:
+            i1 = cos.shape[1] - 1 - np.argmax(cos[:, ::-1], axis=1)
+        else:
+            i1 = np.argmax(cos, axis=1)
+        rows = np.arange(len(toks))
+        t1 = cos[rows, i1]
+        c2 = cos.copy()
+        c2[rows, i1] = -np.inf
+        t2 = c2.max(1) if R > 1 else np.full(len(toks), -np.inf)
+        return i1, t1, np.where(np.isfinite(t2), t1 - t2, np.inf)
+    return search
+
+
+def _encode_sign(k, mu, xt, s, idx, w_down, storage):
+    toks = OD.nonref_positions(k.shape[0], s)
+    delta = (k[toks] - mu) + xt[np.asarray(idx) * s]
+    return OD.rnd(delta @ w_down.T, storage)
+
+
+def _encode_no_mu(k, mu, xt, s, idx, w_down, storage):
+    toks = OD.nonref_positions(k.shape[0], s)
+    delta = k[toks] - xt[np.asarray(idx) * s]
+    return OD.rnd(delta @ w_down.T, storage)
+
+
+def _encode_transposed(k, mu, xt, s, idx, w_down, storage):
+    toks = OD.nonref_positions(k.shape[0], s)
+    delta = (k[toks] - mu) - xt[np.asarray(idx) * s]
+    return OD.rnd(delta @ w_down, storage)
+
+
+def _encode_rounded_token(k, mu, xt, s, idx, w_down, storage):
+    toks = OD.nonref_positions(k.shape[0], s)
+    delta = xt[toks] - xt[np.asarray(idx) * s]
+    return OD.rnd(delta @ w_down.T, storage)
+
+
+def _recon_no_mu(mu, refs, idx, codes, w_up, s, T):
+    return _ORIG["reconstruct"](np.zeros_like(mu), refs, idx, codes, w_up, s, T)
+
+
+def _recon_shifted_ref(mu, refs, idx, codes, w_up, s, T):
+    return _ORIG["reconstruct"](mu, refs, np.minimum(np.asarray(idx) + 1, len(refs) - 1),
+                                            codes, w_up, s, T)
+
+
+def _recon_no_code(mu, refs, idx, codes, w_up, s, T):
+    return _ORIG["reconstruct"](mu, refs, idx, np.zeros_like(codes), w_up, s, T)
+
+
+def _attend_gqa_mod(q, khat, vhat, scale):
+    Hq, H = q.shape[0], khat.shape[0]
+    out = np.empty((Hq, vhat.shape[2]))
+    for g in range(Hq):
+        h = g % H
+        sc = (khat[h] @ q[g]) * scale
+        p = np.exp(sc - sc.max())
+        out[g] = (p @ vhat[h]) / p.sum()
+    return out
+
+
+def _attend_no_scale(q, khat, vhat, scale):
+    return _ORIG["attend"](q, khat, vhat, 1.0)
+
+
+def _mean_biased(k, storage):
+    return OD.rnd(k.sum(0) / max(k.shape[0] - 1, 1), storage)
+
+
+def _center_unrounded(k, mu, storage):
+    return k - mu
+
+
+def _rnd_via_f32(x, storage):
+    x = np.asarray(x, np.float64)
+    if storage == "bf16":
+        return _ORIG["rnd"](x.astype(np.float32).astype(np.float64), "bf16")
+    return _ORIG["rnd"](x, storage)
+
+
+def _rnd_truncate(x, storage):
+    x = np.asarray(x, np.float64)
+    if storage == "bf16":
+        _, e = np.frexp(x)
+        q = np.maximum(e, -125) - 8
+        return np.ldexp(np.trunc(np.ldexp(x, -q)), q)
+    return _ORIG["rnd"](x, storage)
+
+
+def _stream_bytes_no_idx(T, s, d, dc, storage):
+    e = OD.ELEM_BYTES[storage]
+    R = OD.n_refs(T, s)
+    return R * d * e + (T - R) * dc * e + d * e
+
+
+MUTATIONS = {
+    "search: also sees the next (later) reference": ("search", _search_factory(see_next=True)),
+    "search: ties to highest ordinal": ("search", _search_factory(last_tie=True)),
+    "search: raw dot product, no normalisation": ("search", _search_factory(raw_dot=True)),
+    "encode: + reference instead of -": ("encode", _encode_sign),
+    "encode: shared component not removed": ("encode", _encode_no_mu),
+    "encode: W_down transposed": ("encode", _encode_transposed),
+    "encode: residual of the rounded token": ("encode", _encode_rounded_token),
+    "reconstruct: mean not added back": ("reconstruct_stream", _recon_no_mu),
+    "reconstruct: reference index off by one": ("reconstruct_stream", _recon_shifted_ref),
+    "reconstruct: code term dropped": ("reconstruct_stream", _recon_no_code),
+    "attend: query head g reads KV head g % H": ("attend", _attend_gqa_mod),
+    "attend: softmax scale dropped": ("attend", _attend_no_scale),
+    "mean: divides by T - 1": ("shared_component", _mean_biased),
+    "center: not rounded to storage": ("center", _center_unrounded),
+    "rnd: bf16 through fp32 (double rounding)": ("rnd", _rnd_via_f32),
+    "rnd: bf16 truncates": ("rnd", _rnd_truncate),
+    "stream_bytes: index bytes forgotten": ("stream_bytes", _stream_bytes_no_idx),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(OD, attr, fn)
+    monkeypatch.setattr(oracle, attr, fn)
+    caught = []
+    for pin in PINS:
+        try:
+            pin()
+        except Exception as e:  # an assertion or a shape error both expose the mistake
+            caught.append((getattr(pin, "__name__", "pin"), type(e).__name__))
+    assert caught, f"no pin caught planted mistake: {name}"
+
+
+def test_unmutated_oracle_passes_all_pins():
+    for pin in PINS:
+        pin()
+
+
+def test_mutation_helpers_are_live():
+    """Sanity: the helper copies of the original functions exist and the
+    planted search variant really differs from the oracle on some input."""
+    rng = np.random.default_rng(0)
+    xt = rng.integers(-1, 2, size=(40, 3)).astype(float)
+    a = OD.search(xt, 3)[0]
+    b = _search_factory(last_tie=True)(xt, 3)[0]
+    assert not np.array_equal(a, b)
