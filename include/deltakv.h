@@ -1,0 +1,226 @@
+/*
+ * deltakv.h - C ABI of the DeltaKV hot path on AMD Instinct MI355X (gfx950).
+ *
+ * DeltaKV ("DeltaKV: Residual-Based KV Cache Compression via Long-Range
+ * Similarity", arXiv 2602.08005; explainer pages on gist.science) stores a
+ * KV cache as a few full reference tokens taken at a fixed stride plus, for
+ * every other token, a short code of its residual against the most similar
+ * earlier reference, after a component shared by all tokens is removed.
+ * Two calls make up the hot path:
+ *
+ *   deltakv_compress     prefill K/V -> compressed cache
+ *   deltakv_decode_attn  decode queries x compressed cache -> attention output
+ *
+ * Method statement implemented here (per stream = one sequence b, one KV
+ * head h, one of K or V; rnd = round to the storage dtype, nearest even):
+ *
+ *   mu      = rnd(mean_t k_t)                          shared component
+ *   x~_t    = rnd(k_t - mu)
+ *   refs[r] = x~_{r*s}            r = 0 .. R-1, R = ceil(T / s)
+ *   ref(t)  = argmax over r with r*s < t of cos(x~_t, refs[r]),
+ *             lowest r on exact ties, cos = 0 for a zero vector
+ *   code_t  = rnd(W_down ((k_t - mu) - refs[ref(t)]))   d_c values
+ *   decode: k^_t = mu + refs[ref(t)] + W_up code_t (refs are tokens too:
+ *           k^_{r*s} = mu + refs[r]); out_g = softmax_t(q_g . k^_t * scale) V^
+ *
+ * Sources (English page unless noted): Technical Summary §2 "Highly Shared
+ * Latent Components" (shared high-norm component removed first); §3
+ * "Strided Reference Selection" (references at stride s, retrieval of the
+ * nearest earlier references for each token); §3 "Residual Encoding"
+ * (z = f_c(KV) - f_c(KV^R)); §3 "Reconstruction" (KV^ = f_d(z) + KV^R);
+ * French page, Méthodologie §2 "Architecture de compression" (linear
+ * projection to a d_c-dimensional code).  Top-1 cosine, the mean as the
+ * shared component and a linear code are this library's concrete reading of
+ * the pages' retrieval, shared-component and compressor descriptions.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named as device pointers must be device memory on the current
+ *    HIP device; every other pointer is host memory and is only read during
+ *    the call.  The caller owns all memory, including workspaces.  The
+ *    library never allocates, frees or synchronises.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *    and runs asynchronously; outputs are valid once the stream reaches it.
+ *  - Argument checks run on the host before anything is enqueued; on any
+ *    error nothing is launched and outputs are untouched.  Launch failures
+ *    are reported as DKV_ERR_DEVICE.  No C++ exception crosses this ABI.
+ *  - The library holds no mutable global state; calls on different streams
+ *    with disjoint outputs and workspaces may run concurrently.
+ *  - Results are deterministic: the same inputs give the same bytes.
+ */
+#ifndef DELTAKV_H
+#define DELTAKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DKV_ABI_VERSION 1u
+
+typedef enum dkv_status {
+  DKV_OK = 0,
+  DKV_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  DKV_ERR_SHAPE = 2,       /* a size is zero or sizes are inconsistent       */
+  DKV_ERR_DTYPE = 3,       /* unknown storage dtype                          */
+  DKV_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned         */
+  DKV_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required        */
+  DKV_ERR_UNSUPPORTED = 6, /* a valid but unsupported size (see dkv_layout)  */
+  DKV_ERR_VERSION = 7,     /* dkv_layout.abi_version != DKV_ABI_VERSION      */
+  DKV_ERR_DEVICE = 8       /* a HIP launch or device query failed            */
+} dkv_status;
+
+typedef enum dkv_dtype {
+  DKV_F32 = 0,  /* IEEE binary32 storage                                   */
+  DKV_BF16 = 1  /* bfloat16 storage (raw 16-bit patterns), fp32 arithmetic */
+} dkv_dtype;
+
+/*
+ * Shape of one layer's compressed cache.  Plain data, passed by pointer.
+ *   abi_version  must equal DKV_ABI_VERSION
+ *   dtype        dkv_dtype of K, V, queries, W matrices and of refs/codes/mu
+ *   head_dim     d; supported: 64 or 128
+ *   code_dim     d_c; supported: a multiple of 16 with 16 <= d_c <= d
+ *   stride       s >= 1 (s = 1 stores every token whole)
+ *   idx_bytes    width of a stored reference ordinal: 2 (requires R <= 65536)
+ *                or 4
+ *   n_kv_heads   H >= 1;  batch  B >= 1;  seq_len  T >= 1
+ * Derived: R = ceil(T / s) references, N = T - R coded tokens per stream.
+ */
+typedef struct dkv_layout {
+  uint32_t abi_version;
+  uint32_t dtype;
+  uint32_t head_dim;
+  uint32_t code_dim;
+  uint32_t stride;
+  uint32_t idx_bytes;
+  uint32_t n_kv_heads;
+  uint32_t batch;
+  uint32_t seq_len;
+  uint32_t reserved; /* must be 0 */
+} dkv_layout;
+
+/*
+ * Device pointers of a compressed cache.  All arrays are dense, row-major,
+ * indexed [b][h][kv][...] with kv = 0 for K and 1 for V:
+ *   refs   [B][H][2][R][d]    storage dtype: x~ of the reference tokens
+ *   codes  [B][H][2][N][d_c]  storage dtype: one row per non-reference token
+ *                             in position order; token t (t mod s != 0)
+ *                             sits in row t - floor(t / s) - 1
+ *   idx    [B][H][2][N]       uint16 or uint32 (idx_bytes): reference
+ *                             ordinal r of each row (the token at r*s)
+ *   mu     [B][H][2][d]       storage dtype: the shared component
+ * Each pointer must be 16-byte aligned.
+ */
+typedef struct dkv_cache {
+  void* refs;
+  void* codes;
+  void* idx;
+  void* mu;
+} dkv_cache;
+
+/*
+ * Inputs of deltakv_compress.
+ *   k, v       device; element (b, h, t, i) of K is at
+ *              k[b*stride_b + h*stride_h + t*stride_t + i] (elements, storage
+ *              dtype); the same strides apply to v; the head_dim elements of
+ *              a token are contiguous; stride_t must be a multiple of 8
+ *   w_down_k   device [d_c][d] storage dtype, compressor of K (row j gives
+ *              code element j); w_down_v likewise for V
+ *   w_head_stride  elements between consecutive heads' matrices; 0 = one
+ *              matrix shared by all heads
+ *   mu_in      optional device [B][H][2][d]: use this shared component
+ *              instead of computing the mean (NULL = compute)
+ */
+typedef struct dkv_compress_in {
+  const void* k;
+  const void* v;
+  int64_t stride_b;
+  int64_t stride_h;
+  int64_t stride_t;
+  const void* w_down_k;
+  const void* w_down_v;
+  int64_t w_head_stride;
+  const void* mu_in;
+} dkv_compress_in;
+
+/*
+ * Inputs and output of deltakv_decode_attn (one query token per sequence).
+ *   q          device [B][Hq][d] storage dtype, contiguous
+ *   w_up_k     device [d][d_c] storage dtype, decompressor of K (column j
+ *              multiplies code element j); w_up_v likewise for V
+ *   w_head_stride  as in dkv_compress_in
+ *   n_q_heads  Hq, a multiple of H with G = Hq / H <= 16; query head g
+ *              attends over KV head g / G
+ *   n_splits   sequence splits per (b, h); 0 = choose automatically (see
+ *              dkv_decode_auto_splits); at most 1024
+ *   softmax_scale  multiplies q . k^; 0 means 1 / sqrt(d)
+ *   out        device [B][Hq][d] float32, written whole
+ */
+typedef struct dkv_decode_in {
+  const void* q;
+  const void* w_up_k;
+  const void* w_up_v;
+  int64_t w_head_stride;
+  uint32_t n_q_heads;
+  uint32_t n_splits;
+  float softmax_scale;
+  uint32_t reserved; /* must be 0 */
+  float* out;
+} dkv_decode_in;
+
+/* DKV_ABI_VERSION of the loaded library. */
+uint32_t dkv_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* dkv_status_str(dkv_status status);
+
+/* Validates a layout: DKV_OK or the first error found. */
+dkv_status dkv_layout_check(const dkv_layout* layout);
+
+/* Bytes of the four cache arrays, each rounded up to 256 bytes, as carved by
+ * dkv_cache_carve.  0 if the layout is invalid. */
+size_t dkv_cache_bytes(const dkv_layout* layout);
+
+/* Splits one device buffer of dkv_cache_bytes(layout) bytes starting at
+ * `base` (256-byte aligned) into refs, codes, idx and mu, in that order,
+ * each at a 256-byte boundary.  Writes only *cache. */
+dkv_status dkv_cache_carve(const dkv_layout* layout, void* base, dkv_cache* cache);
+
+/* Workspace bytes deltakv_compress needs for this layout (0 if invalid). */
+size_t dkv_compress_workspace_bytes(const dkv_layout* layout);
+
+/* Split count deltakv_decode_attn uses when n_splits = 0. */
+uint32_t dkv_decode_auto_splits(const dkv_layout* layout, uint32_t n_q_heads);
+
+/* Workspace bytes deltakv_decode_attn needs (0 if invalid); n_splits = 0
+ * means the automatic count. */
+size_t dkv_decode_workspace_bytes(const dkv_layout* layout, uint32_t n_q_heads, uint32_t n_splits);
+
+/*
+ * Compresses one layer's prefill K and V into `cache` (all four arrays are
+ * written whole).  `ws` is a device buffer of at least
+ * dkv_compress_workspace_bytes(layout) bytes, 16-byte aligned; its contents
+ * on entry do not matter.  Steps: shared component, centred references and
+ * their norms, reference search, residual codes.
+ */
+dkv_status deltakv_compress(const dkv_layout* layout, const dkv_compress_in* in, const dkv_cache* cache,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Decode attention of one query per sequence over a compressed cache, as if
+ * every token were reconstructed and attended to; mathematically equal to
+ * softmax(q K^T * scale) V^ over the reconstructed K^ and V^, computed
+ * without materialising them (the shared key component shifts every score
+ * equally and is not read).  `ws` as for deltakv_compress, of at least
+ * dkv_decode_workspace_bytes(layout, n_q_heads, n_splits) bytes.
+ */
+dkv_status deltakv_decode_attn(const dkv_layout* layout, const dkv_cache* cache, const dkv_decode_in* in,
+                               void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DELTAKV_H */

@@ -181,21 +181,22 @@ def cosines(xt: np.ndarray, tok: np.ndarray, ref: np.ndarray, s: int) -> np.ndar
     return np.where(den > 0, dot / np.where(den > 0, den, 1.0), 0.0)
 
 
-def search(xt: np.ndarray, s: int, block: int = 2048):
+def search(xt: np.ndarray, s: int, block: int = 2048, toks=None):
     """O5.  For every non-reference token, the earlier reference of highest
     cosine similarity ([en] §3 "Strided Reference Selection": each new token
     retrieves its nearest references from the strided set only; [de] §2: the
     most similar references).  Ties go to the lowest ordinal (np.argmax
     returns the first maximum).
 
-    Returns (idx, top1, margin) over non-reference tokens in position order;
-    margin = best minus second-best cosine (inf with a single candidate).
-    Each cosine is one fp64 dot product divided by the two fp64 norms; the
-    blocking over tokens only bounds memory.
+    Returns (idx, top1, margin) over non-reference tokens in position order
+    (or over the given non-reference positions ``toks``); margin = best minus
+    second-best cosine (inf with a single candidate).  Each cosine is one
+    fp64 dot product divided by the two fp64 norms; the blocking over tokens
+    only bounds memory.
     """
     T, _ = xt.shape
     R = n_refs(T, s)
-    toks = nonref_positions(T, s)
+    toks = nonref_positions(T, s) if toks is None else np.asarray(toks, np.int64)
     refs = xt[ref_positions(T, s)]
     nr = np.sqrt((refs * refs).sum(axis=1))
     idx = np.empty(len(toks), np.int64)
@@ -221,14 +222,14 @@ def search(xt: np.ndarray, s: int, block: int = 2048):
     return idx, top1, margin
 
 
-def encode(k, mu, xt, s, idx, w_down, storage):
+def encode(k, mu, xt, s, idx, w_down, storage, toks=None):
     """O6.  Residual of each non-reference token against its reference,
     projected to d_c dimensions and rounded to storage ([en] §3 "Residual
     Encoding": z = f_c(KV) - f_c(KV^R), which for a linear bias-free f_c is
     f_c applied to the difference; [fr] §2: a light linear projection to a
     d_c-dimensional code)."""
     T = k.shape[0]
-    toks = nonref_positions(T, s)
+    toks = nonref_positions(T, s) if toks is None else np.asarray(toks, np.int64)
     delta = (k[toks] - mu) - xt[np.asarray(idx, np.int64) * s]
     return rnd(delta @ w_down.T, storage)
 

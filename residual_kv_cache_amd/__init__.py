@@ -1,0 +1,224 @@
+"""Python binding of the DeltaKV HIP library (libdeltakv.so, gfx950).
+
+Argument marshalling only: every step of compression and decode attention
+runs in the library's HIP kernels.  PyTorch supplies device memory and the
+current stream.  The functions keep the C names of include/deltakv.h; a
+non-OK status raises DeltaKVError.  There is no fallback: if the library is
+missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdeltakv.so")
+
+ABI_VERSION = 1
+F32, BF16 = 0, 1
+STATUS = {0: "DKV_OK", 1: "DKV_ERR_NULL", 2: "DKV_ERR_SHAPE", 3: "DKV_ERR_DTYPE", 4: "DKV_ERR_ALIGN",
+          5: "DKV_ERR_WORKSPACE", 6: "DKV_ERR_UNSUPPORTED", 7: "DKV_ERR_VERSION", 8: "DKV_ERR_DEVICE"}
+EXPORTS = ["dkv_abi_version", "dkv_status_str", "dkv_layout_check", "dkv_cache_bytes", "dkv_cache_carve",
+           "dkv_compress_workspace_bytes", "dkv_decode_auto_splits", "dkv_decode_workspace_bytes",
+           "deltakv_compress", "deltakv_decode_attn"]
+
+
+class DeltaKVError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)}")
+
+
+class dkv_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint32) for n in ("abi_version", "dtype", "head_dim", "code_dim", "stride",
+                                              "idx_bytes", "n_kv_heads", "batch", "seq_len", "reserved")]
+
+    @property
+    def n_refs(self) -> int:
+        return -(-self.seq_len // self.stride)
+
+    @property
+    def n_codes(self) -> int:
+        return self.seq_len - self.n_refs
+
+
+class dkv_cache(ctypes.Structure):
+    _fields_ = [("refs", ctypes.c_void_p), ("codes", ctypes.c_void_p), ("idx", ctypes.c_void_p),
+                ("mu", ctypes.c_void_p)]
+
+
+class dkv_compress_in(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64), ("stride_t", ctypes.c_int64), ("w_down_k", ctypes.c_void_p),
+                ("w_down_v", ctypes.c_void_p), ("w_head_stride", ctypes.c_int64), ("mu_in", ctypes.c_void_p)]
+
+
+class dkv_decode_in(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("w_up_k", ctypes.c_void_p), ("w_up_v", ctypes.c_void_p),
+                ("w_head_stride", ctypes.c_int64), ("n_q_heads", ctypes.c_uint32), ("n_splits", ctypes.c_uint32),
+                ("softmax_scale", ctypes.c_float), ("reserved", ctypes.c_uint32), ("out", ctypes.c_void_p)]
+
+
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it was not built."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m residual_kv_cache_amd.build_lib`")
+        h = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        h.dkv_abi_version.restype = ctypes.c_uint32
+        h.dkv_status_str.restype = ctypes.c_char_p
+        h.dkv_status_str.argtypes = [ctypes.c_int]
+        h.dkv_layout_check.argtypes = [P(dkv_layout)]
+        h.dkv_cache_bytes.restype = ctypes.c_size_t
+        h.dkv_cache_bytes.argtypes = [P(dkv_layout)]
+        h.dkv_cache_carve.argtypes = [P(dkv_layout), ctypes.c_void_p, P(dkv_cache)]
+        h.dkv_compress_workspace_bytes.restype = ctypes.c_size_t
+        h.dkv_compress_workspace_bytes.argtypes = [P(dkv_layout)]
+        h.dkv_decode_auto_splits.restype = ctypes.c_uint32
+        h.dkv_decode_auto_splits.argtypes = [P(dkv_layout), ctypes.c_uint32]
+        h.dkv_decode_workspace_bytes.restype = ctypes.c_size_t
+        h.dkv_decode_workspace_bytes.argtypes = [P(dkv_layout), ctypes.c_uint32, ctypes.c_uint32]
+        h.deltakv_compress.argtypes = [P(dkv_layout), P(dkv_compress_in), P(dkv_cache), ctypes.c_void_p,
+                                       ctypes.c_size_t, ctypes.c_void_p]
+        h.deltakv_decode_attn.argtypes = [P(dkv_layout), P(dkv_cache), P(dkv_decode_in), ctypes.c_void_p,
+                                          ctypes.c_size_t, ctypes.c_void_p]
+        if h.dkv_abi_version() != ABI_VERSION:
+            raise RuntimeError("libdeltakv.so ABI version mismatch")
+        _lib_handle = h
+    return _lib_handle
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise DeltaKVError(status, what)
+
+
+# ---------------------------------------------------------------------------
+# Layout and cache.
+# ---------------------------------------------------------------------------
+
+def make_layout(dtype: str, head_dim: int, code_dim: int, stride: int, n_kv_heads: int, batch: int,
+                seq_len: int, idx_bytes: int | None = None) -> dkv_layout:
+    R = -(-seq_len // stride) if stride > 0 else 0
+    if idx_bytes is None:
+        idx_bytes = 2 if R <= 65536 else 4
+    return dkv_layout(ABI_VERSION, {"f32": F32, "bf16": BF16}[dtype], head_dim, code_dim, stride, idx_bytes,
+                      n_kv_heads, batch, seq_len, 0)
+
+
+def dkv_layout_check(layout: dkv_layout) -> int:
+    return lib().dkv_layout_check(ctypes.byref(layout))
+
+
+def dkv_cache_bytes(layout: dkv_layout) -> int:
+    return lib().dkv_cache_bytes(ctypes.byref(layout))
+
+
+def dkv_cache_carve(layout: dkv_layout, base: int) -> dkv_cache:
+    c = dkv_cache()
+    _check(lib().dkv_cache_carve(ctypes.byref(layout), ctypes.c_void_p(base), ctypes.byref(c)), "dkv_cache_carve")
+    return c
+
+
+def dkv_compress_workspace_bytes(layout: dkv_layout) -> int:
+    return lib().dkv_compress_workspace_bytes(ctypes.byref(layout))
+
+
+def dkv_decode_auto_splits(layout: dkv_layout, n_q_heads: int) -> int:
+    return lib().dkv_decode_auto_splits(ctypes.byref(layout), n_q_heads)
+
+
+def dkv_decode_workspace_bytes(layout: dkv_layout, n_q_heads: int, n_splits: int = 0) -> int:
+    return lib().dkv_decode_workspace_bytes(ctypes.byref(layout), n_q_heads, n_splits)
+
+
+def storage_torch_dtype(layout: dkv_layout):
+    return torch.bfloat16 if layout.dtype == BF16 else torch.float32
+
+
+class Cache:
+    """A compressed cache in one device buffer carved by dkv_cache_carve,
+    with torch views of its four arrays."""
+
+    def __init__(self, layout: dkv_layout, device="cuda"):
+        self.layout = layout
+        nbytes = dkv_cache_bytes(layout)
+        if nbytes == 0:
+            _check(dkv_layout_check(layout), "layout")
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.c = dkv_cache_carve(layout, self.buf.data_ptr())
+
+    def _view(self, ptr: int, shape, dtype) -> torch.Tensor:
+        off = ptr - self.buf.data_ptr()
+        n = math.prod(shape) * torch.empty((), dtype=dtype).element_size()
+        return self.buf[off:off + n].view(dtype).view(shape)
+
+    def arrays(self) -> dict:
+        L = self.layout
+        dt = storage_torch_dtype(L)
+        B, H, R, N, d, dc = L.batch, L.n_kv_heads, L.n_refs, L.n_codes, L.head_dim, L.code_dim
+        it = torch.int16 if L.idx_bytes == 2 else torch.int32
+        return {"refs": self._view(self.c.refs, (B, H, 2, R, d), dt),
+                "codes": self._view(self.c.codes, (B, H, 2, N, dc), dt),
+                "idx": self._view(self.c.idx, (B, H, 2, N), it),
+                "mu": self._view(self.c.mu, (B, H, 2, d), dt)}
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+# ---------------------------------------------------------------------------
+# Entry points.
+# ---------------------------------------------------------------------------
+
+def deltakv_compress(layout: dkv_layout, k: torch.Tensor, v: torch.Tensor, w_down_k: torch.Tensor,
+                     w_down_v: torch.Tensor, cache: Cache, ws: torch.Tensor, mu_in: torch.Tensor | None = None,
+                     w_head_stride: int = 0, stream=None) -> None:
+    """k, v: [B][H][T][d] (head dim contiguous; strides (b, h, t) taken from
+    k and required equal for v).  w_down_*: [d_c][d].  ws: device buffer of
+    at least dkv_compress_workspace_bytes(layout) bytes."""
+    if k.stride() != v.stride() or k.stride(-1) != 1:
+        raise ValueError("k and v need equal strides and a contiguous head dim")
+    a = dkv_compress_in(_ptr(k), _ptr(v), k.stride(0), k.stride(1), k.stride(2), _ptr(w_down_k), _ptr(w_down_v),
+                        w_head_stride, _ptr(mu_in))
+    _check(lib().deltakv_compress(ctypes.byref(layout), ctypes.byref(a), ctypes.byref(cache.c),
+                                  ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
+                                  ctypes.c_void_p(_stream(stream))), "deltakv_compress")
+
+
+def deltakv_decode_attn(layout: dkv_layout, cache: Cache, q: torch.Tensor, w_up_k: torch.Tensor,
+                        w_up_v: torch.Tensor, out: torch.Tensor, ws: torch.Tensor, n_splits: int = 0,
+                        softmax_scale: float = 0.0, w_head_stride: int = 0, stream=None) -> None:
+    """q: [B][Hq][d] contiguous; w_up_*: [d][d_c]; out: [B][Hq][d] float32."""
+    if not q.is_contiguous() or not out.is_contiguous() or out.dtype != torch.float32:
+        raise ValueError("q and out must be contiguous; out must be float32")
+    a = dkv_decode_in(_ptr(q), _ptr(w_up_k), _ptr(w_up_v), w_head_stride, q.shape[1], n_splits,
+                      softmax_scale, 0, _ptr(out))
+    _check(lib().deltakv_decode_attn(ctypes.byref(layout), ctypes.byref(cache.c), ctypes.byref(a),
+                                     ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
+                                     ctypes.c_void_p(_stream(stream))), "deltakv_decode_attn")
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+__all__ = ["lib", "make_layout", "dkv_layout", "dkv_cache", "dkv_compress_in", "dkv_decode_in", "Cache",
+           "DeltaKVError", "dkv_layout_check", "dkv_cache_bytes", "dkv_cache_carve", "dkv_compress_workspace_bytes",
+           "dkv_decode_auto_splits", "dkv_decode_workspace_bytes", "deltakv_compress", "deltakv_decode_attn",
+           "workspace", "storage_torch_dtype", "EXPORTS", "LIB_PATH"]

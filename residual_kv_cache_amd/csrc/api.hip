@@ -1,0 +1,238 @@
+// Host side of the DeltaKV C ABI: validation, layout arithmetic, workspace
+// carving and kernel dispatch.  Every check runs before anything is
+// enqueued; on error nothing is launched.
+
+#include <math.h>
+#include <stdint.h>
+
+#include "dkv_internal.h"
+
+using dkv::Shape;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+dkv_status check_layout(const dkv_layout* L, Shape* out) {
+  if (!L) return DKV_ERR_NULL;
+  if (L->abi_version != DKV_ABI_VERSION) return DKV_ERR_VERSION;
+  if (L->dtype != DKV_F32 && L->dtype != DKV_BF16) return DKV_ERR_DTYPE;
+  if (L->reserved != 0) return DKV_ERR_SHAPE;
+  if (L->head_dim == 0 || L->code_dim == 0 || L->stride == 0 || L->n_kv_heads == 0 || L->batch == 0 ||
+      L->seq_len == 0)
+    return DKV_ERR_SHAPE;
+  if (L->code_dim > L->head_dim) return DKV_ERR_SHAPE;
+  if (L->idx_bytes != 2 && L->idx_bytes != 4) return DKV_ERR_SHAPE;
+  if (L->head_dim != 64 && L->head_dim != 128) return DKV_ERR_UNSUPPORTED;
+  if (L->code_dim % 16 != 0) return DKV_ERR_UNSUPPORTED;
+  if (L->seq_len > (1u << 30) || L->n_kv_heads > 4096 || L->batch > 65535) return DKV_ERR_UNSUPPORTED;
+  const uint32_t R = (L->seq_len + L->stride - 1) / L->stride;
+  if (L->idx_bytes == 2 && R > 65536) return DKV_ERR_UNSUPPORTED;
+  const uint64_t streams = 2ull * L->batch * L->n_kv_heads;
+  if (streams > 65535) return DKV_ERR_UNSUPPORTED;  // grid y limit of the stream axis
+  if (out) {
+    out->d = (int)L->head_dim;
+    out->dc = (int)L->code_dim;
+    out->s = (int)L->stride;
+    out->T = (int)L->seq_len;
+    out->R = (int)R;
+    out->N = (int)(L->seq_len - R);
+    out->H = (int)L->n_kv_heads;
+    out->B = (int)L->batch;
+    out->idx_bytes = (int)L->idx_bytes;
+    out->bf16 = L->dtype == DKV_BF16;
+  }
+  return DKV_OK;
+}
+
+struct ArrayBytes {
+  size_t refs, codes, idx, mu;
+};
+
+ArrayBytes array_bytes(const Shape& sh) {
+  const size_t n = (size_t)sh.n_streams();
+  ArrayBytes a;
+  a.refs = n * sh.R * sh.d * sh.elem();
+  a.codes = n * sh.N * sh.dc * sh.elem();
+  a.idx = n * sh.N * sh.idx_bytes;
+  a.mu = n * sh.d * sh.elem();
+  return a;
+}
+
+size_t pad(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+dkv_status check_cache(const dkv_cache* c, const Shape& sh) {
+  if (!c) return DKV_ERR_NULL;
+  if (!c->refs || !c->mu) return DKV_ERR_NULL;
+  if (sh.N > 0 && (!c->codes || !c->idx)) return DKV_ERR_NULL;
+  if (!aligned16(c->refs) || !aligned16(c->codes) || !aligned16(c->idx) || !aligned16(c->mu)) return DKV_ERR_ALIGN;
+  return DKV_OK;
+}
+
+uint32_t auto_splits(const Shape& sh) {
+  // Aim for about 2048 blocks over the B*H heads (8 per CU on 256 CUs), at
+  // least ~256 cached tokens per split, at most 1024 splits.
+  const int64_t heads = (int64_t)sh.B * sh.H;
+  int64_t by_chip = (2048 + heads - 1) / heads;
+  int64_t by_len = (sh.T + 255) / 256;
+  int64_t s = by_chip < by_len ? by_chip : by_len;
+  if (s < 1) s = 1;
+  if (s > 1024) s = 1024;
+  return (uint32_t)s;
+}
+
+dkv_status from_hip(hipError_t e) { return e == hipSuccess ? DKV_OK : DKV_ERR_DEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+uint32_t dkv_abi_version(void) { return DKV_ABI_VERSION; }
+
+const char* dkv_status_str(dkv_status s) {
+  switch (s) {
+    case DKV_OK: return "DKV_OK";
+    case DKV_ERR_NULL: return "DKV_ERR_NULL: a required pointer is NULL";
+    case DKV_ERR_SHAPE: return "DKV_ERR_SHAPE: a size is zero or sizes are inconsistent";
+    case DKV_ERR_DTYPE: return "DKV_ERR_DTYPE: unknown storage dtype";
+    case DKV_ERR_ALIGN: return "DKV_ERR_ALIGN: a device pointer or stride is not 16-byte aligned";
+    case DKV_ERR_WORKSPACE: return "DKV_ERR_WORKSPACE: workspace missing or too small";
+    case DKV_ERR_UNSUPPORTED: return "DKV_ERR_UNSUPPORTED: valid but unsupported size";
+    case DKV_ERR_VERSION: return "DKV_ERR_VERSION: ABI version mismatch";
+    case DKV_ERR_DEVICE: return "DKV_ERR_DEVICE: a HIP launch or device query failed";
+  }
+  return "DKV_ERR_UNKNOWN";
+}
+
+dkv_status dkv_layout_check(const dkv_layout* layout) { return check_layout(layout, nullptr); }
+
+size_t dkv_cache_bytes(const dkv_layout* layout) {
+  Shape sh;
+  if (check_layout(layout, &sh) != DKV_OK) return 0;
+  const ArrayBytes a = array_bytes(sh);
+  return pad(a.refs) + pad(a.codes) + pad(a.idx) + pad(a.mu);
+}
+
+dkv_status dkv_cache_carve(const dkv_layout* layout, void* base, dkv_cache* cache) {
+  Shape sh;
+  dkv_status st = check_layout(layout, &sh);
+  if (st != DKV_OK) return st;
+  if (!base || !cache) return DKV_ERR_NULL;
+  if (((uintptr_t)base % kAlign) != 0) return DKV_ERR_ALIGN;
+  const ArrayBytes a = array_bytes(sh);
+  char* p = (char*)base;
+  cache->refs = p;
+  p += pad(a.refs);
+  cache->codes = p;
+  p += pad(a.codes);
+  cache->idx = p;
+  p += pad(a.idx);
+  cache->mu = p;
+  return DKV_OK;
+}
+
+size_t dkv_compress_workspace_bytes(const dkv_layout* layout) {
+  Shape sh;
+  if (check_layout(layout, &sh) != DKV_OK) return 0;
+  return dkv::compress_ws_bytes(sh);
+}
+
+uint32_t dkv_decode_auto_splits(const dkv_layout* layout, uint32_t n_q_heads) {
+  Shape sh;
+  (void)n_q_heads;
+  if (check_layout(layout, &sh) != DKV_OK) return 0;
+  return auto_splits(sh);
+}
+
+size_t dkv_decode_workspace_bytes(const dkv_layout* layout, uint32_t n_q_heads, uint32_t n_splits) {
+  Shape sh;
+  if (check_layout(layout, &sh) != DKV_OK) return 0;
+  if (n_q_heads == 0 || n_q_heads % sh.H != 0 || n_q_heads / sh.H > 16) return 0;
+  if (n_splits > 1024) return 0;
+  const int splits = n_splits ? (int)n_splits : (int)auto_splits(sh);
+  return dkv::decode_ws_bytes(sh, (int)(n_q_heads / sh.H), splits);
+}
+
+dkv_status deltakv_compress(const dkv_layout* layout, const dkv_compress_in* in, const dkv_cache* cache, void* ws,
+                            size_t ws_bytes, void* stream) {
+  Shape sh;
+  dkv_status st = check_layout(layout, &sh);
+  if (st != DKV_OK) return st;
+  if (!in) return DKV_ERR_NULL;
+  if (!in->k || !in->v || !in->w_down_k || !in->w_down_v) return DKV_ERR_NULL;
+  if ((st = check_cache(cache, sh)) != DKV_OK) return st;
+  if (!aligned16(in->k) || !aligned16(in->v) || !aligned16(in->w_down_k) || !aligned16(in->w_down_v) ||
+      !aligned16(in->mu_in))
+    return DKV_ERR_ALIGN;
+  if (in->stride_t < sh.d || in->stride_b < 0 || in->stride_h < 0 || in->w_head_stride < 0) return DKV_ERR_SHAPE;
+  if (in->stride_t % 8 || in->stride_b % 8 || in->stride_h % 8 || in->w_head_stride % 8) return DKV_ERR_ALIGN;
+  if (in->w_head_stride != 0 && in->w_head_stride < (int64_t)sh.d * sh.dc) return DKV_ERR_SHAPE;
+  const size_t need = dkv::compress_ws_bytes(sh);
+  if (!ws || ws_bytes < need) return DKV_ERR_WORKSPACE;
+  if (!aligned16(ws)) return DKV_ERR_ALIGN;
+
+  dkv::CompressArgs a;
+  a.k = in->k;
+  a.v = in->v;
+  a.sb = in->stride_b;
+  a.sh = in->stride_h;
+  a.st = in->stride_t;
+  a.wdk = in->w_down_k;
+  a.wdv = in->w_down_v;
+  a.w_hs = in->w_head_stride;
+  a.mu_in = in->mu_in;
+  a.refs = cache->refs;
+  a.codes = cache->codes;
+  a.idx = cache->idx;
+  a.mu = cache->mu;
+  a.mean_part = (double*)((char*)ws + dkv::ws_mean_off(sh));
+  a.inv_n = (float*)((char*)ws + dkv::ws_invn_off(sh));
+  return from_hip(dkv::launch_compress(sh, a, (hipStream_t)stream));
+}
+
+dkv_status deltakv_decode_attn(const dkv_layout* layout, const dkv_cache* cache, const dkv_decode_in* in, void* ws,
+                               size_t ws_bytes, void* stream) {
+  Shape sh;
+  dkv_status st = check_layout(layout, &sh);
+  if (st != DKV_OK) return st;
+  if (!in) return DKV_ERR_NULL;
+  if ((st = check_cache(cache, sh)) != DKV_OK) return st;
+  if (!in->q || !in->w_up_k || !in->w_up_v || !in->out) return DKV_ERR_NULL;
+  if (!aligned16(in->q) || !aligned16(in->w_up_k) || !aligned16(in->w_up_v) || !aligned16(in->out))
+    return DKV_ERR_ALIGN;
+  if (in->reserved != 0) return DKV_ERR_SHAPE;
+  if (in->n_q_heads == 0 || in->n_q_heads % sh.H != 0) return DKV_ERR_SHAPE;
+  if (in->n_q_heads / sh.H > 16) return DKV_ERR_UNSUPPORTED;
+  if (in->n_splits > 1024) return DKV_ERR_UNSUPPORTED;
+  if (in->w_head_stride < 0) return DKV_ERR_SHAPE;
+  if (in->w_head_stride != 0 && in->w_head_stride < (int64_t)sh.d * sh.dc) return DKV_ERR_SHAPE;
+  if (!(in->softmax_scale >= 0.f) || isinf(in->softmax_scale)) return DKV_ERR_SHAPE;
+  const int G = (int)(in->n_q_heads / sh.H);
+  const int splits = in->n_splits ? (int)in->n_splits : (int)auto_splits(sh);
+  const size_t need = dkv::decode_ws_bytes(sh, G, splits);
+  if (!ws || ws_bytes < need) return DKV_ERR_WORKSPACE;
+  if (!aligned16(ws)) return DKV_ERR_ALIGN;
+
+  dkv::DecodeArgs a;
+  a.q = in->q;
+  a.wuk = in->w_up_k;
+  a.wuv = in->w_up_v;
+  a.w_hs = in->w_head_stride;
+  a.G = G;
+  a.Hq = (int)in->n_q_heads;
+  a.splits = splits;
+  a.scale = in->softmax_scale > 0.f ? in->softmax_scale : 1.0f / sqrtf((float)sh.d);
+  a.out = in->out;
+  a.refs = cache->refs;
+  a.codes = cache->codes;
+  a.idx = cache->idx;
+  a.mu = cache->mu;
+  a.score = (float*)ws;
+  a.qp = (float*)((char*)ws + dkv::ws_qp_off(sh, G));
+  a.part = (float*)((char*)ws + dkv::ws_part_off(sh, G));
+  return from_hip(dkv::launch_decode(sh, a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,481 @@
+// DeltaKV compression kernels for gfx950.
+//
+// One stream = one (sequence b, KV head h, tensor kv) with kv = 0 for K and
+// 1 for V; stream id = (b * H + h) * 2 + kv.  Four steps per stream:
+//
+//   mean    mu = rnd(mean_t k_t), fp64 partial sums then a fixed-order fp64
+//           total (the component all tokens share; DeltaKV explainer,
+//           English page, Technical Summary §2 "Highly Shared Latent
+//           Components")
+//   center  refs[r] = rnd(k_{r*s} - mu) and 1/||refs[r]|| (English page §3
+//           "Strided Reference Selection": references at a fixed stride)
+//   search  ref(t) = argmax over earlier references of the cosine, lowest
+//           ordinal on ties (same section: each token retrieves its most
+//           similar references from the strided set)
+//   encode  code_t = rnd(W_down ((k_t - mu) - refs[ref(t)])) (English page
+//           §3 "Residual Encoding"; French page §2 "Architecture de
+//           compression": projection to d_c dimensions)
+//
+// bfloat16 storage runs the search and the encode on MFMA: the centred
+// tokens and references are exact bf16 values, so the bf16 x bf16 products
+// are exact and only the fp32 accumulation rounds.  float32 storage runs
+// plain fp32 VALU kernels.
+
+#include "dkv_device.h"
+#include "dkv_internal.h"
+
+namespace dkv {
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Loads of 8 consecutive storage elements (16-byte aligned) as floats.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void load8(const uint16_t* p, float* out) {
+  uint4 u = *reinterpret_cast<const uint4*>(p);
+  uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+__device__ __forceinline__ void load8(const float* p, float* out) {
+  float4 a = *reinterpret_cast<const float4*>(p);
+  float4 b = *reinterpret_cast<const float4*>(p + 4);
+  out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+  out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+
+struct StreamId {
+  int b, h, kv;
+};
+
+__device__ __forceinline__ StreamId decode_stream(int stream, int H) {
+  StreamId id;
+  id.kv = stream & 1;
+  int bh = stream >> 1;
+  id.b = bh / H;
+  id.h = bh % H;
+  return id;
+}
+
+template <class S>
+__device__ __forceinline__ const typename S::T* stream_src(const CompressArgs& a, StreamId id) {
+  const typename S::T* base = (const typename S::T*)(id.kv ? a.v : a.k);
+  return base + id.b * a.sb + id.h * a.sh;
+}
+
+// ---------------------------------------------------------------------------
+// Mean: stage 1, fp64 partial sums over kMeanChunk tokens.
+// grid (chunks, streams), block 256.
+// ---------------------------------------------------------------------------
+
+template <class S>
+__global__ __launch_bounds__(256) void k_mean_partial(CompressArgs a, Shape sh) {
+  __shared__ double red[256 / 8][128];
+  const int stream = blockIdx.y;
+  const StreamId id = decode_stream(stream, sh.H);
+  const typename S::T* src = stream_src<S>(a, id);
+  const int tpr = sh.d / 8;           // threads per token row
+  const int rows = 256 / tpr;         // rows per pass
+  const int tid = threadIdx.x;
+  const int c0 = (tid % tpr) * 8;
+  const int r0 = tid / tpr;
+  const int t0 = blockIdx.x * kMeanChunk;
+  const int t1 = min(sh.T, t0 + kMeanChunk);
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int t = t0 + r0; t < t1; t += rows) {
+    float x[8];
+    load8(src + (int64_t)t * a.st + c0, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += (double)x[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[r0][c0 + e] = acc[e];
+  __syncthreads();
+  if (tid < sh.d) {
+    double s = 0.0;
+    for (int r = 0; r < rows; ++r) s += red[r][tid];
+    a.mean_part[((size_t)stream * gridDim.x + blockIdx.x) * sh.d + tid] = s;
+  }
+}
+
+// Mean: stage 2, fixed-order total, divide, round once.  grid streams, block d.
+template <class S>
+__global__ __launch_bounds__(128) void k_mean_final(CompressArgs a, Shape sh, int chunks) {
+  const int stream = blockIdx.x;
+  const int i = threadIdx.x;
+  if (i >= sh.d) return;
+  typename S::T* mu = (typename S::T*)a.mu;
+  if (a.mu_in) {
+    mu[(size_t)stream * sh.d + i] = ((const typename S::T*)a.mu_in)[(size_t)stream * sh.d + i];
+    return;
+  }
+  double s = 0.0;
+  for (int c = 0; c < chunks; ++c) s += a.mean_part[((size_t)stream * chunks + c) * sh.d + i];
+  mu[(size_t)stream * sh.d + i] = S::from_f64(s / (double)sh.T);
+}
+
+// ---------------------------------------------------------------------------
+// Centred references and their inverse norms.  grid (ceil(R/4), streams),
+// block 256: one wave per reference, lanes across the head dim.
+// ---------------------------------------------------------------------------
+
+template <class S>
+__global__ __launch_bounds__(256) void k_center_refs(CompressArgs a, Shape sh) {
+  const int stream = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + wave;
+  if (r >= sh.R) return;
+  const StreamId id = decode_stream(stream, sh.H);
+  const typename S::T* src = stream_src<S>(a, id) + (int64_t)r * sh.s * a.st;
+  const typename S::T* mu = (const typename S::T*)a.mu + (size_t)stream * sh.d;
+  typename S::T* dst = (typename S::T*)a.refs + ((size_t)stream * sh.R + r) * sh.d;
+  float n2 = 0.f;
+  for (int i = lane; i < sh.d; i += 64) {
+    typename S::T x = S::sub_rn(S::load(src[i]), S::load(mu[i]));
+    dst[i] = x;
+    float f = S::load(x);
+    n2 += f * f;
+  }
+  n2 = wave_sum(n2);
+  if (lane == 0) a.inv_n[(size_t)stream * sh.R + r] = n2 > 0.f ? 1.0f / sqrtf(n2) : 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Reference search, bfloat16 storage, MFMA.
+//
+// Block = 4 waves = 256 consecutive positions of one stream; wave w owns 64
+// of them (4 MFMA N-tiles of 16 tokens).  The centred tokens x~_t are built
+// once in registers as MFMA B operands (exact bf16).  References stream
+// through LDS in chunks of 64 (4 M-tiles of 16); each M-tile x N-tile block
+// of cosines is an MFMA 16x16x32 chain over the head dim.  The C fragment of
+// lane l holds references 4*(l/16)+i (i = 0..3) for token l%16, so each lane
+// keeps a running best (score, ordinal) per N-tile and sees its references
+// in increasing order; a strict '>' keeps the lowest ordinal on ties.  The
+// four lane groups that share a token merge at the end (larger score, then
+// lower ordinal).  Scores are <x~_t, x~_r> / ||x~_r||: the token's own norm
+// is the same for every candidate and does not change the argmax.
+// ---------------------------------------------------------------------------
+
+constexpr int kSearchRefs = 64;   // references per LDS chunk
+constexpr int kSearchTok = 256;   // positions per block
+
+template <int D>
+__global__ __launch_bounds__(256) void k_search_mfma(CompressArgs a, Shape sh) {
+  constexpr int KS = D / 32;      // MFMA K-steps over the head dim
+  constexpr int LDR = D + 8;      // padded LDS row (elements)
+  __shared__ __attribute__((aligned(16))) uint16_t lds_ref[kSearchRefs * LDR];
+  __shared__ float lds_inv[kSearchRefs];
+
+  const int stream = blockIdx.y;
+  const int tile = gridDim.x - 1 - blockIdx.x;   // heavy (late) tiles first
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lrow = lane & 15, lgrp = lane >> 4;
+  const StreamId id = decode_stream(stream, sh.H);
+  const uint16_t* src = stream_src<BF16>(a, id);
+  const uint16_t* mu = (const uint16_t*)a.mu + (size_t)stream * D;
+  const uint16_t* refs = (const uint16_t*)a.refs + (size_t)stream * sh.R * D;
+  const float* inv_n = a.inv_n + (size_t)stream * sh.R;
+
+  const int tb = tile * kSearchTok;
+  const int tw = tb + wave * 64;
+  // References any position of the block / wave may use: r*s < t.
+  const int tmax_b = min(sh.T - 1, tb + kSearchTok - 1);
+  const int rend_b = (tmax_b + sh.s - 1) / sh.s;
+  const int tmax_w = min(sh.T - 1, tw + 63);
+  const int rend_w = tw < sh.T ? (tmax_w + sh.s - 1) / sh.s : 0;
+
+  // B operands: centred tokens, [N-tile][K-step].
+  bf16x8 bt[4][KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int c = ks * 32 + lgrp * 8;
+    float m[8];
+    load8(mu + c, m);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int t = tw + nt * 16 + lrow;
+      union { bf16x8 v; uint16_t u[8]; } p;
+      if (t < sh.T) {
+        float x[8];
+        load8(src + (int64_t)t * a.st + c, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p.u[e] = bf16_sub_rn(x[e], m[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p.u[e] = 0;
+      }
+      bt[nt][ks] = p.v;
+    }
+  }
+
+  float best[4];
+  int bidx[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) { best[nt] = -INFINITY; bidx[nt] = 0; }
+
+  const int nchunks = (rend_b + kSearchRefs - 1) / kSearchRefs;
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int rc = ch * kSearchRefs;
+    __syncthreads();
+    // Stage 64 references (16 B per thread per step) and their inverse norms.
+    for (int p = threadIdx.x; p < kSearchRefs * (D / 8); p += 256) {
+      const int row = p / (D / 8), col = (p % (D / 8)) * 8;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (rc + row < rend_b) v = *reinterpret_cast<const uint4*>(refs + (size_t)(rc + row) * D + col);
+      *reinterpret_cast<uint4*>(&lds_ref[row * LDR + col]) = v;
+    }
+    if (threadIdx.x < kSearchRefs) {
+      const int r = rc + threadIdx.x;
+      lds_inv[threadIdx.x] = r < rend_b ? inv_n[r] : 0.f;
+    }
+    __syncthreads();
+    if (rc >= rend_w) continue;
+#pragma unroll 1
+    for (int mt = 0; mt < kSearchRefs / 16; ++mt) {
+      const int rbase = rc + mt * 16;
+      if (rbase >= rend_w) break;
+      bf16x8 ar[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        ar[ks] = *reinterpret_cast<const bf16x8*>(&lds_ref[(mt * 16 + lrow) * LDR + ks * 32 + lgrp * 8]);
+      f32x4 acc[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar[ks], bt[nt][ks], acc[nt], 0, 0, 0);
+      float inv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) inv[i] = lds_inv[mt * 16 + lgrp * 4 + i];
+      const int r0 = rbase + lgrp * 4;
+      // A tile needs the causal mask when its last reference is not earlier
+      // than the wave's first position.
+      if ((rbase + 15) * sh.s >= tw) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int t = tw + nt * 16 + lrow;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float sc = acc[nt][i] * inv[i];
+            if ((r0 + i) * sh.s < t && sc > best[nt]) { best[nt] = sc; bidx[nt] = r0 + i; }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float sc = acc[nt][i] * inv[i];
+            if (sc > best[nt]) { best[nt] = sc; bidx[nt] = r0 + i; }
+          }
+      }
+    }
+  }
+
+  // Merge the four lane groups of each token; lanes 0..15 write.
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    float v = best[nt];
+    int r = bidx[nt];
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      const float v2 = __shfl_xor(v, o, 64);
+      const int r2 = __shfl_xor(r, o, 64);
+      if (v2 > v || (v2 == v && r2 < r)) { v = v2; r = r2; }
+    }
+    const int t = tw + nt * 16 + lrow;
+    if (lgrp == 0 && t < sh.T && t % sh.s != 0)
+      store_idx(a.idx, (size_t)stream * sh.N + pos_to_slot(t, sh.s), sh.idx_bytes, (uint32_t)r);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Reference search, float32 storage: one thread per position, fp32 VALU.
+// grid (ceil(T/256), streams), block 256.  References in LDS chunks of 32.
+// ---------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(256) void k_search_f32(CompressArgs a, Shape sh) {
+  constexpr int CH = 32;
+  __shared__ float lds_ref[CH][D];
+  __shared__ float lds_inv[CH];
+  const int stream = blockIdx.y;
+  const int tile = gridDim.x - 1 - blockIdx.x;
+  const StreamId id = decode_stream(stream, sh.H);
+  const float* src = stream_src<F32>(a, id);
+  const float* mu = (const float*)a.mu + (size_t)stream * D;
+  const float* refs = (const float*)a.refs + (size_t)stream * sh.R * D;
+  const float* inv_n = a.inv_n + (size_t)stream * sh.R;
+  const int t = tile * 256 + threadIdx.x;
+  const int tmax_b = min(sh.T - 1, tile * 256 + 255);
+  const int rend_b = (tmax_b + sh.s - 1) / sh.s;
+  float x[D];
+  if (t < sh.T) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) x[i] = src[(int64_t)t * a.st + i] - mu[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < D; ++i) x[i] = 0.f;
+  }
+  float best = -INFINITY;
+  int bi = 0;
+  for (int rc = 0; rc < rend_b; rc += CH) {
+    __syncthreads();
+    for (int p = threadIdx.x; p < CH * D; p += 256) {
+      const int row = p / D, col = p % D;
+      lds_ref[row][col] = rc + row < rend_b ? refs[(size_t)(rc + row) * D + col] : 0.f;
+    }
+    if (threadIdx.x < CH) lds_inv[threadIdx.x] = rc + threadIdx.x < rend_b ? inv_n[rc + threadIdx.x] : 0.f;
+    __syncthreads();
+    for (int j = 0; j < CH; ++j) {
+      const int r = rc + j;
+      if (r * sh.s >= t) break;
+      float dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < D; ++i) dot = fmaf(x[i], lds_ref[j][i], dot);
+      const float sc = dot * lds_inv[j];
+      if (sc > best) { best = sc; bi = r; }
+    }
+  }
+  if (t < sh.T && t % sh.s != 0)
+    store_idx(a.idx, (size_t)stream * sh.N + pos_to_slot(t, sh.s), sh.idx_bytes, (uint32_t)bi);
+}
+
+// ---------------------------------------------------------------------------
+// Encode, bfloat16 storage, MFMA.
+//
+// grid (ceil(N/64), streams), block 256: wave w encodes coded rows
+// 64*blockIdx.x + 16*w + (0..15).  A = W_down rows (M = code elements),
+// B = residuals of 16 tokens (N), K = head dim.  The fp32 residual
+// delta = (k - mu) - ref is split into three bf16 parts hi + mid + lo that
+// sum to it within 2^-24 relative, so three MFMA passes reproduce the fp32
+// projection; the code is rounded once to bf16.
+// ---------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(256) void k_encode_mfma(CompressArgs a, Shape sh) {
+  constexpr int KS = D / 32;
+  const int stream = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lrow = lane & 15, lgrp = lane >> 4;
+  const StreamId id = decode_stream(stream, sh.H);
+  const uint16_t* src = stream_src<BF16>(a, id);
+  const uint16_t* mu = (const uint16_t*)a.mu + (size_t)stream * D;
+  const uint16_t* refs = (const uint16_t*)a.refs + (size_t)stream * sh.R * D;
+  const uint16_t* wd = (const uint16_t*)(id.kv ? a.wdv : a.wdk) + (size_t)id.h * a.w_hs;
+  uint16_t* codes = (uint16_t*)a.codes + (size_t)stream * sh.N * sh.dc;
+
+  const int n = blockIdx.x * 64 + wave * 16 + lrow;   // this lane's coded row
+  const bool valid = n < sh.N;
+  const int t = valid ? slot_to_pos(n, sh.s) : 0;
+  const int r = valid ? min((int)load_idx(a.idx, (size_t)stream * sh.N + n, sh.idx_bytes), sh.R - 1) : 0;
+
+  bf16x8 bh[KS], bm[KS], bl[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int c = ks * 32 + lgrp * 8;
+    union { bf16x8 v; uint16_t u[8]; } ph, pm, pl;
+    if (valid) {
+      float x[8], m[8], rf[8];
+      load8(src + (int64_t)t * a.st + c, x);
+      load8(mu + c, m);
+      load8(refs + (size_t)r * D + c, rf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float dlt = (x[e] - m[e]) - rf[e];
+        const uint16_t h = f2bf(dlt);
+        const float r1 = dlt - bf2f(h);
+        const uint16_t md = f2bf(r1);
+        const float r2 = r1 - bf2f(md);
+        ph.u[e] = h; pm.u[e] = md; pl.u[e] = f2bf(r2);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { ph.u[e] = 0; pm.u[e] = 0; pl.u[e] = 0; }
+    }
+    bh[ks] = ph.v; bm[ks] = pm.v; bl[ks] = pl.v;
+  }
+
+  for (int mt = 0; mt < sh.dc / 16; ++mt) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 aw = *reinterpret_cast<const bf16x8*>(wd + (size_t)(mt * 16 + lrow) * D + ks * 32 + lgrp * 8);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bl[ks], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bm[ks], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bh[ks], acc, 0, 0, 0);
+    }
+    // Lane l holds code elements mt*16 + 4*(l/16) + (0..3) of row l%16.
+    if (valid) {
+      uint2 o;
+      o.x = (uint32_t)f2bf(acc[0]) | ((uint32_t)f2bf(acc[1]) << 16);
+      o.y = (uint32_t)f2bf(acc[2]) | ((uint32_t)f2bf(acc[3]) << 16);
+      *reinterpret_cast<uint2*>(codes + (size_t)n * sh.dc + mt * 16 + lgrp * 4) = o;
+    }
+  }
+}
+
+// Encode, float32 storage: one thread per coded row, fp32 VALU.
+// grid (ceil(N/256), streams), block 256.
+template <int D>
+__global__ __launch_bounds__(256) void k_encode_f32(CompressArgs a, Shape sh) {
+  const int stream = blockIdx.y;
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= sh.N) return;
+  const StreamId id = decode_stream(stream, sh.H);
+  const float* wd = (const float*)(id.kv ? a.wdv : a.wdk) + (size_t)id.h * a.w_hs;
+  const float* src = stream_src<F32>(a, id);
+  const float* mu = (const float*)a.mu + (size_t)stream * D;
+  const float* refs = (const float*)a.refs + (size_t)stream * sh.R * D;
+  const int t = slot_to_pos(n, sh.s);
+  const int r = min((int)load_idx(a.idx, (size_t)stream * sh.N + n, sh.idx_bytes), sh.R - 1);
+  float dl[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) dl[i] = (src[(int64_t)t * a.st + i] - mu[i]) - refs[(size_t)r * D + i];
+  float* codes = (float*)a.codes + ((size_t)stream * sh.N + n) * sh.dc;
+  for (int j = 0; j < sh.dc; ++j) {
+    float c = 0.f;
+#pragma unroll
+    for (int i = 0; i < D; ++i) c = fmaf(wd[(size_t)j * D + i], dl[i], c);
+    codes[j] = c;
+  }
+}
+
+template <int D>
+hipError_t launch_compress_d(const Shape& sh, const CompressArgs& a, hipStream_t st) {
+  const int ns = sh.n_streams();
+  const int chunks = mean_chunks(sh);
+  if (sh.bf16) {
+    k_mean_partial<BF16><<<dim3(chunks, ns), 256, 0, st>>>(a, sh);
+    k_mean_final<BF16><<<ns, 128, 0, st>>>(a, sh, chunks);
+    k_center_refs<BF16><<<dim3((sh.R + 3) / 4, ns), 256, 0, st>>>(a, sh);
+    if (sh.N > 0) {
+      k_search_mfma<D><<<dim3((sh.T + kSearchTok - 1) / kSearchTok, ns), 256, 0, st>>>(a, sh);
+      k_encode_mfma<D><<<dim3((sh.N + 63) / 64, ns), 256, 0, st>>>(a, sh);
+    }
+  } else {
+    k_mean_partial<F32><<<dim3(chunks, ns), 256, 0, st>>>(a, sh);
+    k_mean_final<F32><<<ns, 128, 0, st>>>(a, sh, chunks);
+    k_center_refs<F32><<<dim3((sh.R + 3) / 4, ns), 256, 0, st>>>(a, sh);
+    if (sh.N > 0) {
+      k_search_f32<D><<<dim3((sh.T + 255) / 256, ns), 256, 0, st>>>(a, sh);
+      k_encode_f32<D><<<dim3((sh.N + 255) / 256, ns), 256, 0, st>>>(a, sh);
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_compress(const Shape& sh, const CompressArgs& a, hipStream_t st) {
+  return sh.d == 128 ? launch_compress_d<128>(sh, a, st) : launch_compress_d<64>(sh, a, st);
+}
+
+}  // namespace dkv

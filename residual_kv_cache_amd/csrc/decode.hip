@@ -1,0 +1,319 @@
+// DeltaKV decode attention over the compressed cache, gfx950.
+//
+// Attention of one query per sequence over every cached token as if each
+// were reconstructed, k^_t = mu + ref + W_up code (DeltaKV explainer,
+// English page, Technical Summary §3 "Reconstruction": KV^ = f_d(z) + KV^R),
+// without materialising k^ or v^:
+//
+//   q . k^_t = q . mu_K + q . refs_K[ref(t)] + (W_up_K^T q) . code_K(t)
+//
+// The first term is the same for every token and cancels in the softmax, so
+// mu_K is never read.  With S[r][g] = scale * <q_g, refs_K[r]> (one pass over
+// the key references) and q'_g = scale * W_up_K^T q_g, a coded token scores
+// S[ref_K(t)][g] + <q'_g, code_K(t)>, and a reference token r scores
+// S[r][g].  On the value side
+//
+//   sum_t p_t v^_t = mu_V + sum_t p_t refs_V[ref_V(t)] + W_up_V sum_t p_t code_V(t)
+//
+// so each split keeps, per query head, an online-softmax state (max m, sum
+// l) and two accumulators: acc_r over value references (head dim) and acc_c
+// over value codes (code dim).  A final pass merges the splits and applies
+// mu_V and W_up_V once per query head.  All arithmetic is fp32; scores are
+// kept in base-2 units (scale * log2 e) so the exponentials are exp2.
+//
+// Kernels: refscore (S and q'), split (the token stream), combine.
+
+#include "dkv_device.h"
+#include "dkv_internal.h"
+
+namespace dkv {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <class S>
+__device__ __forceinline__ float ld(const void* p, size_t i) {
+  return S::load(((const typename S::T*)p)[i]);
+}
+
+// ---------------------------------------------------------------------------
+// refscore: S[b][h][r][g] for 64 references per block, and q'[b][h][g][:]
+// from the first block of each (b, h).  grid (ceil(R/64), B*H), block 256.
+// ---------------------------------------------------------------------------
+
+template <class S, int D>
+__global__ __launch_bounds__(256) void k_refscore(DecodeArgs a, Shape sh) {
+  __shared__ float qs[16][D];
+  __shared__ float rs[64][D + 1];
+  const int bh = blockIdx.y;
+  const int b = bh / sh.H, h = bh % sh.H;
+  const int G = a.G;
+  const float sc = a.scale * kLog2e;
+  for (int p = threadIdx.x; p < G * D; p += 256) {
+    const int g = p / D, i = p % D;
+    qs[g][i] = ld<S>(a.q, ((size_t)b * a.Hq + h * G + g) * D + i) * sc;
+  }
+  const int r0 = blockIdx.x * 64;
+  const size_t rbase = ((size_t)bh * 2 + 0) * sh.R;  // K references of (b, h)
+  for (int p = threadIdx.x; p < 64 * D; p += 256) {
+    const int row = p / D, i = p % D;
+    rs[row][i] = r0 + row < sh.R ? ld<S>(a.refs, (rbase + r0 + row) * D + i) : 0.f;
+  }
+  __syncthreads();
+  for (int p = threadIdx.x; p < 64 * G; p += 256) {
+    const int row = p / G, g = p % G;
+    if (r0 + row >= sh.R) continue;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int i = 0; i < D; ++i) acc = fmaf(qs[g][i], rs[row][i], acc);
+    a.score[((size_t)bh * sh.R + r0 + row) * G + g] = acc;
+  }
+  if (blockIdx.x == 0) {
+    const typename S::T* wu = (const typename S::T*)a.wuk + (size_t)h * a.w_hs;
+    for (int p = threadIdx.x; p < G * sh.dc; p += 256) {
+      const int g = p / sh.dc, j = p % sh.dc;
+      float acc = 0.f;
+      for (int i = 0; i < D; ++i) acc = fmaf(qs[g][i], S::load(wu[(size_t)i * sh.dc + j]), acc);
+      a.qp[((size_t)bh * G + g) * sh.dc + j] = acc;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// split: one block per (split, b, h); 4 waves take 64-token chunks in turn.
+// Coded rows [n0, n1) and reference tokens [r0, r1) of the split.
+// Score phase: lane = token.  Accumulate phase: the wave walks the chunk's
+// tokens; lanes own head-dim columns (acc_r) and code columns (acc_c).
+// ---------------------------------------------------------------------------
+
+template <class S, int D, int GP>
+__global__ __launch_bounds__(256) void k_split_valu(DecodeArgs a, Shape sh) {
+  constexpr int RPL = D / 64;            // head-dim columns per lane
+  __shared__ float qp_l[GP][D];
+  __shared__ float mw[4][GP];
+  __shared__ float merge[GP][2 * D + 1];   // acc_r | acc_c | l
+  const int sp = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int G = a.G, dc = sh.dc;
+  const int n0 = (int)((int64_t)sh.N * sp / a.splits), n1 = (int)((int64_t)sh.N * (sp + 1) / a.splits);
+  const int r0 = (int)((int64_t)sh.R * sp / a.splits), r1 = (int)((int64_t)sh.R * (sp + 1) / a.splits);
+
+  for (int p = threadIdx.x; p < G * dc; p += 256) qp_l[p / dc][p % dc] = a.qp[(size_t)bh * G * dc + p];
+  __syncthreads();
+
+  const size_t sK = (size_t)bh * 2, sV = sK + 1;             // stream ids
+  const float* score = a.score + (size_t)bh * sh.R * G;
+  const typename S::T* refsV = (const typename S::T*)a.refs + sV * sh.R * D;
+  const typename S::T* codesK = (const typename S::T*)a.codes + sK * sh.N * dc;
+  const typename S::T* codesV = (const typename S::T*)a.codes + sV * sh.N * dc;
+
+  float m[GP], lsum[GP], accr[GP][RPL], accc[GP][2];
+#pragma unroll
+  for (int g = 0; g < GP; ++g) {
+    m[g] = -INFINITY; lsum[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < RPL; ++e) accr[g][e] = 0.f;
+    accc[g][0] = accc[g][1] = 0.f;
+  }
+
+  const int nc_codes = (n1 - n0 + 63) / 64;
+  const int nc_refs = (r1 - r0 + 63) / 64;
+  for (int c = wave; c < nc_codes + nc_refs; c += 4) {
+    const bool coded = c < nc_codes;
+    const int base = coded ? n0 + c * 64 : r0 + (c - nc_codes) * 64;
+    const int end = coded ? n1 : r1;
+    const int cnt = min(64, end - base);
+    const int u = base + lane;
+    const bool valid = lane < cnt;
+    int rk = 0, rv = 0;
+    float sc[GP];
+    if (valid) {
+      if (coded) {
+        // Ordinals come from caller memory: clamp so a corrupt cache can never
+        // address outside the reference arrays.
+        rk = min((int)load_idx(a.idx, sK * sh.N + u, sh.idx_bytes), sh.R - 1);
+        rv = min((int)load_idx(a.idx, sV * sh.N + u, sh.idx_bytes), sh.R - 1);
+      } else {
+        rk = rv = u;
+      }
+#pragma unroll
+      for (int g = 0; g < GP; ++g) sc[g] = g < G ? score[(size_t)rk * G + g] : -INFINITY;
+      if (coded) {
+        for (int j = 0; j < dc; ++j) {
+          const float cj = S::load(codesK[(size_t)u * dc + j]);
+#pragma unroll
+          for (int g = 0; g < GP; ++g) sc[g] = fmaf(qp_l[g][j], cj, sc[g]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < GP; ++g) sc[g] = -INFINITY;
+    }
+    float p[GP];
+#pragma unroll
+    for (int g = 0; g < GP; ++g) {
+      if (g >= G) { p[g] = 0.f; continue; }
+      const float mn = fmaxf(m[g], wave_max(sc[g]));
+      const float alpha = exp2f(m[g] - mn);   // m = -inf on the first chunk -> 0
+      p[g] = exp2f(sc[g] - mn);
+      m[g] = mn;
+      lsum[g] = lsum[g] * alpha + p[g];
+#pragma unroll
+      for (int e = 0; e < RPL; ++e) accr[g][e] *= alpha;
+      accc[g][0] *= alpha;
+      accc[g][1] *= alpha;
+    }
+    for (int k = 0; k < cnt; ++k) {
+      const int r = __builtin_amdgcn_readlane(rv, k);
+      float xr[RPL];
+#pragma unroll
+      for (int e = 0; e < RPL; ++e) xr[e] = S::load(refsV[(size_t)r * D + lane * RPL + e]);
+      float c0 = 0.f, c1 = 0.f;
+      if (coded) {
+        const size_t row = (size_t)(base + k) * dc;
+        if (lane < dc) c0 = S::load(codesV[row + lane]);
+        if (lane + 64 < dc) c1 = S::load(codesV[row + lane + 64]);
+      }
+#pragma unroll
+      for (int g = 0; g < GP; ++g) {
+        if (g >= G) break;
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p[g]), k));
+#pragma unroll
+        for (int e = 0; e < RPL; ++e) accr[g][e] = fmaf(w, xr[e], accr[g][e]);
+        accc[g][0] = fmaf(w, c0, accc[g][0]);
+        accc[g][1] = fmaf(w, c1, accc[g][1]);
+      }
+    }
+  }
+
+  // Merge the four waves in a fixed order.
+#pragma unroll
+  for (int g = 0; g < GP; ++g) {
+    lsum[g] = wave_sum(lsum[g]);
+    if (lane == 0) mw[wave][g] = m[g];
+  }
+  __syncthreads();
+  float mb[GP], wgt[GP];
+#pragma unroll
+  for (int g = 0; g < GP; ++g) {
+    mb[g] = fmaxf(fmaxf(mw[0][g], mw[1][g]), fmaxf(mw[2][g], mw[3][g]));
+    wgt[g] = m[g] == -INFINITY ? 0.f : exp2f(m[g] - mb[g]);
+  }
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+      for (int g = 0; g < G; ++g) {
+#pragma unroll
+        for (int e = 0; e < RPL; ++e) {
+          const int i = lane * RPL + e;
+          const float v = accr[g][e] * wgt[g];
+          merge[g][i] = w == 0 ? v : merge[g][i] + v;
+        }
+        if (lane < dc) merge[g][D + lane] = (w == 0 ? 0.f : merge[g][D + lane]) + accc[g][0] * wgt[g];
+        if (lane + 64 < dc) merge[g][D + lane + 64] = (w == 0 ? 0.f : merge[g][D + lane + 64]) + accc[g][1] * wgt[g];
+        if (lane == 0) merge[g][2 * D] = (w == 0 ? 0.f : merge[g][2 * D]) + lsum[g] * wgt[g];
+      }
+    }
+    __syncthreads();
+  }
+  const int rec = partial_rec(sh);
+  float* out = a.part + ((size_t)bh * a.splits + sp) * G * rec;
+  for (int p = threadIdx.x; p < G * rec; p += 256) {
+    const int g = p / rec, f = p % rec;
+    float v = 0.f;
+    if (f == 0) {
+      v = fmaxf(fmaxf(mw[0][g], mw[1][g]), fmaxf(mw[2][g], mw[3][g]));
+    } else if (f == 1) {
+      v = merge[g][2 * D];
+    } else if (f < 2 + dc) {
+      v = merge[g][D + f - 2];
+    } else if (f < 2 + dc + D) {
+      v = merge[g][f - 2 - dc];
+    }
+    out[p] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// combine: one block per (b, query head); merges the splits, then
+// out = mu_V + (acc_r + W_up_V acc_c) / l.  grid B*Hq, block 128.
+// ---------------------------------------------------------------------------
+
+template <class S, int D>
+__global__ __launch_bounds__(128) void k_combine(DecodeArgs a, Shape sh) {
+  __shared__ float accc[128];
+  __shared__ float mx_s, l_s;
+  const int bq = blockIdx.x;
+  const int b = bq / a.Hq, gq = bq % a.Hq;
+  const int h = gq / a.G, g = gq % a.G;
+  const int bh = b * sh.H + h;
+  const int rec = partial_rec(sh);
+  const int dc = sh.dc;
+  const float* part = a.part + (size_t)bh * a.splits * a.G * rec + (size_t)g * rec;
+  const size_t pstride = (size_t)a.G * rec;
+  if (threadIdx.x == 0) {
+    float mx = -INFINITY;
+    for (int s = 0; s < a.splits; ++s) mx = fmaxf(mx, part[s * pstride]);
+    float l = 0.f;
+    for (int s = 0; s < a.splits; ++s) {
+      const float ms = part[s * pstride];
+      if (ms != -INFINITY) l += exp2f(ms - mx) * part[s * pstride + 1];
+    }
+    mx_s = mx;
+    l_s = l;
+  }
+  __syncthreads();
+  const float mx = mx_s, inv_l = 1.0f / l_s;
+  const int i = threadIdx.x;
+  if (i < dc) {
+    float c = 0.f;
+    for (int s = 0; s < a.splits; ++s) {
+      const float ms = part[s * pstride];
+      if (ms != -INFINITY) c = fmaf(exp2f(ms - mx), part[s * pstride + 2 + i], c);
+    }
+    accc[i] = c;
+  }
+  __syncthreads();
+  if (i < D) {
+    float r = 0.f;
+    for (int s = 0; s < a.splits; ++s) {
+      const float ms = part[s * pstride];
+      if (ms != -INFINITY) r = fmaf(exp2f(ms - mx), part[s * pstride + 2 + dc + i], r);
+    }
+    const typename S::T* wu = (const typename S::T*)a.wuv + (size_t)h * a.w_hs;
+    float u = 0.f;
+    for (int j = 0; j < dc; ++j) u = fmaf(S::load(wu[(size_t)i * dc + j]), accc[j], u);
+    const float muv = ld<S>(a.mu, ((size_t)bh * 2 + 1) * D + i);
+    a.out[((size_t)b * a.Hq + gq) * D + i] = muv + (r + u) * inv_l;
+  }
+}
+
+template <class S, int D, int GP>
+hipError_t launch_split(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
+  k_split_valu<S, D, GP><<<dim3(a.splits, sh.B * sh.H), 256, 0, st>>>(a, sh);
+  return hipGetLastError();
+}
+
+template <class S, int D>
+hipError_t launch_decode_sd(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
+  k_refscore<S, D><<<dim3((sh.R + 63) / 64, sh.B * sh.H), 256, 0, st>>>(a, sh);
+  hipError_t e;
+  if (a.G <= 1) e = launch_split<S, D, 1>(sh, a, st);
+  else if (a.G <= 2) e = launch_split<S, D, 2>(sh, a, st);
+  else if (a.G <= 4) e = launch_split<S, D, 4>(sh, a, st);
+  else if (a.G <= 8) e = launch_split<S, D, 8>(sh, a, st);
+  else e = launch_split<S, D, 16>(sh, a, st);
+  if (e != hipSuccess) return e;
+  k_combine<S, D><<<sh.B * a.Hq, 128, 0, st>>>(a, sh);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
+  if (sh.bf16) return sh.d == 128 ? launch_decode_sd<BF16, 128>(sh, a, st) : launch_decode_sd<BF16, 64>(sh, a, st);
+  return sh.d == 128 ? launch_decode_sd<F32, 128>(sh, a, st) : launch_decode_sd<F32, 64>(sh, a, st);
+}
+
+}  // namespace dkv

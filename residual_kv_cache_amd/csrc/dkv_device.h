@@ -1,0 +1,110 @@
+// Device-side helpers of the DeltaKV kernels: storage conversions with
+// exact rounding, MFMA operand types and small wave reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dkv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// bfloat16 <-> float32.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float32 -> bfloat16, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Moves a float32 that was rounded to nearest from an exact value x = a + err
+// (|err| <= half an ulp of a) to x rounded to odd: if the rounding was
+// inexact and a's last significand bit is 0, step one ulp towards x.  A value
+// rounded to odd at 24 bits and then to nearest-even at 8 bits equals x
+// rounded to nearest-even at 8 bits directly (no double-rounding error).
+__device__ __forceinline__ float to_odd(float a, float err) {
+  uint32_t u = __float_as_uint(a);
+  if (err != 0.0f && (u & 1u) == 0u) {
+    // step away from zero when err has a's sign, towards zero otherwise
+    bool away = (err > 0.0f) == (a > 0.0f);
+    u = away ? u + 1u : u - 1u;
+  }
+  return __uint_as_float(u);
+}
+
+// Correctly rounded bfloat16(x - y) for bfloat16-valued x and y.  The
+// float32 difference and its exact error come from the TwoSum
+// transformation; rounding to odd then to bf16 gives the correct result
+// even where the float32 subtraction itself is inexact.
+__device__ __forceinline__ uint16_t bf16_sub_rn(float x, float y) {
+  float a = x - y;
+  float bv = a - x;
+  float av = a - bv;
+  float err = (x - av) + (-y - bv);
+  return f2bf(to_odd(a, err));
+}
+
+// Correctly rounded bfloat16 of a double.
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+  float a = (float)x;
+  double e = x - (double)a;  // exact: a is x rounded to the nearest float
+  return f2bf(to_odd(a, e > 0.0 ? 1.0f : (e < 0.0 ? -1.0f : 0.0f)));
+}
+
+// Storage types: raw bfloat16 bits or float.
+struct BF16 {
+  typedef uint16_t T;
+  static __device__ __forceinline__ float load(T v) { return bf2f(v); }
+  static __device__ __forceinline__ T from_f32(float f) { return f2bf(f); }
+  static __device__ __forceinline__ T from_f64(double x) { return f64_to_bf16(x); }
+  static __device__ __forceinline__ T sub_rn(float x, float y) { return bf16_sub_rn(x, y); }
+};
+
+struct F32 {
+  typedef float T;
+  static __device__ __forceinline__ float load(T v) { return v; }
+  static __device__ __forceinline__ T from_f32(float f) { return f; }
+  static __device__ __forceinline__ T from_f64(double x) { return (float)x; }
+  static __device__ __forceinline__ T sub_rn(float x, float y) { return x - y; }
+};
+
+// ---------------------------------------------------------------------------
+// Wave64 reductions (butterfly; every lane ends with the result).
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Position of coded row n (non-reference tokens in position order), s >= 2.
+__device__ __forceinline__ int slot_to_pos(int n, int s) { return (n / (s - 1)) * s + (n % (s - 1)) + 1; }
+
+// Coded row of a non-reference position t.
+__device__ __forceinline__ int pos_to_slot(int t, int s) { return t - t / s - 1; }
+
+__device__ __forceinline__ uint32_t load_idx(const void* idx, size_t i, int idx_bytes) {
+  return idx_bytes == 2 ? (uint32_t)((const uint16_t*)idx)[i] : ((const uint32_t*)idx)[i];
+}
+
+__device__ __forceinline__ void store_idx(void* idx, size_t i, int idx_bytes, uint32_t r) {
+  if (idx_bytes == 2)
+    ((uint16_t*)idx)[i] = (uint16_t)r;
+  else
+    ((uint32_t*)idx)[i] = r;
+}
+
+}  // namespace dkv

@@ -1,0 +1,95 @@
+// Internal declarations shared by the host entry points and the kernels of
+// the DeltaKV library.  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/deltakv.h"
+
+namespace dkv {
+
+// Sizes derived from a validated dkv_layout.
+struct Shape {
+  int d;        // head dim
+  int dc;       // code dim
+  int s;        // reference stride
+  int R;        // references per stream, ceil(T / s)
+  int N;        // coded tokens per stream, T - R
+  int T;        // tokens per stream
+  int H;        // KV heads
+  int B;        // sequences
+  int idx_bytes;
+  int bf16;     // 1 = bfloat16 storage, 0 = float32
+  __host__ __device__ int n_streams() const { return B * H * 2; }
+  int elem() const { return bf16 ? 2 : 4; }
+};
+
+// Tokens summed per block in the first mean stage.
+constexpr int kMeanChunk = 512;
+
+inline int mean_chunks(const Shape& sh) { return (sh.T + kMeanChunk - 1) / kMeanChunk; }
+
+// Compress workspace: fp64 mean partials, then fp32 inverse reference norms.
+inline size_t ws_mean_off(const Shape&) { return 0; }
+inline size_t ws_mean_bytes(const Shape& sh) {
+  return (size_t)sh.n_streams() * mean_chunks(sh) * sh.d * sizeof(double);
+}
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline size_t ws_invn_off(const Shape& sh) { return align_up(ws_mean_bytes(sh), 256); }
+inline size_t ws_invn_bytes(const Shape& sh) { return (size_t)sh.n_streams() * sh.R * sizeof(float); }
+inline size_t compress_ws_bytes(const Shape& sh) { return align_up(ws_invn_off(sh) + ws_invn_bytes(sh), 256); }
+
+// Decode workspace: reference scores S [B][H][R][G], projected queries
+// q' [B][Hq][dc] and split partials [B][H][splits][G][rec].
+__host__ __device__ inline int partial_rec(const Shape& sh) { return (2 + sh.dc + sh.d + 3) / 4 * 4; }
+inline size_t ws_score_bytes(const Shape& sh, int G) { return (size_t)sh.B * sh.H * sh.R * G * sizeof(float); }
+inline size_t ws_qp_off(const Shape& sh, int G) { return align_up(ws_score_bytes(sh, G), 256); }
+inline size_t ws_qp_bytes(const Shape& sh, int G) { return (size_t)sh.B * sh.H * G * sh.dc * sizeof(float); }
+inline size_t ws_part_off(const Shape& sh, int G) { return align_up(ws_qp_off(sh, G) + ws_qp_bytes(sh, G), 256); }
+inline size_t ws_part_bytes(const Shape& sh, int G, int splits) {
+  return (size_t)sh.B * sh.H * splits * G * partial_rec(sh) * sizeof(float);
+}
+inline size_t decode_ws_bytes(const Shape& sh, int G, int splits) {
+  return align_up(ws_part_off(sh, G) + ws_part_bytes(sh, G, splits), 256);
+}
+
+struct CompressArgs {
+  const void* k;
+  const void* v;
+  int64_t sb, sh, st;        // element strides of k and v
+  const void* wdk;
+  const void* wdv;
+  int64_t w_hs;              // head stride of W_down (elements), 0 = shared
+  const void* mu_in;
+  void* refs;
+  void* codes;
+  void* idx;
+  void* mu;
+  double* mean_part;
+  float* inv_n;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* wuk;
+  const void* wuv;
+  int64_t w_hs;
+  int G;                     // query heads per KV head
+  int Hq;
+  int splits;
+  float scale;
+  float* out;
+  const void* refs;
+  const void* codes;
+  const void* idx;
+  const void* mu;
+  float* score;              // [B][H][R][G]
+  float* qp;                 // [B][H][G][dc]
+  float* part;               // [B][H][splits][G][rec]
+};
+
+hipError_t launch_compress(const Shape& sh, const CompressArgs& a, hipStream_t st);
+hipError_t launch_decode(const Shape& sh, const DecodeArgs& a, hipStream_t st);
+
+}  // namespace dkv

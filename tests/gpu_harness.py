@@ -1,0 +1,168 @@
+"""Shared helpers of the GPU parity tests: move seeded inputs to the device,
+run the library through its C ABI, bring results back, and compare them
+with the oracle under the stated tolerances.
+
+Tolerances (derived in the design notes):
+  * mean, references, cache layout: bit-exact;
+  * reference ordinals: exact wherever the oracle's top-1/top-2 cosine margin
+    exceeds 1e-4; inside that margin any earlier reference whose cosine is
+    within 1e-4 of the best is accepted;
+  * codes: compared with the oracle re-encoding the same tokens against the
+    GPU's references; |c_gpu - c| <= ulp(c) + 2 (d + 2) 2^-24 sum_i |W_ji delta_i|
+    (one storage rounding plus an fp32 dot-product error bound);
+  * attention output: max-abs 1e-4 for float32 storage, 2e-2 for bfloat16.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import kvsynth as K
+import oracle as O
+import residual_kv_cache_amd as D
+
+MARGIN = 1e-4
+OUT_TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(raw: np.ndarray) -> torch.Tensor:
+    """Storage array (np.float32, or np.uint16 bf16 bits) -> device tensor."""
+    if raw.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(raw, dtype=np.float32)).cuda()
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def layout_of(cfg: K.Config) -> D.dkv_layout:
+    return D.make_layout(cfg.dtype, cfg.head_dim, cfg.code_dim, cfg.stride, cfg.n_kv_heads, cfg.batch, cfg.seq_len)
+
+
+class Inputs:
+    """One layer of seeded inputs: K, V [B][H][T][d] and the four matrices."""
+
+    def __init__(self, cfg: K.Config, layer: int = 0):
+        self.cfg = cfg
+        self.layer = layer
+        kv = K.gen_layer(cfg, layer)
+        self.k_raw, self.v_raw = kv["k"], kv["v"]
+        self.k, self.v = kv["k_f64"], kv["v_f64"]
+        (self.wuk, self.wdk), (self.wuv, self.wdv) = K.gen_w(cfg, layer, 0), K.gen_w(cfg, layer, 1)
+
+    def q(self, step: int) -> K.Stored:
+        qs = [K.gen_q(self.cfg, self.layer, b, step) for b in range(self.cfg.batch)]
+        return K.Stored(np.stack([x.raw for x in qs]), np.stack([x.f64 for x in qs]), self.cfg.dtype)
+
+
+def gpu_compress(cfg: K.Config, inp: Inputs, k_dev=None, v_dev=None, mu_in=None):
+    lay = layout_of(cfg)
+    cache = D.Cache(lay)
+    ws = D.workspace(D.dkv_compress_workspace_bytes(lay))
+    k = dev(inp.k_raw) if k_dev is None else k_dev
+    v = dev(inp.v_raw) if v_dev is None else v_dev
+    D.deltakv_compress(lay, k, v, dev(inp.wdk.raw), dev(inp.wdv.raw), cache, ws, mu_in=mu_in)
+    torch.cuda.synchronize()
+    return lay, cache
+
+
+def cache_numpy(cache: D.Cache) -> dict:
+    a = cache.arrays()
+    idx = a["idx"].cpu().numpy()
+    idx = idx.view(np.uint16) if idx.dtype == np.int16 else idx.view(np.uint32)
+    return {"refs": f64(a["refs"]), "codes": f64(a["codes"]), "mu": f64(a["mu"]),
+            "idx": idx.astype(np.int64)}
+
+
+def gpu_decode(lay, cache, q_raw, inp: Inputs, n_splits=0, scale=0.0) -> np.ndarray:
+    B, Hq, d = q_raw.shape
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    ws = D.workspace(D.dkv_decode_workspace_bytes(lay, Hq, n_splits))
+    D.deltakv_decode_attn(lay, cache, dev(q_raw), dev(inp.wuk.raw), dev(inp.wuv.raw), out, ws,
+                          n_splits=n_splits, softmax_scale=scale)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def ulp(c: np.ndarray, storage: str) -> np.ndarray:
+    if storage == "f32":
+        return np.spacing(np.abs(c).astype(np.float32)).astype(np.float64)
+    _, e = np.frexp(c)
+    return np.ldexp(1.0, np.maximum(e, -125) - 8)
+
+
+def check_stream(x: np.ndarray, s: int, w_down: np.ndarray, storage: str, g: dict, toks=None) -> dict:
+    """Compare one GPU stream (g: mu [d], refs [R][d], idx [N], codes [N][dc])
+    with the oracle on stream tokens x [T][d].  ``toks`` restricts the
+    search/code comparison to a sample of non-reference positions."""
+    T, d = x.shape
+    mu = O.shared_component(x, storage)
+    assert np.array_equal(g["mu"], mu), "shared component differs"
+    xt = O.center(x, mu, storage)
+    refs = xt[O.ref_positions(T, s)]
+    assert np.array_equal(g["refs"], refs), "references differ"
+    all_toks = O.nonref_positions(T, s)
+    if toks is None:
+        toks = all_toks
+        rows = np.arange(len(all_toks))
+    else:
+        toks = np.asarray(toks, np.int64)
+        rows = toks - toks // s - 1
+    if len(toks) == 0:
+        return {"tokens": 0, "exempt": 0, "max_code_err_over_tol": 0.0}
+    idx_o, top1, margin = O.search(xt, s, toks=toks)
+    idx_g = g["idx"][rows]
+    assert np.all(idx_g * s < toks), "a chosen reference is not earlier than its token"
+    diff = idx_g != idx_o
+    if diff.any():
+        assert np.all(margin[diff] <= MARGIN), (
+            f"{int((diff & (margin > MARGIN)).sum())} ordinals differ outside the {MARGIN} margin")
+        cg = O.cosines(xt, toks[diff], idx_g[diff], s)
+        assert np.all(cg >= top1[diff] - MARGIN), "an accepted ordinal is not within the margin of the best"
+    codes_o = O.encode(x, mu, xt, s, idx_g, w_down, storage, toks=toks)
+    delta = (x[toks] - mu) - xt[idx_g * s]
+    mag = np.abs(delta) @ np.abs(w_down).T
+    tol = ulp(codes_o, storage) + 2 * (d + 2) * 2.0 ** -24 * mag
+    err = np.abs(g["codes"][rows] - codes_o)
+    assert np.all(err <= tol), f"codes differ beyond bound: worst {float((err / tol).max()):.3g}x"
+    return {"tokens": len(toks), "exempt": int(diff.sum()), "max_code_err_over_tol": float((err / tol).max())}
+
+
+def check_layer_compress(inp: Inputs, gc: dict, heads=None, seqs=None, toks=None) -> dict:
+    cfg = inp.cfg
+    heads = range(cfg.n_kv_heads) if heads is None else heads
+    seqs = range(cfg.batch) if seqs is None else seqs
+    tot = {"tokens": 0, "exempt": 0, "worst_code": 0.0}
+    for b in seqs:
+        for h in heads:
+            for kv, x, w in ((0, inp.k, inp.wdk), (1, inp.v, inp.wdv)):
+                st = check_stream(x[b, h], cfg.stride, w.f64, cfg.dtype,
+                                  {n: gc[n][b, h, kv] for n in ("mu", "refs", "idx", "codes")}, toks=toks)
+                tot["tokens"] += st["tokens"]
+                tot["exempt"] += st["exempt"]
+                tot["worst_code"] = max(tot["worst_code"], st["max_code_err_over_tol"])
+    return tot
+
+
+def oracle_decode_on(gc: dict, q: np.ndarray, inp: Inputs, scale=None, seqs=None) -> np.ndarray:
+    """Oracle decode over the GPU's cache bytes (literal reconstruction)."""
+    cfg = inp.cfg
+    seqs = range(cfg.batch) if seqs is None else seqs
+    outs = []
+    for b in seqs:
+        sub = {n: gc[n][b:b + 1] for n in ("mu", "refs", "idx", "codes")}
+        outs.append(O.decode(sub, q[b:b + 1], inp.wuk.f64, inp.wuv.f64, cfg.stride, cfg.seq_len, scale=scale)[0])
+    return np.stack(outs)
+
+
+def default_scale(cfg):
+    return 1.0 / math.sqrt(cfg.head_dim)

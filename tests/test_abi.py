@@ -1,0 +1,208 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol,
+computes sizes, and rejects bad arguments before touching a device (these
+calls never reach a HIP launch, so no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import kvsynth as K
+import oracle as O
+import residual_kv_cache_amd as D
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    if not os.path.exists(D.LIB_PATH):
+        pytest.skip("libdeltakv.so not built")
+    return D.lib()
+
+
+def test_header_declarations_are_exported():
+    lib = _lib()
+    with open(os.path.join(ROOT, "include", "deltakv.h")) as f:
+        text = f.read()
+    declared = set(re.findall(r"^(?:const\s+)?\w+\s*\**\s*(dkv_\w+|deltakv_\w+)\(", text, re.M))
+    assert declared == set(D.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings():
+    lib = _lib()
+    assert lib.dkv_abi_version() == 1
+    for code, name in D.STATUS.items():
+        assert lib.dkv_status_str(code).decode().startswith(name)
+
+
+def L(**kw):
+    base = dict(dtype="bf16", head_dim=128, code_dim=32, stride=16, n_kv_heads=8, batch=1, seq_len=32768)
+    base.update(kw)
+    return D.make_layout(**base)
+
+
+@pytest.mark.parametrize("name", list(K.CONFIGS))
+def test_cache_bytes_match_oracle_layout(name):
+    _lib()
+    c = K.CONFIGS[name]
+    lay = D.make_layout(c.dtype, c.head_dim, c.code_dim, c.stride, c.n_kv_heads, c.batch, c.seq_len)
+    assert D.dkv_cache_bytes(lay) == O.cache_bytes(c.batch, c.n_kv_heads, c.seq_len, c.stride, c.head_dim,
+                                                   c.code_dim, c.dtype)
+
+
+@pytest.mark.parametrize("T,s", [(1, 1), (1, 16), (15, 16), (17, 16), (1000, 7), (4096, 1)])
+def test_cache_bytes_ragged(T, s):
+    _lib()
+    lay = L(seq_len=T, stride=s, n_kv_heads=3, batch=2)
+    assert D.dkv_cache_bytes(lay) == O.cache_bytes(2, 3, T, s, 128, 32, "bf16")
+
+
+def test_carve_offsets():
+    _lib()
+    lay = L(seq_len=1000, stride=7)
+    base = 1 << 20
+    c = D.dkv_cache_carve(lay, base)
+    sizes = O.cache_array_bytes(1, 8, 1000, 7, 128, 32, "bf16")
+    pad = lambda x: -(-x // 256) * 256
+    assert c.refs == base
+    assert c.codes == base + pad(sizes["refs"])
+    assert c.idx == c.codes + pad(sizes["codes"])
+    assert c.mu == c.idx + pad(sizes["idx"])
+    assert c.mu + pad(sizes["mu"]) == base + D.dkv_cache_bytes(lay)
+    with pytest.raises(D.DeltaKVError):
+        D.dkv_cache_carve(lay, base + 16)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), 6), (dict(code_dim=24), 6), (dict(code_dim=256), 2), (dict(stride=0), 2),
+    (dict(seq_len=0), 2), (dict(n_kv_heads=0), 2), (dict(batch=0), 2), (dict(idx_bytes=3), 2),
+    (dict(seq_len=65537 * 2, stride=2, idx_bytes=2), 6), (dict(dtype="f32"), 0),
+])
+def test_layout_check(kw, code):
+    _lib()
+    assert D.dkv_layout_check(L(**kw)) == code
+
+
+def test_layout_version_and_dtype():
+    _lib()
+    lay = L()
+    lay.abi_version = 2
+    assert D.dkv_layout_check(lay) == 7
+    lay = L()
+    lay.dtype = 9
+    assert D.dkv_layout_check(lay) == 3
+    lay = L()
+    lay.reserved = 1
+    assert D.dkv_layout_check(lay) == 2
+    assert D.lib().dkv_layout_check(None) == 1
+
+
+def test_idx_width_switch():
+    _lib()
+    assert D.make_layout("bf16", 128, 32, 2, 1, 1, 131072).idx_bytes == 2
+    lay = D.make_layout("bf16", 128, 32, 1, 1, 1, 65537)
+    assert lay.idx_bytes == 4 and D.dkv_layout_check(lay) == 0
+
+
+def test_workspace_sizes():
+    _lib()
+    lay = L()
+    assert D.dkv_compress_workspace_bytes(lay) > 0
+    n = D.dkv_decode_workspace_bytes(lay, 32, 0)
+    assert n > 0
+    assert D.dkv_decode_workspace_bytes(lay, 30, 0) == 0     # Hq not a multiple of H
+    assert D.dkv_decode_workspace_bytes(lay, 8 * 17, 0) == 0  # G > 16
+    assert D.dkv_decode_workspace_bytes(lay, 32, 2000) == 0
+    s = D.dkv_decode_auto_splits(lay, 32)
+    assert 1 <= s <= 1024
+    assert D.dkv_decode_workspace_bytes(lay, 32, s) == n
+
+
+def _no_device():
+    """Calls below pass made-up device addresses that validation must reject.
+    They run only where no GPU is visible, so a validation bug can never turn
+    into a launch on real memory."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("made-up pointers are only passed where no GPU is visible")
+
+
+class FakeCache:
+    def __init__(self, ptr):
+        self.c = D.dkv_cache(ptr, ptr + 4096, ptr + 8192, ptr + 12288)
+
+
+def _compress_status(lay, k, v, wd, ws, cache, ws_bytes=None):
+    a = D.dkv_compress_in(k, v, 8 * 32768 * 128, 32768 * 128, 128, wd, wd, 0, None)
+    return D.lib().deltakv_compress(ctypes.byref(lay), ctypes.byref(a), ctypes.byref(cache.c),
+                                    ctypes.c_void_p(ws), ws_bytes if ws_bytes is not None else 1 << 30, None)
+
+
+def test_compress_rejects_before_launch():
+    _lib()
+    _no_device()
+    lay = L()
+    P = 1 << 30
+    cache = FakeCache(P)
+    need = D.dkv_compress_workspace_bytes(lay)
+    assert _compress_status(lay, None, P, P, P, cache) == 1
+    assert _compress_status(lay, P, P, None, P, cache) == 1
+    assert _compress_status(lay, P + 2, P, P, P, cache) == 4
+    assert _compress_status(lay, P, P, P, None, cache) == 5
+    assert _compress_status(lay, P, P, P, P, cache, ws_bytes=need - 1) == 5
+    bad = FakeCache(P)
+    bad.c.refs = None
+    assert _compress_status(lay, P, P, P, P, bad) == 1
+    bad = FakeCache(P)
+    bad.c.codes = P + 4
+    assert _compress_status(lay, P, P, P, P, bad) == 4
+    a = D.dkv_compress_in(P, P, 0, 0, 132, P, P, 0, None)  # stride_t not a multiple of 8
+    assert D.lib().deltakv_compress(ctypes.byref(lay), ctypes.byref(a), ctypes.byref(cache.c), P, 1 << 30,
+                                    None) == 4
+    a = D.dkv_compress_in(P, P, 0, 0, 64, P, P, 0, None)   # stride_t < head_dim
+    assert D.lib().deltakv_compress(ctypes.byref(lay), ctypes.byref(a), ctypes.byref(cache.c), P, 1 << 30,
+                                    None) == 2
+    a = D.dkv_compress_in(P, P, 0, 0, 128, P, P, 8, None)  # head stride smaller than one matrix
+    assert D.lib().deltakv_compress(ctypes.byref(lay), ctypes.byref(a), ctypes.byref(cache.c), P, 1 << 30,
+                                    None) == 2
+    assert D.lib().deltakv_compress(ctypes.byref(lay), None, ctypes.byref(cache.c), P, 1 << 30, None) == 1
+    lay2 = L(head_dim=96)
+    assert _compress_status(lay2, P, P, P, P, cache) == 6
+
+
+def _decode_status(lay, q, wu, out, ws, cache, hq=32, splits=0, scale=0.0, ws_bytes=None, reserved=0):
+    a = D.dkv_decode_in(q, wu, wu, 0, hq, splits, scale, reserved, out)
+    return D.lib().deltakv_decode_attn(ctypes.byref(lay), ctypes.byref(cache.c), ctypes.byref(a),
+                                       ctypes.c_void_p(ws), ws_bytes if ws_bytes is not None else 1 << 30, None)
+
+
+def test_decode_rejects_before_launch():
+    _lib()
+    _no_device()
+    lay = L()
+    P = 1 << 30
+    cache = FakeCache(P)
+    need = D.dkv_decode_workspace_bytes(lay, 32, 0)
+    assert _decode_status(lay, None, P, P, P, cache) == 1
+    assert _decode_status(lay, P, P, None, P, cache) == 1
+    assert _decode_status(lay, P + 8, P, P, P, cache) == 4
+    assert _decode_status(lay, P, P, P, P, cache, hq=30) == 2
+    assert _decode_status(lay, P, P, P, P, cache, hq=8 * 32) == 6
+    assert _decode_status(lay, P, P, P, P, cache, splits=4096) == 6
+    assert _decode_status(lay, P, P, P, P, cache, scale=-1.0) == 2
+    assert _decode_status(lay, P, P, P, P, cache, scale=float("nan")) == 2
+    assert _decode_status(lay, P, P, P, P, cache, reserved=1) == 2
+    assert _decode_status(lay, P, P, P, None, cache) == 5
+    assert _decode_status(lay, P, P, P, P, cache, ws_bytes=need - 1) == 5
+    bad = FakeCache(P)
+    bad.c.mu = None
+    assert _decode_status(lay, P, P, P, P, bad) == 1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(D, "_lib_handle", None)
+    monkeypatch.setattr(D, "LIB_PATH", "/nonexistent/libdeltakv.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        D.lib()
