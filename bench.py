@@ -1,0 +1,341 @@
+#!/usr/bin/env python3
+"""DeltaKV hot-path benchmark on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input: compress a
+full prefill (K and V of every KV head) into the compressed cache, then run
+256 decode-attention steps over it.  Default workload: Llama-3-8B-shaped
+single layer, batch 1, 8 KV / 32 query heads, head dim 128, 32768 prefill
+tokens, bf16 storage, stride 16, code dim 32.
+
+Inputs (K, V, W, the 256 queries) are resident in HBM before timing.  Each
+step is one HIP graph: compress into cache replica 0, then decode step i over
+replica i mod R (R replicas of the cache, together larger than the 256 MB
+Infinity Cache, so decode reads come from HBM as they would across the
+layers of a model).  Stage events recorded inside the graph time every
+kernel of the last timed step.
+
+Prints one JSON line.  `value` is decode-attention throughput in GB/s over
+the decode window of a step (effective bytes: every cache array, V's mean,
+both W_up, the queries and the fp32 outputs, each counted once per decode
+step).  The oracle (fp64, CPU) is timed on a bounded sample afterwards as a
+baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "compressed-KV decode attn GB/s & tokens/s vs HBM roofline; compress tok/s"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2516.6
+DECODE_STEPS = 256
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """The few HIP runtime calls the benchmark needs (events, graphs)."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipGraphLaunch.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipStreamBeginCapture.argtypes = [ctypes.c_void_p, ctypes.c_int]
+        self.h.hipStreamEndCapture.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipGraphInstantiate.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_void_p,
+                                               ctypes.c_char_p, ctypes.c_size_t]
+        self.h.hipStreamSynchronize.argtypes = [ctypes.c_void_p]
+
+    def ok(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed: hipError {rc}")
+
+    def events(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            self.ok(self.h.hipEventCreate(ctypes.byref(ev)), "hipEventCreate")
+            arr[i] = ev.value
+        return arr
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        self.ok(self.h.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)),
+                "hipEventElapsedTime")
+        return ms.value
+
+    def begin_capture(self, stream):
+        self.ok(self.h.hipStreamBeginCapture(ctypes.c_void_p(stream), 2), "hipStreamBeginCapture")  # relaxed
+
+    def end_capture(self, stream):
+        g = ctypes.c_void_p()
+        self.ok(self.h.hipStreamEndCapture(ctypes.c_void_p(stream), ctypes.byref(g)), "hipStreamEndCapture")
+        ex = ctypes.c_void_p()
+        self.ok(self.h.hipGraphInstantiate(ctypes.byref(ex), g, None, None, 0), "hipGraphInstantiate")
+        return g, ex
+
+    def launch(self, ex, stream):
+        self.ok(self.h.hipGraphLaunch(ex, ctypes.c_void_p(stream)), "hipGraphLaunch")
+
+    def sync(self, stream):
+        self.ok(self.h.hipStreamSynchronize(ctypes.c_void_p(stream)), "hipStreamSynchronize")
+
+
+def effective_decode_bytes(cfg) -> int:
+    """Bytes one decode step must move once: references, codes and ordinals of
+    K and V, V's mean, W_up of K and V, the queries and the fp32 outputs."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    R = -(-cfg.seq_len // cfg.stride)
+    N = cfg.seq_len - R
+    ib = 2 if R <= 65536 else 4
+    n = cfg.batch * cfg.n_kv_heads * 2
+    cache = n * (R * cfg.head_dim * e + N * (cfg.code_dim * e + ib))
+    mu_v = cfg.batch * cfg.n_kv_heads * cfg.head_dim * e
+    w = 2 * cfg.head_dim * cfg.code_dim * e
+    q_out = cfg.batch * cfg.n_q_heads * cfg.head_dim * (e + 4)
+    return cache + mu_v + w + q_out
+
+
+def split_kernel_bytes_per_head(cfg, splits: int) -> int:
+    """Algorithmic bytes of the split kernel per (sequence, KV head): K and V
+    codes and ordinals, V references, the reference scores and projected
+    queries it reads, and the split partials it writes."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    R = -(-cfg.seq_len // cfg.stride)
+    N = cfg.seq_len - R
+    ib = 2 if R <= 65536 else 4
+    G = cfg.group
+    rec = (2 + cfg.code_dim + cfg.head_dim + 3) // 4 * 4
+    return (2 * N * (cfg.code_dim * e + ib) + R * cfg.head_dim * e + R * G * 4 + G * cfg.code_dim * 4
+            + splits * G * rec * 4)
+
+
+def search_flops_per_stream(cfg) -> int:
+    """2 d flops per (token, earlier reference) pair over non-reference tokens."""
+    s, T = cfg.stride, cfg.seq_len
+    pairs = 0
+    for t in range(T):
+        if t % s:
+            pairs += -(-t // s)
+    return 2 * cfg.head_dim * pairs
+
+
+def cpu_baseline(cfg, budget_s: float = 20.0) -> dict:
+    """Time the fp64 oracle on the host: compress of whole K and V streams of
+    the first KV heads, and decode steps over the full layer cache it would
+    produce, scaled to the GPU metric's units."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import kvsynth as K
+    import oracle as O
+
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    wu = [K.gen_w(cfg, 0, kv) for kv in (0, 1)]
+    t_comp, heads = 0.0, 0
+    caches = []
+    t_start = time.perf_counter()
+    for h in range(cfg.n_kv_heads):
+        k = K.gen_stream(cfg, 0, 0, h, 0).f64
+        v = K.gen_stream(cfg, 0, 0, h, 1).f64
+        t0 = time.perf_counter()
+        ck = O.compress_stream(k, cfg.stride, wu[0][1].f64, cfg.dtype)
+        cv = O.compress_stream(v, cfg.stride, wu[1][1].f64, cfg.dtype)
+        t_comp += time.perf_counter() - t0
+        heads += 1
+        caches.append((ck, cv))
+        if time.perf_counter() - t_start > budget_s * 0.5:
+            break
+    comp_tok_s = cfg.seq_len * heads / (t_comp * cfg.n_kv_heads)
+    # Decode: the whole layer needs all KV heads; reuse the compressed heads
+    # cyclically (the oracle's decode work does not depend on the values).
+    cache = {n: np.stack([[np.stack([caches[h % heads][0][n], caches[h % heads][1][n]])
+                           for h in range(cfg.n_kv_heads)]]) for n in ("mu", "refs", "idx", "codes")}
+    steps, t_dec = 0, 0.0
+    while steps < 1 or (t_dec < budget_s * 0.4 and steps < 8):
+        q = K.gen_q(cfg, 0, 0, steps).f64[None]
+        t0 = time.perf_counter()
+        O.decode(cache, q, wu[0][0].f64, wu[1][0].f64, cfg.stride, cfg.seq_len)
+        t_dec += time.perf_counter() - t0
+        steps += 1
+    per_step = t_dec / steps
+    return {
+        "value": effective_decode_bytes(cfg) / per_step / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle: compress of {heads} of {cfg.n_kv_heads} KV heads (K and V, "
+                   f"{cfg.seq_len} tokens each), scaled x{cfg.n_kv_heads / heads:g}; {steps} decode steps by "
+                   f"literal reconstruction over the full layer cache"),
+        "decode_ms_per_step": per_step * 1e3,
+        "decode_tokens_per_s": cfg.batch / per_step,
+        "compress_tokens_per_s": comp_tok_s,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="llama8b_32k")
+    ap.add_argument("--splits", type=int, default=0, help="decode splits per head (0 = library default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the DeltaKV hot path here is a single-GPU build "
+              "(every (sequence, head) stream is independent; see the sharding notes). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import kvsynth as K
+    import residual_kv_cache_amd as D
+
+    cfg = K.CONFIGS[args.config]
+    if cfg.decode_steps == 0:
+        raise SystemExit(f"{cfg.name} has no decode steps; pick a decode workload")
+    torch.cuda.set_device(0)
+    hip = Hip()
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+    def dev(raw):
+        if raw.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(raw, dtype=np.float32)).cuda()
+
+    t0 = time.perf_counter()
+    log(f"[bench] generating {cfg.name} inputs")
+    kv = K.gen_layer(cfg, 0)
+    k_d, v_d = dev(kv["k"]), dev(kv["v"])
+    del kv
+    (wuk, wdk), (wuv, wdv) = K.gen_w(cfg, 0, 0), K.gen_w(cfg, 0, 1)
+    wuk_d, wdk_d, wuv_d, wdv_d = dev(wuk.raw), dev(wdk.raw), dev(wuv.raw), dev(wdv.raw)
+    nsteps = DECODE_STEPS
+    q_d = torch.stack([dev(np.stack([K.gen_q(cfg, 0, b, i).raw for b in range(cfg.batch)])) for i in range(nsteps)])
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f}s")
+
+    lay = D.make_layout(cfg.dtype, cfg.head_dim, cfg.code_dim, cfg.stride, cfg.n_kv_heads, cfg.batch, cfg.seq_len)
+    cache_bytes = D.dkv_cache_bytes(lay)
+    nrep = max(1, math.ceil(2 * MALL_BYTES / cache_bytes))
+    caches = [D.Cache(lay) for _ in range(nrep)]
+    splits = args.splits or D.dkv_decode_auto_splits(lay, cfg.n_q_heads)
+    ws_c = D.workspace(D.dkv_compress_workspace_bytes(lay))
+    ws_d = D.workspace(D.dkv_decode_workspace_bytes(lay, cfg.n_q_heads, splits))
+    outs = torch.empty((nsteps, cfg.batch, cfg.n_q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
+
+    # Eager pass: fill every replica and keep reference outputs for steps 0 and 255.
+    for c in caches:
+        D.deltakv_compress(lay, k_d, v_d, wdk_d, wdv_d, c, ws_c)
+    D.deltakv_decode_attn(lay, caches[0], q_d[0], wuk_d, wuv_d, outs[0], ws_d, n_splits=splits)
+    eager0 = outs[0].clone()
+    D.deltakv_decode_attn(lay, caches[(nsteps - 1) % nrep], q_d[nsteps - 1], wuk_d, wuv_d, outs[nsteps - 1], ws_d,
+                          n_splits=splits)
+    eager_last = outs[nsteps - 1].clone()
+    torch.cuda.synchronize()
+
+    # Capture one step as a graph on a side stream.
+    stream = torch.cuda.Stream()
+    s_h = stream.cuda_stream
+    ev_c = hip.events(5)
+    ev_d = [hip.events(4) for _ in range(nsteps)]
+    torch.cuda.synchronize()
+    hip.begin_capture(s_h)
+    try:
+        D.deltakv_compress(lay, k_d, v_d, wdk_d, wdv_d, caches[0], ws_c, stream=s_h, stage_events=ev_c)
+        for i in range(nsteps):
+            D.deltakv_decode_attn(lay, caches[i % nrep], q_d[i], wuk_d, wuv_d, outs[i], ws_d, n_splits=splits,
+                                  stream=s_h, stage_events=ev_d[i])
+    finally:
+        graph, gexec = hip.end_capture(s_h)
+
+    for _ in range(args.warmup):
+        hip.launch(gexec, s_h)
+    hip.sync(s_h)
+    if not (torch.equal(outs[0], eager0) and torch.equal(outs[nsteps - 1], eager_last)):
+        raise RuntimeError("graph replay output differs from the eager run")
+
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        hip.launch(gexec, s_h)
+    hip.sync(s_h)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    if not (torch.equal(outs[0], eager0) and torch.equal(outs[nsteps - 1], eager_last)):
+        raise RuntimeError("timed graph replay output differs from the eager run")
+
+    # Stage times of the last timed step.
+    c_stage = [hip.elapsed_ms(ev_c[i], ev_c[i + 1]) for i in range(4)]
+    d_stage = np.array([[hip.elapsed_ms(e[i], e[i + 1]) for i in range(3)] for e in ev_d])
+    decode_window_ms = hip.elapsed_ms(ev_d[0][0], ev_d[-1][3])
+    compress_ms = hip.elapsed_ms(ev_c[0], ev_c[4])
+
+    eff = effective_decode_bytes(cfg)
+    value = nsteps * eff / (decode_window_ms * 1e-3) / 1e9
+    split_ms = float(d_stage[:, 1].mean())
+    split_bytes = split_kernel_bytes_per_head(cfg, splits) * cfg.batch * cfg.n_kv_heads
+    n_streams = cfg.batch * cfg.n_kv_heads * 2
+    search_flops = search_flops_per_stream(cfg) * n_streams
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded generator: shared high-norm mean + Zipf-clustered tokens + noise; random "
+                "orthonormal W)",
+        "config": {"workload": f"{cfg.name}: Llama-3-8B-shaped layer, compress {cfg.seq_len}-token prefill then "
+                               f"{nsteps} decode steps", "batch": cfg.batch, "n_kv_heads": cfg.n_kv_heads,
+                   "n_q_heads": cfg.n_q_heads, "head_dim": cfg.head_dim, "seq_len": cfg.seq_len,
+                   "stride": cfg.stride, "code_dim": cfg.code_dim, "decode_steps": nsteps, "splits": splits,
+                   "cache_replicas": nrep, "cache_mb": round(cache_bytes / 1e6, 2)},
+        "decode_tokens_per_s": round(cfg.batch * nsteps / (decode_window_ms * 1e-3), 1),
+        "decode_us_per_step": round(decode_window_ms * 1e3 / nsteps, 3),
+        "decode_hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "compress_tokens_per_s": round(cfg.batch * cfg.seq_len * cfg.n_layers / (compress_ms * 1e-3), 1),
+        "compress_ms": round(compress_ms, 4),
+        "compress_stage_ms": {"mean": round(c_stage[0], 4), "center": round(c_stage[1], 4),
+                              "search": round(c_stage[2], 4), "encode": round(c_stage[3], 4)},
+        "decode_stage_us": {"refscore": round(float(d_stage[:, 0].mean()) * 1e3, 3),
+                            "split": round(split_ms * 1e3, 3),
+                            "combine": round(float(d_stage[:, 2].mean()) * 1e3, 3)},
+        "roofline": {"kernel": "k_split (decode token stream)", "bound": "hbm",
+                     "achieved": round(split_bytes / (split_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(split_bytes / (split_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": split_bytes},
+        "roofline_search": {"kernel": "k_search_mfma", "bound": "mfma",
+                            "achieved": round(search_flops / (c_stage[2] * 1e-3) / 1e12, 2),
+                            "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(search_flops / (c_stage[2] * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                            "flops_per_launch": search_flops},
+    }
+    log(f"[bench] gpu done: {json.dumps(res)}")
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host")
+        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -132,7 +132,14 @@ typedef struct dkv_cache {
  *              matrix shared by all heads
  *   mu_in      optional device [B][H][2][d]: use this shared component
  *              instead of computing the mean (NULL = compute)
+ *   stage_events  optional host array of DKV_COMPRESS_EVENTS hipEvent_t
+ *              handles (NULL = none).  Event i is recorded on the stream
+ *              before stage i (mean, center, search, encode) and the last
+ *              after the encode, so hipEventElapsedTime between events i
+ *              and i+1 times stage i.  Events may be recorded under stream
+ *              capture.
  */
+#define DKV_COMPRESS_EVENTS 5
 typedef struct dkv_compress_in {
   const void* k;
   const void* v;
@@ -143,6 +150,7 @@ typedef struct dkv_compress_in {
   const void* w_down_v;
   int64_t w_head_stride;
   const void* mu_in;
+  void* const* stage_events;
 } dkv_compress_in;
 
 /*
@@ -157,7 +165,12 @@ typedef struct dkv_compress_in {
  *              dkv_decode_auto_splits); at most 1024
  *   softmax_scale  multiplies q . k^; 0 means 1 / sqrt(d)
  *   out        device [B][Hq][d] float32, written whole
+ *   stage_events  optional host array of DKV_DECODE_EVENTS hipEvent_t
+ *              handles (NULL = none), recorded before each stage (reference
+ *              scores, split, combine) and after the last, as for
+ *              dkv_compress_in.stage_events
  */
+#define DKV_DECODE_EVENTS 4
 typedef struct dkv_decode_in {
   const void* q;
   const void* w_up_k;
@@ -168,6 +181,7 @@ typedef struct dkv_decode_in {
   float softmax_scale;
   uint32_t reserved; /* must be 0 */
   float* out;
+  void* const* stage_events;
 } dkv_decode_in;
 
 /* DKV_ABI_VERSION of the loaded library. */

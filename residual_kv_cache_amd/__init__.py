@@ -53,13 +53,15 @@ class dkv_cache(ctypes.Structure):
 class dkv_compress_in(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
                 ("stride_h", ctypes.c_int64), ("stride_t", ctypes.c_int64), ("w_down_k", ctypes.c_void_p),
-                ("w_down_v", ctypes.c_void_p), ("w_head_stride", ctypes.c_int64), ("mu_in", ctypes.c_void_p)]
+                ("w_down_v", ctypes.c_void_p), ("w_head_stride", ctypes.c_int64), ("mu_in", ctypes.c_void_p),
+                ("stage_events", ctypes.c_void_p)]
 
 
 class dkv_decode_in(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("w_up_k", ctypes.c_void_p), ("w_up_v", ctypes.c_void_p),
                 ("w_head_stride", ctypes.c_int64), ("n_q_heads", ctypes.c_uint32), ("n_splits", ctypes.c_uint32),
-                ("softmax_scale", ctypes.c_float), ("reserved", ctypes.c_uint32), ("out", ctypes.c_void_p)]
+                ("softmax_scale", ctypes.c_float), ("reserved", ctypes.c_uint32), ("out", ctypes.c_void_p),
+                ("stage_events", ctypes.c_void_p)]
 
 
 _lib_handle = None
@@ -182,20 +184,26 @@ def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
+def _events(ev) -> int | None:
+    """stage_events: None, or a ctypes array of hipEvent_t handles (kept
+    alive by the caller for the duration of the call)."""
+    return None if ev is None else ctypes.addressof(ev)
+
+
 # ---------------------------------------------------------------------------
 # Entry points.
 # ---------------------------------------------------------------------------
 
 def deltakv_compress(layout: dkv_layout, k: torch.Tensor, v: torch.Tensor, w_down_k: torch.Tensor,
                      w_down_v: torch.Tensor, cache: Cache, ws: torch.Tensor, mu_in: torch.Tensor | None = None,
-                     w_head_stride: int = 0, stream=None) -> None:
+                     w_head_stride: int = 0, stream=None, stage_events=None) -> None:
     """k, v: [B][H][T][d] (head dim contiguous; strides (b, h, t) taken from
     k and required equal for v).  w_down_*: [d_c][d].  ws: device buffer of
     at least dkv_compress_workspace_bytes(layout) bytes."""
     if k.stride() != v.stride() or k.stride(-1) != 1:
         raise ValueError("k and v need equal strides and a contiguous head dim")
     a = dkv_compress_in(_ptr(k), _ptr(v), k.stride(0), k.stride(1), k.stride(2), _ptr(w_down_k), _ptr(w_down_v),
-                        w_head_stride, _ptr(mu_in))
+                        w_head_stride, _ptr(mu_in), _events(stage_events))
     _check(lib().deltakv_compress(ctypes.byref(layout), ctypes.byref(a), ctypes.byref(cache.c),
                                   ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
                                   ctypes.c_void_p(_stream(stream))), "deltakv_compress")
@@ -203,12 +211,12 @@ def deltakv_compress(layout: dkv_layout, k: torch.Tensor, v: torch.Tensor, w_dow
 
 def deltakv_decode_attn(layout: dkv_layout, cache: Cache, q: torch.Tensor, w_up_k: torch.Tensor,
                         w_up_v: torch.Tensor, out: torch.Tensor, ws: torch.Tensor, n_splits: int = 0,
-                        softmax_scale: float = 0.0, w_head_stride: int = 0, stream=None) -> None:
+                        softmax_scale: float = 0.0, w_head_stride: int = 0, stream=None, stage_events=None) -> None:
     """q: [B][Hq][d] contiguous; w_up_*: [d][d_c]; out: [B][Hq][d] float32."""
     if not q.is_contiguous() or not out.is_contiguous() or out.dtype != torch.float32:
         raise ValueError("q and out must be contiguous; out must be float32")
     a = dkv_decode_in(_ptr(q), _ptr(w_up_k), _ptr(w_up_v), w_head_stride, q.shape[1], n_splits,
-                      softmax_scale, 0, _ptr(out))
+                      softmax_scale, 0, _ptr(out), _events(stage_events))
     _check(lib().deltakv_decode_attn(ctypes.byref(layout), ctypes.byref(cache.c), ctypes.byref(a),
                                      ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
                                      ctypes.c_void_p(_stream(stream))), "deltakv_decode_attn")

@@ -189,6 +189,7 @@ dkv_status deltakv_compress(const dkv_layout* layout, const dkv_compress_in* in,
   a.mu = cache->mu;
   a.mean_part = (double*)((char*)ws + dkv::ws_mean_off(sh));
   a.inv_n = (float*)((char*)ws + dkv::ws_invn_off(sh));
+  a.events = in->stage_events;
   return from_hip(dkv::launch_compress(sh, a, (hipStream_t)stream));
 }
 
@@ -232,6 +233,7 @@ dkv_status deltakv_decode_attn(const dkv_layout* layout, const dkv_cache* cache,
   a.score = (float*)ws;
   a.qp = (float*)((char*)ws + dkv::ws_qp_off(sh, G));
   a.part = (float*)((char*)ws + dkv::ws_part_off(sh, G));
+  a.events = in->stage_events;
   return from_hip(dkv::launch_decode(sh, a, (hipStream_t)stream));
 }
 

@@ -452,24 +452,44 @@ template <int D>
 hipError_t launch_compress_d(const Shape& sh, const CompressArgs& a, hipStream_t st) {
   const int ns = sh.n_streams();
   const int chunks = mean_chunks(sh);
+  const dim3 g_mean(chunks, ns), g_ref((sh.R + 3) / 4, ns);
+  hipError_t e;
+#define DKV_TRY(x) \
+  if ((e = (x)) != hipSuccess) return e
+  DKV_TRY(mark(a.events, 0, st));
   if (sh.bf16) {
-    k_mean_partial<BF16><<<dim3(chunks, ns), 256, 0, st>>>(a, sh);
+    k_mean_partial<BF16><<<g_mean, 256, 0, st>>>(a, sh);
     k_mean_final<BF16><<<ns, 128, 0, st>>>(a, sh, chunks);
-    k_center_refs<BF16><<<dim3((sh.R + 3) / 4, ns), 256, 0, st>>>(a, sh);
-    if (sh.N > 0) {
-      k_search_mfma<D><<<dim3((sh.T + kSearchTok - 1) / kSearchTok, ns), 256, 0, st>>>(a, sh);
-      k_encode_mfma<D><<<dim3((sh.N + 63) / 64, ns), 256, 0, st>>>(a, sh);
-    }
   } else {
-    k_mean_partial<F32><<<dim3(chunks, ns), 256, 0, st>>>(a, sh);
+    k_mean_partial<F32><<<g_mean, 256, 0, st>>>(a, sh);
     k_mean_final<F32><<<ns, 128, 0, st>>>(a, sh, chunks);
-    k_center_refs<F32><<<dim3((sh.R + 3) / 4, ns), 256, 0, st>>>(a, sh);
-    if (sh.N > 0) {
-      k_search_f32<D><<<dim3((sh.T + 255) / 256, ns), 256, 0, st>>>(a, sh);
-      k_encode_f32<D><<<dim3((sh.N + 255) / 256, ns), 256, 0, st>>>(a, sh);
-    }
   }
-  return hipGetLastError();
+  DKV_TRY(hipGetLastError());
+  DKV_TRY(mark(a.events, 1, st));
+  if (sh.bf16)
+    k_center_refs<BF16><<<g_ref, 256, 0, st>>>(a, sh);
+  else
+    k_center_refs<F32><<<g_ref, 256, 0, st>>>(a, sh);
+  DKV_TRY(hipGetLastError());
+  DKV_TRY(mark(a.events, 2, st));
+  if (sh.N > 0) {
+    if (sh.bf16)
+      k_search_mfma<D><<<dim3((sh.T + kSearchTok - 1) / kSearchTok, ns), 256, 0, st>>>(a, sh);
+    else
+      k_search_f32<D><<<dim3((sh.T + 255) / 256, ns), 256, 0, st>>>(a, sh);
+  }
+  DKV_TRY(hipGetLastError());
+  DKV_TRY(mark(a.events, 3, st));
+  if (sh.N > 0) {
+    if (sh.bf16)
+      k_encode_mfma<D><<<dim3((sh.N + 63) / 64, ns), 256, 0, st>>>(a, sh);
+    else
+      k_encode_f32<D><<<dim3((sh.N + 255) / 256, ns), 256, 0, st>>>(a, sh);
+  }
+  DKV_TRY(hipGetLastError());
+  DKV_TRY(mark(a.events, 4, st));
+#undef DKV_TRY
+  return hipSuccess;
 }
 
 }  // namespace

@@ -297,16 +297,21 @@ hipError_t launch_split(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
 
 template <class S, int D>
 hipError_t launch_decode_sd(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
-  k_refscore<S, D><<<dim3((sh.R + 63) / 64, sh.B * sh.H), 256, 0, st>>>(a, sh);
   hipError_t e;
+  if ((e = mark(a.events, 0, st)) != hipSuccess) return e;
+  k_refscore<S, D><<<dim3((sh.R + 63) / 64, sh.B * sh.H), 256, 0, st>>>(a, sh);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = mark(a.events, 1, st)) != hipSuccess) return e;
   if (a.G <= 1) e = launch_split<S, D, 1>(sh, a, st);
   else if (a.G <= 2) e = launch_split<S, D, 2>(sh, a, st);
   else if (a.G <= 4) e = launch_split<S, D, 4>(sh, a, st);
   else if (a.G <= 8) e = launch_split<S, D, 8>(sh, a, st);
   else e = launch_split<S, D, 16>(sh, a, st);
   if (e != hipSuccess) return e;
+  if ((e = mark(a.events, 2, st)) != hipSuccess) return e;
   k_combine<S, D><<<sh.B * a.Hq, 128, 0, st>>>(a, sh);
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return mark(a.events, 3, st);
 }
 
 }  // namespace

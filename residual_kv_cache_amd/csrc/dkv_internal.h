@@ -68,6 +68,7 @@ struct CompressArgs {
   void* mu;
   double* mean_part;
   float* inv_n;
+  void* const* events;       // DKV_COMPRESS_EVENTS hipEvent_t or NULL
 };
 
 struct DecodeArgs {
@@ -87,7 +88,13 @@ struct DecodeArgs {
   float* score;              // [B][H][R][G]
   float* qp;                 // [B][H][G][dc]
   float* part;               // [B][H][splits][G][rec]
+  void* const* events;       // DKV_DECODE_EVENTS hipEvent_t or NULL
 };
+
+// Records stage event i of an optional event array on the stream.
+inline hipError_t mark(void* const* ev, int i, hipStream_t st) {
+  return ev ? hipEventRecord((hipEvent_t)ev[i], st) : hipSuccess;
+}
 
 hipError_t launch_compress(const Shape& sh, const CompressArgs& a, hipStream_t st);
 hipError_t launch_decode(const Shape& sh, const DecodeArgs& a, hipStream_t st);

@@ -135,7 +135,7 @@ class FakeCache:
 
 
 def _compress_status(lay, k, v, wd, ws, cache, ws_bytes=None):
-    a = D.dkv_compress_in(k, v, 8 * 32768 * 128, 32768 * 128, 128, wd, wd, 0, None)
+    a = D.dkv_compress_in(k, v, 8 * 32768 * 128, 32768 * 128, 128, wd, wd, 0, None, None)
     return D.lib().deltakv_compress(ctypes.byref(lay), ctypes.byref(a), ctypes.byref(cache.c),
                                     ctypes.c_void_p(ws), ws_bytes if ws_bytes is not None else 1 << 30, None)
 
@@ -158,13 +158,13 @@ def test_compress_rejects_before_launch():
     bad = FakeCache(P)
     bad.c.codes = P + 4
     assert _compress_status(lay, P, P, P, P, bad) == 4
-    a = D.dkv_compress_in(P, P, 0, 0, 132, P, P, 0, None)  # stride_t not a multiple of 8
+    a = D.dkv_compress_in(P, P, 0, 0, 132, P, P, 0, None, None)  # stride_t not a multiple of 8
     assert D.lib().deltakv_compress(ctypes.byref(lay), ctypes.byref(a), ctypes.byref(cache.c), P, 1 << 30,
                                     None) == 4
-    a = D.dkv_compress_in(P, P, 0, 0, 64, P, P, 0, None)   # stride_t < head_dim
+    a = D.dkv_compress_in(P, P, 0, 0, 64, P, P, 0, None, None)   # stride_t < head_dim
     assert D.lib().deltakv_compress(ctypes.byref(lay), ctypes.byref(a), ctypes.byref(cache.c), P, 1 << 30,
                                     None) == 2
-    a = D.dkv_compress_in(P, P, 0, 0, 128, P, P, 8, None)  # head stride smaller than one matrix
+    a = D.dkv_compress_in(P, P, 0, 0, 128, P, P, 8, None, None)  # head stride smaller than one matrix
     assert D.lib().deltakv_compress(ctypes.byref(lay), ctypes.byref(a), ctypes.byref(cache.c), P, 1 << 30,
                                     None) == 2
     assert D.lib().deltakv_compress(ctypes.byref(lay), None, ctypes.byref(cache.c), P, 1 << 30, None) == 1
@@ -173,7 +173,7 @@ def test_compress_rejects_before_launch():
 
 
 def _decode_status(lay, q, wu, out, ws, cache, hq=32, splits=0, scale=0.0, ws_bytes=None, reserved=0):
-    a = D.dkv_decode_in(q, wu, wu, 0, hq, splits, scale, reserved, out)
+    a = D.dkv_decode_in(q, wu, wu, 0, hq, splits, scale, reserved, out, None)
     return D.lib().deltakv_decode_attn(ctypes.byref(lay), ctypes.byref(cache.c), ctypes.byref(a),
                                        ctypes.c_void_p(ws), ws_bytes if ws_bytes is not None else 1 << 30, None)
 
