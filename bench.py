@@ -8,11 +8,13 @@ single layer, batch 1, 8 KV / 32 query heads, head dim 128, 32768 prefill
 tokens, bf16 storage, stride 16, code dim 32.
 
 Inputs (K, V, W, the 256 queries) are resident in HBM before timing.  Each
-step is one HIP graph: compress into cache replica 0, then decode step i over
-replica i mod R (R replicas of the cache, together larger than the 256 MB
-Infinity Cache, so decode reads come from HBM as they would across the
-layers of a model).  Stage events recorded inside the graph time every
-kernel of the last timed step.
+step replays two HIP graphs: compress into cache replica 0, then decode step
+i over replica i mod R (R replicas of the cache, together larger than the
+256 MB Infinity Cache, so decode reads come from HBM as they would across
+the layers of a model).  Events between the two graph launches time the
+compress and decode phases of every timed step.  Per-kernel device times
+(for the roofline) come from the library's stage events on an eager pass of
+the same work, stamped at kernel start and end.
 
 Prints one JSON line.  `value` is decode-attention throughput in GB/s over
 the decode window of a step (effective bytes: every cache array, V's mean,
@@ -248,42 +250,68 @@ def main():
     eager_last = outs[nsteps - 1].clone()
     torch.cuda.synchronize()
 
-    # Capture one step as a graph on a side stream.
+    # Capture the step as two graphs on a side stream: compress, then the
+    # 256 decode steps.  Events between the graph launches split the step.
     stream = torch.cuda.Stream()
     s_h = stream.cuda_stream
-    ev_c = hip.events(5)
-    ev_d = [hip.events(4) for _ in range(nsteps)]
     torch.cuda.synchronize()
     hip.begin_capture(s_h)
     try:
-        D.deltakv_compress(lay, k_d, v_d, wdk_d, wdv_d, caches[0], ws_c, stream=s_h, stage_events=ev_c)
+        D.deltakv_compress(lay, k_d, v_d, wdk_d, wdv_d, caches[0], ws_c, stream=s_h)
+    finally:
+        _, g_comp = hip.end_capture(s_h)
+    hip.begin_capture(s_h)
+    try:
         for i in range(nsteps):
             D.deltakv_decode_attn(lay, caches[i % nrep], q_d[i], wuk_d, wuv_d, outs[i], ws_d, n_splits=splits,
-                                  stream=s_h, stage_events=ev_d[i])
+                                  stream=s_h)
     finally:
-        graph, gexec = hip.end_capture(s_h)
+        _, g_dec = hip.end_capture(s_h)
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        hip.launch(g_comp, s_h)
+        if evs:
+            evs[1].record(stream)
+        hip.launch(g_dec, s_h)
+        if evs:
+            evs[2].record(stream)
 
     for _ in range(args.warmup):
-        hip.launch(gexec, s_h)
+        step()
     hip.sync(s_h)
     if not (torch.equal(outs[0], eager0) and torch.equal(outs[nsteps - 1], eager_last)):
         raise RuntimeError("graph replay output differs from the eager run")
 
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for _ in range(args.steps):
-        hip.launch(gexec, s_h)
+    for i in range(args.steps):
+        step(evs[i])
     hip.sync(s_h)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     if not (torch.equal(outs[0], eager0) and torch.equal(outs[nsteps - 1], eager_last)):
         raise RuntimeError("timed graph replay output differs from the eager run")
+    compress_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    decode_window_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
 
-    # Stage times of the last timed step.
-    c_stage = [hip.elapsed_ms(ev_c[i], ev_c[i + 1]) for i in range(4)]
-    d_stage = np.array([[hip.elapsed_ms(e[i], e[i + 1]) for i in range(3)] for e in ev_d])
-    decode_window_ms = hip.elapsed_ms(ev_d[0][0], ev_d[-1][3])
-    compress_ms = hip.elapsed_ms(ev_c[0], ev_c[4])
+    # Per-kernel device times: the same work launched eagerly with the
+    # library's stage events (stamped at kernel start and end).
+    ev_c = hip.events(8)
+    ev_d = [hip.events(6) for _ in range(nsteps)]
+    c_stage, d_stage = [], []
+    for rep in range(2):
+        D.deltakv_compress(lay, k_d, v_d, wdk_d, wdv_d, caches[0], ws_c, stream=s_h, stage_events=ev_c)
+        for i in range(nsteps):
+            D.deltakv_decode_attn(lay, caches[i % nrep], q_d[i], wuk_d, wuv_d, outs[i], ws_d, n_splits=splits,
+                                  stream=s_h, stage_events=ev_d[i])
+        hip.sync(s_h)
+        c_stage.append([hip.elapsed_ms(ev_c[2 * j], ev_c[2 * j + 1]) for j in range(4)])
+        d_stage.extend([[hip.elapsed_ms(e[2 * j], e[2 * j + 1]) for j in range(3)] for e in ev_d])
+    c_stage = np.mean(np.array(c_stage), axis=0)
+    d_stage = np.array(d_stage)
 
     eff = effective_decode_bytes(cfg)
     value = nsteps * eff / (decode_window_ms * 1e-3) / 1e9

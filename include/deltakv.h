@@ -133,13 +133,14 @@ typedef struct dkv_cache {
  *   mu_in      optional device [B][H][2][d]: use this shared component
  *              instead of computing the mean (NULL = compute)
  *   stage_events  optional host array of DKV_COMPRESS_EVENTS hipEvent_t
- *              handles (NULL = none).  Event i is recorded on the stream
- *              before stage i (mean, center, search, encode) and the last
- *              after the encode, so hipEventElapsedTime between events i
- *              and i+1 times stage i.  Events may be recorded under stream
- *              capture.
+ *              handles (NULL = none): a (start, stop) pair per stage, in the
+ *              order mean, center, search, encode.  Start is stamped when the
+ *              stage's first kernel starts executing and stop when its last
+ *              kernel ends, so hipEventElapsedTime(start, stop) is the
+ *              stage's device time.  Not allowed while `stream` is being
+ *              captured into a graph (DKV_ERR_UNSUPPORTED).
  */
-#define DKV_COMPRESS_EVENTS 5
+#define DKV_COMPRESS_EVENTS 8
 typedef struct dkv_compress_in {
   const void* k;
   const void* v;
@@ -166,11 +167,11 @@ typedef struct dkv_compress_in {
  *   softmax_scale  multiplies q . k^; 0 means 1 / sqrt(d)
  *   out        device [B][Hq][d] float32, written whole
  *   stage_events  optional host array of DKV_DECODE_EVENTS hipEvent_t
- *              handles (NULL = none), recorded before each stage (reference
- *              scores, split, combine) and after the last, as for
+ *              handles (NULL = none): (start, stop) pairs of the stages
+ *              reference scores, split, combine, as for
  *              dkv_compress_in.stage_events
  */
-#define DKV_DECODE_EVENTS 4
+#define DKV_DECODE_EVENTS 6
 typedef struct dkv_decode_in {
   const void* q;
   const void* w_up_k;

@@ -223,7 +223,8 @@ def deltakv_decode_attn(layout: dkv_layout, cache: Cache, q: torch.Tensor, w_up_
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
-    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    """A zero-filled device workspace (the decode workspace must start zeroed)."""
+    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
 __all__ = ["lib", "make_layout", "dkv_layout", "dkv_cache", "dkv_compress_in", "dkv_decode_in", "Cache",

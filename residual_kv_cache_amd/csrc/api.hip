@@ -71,9 +71,10 @@ dkv_status check_cache(const dkv_cache* c, const Shape& sh) {
   return DKV_OK;
 }
 
-uint32_t auto_splits(const Shape& sh) {
-  // Aim for about 2048 blocks over the B*H heads (8 per CU on 256 CUs), at
-  // least ~256 cached tokens per split, at most 1024 splits.
+uint32_t auto_splits(const Shape& sh, int G) {
+  if (dkv::decode_fused_supported(sh, G, 1)) return (uint32_t)dkv::decode_fused_auto_splits(sh);
+  // General path (256-thread blocks): about 2048 blocks over the B*H heads,
+  // at least 256 cached tokens per split, at most 1024 splits.
   const int64_t heads = (int64_t)sh.B * sh.H;
   int64_t by_chip = (2048 + heads - 1) / heads;
   int64_t by_len = (sh.T + 255) / 256;
@@ -84,6 +85,14 @@ uint32_t auto_splits(const Shape& sh) {
 }
 
 dkv_status from_hip(hipError_t e) { return e == hipSuccess ? DKV_OK : DKV_ERR_DEVICE; }
+
+// Stage events use the extended launch, which stream capture does not take.
+dkv_status check_events(void* const* ev, void* stream) {
+  if (!ev) return DKV_OK;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing((hipStream_t)stream, &cs) != hipSuccess) return DKV_ERR_DEVICE;
+  return cs == hipStreamCaptureStatusNone ? DKV_OK : DKV_ERR_UNSUPPORTED;
+}
 
 }  // namespace
 
@@ -141,9 +150,9 @@ size_t dkv_compress_workspace_bytes(const dkv_layout* layout) {
 
 uint32_t dkv_decode_auto_splits(const dkv_layout* layout, uint32_t n_q_heads) {
   Shape sh;
-  (void)n_q_heads;
   if (check_layout(layout, &sh) != DKV_OK) return 0;
-  return auto_splits(sh);
+  if (n_q_heads == 0 || n_q_heads % sh.H != 0 || n_q_heads / sh.H > 16) return 0;
+  return auto_splits(sh, (int)(n_q_heads / sh.H));
 }
 
 size_t dkv_decode_workspace_bytes(const dkv_layout* layout, uint32_t n_q_heads, uint32_t n_splits) {
@@ -151,8 +160,9 @@ size_t dkv_decode_workspace_bytes(const dkv_layout* layout, uint32_t n_q_heads, 
   if (check_layout(layout, &sh) != DKV_OK) return 0;
   if (n_q_heads == 0 || n_q_heads % sh.H != 0 || n_q_heads / sh.H > 16) return 0;
   if (n_splits > 1024) return 0;
-  const int splits = n_splits ? (int)n_splits : (int)auto_splits(sh);
-  return dkv::decode_ws_bytes(sh, (int)(n_q_heads / sh.H), splits);
+  const int G = (int)(n_q_heads / sh.H);
+  const int splits = n_splits ? (int)n_splits : (int)auto_splits(sh, G);
+  return dkv::decode_ws_bytes(sh, G, splits);
 }
 
 dkv_status deltakv_compress(const dkv_layout* layout, const dkv_compress_in* in, const dkv_cache* cache, void* ws,
@@ -190,6 +200,7 @@ dkv_status deltakv_compress(const dkv_layout* layout, const dkv_compress_in* in,
   a.mean_part = (double*)((char*)ws + dkv::ws_mean_off(sh));
   a.inv_n = (float*)((char*)ws + dkv::ws_invn_off(sh));
   a.events = in->stage_events;
+  if ((st = check_events(a.events, stream)) != DKV_OK) return st;
   return from_hip(dkv::launch_compress(sh, a, (hipStream_t)stream));
 }
 
@@ -211,7 +222,7 @@ dkv_status deltakv_decode_attn(const dkv_layout* layout, const dkv_cache* cache,
   if (in->w_head_stride != 0 && in->w_head_stride < (int64_t)sh.d * sh.dc) return DKV_ERR_SHAPE;
   if (!(in->softmax_scale >= 0.f) || isinf(in->softmax_scale)) return DKV_ERR_SHAPE;
   const int G = (int)(in->n_q_heads / sh.H);
-  const int splits = in->n_splits ? (int)in->n_splits : (int)auto_splits(sh);
+  const int splits = in->n_splits ? (int)in->n_splits : (int)auto_splits(sh, G);
   const size_t need = dkv::decode_ws_bytes(sh, G, splits);
   if (!ws || ws_bytes < need) return DKV_ERR_WORKSPACE;
   if (!aligned16(ws)) return DKV_ERR_ALIGN;
@@ -234,6 +245,7 @@ dkv_status deltakv_decode_attn(const dkv_layout* layout, const dkv_cache* cache,
   a.qp = (float*)((char*)ws + dkv::ws_qp_off(sh, G));
   a.part = (float*)((char*)ws + dkv::ws_part_off(sh, G));
   a.events = in->stage_events;
+  if ((st = check_events(a.events, stream)) != DKV_OK) return st;
   return from_hip(dkv::launch_decode(sh, a, (hipStream_t)stream));
 }
 

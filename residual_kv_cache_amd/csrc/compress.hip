@@ -453,41 +453,36 @@ hipError_t launch_compress_d(const Shape& sh, const CompressArgs& a, hipStream_t
   const int ns = sh.n_streams();
   const int chunks = mean_chunks(sh);
   const dim3 g_mean(chunks, ns), g_ref((sh.R + 3) / 4, ns);
+  const dim3 g_search((sh.T + kSearchTok - 1) / kSearchTok, ns), g_search32((sh.T + 255) / 256, ns);
+  const dim3 g_enc((sh.N + 63) / 64, ns), g_enc32((sh.N + 255) / 256, ns);
+  void* const* ev = a.events;
   hipError_t e;
 #define DKV_TRY(x) \
   if ((e = (x)) != hipSuccess) return e
-  DKV_TRY(mark(a.events, 0, st));
   if (sh.bf16) {
-    k_mean_partial<BF16><<<g_mean, 256, 0, st>>>(a, sh);
-    k_mean_final<BF16><<<ns, 128, 0, st>>>(a, sh, chunks);
+    DKV_TRY(launch(k_mean_partial<BF16>, g_mean, 256, st, ev_start(ev, 0), nullptr, a, sh));
+    DKV_TRY(launch(k_mean_final<BF16>, ns, 128, st, nullptr, ev_stop(ev, 0), a, sh, chunks));
+    DKV_TRY(launch(k_center_refs<BF16>, g_ref, 256, st, ev_start(ev, 1), ev_stop(ev, 1), a, sh));
+    if (sh.N > 0) {
+      DKV_TRY(launch(k_search_mfma<D>, g_search, 256, st, ev_start(ev, 2), ev_stop(ev, 2), a, sh));
+      DKV_TRY(launch(k_encode_mfma<D>, g_enc, 256, st, ev_start(ev, 3), ev_stop(ev, 3), a, sh));
+    }
   } else {
-    k_mean_partial<F32><<<g_mean, 256, 0, st>>>(a, sh);
-    k_mean_final<F32><<<ns, 128, 0, st>>>(a, sh, chunks);
+    DKV_TRY(launch(k_mean_partial<F32>, g_mean, 256, st, ev_start(ev, 0), nullptr, a, sh));
+    DKV_TRY(launch(k_mean_final<F32>, ns, 128, st, nullptr, ev_stop(ev, 0), a, sh, chunks));
+    DKV_TRY(launch(k_center_refs<F32>, g_ref, 256, st, ev_start(ev, 1), ev_stop(ev, 1), a, sh));
+    if (sh.N > 0) {
+      DKV_TRY(launch(k_search_f32<D>, g_search32, 256, st, ev_start(ev, 2), ev_stop(ev, 2), a, sh));
+      DKV_TRY(launch(k_encode_f32<D>, g_enc32, 256, st, ev_start(ev, 3), ev_stop(ev, 3), a, sh));
+    }
   }
-  DKV_TRY(hipGetLastError());
-  DKV_TRY(mark(a.events, 1, st));
-  if (sh.bf16)
-    k_center_refs<BF16><<<g_ref, 256, 0, st>>>(a, sh);
-  else
-    k_center_refs<F32><<<g_ref, 256, 0, st>>>(a, sh);
-  DKV_TRY(hipGetLastError());
-  DKV_TRY(mark(a.events, 2, st));
-  if (sh.N > 0) {
-    if (sh.bf16)
-      k_search_mfma<D><<<dim3((sh.T + kSearchTok - 1) / kSearchTok, ns), 256, 0, st>>>(a, sh);
-    else
-      k_search_f32<D><<<dim3((sh.T + 255) / 256, ns), 256, 0, st>>>(a, sh);
+  if (sh.N == 0 && ev) {
+    // No coded tokens: the search and encode stages are empty.
+    for (int i = 2; i < 4; ++i) {
+      DKV_TRY(hipEventRecord(ev_start(ev, i), st));
+      DKV_TRY(hipEventRecord(ev_stop(ev, i), st));
+    }
   }
-  DKV_TRY(hipGetLastError());
-  DKV_TRY(mark(a.events, 3, st));
-  if (sh.N > 0) {
-    if (sh.bf16)
-      k_encode_mfma<D><<<dim3((sh.N + 63) / 64, ns), 256, 0, st>>>(a, sh);
-    else
-      k_encode_f32<D><<<dim3((sh.N + 255) / 256, ns), 256, 0, st>>>(a, sh);
-  }
-  DKV_TRY(hipGetLastError());
-  DKV_TRY(mark(a.events, 4, st));
 #undef DKV_TRY
   return hipSuccess;
 }

@@ -21,7 +21,10 @@
 // mu_V and W_up_V once per query head.  All arithmetic is fp32; scores are
 // kept in base-2 units (scale * log2 e) so the exponentials are exp2.
 //
-// Kernels: refscore (S and q'), split (the token stream), combine.
+// Kernels: refscore (S and q'), split (the token stream), combine.  This is
+// the general path (float32 storage, head dim 64, more than 4 query heads
+// per KV head, code dim 64..128); the common bfloat16 shapes take the fused
+// MFMA kernel of decode_mfma.hip.
 
 #include "dkv_device.h"
 #include "dkv_internal.h"
@@ -291,32 +294,28 @@ __global__ __launch_bounds__(128) void k_combine(DecodeArgs a, Shape sh) {
 
 template <class S, int D, int GP>
 hipError_t launch_split(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
-  k_split_valu<S, D, GP><<<dim3(a.splits, sh.B * sh.H), 256, 0, st>>>(a, sh);
-  return hipGetLastError();
+  return launch(k_split_valu<S, D, GP>, dim3(a.splits, sh.B * sh.H), 256, st, ev_start(a.events, 1),
+                ev_stop(a.events, 1), a, sh);
 }
 
 template <class S, int D>
 hipError_t launch_decode_sd(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
-  hipError_t e;
-  if ((e = mark(a.events, 0, st)) != hipSuccess) return e;
-  k_refscore<S, D><<<dim3((sh.R + 63) / 64, sh.B * sh.H), 256, 0, st>>>(a, sh);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = mark(a.events, 1, st)) != hipSuccess) return e;
+  hipError_t e = launch(k_refscore<S, D>, dim3((sh.R + 63) / 64, sh.B * sh.H), 256, st, ev_start(a.events, 0),
+                        ev_stop(a.events, 0), a, sh);
+  if (e != hipSuccess) return e;
   if (a.G <= 1) e = launch_split<S, D, 1>(sh, a, st);
   else if (a.G <= 2) e = launch_split<S, D, 2>(sh, a, st);
   else if (a.G <= 4) e = launch_split<S, D, 4>(sh, a, st);
   else if (a.G <= 8) e = launch_split<S, D, 8>(sh, a, st);
   else e = launch_split<S, D, 16>(sh, a, st);
   if (e != hipSuccess) return e;
-  if ((e = mark(a.events, 2, st)) != hipSuccess) return e;
-  k_combine<S, D><<<sh.B * a.Hq, 128, 0, st>>>(a, sh);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  return mark(a.events, 3, st);
+  return launch(k_combine<S, D>, dim3(sh.B * a.Hq), 128, st, ev_start(a.events, 2), ev_stop(a.events, 2), a, sh);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
+  if (decode_fused_supported(sh, a.G, a.splits)) return launch_decode_fused(sh, a, st);
   if (sh.bf16) return sh.d == 128 ? launch_decode_sd<BF16, 128>(sh, a, st) : launch_decode_sd<BF16, 64>(sh, a, st);
   return sh.d == 128 ? launch_decode_sd<F32, 128>(sh, a, st) : launch_decode_sd<F32, 64>(sh, a, st);
 }

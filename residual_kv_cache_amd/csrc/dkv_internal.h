@@ -2,6 +2,7 @@
 // the DeltaKV library.  Not part of the ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -54,6 +55,12 @@ inline size_t decode_ws_bytes(const Shape& sh, int G, int splits) {
   return align_up(ws_part_off(sh, G) + ws_part_bytes(sh, G, splits), 256);
 }
 
+// Fused MFMA decode (decode_mfma.hip): bfloat16 storage, head dim 128, up to
+// 4 query heads per KV head, code dim up to 48, at most kMfmaMaxSplits splits.
+constexpr int kMfmaMaxSplits = 256;
+bool decode_fused_supported(const Shape& sh, int G, int splits);
+int decode_fused_auto_splits(const Shape& sh);
+
 struct CompressArgs {
   const void* k;
   const void* v;
@@ -91,12 +98,25 @@ struct DecodeArgs {
   void* const* events;       // DKV_DECODE_EVENTS hipEvent_t or NULL
 };
 
-// Records stage event i of an optional event array on the stream.
-inline hipError_t mark(void* const* ev, int i, hipStream_t st) {
-  return ev ? hipEventRecord((hipEvent_t)ev[i], st) : hipSuccess;
+// Stage timing: event pair (start, stop) of stage i from an optional array.
+inline hipEvent_t ev_start(void* const* ev, int i) { return ev ? (hipEvent_t)ev[2 * i] : nullptr; }
+inline hipEvent_t ev_stop(void* const* ev, int i) { return ev ? (hipEvent_t)ev[2 * i + 1] : nullptr; }
+
+// Launches a kernel; with events, the start event is stamped when the
+// kernel begins executing and the stop event when it ends (AMD's extended
+// launch), so host-side launch gaps never enter the measured time.
+template <typename... KArgs, typename... Args>
+inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t st, hipEvent_t start,
+                         hipEvent_t stop, Args... args) {
+  if (start || stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, start, stop, 0, args...);
+  else
+    kernel<<<grid, block, 0, st>>>(args...);
+  return hipGetLastError();
 }
 
 hipError_t launch_compress(const Shape& sh, const CompressArgs& a, hipStream_t st);
 hipError_t launch_decode(const Shape& sh, const DecodeArgs& a, hipStream_t st);
+hipError_t launch_decode_fused(const Shape& sh, const DecodeArgs& a, hipStream_t st);
 
 }  // namespace dkv

@@ -27,6 +27,9 @@ SMALL = {
                                             n_kv_heads=1, n_q_heads=16),
     "bf16_g3": BASE_BF16.replace(name="bf16_g3", head_dim=64, code_dim=64, stride=8, seq_len=1500, n_kv_heads=3,
                                  n_q_heads=9),
+    "bf16_dc48_s8": BASE_BF16.replace(name="bf16_dc48_s8", code_dim=48, stride=8, seq_len=2500, n_kv_heads=2,
+                                      n_q_heads=4, sigma=0.2),
+    "bf16_g2_b3": BASE_BF16.replace(name="bf16_g2_b3", seq_len=777, n_kv_heads=2, n_q_heads=4, batch=3),
     "f32_ragged_g2": K.CONFIGS["tiny"].replace(name="f32_ragged_g2", seq_len=1234, n_kv_heads=2, n_q_heads=4,
                                                head_dim=128, code_dim=32, stride=5),
 }
