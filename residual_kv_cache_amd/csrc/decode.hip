@@ -23,8 +23,8 @@
 //
 // Kernels: refscore (S and q'), split (the token stream), combine.  This is
 // the general path (float32 storage, head dim 64, more than 4 query heads
-// per KV head, code dim 64..128); the common bfloat16 shapes take the fused
-// MFMA kernel of decode_mfma.hip.
+// per KV head, code dim 64..128); the common bfloat16 shapes take the MFMA
+// kernels of decode_mfma.hip.
 
 #include "dkv_device.h"
 #include "dkv_internal.h"
@@ -41,7 +41,7 @@ __device__ __forceinline__ float ld(const void* p, size_t i) {
 }
 
 // ---------------------------------------------------------------------------
-// refscore: S[b][h][r][g] for 64 references per block, and q'[b][h][g][:]
+// refscore: S[b][h][r][g] (row stride score_cols(G)) for 64 references per block, and q'[b][h][g][:]
 // from the first block of each (b, h).  grid (ceil(R/64), B*H), block 256.
 // ---------------------------------------------------------------------------
 
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void k_refscore(DecodeArgs a, Shape sh) {
     float acc = 0.f;
 #pragma unroll 8
     for (int i = 0; i < D; ++i) acc = fmaf(qs[g][i], rs[row][i], acc);
-    a.score[((size_t)bh * sh.R + r0 + row) * G + g] = acc;
+    a.score[((size_t)bh * sh.R + r0 + row) * score_cols(G) + g] = acc;
   }
   if (blockIdx.x == 0) {
     const typename S::T* wu = (const typename S::T*)a.wuk + (size_t)h * a.w_hs;
@@ -107,7 +107,8 @@ __global__ __launch_bounds__(256) void k_split_valu(DecodeArgs a, Shape sh) {
   __syncthreads();
 
   const size_t sK = (size_t)bh * 2, sV = sK + 1;             // stream ids
-  const float* score = a.score + (size_t)bh * sh.R * G;
+  const int Gs = score_cols(G);
+  const float* score = a.score + (size_t)bh * sh.R * Gs;
   const typename S::T* refsV = (const typename S::T*)a.refs + sV * sh.R * D;
   const typename S::T* codesK = (const typename S::T*)a.codes + sK * sh.N * dc;
   const typename S::T* codesV = (const typename S::T*)a.codes + sV * sh.N * dc;
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(256) void k_split_valu(DecodeArgs a, Shape sh) {
         rk = rv = u;
       }
 #pragma unroll
-      for (int g = 0; g < GP; ++g) sc[g] = g < G ? score[(size_t)rk * G + g] : -INFINITY;
+      for (int g = 0; g < GP; ++g) sc[g] = g < G ? score[(size_t)rk * Gs + g] : -INFINITY;
       if (coded) {
         for (int j = 0; j < dc; ++j) {
           const float cj = S::load(codesK[(size_t)u * dc + j]);

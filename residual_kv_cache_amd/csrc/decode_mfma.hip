@@ -1,36 +1,44 @@
-// DeltaKV decode attention, fused MFMA kernel (bfloat16 storage, head dim
-// 128, up to 4 query heads per KV head, code dim 16..48).
+// DeltaKV decode attention, MFMA path (bfloat16 storage, head dim 128, up to
+// 4 query heads per KV head, code dim 16..48).
 //
-// Two kernels per decode step (split, combine).  Attention of query head g over every cached
-// token t as if it were reconstructed, k^_t = mu + ref + W_up code (DeltaKV
-// explainer, English page, Technical Summary §3 "Reconstruction"):
+// Attention of query head g over every cached token t as if it were
+// reconstructed, k^_t = mu + ref + W_up code (DeltaKV explainer, English
+// page, Technical Summary §3 "Reconstruction"):
 //
-//   score(t) = scale * (q_g . refs_K[ref_K(t)] + (W_up_K^T q_g) . code_K(t))
+//   score(t) = S[ref_K(t)][g] + q'_g . code_K(t),
+//              S[r][g] = c * q_g . refs_K[r],  q'_g = c * W_up_K^T q_g,  c = scale * log2 e
 //   out_g    = mu_V + (sum_t p_t refs_V[ref_V(t)] + W_up_V sum_t p_t code_V(t)) / sum_t p_t
 //
-// (q_g . mu_K is the same for every token and cancels in the softmax.)  A
-// reference token r is a token whose reference is itself and whose code is 0.
+// (q_g . mu_K is the same for every token and cancels in the softmax; a
+// reference token r is a token whose reference is itself and whose code is
+// 0.)  Three kernels per decode step:
 //
-// Work split: the B*H (sequence, KV head) pairs are split along the sequence
-// into `splits` pieces; a 512-thread block (8 waves) owns one piece, each wave
-// a contiguous run of 16-token tiles.  Blocks of head bh run on XCD bh % 8
-// (workgroups are dispatched to the eight XCDs round-robin), so the gathered
-// key and value reference rows of a head stay in one L2.  Each block writes
-// an online-softmax partial (max, sum, code and reference accumulators per
-// query head); the last block of a head to finish (an atomic arrival count)
-// merges the partials and writes the output, then rearms the count.
+//   refscore  S for every key reference (one MFMA chain per 16 references)
+//             and q' (16 lanes per output element);
+//   split     the token stream: the B*H (sequence, KV head) pairs are split
+//             along the sequence; a 512-thread block (8 waves) owns one
+//             piece, each wave a contiguous run of 16-token tiles.  The
+//             head's S table sits in LDS, so a token's key reference costs
+//             one LDS read instead of a 256-byte row gather;
+//   combine   merges the splits of each query head and applies mu_V, W_up_V.
 //
-// Per 16-token tile, three MFMA 16x16x32 (bf16 in, fp32 accumulate) chains
-// keep every operand lane-local (lane l: n16 = l % 16, q4 = l / 16):
-//   scores  C[token][(g, e)]: A = key reference row / key code row of token
-//           n16, B = q_g (exact bf16) / q'_g split into bf16 hi + lo;
-//           lane l ends with the scores of query head (l%16)/4 for tokens
-//           4*q4 + i, i = 0..3 (replicated over e = l % 4)
+// Blocks of head bh run on XCD bh % 8 (workgroups are dispatched to the
+// eight XCDs round-robin), so the value reference rows a head gathers stay
+// in one L2.
+//
+// Per 16-token tile a wave issues one MFMA 16x16x32 (bf16 in, fp32
+// accumulate) chain for the code part of the scores and three for the value
+// side, every operand lane-local (lane l: n16 = l % 16, q4 = l / 16):
+//   scores  C[token][(g, e)] = code_K(token) . q'_g: A = key code rows
+//           (token n16), B = q'_g split into bf16 hi + lo parts, replicated
+//           over e; lane l ends with the scores of query head n16 / 4 for
+//           tokens 4 q4 + i, i = 0..3, and adds S[ref_K(token)][g] from LDS;
 //   values  C[(g, e)][n] += sum_k P[(g, e)][k] X[k][n], k = (token, e'),
 //           P[(g, e)][(token, e')] = p_g(token) if e == e' else 0,
-//           X[(token, e')][n] = row(token)[4n + e'] (+ column offset):
-//           the weights a lane holds are the ones it feeds (A), and B is
-//           whole 8-byte row segments; lane l accumulates query head l/16.
+//           X[(token, e')][n] = row(token)[8n + e' (+4)] (value reference
+//           rows) or [4n + e'] (value code rows): the weights a lane holds
+//           are the ones it feeds (A), B is whole row segments as loaded,
+//           and lane l accumulates query head q4.
 // Softmax weights go in as bf16 hi + lo parts (about 16 significant bits);
 // their sum comes from a spare value-code column set to 1.0, so the
 // normaliser uses exactly the weights the accumulators used.  The running
@@ -49,11 +57,15 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kD = 128;
 constexpr int kMaxDc = 48;
+constexpr int kRsRefs = 64;                              // references per refscore block
+constexpr int kRedFloats = kWaves * 4 * (kD + 64);       // wave-merge buffer of the split kernel
+constexpr size_t kSplitLdsMax = 160 * 1024 - 1024;       // dynamic LDS of one split block
 
 typedef uint32_t Frag __attribute__((ext_vector_type(4)));
 typedef uint32_t U32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef const __attribute__((address_space(1))) char* GPtr;
 
 __device__ __forceinline__ f32x4 mfma16(Frag a, Frag b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -65,39 +77,108 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
+// Global-memory load at a byte offset (the address space is explicit so that
+// selected base pointers still compile to global, not flat, loads).
 template <typename T>
 __device__ __forceinline__ T ldg(const void* base, uint32_t byte_off) {
-  return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off);
+  return *(const __attribute__((address_space(1))) T*)((GPtr)base + byte_off);
 }
 
-// Reference ordinals of one 16-token tile, loaded one step ahead of the
-// tile's data so that the data loads never wait on them.  Coded tiles and
-// reference tiles are separate instantiations, so that the loop bodies have
-// no control flow (a branch merge would make the compiler drain every
-// outstanding load).
+// bf16 {1, 0, 0, 0}: value-code operand of the weight-sum column.
+__device__ const uint16_t kOnePair[4] __attribute__((aligned(16))) = {0x3F80u, 0u, 0u, 0u};
+
+// ---------------------------------------------------------------------------
+// refscore.  Block (bh, chunk) of 256 threads: S rows of kRsRefs references
+// (wave w: references chunk*64 + 16w + n16; A = q_g, B = reference rows, so
+// lane (n16, q4 = 0) ends with S[r][0..3]), and the q' outputs
+// o = chunk + chunks * (16 t + quarter) (16 lanes per output, 8 products
+// each, summed by a fixed butterfly).
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void k_refscore_mfma(DecodeArgs a, Shape sh, int chunks) {
+  const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
+  const int bh = xcd + 8 * (kx / chunks), c = kx % chunks;
+  if (bh >= sh.B * sh.H) return;
+  const int b = bh / sh.H, h = bh % sh.H;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n16 = lane & 15, q4 = lane >> 4;
+  const int G = a.G, dc = sh.dc;
+  const float cs = a.scale * kLog2e;
+  const uint16_t* q = (const uint16_t*)a.q + ((size_t)b * a.Hq + h * G) * kD;
+
+  const int r = c * kRsRefs + wave * 16 + n16;
+  const uint32_t rr = (uint32_t)min(r, sh.R - 1);
+  const uint16_t* refsK = (const uint16_t*)a.refs + (size_t)bh * 2 * sh.R * kD;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint32_t col = ks * 32 + q4 * 8;
+    const Frag aq = n16 < G ? ldg<Frag>(q, ((uint32_t)n16 * kD + col) * 2u) : Frag{0u, 0u, 0u, 0u};
+    const Frag br = ldg<Frag>(refsK, (rr * kD + col) * 2u);
+    acc = mfma16(aq, br, acc);
+  }
+  if (q4 == 0 && r < sh.R)
+    *reinterpret_cast<f32x4*>(a.score + ((size_t)bh * sh.R + r) * 4) = acc * cs;
+
+  const int quarter = wave * 4 + q4;
+  const uint16_t* wu = (const uint16_t*)a.wuk + (size_t)h * a.w_hs;
+  for (int o = c + chunks * quarter; o < G * dc; o += chunks * 16) {
+    const int g = o / dc, j = o % dc;
+    const Frag qv = ldg<Frag>(q, ((uint32_t)g * kD + n16 * 8) * 2u);
+    float s = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t qw = qv[t >> 1];
+      const float qf = __uint_as_float((t & 1) ? (qw & 0xFFFF0000u) : (qw << 16));
+      s = fmaf(qf, bf2f(wu[(size_t)(n16 * 8 + t) * dc + j]), s);
+    }
+    s += __shfl_xor(s, 8, 64);
+    s += __shfl_xor(s, 4, 64);
+    s += __shfl_xor(s, 2, 64);
+    s += __shfl_xor(s, 1, 64);
+    if (n16 == 0) a.qp[((size_t)bh * G + g) * dc + j] = s * cs;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// split.
+// ---------------------------------------------------------------------------
+
+// One 16-token tile.  Lane (n16, q4) with n16 < 4 holds the key ordinal of
+// token 4 q4 + n16, with 4 <= n16 < 8 the value ordinal of token
+// 4 q4 + n16 - 4; a row broadcast hands every lane of row q4 the ordinals of
+// its four tokens.  Ordinals are loaded a step ahead of the tile's data.
+// Coded tiles and reference tiles are separate instantiations, so that the
+// loop bodies have no control flow (a branch merge would make the compiler
+// drain every outstanding load).
 struct TileIdx {
   int base, cnt;   // first token (coded row or reference ordinal); valid tokens (0 = dead tile)
-  int rkA;         // key reference of score row n16
-  int rv[4];       // value references of tokens 4*q4 + i
+  int raw;
 };
 
 struct Tile {
-  Frag kr[4];      // score A: key reference row of token n16, K-steps 0..3
+  float sb[4];     // S[ref_K(token 4 q4 + i)][n16 / 4]
   Frag ck[2];      // score A: key code row of token n16 (coded tiles)
-  Frag xv[2][2];   // value B [group][half]: tokens 4*q4 + 2*group + {0,1}
+  Frag xv[2][2];   // value B [group][half]: tokens 4 q4 + 2 group + {0, 1}
   Frag bc[2];      // value-code B [group] (+ the 1.0 column)
   int cnt;
 };
 
 struct Args {
   // per (b, h) stream bases
-  const uint16_t* refsK;
   const uint16_t* refsV;
   const uint16_t* codesK;
   const uint16_t* codesV;
   const void* idxK;       // uint16_t or uint32_t ordinals
   const void* idxV;
+  const float* score;     // S rows of this (b, h), 4 floats each
 };
+
+// Lane k of each 16-lane row, broadcast over the row.
+template <int K>
+__device__ __forceinline__ int row_bcast(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, 0x150 + K, 0xF, 0xF, false);
+}
 
 // Tile tt of a run [t0, t1) of 16-token tiles starting at token `first`
 // and ending at token `last` (exclusive).  Tiles past t1 are dead: they
@@ -111,92 +192,99 @@ __device__ __forceinline__ void load_idx(const Args& p, int tt, int t1, int firs
   const int cnt = min(16, last - base);
   ti.base = base;
   ti.cnt = live ? cnt : 0;
-  const int ua = base + min(n16, cnt - 1);
+  const int u = base + min(q4 * 4 + (n16 & 3), cnt - 1);
   if (CODED) {
-    const IdxT* ik = (const IdxT*)p.idxK;
-    const IdxT* iv = (const IdxT*)p.idxV;
-    ti.rkA = (int)ik[ua];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ti.rv[i] = (int)iv[base + min(q4 * 4 + i, cnt - 1)];
+    const IdxT* src = (const IdxT*)(n16 < 4 ? p.idxK : p.idxV);
+    ti.raw = (int)src[u];
   } else {
-    ti.rkA = ua;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ti.rv[i] = base + min(q4 * 4 + i, cnt - 1);
+    ti.raw = u;
   }
 }
 
-template <bool CODED, int DCK>
-__device__ __forceinline__ void load_data(const Args& p, const Shape& sh, const TileIdx& ti, int n16, int q4,
-                                          Tile& td) {
+template <int I, bool SLDS>
+__device__ __forceinline__ float s_lookup(const Args& p, const float* s_lds, int raw, int R, int gl) {
+  const uint32_t rk = (uint32_t)min(row_bcast<I>(raw), R - 1);
+  return SLDS ? s_lds[rk * 4 + gl] : ldg<float>(p.score, (rk * 4 + gl) * 4u);
+}
+
+template <bool CODED, int DCK, bool SLDS>
+__device__ __forceinline__ void load_data(const Args& p, const Shape& sh, const float* s_lds, const TileIdx& ti,
+                                          int n16, int q4, Tile& td) {
   const int dc = sh.dc;
+  const int gl = n16 >> 2;
   td.cnt = ti.cnt;
   // Ordinals come from caller memory: clamp so that a corrupt cache can never
-  // address outside the reference arrays.
-  const uint32_t rkA = (uint32_t)min(ti.rkA, sh.R - 1);
-  uint32_t rv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) rv[i] = (uint32_t)min(ti.rv[i], sh.R - 1);
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) td.kr[ks] = ldg<Frag>(p.refsK, (rkA * kD + ks * 32 + q4 * 8) * 2u);
-#pragma unroll
-  for (int g2 = 0; g2 < 2; ++g2)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const U32x2 a = ldg<U32x2>(p.refsV, (rv[2 * g2] * kD + n16 * 8 + hh * 4) * 2u);
-      const U32x2 b = ldg<U32x2>(p.refsV, (rv[2 * g2 + 1] * kD + n16 * 8 + hh * 4) * 2u);
-      td.xv[g2][hh] = Frag{a.x, a.y, b.x, b.y};
-    }
-  // Spare value-code column (the first past d_c) accumulates the weights.
-  const bool ones = n16 * 4 == dc;
-  const Frag one_col = Frag{ones ? 0x3F80u : 0u, 0u, ones ? 0x3F80u : 0u, 0u};
+  // address outside the reference arrays or the S table.
+  td.sb[0] = s_lookup<0, SLDS>(p, s_lds, ti.raw, sh.R, gl);
+  td.sb[1] = s_lookup<1, SLDS>(p, s_lds, ti.raw, sh.R, gl);
+  td.sb[2] = s_lookup<2, SLDS>(p, s_lds, ti.raw, sh.R, gl);
+  td.sb[3] = s_lookup<3, SLDS>(p, s_lds, ti.raw, sh.R, gl);
+  const uint32_t rv0 = (uint32_t)min(row_bcast<4>(ti.raw), sh.R - 1);
+  const uint32_t rv1 = (uint32_t)min(row_bcast<5>(ti.raw), sh.R - 1);
+  const uint32_t rv2 = (uint32_t)min(row_bcast<6>(ti.raw), sh.R - 1);
+  const uint32_t rv3 = (uint32_t)min(row_bcast<7>(ti.raw), sh.R - 1);
+  {
+    const Frag a = ldg<Frag>(p.refsV, (rv0 * kD + n16 * 8) * 2u);
+    const Frag b = ldg<Frag>(p.refsV, (rv1 * kD + n16 * 8) * 2u);
+    td.xv[0][0] = Frag{a.x, a.y, b.x, b.y};
+    td.xv[0][1] = Frag{a.z, a.w, b.z, b.w};
+  }
+  {
+    const Frag a = ldg<Frag>(p.refsV, (rv2 * kD + n16 * 8) * 2u);
+    const Frag b = ldg<Frag>(p.refsV, (rv3 * kD + n16 * 8) * 2u);
+    td.xv[1][0] = Frag{a.x, a.y, b.x, b.y};
+    td.xv[1][1] = Frag{a.z, a.w, b.z, b.w};
+  }
   if (CODED) {
     const int cnt = max(ti.cnt, 1);
     const uint32_t ua = ti.base + min(n16, cnt - 1);
 #pragma unroll
     for (int ks = 0; ks < DCK; ++ks) {
       // Columns past d_c (only when d_c is not a multiple of 32) read the
-      // row's own first columns and are zeroed after the load.
+      // row's own first columns; q' is zero there.
       const int c = ks * 32 + q4 * 8;
-      const Frag v = ldg<Frag>(p.codesK, (ua * dc + (c < dc ? c : 0)) * 2u);
-      td.ck[ks] = c < dc ? v : Frag{0u, 0u, 0u, 0u};
+      td.ck[ks] = ldg<Frag>(p.codesK, (ua * dc + (c < dc ? c : 0)) * 2u);
     }
-    const int cc = n16 * 4 < dc ? n16 * 4 : 0;
+    // Lanes past the code columns read the 1.0 pair (the lane at column d_c
+    // accumulates the weight sum; the others are never read).
+    const bool in_code = n16 * 4 < dc;
+    const uint16_t* vb = in_code ? p.codesV : kOnePair;
 #pragma unroll
     for (int g2 = 0; g2 < 2; ++g2) {
       const uint32_t u0 = ti.base + min(q4 * 4 + 2 * g2, cnt - 1);
       const uint32_t u1 = ti.base + min(q4 * 4 + 2 * g2 + 1, cnt - 1);
-      const U32x2 a = ldg<U32x2>(p.codesV, (u0 * dc + cc) * 2u);
-      const U32x2 b = ldg<U32x2>(p.codesV, (u1 * dc + cc) * 2u);
-      td.bc[g2] = n16 * 4 < dc ? Frag{a.x, a.y, b.x, b.y} : one_col;
+      const U32x2 a = ldg<U32x2>(vb, in_code ? (u0 * dc + n16 * 4) * 2u : 0u);
+      const U32x2 b = ldg<U32x2>(vb, in_code ? (u1 * dc + n16 * 4) * 2u : 0u);
+      td.bc[g2] = Frag{a.x, a.y, b.x, b.y};
     }
   } else {
-    td.bc[0] = td.bc[1] = one_col;
+    const bool ones = n16 * 4 == dc;
+    td.bc[0] = td.bc[1] = Frag{ones ? 0x3F80u : 0u, 0u, ones ? 0x3F80u : 0u, 0u};
   }
 }
 
 struct State {
-  float m;         // running max (base-2 units) of query head (l%16)/4
-  f32x4 accr[2];   // value-reference accumulators of query head l/16
+  float m;         // running max (base-2 units) of query head n16 / 4
+  f32x4 accr[2];   // value-reference accumulators of query head q4
   f32x4 accc;      // value-code accumulators (+ weight sum column)
 };
 
 template <bool CODED, int DCK>
-__device__ __forceinline__ void compute_tile(const Tile& td, const Frag* qk, const Frag* qh, const Frag* ql, float cs,
-                                             int q4, const uint32_t* sel, State& st) {
-  f32x4 sr = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) sr = mfma16(td.kr[ks], qk[ks], sr);
-  f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ void compute_tile(const Tile& td, const Frag* qh, const Frag* ql, int q4,
+                                             const uint32_t* sel, State& st) {
+  float s[4] = {td.sb[0], td.sb[1], td.sb[2], td.sb[3]};
   if (CODED) {
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < DCK; ++ks) {
-      sc = mfma16(td.ck[ks], qh[ks], sc);
-      sc = mfma16(td.ck[ks], ql[ks], sc);
+      c = mfma16(td.ck[ks], qh[ks], c);
+      c = mfma16(td.ck[ks], ql[ks], c);
     }
-  }
-  float s[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) s[i] = q4 * 4 + i < td.cnt ? fmaf(sr[i], cs, sc[i]) : -INFINITY;
+    for (int i = 0; i < 4; ++i) s[i] += c[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s[i] = q4 * 4 + i < td.cnt ? s[i] : -INFINITY;
   const float tmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
   if (__ballot(tmax > st.m + kTau) != 0ull) {
     float t2 = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
@@ -233,24 +321,29 @@ __device__ __forceinline__ void compute_tile(const Tile& td, const Frag* qk, con
 
 // One run of tiles of a wave: software pipeline, two tiles per trip
 // (buffers A and B); the ordinals of tile t+2 and the data of tile t+1 are
-// in flight while tile t computes.  Dead tiles (past the run) are masked.
-template <bool CODED, int DCK, typename IdxT>
-__device__ __forceinline__ void run_tiles(const Args& p, const Shape& sh, int t0, int t1, int first, int last,
-                                          int n16, int q4, const Frag* qk, const Frag* qh, const Frag* ql, float cs,
+// in flight while tile t computes.  The scheduling barriers keep the
+// compiler from hoisting a tile's arithmetic above the next tile's loads.
+template <bool CODED, int DCK, typename IdxT, bool SLDS>
+__device__ __forceinline__ void run_tiles(const Args& p, const Shape& sh, const float* s_lds, int t0, int t1,
+                                          int first, int last, int n16, int q4, const Frag* qh, const Frag* ql,
                                           const uint32_t* sel, State& st) {
   if (t0 >= t1) return;
   TileIdx ia, ib;
   Tile da, db;
   load_idx<CODED, IdxT>(p, t0, t1, first, last, n16, q4, ia);
   load_idx<CODED, IdxT>(p, t0 + 1, t1, first, last, n16, q4, ib);
-  load_data<CODED, DCK>(p, sh, ia, n16, q4, da);
+  load_data<CODED, DCK, SLDS>(p, sh, s_lds, ia, n16, q4, da);
   for (int tt = t0; tt < t1; tt += 2) {
     load_idx<CODED, IdxT>(p, tt + 2, t1, first, last, n16, q4, ia);
-    load_data<CODED, DCK>(p, sh, ib, n16, q4, db);
-    compute_tile<CODED, DCK>(da, qk, qh, ql, cs, q4, sel, st);
+    load_data<CODED, DCK, SLDS>(p, sh, s_lds, ib, n16, q4, db);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_tile<CODED, DCK>(da, qh, ql, q4, sel, st);
+    __builtin_amdgcn_sched_barrier(0);
     load_idx<CODED, IdxT>(p, tt + 3, t1, first, last, n16, q4, ib);
-    load_data<CODED, DCK>(p, sh, ia, n16, q4, da);
-    compute_tile<CODED, DCK>(db, qk, qh, ql, cs, q4, sel, st);
+    load_data<CODED, DCK, SLDS>(p, sh, s_lds, ia, n16, q4, da);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_tile<CODED, DCK>(db, qh, ql, q4, sel, st);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -260,25 +353,20 @@ __device__ __forceinline__ int split_lo(int n, int sp, int splits, int align) {
   return sp == splits ? n : (int)(x / align * align);
 }
 
-template <int DCK, typename IdxT>
-__global__ __launch_bounds__(kThreads) void k_decode_mfma(DecodeArgs a, Shape sh) {
-  __shared__ __attribute__((aligned(16))) uint16_t w_lds[kD * kMaxDc];
-  __shared__ float q_lds[4][kD];
-  __shared__ float qp4[4][4 * kMaxDc];
-  __shared__ float qp_lds[4][kMaxDc];
+// Dynamic LDS: the S table (SLDS) and, after the tile loop, the wave-merge
+// buffer in the same bytes.
+template <int DCK, typename IdxT, bool SLDS>
+__global__ __launch_bounds__(kThreads) void k_split_mfma(DecodeArgs a, Shape sh) {
+  extern __shared__ __attribute__((aligned(16))) float lds[];
   __shared__ float red_m[kWaves][4];
-  __shared__ float red_acc[kWaves][4][kD + 64];
 
   const int BH = sh.B * sh.H;
   const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
   const int bh = xcd + 8 * (kx / a.splits), sp = kx % a.splits;
   if (bh >= BH) return;
-  const int b = bh / sh.H, h = bh % sh.H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n16 = lane & 15, q4 = lane >> 4;
-  const int gl = n16 >> 2, el = lane & 3;   // score layout: query head, e
   const int G = a.G, dc = sh.dc;
-  const float cs = a.scale * kLog2e;
 
   const int n0 = split_lo(sh.N, sp, a.splits, 16), n1 = split_lo(sh.N, sp + 1, a.splits, 16);
   const int r0 = split_lo(sh.R, sp, a.splits, 1), r1 = split_lo(sh.R, sp + 1, a.splits, 1);
@@ -288,55 +376,45 @@ __global__ __launch_bounds__(kThreads) void k_decode_mfma(DecodeArgs a, Shape sh
 
   Args p;
   const size_t sK = (size_t)bh * 2, sV = sK + 1;
-  p.refsK = (const uint16_t*)a.refs + sK * sh.R * kD;
   p.refsV = (const uint16_t*)a.refs + sV * sh.R * kD;
   p.codesK = (const uint16_t*)a.codes + sK * sh.N * dc;
   p.codesV = (const uint16_t*)a.codes + sV * sh.N * dc;
   p.idxK = (const IdxT*)a.idx + sK * sh.N;
   p.idxV = (const IdxT*)a.idx + sV * sh.N;
+  p.score = a.score + (size_t)bh * sh.R * 4;
 
-  // ---- q'_g = scale * log2e * W_up_K^T q_g, through LDS ----
-  const uint16_t* q = (const uint16_t*)a.q + ((size_t)b * a.Hq + h * G) * kD;
-  {
-    const uint16_t* wu = (const uint16_t*)a.wuk + (size_t)h * a.w_hs;
-    for (int i = tid; i < kD * dc / 8; i += kThreads)
-      *reinterpret_cast<uint4*>(&w_lds[i * 8]) = *reinterpret_cast<const uint4*>(wu + (size_t)i * 8);
-    for (int i = tid; i < G * kD; i += kThreads) q_lds[i / kD][i % kD] = bf2f(q[i]);
+  // The head's S table into LDS.
+  if (SLDS) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(p.score);
+    f32x4* dst = reinterpret_cast<f32x4*>(lds);
+    for (int i = tid; i < sh.R; i += kThreads) dst[i] = src[i];
   }
-  // The score B operands of the key references: q_g itself (exact bf16).
-  Frag qk[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-    qk[ks] = gl < G ? ldg<Frag>(q, ((uint32_t)gl * kD + ks * 32 + q4 * 8) * 2u) : Frag{0u, 0u, 0u, 0u};
-  __syncthreads();
-  for (int i = tid; i < 4 * G * dc; i += kThreads) {
-    const int qt = i / (G * dc), r = i % (G * dc), g = r / dc, j = r % dc;
-    float acc = 0.f;
-#pragma unroll 8
-    for (int k = qt * (kD / 4); k < (qt + 1) * (kD / 4); ++k) acc = fmaf(q_lds[g][k], bf2f(w_lds[k * dc + j]), acc);
-    qp4[qt][r] = acc;
-  }
-  __syncthreads();
-  for (int i = tid; i < G * dc; i += kThreads)
-    qp_lds[i / dc][i % dc] = (qp4[0][i] + qp4[1][i] + qp4[2][i] + qp4[3][i]) * cs;
-  __syncthreads();
+  // Score B operands: q'_g (g = n16 / 4) split into bf16 hi + lo parts.
   Frag qh[DCK], ql[DCK];
+  {
+    const int g = n16 >> 2;
+    const float* qp = a.qp + ((size_t)bh * G + min(g, G - 1)) * dc;
 #pragma unroll
-  for (int ks = 0; ks < DCK; ++ks) {
+    for (int ks = 0; ks < DCK; ++ks) {
+      const int k0 = ks * 32 + q4 * 8;
+      const bool live = g < G && k0 < dc;
+      const f32x4 v0 = live ? *reinterpret_cast<const f32x4*>(qp + k0) : f32x4{0.f, 0.f, 0.f, 0.f};
+      const f32x4 v1 = live ? *reinterpret_cast<const f32x4*>(qp + k0 + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+      const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
 #pragma unroll
-    for (int k2 = 0; k2 < 4; ++k2) {
-      const int j = ks * 32 + q4 * 8 + k2 * 2;
-      const float v0 = (gl < G && j < dc) ? qp_lds[gl][j] : 0.f;
-      const float v1 = (gl < G && j + 1 < dc) ? qp_lds[gl][j + 1] : 0.f;
-      const uint32_t hp = pk_bf16(v0, v1);
-      qh[ks][k2] = hp;
-      ql[ks][k2] = pk_bf16(v0 - __uint_as_float(hp << 16), v1 - __uint_as_float(hp & 0xFFFF0000u));
+      for (int k2 = 0; k2 < 4; ++k2) {
+        const uint32_t hp = pk_bf16(v[2 * k2], v[2 * k2 + 1]);
+        qh[ks][k2] = hp;
+        ql[ks][k2] = pk_bf16(v[2 * k2] - __uint_as_float(hp << 16), v[2 * k2 + 1] - __uint_as_float(hp & 0xFFFF0000u));
+      }
     }
   }
   // v_perm selectors that place a packed pair (p_a low, p_b high) at
-  // positions e and 4 + e of an 8 x bf16 A operand (zeros elsewhere).
+  // positions e and 4 + e of an 8 x bf16 A operand (zeros elsewhere),
+  // e = n16 % 4.
   uint32_t sel[4];
   {
+    const int el = n16 & 3;
     const uint32_t lo_a = (el & 1) ? 0x01000c0cu : 0x0c0c0100u;  // p_a into half e&1
     const uint32_t lo_b = (el & 1) ? 0x03020c0cu : 0x0c0c0302u;  // p_b into half e&1
     const int dw = el >> 1;
@@ -345,34 +423,37 @@ __global__ __launch_bounds__(kThreads) void k_decode_mfma(DecodeArgs a, Shape sh
     sel[2] = dw == 0 ? lo_b : 0x0c0c0c0cu;
     sel[3] = dw == 1 ? lo_b : 0x0c0c0c0cu;
   }
+  if (SLDS) __syncthreads();
 
   State st;
   st.m = -INFINITY;
   st.accr[0] = st.accr[1] = st.accc = f32x4{0.f, 0.f, 0.f, 0.f};
   // The wave's tiles: coded tiles [0, nct) then reference tiles [nct, nt).
-  run_tiles<true, DCK, IdxT>(p, sh, t_beg, min(t_end, nct), n0, n1, n16, q4, qk, qh, ql, cs, sel, st);
-  run_tiles<false, DCK, IdxT>(p, sh, max(t_beg, nct) - nct, t_end - nct, r0, r1, n16, q4, qk, qh, ql, cs, sel, st);
+  run_tiles<true, DCK, IdxT, SLDS>(p, sh, lds, t_beg, min(t_end, nct), n0, n1, n16, q4, qh, ql, sel, st);
+  run_tiles<false, DCK, IdxT, SLDS>(p, sh, lds, max(t_beg, nct) - nct, t_end - nct, r0, r1, n16, q4, qh, ql, sel,
+                                    st);
 
   // ---- merge the block's waves (fixed order) ----
-  if (lane < 16 && el == 0) red_m[wave][gl] = st.m;
-  __syncthreads();
+  if (lane < 16 && (n16 & 3) == 0) red_m[wave][n16 >> 2] = st.m;
+  __syncthreads();  // also: every wave is done with the S table
+  float* red_acc = lds;  // [kWaves][4][kD + 64]
   float mb = -INFINITY;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) mb = fmaxf(mb, red_m[w][q4]);
   const float mw = red_m[wave][q4];
   const float wgt = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - mb);
+  float* mine_acc = red_acc + (wave * 4 + q4) * (kD + 64);
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red_acc[wave][q4][n16 * 8 + hh * 4 + i] = st.accr[hh][i] * wgt;
+    for (int i = 0; i < 4; ++i) mine_acc[n16 * 8 + hh * 4 + i] = st.accr[hh][i] * wgt;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    if (n16 * 4 + i <= dc) red_acc[wave][q4][kD + n16 * 4 + i] = st.accc[i] * wgt;
+    if (n16 * 4 + i <= dc) mine_acc[kD + n16 * 4 + i] = st.accc[i] * wgt;
   __syncthreads();
   // Partial record per query head: [max, sum, code acc[dc], reference acc[d]].
   const int rec = partial_rec(sh);
-  float* part = a.part + (size_t)bh * a.splits * G * rec;
-  float* mine = part + (size_t)sp * G * rec;
+  float* part = a.part + ((size_t)bh * a.splits + sp) * G * rec;
   for (int i = tid; i < G * rec; i += kThreads) {
     const int g = i / rec, f = i % rec;
     float v = 0.f;
@@ -381,48 +462,49 @@ __global__ __launch_bounds__(kThreads) void k_decode_mfma(DecodeArgs a, Shape sh
       for (int w = 0; w < kWaves; ++w) v = w == 0 ? red_m[0][g] : fmaxf(v, red_m[w][g]);
     } else if (f == 1) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) v += red_acc[w][g][kD + dc];
+      for (int w = 0; w < kWaves; ++w) v += red_acc[(w * 4 + g) * (kD + 64) + kD + dc];
     } else if (f < 2 + dc) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) v += red_acc[w][g][kD + f - 2];
+      for (int w = 0; w < kWaves; ++w) v += red_acc[(w * 4 + g) * (kD + 64) + kD + f - 2];
     } else if (f < 2 + dc + kD) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) v += red_acc[w][g][f - 2 - dc];
+      for (int w = 0; w < kWaves; ++w) v += red_acc[(w * 4 + g) * (kD + 64) + f - 2 - dc];
     }
-    mine[i] = v;
+    part[i] = v;
   }
-
 }
 
 // combine: merges the splits of one (b, query head) and applies mu_V and
-// W_up_V.  grid B*Hq, block 256: thread t owns column t of the partial
-// records (code columns, then head-dim columns) and issues its loads of 32
-// splits at once, together with the split maxima and sums, so the records
-// (written by blocks on several XCDs) arrive in few round trips.
+// W_up_V.  Block L (256 threads) runs on XCD L % 8, the XCD of its head's
+// split blocks; thread t owns column t of the partial records (code columns,
+// then head-dim columns) and issues its loads of 32 splits at once, together
+// with the split maxima and sums, so the records arrive in few round trips.
 constexpr int kCombineBatch = 32;
 
 __global__ __launch_bounds__(256) void k_combine(DecodeArgs a, Shape sh) {
   __shared__ float mls[2][kMfmaMaxSplits];
   __shared__ float accc[kMaxDc];
   __shared__ float red[1];
-  const int bq = blockIdx.x;
-  const int b = bq / a.Hq, gq = bq % a.Hq;
-  const int h = gq / a.G, g = gq % a.G;
-  const int bh = b * sh.H + h;
+  const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
+  const int bh = xcd + 8 * (kx / a.G), g = kx % a.G;
+  if (bh >= sh.B * sh.H) return;
+  const int b = bh / sh.H, h = bh % sh.H;
+  const int gq = h * a.G + g;
   const int rec = partial_rec(sh), dc = sh.dc, ns = a.splits;
   const size_t pstride = (size_t)a.G * rec;
   const float* part = a.part + (size_t)bh * ns * pstride + (size_t)g * rec;
   const int t = threadIdx.x;
   const bool has_col = t < dc + kD;
   const float* pc = part + 2 + (has_col ? t : 0);
-  // W_up_V row of this thread's output column, loaded early.
+  // W_up_V row and mu_V of this thread's output column, loaded early.
   const int i_out = t - dc;
+  const bool is_out = i_out >= 0 && has_col;
   const uint16_t* wuv = (const uint16_t*)a.wuv + (size_t)h * a.w_hs;
   U32x2 wrow[kMaxDc / 4];
 #pragma unroll
   for (int j = 0; j < kMaxDc / 4; ++j)
-    wrow[j] = (i_out >= 0 && has_col && j * 4 < dc) ? ldg<U32x2>(wuv, ((uint32_t)i_out * dc + j * 4) * 2u)
-                                                      : U32x2{0u, 0u};
+    wrow[j] = (is_out && j * 4 < dc) ? ldg<U32x2>(wuv, ((uint32_t)i_out * dc + j * 4) * 2u) : U32x2{0u, 0u};
+  const float muv = is_out ? bf2f(((const uint16_t*)a.mu)[((size_t)bh * 2 + 1) * kD + i_out]) : 0.f;
   float v[kCombineBatch];
 #pragma unroll
   for (int k = 0; k < kCombineBatch; ++k) v[k] = (has_col && k < ns) ? pc[(size_t)k * pstride] : 0.f;
@@ -461,7 +543,7 @@ __global__ __launch_bounds__(256) void k_combine(DecodeArgs a, Shape sh) {
   }
   if (t < dc) accc[t] = acc;
   __syncthreads();
-  if (i_out >= 0 && has_col) {
+  if (is_out) {
     float u = 0.f;
 #pragma unroll
     for (int j = 0; j < kMaxDc / 4; ++j) {
@@ -471,9 +553,29 @@ __global__ __launch_bounds__(256) void k_combine(DecodeArgs a, Shape sh) {
       u = fmaf(__uint_as_float(wrow[j].y << 16), accc[j * 4 + 2], u);
       u = fmaf(__uint_as_float(wrow[j].y & 0xFFFF0000u), accc[j * 4 + 3], u);
     }
-    const float muv = bf2f(((const uint16_t*)a.mu)[((size_t)bh * 2 + 1) * kD + i_out]);
     a.out[((size_t)b * a.Hq + gq) * kD + i_out] = muv + (acc + u) / red[0];
   }
+}
+
+size_t split_lds_bytes(const Shape& sh, bool slds) {
+  const size_t red = (size_t)kRedFloats * sizeof(float);
+  const size_t s = slds ? (size_t)sh.R * 4 * sizeof(float) : 0;
+  return s > red ? s : red;
+}
+
+template <int DCK, typename IdxT, bool SLDS>
+hipError_t launch_split(const Shape& sh, const DecodeArgs& a, hipStream_t st, dim3 grid) {
+  const size_t lds = split_lds_bytes(sh, SLDS);
+  auto* k = k_split_mfma<DCK, IdxT, SLDS>;
+  hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  return launch_lds(k, grid, kThreads, lds, st, ev_start(a.events, 1), ev_stop(a.events, 1), a, sh);
+}
+
+template <int DCK, typename IdxT>
+hipError_t launch_split_s(const Shape& sh, const DecodeArgs& a, hipStream_t st, dim3 grid) {
+  return split_lds_bytes(sh, true) <= kSplitLdsMax ? launch_split<DCK, IdxT, true>(sh, a, st, grid)
+                                                   : launch_split<DCK, IdxT, false>(sh, a, st, grid);
 }
 
 }  // namespace
@@ -482,6 +584,7 @@ bool decode_fused_supported(const Shape& sh, int G, int splits) {
   return sh.bf16 && sh.d == kD && G <= 4 && sh.dc <= kMaxDc && splits <= kMfmaMaxSplits;
 }
 
+// About 512 split blocks over the chip, at least 512 tokens per split.
 int decode_fused_auto_splits(const Shape& sh) {
   const int64_t heads_per_xcd = (sh.B * sh.H + 7) / 8;
   int64_t s = (512 + 8 * heads_per_xcd - 1) / (8 * heads_per_xcd);
@@ -493,22 +596,19 @@ int decode_fused_auto_splits(const Shape& sh) {
 }
 
 hipError_t launch_decode_fused(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
-  const dim3 grid(8 * ((sh.B * sh.H + 7) / 8) * a.splits);
-  const bool i16 = sh.idx_bytes == 2;
-  hipError_t e;
-  hipEvent_t e0 = ev_start(a.events, 1), e1 = ev_stop(a.events, 1);
-  if (sh.dc <= 32)
-    e = i16 ? launch(k_decode_mfma<1, uint16_t>, grid, kThreads, st, e0, e1, a, sh)
-            : launch(k_decode_mfma<1, uint32_t>, grid, kThreads, st, e0, e1, a, sh);
-  else
-    e = i16 ? launch(k_decode_mfma<2, uint16_t>, grid, kThreads, st, e0, e1, a, sh)
-            : launch(k_decode_mfma<2, uint32_t>, grid, kThreads, st, e0, e1, a, sh);
+  const int BH8 = 8 * ((sh.B * sh.H + 7) / 8);
+  const int chunks = (sh.R + kRsRefs - 1) / kRsRefs;
+  hipError_t e = launch(k_refscore_mfma, dim3(BH8 * chunks), 256, st, ev_start(a.events, 0), ev_stop(a.events, 0),
+                        a, sh, chunks);
   if (e != hipSuccess) return e;
-  e = launch(k_combine, dim3(sh.B * a.Hq), 256, st, ev_start(a.events, 2), ev_stop(a.events, 2), a, sh);
-  if (e != hipSuccess || !a.events) return e;
-  // The reference scores are computed inside the split kernel: an empty stage.
-  if ((e = hipEventRecord(ev_start(a.events, 0), st)) != hipSuccess) return e;
-  return hipEventRecord(ev_stop(a.events, 0), st);
+  const dim3 grid(BH8 * a.splits);
+  const bool i16 = sh.idx_bytes == 2;
+  if (sh.dc <= 32)
+    e = i16 ? launch_split_s<1, uint16_t>(sh, a, st, grid) : launch_split_s<1, uint32_t>(sh, a, st, grid);
+  else
+    e = i16 ? launch_split_s<2, uint16_t>(sh, a, st, grid) : launch_split_s<2, uint32_t>(sh, a, st, grid);
+  if (e != hipSuccess) return e;
+  return launch(k_combine, dim3(BH8 * a.G), 256, st, ev_start(a.events, 2), ev_stop(a.events, 2), a, sh);
 }
 
 }  // namespace dkv

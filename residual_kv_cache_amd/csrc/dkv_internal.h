@@ -41,10 +41,14 @@ inline size_t ws_invn_off(const Shape& sh) { return align_up(ws_mean_bytes(sh), 
 inline size_t ws_invn_bytes(const Shape& sh) { return (size_t)sh.n_streams() * sh.R * sizeof(float); }
 inline size_t compress_ws_bytes(const Shape& sh) { return align_up(ws_invn_off(sh) + ws_invn_bytes(sh), 256); }
 
-// Decode workspace: reference scores S [B][H][R][G], projected queries
-// q' [B][Hq][dc] and split partials [B][H][splits][G][rec].
+// Decode workspace: reference scores S [B][H][R][Gs] (Gs = G rounded up to
+// a multiple of 4, padding zero), projected queries q' [B][H][G][dc] and
+// split partials [B][H][splits][G][rec].
 __host__ __device__ inline int partial_rec(const Shape& sh) { return (2 + sh.dc + sh.d + 3) / 4 * 4; }
-inline size_t ws_score_bytes(const Shape& sh, int G) { return (size_t)sh.B * sh.H * sh.R * G * sizeof(float); }
+__host__ __device__ inline int score_cols(int G) { return (G + 3) / 4 * 4; }
+inline size_t ws_score_bytes(const Shape& sh, int G) {
+  return (size_t)sh.B * sh.H * sh.R * score_cols(G) * sizeof(float);
+}
 inline size_t ws_qp_off(const Shape& sh, int G) { return align_up(ws_score_bytes(sh, G), 256); }
 inline size_t ws_qp_bytes(const Shape& sh, int G) { return (size_t)sh.B * sh.H * G * sh.dc * sizeof(float); }
 inline size_t ws_part_off(const Shape& sh, int G) { return align_up(ws_qp_off(sh, G) + ws_qp_bytes(sh, G), 256); }
@@ -55,8 +59,8 @@ inline size_t decode_ws_bytes(const Shape& sh, int G, int splits) {
   return align_up(ws_part_off(sh, G) + ws_part_bytes(sh, G, splits), 256);
 }
 
-// Fused MFMA decode (decode_mfma.hip): bfloat16 storage, head dim 128, up to
-// 4 query heads per KV head, code dim up to 48, at most kMfmaMaxSplits splits.
+// MFMA decode (decode_mfma.hip): bfloat16 storage, head dim 128, up to 4
+// query heads per KV head, code dim up to 48, at most kMfmaMaxSplits splits.
 constexpr int kMfmaMaxSplits = 256;
 bool decode_fused_supported(const Shape& sh, int G, int splits);
 int decode_fused_auto_splits(const Shape& sh);
@@ -92,7 +96,7 @@ struct DecodeArgs {
   const void* codes;
   const void* idx;
   const void* mu;
-  float* score;              // [B][H][R][G]
+  float* score;              // [B][H][R][score_cols(G)]
   float* qp;                 // [B][H][G][dc]
   float* part;               // [B][H][splits][G][rec]
   void* const* events;       // DKV_DECODE_EVENTS hipEvent_t or NULL
@@ -106,13 +110,18 @@ inline hipEvent_t ev_stop(void* const* ev, int i) { return ev ? (hipEvent_t)ev[2
 // kernel begins executing and the stop event when it ends (AMD's extended
 // launch), so host-side launch gaps never enter the measured time.
 template <typename... KArgs, typename... Args>
+inline hipError_t launch_lds(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t st,
+                             hipEvent_t start, hipEvent_t stop, Args... args) {
+  if (start || stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, st, start, stop, 0, args...);
+  else
+    kernel<<<grid, block, lds, st>>>(args...);
+  return hipGetLastError();
+}
+template <typename... KArgs, typename... Args>
 inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t st, hipEvent_t start,
                          hipEvent_t stop, Args... args) {
-  if (start || stop)
-    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, start, stop, 0, args...);
-  else
-    kernel<<<grid, block, 0, st>>>(args...);
-  return hipGetLastError();
+  return launch_lds(kernel, grid, block, 0, st, start, stop, args...);
 }
 
 hipError_t launch_compress(const Shape& sh, const CompressArgs& a, hipStream_t st);
