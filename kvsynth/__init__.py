@@ -186,21 +186,38 @@ def gen_q(cfg: Config, layer: int, seq: int, step: int) -> Stored:
     return to_storage(rng.standard_normal((cfg.n_q_heads, cfg.head_dim)), cfg.dtype)
 
 
-def gen_layer(cfg: Config, layer: int, seqs=None, heads=None):
-    """K and V of one layer as float64 value arrays and raw storage arrays,
-    shaped [B'][H'][T][d] over the selected sequences and heads."""
+def gen_layer(cfg: Config, layer: int, seqs=None, heads=None, workers: int = 1, f64: bool = True):
+    """K and V of one layer as raw storage arrays (and, with ``f64``, float64
+    value arrays), shaped [B'][H'][T][d] over the selected sequences and
+    heads.  Every stream has its own seeded generator, so ``workers`` threads
+    give the same arrays as one."""
     seqs = range(cfg.batch) if seqs is None else list(seqs)
     heads = range(cfg.n_kv_heads) if heads is None else list(heads)
+    jobs = [(kv, b, h) for kv in (0, 1) for b in seqs for h in heads]
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(workers) as ex:
+            res = list(ex.map(lambda j: gen_stream(cfg, layer, j[1], j[2], j[0]), jobs))
+    else:
+        res = [gen_stream(cfg, layer, b, h, kv) for kv, b, h in jobs]
+    nb, nh = len(seqs), len(heads)
     out = {}
     for kv, name in ((0, "k"), (1, "v")):
-        streams = [[gen_stream(cfg, layer, b, h, kv) for h in heads] for b in seqs]
-        out[name] = np.stack([np.stack([s.raw for s in row]) for row in streams])
-        out[name + "_f64"] = np.stack([np.stack([s.f64 for s in row]) for row in streams])
+        part = res[kv * nb * nh:(kv + 1) * nb * nh]
+        out[name] = np.stack([s.raw for s in part]).reshape(nb, nh, cfg.seq_len, cfg.head_dim)
+        if f64:
+            out[name + "_f64"] = np.stack([s.f64 for s in part]).reshape(nb, nh, cfg.seq_len, cfg.head_dim)
+        del part
     return out
+
+
+def storage_to_f64(raw: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 values of a raw storage array."""
+    return bf16_bits_to_f64(raw) if dtype == "bf16" else np.asarray(raw, np.float64)
 
 
 __all__ = [
     "Config", "CONFIGS", "Stored", "to_storage", "f64_to_bf16_bits", "bf16_bits_to_f64",
-    "gen_stream", "gen_cluster_ids", "gen_w", "gen_q", "gen_layer", "zipf_probs",
+    "gen_stream", "gen_cluster_ids", "gen_w", "gen_q", "gen_layer", "zipf_probs", "storage_to_f64",
     "ENTROPY",
 ]

@@ -565,11 +565,10 @@ size_t split_lds_bytes(const Shape& sh, bool slds) {
 
 template <int DCK, typename IdxT, bool SLDS>
 hipError_t launch_split(const Shape& sh, const DecodeArgs& a, hipStream_t st, dim3 grid) {
-  const size_t lds = split_lds_bytes(sh, SLDS);
-  auto* k = k_split_mfma<DCK, IdxT, SLDS>;
-  hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  return launch_lds(k, grid, kThreads, lds, st, ev_start(a.events, 1), ev_stop(a.events, 1), a, sh);
+  // gfx950 gives a workgroup up to 160 KB of LDS; dynamic sizes above 64 KB
+  // need no opt-in attribute on this runtime.
+  return launch_lds(k_split_mfma<DCK, IdxT, SLDS>, grid, kThreads, split_lds_bytes(sh, SLDS), st,
+                    ev_start(a.events, 1), ev_stop(a.events, 1), a, sh);
 }
 
 template <int DCK, typename IdxT>
@@ -584,10 +583,11 @@ bool decode_fused_supported(const Shape& sh, int G, int splits) {
   return sh.bf16 && sh.d == kD && G <= 4 && sh.dc <= kMaxDc && splits <= kMfmaMaxSplits;
 }
 
-// About 512 split blocks over the chip, at least 512 tokens per split.
+// The split kernel holds one 512-thread block per CU: about 256 blocks over
+// the chip (32 per XCD), at least 512 tokens per split.
 int decode_fused_auto_splits(const Shape& sh) {
   const int64_t heads_per_xcd = (sh.B * sh.H + 7) / 8;
-  int64_t s = (512 + 8 * heads_per_xcd - 1) / (8 * heads_per_xcd);
+  int64_t s = (32 + heads_per_xcd - 1) / heads_per_xcd;
   const int64_t by_len = (sh.T + 511) / 512;
   if (s > by_len) s = by_len;
   if (s < 1) s = 1;

@@ -49,15 +49,43 @@ def layout_of(cfg: K.Config) -> D.dkv_layout:
 
 
 class Inputs:
-    """One layer of seeded inputs: K, V [B][H][T][d] and the four matrices."""
+    """One layer of seeded inputs: K, V [B][H][T][d] and the four matrices.
+    The float64 values of K and V are made on first use (``k``, ``v``) or
+    per stream (``stream``), so that full-size layers hold raw arrays only."""
 
-    def __init__(self, cfg: K.Config, layer: int = 0):
+    def __init__(self, cfg: K.Config, layer: int = 0, workers: int = 8):
         self.cfg = cfg
         self.layer = layer
-        kv = K.gen_layer(cfg, layer)
+        kv = K.gen_layer(cfg, layer, workers=workers, f64=False)
         self.k_raw, self.v_raw = kv["k"], kv["v"]
-        self.k, self.v = kv["k_f64"], kv["v_f64"]
+        self._k = self._v = None
         (self.wuk, self.wdk), (self.wuv, self.wdv) = K.gen_w(cfg, layer, 0), K.gen_w(cfg, layer, 1)
+
+    @property
+    def k(self) -> np.ndarray:
+        if self._k is None:
+            self._k = K.storage_to_f64(self.k_raw, self.cfg.dtype)
+        return self._k
+
+    @k.setter
+    def k(self, x):
+        self._k = x
+
+    @property
+    def v(self) -> np.ndarray:
+        if self._v is None:
+            self._v = K.storage_to_f64(self.v_raw, self.cfg.dtype)
+        return self._v
+
+    @v.setter
+    def v(self, x):
+        self._v = x
+
+    def stream(self, kv: int, b: int, h: int) -> np.ndarray:
+        """float64 tokens [T][d] of one stream."""
+        if (self._k if kv == 0 else self._v) is not None:
+            return (self._k if kv == 0 else self._v)[b, h]
+        return K.storage_to_f64((self.k_raw if kv == 0 else self.v_raw)[b, h], self.cfg.dtype)
 
     def q(self, step: int) -> K.Stored:
         qs = [K.gen_q(self.cfg, self.layer, b, step) for b in range(self.cfg.batch)]
@@ -144,8 +172,8 @@ def check_layer_compress(inp: Inputs, gc: dict, heads=None, seqs=None, toks=None
     tot = {"tokens": 0, "exempt": 0, "worst_code": 0.0}
     for b in seqs:
         for h in heads:
-            for kv, x, w in ((0, inp.k, inp.wdk), (1, inp.v, inp.wdv)):
-                st = check_stream(x[b, h], cfg.stride, w.f64, cfg.dtype,
+            for kv, w in ((0, inp.wdk), (1, inp.wdv)):
+                st = check_stream(inp.stream(kv, b, h), cfg.stride, w.f64, cfg.dtype,
                                   {n: gc[n][b, h, kv] for n in ("mu", "refs", "idx", "codes")}, toks=toks)
                 tot["tokens"] += st["tokens"]
                 tot["exempt"] += st["exempt"]
