@@ -46,6 +46,46 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# Files whose text fixes the decode split kernel; a stored counter reading is
+# used only while their hash is the one it was taken with.
+SPLIT_SOURCES = ["residual_kv_cache_amd/csrc/decode_mfma.hip", "residual_kv_cache_amd/csrc/dkv_device.h",
+                 "residual_kv_cache_amd/csrc/dkv_internal.h"]
+TRAFFIC_FILE = "profiles/decode_split_llama8b_32k_traffic.txt"
+CALIB_BYTES = 256 << 20
+
+
+def sources_sha256(paths) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(cfg_name: str, splits: int):
+    """HBM bytes per split-kernel launch from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None when the
+    summary is missing, was taken on another workload, or the kernel's
+    sources changed since."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith((" ", "#", "$")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if (kv.get("sources_sha256") != sources_sha256(SPLIT_SOURCES) or kv.get("workload") != cfg_name
+            or kv.get("splits") != str(splits)):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 class Hip:
     """The few HIP runtime calls the benchmark needs (events, graphs)."""
 
@@ -111,15 +151,17 @@ def effective_decode_bytes(cfg) -> int:
 
 def split_kernel_bytes_per_head(cfg, splits: int) -> int:
     """Algorithmic bytes of the split kernel per (sequence, KV head): K and V
-    codes and ordinals, V references, the reference scores and projected
-    queries it reads, and the split partials it writes."""
+    codes and ordinals, V references, the reference-score table (4 floats
+    per reference) and projected queries it reads, each once, and the split
+    partials it writes."""
     e = 2 if cfg.dtype == "bf16" else 4
     R = -(-cfg.seq_len // cfg.stride)
     N = cfg.seq_len - R
     ib = 2 if R <= 65536 else 4
     G = cfg.group
     rec = (2 + cfg.code_dim + cfg.head_dim + 3) // 4 * 4
-    return (2 * N * (cfg.code_dim * e + ib) + R * cfg.head_dim * e + R * G * 4 + G * cfg.code_dim * 4
+    gs = (G + 3) // 4 * 4
+    return (2 * N * (cfg.code_dim * e + ib) + R * cfg.head_dim * e + R * gs * 4 + G * cfg.code_dim * 4
             + splits * G * rec * 4)
 
 
@@ -195,11 +237,14 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="decode splits per head (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--profile", action="store_true",
+                    help="profiling driver for rocprofv3: a calibration copy of 256 MiB, then --steps eager "
+                         "decode steps over the cache replicas; prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the DeltaKV hot path here is a single-GPU build "
-              "(every (sequence, head) stream is independent; see the sharding notes). Run with --gpus 1.",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: this build runs the DeltaKV hot path on a single GPU (every "
+              "(sequence, KV head) stream is independent, so more GPUs would each take their own share of "
+              "sequences or heads). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -222,7 +267,7 @@ def main():
 
     t0 = time.perf_counter()
     log(f"[bench] generating {cfg.name} inputs")
-    kv = K.gen_layer(cfg, 0)
+    kv = K.gen_layer(cfg, 0, workers=16, f64=False)
     k_d, v_d = dev(kv["k"]), dev(kv["v"])
     del kv
     (wuk, wdk), (wuv, wdv) = K.gen_w(cfg, 0, 0), K.gen_w(cfg, 0, 1)
@@ -243,6 +288,19 @@ def main():
     # Eager pass: fill every replica and keep reference outputs for steps 0 and 255.
     for c in caches:
         D.deltakv_compress(lay, k_d, v_d, wdk_d, wdv_d, c, ws_c)
+    if args.profile:
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # calibration: reads and writes CALIB_BYTES once
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            D.deltakv_decode_attn(lay, caches[i % nrep], q_d[i % nsteps], wuk_d, wuv_d, outs[i % nsteps], ws_d,
+                                  n_splits=splits)
+        torch.cuda.synchronize()
+        log(f"[bench] profile driver: calibration copy of {CALIB_BYTES} bytes, {args.steps} decode steps, "
+            f"splits {splits}, {nrep} cache replicas")
+        return
     D.deltakv_decode_attn(lay, caches[0], q_d[0], wuk_d, wuv_d, outs[0], ws_d, n_splits=splits)
     eager0 = outs[0].clone()
     D.deltakv_decode_attn(lay, caches[(nsteps - 1) % nrep], q_d[nsteps - 1], wuk_d, wuv_d, outs[nsteps - 1], ws_d,
@@ -348,10 +406,11 @@ def main():
         "decode_stage_us": {"refscore": round(float(d_stage[:, 0].mean()) * 1e3, 3),
                             "split": round(split_ms * 1e3, 3),
                             "combine": round(float(d_stage[:, 2].mean()) * 1e3, 3)},
-        "roofline": {"kernel": "k_split (decode token stream)", "bound": "hbm",
+        "roofline": {"kernel": "k_split_mfma (decode token stream)", "bound": "hbm",
                      "achieved": round(split_bytes / (split_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(split_bytes / (split_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": split_bytes},
+                     "traffic": stored_traffic(cfg.name, splits), "bytes_per_launch": split_bytes,
+                     "launch_us": round(split_ms * 1e3, 3)},
         "roofline_search": {"kernel": "k_search_mfma", "bound": "mfma",
                             "achieved": round(search_flops / (c_stage[2] * 1e-3) / 1e12, 2),
                             "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
