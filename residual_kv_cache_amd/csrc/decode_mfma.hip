@@ -84,8 +84,9 @@ __device__ __forceinline__ T ldg(const void* base, uint32_t byte_off) {
   return *(const __attribute__((address_space(1))) T*)((GPtr)base + byte_off);
 }
 
-// bf16 {1, 0, 0, 0}: value-code operand of the weight-sum column.
-__device__ const uint16_t kOnePair[4] __attribute__((aligned(16))) = {0x3F80u, 0u, 0u, 0u};
+// bf16 {1, 0, 0, 0}: value-code operand of the weight-sum column (read by
+// lanes past the code columns; 16 bytes so that 16-byte loads may read it).
+__device__ const uint16_t kOnePair[8] __attribute__((aligned(16))) = {0x3F80u, 0u, 0u, 0u, 0x3F80u, 0u, 0u, 0u};
 
 // ---------------------------------------------------------------------------
 // refscore.  Block (bh, chunk) of 256 threads: S rows of kRsRefs references
@@ -160,7 +161,8 @@ struct Tile {
   float sb[4];     // S[ref_K(token 4 q4 + i)][n16 / 4]
   Frag ck[2];      // score A: key code row of token n16 (coded tiles)
   Frag xv[2][2];   // value B [group][half]: tokens 4 q4 + 2 group + {0, 1}
-  Frag bc[2];      // value-code B [group] (+ the 1.0 column)
+  Frag bc[2];      // value-code B [group] (+ the 1.0 column); d_c > 32
+  Frag cv;         // d_c <= 32: the tile's value codes, one 16-byte load per lane
   int cnt;
 };
 
@@ -245,17 +247,29 @@ __device__ __forceinline__ void load_data(const Args& p, const Shape& sh, const 
       const int c = ks * 32 + q4 * 8;
       td.ck[ks] = ldg<Frag>(p.codesK, (ua * dc + (c < dc ? c : 0)) * 2u);
     }
-    // Lanes past the code columns read the 1.0 pair (the lane at column d_c
-    // accumulates the weight sum; the others are never read).
-    const bool in_code = n16 * 4 < dc;
-    const uint16_t* vb = in_code ? p.codesV : kOnePair;
+    if (DCK == 1) {
+      // One 16-byte load per lane covers the tile's value codes: lanes
+      // n16 < 8 load group 0, lanes n16 >= 8 group 1; within a group, lane
+      // c = n16 % 8 loads token 4 q4 + 2 group + (c & 1) at columns
+      // 4 (c & ~1) .. + 7 (compute_tile pairs the lanes up).
+      const int g2 = n16 >> 3, c = n16 & 7;
+      const int col = 4 * (c & ~1);
+      const uint32_t u = ti.base + min(q4 * 4 + 2 * g2 + (c & 1), cnt - 1);
+      const bool in_code = col < dc;
+      td.cv = ldg<Frag>(in_code ? p.codesV : kOnePair, in_code ? (u * dc + col) * 2u : 0u);
+    } else {
+      // Lanes past the code columns read the 1.0 pair (the lane at column
+      // d_c accumulates the weight sum; the others are never read).
+      const bool in_code = n16 * 4 < dc;
+      const uint16_t* vb = in_code ? p.codesV : kOnePair;
 #pragma unroll
-    for (int g2 = 0; g2 < 2; ++g2) {
-      const uint32_t u0 = ti.base + min(q4 * 4 + 2 * g2, cnt - 1);
-      const uint32_t u1 = ti.base + min(q4 * 4 + 2 * g2 + 1, cnt - 1);
-      const U32x2 a = ldg<U32x2>(vb, in_code ? (u0 * dc + n16 * 4) * 2u : 0u);
-      const U32x2 b = ldg<U32x2>(vb, in_code ? (u1 * dc + n16 * 4) * 2u : 0u);
-      td.bc[g2] = Frag{a.x, a.y, b.x, b.y};
+      for (int g2 = 0; g2 < 2; ++g2) {
+        const uint32_t u0 = ti.base + min(q4 * 4 + 2 * g2, cnt - 1);
+        const uint32_t u1 = ti.base + min(q4 * 4 + 2 * g2 + 1, cnt - 1);
+        const U32x2 a = ldg<U32x2>(vb, in_code ? (u0 * dc + n16 * 4) * 2u : 0u);
+        const U32x2 b = ldg<U32x2>(vb, in_code ? (u1 * dc + n16 * 4) * 2u : 0u);
+        td.bc[g2] = Frag{a.x, a.y, b.x, b.y};
+      }
     }
   } else {
     const bool ones = n16 * 4 == dc;
@@ -269,8 +283,35 @@ struct State {
   f32x4 accc;      // value-code accumulators (+ weight sum column)
 };
 
+// DPP lane moves within 16-lane rows: swap neighbours (quad_perm 1,0,3,2)
+// and rotate by 8.
+__device__ __forceinline__ uint32_t swap_pairs(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t ror8(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);
+}
+
+// Value-code B operands of both groups from the one 16-byte load per lane
+// (d_c <= 32): a lane pair (c even, c + 1) holds tokens (a, b) at columns
+// 4c .. 4c + 7; swapping halves gives lane c columns 4c .. 4c + 3 and lane
+// c + 1 columns 4c + 4 .. 4c + 7 of both tokens, and group 1 sits 8 lanes
+// up.  Lanes at or past column d_c get the 1.0 column (only the lane at d_c
+// is read).
+__device__ __forceinline__ void value_code_operands(const Frag& x, int n16, int dc, Frag* bc) {
+  const bool odd = n16 & 1;
+  const uint32_t r0 = swap_pairs(odd ? x.x : x.z), r1 = swap_pairs(odd ? x.y : x.w);
+  const Frag mine = odd ? Frag{r0, r1, x.z, x.w} : Frag{x.x, x.y, r0, r1};
+  const Frag up = Frag{ror8(mine.x), ror8(mine.y), ror8(mine.z), ror8(mine.w)};
+  const bool data = n16 * 4 < dc;
+  const uint32_t one = n16 * 4 == dc ? 0x3F80u : 0u;
+  const Frag ones = Frag{one, 0u, one, 0u};
+  bc[0] = data ? mine : ones;
+  bc[1] = data ? up : ones;
+}
+
 template <bool CODED, int DCK>
-__device__ __forceinline__ void compute_tile(const Tile& td, const Frag* qh, const Frag* ql, int q4,
+__device__ __forceinline__ void compute_tile(const Tile& td, const Frag* qh, const Frag* ql, int n16, int q4, int dc,
                                              const uint32_t* sel, State& st) {
   float s[4] = {td.sb[0], td.sb[1], td.sb[2], td.sb[3]};
   if (CODED) {
@@ -297,6 +338,8 @@ __device__ __forceinline__ void compute_tile(const Tile& td, const Frag* qh, con
     st.accr[1] *= aa;
     st.accc *= aa;
   }
+  Frag bc[2] = {td.bc[0], td.bc[1]};
+  if (CODED && DCK == 1) value_code_operands(td.cv, n16, dc, bc);
   float p[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(s[i] - st.m);
@@ -314,8 +357,8 @@ __device__ __forceinline__ void compute_tile(const Tile& td, const Frag* qh, con
     st.accr[0] = mfma16(al, td.xv[g2][0], st.accr[0]);
     st.accr[1] = mfma16(ah, td.xv[g2][1], st.accr[1]);
     st.accr[1] = mfma16(al, td.xv[g2][1], st.accr[1]);
-    st.accc = mfma16(ah, td.bc[g2], st.accc);
-    st.accc = mfma16(al, td.bc[g2], st.accc);
+    st.accc = mfma16(ah, bc[g2], st.accc);
+    st.accc = mfma16(al, bc[g2], st.accc);
   }
 }
 
@@ -337,12 +380,12 @@ __device__ __forceinline__ void run_tiles(const Args& p, const Shape& sh, const 
     load_idx<CODED, IdxT>(p, tt + 2, t1, first, last, n16, q4, ia);
     load_data<CODED, DCK, SLDS>(p, sh, s_lds, ib, n16, q4, db);
     __builtin_amdgcn_sched_barrier(0);
-    compute_tile<CODED, DCK>(da, qh, ql, q4, sel, st);
+    compute_tile<CODED, DCK>(da, qh, ql, n16, q4, sh.dc, sel, st);
     __builtin_amdgcn_sched_barrier(0);
     load_idx<CODED, IdxT>(p, tt + 3, t1, first, last, n16, q4, ib);
     load_data<CODED, DCK, SLDS>(p, sh, s_lds, ia, n16, q4, da);
     __builtin_amdgcn_sched_barrier(0);
-    compute_tile<CODED, DCK>(db, qh, ql, q4, sel, st);
+    compute_tile<CODED, DCK>(db, qh, ql, n16, q4, sh.dc, sel, st);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
