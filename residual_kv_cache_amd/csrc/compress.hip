@@ -49,6 +49,14 @@ __device__ __forceinline__ void load8(const float* p, float* out) {
   out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pk_bf16_rn(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 struct StreamId {
   int b, h, kv;
 };
@@ -148,32 +156,38 @@ __global__ __launch_bounds__(256) void k_center_refs(CompressArgs a, Shape sh) {
 // ---------------------------------------------------------------------------
 // Reference search, bfloat16 storage, MFMA.
 //
-// Block = 4 waves = 256 consecutive positions of one stream; wave w owns 64
-// of them (4 MFMA N-tiles of 16 tokens).  The centred tokens x~_t are built
+// Block = 8 waves = 256 consecutive positions of one stream; wave w owns 32
+// of them (2 MFMA N-tiles of 16 tokens).  The centred tokens x~_t are built
 // once in registers as MFMA B operands (exact bf16).  References stream
-// through LDS in chunks of 64 (4 M-tiles of 16); each M-tile x N-tile block
-// of cosines is an MFMA 16x16x32 chain over the head dim.  The C fragment of
-// lane l holds references 4*(l/16)+i (i = 0..3) for token l%16, so each lane
-// keeps a running best (score, ordinal) per N-tile and sees its references
-// in increasing order; a strict '>' keeps the lowest ordinal on ties.  The
-// four lane groups that share a token merge at the end (larger score, then
-// lower ordinal).  Scores are <x~_t, x~_r> / ||x~_r||: the token's own norm
-// is the same for every candidate and does not change the argmax.
+// through LDS in double-buffered chunks of 64 (4 M-tiles of 16; the next
+// chunk is fetched into registers while the current one is used); each
+// M-tile x N-tile block of scores is an MFMA 16x16x32 chain over the head
+// dim.  The C fragment of lane l holds references 4*(l/16)+i (i = 0..3) for
+// token l%16.  Scores are <x~_t, x~_r> / ||x~_r||: the token's own norm is
+// the same for every candidate and does not change the argmax.  Each score
+// becomes an integer selection key (see below) so that a lane's running
+// best is one max instruction per score; the four lane groups that share a
+// token merge at the end (larger key, then lower ordinal).
 // ---------------------------------------------------------------------------
 
 constexpr int kSearchRefs = 64;   // references per LDS chunk
-constexpr int kSearchTok = 256;   // positions per block
+constexpr int kSearchWaves = 8;
+constexpr int kSearchNT = 2;                    // 16-token MFMA tiles per wave
+constexpr int kSearchThreads = 64 * kSearchWaves;
+constexpr int kSearchTok = 16 * kSearchNT * kSearchWaves;   // positions per block
 
 template <int D>
-__global__ __launch_bounds__(256) void k_search_mfma(CompressArgs a, Shape sh) {
+__global__ __launch_bounds__(kSearchThreads) void k_search_mfma(CompressArgs a, Shape sh) {
   constexpr int KS = D / 32;      // MFMA K-steps over the head dim
   constexpr int LDR = D + 8;      // padded LDS row (elements)
-  __shared__ __attribute__((aligned(16))) uint16_t lds_ref[kSearchRefs * LDR];
-  __shared__ float lds_inv[kSearchRefs];
+  constexpr int PER = kSearchRefs * (D / 8) / kSearchThreads;   // 16-byte pieces per thread per chunk
+  __shared__ __attribute__((aligned(16))) uint16_t lds_ref[2][kSearchRefs * LDR];
+  __shared__ float lds_inv[2][kSearchRefs];
 
   const int stream = blockIdx.y;
   const int tile = gridDim.x - 1 - blockIdx.x;   // heavy (late) tiles first
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lrow = lane & 15, lgrp = lane >> 4;
   const StreamId id = decode_stream(stream, sh.H);
   const uint16_t* src = stream_src<BF16>(a, id);
@@ -182,111 +196,155 @@ __global__ __launch_bounds__(256) void k_search_mfma(CompressArgs a, Shape sh) {
   const float* inv_n = a.inv_n + (size_t)stream * sh.R;
 
   const int tb = tile * kSearchTok;
-  const int tw = tb + wave * 64;
+  const int tw = tb + wave * 16 * kSearchNT;
   // References any position of the block / wave may use: r*s < t.
   const int tmax_b = min(sh.T - 1, tb + kSearchTok - 1);
   const int rend_b = (tmax_b + sh.s - 1) / sh.s;
-  const int tmax_w = min(sh.T - 1, tw + 63);
+  const int tmax_w = min(sh.T - 1, tw + 16 * kSearchNT - 1);
   const int rend_w = tw < sh.T ? (tmax_w + sh.s - 1) / sh.s : 0;
+  const int nchunks = (rend_b + kSearchRefs - 1) / kSearchRefs;
 
-  // B operands: centred tokens, [N-tile][K-step].
-  bf16x8 bt[4][KS];
+  // Chunk staging: global -> registers (one chunk ahead) -> LDS.
+  uint4 pre[PER];
+  float pinv = 0.f;
+  auto fetch = [&](int ch) {
+    const int rc = ch * kSearchRefs;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int p = tid + j * kSearchThreads;
+      const int row = p / (D / 8), col = (p % (D / 8)) * 8;
+      pre[j] = rc + row < rend_b ? *reinterpret_cast<const uint4*>(refs + (size_t)(rc + row) * D + col)
+                                 : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < kSearchRefs) pinv = rc + tid < rend_b ? inv_n[rc + tid] : 0.f;
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int p = tid + j * kSearchThreads;
+      const int row = p / (D / 8), col = (p % (D / 8)) * 8;
+      *reinterpret_cast<uint4*>(&lds_ref[buf][row * LDR + col]) = pre[j];
+    }
+    if (tid < kSearchRefs) lds_inv[buf][tid] = pinv;
+  };
+  if (nchunks > 0) fetch(0);
+
+  // B operands: centred tokens, [N-tile][K-step].  x - mu of two bf16
+  // values is exact in fp32 or too far from a bf16 tie to round
+  // differently, so one fp32 subtraction and one rounding give rnd(x - mu).
+  bf16x8 bt[kSearchNT][KS];
+  float n2[kSearchNT] = {};
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const int c = ks * 32 + lgrp * 8;
     float m[8];
     load8(mu + c, m);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < kSearchNT; ++nt) {
       const int t = tw + nt * 16 + lrow;
-      union { bf16x8 v; uint16_t u[8]; } p;
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
       if (t < sh.T) {
         float x[8];
         load8(src + (int64_t)t * a.st + c, x);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) p.u[e] = bf16_sub_rn(x[e], m[e]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) p.u[e] = 0;
+        for (int e = 0; e < 4; ++e) {
+          w[e] = pk_bf16_rn(x[2 * e] - m[2 * e], x[2 * e + 1] - m[2 * e + 1]);
+          const float lo = __uint_as_float(w[e] << 16), hi = __uint_as_float(w[e] & 0xFFFF0000u);
+          n2[nt] = fmaf(lo, lo, fmaf(hi, hi, n2[nt]));
+        }
       }
-      bt[nt][ks] = p.v;
+      bt[nt][ks] = __builtin_bit_cast(bf16x8, w);
     }
   }
-
-  float best[4];
-  int bidx[4];
+  // Selection keys.  A candidate's score <x~_t, x~_r> / ||x~_r|| lies in
+  // [-||x~_t||, ||x~_t||]; adding off = 2 ||x~_t|| (+ a tiny constant, so that
+  // keys of a zero token stay positive) makes every key a positive float, so
+  // keys order as unsigned integers.  The low 4 bits of a key are replaced by
+  // 15 - (4 mt + i), the candidate's place in its 64-reference chunk, so an
+  // integer max picks the best score and, among equal scores, the lowest
+  // ordinal; the change is below 2^-19 relative to the key, far inside the
+  // 1e-4 cosine margin within which any near-best reference is accepted.
+  // Across chunks a lane keeps the earlier chunk unless the new chunk's key
+  // is strictly larger above those 4 bits.
+  float off[kSearchNT];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) { best[nt] = -INFINITY; bidx[nt] = 0; }
+  for (int nt = 0; nt < kSearchNT; ++nt) {
+    float v = n2[nt];
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    off[nt] = 2.0f * sqrtf(v) + 1e-30f;
+  }
+  uint32_t bkey[kSearchNT] = {};
+  int bch[kSearchNT] = {};
 
-  const int nchunks = (rend_b + kSearchRefs - 1) / kSearchRefs;
+  if (nchunks > 0) stash(0);
+  __syncthreads();
   for (int ch = 0; ch < nchunks; ++ch) {
     const int rc = ch * kSearchRefs;
-    __syncthreads();
-    // Stage 64 references (16 B per thread per step) and their inverse norms.
-    for (int p = threadIdx.x; p < kSearchRefs * (D / 8); p += 256) {
-      const int row = p / (D / 8), col = (p % (D / 8)) * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (rc + row < rend_b) v = *reinterpret_cast<const uint4*>(refs + (size_t)(rc + row) * D + col);
-      *reinterpret_cast<uint4*>(&lds_ref[row * LDR + col]) = v;
-    }
-    if (threadIdx.x < kSearchRefs) {
-      const int r = rc + threadIdx.x;
-      lds_inv[threadIdx.x] = r < rend_b ? inv_n[r] : 0.f;
-    }
-    __syncthreads();
-    if (rc >= rend_w) continue;
-#pragma unroll 1
-    for (int mt = 0; mt < kSearchRefs / 16; ++mt) {
-      const int rbase = rc + mt * 16;
-      if (rbase >= rend_w) break;
-      bf16x8 ar[KS];
+    const int buf = ch & 1;
+    if (ch + 1 < nchunks) fetch(ch + 1);
+    if (rc < rend_w) {
+      uint32_t ckey[kSearchNT] = {};
+      const int nmt = min(kSearchRefs / 16, (rend_w - rc + 15) / 16);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        ar[ks] = *reinterpret_cast<const bf16x8*>(&lds_ref[(mt * 16 + lrow) * LDR + ks * 32 + lgrp * 8]);
-      f32x4 acc[4];
+      for (int mt = 0; mt < kSearchRefs / 16; ++mt) {
+        if (mt < nmt) {
+          const int rbase = rc + mt * 16;
+          bf16x8 ar[KS];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int ks = 0; ks < KS; ++ks)
+            ar[ks] = *reinterpret_cast<const bf16x8*>(&lds_ref[buf][(mt * 16 + lrow) * LDR + ks * 32 + lgrp * 8]);
+          f32x4 acc[kSearchNT];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+          for (int nt = 0; nt < kSearchNT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar[ks], bt[nt][ks], acc[nt], 0, 0, 0);
-      float inv[4];
+          for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) inv[i] = lds_inv[mt * 16 + lgrp * 4 + i];
-      const int r0 = rbase + lgrp * 4;
-      // A tile needs the causal mask when its last reference is not earlier
-      // than the wave's first position.
-      if ((rbase + 15) * sh.s >= tw) {
+            for (int nt = 0; nt < kSearchNT; ++nt)
+              acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar[ks], bt[nt][ks], acc[nt], 0, 0, 0);
+          float inv[4];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const int t = tw + nt * 16 + lrow;
+          for (int i = 0; i < 4; ++i) inv[i] = lds_inv[buf][mt * 16 + lgrp * 4 + i];
+          // A tile needs the causal mask when its last reference is not
+          // earlier than the wave's first position.
+          const bool masked = (rbase + 15) * sh.s >= tw;
+          const int r0 = rbase + lgrp * 4;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float sc = acc[nt][i] * inv[i];
-            if ((r0 + i) * sh.s < t && sc > best[nt]) { best[nt] = sc; bidx[nt] = r0 + i; }
+          for (int nt = 0; nt < kSearchNT; ++nt) {
+            const int t = tw + nt * 16 + lrow;
+            uint32_t k[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              k[i] = (__float_as_uint(fmaf(acc[nt][i], inv[i], off[nt])) & ~15u) | (uint32_t)(15 - (4 * mt + i));
+            if (masked) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) k[i] = (r0 + i) * sh.s < t ? k[i] : 0u;
+            }
+            ckey[nt] = max(max(max(k[0], k[1]), max(k[2], k[3])), ckey[nt]);
           }
         }
-      } else {
+      }
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float sc = acc[nt][i] * inv[i];
-            if (sc > best[nt]) { best[nt] = sc; bidx[nt] = r0 + i; }
-          }
+      for (int nt = 0; nt < kSearchNT; ++nt) {
+        const bool g = (ckey[nt] & ~15u) > (bkey[nt] & ~15u);
+        bkey[nt] = g ? ckey[nt] : bkey[nt];
+        bch[nt] = g ? ch : bch[nt];
       }
     }
+    if (ch + 1 < nchunks) stash(buf ^ 1);
+    __syncthreads();
   }
 
-  // Merge the four lane groups of each token; lanes 0..15 write.
+  // Merge the four lane groups of each token (larger key above the place
+  // bits, then lower ordinal); lanes 0..15 write.
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    float v = best[nt];
-    int r = bidx[nt];
+  for (int nt = 0; nt < kSearchNT; ++nt) {
+    const int q = 15 - (int)(bkey[nt] & 15u);
+    uint32_t v = bkey[nt] & ~15u;
+    int r = bch[nt] * kSearchRefs + (q >> 2) * 16 + lgrp * 4 + (q & 3);
 #pragma unroll
     for (int o = 16; o <= 32; o <<= 1) {
-      const float v2 = __shfl_xor(v, o, 64);
+      const uint32_t v2 = (uint32_t)__shfl_xor((int)v, o, 64);
       const int r2 = __shfl_xor(r, o, 64);
       if (v2 > v || (v2 == v && r2 < r)) { v = v2; r = r2; }
     }
@@ -464,7 +522,7 @@ hipError_t launch_compress_d(const Shape& sh, const CompressArgs& a, hipStream_t
     DKV_TRY(launch(k_mean_final<BF16>, ns, 128, st, nullptr, ev_stop(ev, 0), a, sh, chunks));
     DKV_TRY(launch(k_center_refs<BF16>, g_ref, 256, st, ev_start(ev, 1), ev_stop(ev, 1), a, sh));
     if (sh.N > 0) {
-      DKV_TRY(launch(k_search_mfma<D>, g_search, 256, st, ev_start(ev, 2), ev_stop(ev, 2), a, sh));
+      DKV_TRY(launch(k_search_mfma<D>, g_search, kSearchThreads, st, ev_start(ev, 2), ev_stop(ev, 2), a, sh));
       DKV_TRY(launch(k_encode_mfma<D>, g_enc, 256, st, ev_start(ev, 3), ev_stop(ev, 3), a, sh));
     }
   } else {

@@ -38,17 +38,14 @@ __device__ __forceinline__ float to_odd(float a, float err) {
   return __uint_as_float(u);
 }
 
-// Correctly rounded bfloat16(x - y) for bfloat16-valued x and y.  The
-// float32 difference and its exact error come from the TwoSum
-// transformation; rounding to odd then to bf16 gives the correct result
-// even where the float32 subtraction itself is inexact.
-__device__ __forceinline__ uint16_t bf16_sub_rn(float x, float y) {
-  float a = x - y;
-  float bv = a - x;
-  float av = a - bv;
-  float err = (x - av) + (-y - bv);
-  return f2bf(to_odd(a, err));
-}
+// Correctly rounded bfloat16(x - y) for bfloat16-valued x and y.  When the
+// exponents of x and y differ by at most 15, x - y has at most 24
+// significant bits and the float32 subtraction is exact.  Otherwise the
+// smaller operand is below 2^-15 of the larger one's leading bit, so both the
+// exact and the float32 difference lie within 2^-8 of a bfloat16 ulp of the
+// larger operand, which is itself a bfloat16 value, and round to it.  Either
+// way one float32 subtraction and one rounding give the correct result.
+__device__ __forceinline__ uint16_t bf16_sub_rn(float x, float y) { return f2bf(x - y); }
 
 // Correctly rounded bfloat16 of a double.
 __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
