@@ -111,20 +111,38 @@ __global__ __launch_bounds__(256) void k_mean_partial(CompressArgs a, Shape sh) 
   }
 }
 
-// Mean: stage 2, fixed-order total, divide, round once.  grid streams, block d.
+// Mean: stage 2, fixed-order total, divide, round once.  grid streams,
+// block 256: thread (g, i) sums chunks g, g + G, ... of column i
+// (G = 256 / d groups, loads issued 8 at a time), then the G partial sums
+// are added in group order.
 template <class S>
-__global__ __launch_bounds__(128) void k_mean_final(CompressArgs a, Shape sh, int chunks) {
+__global__ __launch_bounds__(256) void k_mean_final(CompressArgs a, Shape sh, int chunks) {
+  __shared__ double part[256];
   const int stream = blockIdx.x;
-  const int i = threadIdx.x;
-  if (i >= sh.d) return;
+  const int i = threadIdx.x % sh.d, g = threadIdx.x / sh.d, G = 256 / sh.d;
   typename S::T* mu = (typename S::T*)a.mu;
   if (a.mu_in) {
-    mu[(size_t)stream * sh.d + i] = ((const typename S::T*)a.mu_in)[(size_t)stream * sh.d + i];
+    if (g == 0) mu[(size_t)stream * sh.d + i] = ((const typename S::T*)a.mu_in)[(size_t)stream * sh.d + i];
     return;
   }
+  const double* src = a.mean_part + (size_t)stream * chunks * sh.d + i;
   double s = 0.0;
-  for (int c = 0; c < chunks; ++c) s += a.mean_part[((size_t)stream * chunks + c) * sh.d + i];
-  mu[(size_t)stream * sh.d + i] = S::from_f64(s / (double)sh.T);
+  int c = g;
+  for (; c + 7 * G < chunks; c += 8 * G) {
+    double v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = src[(size_t)(c + k * G) * sh.d];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += v[k];
+  }
+  for (; c < chunks; c += G) s += src[(size_t)c * sh.d];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  if (g == 0) {
+    double t = 0.0;
+    for (int k = 0; k < G; ++k) t += part[k * sh.d + i];
+    mu[(size_t)stream * sh.d + i] = S::from_f64(t / (double)sh.T);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -410,16 +428,19 @@ __global__ __launch_bounds__(256) void k_search_f32(CompressArgs a, Shape sh) {
 // Encode, bfloat16 storage, MFMA.
 //
 // grid (ceil(N/64), streams), block 256: wave w encodes coded rows
-// 64*blockIdx.x + 16*w + (0..15).  A = W_down rows (M = code elements),
-// B = residuals of 16 tokens (N), K = head dim.  The fp32 residual
-// delta = (k - mu) - ref is split into three bf16 parts hi + mid + lo that
-// sum to it within 2^-24 relative, so three MFMA passes reproduce the fp32
-// projection; the code is rounded once to bf16.
+// 64*blockIdx.x + 16*w + (0..15).  A = W_down rows (M = code elements, from
+// LDS), B = residuals of 16 tokens (N), K = head dim.  The fp32 residual
+// delta = (k - mu) - ref is split into bf16 parts hi + lo, which hold it to
+// 16 significant bits; two MFMA passes give the projection to about 2^-16
+// relative, far below the final rounding of the code to bf16 (2^-9).
 // ---------------------------------------------------------------------------
+
 
 template <int D>
 __global__ __launch_bounds__(256) void k_encode_mfma(CompressArgs a, Shape sh) {
   constexpr int KS = D / 32;
+  constexpr int LDW = D + 8;          // padded LDS row of W_down
+  extern __shared__ __attribute__((aligned(16))) uint16_t w_lds[];   // [d_c][LDW]
   const int stream = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int lrow = lane & 15, lgrp = lane >> 4;
@@ -435,46 +456,47 @@ __global__ __launch_bounds__(256) void k_encode_mfma(CompressArgs a, Shape sh) {
   const int t = valid ? slot_to_pos(n, sh.s) : 0;
   const int r = valid ? min((int)load_idx(a.idx, (size_t)stream * sh.N + n, sh.idx_bytes), sh.R - 1) : 0;
 
-  bf16x8 bh[KS], bm[KS], bl[KS];
+  for (int p = threadIdx.x; p < sh.dc * (D / 8); p += 256) {
+    const int row = p / (D / 8), col = (p % (D / 8)) * 8;
+    *reinterpret_cast<uint4*>(&w_lds[row * LDW + col]) = *reinterpret_cast<const uint4*>(wd + (size_t)row * D + col);
+  }
+
+  bf16x8 bh[KS], bl[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const int c = ks * 32 + lgrp * 8;
-    union { bf16x8 v; uint16_t u[8]; } ph, pm, pl;
+    uint32_t wh[4] = {0u, 0u, 0u, 0u}, wl[4] = {0u, 0u, 0u, 0u};
     if (valid) {
       float x[8], m[8], rf[8];
       load8(src + (int64_t)t * a.st + c, x);
       load8(mu + c, m);
       load8(refs + (size_t)r * D + c, rf);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float dlt = (x[e] - m[e]) - rf[e];
-        const uint16_t h = f2bf(dlt);
-        const float r1 = dlt - bf2f(h);
-        const uint16_t md = f2bf(r1);
-        const float r2 = r1 - bf2f(md);
-        ph.u[e] = h; pm.u[e] = md; pl.u[e] = f2bf(r2);
+      for (int e = 0; e < 4; ++e) {
+        const float d0 = (x[2 * e] - m[2 * e]) - rf[2 * e];
+        const float d1 = (x[2 * e + 1] - m[2 * e + 1]) - rf[2 * e + 1];
+        wh[e] = pk_bf16_rn(d0, d1);
+        wl[e] = pk_bf16_rn(d0 - __uint_as_float(wh[e] << 16), d1 - __uint_as_float(wh[e] & 0xFFFF0000u));
       }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { ph.u[e] = 0; pm.u[e] = 0; pl.u[e] = 0; }
     }
-    bh[ks] = ph.v; bm[ks] = pm.v; bl[ks] = pl.v;
+    bh[ks] = __builtin_bit_cast(bf16x8, wh);
+    bl[ks] = __builtin_bit_cast(bf16x8, wl);
   }
+  __syncthreads();
 
   for (int mt = 0; mt < sh.dc / 16; ++mt) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 aw = *reinterpret_cast<const bf16x8*>(wd + (size_t)(mt * 16 + lrow) * D + ks * 32 + lgrp * 8);
+      const bf16x8 aw = *reinterpret_cast<const bf16x8*>(&w_lds[(mt * 16 + lrow) * LDW + ks * 32 + lgrp * 8]);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bl[ks], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bm[ks], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bh[ks], acc, 0, 0, 0);
     }
     // Lane l holds code elements mt*16 + 4*(l/16) + (0..3) of row l%16.
     if (valid) {
       uint2 o;
-      o.x = (uint32_t)f2bf(acc[0]) | ((uint32_t)f2bf(acc[1]) << 16);
-      o.y = (uint32_t)f2bf(acc[2]) | ((uint32_t)f2bf(acc[3]) << 16);
+      o.x = pk_bf16_rn(acc[0], acc[1]);
+      o.y = pk_bf16_rn(acc[2], acc[3]);
       *reinterpret_cast<uint2*>(codes + (size_t)n * sh.dc + mt * 16 + lgrp * 4) = o;
     }
   }
@@ -519,15 +541,16 @@ hipError_t launch_compress_d(const Shape& sh, const CompressArgs& a, hipStream_t
   if ((e = (x)) != hipSuccess) return e
   if (sh.bf16) {
     DKV_TRY(launch(k_mean_partial<BF16>, g_mean, 256, st, ev_start(ev, 0), nullptr, a, sh));
-    DKV_TRY(launch(k_mean_final<BF16>, ns, 128, st, nullptr, ev_stop(ev, 0), a, sh, chunks));
+    DKV_TRY(launch(k_mean_final<BF16>, ns, 256, st, nullptr, ev_stop(ev, 0), a, sh, chunks));
     DKV_TRY(launch(k_center_refs<BF16>, g_ref, 256, st, ev_start(ev, 1), ev_stop(ev, 1), a, sh));
     if (sh.N > 0) {
       DKV_TRY(launch(k_search_mfma<D>, g_search, kSearchThreads, st, ev_start(ev, 2), ev_stop(ev, 2), a, sh));
-      DKV_TRY(launch(k_encode_mfma<D>, g_enc, 256, st, ev_start(ev, 3), ev_stop(ev, 3), a, sh));
+      DKV_TRY(launch_lds(k_encode_mfma<D>, g_enc, 256, (size_t)sh.dc * (D + 8) * 2, st, ev_start(ev, 3),
+                         ev_stop(ev, 3), a, sh));
     }
   } else {
     DKV_TRY(launch(k_mean_partial<F32>, g_mean, 256, st, ev_start(ev, 0), nullptr, a, sh));
-    DKV_TRY(launch(k_mean_final<F32>, ns, 128, st, nullptr, ev_stop(ev, 0), a, sh, chunks));
+    DKV_TRY(launch(k_mean_final<F32>, ns, 256, st, nullptr, ev_stop(ev, 0), a, sh, chunks));
     DKV_TRY(launch(k_center_refs<F32>, g_ref, 256, st, ev_start(ev, 1), ev_stop(ev, 1), a, sh));
     if (sh.N > 0) {
       DKV_TRY(launch(k_search_f32<D>, g_search32, 256, st, ev_start(ev, 2), ev_stop(ev, 2), a, sh));
