@@ -57,6 +57,24 @@ __device__ __forceinline__ uint32_t pk_bf16_rn(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
+// XCD-aware block order: block L runs on XCD L % 8 (workgroups are
+// dispatched to the eight XCDs round-robin).  Streams x, x + 8, ... are
+// given to XCD x, so the references a stream re-reads stay in one L2; within
+// an XCD, work items go in the given order across its streams.
+struct XcdItem {
+  int stream, item;   // stream < 0: no work
+};
+__device__ __forceinline__ XcdItem xcd_item(int ns) {
+  const int per = (ns + 7) / 8;
+  const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
+  XcdItem r;
+  r.stream = xcd + 8 * (k % per);
+  r.item = k / per;
+  if (r.stream >= ns) r.stream = -1;
+  return r;
+}
+inline unsigned xcd_grid(int ns, int items) { return 8u * (unsigned)((ns + 7) / 8) * (unsigned)items; }
+
 struct StreamId {
   int b, h, kv;
 };
@@ -202,8 +220,10 @@ __global__ __launch_bounds__(kSearchThreads) void k_search_mfma(CompressArgs a, 
   __shared__ __attribute__((aligned(16))) uint16_t lds_ref[2][kSearchRefs * LDR];
   __shared__ float lds_inv[2][kSearchRefs];
 
-  const int stream = blockIdx.y;
-  const int tile = gridDim.x - 1 - blockIdx.x;   // heavy (late) tiles first
+  const XcdItem xi = xcd_item(sh.n_streams());
+  if (xi.stream < 0) return;
+  const int stream = xi.stream;
+  const int tile = (sh.T + kSearchTok - 1) / kSearchTok - 1 - xi.item;   // heavy (late) tiles first
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lrow = lane & 15, lgrp = lane >> 4;
@@ -441,7 +461,9 @@ __global__ __launch_bounds__(256) void k_encode_mfma(CompressArgs a, Shape sh) {
   constexpr int KS = D / 32;
   constexpr int LDW = D + 8;          // padded LDS row of W_down
   extern __shared__ __attribute__((aligned(16))) uint16_t w_lds[];   // [d_c][LDW]
-  const int stream = blockIdx.y;
+  const XcdItem xi = xcd_item(sh.n_streams());
+  if (xi.stream < 0) return;
+  const int stream = xi.stream;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int lrow = lane & 15, lgrp = lane >> 4;
   const StreamId id = decode_stream(stream, sh.H);
@@ -451,7 +473,7 @@ __global__ __launch_bounds__(256) void k_encode_mfma(CompressArgs a, Shape sh) {
   const uint16_t* wd = (const uint16_t*)(id.kv ? a.wdv : a.wdk) + (size_t)id.h * a.w_hs;
   uint16_t* codes = (uint16_t*)a.codes + (size_t)stream * sh.N * sh.dc;
 
-  const int n = blockIdx.x * 64 + wave * 16 + lrow;   // this lane's coded row
+  const int n = xi.item * 64 + wave * 16 + lrow;   // this lane's coded row
   const bool valid = n < sh.N;
   const int t = valid ? slot_to_pos(n, sh.s) : 0;
   const int r = valid ? min((int)load_idx(a.idx, (size_t)stream * sh.N + n, sh.idx_bytes), sh.R - 1) : 0;
@@ -533,8 +555,8 @@ hipError_t launch_compress_d(const Shape& sh, const CompressArgs& a, hipStream_t
   const int ns = sh.n_streams();
   const int chunks = mean_chunks(sh);
   const dim3 g_mean(chunks, ns), g_ref((sh.R + 3) / 4, ns);
-  const dim3 g_search((sh.T + kSearchTok - 1) / kSearchTok, ns), g_search32((sh.T + 255) / 256, ns);
-  const dim3 g_enc((sh.N + 63) / 64, ns), g_enc32((sh.N + 255) / 256, ns);
+  const dim3 g_search(xcd_grid(ns, (sh.T + kSearchTok - 1) / kSearchTok)), g_search32((sh.T + 255) / 256, ns);
+  const dim3 g_enc(xcd_grid(ns, (sh.N + 63) / 64)), g_enc32((sh.N + 255) / 256, ns);
   void* const* ev = a.events;
   hipError_t e;
 #define DKV_TRY(x) \
