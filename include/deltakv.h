@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define DKV_ABI_VERSION 1u
+#define DKV_ABI_VERSION 2u
 
 typedef enum dkv_status {
   DKV_OK = 0,
@@ -83,10 +83,16 @@ typedef enum dkv_dtype {
  *   head_dim     d; supported: 64 or 128
  *   code_dim     d_c; supported: a multiple of 16 with 16 <= d_c <= d
  *   stride       s >= 1 (s = 1 stores every token whole)
- *   idx_bytes    width of a stored reference ordinal: 2 (requires R <= 65536)
- *                or 4
- *   n_kv_heads   H >= 1;  batch  B >= 1;  seq_len  T >= 1
- * Derived: R = ceil(T / s) references, N = T - R coded tokens per stream.
+ *   idx_bytes    width of a stored reference ordinal: 2 (requires
+ *                R_cap <= 65536) or 4
+ *   n_kv_heads   H >= 1;  batch  B >= 1
+ *   seq_len      T >= 1, tokens held in the cache
+ *   capacity     tokens the arrays are sized for (T_cap >= T), so that
+ *                tokens can be appended in place; 0 means T_cap = T
+ * Derived: R = ceil(T / s) references and N = T - R coded tokens per stream
+ * are held; the arrays are laid out for R_cap = ceil(T_cap / s) and
+ * N_cap = T_cap - R_cap (a cache's layout is fixed by T_cap, so a layout
+ * with a larger seq_len and the same capacity describes the same buffer).
  */
 typedef struct dkv_layout {
   uint32_t abi_version;
@@ -98,19 +104,21 @@ typedef struct dkv_layout {
   uint32_t n_kv_heads;
   uint32_t batch;
   uint32_t seq_len;
-  uint32_t reserved; /* must be 0 */
+  uint32_t capacity;
 } dkv_layout;
 
 /*
  * Device pointers of a compressed cache.  All arrays are dense, row-major,
  * indexed [b][h][kv][...] with kv = 0 for K and 1 for V:
- *   refs   [B][H][2][R][d]    storage dtype: x~ of the reference tokens
- *   codes  [B][H][2][N][d_c]  storage dtype: one row per non-reference token
- *                             in position order; token t (t mod s != 0)
- *                             sits in row t - floor(t / s) - 1
- *   idx    [B][H][2][N]       uint16 or uint32 (idx_bytes): reference
- *                             ordinal r of each row (the token at r*s)
- *   mu     [B][H][2][d]       storage dtype: the shared component
+ *   refs   [B][H][2][R_cap][d]    storage dtype: x~ of the reference tokens
+ *                                 (rows 0 .. R-1 in use)
+ *   codes  [B][H][2][N_cap][d_c]  storage dtype: one row per non-reference
+ *                                 token in position order; token t
+ *                                 (t mod s != 0) sits in row
+ *                                 t - floor(t / s) - 1 (rows 0 .. N-1 in use)
+ *   idx    [B][H][2][N_cap]       uint16 or uint32 (idx_bytes): reference
+ *                                 ordinal r of each row (the token at r*s)
+ *   mu     [B][H][2][d]           storage dtype: the shared component
  * Each pointer must be 16-byte aligned.
  */
 typedef struct dkv_cache {
@@ -185,6 +193,24 @@ typedef struct dkv_decode_in {
   void* const* stage_events;
 } dkv_decode_in;
 
+/*
+ * Inputs of deltakv_append (one new token per sequence, at position seq_len).
+ *   k, v       device; element (b, h, i) of the new K token is at
+ *              k[b*stride_b + h*stride_h + i] (elements, storage dtype); the
+ *              same strides apply to v; the head_dim elements are contiguous
+ *              and 16-byte aligned
+ *   w_down_k, w_down_v, w_head_stride  as in dkv_compress_in
+ */
+typedef struct dkv_append_in {
+  const void* k;
+  const void* v;
+  int64_t stride_b;
+  int64_t stride_h;
+  const void* w_down_k;
+  const void* w_down_v;
+  int64_t w_head_stride;
+} dkv_append_in;
+
 /* DKV_ABI_VERSION of the loaded library. */
 uint32_t dkv_abi_version(void);
 
@@ -222,6 +248,24 @@ size_t dkv_decode_workspace_bytes(const dkv_layout* layout, uint32_t n_q_heads, 
  */
 dkv_status deltakv_compress(const dkv_layout* layout, const dkv_compress_in* in, const dkv_cache* cache,
                             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Appends the token at position T = layout->seq_len of every sequence to a
+ * cache that holds T tokens, in place: with the shared component mu kept
+ * as it is in the cache, a token with T mod s = 0 becomes reference T / s;
+ * any other token is searched against the references r with r*s < T and
+ * stored as its ordinal and code in row T - floor(T / s) - 1, exactly as
+ * deltakv_compress of the T + 1 tokens with mu_in = mu would store it (the
+ * same readings; DeltaKV explainer, English page, Technical Summary §3
+ * "Strided Reference Selection", which retrieves references for each new
+ * token).  Requires T + 1 <= capacity; the caller then describes the cache
+ * with seq_len = T + 1.  Writes only that token's row of refs, or of codes
+ * and idx.  `ws` as for deltakv_compress, of at least
+ * dkv_append_workspace_bytes(layout) bytes (0 bytes: `ws` may be NULL).
+ */
+size_t dkv_append_workspace_bytes(const dkv_layout* layout);
+dkv_status deltakv_append(const dkv_layout* layout, const dkv_append_in* in, const dkv_cache* cache, void* ws,
+                          size_t ws_bytes, void* stream);
 
 /*
  * Decode attention of one query per sequence over a compressed cache, as if

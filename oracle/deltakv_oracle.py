@@ -268,6 +268,41 @@ def compress(k, v, s, w_down_k, w_down_v, storage) -> dict:
     return {n: np.stack(a) for n, a in out.items()}
 
 
+def append_token(mu, refs, k_t, t, s, w_down, storage) -> dict:
+    """A decode-time token joins a compressed stream ([en] §3 "Strided
+    Reference Selection": references sit at a fixed stride and each new
+    token retrieves the nearest earlier one; §3 "Residual Encoding").
+
+    The stream holds positions 0 .. t-1 with shared component ``mu``, which
+    stays frozen; ``refs`` are its references (those at positions below t).
+    Token t is centred in storage precision; at a reference position it is
+    stored whole and nothing else is written, otherwise it takes the earlier
+    reference of highest cosine (the first one met on ties, cosine 0 for a
+    zero vector) and the rounded projection of its residual against it.
+
+    Returns {"ref": row} or {"idx": r, "code": c, "cos": best, "margin": m}
+    where m is best minus the runner-up cosine (inf with one candidate)."""
+    x = rnd(np.asarray(k_t, np.float64) - mu, storage)
+    if t % s == 0:
+        return {"ref": x}
+    nx = math.sqrt(float(x @ x))
+    cands = []
+    for r in range(len(refs)):
+        if r * s >= t:
+            break
+        y = refs[r]
+        ny = math.sqrt(float(y @ y))
+        cands.append(float(x @ y) / (nx * ny) if nx * ny > 0 else 0.0)
+    best = 0
+    for r in range(1, len(cands)):
+        if cands[r] > cands[best]:
+            best = r
+    others = [c for r, c in enumerate(cands) if r != best]
+    resid = (np.asarray(k_t, np.float64) - mu) - refs[best]
+    return {"idx": best, "code": rnd(w_down @ resid, storage), "cos": cands[best],
+            "margin": cands[best] - max(others) if others else math.inf}
+
+
 # ---------------------------------------------------------------------------
 # Decode.
 # ---------------------------------------------------------------------------

@@ -17,13 +17,13 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdeltakv.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 F32, BF16 = 0, 1
 STATUS = {0: "DKV_OK", 1: "DKV_ERR_NULL", 2: "DKV_ERR_SHAPE", 3: "DKV_ERR_DTYPE", 4: "DKV_ERR_ALIGN",
           5: "DKV_ERR_WORKSPACE", 6: "DKV_ERR_UNSUPPORTED", 7: "DKV_ERR_VERSION", 8: "DKV_ERR_DEVICE"}
 EXPORTS = ["dkv_abi_version", "dkv_status_str", "dkv_layout_check", "dkv_cache_bytes", "dkv_cache_carve",
            "dkv_compress_workspace_bytes", "dkv_decode_auto_splits", "dkv_decode_workspace_bytes",
-           "deltakv_compress", "deltakv_decode_attn"]
+           "dkv_append_workspace_bytes", "deltakv_compress", "deltakv_append", "deltakv_decode_attn"]
 
 
 class DeltaKVError(RuntimeError):
@@ -34,7 +34,7 @@ class DeltaKVError(RuntimeError):
 
 class dkv_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint32) for n in ("abi_version", "dtype", "head_dim", "code_dim", "stride",
-                                              "idx_bytes", "n_kv_heads", "batch", "seq_len", "reserved")]
+                                              "idx_bytes", "n_kv_heads", "batch", "seq_len", "capacity")]
 
     @property
     def n_refs(self) -> int:
@@ -43,6 +43,18 @@ class dkv_layout(ctypes.Structure):
     @property
     def n_codes(self) -> int:
         return self.seq_len - self.n_refs
+
+    @property
+    def cap_tokens(self) -> int:
+        return self.capacity or self.seq_len
+
+    @property
+    def cap_refs(self) -> int:
+        return -(-self.cap_tokens // self.stride)
+
+    @property
+    def cap_codes(self) -> int:
+        return self.cap_tokens - self.cap_refs
 
 
 class dkv_cache(ctypes.Structure):
@@ -55,6 +67,12 @@ class dkv_compress_in(ctypes.Structure):
                 ("stride_h", ctypes.c_int64), ("stride_t", ctypes.c_int64), ("w_down_k", ctypes.c_void_p),
                 ("w_down_v", ctypes.c_void_p), ("w_head_stride", ctypes.c_int64), ("mu_in", ctypes.c_void_p),
                 ("stage_events", ctypes.c_void_p)]
+
+
+class dkv_append_in(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64), ("w_down_k", ctypes.c_void_p), ("w_down_v", ctypes.c_void_p),
+                ("w_head_stride", ctypes.c_int64)]
 
 
 class dkv_decode_in(ctypes.Structure):
@@ -92,6 +110,10 @@ def lib() -> ctypes.CDLL:
                                        ctypes.c_size_t, ctypes.c_void_p]
         h.deltakv_decode_attn.argtypes = [P(dkv_layout), P(dkv_cache), P(dkv_decode_in), ctypes.c_void_p,
                                           ctypes.c_size_t, ctypes.c_void_p]
+        h.dkv_append_workspace_bytes.restype = ctypes.c_size_t
+        h.dkv_append_workspace_bytes.argtypes = [P(dkv_layout)]
+        h.deltakv_append.argtypes = [P(dkv_layout), P(dkv_append_in), P(dkv_cache), ctypes.c_void_p,
+                                     ctypes.c_size_t, ctypes.c_void_p]
         if h.dkv_abi_version() != ABI_VERSION:
             raise RuntimeError("libdeltakv.so ABI version mismatch")
         _lib_handle = h
@@ -108,12 +130,22 @@ def _check(status: int, what: str):
 # ---------------------------------------------------------------------------
 
 def make_layout(dtype: str, head_dim: int, code_dim: int, stride: int, n_kv_heads: int, batch: int,
-                seq_len: int, idx_bytes: int | None = None) -> dkv_layout:
-    R = -(-seq_len // stride) if stride > 0 else 0
+                seq_len: int, idx_bytes: int | None = None, capacity: int = 0) -> dkv_layout:
+    """capacity: tokens the cache arrays are sized for (0 = seq_len)."""
+    cap = capacity or seq_len
+    R = -(-cap // stride) if stride > 0 else 0
     if idx_bytes is None:
         idx_bytes = 2 if R <= 65536 else 4
     return dkv_layout(ABI_VERSION, {"f32": F32, "bf16": BF16}[dtype], head_dim, code_dim, stride, idx_bytes,
-                      n_kv_heads, batch, seq_len, 0)
+                      n_kv_heads, batch, seq_len, capacity)
+
+
+def with_seq_len(layout: dkv_layout, seq_len: int) -> dkv_layout:
+    """The same cache buffer described as holding seq_len tokens (the
+    capacity, and with it the array layout, stays fixed)."""
+    cap = layout.cap_tokens
+    return dkv_layout(layout.abi_version, layout.dtype, layout.head_dim, layout.code_dim, layout.stride,
+                      layout.idx_bytes, layout.n_kv_heads, layout.batch, seq_len, cap)
 
 
 def dkv_layout_check(layout: dkv_layout) -> int:
@@ -164,9 +196,11 @@ class Cache:
         return self.buf[off:off + n].view(dtype).view(shape)
 
     def arrays(self) -> dict:
+        """Views of the whole arrays (capacity rows; the first n_refs /
+        n_codes rows of a stream are in use)."""
         L = self.layout
         dt = storage_torch_dtype(L)
-        B, H, R, N, d, dc = L.batch, L.n_kv_heads, L.n_refs, L.n_codes, L.head_dim, L.code_dim
+        B, H, R, N, d, dc = L.batch, L.n_kv_heads, L.cap_refs, L.cap_codes, L.head_dim, L.code_dim
         it = torch.int16 if L.idx_bytes == 2 else torch.int32
         return {"refs": self._view(self.c.refs, (B, H, 2, R, d), dt),
                 "codes": self._view(self.c.codes, (B, H, 2, N, dc), dt),
@@ -222,12 +256,29 @@ def deltakv_decode_attn(layout: dkv_layout, cache: Cache, q: torch.Tensor, w_up_
                                      ctypes.c_void_p(_stream(stream))), "deltakv_decode_attn")
 
 
+def deltakv_append(layout: dkv_layout, k: torch.Tensor, v: torch.Tensor, w_down_k: torch.Tensor,
+                   w_down_v: torch.Tensor, cache: Cache, w_head_stride: int = 0, stream=None) -> None:
+    """Appends token layout.seq_len of every sequence: k, v [B][H][d] (head
+    dim contiguous, equal strides).  The cache then holds seq_len + 1 tokens
+    (describe it with with_seq_len)."""
+    if k.stride() != v.stride() or k.stride(-1) != 1:
+        raise ValueError("k and v need equal strides and a contiguous head dim")
+    a = dkv_append_in(_ptr(k), _ptr(v), k.stride(0), k.stride(1), _ptr(w_down_k), _ptr(w_down_v), w_head_stride)
+    _check(lib().deltakv_append(ctypes.byref(layout), ctypes.byref(a), ctypes.byref(cache.c), None, 0,
+                                ctypes.c_void_p(_stream(stream))), "deltakv_append")
+
+
+def dkv_append_workspace_bytes(layout: dkv_layout) -> int:
+    return lib().dkv_append_workspace_bytes(ctypes.byref(layout))
+
+
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
-    """A zero-filled device workspace (the decode workspace must start zeroed)."""
+    """A device workspace (its contents on entry do not matter to the library)."""
     return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
-__all__ = ["lib", "make_layout", "dkv_layout", "dkv_cache", "dkv_compress_in", "dkv_decode_in", "Cache",
+__all__ = ["lib", "make_layout", "with_seq_len", "dkv_layout", "dkv_cache", "dkv_compress_in", "dkv_append_in",
+           "dkv_decode_in", "Cache", "deltakv_append", "dkv_append_workspace_bytes",
            "DeltaKVError", "dkv_layout_check", "dkv_cache_bytes", "dkv_cache_carve", "dkv_compress_workspace_bytes",
            "dkv_decode_auto_splits", "dkv_decode_workspace_bytes", "deltakv_compress", "deltakv_decode_attn",
            "workspace", "storage_torch_dtype", "EXPORTS", "LIB_PATH"]

@@ -11,7 +11,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdeltakv.so")
-SOURCES = ["api.hip", "compress.hip", "decode.hip", "decode_mfma.hip"]
+SOURCES = ["api.hip", "compress.hip", "decode.hip", "decode_mfma.hip", "append.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

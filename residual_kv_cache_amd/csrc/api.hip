@@ -19,17 +19,19 @@ dkv_status check_layout(const dkv_layout* L, Shape* out) {
   if (!L) return DKV_ERR_NULL;
   if (L->abi_version != DKV_ABI_VERSION) return DKV_ERR_VERSION;
   if (L->dtype != DKV_F32 && L->dtype != DKV_BF16) return DKV_ERR_DTYPE;
-  if (L->reserved != 0) return DKV_ERR_SHAPE;
   if (L->head_dim == 0 || L->code_dim == 0 || L->stride == 0 || L->n_kv_heads == 0 || L->batch == 0 ||
       L->seq_len == 0)
     return DKV_ERR_SHAPE;
+  const uint32_t cap = L->capacity ? L->capacity : L->seq_len;
+  if (cap < L->seq_len) return DKV_ERR_SHAPE;
   if (L->code_dim > L->head_dim) return DKV_ERR_SHAPE;
   if (L->idx_bytes != 2 && L->idx_bytes != 4) return DKV_ERR_SHAPE;
   if (L->head_dim != 64 && L->head_dim != 128) return DKV_ERR_UNSUPPORTED;
   if (L->code_dim % 16 != 0) return DKV_ERR_UNSUPPORTED;
-  if (L->seq_len > (1u << 30) || L->n_kv_heads > 4096 || L->batch > 65535) return DKV_ERR_UNSUPPORTED;
+  if (cap > (1u << 30) || L->n_kv_heads > 4096 || L->batch > 65535) return DKV_ERR_UNSUPPORTED;
   const uint32_t R = (L->seq_len + L->stride - 1) / L->stride;
-  if (L->idx_bytes == 2 && R > 65536) return DKV_ERR_UNSUPPORTED;
+  const uint32_t Rc = (cap + L->stride - 1) / L->stride;
+  if (L->idx_bytes == 2 && Rc > 65536) return DKV_ERR_UNSUPPORTED;
   const uint64_t streams = 2ull * L->batch * L->n_kv_heads;
   if (streams > 65535) return DKV_ERR_UNSUPPORTED;  // grid y limit of the stream axis
   if (out) {
@@ -39,6 +41,8 @@ dkv_status check_layout(const dkv_layout* L, Shape* out) {
     out->T = (int)L->seq_len;
     out->R = (int)R;
     out->N = (int)(L->seq_len - R);
+    out->Rc = (int)Rc;
+    out->Nc = (int)(cap - Rc);
     out->H = (int)L->n_kv_heads;
     out->B = (int)L->batch;
     out->idx_bytes = (int)L->idx_bytes;
@@ -54,9 +58,9 @@ struct ArrayBytes {
 ArrayBytes array_bytes(const Shape& sh) {
   const size_t n = (size_t)sh.n_streams();
   ArrayBytes a;
-  a.refs = n * sh.R * sh.d * sh.elem();
-  a.codes = n * sh.N * sh.dc * sh.elem();
-  a.idx = n * sh.N * sh.idx_bytes;
+  a.refs = n * sh.Rc * sh.d * sh.elem();
+  a.codes = n * sh.Nc * sh.dc * sh.elem();
+  a.idx = n * sh.Nc * sh.idx_bytes;
   a.mu = n * sh.d * sh.elem();
   return a;
 }
@@ -66,7 +70,7 @@ size_t pad(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 dkv_status check_cache(const dkv_cache* c, const Shape& sh) {
   if (!c) return DKV_ERR_NULL;
   if (!c->refs || !c->mu) return DKV_ERR_NULL;
-  if (sh.N > 0 && (!c->codes || !c->idx)) return DKV_ERR_NULL;
+  if (sh.Nc > 0 && (!c->codes || !c->idx)) return DKV_ERR_NULL;
   if (!aligned16(c->refs) || !aligned16(c->codes) || !aligned16(c->idx) || !aligned16(c->mu)) return DKV_ERR_ALIGN;
   return DKV_OK;
 }
@@ -202,6 +206,48 @@ dkv_status deltakv_compress(const dkv_layout* layout, const dkv_compress_in* in,
   a.events = in->stage_events;
   if ((st = check_events(a.events, stream)) != DKV_OK) return st;
   return from_hip(dkv::launch_compress(sh, a, (hipStream_t)stream));
+}
+
+size_t dkv_append_workspace_bytes(const dkv_layout* layout) {
+  (void)layout;
+  return 0;
+}
+
+dkv_status deltakv_append(const dkv_layout* layout, const dkv_append_in* in, const dkv_cache* cache, void* ws,
+                          size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  Shape sh;
+  dkv_status st = check_layout(layout, &sh);
+  if (st != DKV_OK) return st;
+  if (!in) return DKV_ERR_NULL;
+  if (!in->k || !in->v || !in->w_down_k || !in->w_down_v) return DKV_ERR_NULL;
+  if ((st = check_cache(cache, sh)) != DKV_OK) return st;
+  const uint32_t cap = layout->capacity ? layout->capacity : layout->seq_len;
+  if (layout->seq_len + 1 > cap) return DKV_ERR_SHAPE;
+  if (!aligned16(in->k) || !aligned16(in->v) || !aligned16(in->w_down_k) || !aligned16(in->w_down_v))
+    return DKV_ERR_ALIGN;
+  if (in->stride_b < 0 || in->stride_h < 0 || in->w_head_stride < 0) return DKV_ERR_SHAPE;
+  if (in->stride_b % 8 || in->stride_h % 8 || in->w_head_stride % 8) return DKV_ERR_ALIGN;
+  if (in->w_head_stride != 0 && in->w_head_stride < (int64_t)sh.d * sh.dc) return DKV_ERR_SHAPE;
+  // The new token is position T: references and codes of T + 1 tokens.
+  Shape s2 = sh;
+  s2.T = sh.T + 1;
+  s2.R = (s2.T + sh.s - 1) / sh.s;
+  s2.N = s2.T - s2.R;
+  dkv::AppendArgs a;
+  a.k = in->k;
+  a.v = in->v;
+  a.sb = in->stride_b;
+  a.sh = in->stride_h;
+  a.wdk = in->w_down_k;
+  a.wdv = in->w_down_v;
+  a.w_hs = in->w_head_stride;
+  a.refs = cache->refs;
+  a.codes = cache->codes;
+  a.idx = cache->idx;
+  a.mu = cache->mu;
+  return from_hip(dkv::launch_append(s2, a, (hipStream_t)stream));
 }
 
 dkv_status deltakv_decode_attn(const dkv_layout* layout, const dkv_cache* cache, const dkv_decode_in* in, void* ws,

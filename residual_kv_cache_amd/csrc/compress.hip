@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256) void k_center_refs(CompressArgs a, Shape sh) {
   const StreamId id = decode_stream(stream, sh.H);
   const typename S::T* src = stream_src<S>(a, id) + (int64_t)r * sh.s * a.st;
   const typename S::T* mu = (const typename S::T*)a.mu + (size_t)stream * sh.d;
-  typename S::T* dst = (typename S::T*)a.refs + ((size_t)stream * sh.R + r) * sh.d;
+  typename S::T* dst = (typename S::T*)a.refs + ((size_t)stream * sh.Rc + r) * sh.d;
   float n2 = 0.f;
   for (int i = lane; i < sh.d; i += 64) {
     typename S::T x = S::sub_rn(S::load(src[i]), S::load(mu[i]));
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(kSearchThreads) void k_search_mfma(CompressArgs a, 
   const StreamId id = decode_stream(stream, sh.H);
   const uint16_t* src = stream_src<BF16>(a, id);
   const uint16_t* mu = (const uint16_t*)a.mu + (size_t)stream * D;
-  const uint16_t* refs = (const uint16_t*)a.refs + (size_t)stream * sh.R * D;
+  const uint16_t* refs = (const uint16_t*)a.refs + (size_t)stream * sh.Rc * D;
   const float* inv_n = a.inv_n + (size_t)stream * sh.R;
 
   const int tb = tile * kSearchTok;
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(kSearchThreads) void k_search_mfma(CompressArgs a, 
     }
     const int t = tw + nt * 16 + lrow;
     if (lgrp == 0 && t < sh.T && t % sh.s != 0)
-      store_idx(a.idx, (size_t)stream * sh.N + pos_to_slot(t, sh.s), sh.idx_bytes, (uint32_t)r);
+      store_idx(a.idx, (size_t)stream * sh.Nc + pos_to_slot(t, sh.s), sh.idx_bytes, (uint32_t)r);
   }
 }
 
@@ -407,7 +407,7 @@ __global__ __launch_bounds__(256) void k_search_f32(CompressArgs a, Shape sh) {
   const StreamId id = decode_stream(stream, sh.H);
   const float* src = stream_src<F32>(a, id);
   const float* mu = (const float*)a.mu + (size_t)stream * D;
-  const float* refs = (const float*)a.refs + (size_t)stream * sh.R * D;
+  const float* refs = (const float*)a.refs + (size_t)stream * sh.Rc * D;
   const float* inv_n = a.inv_n + (size_t)stream * sh.R;
   const int t = tile * 256 + threadIdx.x;
   const int tmax_b = min(sh.T - 1, tile * 256 + 255);
@@ -441,7 +441,7 @@ __global__ __launch_bounds__(256) void k_search_f32(CompressArgs a, Shape sh) {
     }
   }
   if (t < sh.T && t % sh.s != 0)
-    store_idx(a.idx, (size_t)stream * sh.N + pos_to_slot(t, sh.s), sh.idx_bytes, (uint32_t)bi);
+    store_idx(a.idx, (size_t)stream * sh.Nc + pos_to_slot(t, sh.s), sh.idx_bytes, (uint32_t)bi);
 }
 
 // ---------------------------------------------------------------------------
@@ -469,14 +469,14 @@ __global__ __launch_bounds__(256) void k_encode_mfma(CompressArgs a, Shape sh) {
   const StreamId id = decode_stream(stream, sh.H);
   const uint16_t* src = stream_src<BF16>(a, id);
   const uint16_t* mu = (const uint16_t*)a.mu + (size_t)stream * D;
-  const uint16_t* refs = (const uint16_t*)a.refs + (size_t)stream * sh.R * D;
+  const uint16_t* refs = (const uint16_t*)a.refs + (size_t)stream * sh.Rc * D;
   const uint16_t* wd = (const uint16_t*)(id.kv ? a.wdv : a.wdk) + (size_t)id.h * a.w_hs;
-  uint16_t* codes = (uint16_t*)a.codes + (size_t)stream * sh.N * sh.dc;
+  uint16_t* codes = (uint16_t*)a.codes + (size_t)stream * sh.Nc * sh.dc;
 
   const int n = xi.item * 64 + wave * 16 + lrow;   // this lane's coded row
   const bool valid = n < sh.N;
   const int t = valid ? slot_to_pos(n, sh.s) : 0;
-  const int r = valid ? min((int)load_idx(a.idx, (size_t)stream * sh.N + n, sh.idx_bytes), sh.R - 1) : 0;
+  const int r = valid ? min((int)load_idx(a.idx, (size_t)stream * sh.Nc + n, sh.idx_bytes), sh.R - 1) : 0;
 
   for (int p = threadIdx.x; p < sh.dc * (D / 8); p += 256) {
     const int row = p / (D / 8), col = (p % (D / 8)) * 8;
@@ -535,13 +535,13 @@ __global__ __launch_bounds__(256) void k_encode_f32(CompressArgs a, Shape sh) {
   const float* wd = (const float*)(id.kv ? a.wdv : a.wdk) + (size_t)id.h * a.w_hs;
   const float* src = stream_src<F32>(a, id);
   const float* mu = (const float*)a.mu + (size_t)stream * D;
-  const float* refs = (const float*)a.refs + (size_t)stream * sh.R * D;
+  const float* refs = (const float*)a.refs + (size_t)stream * sh.Rc * D;
   const int t = slot_to_pos(n, sh.s);
-  const int r = min((int)load_idx(a.idx, (size_t)stream * sh.N + n, sh.idx_bytes), sh.R - 1);
+  const int r = min((int)load_idx(a.idx, (size_t)stream * sh.Nc + n, sh.idx_bytes), sh.R - 1);
   float dl[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) dl[i] = (src[(int64_t)t * a.st + i] - mu[i]) - refs[(size_t)r * D + i];
-  float* codes = (float*)a.codes + ((size_t)stream * sh.N + n) * sh.dc;
+  float* codes = (float*)a.codes + ((size_t)stream * sh.Nc + n) * sh.dc;
   for (int j = 0; j < sh.dc; ++j) {
     float c = 0.f;
 #pragma unroll

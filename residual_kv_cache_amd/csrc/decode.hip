@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void k_refscore(DecodeArgs a, Shape sh) {
     qs[g][i] = ld<S>(a.q, ((size_t)b * a.Hq + h * G + g) * D + i) * sc;
   }
   const int r0 = blockIdx.x * 64;
-  const size_t rbase = ((size_t)bh * 2 + 0) * sh.R;  // K references of (b, h)
+  const size_t rbase = ((size_t)bh * 2 + 0) * sh.Rc;  // K references of (b, h)
   for (int p = threadIdx.x; p < 64 * D; p += 256) {
     const int row = p / D, i = p % D;
     rs[row][i] = r0 + row < sh.R ? ld<S>(a.refs, (rbase + r0 + row) * D + i) : 0.f;
@@ -109,9 +109,9 @@ __global__ __launch_bounds__(256) void k_split_valu(DecodeArgs a, Shape sh) {
   const size_t sK = (size_t)bh * 2, sV = sK + 1;             // stream ids
   const int Gs = score_cols(G);
   const float* score = a.score + (size_t)bh * sh.R * Gs;
-  const typename S::T* refsV = (const typename S::T*)a.refs + sV * sh.R * D;
-  const typename S::T* codesK = (const typename S::T*)a.codes + sK * sh.N * dc;
-  const typename S::T* codesV = (const typename S::T*)a.codes + sV * sh.N * dc;
+  const typename S::T* refsV = (const typename S::T*)a.refs + sV * sh.Rc * D;
+  const typename S::T* codesK = (const typename S::T*)a.codes + sK * sh.Nc * dc;
+  const typename S::T* codesV = (const typename S::T*)a.codes + sV * sh.Nc * dc;
 
   float m[GP], lsum[GP], accr[GP][RPL], accc[GP][2];
 #pragma unroll
@@ -137,8 +137,8 @@ __global__ __launch_bounds__(256) void k_split_valu(DecodeArgs a, Shape sh) {
       if (coded) {
         // Ordinals come from caller memory: clamp so a corrupt cache can never
         // address outside the reference arrays.
-        rk = min((int)load_idx(a.idx, sK * sh.N + u, sh.idx_bytes), sh.R - 1);
-        rv = min((int)load_idx(a.idx, sV * sh.N + u, sh.idx_bytes), sh.R - 1);
+        rk = min((int)load_idx(a.idx, sK * sh.Nc + u, sh.idx_bytes), sh.R - 1);
+        rv = min((int)load_idx(a.idx, sV * sh.Nc + u, sh.idx_bytes), sh.R - 1);
       } else {
         rk = rv = u;
       }

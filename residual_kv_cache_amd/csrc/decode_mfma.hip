@@ -109,7 +109,7 @@ __global__ __launch_bounds__(256) void k_refscore_mfma(DecodeArgs a, Shape sh, i
 
   const int r = c * kRsRefs + wave * 16 + n16;
   const uint32_t rr = (uint32_t)min(r, sh.R - 1);
-  const uint16_t* refsK = (const uint16_t*)a.refs + (size_t)bh * 2 * sh.R * kD;
+  const uint16_t* refsK = (const uint16_t*)a.refs + (size_t)bh * 2 * sh.Rc * kD;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
@@ -419,11 +419,11 @@ __global__ __launch_bounds__(kThreads) void k_split_mfma(DecodeArgs a, Shape sh)
 
   Args p;
   const size_t sK = (size_t)bh * 2, sV = sK + 1;
-  p.refsV = (const uint16_t*)a.refs + sV * sh.R * kD;
-  p.codesK = (const uint16_t*)a.codes + sK * sh.N * dc;
-  p.codesV = (const uint16_t*)a.codes + sV * sh.N * dc;
-  p.idxK = (const IdxT*)a.idx + sK * sh.N;
-  p.idxV = (const IdxT*)a.idx + sV * sh.N;
+  p.refsV = (const uint16_t*)a.refs + sV * sh.Rc * kD;
+  p.codesK = (const uint16_t*)a.codes + sK * sh.Nc * dc;
+  p.codesV = (const uint16_t*)a.codes + sV * sh.Nc * dc;
+  p.idxK = (const IdxT*)a.idx + sK * sh.Nc;
+  p.idxV = (const IdxT*)a.idx + sV * sh.Nc;
   p.score = a.score + (size_t)bh * sh.R * 4;
 
   // The head's S table into LDS.

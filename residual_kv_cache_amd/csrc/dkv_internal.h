@@ -18,6 +18,8 @@ struct Shape {
   int R;        // references per stream, ceil(T / s)
   int N;        // coded tokens per stream, T - R
   int T;        // tokens per stream
+  int Rc;       // reference rows per stream in the arrays, ceil(T_cap / s)
+  int Nc;       // code rows per stream in the arrays, T_cap - Rc
   int H;        // KV heads
   int B;        // sequences
   int idx_bytes;
@@ -124,7 +126,21 @@ inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStr
   return launch_lds(kernel, grid, block, 0, st, start, stop, args...);
 }
 
+struct AppendArgs {
+  const void* k;
+  const void* v;
+  int64_t sb, sh;            // element strides of k and v
+  const void* wdk;
+  const void* wdv;
+  int64_t w_hs;
+  void* refs;
+  void* codes;
+  void* idx;
+  const void* mu;
+};
+
 hipError_t launch_compress(const Shape& sh, const CompressArgs& a, hipStream_t st);
+hipError_t launch_append(const Shape& sh, const AppendArgs& a, hipStream_t st);
 hipError_t launch_decode(const Shape& sh, const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_fused(const Shape& sh, const DecodeArgs& a, hipStream_t st);
 

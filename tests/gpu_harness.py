@@ -128,12 +128,13 @@ def ulp(c: np.ndarray, storage: str) -> np.ndarray:
     return np.ldexp(1.0, np.maximum(e, -125) - 8)
 
 
-def check_stream(x: np.ndarray, s: int, w_down: np.ndarray, storage: str, g: dict, toks=None) -> dict:
+def check_stream(x: np.ndarray, s: int, w_down: np.ndarray, storage: str, g: dict, toks=None, mu=None) -> dict:
     """Compare one GPU stream (g: mu [d], refs [R][d], idx [N], codes [N][dc])
     with the oracle on stream tokens x [T][d].  ``toks`` restricts the
-    search/code comparison to a sample of non-reference positions."""
+    search/code comparison to a sample of non-reference positions; ``mu``
+    gives the shared component (default: the mean of x)."""
     T, d = x.shape
-    mu = O.shared_component(x, storage)
+    mu = O.shared_component(x, storage) if mu is None else mu
     assert np.array_equal(g["mu"], mu), "shared component differs"
     xt = O.center(x, mu, storage)
     refs = xt[O.ref_positions(T, s)]

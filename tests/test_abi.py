@@ -32,7 +32,7 @@ def test_header_declarations_are_exported():
 
 def test_abi_version_and_status_strings():
     lib = _lib()
-    assert lib.dkv_abi_version() == 1
+    assert lib.dkv_abi_version() == D.ABI_VERSION == 2
     for code, name in D.STATUS.items():
         assert lib.dkv_status_str(code).decode().startswith(name)
 
@@ -88,14 +88,16 @@ def test_layout_check(kw, code):
 def test_layout_version_and_dtype():
     _lib()
     lay = L()
-    lay.abi_version = 2
+    lay.abi_version = 1
     assert D.dkv_layout_check(lay) == 7
     lay = L()
     lay.dtype = 9
     assert D.dkv_layout_check(lay) == 3
     lay = L()
-    lay.reserved = 1
+    lay.capacity = lay.seq_len - 1
     assert D.dkv_layout_check(lay) == 2
+    lay.capacity = lay.seq_len
+    assert D.dkv_layout_check(lay) == 0
     assert D.lib().dkv_layout_check(None) == 1
 
 
@@ -206,3 +208,46 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(D, "LIB_PATH", "/nonexistent/libdeltakv.so")
     with pytest.raises(RuntimeError, match="missing"):
         D.lib()
+
+
+@pytest.mark.parametrize("T,cap,s", [(100, 0, 16), (100, 100, 16), (100, 4096, 16), (1, 17, 16), (999, 1000, 7)])
+def test_capacity_layout(T, cap, s):
+    """Arrays are laid out for the capacity: bytes and offsets are those of a
+    cache of capacity tokens, whatever the held length."""
+    _lib()
+    lay = D.make_layout("bf16", 128, 32, s, 3, 2, T, capacity=cap)
+    full = D.make_layout("bf16", 128, 32, s, 3, 2, cap or T)
+    assert D.dkv_cache_bytes(lay) == D.dkv_cache_bytes(full) == O.cache_bytes(2, 3, cap or T, s, 128, 32, "bf16")
+    base = 1 << 20
+    a, b = D.dkv_cache_carve(lay, base), D.dkv_cache_carve(full, base)
+    assert (a.refs, a.codes, a.idx, a.mu) == (b.refs, b.codes, b.idx, b.mu)
+    grown = D.with_seq_len(lay, cap or T)
+    assert D.dkv_cache_bytes(grown) == D.dkv_cache_bytes(lay)
+
+
+def test_capacity_picks_index_width():
+    _lib()
+    lay = D.make_layout("bf16", 128, 32, 1, 1, 1, 1000, capacity=70000)
+    assert lay.idx_bytes == 4
+    lay.idx_bytes = 2
+    assert D.dkv_layout_check(lay) == 6
+
+
+def _append_status(lay, k, v, w, cache):
+    a = D.dkv_append_in(k, v, 0, 0, w, w, 0)
+    return D.lib().deltakv_append(ctypes.byref(lay), ctypes.byref(a), ctypes.byref(cache.c), None, 0, None)
+
+
+def test_append_rejects_bad_arguments():
+    """Validation only: every call here fails before any launch."""
+    _lib()
+    _no_device()
+    P = 1 << 30
+    lay = D.make_layout("bf16", 128, 32, 16, 8, 1, 100, capacity=101)
+    cache = FakeCache(P)
+    assert _append_status(lay, None, P, P, cache) == 1
+    assert _append_status(lay, P, P, None, cache) == 1
+    assert _append_status(lay, P + 8, P, P, cache) == 4
+    full = D.with_seq_len(lay, 101)
+    assert _append_status(full, P, P, P, cache) == 2
+    assert D.dkv_append_workspace_bytes(lay) == 0

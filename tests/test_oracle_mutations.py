@@ -27,6 +27,9 @@ PINS = [
     P.test_bytes_identity_matches_arrays,
     P.test_stored_values_are_representable,
     lambda: P.test_search_matches_brute_force_integer_data(97, 5, 6, 6),
+    lambda: P.test_append_equals_compress_with_frozen_mean("bf16", 33, 70, 8),
+    lambda: P.test_append_search_matches_brute_force_integer_data(97, 5, 6, 6),
+    P.test_append_hand_worked,
 ]
 
 
@@ -134,6 +137,31 @@ def _rnd_truncate(x, storage):
     return _ORIG["rnd"](x, storage)
 
 
+def _append_factory(*, no_causal=False, last_tie=False, plus_ref=False, rounded_token=False, raw_dot=False):
+    def append_token(mu, refs, k_t, t, s, w_down, storage):
+        k_t = np.asarray(k_t, np.float64)
+        x = OD.rnd(k_t - mu, storage)
+        if t % s == 0:
+            return {"ref": x}
+        cands = []
+        for r in range(len(refs)):
+            if r * s >= t and not no_causal:
+                break
+            y = refs[r]
+            den = np.sqrt(x @ x) * np.sqrt(y @ y)
+            cands.append(float(x @ y) if raw_dot else (float(x @ y) / den if den > 0 else 0.0))
+        best = 0
+        for r in range(1, len(cands)):
+            if cands[r] > cands[best] or (last_tie and cands[r] == cands[best]):
+                best = r
+        base = x if rounded_token else k_t - mu
+        resid = base + refs[best] if plus_ref else base - refs[best]
+        others = [c for r, c in enumerate(cands) if r != best]
+        return {"idx": best, "code": OD.rnd(w_down @ resid, storage), "cos": cands[best],
+                "margin": cands[best] - max(others) if others else np.inf}
+    return append_token
+
+
 def _stream_bytes_no_idx(T, s, d, dc, storage):
     e = OD.ELEM_BYTES[storage]
     R = OD.n_refs(T, s)
@@ -158,6 +186,11 @@ MUTATIONS = {
     "rnd: bf16 through fp32 (double rounding)": ("rnd", _rnd_via_f32),
     "rnd: bf16 truncates": ("rnd", _rnd_truncate),
     "stream_bytes: index bytes forgotten": ("stream_bytes", _stream_bytes_no_idx),
+    "append: sees references at or after its own position": ("append_token", _append_factory(no_causal=True)),
+    "append: ties to highest ordinal": ("append_token", _append_factory(last_tie=True)),
+    "append: + reference instead of -": ("append_token", _append_factory(plus_ref=True)),
+    "append: residual of the rounded token": ("append_token", _append_factory(rounded_token=True)),
+    "append: raw dot product, no normalisation": ("append_token", _append_factory(raw_dot=True)),
 }
 
 

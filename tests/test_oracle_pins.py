@@ -394,3 +394,91 @@ def test_stored_values_are_representable():
     for name in ("mu", "refs", "codes"):
         x = np.asarray(r[name], np.float64)
         assert np.array_equal(K.to_storage(x, "bf16").f64, x), name
+
+
+# ---------------------------------------------------------------------------
+# Decode-time append ([en] §3 "Strided Reference Selection"): a token that
+# joins a stream with its mean frozen is stored as compressing every token
+# so far with that mean would store it.
+# ---------------------------------------------------------------------------
+
+def _append_chain(k, T0, s, wd, storage):
+    """Compress the first T0 tokens (mean of those T0), then append the rest
+    one by one; returns (mu, refs, idx, codes, margins) of the whole stream."""
+    mu = O.shared_component(k[:T0], storage)
+    r = O.compress_stream(k[:T0], s, wd, storage)
+    refs, idx, codes, margins = list(r["refs"]), list(r["idx"]), list(r["codes"]), list(r["margin"])
+    for t in range(T0, len(k)):
+        a = O.append_token(mu, np.array(refs), k[t], t, s, wd, storage)
+        if "ref" in a:
+            refs.append(a["ref"])
+        else:
+            idx.append(a["idx"])
+            codes.append(a["code"])
+            margins.append(a["margin"])
+    return mu, np.array(refs), np.array(idx, np.int64), np.array(codes).reshape(-1, wd.shape[0]), np.array(margins)
+
+
+@pytest.mark.parametrize("storage,T0,n,s", [("f64", 20, 45, 4), ("bf16", 33, 70, 8), ("f32", 16, 40, 16),
+                                            ("bf16", 1, 30, 3), ("bf16", 5, 12, 1)])
+def test_append_equals_compress_with_frozen_mean(storage, T0, n, s):
+    """Appending tokens one at a time gives the stream that compressing all of
+    them with the prefill's mean gives: references bit-exact, ordinals equal,
+    codes equal up to the fp64 summation order (one storage ulp at most)."""
+    rng = np.random.default_rng(T0 * 100 + n)
+    d, dc = 12, 5
+    k = K.to_storage(rng.standard_normal((T0 + n, d)) * 2 + 1, storage).f64 if storage != "f64" \
+        else rng.standard_normal((T0 + n, d)) * 2 + 1
+    wd = K.to_storage(rng.standard_normal((dc, d)) / 3, storage).f64 if storage != "f64" \
+        else rng.standard_normal((dc, d)) / 3
+    mu, refs, idx, codes, margins = _append_chain(k, T0, s, wd, storage)
+    full = O.compress_stream(k, s, wd, storage, mu_in=mu)
+    assert np.array_equal(refs, full["refs"])
+    assert np.array_equal(idx, full["idx"])
+    assert np.allclose(margins, full["margin"], rtol=0, atol=1e-12)
+    if storage == "f64":
+        assert np.allclose(codes, full["codes"], rtol=1e-13, atol=1e-13)
+    else:
+        gap = np.abs(codes - full["codes"])
+        assert np.all(gap <= np.spacing(np.abs(full["codes"]).astype(np.float32)) * (256 if storage == "bf16" else 1))
+        assert gap.size == 0 or (gap > 0).mean() < 0.01
+
+
+@pytest.mark.parametrize("T,s,d,seed", [(40, 3, 5, 4), (97, 5, 6, 6), (60, 2, 3, 8), (33, 1, 4, 9)])
+def test_append_search_matches_brute_force_integer_data(T, s, d, seed):
+    """Integer vectors make equal cosines bitwise equal: the appended
+    ordinals follow the plain-loop search, first maximum on ties."""
+    rng = np.random.default_rng(seed)
+    xt = rng.integers(-2, 3, size=(T, d)).astype(np.float64)
+    refs, got = [], []
+    for t in range(T):
+        a = O.append_token(np.zeros(d), np.array(refs).reshape(-1, d), xt[t], t, s, np.eye(d), "f64")
+        if "ref" in a:
+            refs.append(a["ref"])
+        else:
+            got.append(a["idx"])
+    assert got == _py_search(xt.tolist(), s)
+
+
+def test_append_hand_worked():
+    """The stream of the hand-worked example, grown by appends with its mean
+    (7/4, 3/4) frozen after the first three tokens:
+      t=3, k=(1,1):  x~ = (-3/4, 1/4); cos with r0 = (1/4,-3/4) is -0.6, with
+                     r1 = (9/4,-3/4) is -1  -> ref 0, code (x~ - r0)[0] = -1
+      t=4, k=(3,2):  a reference position: row x~ = (5/4, 5/4), no code
+      t=5, k=(0,3):  x~ = (-7/4, 9/4); its dot products with r0, r1, r2 are
+                     -17/8, -45/8 and +5/8, so only r2 has a positive cosine
+                     -> ref 2, code (x~ - r2)[0] = -3"""
+    mu = np.array([1.75, 0.75])
+    refs = np.array([[0.25, -0.75], [2.25, -0.75]])
+    wd = np.array([[1.0, 0.0]])
+    a = O.append_token(mu, refs, [1.0, 1.0], 3, 2, wd, "f64")
+    assert a["idx"] == 0 and a["code"].tolist() == [-1.0]
+    assert abs(a["cos"] + 0.6) < 1e-15 and abs(a["margin"] - 0.4) < 1e-15
+    b = O.append_token(mu, refs, [3.0, 2.0], 4, 2, wd, "f64")
+    assert b["ref"].tolist() == [1.25, 1.25]
+    refs = np.vstack([refs, b["ref"]])
+    c = O.append_token(mu, refs, [0.0, 3.0], 5, 2, wd, "f64")
+    assert c["idx"] == 2 and c["code"].tolist() == [-3.0]
+    # The token at position 3 cannot see the reference at position 4.
+    assert O.append_token(mu, refs, [3.0, 2.0], 3, 2, wd, "f64")["idx"] == 1
