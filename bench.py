@@ -21,6 +21,10 @@ the decode window of a step (effective bytes: every cache array, V's mean,
 both W_up, the queries and the fp32 outputs, each counted once per decode
 step).  The oracle (fp64, CPU) is timed on a bounded sample afterwards as a
 baseline.
+
+Decode-time append is reported beside it (not part of `value`): 32 tokens
+appended one at a time to a cache sized for them, each after a copy that
+evicts the references from the Infinity Cache, timed with stage events.
 """
 from __future__ import annotations
 
@@ -39,6 +43,7 @@ METRIC = "compressed-KV decode attn GB/s & tokens/s vs HBM roofline; compress to
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2516.6
 DECODE_STEPS = 256
+APPEND_TOKENS = 32
 MALL_BYTES = 256 << 20
 
 
@@ -298,8 +303,18 @@ def main():
             D.deltakv_decode_attn(lay, caches[i % nrep], q_d[i % nsteps], wuk_d, wuv_d, outs[i % nsteps], ws_d,
                                   n_splits=splits)
         torch.cuda.synchronize()
+        lay_a = D.make_layout(cfg.dtype, cfg.head_dim, cfg.code_dim, cfg.stride, cfg.n_kv_heads, cfg.batch,
+                              cfg.seq_len, capacity=cfg.seq_len + APPEND_TOKENS)
+        cache_a = D.Cache(lay_a)
+        D.deltakv_compress(lay_a, k_d, v_d, wdk_d, wdv_d, cache_a, D.workspace(D.dkv_compress_workspace_bytes(lay_a)))
+        ws_a = D.workspace(D.dkv_append_workspace_bytes(lay_a))
+        for i in range(APPEND_TOKENS):
+            dst.copy_(src)  # evicts the references from the MALL
+            D.deltakv_append(D.with_seq_len(lay_a, cfg.seq_len + i), k_d[:, :, 1000 + i], v_d[:, :, 1000 + i],
+                             wdk_d, wdv_d, cache_a, ws_a)
+        torch.cuda.synchronize()
         log(f"[bench] profile driver: calibration copy of {CALIB_BYTES} bytes, {args.steps} decode steps, "
-            f"splits {splits}, {nrep} cache replicas")
+            f"splits {splits}, {nrep} cache replicas, then {APPEND_TOKENS} appends")
         return
     D.deltakv_decode_attn(lay, caches[0], q_d[0], wuk_d, wuv_d, outs[0], ws_d, n_splits=splits)
     eager0 = outs[0].clone()
@@ -371,6 +386,44 @@ def main():
     c_stage = np.mean(np.array(c_stage), axis=0)
     d_stage = np.array(d_stage)
 
+    # Decode-time append: a cache sized for APPEND_TOKENS more tokens takes
+    # them one at a time after the prefill (each new token of every stream is
+    # a copy of a prefill token, so it has the workload's statistics).  A
+    # copy twice the MALL's size runs between appends, so each append reads
+    # the references from HBM, as it would after the other layers' steps.
+    lay_a = D.make_layout(cfg.dtype, cfg.head_dim, cfg.code_dim, cfg.stride, cfg.n_kv_heads, cfg.batch,
+                          cfg.seq_len, capacity=cfg.seq_len + APPEND_TOKENS)
+    cache_a = D.Cache(lay_a)
+    ws_ca = D.workspace(D.dkv_compress_workspace_bytes(lay_a))
+    ws_a = D.workspace(D.dkv_append_workspace_bytes(lay_a))
+    D.deltakv_compress(lay_a, k_d, v_d, wdk_d, wdv_d, cache_a, ws_ca, stream=s_h)
+    new_k = [k_d[:, :, 1000 + i] for i in range(APPEND_TOKENS)]
+    new_v = [v_d[:, :, 1000 + i] for i in range(APPEND_TOKENS)]
+    ev_a = [hip.events(4) for _ in range(APPEND_TOKENS)]
+    flush_src = torch.ones(MALL_BYTES // 2, dtype=torch.float32, device="cuda")
+    flush_dst = torch.empty_like(flush_src)
+    a_search, a_total = [], []
+    for rep in range(2):
+        for i in range(APPEND_TOKENS):
+            with torch.cuda.stream(stream):
+                flush_dst.copy_(flush_src)
+            D.deltakv_append(D.with_seq_len(lay_a, cfg.seq_len + i), new_k[i], new_v[i], wdk_d, wdv_d, cache_a, ws_a,
+                             stream=s_h, stage_events=ev_a[i])
+        hip.sync(s_h)
+        for i in range(APPEND_TOKENS):
+            t = cfg.seq_len + i
+            a_total.append(hip.elapsed_ms(ev_a[i][0], ev_a[i][3]))
+            if t % cfg.stride:
+                a_search.append((hip.elapsed_ms(ev_a[i][0], ev_a[i][1]), t // cfg.stride + 1))
+    append_us = float(np.mean(a_total)) * 1e3
+    search_us = float(np.mean([x[0] for x in a_search])) * 1e3
+    # Algorithmic bytes of one search launch: every candidate reference row
+    # of every stream once, plus the new token and the mean.
+    n_streams_a = cfg.batch * cfg.n_kv_heads * 2
+    elem = 2 if cfg.dtype == "bf16" else 4
+    append_bytes = float(np.mean([(x[1] + 2) * cfg.head_dim * elem * n_streams_a for x in a_search]))
+    del flush_src, flush_dst, cache_a
+
     eff = effective_decode_bytes(cfg)
     value = nsteps * eff / (decode_window_ms * 1e-3) / 1e9
     split_ms = float(d_stage[:, 1].mean())
@@ -411,6 +464,13 @@ def main():
                      "unit": "GB/s", "frac": round(split_bytes / (split_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": stored_traffic(cfg.name, splits), "bytes_per_launch": split_bytes,
                      "launch_us": round(split_ms * 1e3, 3)},
+        "append_us_per_token": round(append_us, 3),
+        "roofline_append": {"kernel": "k_append_search", "bound": "hbm",
+                            "achieved": round(append_bytes / (search_us * 1e-6) / 1e9, 2), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s",
+                            "frac": round(append_bytes / (search_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                            "bytes_per_launch": round(append_bytes), "launch_us": round(search_us, 3),
+                            "tokens": APPEND_TOKENS},
         "roofline_search": {"kernel": "k_search_mfma", "bound": "mfma",
                             "achieved": round(search_flops / (c_stage[2] * 1e-3) / 1e12, 2),
                             "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -200,7 +200,13 @@ typedef struct dkv_decode_in {
  *              same strides apply to v; the head_dim elements are contiguous
  *              and 16-byte aligned
  *   w_down_k, w_down_v, w_head_stride  as in dkv_compress_in
+ *   stage_events  optional host array of DKV_APPEND_EVENTS hipEvent_t
+ *              handles (NULL = none): (start, stop) pairs of the stages
+ *              search and finish (merge, then store the row), as for
+ *              dkv_compress_in.stage_events; for a token that becomes a
+ *              reference the search pair is recorded with nothing between
  */
+#define DKV_APPEND_EVENTS 4
 typedef struct dkv_append_in {
   const void* k;
   const void* v;
@@ -209,6 +215,7 @@ typedef struct dkv_append_in {
   const void* w_down_k;
   const void* w_down_v;
   int64_t w_head_stride;
+  void* const* stage_events;
 } dkv_append_in;
 
 /* DKV_ABI_VERSION of the loaded library. */
@@ -261,7 +268,9 @@ dkv_status deltakv_compress(const dkv_layout* layout, const dkv_compress_in* in,
  * token).  Requires T + 1 <= capacity; the caller then describes the cache
  * with seq_len = T + 1.  Writes only that token's row of refs, or of codes
  * and idx.  `ws` as for deltakv_compress, of at least
- * dkv_append_workspace_bytes(layout) bytes (0 bytes: `ws` may be NULL).
+ * dkv_append_workspace_bytes(layout) bytes (a few bytes per stream; the
+ * bound covers every length up to the capacity, so one workspace serves all
+ * appends to the cache).
  */
 size_t dkv_append_workspace_bytes(const dkv_layout* layout);
 dkv_status deltakv_append(const dkv_layout* layout, const dkv_append_in* in, const dkv_cache* cache, void* ws,

@@ -72,7 +72,7 @@ class dkv_compress_in(ctypes.Structure):
 class dkv_append_in(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
                 ("stride_h", ctypes.c_int64), ("w_down_k", ctypes.c_void_p), ("w_down_v", ctypes.c_void_p),
-                ("w_head_stride", ctypes.c_int64)]
+                ("w_head_stride", ctypes.c_int64), ("stage_events", ctypes.c_void_p)]
 
 
 class dkv_decode_in(ctypes.Structure):
@@ -257,14 +257,18 @@ def deltakv_decode_attn(layout: dkv_layout, cache: Cache, q: torch.Tensor, w_up_
 
 
 def deltakv_append(layout: dkv_layout, k: torch.Tensor, v: torch.Tensor, w_down_k: torch.Tensor,
-                   w_down_v: torch.Tensor, cache: Cache, w_head_stride: int = 0, stream=None) -> None:
+                   w_down_v: torch.Tensor, cache: Cache, ws: torch.Tensor, w_head_stride: int = 0, stream=None,
+                   stage_events=None) -> None:
     """Appends token layout.seq_len of every sequence: k, v [B][H][d] (head
     dim contiguous, equal strides).  The cache then holds seq_len + 1 tokens
-    (describe it with with_seq_len)."""
+    (describe it with with_seq_len).  ws: device buffer of at least
+    dkv_append_workspace_bytes(layout) bytes."""
     if k.stride() != v.stride() or k.stride(-1) != 1:
         raise ValueError("k and v need equal strides and a contiguous head dim")
-    a = dkv_append_in(_ptr(k), _ptr(v), k.stride(0), k.stride(1), _ptr(w_down_k), _ptr(w_down_v), w_head_stride)
-    _check(lib().deltakv_append(ctypes.byref(layout), ctypes.byref(a), ctypes.byref(cache.c), None, 0,
+    a = dkv_append_in(_ptr(k), _ptr(v), k.stride(0), k.stride(1), _ptr(w_down_k), _ptr(w_down_v), w_head_stride,
+                      _events(stage_events))
+    _check(lib().deltakv_append(ctypes.byref(layout), ctypes.byref(a), ctypes.byref(cache.c),
+                                ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
                                 ctypes.c_void_p(_stream(stream))), "deltakv_append")
 
 

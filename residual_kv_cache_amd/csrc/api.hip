@@ -209,14 +209,13 @@ dkv_status deltakv_compress(const dkv_layout* layout, const dkv_compress_in* in,
 }
 
 size_t dkv_append_workspace_bytes(const dkv_layout* layout) {
-  (void)layout;
-  return 0;
+  Shape sh;
+  if (check_layout(layout, &sh) != DKV_OK) return 0;
+  return dkv::append_ws_bytes(sh);
 }
 
 dkv_status deltakv_append(const dkv_layout* layout, const dkv_append_in* in, const dkv_cache* cache, void* ws,
                           size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   Shape sh;
   dkv_status st = check_layout(layout, &sh);
   if (st != DKV_OK) return st;
@@ -230,6 +229,9 @@ dkv_status deltakv_append(const dkv_layout* layout, const dkv_append_in* in, con
   if (in->stride_b < 0 || in->stride_h < 0 || in->w_head_stride < 0) return DKV_ERR_SHAPE;
   if (in->stride_b % 8 || in->stride_h % 8 || in->w_head_stride % 8) return DKV_ERR_ALIGN;
   if (in->w_head_stride != 0 && in->w_head_stride < (int64_t)sh.d * sh.dc) return DKV_ERR_SHAPE;
+  if (!ws || ws_bytes < dkv::append_ws_bytes(sh)) return DKV_ERR_WORKSPACE;
+  if (!aligned16(ws)) return DKV_ERR_ALIGN;
+  if ((st = check_events(in->stage_events, stream)) != DKV_OK) return st;
   // The new token is position T: references and codes of T + 1 tokens.
   Shape s2 = sh;
   s2.T = sh.T + 1;
@@ -247,7 +249,8 @@ dkv_status deltakv_append(const dkv_layout* layout, const dkv_append_in* in, con
   a.codes = cache->codes;
   a.idx = cache->idx;
   a.mu = cache->mu;
-  return from_hip(dkv::launch_append(s2, a, (hipStream_t)stream));
+  a.events = in->stage_events;
+  return from_hip(dkv::launch_append(s2, a, ws, (hipStream_t)stream));
 }
 
 dkv_status deltakv_decode_attn(const dkv_layout* layout, const dkv_cache* cache, const dkv_decode_in* in, void* ws,

@@ -2,19 +2,26 @@
 // a cache that holds positions 0 .. t-1, with the shared component frozen
 // (DeltaKV explainer, English page, Technical Summary §3 "Strided Reference
 // Selection": references are kept at a fixed stride and each new token
-// retrieves the nearest earlier ones; §3 "Residual Encoding").  The result
-// is the row that compressing all t + 1 tokens with the same mean would
-// store:
+// retrieves the nearest earlier one; §3 "Residual Encoding").  The result is
+// the row that compressing all t + 1 tokens with the same mean would store:
 //
 //   t mod s == 0   refs[t / s] = rnd(k_t - mu)
 //   otherwise      ref(t) = argmax over r with r*s < t of cos(x~_t, refs[r]),
 //                  lowest r on ties;  code_t = rnd(W_down ((k_t - mu) - refs[ref(t)]))
 //
-// One 256-thread block per stream: 16 groups of 16 lanes walk the references
-// (group g takes r = g, g + 16, ...; a lane holds d/16 elements of the row),
-// each group keeps its best (score, ordinal) with a strict '>' over
-// increasing ordinals, and the groups merge in a fixed order.  Scores are
-// <x~_t, x~_r> / ||x~_r||, as in the compress search.
+// The search is one pass over the stream's references, which is HBM-bound,
+// so it is spread over many blocks per stream (k_append_search): block p of
+// a stream scores references [p*chunk, (p+1)*chunk) with 16-lane groups, one
+// reference row per group and one 16-byte load per lane, four rows in flight
+// per group, and writes its best (score, ordinal) together with that
+// candidate's code, encoded in the same block while the row is at hand.
+// k_append_finish takes the maximum of the candidates under the total order
+// (higher score, then lower ordinal) -- unique, so independent of the merge
+// tree -- and copies its code and ordinal into the cache.  Scores are
+// <x~_t, x~_r> / ||x~_r||, which orders the references as the cosine does
+// (||x~_t|| is common to all of them).
+
+#include <algorithm>
 
 #include "dkv_device.h"
 #include "dkv_internal.h"
@@ -23,98 +30,254 @@ namespace dkv {
 
 namespace {
 
+typedef const __attribute__((address_space(1))) uint32_t* GWords;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// E consecutive storage elements as raw 32-bit words.
+template <class S, int E>
+struct RowSlice {
+  static constexpr int kWords = E * (int)sizeof(typename S::T) / 4;
+  uint32_t w[kWords];
+  __device__ __forceinline__ void load(const void* p) {
+    GWords g = (GWords)p;
+    if constexpr (kWords % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < kWords; i += 4) {
+        const u32x4 v = *(const __attribute__((address_space(1))) u32x4*)(g + i);
+        w[i] = v.x;
+        w[i + 1] = v.y;
+        w[i + 2] = v.z;
+        w[i + 3] = v.w;
+      }
+    } else {
+      const u32x2 v = *(const __attribute__((address_space(1))) u32x2*)g;
+      w[0] = v.x;
+      w[1] = v.y;
+    }
+  }
+  // Element e as float.
+  __device__ __forceinline__ float at(int e) const {
+    if constexpr (sizeof(typename S::T) == 2)
+      return __uint_as_float((e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
+    else
+      return __uint_as_float(w[e]);
+  }
+};
+
+__device__ __forceinline__ bool better(float s1, int r1, float s2, int r2) {
+  return s1 > s2 || (s1 == s2 && r1 < r2);
+}
+
+constexpr int kUnroll = 4;
+
+// Search partials in the workspace: (score, ordinal) per block, then the
+// block's winner already encoded, [n_streams][parts][d_c] storage dtype.
+inline size_t pcode_off(int ns, int parts) { return align_up((size_t)ns * parts * sizeof(float2), 256); }
+
 template <class S, int D>
-__global__ __launch_bounds__(256) void k_append(AppendArgs a, Shape sh) {
-  constexpr int E = D / 16;   // elements per lane
-  __shared__ float xs[D];     // x~_t
-  __shared__ float ds[D];     // k_t - mu
+__global__ __launch_bounds__(256) void k_append_search(AppendArgs a, Shape sh, int chunk, int P, float2* part,
+                                                       typename S::T* pcode) {
+  constexpr int E = D / 16;  // elements per lane of a reference row
+  constexpr int Q = D / 4;   // elements per lane of a W_down row
+  typedef typename S::T T;
+  const XcdItem xi = xcd_item(sh.n_streams());  // a stream's blocks share its XCD
+  if (xi.stream < 0) return;
+  const int stream = xi.stream, p = xi.item;
+  const int kv = stream & 1, bh = stream >> 1, b = bh / sh.H, h = bh - b * sh.H;
+  const int t = sh.T - 1;
+  const int nref = t / sh.s + 1;  // references r with r*s < t (t is not a multiple of s)
+  const int r0 = p * chunk, r1 = min(nref, r0 + chunk);
+  const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15;
+  const int j = tid >> 2, l4 = tid & 3;
+  constexpr size_t e = sizeof(T);
+
+  // Every load that does not depend on another goes out first: the first
+  // reference rows, the new token and the mean, this lane's W_down slice.
+  const char* refs = (const char*)a.refs + ((size_t)stream * sh.Rc * D + l16 * E) * e;
+  RowSlice<S, E> row[kUnroll];
+  int r = r0 + grp;
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) row[u].load(refs + (size_t)min(r + 16 * u, r1 - 1) * D * e);
+  const char* src = (const char*)(kv ? a.v : a.k) + ((int64_t)b * a.sb + (int64_t)h * a.sh + l16 * E) * e;
+  RowSlice<S, E> ks, ms;
+  ks.load(src);
+  ms.load((const char*)a.mu + ((size_t)stream * D + l16 * E) * e);
+  const T* wd = (const T*)(kv ? a.wdv : a.wdk) + (size_t)h * a.w_hs;
+  RowSlice<S, Q> wrow;  // rows past d_c load row d_c - 1 (unconditional loads keep the wait counts exact)
+  wrow.load(wd + (size_t)min(j, sh.dc - 1) * D + l4 * Q);
+
+  float x[E], ds[E];  // x~_t = rnd(k_t - mu) and k_t - mu
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    ds[i] = ks.at(i) - ms.at(i);
+    x[i] = S::load(S::sub_rn(ks.at(i), ms.at(i)));
+  }
+
+  float best = -INFINITY;
+  int bidx = 0x7FFFFFFF;
+  RowSlice<S, E> brow = row[0];  // the group's best row so far
+  for (;;) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      float dot = 0.f, n2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const float v = row[u].at(i);
+        dot = fmaf(x[i], v, dot);
+        n2 = fmaf(v, v, n2);
+      }
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) {
+        dot += __shfl_xor(dot, o, 64);
+        n2 += __shfl_xor(n2, o, 64);
+      }
+      const float sc = n2 > 0.f ? dot * (1.0f / sqrtf(n2)) : 0.f;
+      const int ru = r + 16 * u;
+      if (ru < r1 && sc > best) {  // ordinals rise within a group: '>' keeps the lowest on ties
+        best = sc;
+        bidx = ru;
+        brow = row[u];
+      }
+    }
+    r += 16 * kUnroll;
+    if (r >= r1) break;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) row[u].load(refs + (size_t)min(r + 16 * u, r1 - 1) * D * e);
+  }
+
   __shared__ float red_s[16];
   __shared__ int red_r[16];
-  const int stream = blockIdx.x;
-  const int kv = stream & 1, bh = stream >> 1, b = bh / sh.H, h = bh % sh.H;
-  const int t = sh.T - 1;     // the new token's position
-  const int tid = threadIdx.x;
-  const typename S::T* src = (const typename S::T*)(kv ? a.v : a.k) + (int64_t)b * a.sb + (int64_t)h * a.sh;
-  const typename S::T* mu = (const typename S::T*)a.mu + (size_t)stream * D;
-  typename S::T* refs = (typename S::T*)a.refs + (size_t)stream * sh.Rc * D;
-  if (tid < D) {
-    const float x = S::load(src[tid]), m = S::load(mu[tid]);
-    const typename S::T xt = S::sub_rn(x, m);
-    xs[tid] = S::load(xt);
-    ds[tid] = x - m;
-    if (t % sh.s == 0) refs[(size_t)(t / sh.s) * D + tid] = xt;
-  }
-  if (t % sh.s == 0) return;  // a reference token stores no code
-  __syncthreads();
-
-  // ---- search over references r = 0 .. t / s ----
-  const int grp = tid >> 4, l16 = tid & 15;
-  const int nref = t / sh.s + 1;
-  float x[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) x[e] = xs[l16 * E + e];
-  float best = -INFINITY;
-  int bidx = 0;
-  for (int r = grp; r < nref; r += 16) {
-    const typename S::T* row = refs + (size_t)r * D + l16 * E;
-    float dot = 0.f, n2 = 0.f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float v = S::load(row[e]);
-      dot = fmaf(x[e], v, dot);
-      n2 = fmaf(v, v, n2);
-    }
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) {
-      dot += __shfl_xor(dot, o, 64);
-      n2 += __shfl_xor(n2, o, 64);
-    }
-    const float sc = n2 > 0.f ? dot * (1.0f / sqrtf(n2)) : 0.f;
-    if (sc > best) {
-      best = sc;
-      bidx = r;
-    }
-  }
+  __shared__ float diff[D];
   if (l16 == 0) {
     red_s[grp] = best;
     red_r[grp] = bidx;
   }
   __syncthreads();
-  // Fixed-order merge: larger score, then lower ordinal.
   float bs = red_s[0];
   int br = red_r[0];
-  for (int g = 1; g < 16; ++g) {
-    const float v = red_s[g];
-    const int r = red_r[g];
-    if (v > bs || (v == bs && r < br)) {
-      bs = v;
-      br = r;
+  for (int g = 1; g < 16; ++g)
+    if (better(red_s[g], red_r[g], bs, br)) {
+      bs = red_s[g];
+      br = red_r[g];
     }
+  // Ordinal br was scored by group (br - r0) mod 16, which holds its row.
+  if (grp == ((br - r0) & 15)) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) diff[l16 * E + i] = ds[i] - brow.at(i);
   }
+  __syncthreads();
 
-  // ---- code: rnd(W_down ((k - mu) - refs[br])) ----
-  const size_t slot = (size_t)stream * sh.Nc + (size_t)(t - t / sh.s - 1);
-  if (tid < sh.dc) {
-    const typename S::T* w = (const typename S::T*)(kv ? a.wdv : a.wdk) + (size_t)h * a.w_hs + (size_t)tid * D;
-    const typename S::T* rrow = refs + (size_t)br * D;
+  // The block's candidate code: rnd(W_down (k_t - mu - refs[br])), four
+  // lanes per element, 64 elements per pass.
+  T* out = pcode + ((size_t)stream * P + p) * sh.dc;
+  for (int j0 = 0; j0 < sh.dc; j0 += 64) {
+    const int jj = j0 + j;
+    if (j0 > 0) wrow.load(wd + (size_t)min(jj, sh.dc - 1) * D + l4 * Q);
     float c = 0.f;
-    for (int e = 0; e < D; ++e) c = fmaf(S::load(w[e]), ds[e] - S::load(rrow[e]), c);
-    ((typename S::T*)a.codes)[slot * sh.dc + tid] = S::from_f32(c);
+    if (jj < sh.dc) {
+#pragma unroll
+      for (int i = 0; i < Q; ++i) c = fmaf(wrow.at(i), diff[l4 * Q + i], c);
+    }
+    c += __shfl_xor(c, 1, 64);
+    c += __shfl_xor(c, 2, 64);
+    if (jj < sh.dc && l4 == 0) out[jj] = S::from_f32(c);
   }
-  if (tid == 0) store_idx(a.idx, slot, sh.idx_bytes, (uint32_t)br);
+  if (tid == 0) part[(size_t)stream * P + p] = make_float2(bs, __int_as_float(br));
 }
 
-template <class S>
-hipError_t launch_append_s(const Shape& sh, const AppendArgs& a, hipStream_t st) {
-  const dim3 grid(sh.n_streams());
-  return sh.d == 128 ? launch(k_append<S, 128>, grid, 256, st, nullptr, nullptr, a, sh)
-                     : launch(k_append<S, 64>, grid, 256, st, nullptr, nullptr, a, sh);
+// One wave per stream (block x runs on XCD x mod 8, beside the stream's
+// search blocks): the maximum of the search partials under the total order,
+// then its code and ordinal are stored; or, for a token at a reference
+// position, its centred row.
+template <class S, int D>
+__global__ __launch_bounds__(64) void k_append_finish(AppendArgs a, Shape sh, int P, const float2* part,
+                                                      const typename S::T* pcode) {
+  typedef typename S::T T;
+  const int stream = blockIdx.x;
+  const int kv = stream & 1, bh = stream >> 1, b = bh / sh.H, h = bh - b * sh.H;
+  const int t = sh.T - 1;
+  const int lane = threadIdx.x;
+  if (t % sh.s == 0) {
+    const T* src = (const T*)(kv ? a.v : a.k) + (int64_t)b * a.sb + (int64_t)h * a.sh;
+    const T* mu = (const T*)a.mu + (size_t)stream * D;
+    T* row = (T*)a.refs + ((size_t)stream * sh.Rc + t / sh.s) * D;
+    for (int i = lane; i < D; i += 64) row[i] = S::sub_rn(S::load(src[i]), S::load(mu[i]));
+    return;
+  }
+  float bs = -INFINITY;
+  int br = 0x7FFFFFFF, bp = 0;
+  for (int i = lane; i < P; i += 64) {
+    const float2 v = part[(size_t)stream * P + i];
+    if (better(v.x, __float_as_int(v.y), bs, br)) {
+      bs = v.x;
+      br = __float_as_int(v.y);
+      bp = i;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float os = __shfl_xor(bs, o, 64);
+    const int orr = __shfl_xor(br, o, 64);
+    const int op = __shfl_xor(bp, o, 64);
+    if (better(os, orr, bs, br)) {
+      bs = os;
+      br = orr;
+      bp = op;
+    }
+  }
+  const size_t slot = (size_t)stream * sh.Nc + (size_t)(t - t / sh.s - 1);
+  const T* c = pcode + ((size_t)stream * P + bp) * sh.dc;
+  for (int jj = lane; jj < sh.dc; jj += 64) ((T*)a.codes)[slot * sh.dc + jj] = c[jj];
+  if (lane == 0) store_idx(a.idx, slot, sh.idx_bytes, (uint32_t)br);
+}
+
+__global__ void k_append_empty() {}
+
+template <class S, int D>
+hipError_t launch_append_sd(const Shape& sh, const AppendArgs& a, void* ws, hipStream_t st) {
+  const hipEvent_t ev[4] = {ev_start(a.events, 0), ev_stop(a.events, 0), ev_start(a.events, 1),
+                            ev_stop(a.events, 1)};
+  const int t = sh.T - 1, ns = sh.n_streams();
+  const int P = t % sh.s == 0 ? 0 : append_parts(sh, t / sh.s + 1);
+  float2* part = (float2*)ws;
+  typename S::T* pcode = (typename S::T*)((char*)ws + pcode_off(ns, std::max(P, 1)));
+  hipError_t err;
+  if (P > 0)
+    err = launch(k_append_search<S, D>, dim3(xcd_grid(ns, P)), 256, st, ev[0], ev[1], a, sh,
+                 append_chunk(sh, t / sh.s + 1), P, part, pcode);
+  else  // a reference token needs no search: an empty stage keeps the event pairs meaningful
+    err = ev[0] ? launch(k_append_empty, dim3(1), 64, st, ev[0], ev[1]) : hipSuccess;
+  if (err != hipSuccess) return err;
+  return launch(k_append_finish<S, D>, dim3(ns), 64, st, ev[2], ev[3], a, sh, P, (const float2*)part,
+                (const typename S::T*)pcode);
 }
 
 }  // namespace
 
-hipError_t launch_append(const Shape& sh, const AppendArgs& a, hipStream_t st) {
-  return sh.bf16 ? launch_append_s<BF16>(sh, a, st) : launch_append_s<F32>(sh, a, st);
+int append_chunk(const Shape& sh, int nref) {
+  const int target = (kAppendBlocks + sh.n_streams() - 1) / sh.n_streams();
+  const int per = (nref + target - 1) / target;
+  return std::max(kAppendMinChunk, (per + kAppendMinChunk - 1) / kAppendMinChunk * kAppendMinChunk);
+}
+
+int append_parts(const Shape& sh, int nref) { return (nref + append_chunk(sh, nref) - 1) / append_chunk(sh, nref); }
+
+size_t append_ws_bytes(const Shape& sh) {
+  // Bound on the part count at any length the capacity allows: a chunk is
+  // at least kAppendMinChunk references and at least nref / target, so
+  // parts <= min(target, ceil(Rc / kAppendMinChunk)).  The code partials
+  // are laid out with the actual count, which never exceeds the bound.
+  const int ns = sh.n_streams();
+  const int target = (kAppendBlocks + ns - 1) / ns;
+  const int most = std::max(1, std::min(target, (sh.Rc + kAppendMinChunk - 1) / kAppendMinChunk));
+  return align_up(pcode_off(ns, most) + (size_t)ns * most * sh.dc * sh.elem(), 256);
+}
+
+hipError_t launch_append(const Shape& sh, const AppendArgs& a, void* ws, hipStream_t st) {
+  if (sh.bf16)
+    return sh.d == 128 ? launch_append_sd<BF16, 128>(sh, a, ws, st) : launch_append_sd<BF16, 64>(sh, a, ws, st);
+  return sh.d == 128 ? launch_append_sd<F32, 128>(sh, a, ws, st) : launch_append_sd<F32, 64>(sh, a, ws, st);
 }
 
 }  // namespace dkv

@@ -57,23 +57,6 @@ __device__ __forceinline__ uint32_t pk_bf16_rn(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
-// XCD-aware block order: block L runs on XCD L % 8 (workgroups are
-// dispatched to the eight XCDs round-robin).  Streams x, x + 8, ... are
-// given to XCD x, so the references a stream re-reads stay in one L2; within
-// an XCD, work items go in the given order across its streams.
-struct XcdItem {
-  int stream, item;   // stream < 0: no work
-};
-__device__ __forceinline__ XcdItem xcd_item(int ns) {
-  const int per = (ns + 7) / 8;
-  const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
-  XcdItem r;
-  r.stream = xcd + 8 * (k % per);
-  r.item = k / per;
-  if (r.stream >= ns) r.stream = -1;
-  return r;
-}
-inline unsigned xcd_grid(int ns, int items) { return 8u * (unsigned)((ns + 7) / 8) * (unsigned)items; }
 
 struct StreamId {
   int b, h, kv;

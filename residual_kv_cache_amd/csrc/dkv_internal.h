@@ -28,6 +28,24 @@ struct Shape {
   int elem() const { return bf16 ? 2 : 4; }
 };
 
+// XCD-aware block order: block L runs on XCD L % 8 (workgroups are
+// dispatched to the eight XCDs round-robin).  Streams x, x + 8, ... are
+// given to XCD x, so the references a stream re-reads stay in one L2; within
+// an XCD, work items go in the given order across its streams.
+struct XcdItem {
+  int stream, item;   // stream < 0: no work
+};
+__device__ __forceinline__ XcdItem xcd_item(int ns) {
+  const int per = (ns + 7) / 8;
+  const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
+  XcdItem r;
+  r.stream = xcd + 8 * (k % per);
+  r.item = k / per;
+  if (r.stream >= ns) r.stream = -1;
+  return r;
+}
+inline unsigned xcd_grid(int ns, int items) { return 8u * (unsigned)((ns + 7) / 8) * (unsigned)items; }
+
 // Tokens summed per block in the first mean stage.
 constexpr int kMeanChunk = 512;
 
@@ -137,10 +155,20 @@ struct AppendArgs {
   void* codes;
   void* idx;
   const void* mu;
+  void* const* events;       // DKV_APPEND_EVENTS hipEvent_t or NULL
 };
 
+// Append search: about kAppendBlocks blocks over all streams, each scoring a
+// chunk of at least kAppendMinChunk references (a multiple of it).
+constexpr int kAppendBlocks = 2048;
+constexpr int kAppendMinChunk = 64;
+int append_chunk(const Shape& sh, int nref);
+int append_parts(const Shape& sh, int nref);
+size_t append_ws_bytes(const Shape& sh);
+
 hipError_t launch_compress(const Shape& sh, const CompressArgs& a, hipStream_t st);
-hipError_t launch_append(const Shape& sh, const AppendArgs& a, hipStream_t st);
+// sh describes the cache after the append (T = position of the new token + 1).
+hipError_t launch_append(const Shape& sh, const AppendArgs& a, void* ws, hipStream_t st);
 hipError_t launch_decode(const Shape& sh, const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_fused(const Shape& sh, const DecodeArgs& a, hipStream_t st);
 

@@ -233,9 +233,9 @@ def test_capacity_picks_index_width():
     assert D.dkv_layout_check(lay) == 6
 
 
-def _append_status(lay, k, v, w, cache):
-    a = D.dkv_append_in(k, v, 0, 0, w, w, 0)
-    return D.lib().deltakv_append(ctypes.byref(lay), ctypes.byref(a), ctypes.byref(cache.c), None, 0, None)
+def _append_status(lay, k, v, w, cache, ws=1 << 30, ws_bytes=1 << 20):
+    a = D.dkv_append_in(k, v, 0, 0, w, w, 0, None)
+    return D.lib().deltakv_append(ctypes.byref(lay), ctypes.byref(a), ctypes.byref(cache.c), ws, ws_bytes, None)
 
 
 def test_append_rejects_bad_arguments():
@@ -250,4 +250,31 @@ def test_append_rejects_bad_arguments():
     assert _append_status(lay, P + 8, P, P, cache) == 4
     full = D.with_seq_len(lay, 101)
     assert _append_status(full, P, P, P, cache) == 2
-    assert D.dkv_append_workspace_bytes(lay) == 0
+    need = D.dkv_append_workspace_bytes(lay)
+    assert _append_status(lay, P, P, P, cache, ws=None) == 5
+    assert _append_status(lay, P, P, P, cache, ws_bytes=need - 1) == 5
+    assert _append_status(lay, P, P, P, cache, ws=P + 4) == 4
+
+
+@pytest.mark.parametrize("B,H,cap,s", [(1, 8, 101, 16), (1, 8, 32768 + 64, 16), (1, 8, 131072, 16), (16, 8, 32768, 16),
+                                       (1, 1, 131080, 2), (3, 2, 1000, 7)])
+def test_append_workspace_bounds_every_length(B, H, cap, s):
+    """The workspace covers the search partials of an append at every length
+    up to the capacity: per stream and part a (score, ordinal) pair and a
+    code, parts from the chunk rule (chunks of at least 64 references, about
+    2048 blocks in all)."""
+    _lib()
+    lay = D.make_layout("bf16", 128, 32, s, H, B, 1, capacity=cap)
+    need = D.dkv_append_workspace_bytes(lay)
+    ns = B * H * 2
+    target = -(-2048 // ns)
+    worst = 0
+    for t in range(1, cap):
+        if t % s == 0:
+            continue
+        nref = t // s + 1
+        chunk = max(64, -(-(-(-nref // target)) // 64) * 64)
+        worst = max(worst, -(-nref // chunk))
+    pad = lambda x: -(-x // 256) * 256
+    assert need >= pad(ns * worst * 8) + ns * worst * 32 * 2   # (score, ordinal) and a code per part
+    assert need <= pad(ns * max(worst, 1) * 8) + pad(ns * max(worst, 1) * 32 * 2) + 256

@@ -47,9 +47,10 @@ def _grow(cfg: K.Config, T0: int, spare: int, decode_at=()):
     wdk, wdv = GH.dev(inp.wdk.raw), GH.dev(inp.wdv.raw)
     ws = D.workspace(D.dkv_compress_workspace_bytes(lay0))
     D.deltakv_compress(lay0, k[:, :, :T0], v[:, :, :T0], wdk, wdv, cache, ws)
+    ws_a = D.workspace(D.dkv_append_workspace_bytes(lay0))
     outs = {}
     for t in range(T0, cfg.seq_len):
-        D.deltakv_append(D.with_seq_len(lay0, t), k[:, :, t], v[:, :, t], wdk, wdv, cache)
+        D.deltakv_append(D.with_seq_len(lay0, t), k[:, :, t], v[:, :, t], wdk, wdv, cache, ws_a)
         if t + 1 in decode_at:
             outs[t + 1] = GH.gpu_decode(D.with_seq_len(lay0, t + 1), cache, inp.q(t - T0).raw, inp)
     torch.cuda.synchronize()
