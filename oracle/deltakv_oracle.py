@@ -31,6 +31,11 @@ seedable instance computed here is:
     O7  k^_t = mu + x~_{ref(t)*s} + W_up @ c_t   (non-ref t)
         k^_t = mu + x~_t                         (ref t)        same for V
     O8  out_g = softmax_t(<q_g, k^_t> * scale) @ V^   over all T tokens
+  and two further operations on a compressed cache:
+    O9  decode over a chosen list of token positions: O8 with t running
+        over the list (entries at or past T skipped)
+    O10 append of token t with mu frozen: O3-O6 for that one token, against
+        the references at positions below t
 
 ``rnd`` rounds to the storage dtype (nearest, ties to even).  Storage
 "f64" makes rnd the identity; the pins use it to test the mathematics
@@ -332,6 +337,33 @@ def attend(q, khat, vhat, scale) -> np.ndarray:
         p = np.exp(sc - sc.max())
         out[g] = (p @ vhat[h]) / p.sum()
     return out
+
+
+def decode_selected(cache: dict, q, w_up_k, w_up_v, s, T, sel, scale=None) -> np.ndarray:
+    """Decode over a chosen subset of the cached tokens: only the tokens an
+    attention mask selects are reconstructed and attended to ([es] §2
+    "Metodología", on-demand reconstruction alongside sparse attention;
+    [de] §2, an engine that decompresses only the tokens a sparse mask
+    needs).  ``sel`` is [B][n] token positions; each entry is one term of
+    the softmax, so a position listed twice counts twice and the order does
+    not matter.  Entries at or past T are skipped; a sequence with no entry
+    left gets an output of zeros."""
+    B, H = cache["mu"].shape[:2]
+    d = cache["mu"].shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    out = []
+    for b in range(B):
+        toks = np.asarray([t for t in np.asarray(sel[b]).tolist() if t < T], np.int64)
+        Hq = np.asarray(q[b]).shape[0]
+        if len(toks) == 0:
+            out.append(np.zeros((Hq, d)))
+            continue
+        kh = np.stack([reconstruct_stream(cache["mu"][b, h, 0], cache["refs"][b, h, 0], cache["idx"][b, h, 0],
+                                          cache["codes"][b, h, 0], w_up_k, s, T)[toks] for h in range(H)])
+        vh = np.stack([reconstruct_stream(cache["mu"][b, h, 1], cache["refs"][b, h, 1], cache["idx"][b, h, 1],
+                                          cache["codes"][b, h, 1], w_up_v, s, T)[toks] for h in range(H)])
+        out.append(attend(np.asarray(q[b], np.float64), kh, vh, scale))
+    return np.stack(out)
 
 
 def decode(cache: dict, q, w_up_k, w_up_v, s, T, scale=None) -> np.ndarray:

@@ -30,6 +30,10 @@ PINS = [
     lambda: P.test_append_equals_compress_with_frozen_mean("bf16", 33, 70, 8),
     lambda: P.test_append_search_matches_brute_force_integer_data(97, 5, 6, 6),
     P.test_append_hand_worked,
+    P.test_selected_every_token_is_full_decode,
+    P.test_selected_is_dense_attention_over_the_subset,
+    P.test_selected_order_duplicates_and_single_token,
+    P.test_selected_skips_positions_past_the_end,
 ]
 
 
@@ -162,6 +166,25 @@ def _append_factory(*, no_causal=False, last_tie=False, plus_ref=False, rounded_
     return append_token
 
 
+_ORIG_SEL = OD.decode_selected
+
+
+def _sel_ignores_list(cache, q, w_up_k, w_up_v, s, T, sel, scale=None):
+    return OD.decode(cache, q, w_up_k, w_up_v, s, T, scale)
+
+
+def _sel_clamps_past_end(cache, q, w_up_k, w_up_v, s, T, sel, scale=None):
+    return _ORIG_SEL(cache, q, w_up_k, w_up_v, s, T, np.minimum(np.asarray(sel), T - 1), scale)
+
+
+def _sel_unique(cache, q, w_up_k, w_up_v, s, T, sel, scale=None):
+    return _ORIG_SEL(cache, q, w_up_k, w_up_v, s, T, [np.unique(np.asarray(r)) for r in sel], scale)
+
+
+def _sel_off_by_one(cache, q, w_up_k, w_up_v, s, T, sel, scale=None):
+    return _ORIG_SEL(cache, q, w_up_k, w_up_v, s, T, np.asarray(sel) + 1, scale)
+
+
 def _stream_bytes_no_idx(T, s, d, dc, storage):
     e = OD.ELEM_BYTES[storage]
     R = OD.n_refs(T, s)
@@ -191,6 +214,10 @@ MUTATIONS = {
     "append: + reference instead of -": ("append_token", _append_factory(plus_ref=True)),
     "append: residual of the rounded token": ("append_token", _append_factory(rounded_token=True)),
     "append: raw dot product, no normalisation": ("append_token", _append_factory(raw_dot=True)),
+    "selected decode: attends every token": ("decode_selected", _sel_ignores_list),
+    "selected decode: clamps positions past the end": ("decode_selected", _sel_clamps_past_end),
+    "selected decode: drops duplicate entries": ("decode_selected", _sel_unique),
+    "selected decode: positions off by one": ("decode_selected", _sel_off_by_one),
 }
 
 

@@ -482,3 +482,74 @@ def test_append_hand_worked():
     assert c["idx"] == 2 and c["code"].tolist() == [-3.0]
     # The token at position 3 cannot see the reference at position 4.
     assert O.append_token(mu, refs, [3.0, 2.0], 3, 2, wd, "f64")["idx"] == 1
+
+
+# ---------------------------------------------------------------------------
+# Decode over a chosen subset of tokens ([es] §2 "Metodología": only the
+# tokens a sparse-attention mask selects are reconstructed).
+# ---------------------------------------------------------------------------
+
+def _small_cache(storage="f64", s=3, T=41, seed=21):
+    rng = np.random.default_rng(seed)
+    B, H, Hq, d, dc = 2, 2, 4, 8, 3
+    k = rng.standard_normal((B, H, T, d)) * 2 + 1
+    v = rng.standard_normal((B, H, T, d)) - 1
+    w = np.linalg.qr(rng.standard_normal((d, dc)))[0]
+    cache = O.compress(k, v, s, w.T, w.T, storage)
+    q = rng.standard_normal((B, Hq, d))
+    return k, v, w, cache, q
+
+
+def test_selected_every_token_is_full_decode():
+    k, v, w, cache, q = _small_cache()
+    T = k.shape[2]
+    full = O.decode(cache, q, w, w, 3, T)
+    sel = np.tile(np.arange(T), (2, 1))
+    assert np.abs(O.decode_selected(cache, q, w, w, 3, T, sel) - full).max() < 1e-13
+
+
+def test_selected_is_dense_attention_over_the_subset():
+    """s = 1 keeps every token whole: selective decode is textbook attention
+    over the selected keys and values, one term per list entry."""
+    rng = np.random.default_rng(4)
+    B, H, Hq, T, d = 1, 2, 4, 30, 6
+    k = rng.standard_normal((B, H, T, d)) + 2
+    v = rng.standard_normal((B, H, T, d))
+    w = np.linalg.qr(rng.standard_normal((d, 2)))[0]
+    cache = O.compress(k, v, 1, w.T, w.T, "f64")
+    q = rng.standard_normal((B, Hq, d))
+    sel = np.array([[3, 4, 11, 17, 29, 11]])   # 11 listed twice: two softmax terms
+    out = O.decode_selected(cache, q, w, w, 1, T, sel)
+    ref = _dense_attention_loops(q[0], k[0][:, sel[0]], v[0][:, sel[0]], 1 / math.sqrt(d))
+    assert np.abs(out[0] - ref).max() < 1e-12
+
+
+def test_selected_order_duplicates_and_single_token():
+    k, v, w, cache, q = _small_cache()
+    T = k.shape[2]
+    rng = np.random.default_rng(5)
+    sel = np.stack([np.sort(rng.choice(T, 12, replace=False)) for _ in range(2)])
+    base = O.decode_selected(cache, q, w, w, 3, T, sel)
+    shuffled = np.stack([rng.permutation(r) for r in sel])
+    assert np.abs(O.decode_selected(cache, q, w, w, 3, T, shuffled) - base).max() < 1e-13
+    twice = np.concatenate([sel, sel[:, ::-1]], axis=1)       # every entry twice: same softmax
+    assert np.abs(O.decode_selected(cache, q, w, w, 3, T, twice) - base).max() < 1e-13
+    # One token: the softmax has one term, so every query head of a KV head
+    # returns that token's reconstructed value row.
+    one = O.decode_selected(cache, q, w, w, 3, T, np.array([[7], [9]]))
+    for b, t in ((0, 7), (1, 9)):
+        for h in range(2):
+            vh = O.reconstruct_stream(cache["mu"][b, h, 1], cache["refs"][b, h, 1], cache["idx"][b, h, 1],
+                                      cache["codes"][b, h, 1], w, 3, T)
+            assert np.abs(one[b, 2 * h:2 * h + 2] - vh[t]).max() < 1e-13
+
+
+def test_selected_skips_positions_past_the_end():
+    k, v, w, cache, q = _small_cache()
+    T = k.shape[2]
+    sel = np.array([[2, 5, T, T + 7], [T + 1, T + 2, T + 3, T + 4]])
+    out = O.decode_selected(cache, q, w, w, 3, T, sel)
+    first = {n: a[:1] for n, a in cache.items()}
+    want0 = O.decode_selected(first, q[:1], w, w, 3, T, np.array([[2, 5]]))[0]
+    assert np.abs(out[0] - want0).max() < 1e-13
+    assert np.all(out[1] == 0.0)
