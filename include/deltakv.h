@@ -218,6 +218,23 @@ typedef struct dkv_append_in {
   void* const* stage_events;
 } dkv_append_in;
 
+/*
+ * Token list of a selective decode (deltakv_decode_attn_sel).
+ *   tokens     device [B][n_sel] uint32 token positions, 4-byte aligned;
+ *              row b lists the tokens sequence b attends to.  Each entry is
+ *              one term of the softmax: a position listed twice counts
+ *              twice, and the order of a row does not matter (ascending
+ *              order reads the cache in order and is fastest).  Entries at
+ *              or past seq_len are skipped.
+ *   n_sel      entries per sequence, 1 .. 2^30
+ *   reserved   must be 0
+ */
+typedef struct dkv_token_sel {
+  const uint32_t* tokens;
+  uint32_t n_sel;
+  uint32_t reserved;
+} dkv_token_sel;
+
 /* DKV_ABI_VERSION of the loaded library. */
 uint32_t dkv_abi_version(void);
 
@@ -286,6 +303,23 @@ dkv_status deltakv_append(const dkv_layout* layout, const dkv_append_in* in, con
  */
 dkv_status deltakv_decode_attn(const dkv_layout* layout, const dkv_cache* cache, const dkv_decode_in* in,
                                void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Decode attention over a chosen subset of the cached tokens: for each
+ * sequence b, softmax(q k^_t^T * scale) v^_t over the entries t of row b of
+ * sel->tokens, every other token left untouched (DeltaKV explainer, Spanish
+ * page, Resumen Técnico §2 "Metodología": with a sparse-attention method
+ * only the tokens its mask keeps are reconstructed; German page §2, an
+ * engine that decompresses only those tokens).  A sequence whose row holds
+ * no entry below seq_len gets an output of zeros.  Arguments as for
+ * deltakv_decode_attn; in->n_splits = 0 takes
+ * dkv_decode_sel_auto_splits, which never exceeds dkv_decode_auto_splits,
+ * so a workspace of dkv_decode_workspace_bytes(layout, n_q_heads, 0) bytes
+ * serves both calls.  stage_events as for deltakv_decode_attn.
+ */
+uint32_t dkv_decode_sel_auto_splits(const dkv_layout* layout, uint32_t n_q_heads, uint32_t n_sel);
+dkv_status deltakv_decode_attn_sel(const dkv_layout* layout, const dkv_cache* cache, const dkv_decode_in* in,
+                                   const dkv_token_sel* sel, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,8 @@ STATUS = {0: "DKV_OK", 1: "DKV_ERR_NULL", 2: "DKV_ERR_SHAPE", 3: "DKV_ERR_DTYPE"
           5: "DKV_ERR_WORKSPACE", 6: "DKV_ERR_UNSUPPORTED", 7: "DKV_ERR_VERSION", 8: "DKV_ERR_DEVICE"}
 EXPORTS = ["dkv_abi_version", "dkv_status_str", "dkv_layout_check", "dkv_cache_bytes", "dkv_cache_carve",
            "dkv_compress_workspace_bytes", "dkv_decode_auto_splits", "dkv_decode_workspace_bytes",
-           "dkv_append_workspace_bytes", "deltakv_compress", "deltakv_append", "deltakv_decode_attn"]
+           "dkv_append_workspace_bytes", "deltakv_compress", "deltakv_append", "deltakv_decode_attn",
+           "dkv_decode_sel_auto_splits", "deltakv_decode_attn_sel"]
 
 
 class DeltaKVError(RuntimeError):
@@ -75,6 +76,10 @@ class dkv_append_in(ctypes.Structure):
                 ("w_head_stride", ctypes.c_int64), ("stage_events", ctypes.c_void_p)]
 
 
+class dkv_token_sel(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_void_p), ("n_sel", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+
 class dkv_decode_in(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("w_up_k", ctypes.c_void_p), ("w_up_v", ctypes.c_void_p),
                 ("w_head_stride", ctypes.c_int64), ("n_q_heads", ctypes.c_uint32), ("n_splits", ctypes.c_uint32),
@@ -114,6 +119,10 @@ def lib() -> ctypes.CDLL:
         h.dkv_append_workspace_bytes.argtypes = [P(dkv_layout)]
         h.deltakv_append.argtypes = [P(dkv_layout), P(dkv_append_in), P(dkv_cache), ctypes.c_void_p,
                                      ctypes.c_size_t, ctypes.c_void_p]
+        h.dkv_decode_sel_auto_splits.restype = ctypes.c_uint32
+        h.dkv_decode_sel_auto_splits.argtypes = [P(dkv_layout), ctypes.c_uint32, ctypes.c_uint32]
+        h.deltakv_decode_attn_sel.argtypes = [P(dkv_layout), P(dkv_cache), P(dkv_decode_in), P(dkv_token_sel),
+                                              ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         if h.dkv_abi_version() != ABI_VERSION:
             raise RuntimeError("libdeltakv.so ABI version mismatch")
         _lib_handle = h
@@ -256,6 +265,29 @@ def deltakv_decode_attn(layout: dkv_layout, cache: Cache, q: torch.Tensor, w_up_
                                      ctypes.c_void_p(_stream(stream))), "deltakv_decode_attn")
 
 
+def deltakv_decode_attn_sel(layout: dkv_layout, cache: Cache, q: torch.Tensor, w_up_k: torch.Tensor,
+                            w_up_v: torch.Tensor, tokens: torch.Tensor, out: torch.Tensor, ws: torch.Tensor,
+                            n_splits: int = 0, softmax_scale: float = 0.0, w_head_stride: int = 0, stream=None,
+                            stage_events=None) -> None:
+    """Decode over a token list: tokens [B][n_sel] int32/uint32 positions
+    (contiguous, on the device); other arguments as deltakv_decode_attn."""
+    if not q.is_contiguous() or not out.is_contiguous() or out.dtype != torch.float32:
+        raise ValueError("q and out must be contiguous; out must be float32")
+    if not tokens.is_contiguous() or tokens.element_size() != 4 or tokens.dim() != 2:
+        raise ValueError("tokens must be a contiguous [B][n_sel] tensor of 32-bit positions")
+    a = dkv_decode_in(_ptr(q), _ptr(w_up_k), _ptr(w_up_v), w_head_stride, q.shape[1], n_splits,
+                      softmax_scale, 0, _ptr(out), _events(stage_events))
+    sel = dkv_token_sel(_ptr(tokens), tokens.shape[1], 0)
+    _check(lib().deltakv_decode_attn_sel(ctypes.byref(layout), ctypes.byref(cache.c), ctypes.byref(a),
+                                         ctypes.byref(sel), ctypes.c_void_p(ws.data_ptr()),
+                                         ws.numel() * ws.element_size(), ctypes.c_void_p(_stream(stream))),
+           "deltakv_decode_attn_sel")
+
+
+def dkv_decode_sel_auto_splits(layout: dkv_layout, n_q_heads: int, n_sel: int) -> int:
+    return lib().dkv_decode_sel_auto_splits(ctypes.byref(layout), n_q_heads, n_sel)
+
+
 def deltakv_append(layout: dkv_layout, k: torch.Tensor, v: torch.Tensor, w_down_k: torch.Tensor,
                    w_down_v: torch.Tensor, cache: Cache, ws: torch.Tensor, w_head_stride: int = 0, stream=None,
                    stage_events=None) -> None:
@@ -282,7 +314,8 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
 
 
 __all__ = ["lib", "make_layout", "with_seq_len", "dkv_layout", "dkv_cache", "dkv_compress_in", "dkv_append_in",
-           "dkv_decode_in", "Cache", "deltakv_append", "dkv_append_workspace_bytes",
+           "dkv_decode_in", "dkv_token_sel", "Cache", "deltakv_append", "dkv_append_workspace_bytes",
+           "deltakv_decode_attn_sel", "dkv_decode_sel_auto_splits",
            "DeltaKVError", "dkv_layout_check", "dkv_cache_bytes", "dkv_cache_carve", "dkv_compress_workspace_bytes",
            "dkv_decode_auto_splits", "dkv_decode_workspace_bytes", "deltakv_compress", "deltakv_decode_attn",
            "workspace", "storage_torch_dtype", "EXPORTS", "LIB_PATH"]

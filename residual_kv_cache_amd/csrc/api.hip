@@ -253,49 +253,103 @@ dkv_status deltakv_append(const dkv_layout* layout, const dkv_append_in* in, con
   return from_hip(dkv::launch_append(s2, a, ws, (hipStream_t)stream));
 }
 
-dkv_status deltakv_decode_attn(const dkv_layout* layout, const dkv_cache* cache, const dkv_decode_in* in, void* ws,
-                               size_t ws_bytes, void* stream) {
-  Shape sh;
-  dkv_status st = check_layout(layout, &sh);
+}  // extern "C"
+
+namespace {
+
+// Validation and argument set-up shared by the two decode entry points;
+// `sel_splits` > 0 replaces the automatic split count (selective decode).
+dkv_status decode_setup(const dkv_layout* layout, const dkv_cache* cache, const dkv_decode_in* in, void* ws,
+                        size_t ws_bytes, void* stream, int sel_splits, Shape* sh, dkv::DecodeArgs* a) {
+  dkv_status st = check_layout(layout, sh);
   if (st != DKV_OK) return st;
   if (!in) return DKV_ERR_NULL;
-  if ((st = check_cache(cache, sh)) != DKV_OK) return st;
+  if ((st = check_cache(cache, *sh)) != DKV_OK) return st;
   if (!in->q || !in->w_up_k || !in->w_up_v || !in->out) return DKV_ERR_NULL;
   if (!aligned16(in->q) || !aligned16(in->w_up_k) || !aligned16(in->w_up_v) || !aligned16(in->out))
     return DKV_ERR_ALIGN;
   if (in->reserved != 0) return DKV_ERR_SHAPE;
-  if (in->n_q_heads == 0 || in->n_q_heads % sh.H != 0) return DKV_ERR_SHAPE;
-  if (in->n_q_heads / sh.H > 16) return DKV_ERR_UNSUPPORTED;
+  if (in->n_q_heads == 0 || in->n_q_heads % sh->H != 0) return DKV_ERR_SHAPE;
+  if (in->n_q_heads / sh->H > 16) return DKV_ERR_UNSUPPORTED;
   if (in->n_splits > 1024) return DKV_ERR_UNSUPPORTED;
   if (in->w_head_stride < 0) return DKV_ERR_SHAPE;
-  if (in->w_head_stride != 0 && in->w_head_stride < (int64_t)sh.d * sh.dc) return DKV_ERR_SHAPE;
+  if (in->w_head_stride != 0 && in->w_head_stride < (int64_t)sh->d * sh->dc) return DKV_ERR_SHAPE;
   if (!(in->softmax_scale >= 0.f) || isinf(in->softmax_scale)) return DKV_ERR_SHAPE;
-  const int G = (int)(in->n_q_heads / sh.H);
-  const int splits = in->n_splits ? (int)in->n_splits : (int)auto_splits(sh, G);
-  const size_t need = dkv::decode_ws_bytes(sh, G, splits);
+  const int G = (int)(in->n_q_heads / sh->H);
+  const int splits = in->n_splits ? (int)in->n_splits : sel_splits > 0 ? sel_splits : (int)auto_splits(*sh, G);
+  const size_t need = dkv::decode_ws_bytes(*sh, G, splits);
   if (!ws || ws_bytes < need) return DKV_ERR_WORKSPACE;
   if (!aligned16(ws)) return DKV_ERR_ALIGN;
 
+  a->q = in->q;
+  a->wuk = in->w_up_k;
+  a->wuv = in->w_up_v;
+  a->w_hs = in->w_head_stride;
+  a->G = G;
+  a->Hq = (int)in->n_q_heads;
+  a->splits = splits;
+  a->scale = in->softmax_scale > 0.f ? in->softmax_scale : 1.0f / sqrtf((float)sh->d);
+  a->out = in->out;
+  a->refs = cache->refs;
+  a->codes = cache->codes;
+  a->idx = cache->idx;
+  a->mu = cache->mu;
+  a->score = (float*)ws;
+  a->qp = (float*)((char*)ws + dkv::ws_qp_off(*sh, G));
+  a->part = (float*)((char*)ws + dkv::ws_part_off(*sh, G));
+  a->events = in->stage_events;
+  a->sel = nullptr;
+  a->n_sel = 0;
+  return check_events(a->events, stream);
+}
+
+// Automatic split count of a selective decode: the full decode's count,
+// lowered to keep at least 256 list entries per split (so a workspace sized
+// for deltakv_decode_attn always suffices).
+uint32_t sel_auto_splits(const Shape& sh, int G, uint32_t n_sel) {
+  const uint32_t full = auto_splits(sh, G);
+  const uint32_t by_len = (n_sel + 255) / 256;
+  const uint32_t s = by_len < full ? by_len : full;
+  return s < 1 ? 1 : s;
+}
+
+}  // namespace
+
+extern "C" {
+
+dkv_status deltakv_decode_attn(const dkv_layout* layout, const dkv_cache* cache, const dkv_decode_in* in, void* ws,
+                               size_t ws_bytes, void* stream) {
+  Shape sh;
   dkv::DecodeArgs a;
-  a.q = in->q;
-  a.wuk = in->w_up_k;
-  a.wuv = in->w_up_v;
-  a.w_hs = in->w_head_stride;
-  a.G = G;
-  a.Hq = (int)in->n_q_heads;
-  a.splits = splits;
-  a.scale = in->softmax_scale > 0.f ? in->softmax_scale : 1.0f / sqrtf((float)sh.d);
-  a.out = in->out;
-  a.refs = cache->refs;
-  a.codes = cache->codes;
-  a.idx = cache->idx;
-  a.mu = cache->mu;
-  a.score = (float*)ws;
-  a.qp = (float*)((char*)ws + dkv::ws_qp_off(sh, G));
-  a.part = (float*)((char*)ws + dkv::ws_part_off(sh, G));
-  a.events = in->stage_events;
-  if ((st = check_events(a.events, stream)) != DKV_OK) return st;
+  const dkv_status st = decode_setup(layout, cache, in, ws, ws_bytes, stream, 0, &sh, &a);
+  if (st != DKV_OK) return st;
   return from_hip(dkv::launch_decode(sh, a, (hipStream_t)stream));
+}
+
+uint32_t dkv_decode_sel_auto_splits(const dkv_layout* layout, uint32_t n_q_heads, uint32_t n_sel) {
+  Shape sh;
+  if (check_layout(layout, &sh) != DKV_OK) return 0;
+  if (n_q_heads == 0 || n_q_heads % sh.H != 0 || n_q_heads / sh.H > 16 || n_sel == 0) return 0;
+  return sel_auto_splits(sh, (int)(n_q_heads / sh.H), n_sel);
+}
+
+dkv_status deltakv_decode_attn_sel(const dkv_layout* layout, const dkv_cache* cache, const dkv_decode_in* in,
+                                   const dkv_token_sel* sel, void* ws, size_t ws_bytes, void* stream) {
+  if (!sel) return DKV_ERR_NULL;
+  if (!sel->tokens) return DKV_ERR_NULL;
+  if (sel->n_sel == 0 || sel->n_sel > (1u << 30) || sel->reserved != 0) return DKV_ERR_SHAPE;
+  if ((uintptr_t)sel->tokens % 4) return DKV_ERR_ALIGN;
+  Shape sh;
+  const dkv_status lst = check_layout(layout, &sh);
+  if (lst != DKV_OK) return lst;
+  const int G = in && in->n_q_heads && in->n_q_heads % sh.H == 0 ? (int)(in->n_q_heads / sh.H) : 1;
+  dkv::DecodeArgs a;
+  const dkv_status st =
+      decode_setup(layout, cache, in, ws, ws_bytes, stream, (int)sel_auto_splits(sh, G, sel->n_sel), &sh, &a);
+  if (st != DKV_OK) return st;
+  a.sel = sel->tokens;
+  a.n_sel = (int)sel->n_sel;
+  return from_hip(dkv::launch_decode_sel(sh, a, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -31,8 +31,6 @@ namespace dkv {
 namespace {
 
 typedef const __attribute__((address_space(1))) uint32_t* GWords;
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // E consecutive storage elements as raw 32-bit words.
 template <class S, int E>

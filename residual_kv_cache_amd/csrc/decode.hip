@@ -240,6 +240,189 @@ __global__ __launch_bounds__(256) void k_split_valu(DecodeArgs a, Shape sh) {
 }
 
 // ---------------------------------------------------------------------------
+// split over a token list (selective decode): one block per (split, b, h);
+// the split takes list entries [i0, i1) of sequence b, and its 4 waves take
+// 64-entry chunks in turn.  Score phase: lane = entry, whose position t is
+// either a reference (t mod s = 0: row t / s, no code) or coded row
+// t - t/s - 1; entries at or past T score -inf.  Accumulate phase as in
+// k_split_valu, eight entries at a time so that their value rows are loaded
+// together.  Partials have the k_split_valu layout.
+// ---------------------------------------------------------------------------
+
+template <class S, int D, int GP>
+__global__ __launch_bounds__(256) void k_split_sel(DecodeArgs a, Shape sh) {
+  constexpr int RPL = D / 64;            // head-dim columns per lane
+  constexpr int UN = 8;                  // entries per accumulate step
+  __shared__ float qp_l[GP][128];
+  __shared__ float mw[4][GP];
+  __shared__ float merge[GP][2 * D + 1];   // acc_r | acc_c | l
+  const int sp = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int b = bh / sh.H;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int G = a.G, dc = sh.dc;
+  const int i0 = (int)((int64_t)a.n_sel * sp / a.splits), i1 = (int)((int64_t)a.n_sel * (sp + 1) / a.splits);
+  const uint32_t* sel = a.sel + (size_t)b * a.n_sel;
+
+  for (int p = threadIdx.x; p < G * dc; p += 256) qp_l[p / dc][p % dc] = a.qp[(size_t)bh * G * dc + p];
+  __syncthreads();
+
+  const size_t sK = (size_t)bh * 2, sV = sK + 1;
+  const int Gs = score_cols(G);
+  const float* score = a.score + (size_t)bh * sh.R * Gs;
+  const typename S::T* refsV = (const typename S::T*)a.refs + sV * sh.Rc * D;
+  const typename S::T* codesK = (const typename S::T*)a.codes + sK * sh.Nc * dc;
+  const typename S::T* codesV = (const typename S::T*)a.codes + sV * sh.Nc * dc;
+  const bool has_codes = sh.N > 0;
+
+  float m[GP], lsum[GP], accr[GP][RPL], accc[GP][2];
+#pragma unroll
+  for (int g = 0; g < GP; ++g) {
+    m[g] = -INFINITY; lsum[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < RPL; ++e) accr[g][e] = 0.f;
+    accc[g][0] = accc[g][1] = 0.f;
+  }
+
+  const int nchunks = (i1 - i0 + 63) / 64;
+  for (int c = wave; c < nchunks; c += 4) {
+    const int base = i0 + c * 64;
+    const int cnt = min(64, i1 - base);
+    // ---- scores: lane = entry ----
+    const uint32_t t = lane < cnt ? sel[base + lane] : 0xFFFFFFFFu;
+    const bool valid = t < (uint32_t)sh.T;
+    const int tt = valid ? (int)t : 0;
+    const int r = tt / sh.s;
+    const bool coded = valid && tt - r * sh.s != 0;
+    const int u = coded ? tt - r - 1 : 0;     // coded row (0 when unused)
+    int rk = r, rv = r;
+    if (has_codes) {
+      // Ordinals come from caller memory: clamp so a corrupt cache can never
+      // address outside the reference arrays.
+      const int ik = min((int)load_idx(a.idx, sK * sh.Nc + u, sh.idx_bytes), sh.R - 1);
+      const int iv = min((int)load_idx(a.idx, sV * sh.Nc + u, sh.idx_bytes), sh.R - 1);
+      rk = coded ? ik : r;
+      rv = coded ? iv : r;
+    }
+    float sc[GP];
+#pragma unroll
+    for (int g = 0; g < GP; ++g) sc[g] = g < G ? score[(size_t)rk * Gs + g] : 0.f;
+    if (has_codes) {
+      float cd[GP];
+#pragma unroll
+      for (int g = 0; g < GP; ++g) cd[g] = 0.f;
+      for (int j0 = 0; j0 < dc; j0 += 8) {
+        float cv[8];
+        load8<S>(codesK + (size_t)u * dc + j0, cv);
+#pragma unroll
+        for (int g = 0; g < GP; ++g)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) cd[g] = fmaf(qp_l[g][j0 + i], cv[i], cd[g]);
+      }
+#pragma unroll
+      for (int g = 0; g < GP; ++g) sc[g] += coded ? cd[g] : 0.f;
+    }
+#pragma unroll
+    for (int g = 0; g < GP; ++g) sc[g] = valid ? sc[g] : -INFINITY;
+
+    float p[GP];
+#pragma unroll
+    for (int g = 0; g < GP; ++g) {
+      if (g >= G) { p[g] = 0.f; continue; }
+      const float mn = fmaxf(m[g], wave_max(sc[g]));
+      if (mn == -INFINITY) { p[g] = 0.f; continue; }   // nothing valid yet
+      const float alpha = exp2f(m[g] - mn);           // m = -inf on the first valid chunk -> 0
+      p[g] = exp2f(sc[g] - mn);
+      m[g] = mn;
+      lsum[g] = lsum[g] * alpha + p[g];
+#pragma unroll
+      for (int e = 0; e < RPL; ++e) accr[g][e] *= alpha;
+      accc[g][0] *= alpha;
+      accc[g][1] *= alpha;
+    }
+
+    // ---- accumulate: the wave walks the chunk's entries ----
+    const int cl0 = min(lane, dc - 1), cl1 = min(lane + 64, dc - 1);
+    for (int k0 = 0; k0 < cnt; k0 += UN) {
+      float xr[UN][RPL], c0[UN], c1[UN];
+#pragma unroll
+      for (int i = 0; i < UN; ++i) {
+        const int k = min(k0 + i, cnt - 1);
+        const int rr = __builtin_amdgcn_readlane(rv, k);
+        const int uu = __builtin_amdgcn_readlane(u, k);
+#pragma unroll
+        for (int e = 0; e < RPL; ++e) xr[i][e] = S::load(refsV[(size_t)rr * D + lane * RPL + e]);
+        c0[i] = has_codes ? S::load(codesV[(size_t)uu * dc + cl0]) : 0.f;
+        c1[i] = has_codes ? S::load(codesV[(size_t)uu * dc + cl1]) : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < UN; ++i) {
+        const int k = k0 + i;
+        if (k >= cnt) break;
+        const bool ck = __builtin_amdgcn_readlane((int)coded, k) != 0;
+        const float v0 = ck && lane < dc ? c0[i] : 0.f;
+        const float v1 = ck && lane + 64 < dc ? c1[i] : 0.f;
+#pragma unroll
+        for (int g = 0; g < GP; ++g) {
+          if (g >= G) break;
+          const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p[g]), k));
+#pragma unroll
+          for (int e = 0; e < RPL; ++e) accr[g][e] = fmaf(w, xr[i][e], accr[g][e]);
+          accc[g][0] = fmaf(w, v0, accc[g][0]);
+          accc[g][1] = fmaf(w, v1, accc[g][1]);
+        }
+      }
+    }
+  }
+
+  // Merge the four waves in a fixed order.
+#pragma unroll
+  for (int g = 0; g < GP; ++g) {
+    lsum[g] = wave_sum(lsum[g]);
+    if (lane == 0) mw[wave][g] = m[g];
+  }
+  __syncthreads();
+  float mb[GP], wgt[GP];
+#pragma unroll
+  for (int g = 0; g < GP; ++g) {
+    mb[g] = fmaxf(fmaxf(mw[0][g], mw[1][g]), fmaxf(mw[2][g], mw[3][g]));
+    wgt[g] = m[g] == -INFINITY ? 0.f : exp2f(m[g] - mb[g]);
+  }
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+      for (int g = 0; g < G; ++g) {
+#pragma unroll
+        for (int e = 0; e < RPL; ++e) {
+          const int i = lane * RPL + e;
+          const float v = accr[g][e] * wgt[g];
+          merge[g][i] = w == 0 ? v : merge[g][i] + v;
+        }
+        if (lane < dc) merge[g][D + lane] = (w == 0 ? 0.f : merge[g][D + lane]) + accc[g][0] * wgt[g];
+        if (lane + 64 < dc) merge[g][D + lane + 64] = (w == 0 ? 0.f : merge[g][D + lane + 64]) + accc[g][1] * wgt[g];
+        if (lane == 0) merge[g][2 * D] = (w == 0 ? 0.f : merge[g][2 * D]) + lsum[g] * wgt[g];
+      }
+    }
+    __syncthreads();
+  }
+  const int rec = partial_rec(sh);
+  float* out = a.part + ((size_t)bh * a.splits + sp) * G * rec;
+  for (int p = threadIdx.x; p < G * rec; p += 256) {
+    const int g = p / rec, f = p % rec;
+    float v = 0.f;
+    if (f == 0) {
+      v = fmaxf(fmaxf(mw[0][g], mw[1][g]), fmaxf(mw[2][g], mw[3][g]));
+    } else if (f == 1) {
+      v = merge[g][2 * D];
+    } else if (f < 2 + dc) {
+      v = merge[g][D + f - 2];
+    } else if (f < 2 + dc + D) {
+      v = merge[g][f - 2 - dc];
+    }
+    out[p] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // combine: one block per (b, query head); merges the splits, then
 // out = mu_V + (acc_r + W_up_V acc_c) / l.  grid B*Hq, block 128.
 // ---------------------------------------------------------------------------
@@ -268,7 +451,8 @@ __global__ __launch_bounds__(128) void k_combine(DecodeArgs a, Shape sh) {
     l_s = l;
   }
   __syncthreads();
-  const float mx = mx_s, inv_l = 1.0f / l_s;
+  // l = 0 only when a selective decode attended no token: the output is 0.
+  const float mx = mx_s, inv_l = l_s > 0.f ? 1.0f / l_s : 0.f;
   const int i = threadIdx.x;
   if (i < dc) {
     float c = 0.f;
@@ -289,7 +473,7 @@ __global__ __launch_bounds__(128) void k_combine(DecodeArgs a, Shape sh) {
     float u = 0.f;
     for (int j = 0; j < dc; ++j) u = fmaf(S::load(wu[(size_t)i * dc + j]), accc[j], u);
     const float muv = ld<S>(a.mu, ((size_t)bh * 2 + 1) * D + i);
-    a.out[((size_t)b * a.Hq + gq) * D + i] = muv + (r + u) * inv_l;
+    a.out[((size_t)b * a.Hq + gq) * D + i] = l_s > 0.f ? muv + (r + u) * inv_l : 0.f;
   }
 }
 
@@ -313,7 +497,31 @@ hipError_t launch_decode_sd(const Shape& sh, const DecodeArgs& a, hipStream_t st
   return launch(k_combine<S, D>, dim3(sh.B * a.Hq), 128, st, ev_start(a.events, 2), ev_stop(a.events, 2), a, sh);
 }
 
+template <class S, int D>
+hipError_t launch_decode_sel_sd(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
+  hipError_t e = decode_fused_supported(sh, a.G, 1)
+                     ? launch_refscore_mfma(sh, a, st)
+                     : launch(k_refscore<S, D>, dim3((sh.R + 63) / 64, sh.B * sh.H), 256, st, ev_start(a.events, 0),
+                              ev_stop(a.events, 0), a, sh);
+  if (e != hipSuccess) return e;
+  const dim3 grid(a.splits, sh.B * sh.H);
+  const hipEvent_t e0 = ev_start(a.events, 1), e1 = ev_stop(a.events, 1);
+  if (a.G <= 1) e = launch(k_split_sel<S, D, 1>, grid, 256, st, e0, e1, a, sh);
+  else if (a.G <= 2) e = launch(k_split_sel<S, D, 2>, grid, 256, st, e0, e1, a, sh);
+  else if (a.G <= 4) e = launch(k_split_sel<S, D, 4>, grid, 256, st, e0, e1, a, sh);
+  else if (a.G <= 8) e = launch(k_split_sel<S, D, 8>, grid, 256, st, e0, e1, a, sh);
+  else e = launch(k_split_sel<S, D, 16>, grid, 256, st, e0, e1, a, sh);
+  if (e != hipSuccess) return e;
+  return launch(k_combine<S, D>, dim3(sh.B * a.Hq), 128, st, ev_start(a.events, 2), ev_stop(a.events, 2), a, sh);
+}
+
 }  // namespace
+
+hipError_t launch_decode_sel(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
+  if (sh.bf16)
+    return sh.d == 128 ? launch_decode_sel_sd<BF16, 128>(sh, a, st) : launch_decode_sel_sd<BF16, 64>(sh, a, st);
+  return sh.d == 128 ? launch_decode_sel_sd<F32, 128>(sh, a, st) : launch_decode_sel_sd<F32, 64>(sh, a, st);
+}
 
 hipError_t launch_decode(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
   if (decode_fused_supported(sh, a.G, a.splits)) return launch_decode_fused(sh, a, st);

@@ -638,11 +638,16 @@ int decode_fused_auto_splits(const Shape& sh) {
   return (int)s;
 }
 
-hipError_t launch_decode_fused(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
+hipError_t launch_refscore_mfma(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
   const int BH8 = 8 * ((sh.B * sh.H + 7) / 8);
   const int chunks = (sh.R + kRsRefs - 1) / kRsRefs;
-  hipError_t e = launch(k_refscore_mfma, dim3(BH8 * chunks), 256, st, ev_start(a.events, 0), ev_stop(a.events, 0),
-                        a, sh, chunks);
+  return launch(k_refscore_mfma, dim3(BH8 * chunks), 256, st, ev_start(a.events, 0), ev_stop(a.events, 0), a, sh,
+                chunks);
+}
+
+hipError_t launch_decode_fused(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
+  const int BH8 = 8 * ((sh.B * sh.H + 7) / 8);
+  hipError_t e = launch_refscore_mfma(sh, a, st);
   if (e != hipSuccess) return e;
   const dim3 grid(BH8 * a.splits);
   const bool i16 = sh.idx_bytes == 2;

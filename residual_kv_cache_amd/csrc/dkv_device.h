@@ -9,6 +9,8 @@ namespace dkv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
 // bfloat16 <-> float32.
@@ -70,6 +72,28 @@ struct F32 {
   static __device__ __forceinline__ T from_f64(double x) { return (float)x; }
   static __device__ __forceinline__ T sub_rn(float x, float y) { return x - y; }
 };
+
+// Eight consecutive storage elements (16-byte aligned) as floats, through
+// global (not flat) loads.
+template <class S>
+__device__ __forceinline__ void load8(const typename S::T* p, float (&v)[8]) {
+  typedef const __attribute__((address_space(1))) u32x4* G4;
+  if constexpr (sizeof(typename S::T) == 2) {
+    const u32x4 w = *(G4)p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    const u32x4 a = *(G4)p, b = *((G4)p + 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = __uint_as_float(a[i]);
+      v[4 + i] = __uint_as_float(b[i]);
+    }
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Wave64 reductions (butterfly; every lane ends with the result).

@@ -120,6 +120,8 @@ struct DecodeArgs {
   float* qp;                 // [B][H][G][dc]
   float* part;               // [B][H][splits][G][rec]
   void* const* events;       // DKV_DECODE_EVENTS hipEvent_t or NULL
+  const uint32_t* sel;       // selective decode: token positions [B][n_sel], else NULL
+  int n_sel;
 };
 
 // Stage timing: event pair (start, stop) of stage i from an optional array.
@@ -171,5 +173,9 @@ hipError_t launch_compress(const Shape& sh, const CompressArgs& a, hipStream_t s
 hipError_t launch_append(const Shape& sh, const AppendArgs& a, void* ws, hipStream_t st);
 hipError_t launch_decode(const Shape& sh, const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_fused(const Shape& sh, const DecodeArgs& a, hipStream_t st);
+// Decode over a token list (a.sel): reference scores, the list's split, combine.
+hipError_t launch_decode_sel(const Shape& sh, const DecodeArgs& a, hipStream_t st);
+// The MFMA reference-score kernel alone (shapes decode_fused_supported accepts).
+hipError_t launch_refscore_mfma(const Shape& sh, const DecodeArgs& a, hipStream_t st);
 
 }  // namespace dkv

@@ -278,3 +278,37 @@ def test_append_workspace_bounds_every_length(B, H, cap, s):
     pad = lambda x: -(-x // 256) * 256
     assert need >= pad(ns * worst * 8) + ns * worst * 32 * 2   # (score, ordinal) and a code per part
     assert need <= pad(ns * max(worst, 1) * 8) + pad(ns * max(worst, 1) * 32 * 2) + 256
+
+
+def _sel_status(lay, sel, cache, hq=32, splits=0):
+    P = 1 << 30
+    a = D.dkv_decode_in(P, P, P, 0, hq, splits, 0.0, 0, P, None)
+    return D.lib().deltakv_decode_attn_sel(ctypes.byref(lay), ctypes.byref(cache.c), ctypes.byref(a),
+                                           ctypes.byref(sel) if sel is not None else None, P, 1 << 30, None)
+
+
+def test_selective_decode_rejects_bad_arguments():
+    """Validation only: every call here fails before any launch."""
+    _lib()
+    _no_device()
+    P = 1 << 30
+    lay = L()
+    cache = FakeCache(P)
+    assert _sel_status(lay, None, cache) == 1
+    assert _sel_status(lay, D.dkv_token_sel(None, 8, 0), cache) == 1
+    assert _sel_status(lay, D.dkv_token_sel(P, 0, 0), cache) == 2
+    assert _sel_status(lay, D.dkv_token_sel(P, 8, 1), cache) == 2
+    assert _sel_status(lay, D.dkv_token_sel(P + 2, 8, 0), cache) == 4
+    assert _sel_status(lay, D.dkv_token_sel(P, 8, 0), cache, hq=30) == 2
+    assert _sel_status(L(head_dim=96), D.dkv_token_sel(P, 8, 0), cache) == 6
+
+
+@pytest.mark.parametrize("B,H,T,n_sel", [(1, 8, 32768, 8192), (1, 8, 32768, 1), (16, 8, 32768, 32768),
+                                         (1, 2, 3001, 700), (1, 1, 100, 5000)])
+def test_selective_auto_splits_fit_the_decode_workspace(B, H, T, n_sel):
+    _lib()
+    lay = D.make_layout("bf16", 128, 32, 16, H, B, T)
+    s = D.dkv_decode_sel_auto_splits(lay, 4 * H, n_sel)
+    assert 1 <= s <= D.dkv_decode_auto_splits(lay, 4 * H)
+    assert s <= max(1, -(-n_sel // 256))
+    assert D.dkv_decode_workspace_bytes(lay, 4 * H, s) <= D.dkv_decode_workspace_bytes(lay, 4 * H, 0)
