@@ -22,9 +22,12 @@ both W_up, the queries and the fp32 outputs, each counted once per decode
 step).  The oracle (fp64, CPU) is timed on a bounded sample afterwards as a
 baseline.
 
-Decode-time append is reported beside it (not part of `value`): 32 tokens
-appended one at a time to a cache sized for them, each after a copy that
-evicts the references from the Infinity Cache, timed with stage events.
+Two further operations are reported beside it (not part of `value`), each
+timed with stage events: selective decode (each step attends over a quarter
+of the tokens, in random 64-token blocks, over the cache replicas in turn),
+and decode-time append (32 tokens appended one at a time to a cache sized
+for them, each after a copy that evicts the references from the Infinity
+Cache).
 """
 from __future__ import annotations
 
@@ -44,6 +47,10 @@ HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2516.6
 DECODE_STEPS = 256
 APPEND_TOKENS = 32
+SEL_STEPS = 64
+SEL_BLOCK = 64
+SEL_SEED = 77
+SEL_REPLAYS = 5
 MALL_BYTES = 256 << 20
 
 
@@ -280,6 +287,17 @@ def main():
     nsteps = DECODE_STEPS
     q_d = torch.stack([dev(np.stack([K.gen_q(cfg, 0, b, i).raw for b in range(cfg.batch)])) for i in range(nsteps)])
     log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f}s")
+    # Token list of the selective decode: a quarter of the tokens of every
+    # sequence, in random 64-token blocks (a block-sparse attention mask).
+    rng = np.random.default_rng(SEL_SEED)
+    nb = cfg.seq_len // SEL_BLOCK
+    sel_rows = []
+    for b in range(cfg.batch):
+        bl = np.sort(rng.choice(nb, nb // 4, replace=False))
+        sel_rows.append((bl[:, None] * SEL_BLOCK + np.arange(SEL_BLOCK)[None, :]).reshape(-1))
+    sel_np = np.stack(sel_rows).astype(np.int32)
+    tok_d = torch.from_numpy(sel_np).cuda()
+    n_sel = sel_np.shape[1]
 
     lay = D.make_layout(cfg.dtype, cfg.head_dim, cfg.code_dim, cfg.stride, cfg.n_kv_heads, cfg.batch, cfg.seq_len)
     cache_bytes = D.dkv_cache_bytes(lay)
@@ -302,6 +320,9 @@ def main():
         for i in range(args.steps):
             D.deltakv_decode_attn(lay, caches[i % nrep], q_d[i % nsteps], wuk_d, wuv_d, outs[i % nsteps], ws_d,
                                   n_splits=splits)
+        for i in range(SEL_STEPS):
+            D.deltakv_decode_attn_sel(lay, caches[i % nrep], q_d[i % nsteps], wuk_d, wuv_d, tok_d, outs[i % nsteps],
+                                      ws_d)
         torch.cuda.synchronize()
         lay_a = D.make_layout(cfg.dtype, cfg.head_dim, cfg.code_dim, cfg.stride, cfg.n_kv_heads, cfg.batch,
                               cfg.seq_len, capacity=cfg.seq_len + APPEND_TOKENS)
@@ -314,7 +335,8 @@ def main():
                              wdk_d, wdv_d, cache_a, ws_a)
         torch.cuda.synchronize()
         log(f"[bench] profile driver: calibration copy of {CALIB_BYTES} bytes, {args.steps} decode steps, "
-            f"splits {splits}, {nrep} cache replicas, then {APPEND_TOKENS} appends")
+            f"splits {splits}, {nrep} cache replicas, {SEL_STEPS} selective decode steps, then {APPEND_TOKENS} "
+            f"appends")
         return
     D.deltakv_decode_attn(lay, caches[0], q_d[0], wuk_d, wuv_d, outs[0], ws_d, n_splits=splits)
     eager0 = outs[0].clone()
@@ -386,6 +408,52 @@ def main():
     c_stage = np.mean(np.array(c_stage), axis=0)
     d_stage = np.array(d_stage)
 
+    # Selective decode: every step attends over a quarter of the tokens, in
+    # random 64-token blocks (a block-sparse attention mask), over the cache
+    # replicas in turn; stage events time its three kernels.
+    ev_s = [hip.events(6) for _ in range(SEL_STEPS)]
+    s_stage = []
+    for rep in range(2):
+        for i in range(SEL_STEPS):
+            D.deltakv_decode_attn_sel(lay, caches[i % nrep], q_d[i % nsteps], wuk_d, wuv_d, tok_d, outs[i % nsteps],
+                                      ws_d, stream=s_h, stage_events=ev_s[i])
+        hip.sync(s_h)
+        s_stage.extend([[hip.elapsed_ms(e[2 * j], e[2 * j + 1]) for j in range(3)] + [hip.elapsed_ms(e[0], e[5])]
+                        for e in ev_s])
+    s_stage = np.array(s_stage)
+    sel_split_us = float(s_stage[:, 1].mean()) * 1e3
+    # Whole selective steps, replayed from a graph like the decode steps.
+    hip.begin_capture(s_h)
+    try:
+        for i in range(SEL_STEPS):
+            D.deltakv_decode_attn_sel(lay, caches[i % nrep], q_d[i % nsteps], wuk_d, wuv_d, tok_d, outs[i % nsteps],
+                                      ws_d, stream=s_h)
+    finally:
+        _, g_sel = hip.end_capture(s_h)
+    hip.launch(g_sel, s_h)
+    hip.sync(s_h)
+    ev_g = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev_g[0].record(stream)
+    for _ in range(SEL_REPLAYS):
+        hip.launch(g_sel, s_h)
+    ev_g[1].record(stream)
+    hip.sync(s_h)
+    sel_step_us = ev_g[0].elapsed_time(ev_g[1]) * 1e3 / (SEL_REPLAYS * SEL_STEPS)
+    # Algorithmic bytes of one selective split launch: the list, each
+    # selected coded token's K and V codes and ordinals, and each distinct V
+    # reference row the selection uses, once.
+    elem = 2 if cfg.dtype == "bf16" else 4
+    idx_np = caches[0].arrays()["idx"].cpu().numpy()
+    idx_np = (idx_np.view(np.uint16) if idx_np.dtype == np.int16 else idx_np.view(np.uint32)).astype(np.int64)
+    sel_bytes = 0
+    for b in range(cfg.batch):
+        t = sel_np[b].astype(np.int64)
+        coded = t % cfg.stride != 0
+        slots = (t - t // cfg.stride - 1)[coded]
+        for h in range(cfg.n_kv_heads):
+            rv = np.unique(np.concatenate([idx_np[b, h, 1][slots], (t // cfg.stride)[~coded]]))
+            sel_bytes += n_sel * 4 + len(slots) * 2 * (cfg.code_dim * elem + lay.idx_bytes) + len(rv) * cfg.head_dim * elem
+
     # Decode-time append: a cache sized for APPEND_TOKENS more tokens takes
     # them one at a time after the prefill (each new token of every stream is
     # a copy of a prefill token, so it has the workload's statistics).  A
@@ -412,10 +480,10 @@ def main():
         hip.sync(s_h)
         for i in range(APPEND_TOKENS):
             t = cfg.seq_len + i
-            a_total.append(hip.elapsed_ms(ev_a[i][0], ev_a[i][3]))
+            a_total.append(hip.elapsed_ms(ev_a[i][0], ev_a[i][1]) + hip.elapsed_ms(ev_a[i][2], ev_a[i][3]))
             if t % cfg.stride:
                 a_search.append((hip.elapsed_ms(ev_a[i][0], ev_a[i][1]), t // cfg.stride + 1))
-    append_us = float(np.mean(a_total)) * 1e3
+    append_us = float(np.mean(a_total)) * 1e3   # search + finish kernel times
     search_us = float(np.mean([x[0] for x in a_search])) * 1e3
     # Algorithmic bytes of one search launch: every candidate reference row
     # of every stream once, plus the new token and the mean.
@@ -464,7 +532,17 @@ def main():
                      "unit": "GB/s", "frac": round(split_bytes / (split_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": stored_traffic(cfg.name, splits), "bytes_per_launch": split_bytes,
                      "launch_us": round(split_ms * 1e3, 3)},
-        "append_us_per_token": round(append_us, 3),
+        "selective_decode": {"tokens_per_seq": n_sel, "selection": "a quarter of the tokens in random 64-token blocks",
+                             "us_per_step": round(sel_step_us, 3),
+                             "stage_us": {"refscore": round(float(s_stage[:, 0].mean()) * 1e3, 3),
+                                          "split": round(sel_split_us, 3),
+                                          "combine": round(float(s_stage[:, 2].mean()) * 1e3, 3)}},
+        "roofline_selective": {"kernel": "k_split_sel", "bound": "hbm",
+                               "achieved": round(sel_bytes / (sel_split_us * 1e-6) / 1e9, 2), "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s",
+                               "frac": round(sel_bytes / (sel_split_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                               "bytes_per_launch": int(sel_bytes), "launch_us": round(sel_split_us, 3)},
+        "append_kernel_us_per_token": round(append_us, 3),
         "roofline_append": {"kernel": "k_append_search", "bound": "hbm",
                             "achieved": round(append_bytes / (search_us * 1e-6) / 1e9, 2), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s",

@@ -249,10 +249,31 @@ __global__ __launch_bounds__(256) void k_split_valu(DecodeArgs a, Shape sh) {
 // together.  Partials have the k_split_valu layout.
 // ---------------------------------------------------------------------------
 
-template <class S, int D, int GP>
+// Zeros standing in for the code and ordinal rows of streams that hold no
+// coded token, so that the loads of k_split_sel need no condition.
+__device__ const uint32_t kZeroRow[64] __attribute__((aligned(16))) = {0u};
+
+// n consecutive storage elements as floats (n = 1 or 2).
+template <class S, int N>
+__device__ __forceinline__ void load_cols(const typename S::T* p, float (&v)[N]) {
+  if constexpr (N == 2 && sizeof(typename S::T) == 2) {
+    const uint32_t w = *(const __attribute__((address_space(1))) uint32_t*)p;
+    v[0] = __uint_as_float(w << 16);
+    v[1] = __uint_as_float(w & 0xFFFF0000u);
+  } else if constexpr (N == 2) {
+    const u32x2 w = *(const __attribute__((address_space(1))) u32x2*)p;
+    v[0] = __uint_as_float(w[0]);
+    v[1] = __uint_as_float(w[1]);
+  } else {
+    v[0] = S::load(*(const __attribute__((address_space(1))) typename S::T*)p);
+  }
+}
+
+template <class S, int D, int GP, typename IdxT>
 __global__ __launch_bounds__(256) void k_split_sel(DecodeArgs a, Shape sh) {
   constexpr int RPL = D / 64;            // head-dim columns per lane
-  constexpr int UN = 8;                  // entries per accumulate step
+  constexpr int UN = 16;                 // entries per accumulate step
+  typedef typename S::T T;
   __shared__ float qp_l[GP][128];
   __shared__ float mw[4][GP];
   __shared__ float merge[GP][2 * D + 1];   // acc_r | acc_c | l
@@ -264,16 +285,25 @@ __global__ __launch_bounds__(256) void k_split_sel(DecodeArgs a, Shape sh) {
   const int i0 = (int)((int64_t)a.n_sel * sp / a.splits), i1 = (int)((int64_t)a.n_sel * (sp + 1) / a.splits);
   const uint32_t* sel = a.sel + (size_t)b * a.n_sel;
 
-  for (int p = threadIdx.x; p < G * dc; p += 256) qp_l[p / dc][p % dc] = a.qp[(size_t)bh * G * dc + p];
+  // q' of the head's query heads; zero past d_c and past G.
+  for (int p = threadIdx.x; p < GP * 128; p += 256) {
+    const int g = p >> 7, j = p & 127;
+    qp_l[g][j] = g < G && j < dc ? a.qp[((size_t)bh * G + g) * dc + j] : 0.f;
+  }
   __syncthreads();
 
   const size_t sK = (size_t)bh * 2, sV = sK + 1;
   const int Gs = score_cols(G);
   const float* score = a.score + (size_t)bh * sh.R * Gs;
-  const typename S::T* refsV = (const typename S::T*)a.refs + sV * sh.Rc * D;
-  const typename S::T* codesK = (const typename S::T*)a.codes + sK * sh.Nc * dc;
-  const typename S::T* codesV = (const typename S::T*)a.codes + sV * sh.Nc * dc;
+  const T* refsV = (const T*)a.refs + sV * sh.Rc * D;
+  // Without coded tokens every entry is a reference: codes and ordinals come
+  // from the zero row (row 0, stride 0).
   const bool has_codes = sh.N > 0;
+  const int cstride = has_codes ? dc : 0;
+  const T* codesK = has_codes ? (const T*)a.codes + sK * sh.Nc * dc : (const T*)kZeroRow;
+  const T* codesV = has_codes ? (const T*)a.codes + sV * sh.Nc * dc : (const T*)kZeroRow;
+  const IdxT* idxK = has_codes ? (const IdxT*)a.idx + sK * sh.Nc : (const IdxT*)kZeroRow;
+  const IdxT* idxV = has_codes ? (const IdxT*)a.idx + sV * sh.Nc : (const IdxT*)kZeroRow;
 
   float m[GP], lsum[GP], accr[GP][RPL], accc[GP][2];
 #pragma unroll
@@ -284,46 +314,51 @@ __global__ __launch_bounds__(256) void k_split_sel(DecodeArgs a, Shape sh) {
     accc[g][0] = accc[g][1] = 0.f;
   }
 
+  const int cl0 = min(lane, dc - 1), cl1 = min(lane + 64, dc - 1);
   const int nchunks = (i1 - i0 + 63) / 64;
   for (int c = wave; c < nchunks; c += 4) {
     const int base = i0 + c * 64;
     const int cnt = min(64, i1 - base);
     // ---- scores: lane = entry ----
-    const uint32_t t = lane < cnt ? sel[base + lane] : 0xFFFFFFFFu;
-    const bool valid = t < (uint32_t)sh.T;
+    const uint32_t t = sel[base + min(lane, cnt - 1)];
+    const bool valid = lane < cnt && t < (uint32_t)sh.T;
     const int tt = valid ? (int)t : 0;
     const int r = tt / sh.s;
     const bool coded = valid && tt - r * sh.s != 0;
     const int u = coded ? tt - r - 1 : 0;     // coded row (0 when unused)
-    int rk = r, rv = r;
-    if (has_codes) {
-      // Ordinals come from caller memory: clamp so a corrupt cache can never
-      // address outside the reference arrays.
-      const int ik = min((int)load_idx(a.idx, sK * sh.Nc + u, sh.idx_bytes), sh.R - 1);
-      const int iv = min((int)load_idx(a.idx, sV * sh.Nc + u, sh.idx_bytes), sh.R - 1);
-      rk = coded ? ik : r;
-      rv = coded ? iv : r;
-    }
-    float sc[GP];
+    // Ordinals come from caller memory: clamp so a corrupt cache can never
+    // address outside the reference arrays.
+    const int ik = min((int)idxK[u], sh.R - 1), iv = min((int)idxV[u], sh.R - 1);
+    float cd[GP];
 #pragma unroll
-    for (int g = 0; g < GP; ++g) sc[g] = g < G ? score[(size_t)rk * Gs + g] : 0.f;
-    if (has_codes) {
-      float cd[GP];
+    for (int g = 0; g < GP; ++g) cd[g] = 0.f;
+    // Key-code dot products, 32 columns per trip: four 8-column loads go out
+    // together (column blocks past d_c re-read the last block and meet the
+    // zero q' columns).
+    for (int j0 = 0; j0 < dc; j0 += 32) {
+      float cv[4][8];
 #pragma unroll
-      for (int g = 0; g < GP; ++g) cd[g] = 0.f;
-      for (int j0 = 0; j0 < dc; j0 += 8) {
-        float cv[8];
-        load8<S>(codesK + (size_t)u * dc + j0, cv);
+      for (int q = 0; q < 4; ++q)
+        load8<S>(codesK + (size_t)u * cstride + (has_codes ? min(j0 + 8 * q, dc - 8) : 0), cv[q]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int g = 0; g < GP; ++g)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) cd[g] = fmaf(qp_l[g][j0 + i], cv[i], cd[g]);
-      }
-#pragma unroll
-      for (int g = 0; g < GP; ++g) sc[g] += coded ? cd[g] : 0.f;
+          for (int i = 0; i < 8; ++i) cd[g] = fmaf(qp_l[g][j0 + 8 * q + i], cv[q][i], cd[g]);
     }
+    const int rk = coded ? ik : r, rv = coded ? iv : r;
+    // The entry's S row, four columns per 16-byte load (rows hold Gs >= 4
+    // columns; blocks past Gs re-read the last block, unused).
+    constexpr int NQ = (GP + 3) / 4;
+    f32x4 srow[NQ];
 #pragma unroll
-    for (int g = 0; g < GP; ++g) sc[g] = valid ? sc[g] : -INFINITY;
+    for (int q = 0; q < NQ; ++q)
+      srow[q] = *(const __attribute__((address_space(1))) f32x4*)(score + (size_t)rk * Gs + min(4 * q, Gs - 4));
+    float sc[GP];
+#pragma unroll
+    for (int g = 0; g < GP; ++g)
+      sc[g] = valid && g < G ? srow[g >> 2][g & 3] + (coded ? cd[g] : 0.f) : -INFINITY;
 
     float p[GP];
 #pragma unroll
@@ -340,26 +375,28 @@ __global__ __launch_bounds__(256) void k_split_sel(DecodeArgs a, Shape sh) {
       accc[g][0] *= alpha;
       accc[g][1] *= alpha;
     }
+    const int ucol = coded ? u : -1;   // coded row, or -1 for a reference entry
 
-    // ---- accumulate: the wave walks the chunk's entries ----
-    const int cl0 = min(lane, dc - 1), cl1 = min(lane + 64, dc - 1);
+    // ---- accumulate: the wave walks the chunk's entries, UN at a time ----
     for (int k0 = 0; k0 < cnt; k0 += UN) {
       float xr[UN][RPL], c0[UN], c1[UN];
 #pragma unroll
       for (int i = 0; i < UN; ++i) {
         const int k = min(k0 + i, cnt - 1);
         const int rr = __builtin_amdgcn_readlane(rv, k);
-        const int uu = __builtin_amdgcn_readlane(u, k);
-#pragma unroll
-        for (int e = 0; e < RPL; ++e) xr[i][e] = S::load(refsV[(size_t)rr * D + lane * RPL + e]);
-        c0[i] = has_codes ? S::load(codesV[(size_t)uu * dc + cl0]) : 0.f;
-        c1[i] = has_codes ? S::load(codesV[(size_t)uu * dc + cl1]) : 0.f;
+        const int uu = max(__builtin_amdgcn_readlane(ucol, k), 0);
+        load_cols<S, RPL>(refsV + (size_t)rr * D + lane * RPL, xr[i]);
+        float t0[1], t1[1];
+        load_cols<S, 1>(codesV + (size_t)uu * cstride + (has_codes ? cl0 : 0), t0);
+        load_cols<S, 1>(codesV + (size_t)uu * cstride + (has_codes ? cl1 : 0), t1);
+        c0[i] = t0[0];
+        c1[i] = t1[0];
       }
 #pragma unroll
       for (int i = 0; i < UN; ++i) {
         const int k = k0 + i;
         if (k >= cnt) break;
-        const bool ck = __builtin_amdgcn_readlane((int)coded, k) != 0;
+        const bool ck = __builtin_amdgcn_readlane(ucol, k) >= 0;
         const float v0 = ck && lane < dc ? c0[i] : 0.f;
         const float v1 = ck && lane + 64 < dc ? c1[i] : 0.f;
 #pragma unroll
@@ -497,21 +534,27 @@ hipError_t launch_decode_sd(const Shape& sh, const DecodeArgs& a, hipStream_t st
   return launch(k_combine<S, D>, dim3(sh.B * a.Hq), 128, st, ev_start(a.events, 2), ev_stop(a.events, 2), a, sh);
 }
 
-template <class S, int D>
-hipError_t launch_decode_sel_sd(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
-  hipError_t e = decode_fused_supported(sh, a.G, 1)
-                     ? launch_refscore_mfma(sh, a, st)
-                     : launch(k_refscore<S, D>, dim3((sh.R + 63) / 64, sh.B * sh.H), 256, st, ev_start(a.events, 0),
-                              ev_stop(a.events, 0), a, sh);
-  if (e != hipSuccess) return e;
+template <class S, int D, typename IdxT>
+hipError_t launch_split_sel(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.splits, sh.B * sh.H);
   const hipEvent_t e0 = ev_start(a.events, 1), e1 = ev_stop(a.events, 1);
-  if (a.G <= 1) e = launch(k_split_sel<S, D, 1>, grid, 256, st, e0, e1, a, sh);
-  else if (a.G <= 2) e = launch(k_split_sel<S, D, 2>, grid, 256, st, e0, e1, a, sh);
-  else if (a.G <= 4) e = launch(k_split_sel<S, D, 4>, grid, 256, st, e0, e1, a, sh);
-  else if (a.G <= 8) e = launch(k_split_sel<S, D, 8>, grid, 256, st, e0, e1, a, sh);
-  else e = launch(k_split_sel<S, D, 16>, grid, 256, st, e0, e1, a, sh);
+  if (a.G <= 1) return launch(k_split_sel<S, D, 1, IdxT>, grid, 256, st, e0, e1, a, sh);
+  if (a.G <= 2) return launch(k_split_sel<S, D, 2, IdxT>, grid, 256, st, e0, e1, a, sh);
+  if (a.G <= 4) return launch(k_split_sel<S, D, 4, IdxT>, grid, 256, st, e0, e1, a, sh);
+  if (a.G <= 8) return launch(k_split_sel<S, D, 8, IdxT>, grid, 256, st, e0, e1, a, sh);
+  return launch(k_split_sel<S, D, 16, IdxT>, grid, 256, st, e0, e1, a, sh);
+}
+
+template <class S, int D>
+hipError_t launch_decode_sel_sd(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
+  const bool mfma = decode_fused_supported(sh, a.G, a.splits);
+  hipError_t e = mfma ? launch_refscore_mfma(sh, a, st)
+                      : launch(k_refscore<S, D>, dim3((sh.R + 63) / 64, sh.B * sh.H), 256, st,
+                               ev_start(a.events, 0), ev_stop(a.events, 0), a, sh);
   if (e != hipSuccess) return e;
+  e = sh.idx_bytes == 2 ? launch_split_sel<S, D, uint16_t>(sh, a, st) : launch_split_sel<S, D, uint32_t>(sh, a, st);
+  if (e != hipSuccess) return e;
+  if (mfma) return launch_combine_mfma(sh, a, st);
   return launch(k_combine<S, D>, dim3(sh.B * a.Hq), 128, st, ev_start(a.events, 2), ev_stop(a.events, 2), a, sh);
 }
 

@@ -596,7 +596,12 @@ __global__ __launch_bounds__(256) void k_combine(DecodeArgs a, Shape sh) {
       u = fmaf(__uint_as_float(wrow[j].y << 16), accc[j * 4 + 2], u);
       u = fmaf(__uint_as_float(wrow[j].y & 0xFFFF0000u), accc[j * 4 + 3], u);
     }
-    a.out[((size_t)b * a.Hq + gq) * kD + i_out] = muv + (acc + u) / red[0];
+    // l = 0 only when a selective decode attended no token: the output is 0.
+    // A bit mask rather than a select keeps the compiler from branching (a
+    // branch merge would wait for every load in flight).
+    const float res = muv + (acc + u) / red[0];
+    const uint32_t keep = 0u - (uint32_t)(red[0] > 0.f);
+    a.out[((size_t)b * a.Hq + gq) * kD + i_out] = __uint_as_float(__float_as_uint(res) & keep);
   }
 }
 
@@ -643,6 +648,11 @@ hipError_t launch_refscore_mfma(const Shape& sh, const DecodeArgs& a, hipStream_
   const int chunks = (sh.R + kRsRefs - 1) / kRsRefs;
   return launch(k_refscore_mfma, dim3(BH8 * chunks), 256, st, ev_start(a.events, 0), ev_stop(a.events, 0), a, sh,
                 chunks);
+}
+
+hipError_t launch_combine_mfma(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
+  const int BH8 = 8 * ((sh.B * sh.H + 7) / 8);
+  return launch(k_combine, dim3(BH8 * a.G), 256, st, ev_start(a.events, 2), ev_stop(a.events, 2), a, sh);
 }
 
 hipError_t launch_decode_fused(const Shape& sh, const DecodeArgs& a, hipStream_t st) {

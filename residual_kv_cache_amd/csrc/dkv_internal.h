@@ -177,5 +177,7 @@ hipError_t launch_decode_fused(const Shape& sh, const DecodeArgs& a, hipStream_t
 hipError_t launch_decode_sel(const Shape& sh, const DecodeArgs& a, hipStream_t st);
 // The MFMA reference-score kernel alone (shapes decode_fused_supported accepts).
 hipError_t launch_refscore_mfma(const Shape& sh, const DecodeArgs& a, hipStream_t st);
+// The MFMA path's combine alone (reads partial records of any split kernel).
+hipError_t launch_combine_mfma(const Shape& sh, const DecodeArgs& a, hipStream_t st);
 
 }  // namespace dkv
