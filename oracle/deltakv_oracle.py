@@ -36,6 +36,9 @@ seedable instance computed here is:
         over the list (entries at or past T skipped)
     O10 append of token t with mu frozen: O3-O6 for that one token, against
         the references at positions below t
+    O11 4-bit codes: O6 without its rounding, then per row
+        scale = rnd(max|c| / 7), q = clamp(rne(c / scale), -8, 7); the
+        decoder's code is scale * q
 
 ``rnd`` rounds to the storage dtype (nearest, ties to even).  Storage
 "f64" makes rnd the identity; the pins use it to test the mathematics
@@ -116,31 +119,36 @@ def idx_bytes_for(R: int) -> int:
     return 2 if R <= 65536 else 4
 
 
-def stream_bytes(T: int, s: int, d: int, dc: int, storage: str) -> int:
-    """Bytes one compressed stream occupies: references, codes, indices, mean."""
+def stream_bytes(T: int, s: int, d: int, dc: int, storage: str, code_bits: int = 16) -> int:
+    """Bytes one compressed stream occupies: references, codes, indices, mean
+    (with 4-bit codes: d_c / 2 bytes and one scale per coded token)."""
     e = ELEM_BYTES[storage]
     R = n_refs(T, s)
     N = T - R
-    return R * d * e + N * (dc * e + idx_bytes_for(R)) + d * e
+    code = dc // 2 + e if code_bits == 4 else dc * e
+    return R * d * e + N * (code + idx_bytes_for(R)) + d * e
 
 
-def cache_array_bytes(B: int, H: int, T: int, s: int, d: int, dc: int, storage: str) -> dict:
+def cache_array_bytes(B: int, H: int, T: int, s: int, d: int, dc: int, storage: str, code_bits: int = 16) -> dict:
     """Unpadded size of each cache array over B sequences x H heads x {K, V}."""
     e = ELEM_BYTES[storage]
     R = n_refs(T, s)
     N = T - R
     n = B * H * 2
-    return {
+    out = {
         "refs": n * R * d * e,
-        "codes": n * N * dc * e,
+        "codes": n * N * (dc // 2 if code_bits == 4 else dc * e),
         "idx": n * N * idx_bytes_for(R),
         "mu": n * d * e,
     }
+    if code_bits == 4:
+        out["scales"] = n * N * e
+    return out
 
 
-def cache_bytes(B, H, T, s, d, dc, storage, align: int = ALIGN) -> int:
+def cache_bytes(B, H, T, s, d, dc, storage, align: int = ALIGN, code_bits: int = 16) -> int:
     """Total carved cache size: each array padded to ``align`` bytes."""
-    return sum(-(-v // align) * align for v in cache_array_bytes(B, H, T, s, d, dc, storage).values())
+    return sum(-(-v // align) * align for v in cache_array_bytes(B, H, T, s, d, dc, storage, code_bits).values())
 
 
 def dense_kv_bytes(n_layers, n_kv_heads, head_dim, seq_len, batch, elem_bytes=2) -> int:
@@ -148,14 +156,16 @@ def dense_kv_bytes(n_layers, n_kv_heads, head_dim, seq_len, batch, elem_bytes=2)
     return 2 * n_layers * n_kv_heads * head_dim * elem_bytes * seq_len * batch
 
 
-def decode_effective_bytes(B, H, Hq, T, s, d, dc, storage) -> int:
+def decode_effective_bytes(B, H, Hq, T, s, d, dc, storage, code_bits: int = 16) -> int:
     """Bytes one decode step must move at least once: both tensors' references,
-    codes and indices, V's mean, W_up of K and V, the query and the fp32
-    output.  K's mean is never needed (it shifts every score equally)."""
+    codes (and scales) and indices, V's mean, W_up of K and V, the query and
+    the fp32 output.  K's mean is never needed (it shifts every score
+    equally)."""
     e = ELEM_BYTES[storage]
-    a = cache_array_bytes(B, H, T, s, d, dc, storage)
+    a = cache_array_bytes(B, H, T, s, d, dc, storage, code_bits)
     mu_v = B * H * d * e
-    return a["refs"] + a["codes"] + a["idx"] + mu_v + 2 * d * dc * e + B * Hq * d * e + B * Hq * d * 4
+    return (a["refs"] + a["codes"] + a.get("scales", 0) + a["idx"] + mu_v + 2 * d * dc * e + B * Hq * d * e
+            + B * Hq * d * 4)
 
 
 # ---------------------------------------------------------------------------
@@ -239,10 +249,46 @@ def encode(k, mu, xt, s, idx, w_down, storage, toks=None):
     return rnd(delta @ w_down.T, storage)
 
 
-def compress_stream(k, s, w_down, storage, mu_in=None, force_idx=None) -> dict:
+def quantize_q4(c, storage):
+    """O11.  4-bit residual codes ([pt] §4 "Resultados Experimentais": the
+    residuals cluster around zero and suit 4-bit quantization; [es] §4
+    "Resultados Principales" and [en] §5 "Experimental Results", the 29 %
+    figure with 4-bit quantization).  The pages name no scheme; the
+    reading here is symmetric per-row quantization of each token's code
+    vector c (rows of ``c``):
+
+        scale = rnd(max_j |c_j| / 7)            one value per row, storage dtype
+        q_j   = clamp(rne(c_j / scale), -8, 7)  scale = 0 gives q = 0
+
+    and the code the decoder uses is scale * q_j.  Returns (q as int64,
+    scale)."""
+    c = np.atleast_2d(np.asarray(c, np.float64))
+    amax = np.abs(c).max(axis=1) if c.shape[1] else np.zeros(c.shape[0])
+    scale = rnd(amax / 7.0, storage)
+    safe = np.where(scale > 0, scale, 1.0)
+    q = np.clip(np.rint(c / safe[:, None]), -8, 7)
+    q = np.where(scale[:, None] > 0, q, 0.0)
+    return q.astype(np.int64), scale
+
+
+def dequantize_q4(q, scale) -> np.ndarray:
+    return np.asarray(q, np.float64) * np.asarray(scale, np.float64)[:, None]
+
+
+def encode_exact(k, mu, xt, s, idx, w_down, toks=None) -> np.ndarray:
+    """W_down ((k_t - mu) - x~_ref(t)) before any rounding (fp64)."""
+    T = k.shape[0]
+    toks = nonref_positions(T, s) if toks is None else np.asarray(toks, np.int64)
+    delta = (k[toks] - mu) - xt[np.asarray(idx, np.int64) * s]
+    return delta @ w_down.T
+
+
+def compress_stream(k, s, w_down, storage, mu_in=None, force_idx=None, code_bits=16) -> dict:
     """One stream, steps O2-O6.  ``k`` holds storage-dtype values as float64.
     ``force_idx`` re-encodes with given references (used where several
-    references are equally correct within the search tolerance)."""
+    references are equally correct within the search tolerance).  With
+    ``code_bits`` = 4 the codes are quantized (O11): "q" and "scales" hold
+    what is stored and "codes" the values the decoder uses (scale * q)."""
     k = np.asarray(k, np.float64)
     T = k.shape[0]
     mu = shared_component(k, storage) if mu_in is None else np.asarray(mu_in, np.float64)
@@ -251,21 +297,26 @@ def compress_stream(k, s, w_down, storage, mu_in=None, force_idx=None) -> dict:
     idx, top1, margin = search(xt, s)
     if force_idx is not None:
         idx = np.asarray(force_idx, np.int64)
-    codes = encode(k, mu, xt, s, idx, w_down, storage)
-    return {"mu": mu, "refs": refs, "idx": idx, "codes": codes,
-            "top1": top1, "margin": margin, "xt": xt}
+    out = {"mu": mu, "refs": refs, "idx": idx, "top1": top1, "margin": margin, "xt": xt}
+    if code_bits == 4:
+        q, scale = quantize_q4(encode_exact(k, mu, xt, s, idx, w_down).reshape(len(idx), -1), storage)
+        out.update(q=q, scales=scale, codes=dequantize_q4(q, scale))
+    else:
+        out["codes"] = encode(k, mu, xt, s, idx, w_down, storage)
+    return out
 
 
-def compress(k, v, s, w_down_k, w_down_v, storage) -> dict:
+def compress(k, v, s, w_down_k, w_down_v, storage, code_bits=16) -> dict:
     """All streams of one layer: k, v are [B][H][T][d].  Returns arrays shaped
     [B][H][2][...] with index 0 = K and 1 = V."""
     B, H, T, d = k.shape
-    out = {n: [] for n in ("mu", "refs", "idx", "codes", "top1", "margin")}
+    names = ("mu", "refs", "idx", "codes", "top1", "margin") + (("q", "scales") if code_bits == 4 else ())
+    out = {n: [] for n in names}
     for b in range(B):
         row = {n: [] for n in out}
         for h in range(H):
-            pair = [compress_stream(k[b, h], s, w_down_k, storage),
-                    compress_stream(v[b, h], s, w_down_v, storage)]
+            pair = [compress_stream(k[b, h], s, w_down_k, storage, code_bits=code_bits),
+                    compress_stream(v[b, h], s, w_down_v, storage, code_bits=code_bits)]
             for n in out:
                 row[n].append(np.stack([p[n] for p in pair]))
         for n in out:
@@ -273,7 +324,7 @@ def compress(k, v, s, w_down_k, w_down_v, storage) -> dict:
     return {n: np.stack(a) for n, a in out.items()}
 
 
-def append_token(mu, refs, k_t, t, s, w_down, storage) -> dict:
+def append_token(mu, refs, k_t, t, s, w_down, storage, code_bits=16) -> dict:
     """A decode-time token joins a compressed stream ([en] §3 "Strided
     Reference Selection": references sit at a fixed stride and each new
     token retrieves the nearest earlier one; §3 "Residual Encoding").
@@ -304,8 +355,13 @@ def append_token(mu, refs, k_t, t, s, w_down, storage) -> dict:
             best = r
     others = [c for r, c in enumerate(cands) if r != best]
     resid = (np.asarray(k_t, np.float64) - mu) - refs[best]
-    return {"idx": best, "code": rnd(w_down @ resid, storage), "cos": cands[best],
-            "margin": cands[best] - max(others) if others else math.inf}
+    out = {"idx": best, "cos": cands[best], "margin": cands[best] - max(others) if others else math.inf}
+    if code_bits == 4:
+        q, scale = quantize_q4((w_down @ resid)[None], storage)
+        out.update(q=q[0], scale=scale[0], code=q[0] * scale[0])
+    else:
+        out["code"] = rnd(w_down @ resid, storage)
+    return out
 
 
 # ---------------------------------------------------------------------------

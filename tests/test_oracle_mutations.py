@@ -34,6 +34,12 @@ PINS = [
     P.test_selected_is_dense_attention_over_the_subset,
     P.test_selected_order_duplicates_and_single_token,
     P.test_selected_skips_positions_past_the_end,
+    P.test_q4_hand_cases,
+    P.test_q4_matches_plain_python_rule,
+    P.test_q4_grid_values_round_trip_and_error_bound,
+    P.test_q4_compress_stream_uses_unrounded_codes,
+    P.test_q4_full_rank_code_error_bound,
+    lambda: P.test_q4_stream_bytes_closed_form("llama8b_32k", 1138944),
 ]
 
 
@@ -167,6 +173,33 @@ def _append_factory(*, no_causal=False, last_tie=False, plus_ref=False, rounded_
 
 
 _ORIG_SEL = OD.decode_selected
+_ORIG_Q4 = OD.quantize_q4
+_ORIG_EXACT = OD.encode_exact
+
+
+def _q4_half_away(c, storage):
+    c = np.atleast_2d(np.asarray(c, np.float64))
+    scale = OD.rnd(np.abs(c).max(axis=1) / 7.0, storage)
+    safe = np.where(scale > 0, scale, 1.0)
+    x = c / safe[:, None]
+    q = np.clip(np.sign(x) * np.floor(np.abs(x) + 0.5), -8, 7)
+    return np.where(scale[:, None] > 0, q, 0).astype(np.int64), scale
+
+
+def _q4_scale_by_8(c, storage):
+    c = np.atleast_2d(np.asarray(c, np.float64))
+    scale = OD.rnd(np.abs(c).max(axis=1) / 8.0, storage)
+    safe = np.where(scale > 0, scale, 1.0)
+    q = np.clip(np.rint(c / safe[:, None]), -8, 7)
+    return np.where(scale[:, None] > 0, q, 0).astype(np.int64), scale
+
+
+def _exact_rounded_first(k, mu, xt, s, idx, w_down, toks=None):
+    return OD.rnd(_ORIG_EXACT(k, mu, xt, s, idx, w_down, toks), "bf16")
+
+
+def _dequant_no_scale(q, scale):
+    return np.asarray(q, np.float64)
 
 
 def _sel_ignores_list(cache, q, w_up_k, w_up_v, s, T, sel, scale=None):
@@ -218,6 +251,10 @@ MUTATIONS = {
     "selected decode: clamps positions past the end": ("decode_selected", _sel_clamps_past_end),
     "selected decode: drops duplicate entries": ("decode_selected", _sel_unique),
     "selected decode: positions off by one": ("decode_selected", _sel_off_by_one),
+    "4-bit: ties round away from zero": ("quantize_q4", _q4_half_away),
+    "4-bit: scale from max / 8": ("quantize_q4", _q4_scale_by_8),
+    "4-bit: quantizes the storage-rounded code": ("encode_exact", _exact_rounded_first),
+    "4-bit: decoder drops the scale": ("dequantize_q4", _dequant_no_scale),
 }
 
 

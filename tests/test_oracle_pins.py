@@ -553,3 +553,113 @@ def test_selected_skips_positions_past_the_end():
     want0 = O.decode_selected(first, q[:1], w, w, 3, T, np.array([[2, 5]]))[0]
     assert np.abs(out[0] - want0).max() < 1e-13
     assert np.all(out[1] == 0.0)
+
+
+# ---------------------------------------------------------------------------
+# 4-bit codes ([pt] §4 "Resultados Experimentais": residuals cluster around
+# zero and suit 4-bit quantization).
+# ---------------------------------------------------------------------------
+
+def _py_quantize_row(row, storage):
+    """Plain-Python statement of the per-row rule: scale = rnd(max|c| / 7),
+    q = clamp(round-half-even(c / scale), -8, 7)."""
+    amax = max(abs(x) for x in row) if row else 0.0
+    scale = float(O.rnd(np.array([amax / 7.0]), storage)[0])
+    if scale == 0.0:
+        return [0] * len(row), 0.0
+    return [max(-8, min(7, round(x / scale))) for x in row], scale   # round() is half-to-even
+
+
+def test_q4_hand_cases():
+    q, sc = O.quantize_q4([[0.875, -0.4375, 0.125, 0.3125, 0.0]], "f64")
+    assert sc.tolist() == [0.125] and q.tolist() == [[7, -4, 1, 2, 0]]   # -3.5 -> -4 and 2.5 -> 2 (ties to even)
+    q, sc = O.quantize_q4([[0.0, 0.0]], "bf16")
+    assert sc.tolist() == [0.0] and q.tolist() == [[0, 0]]
+    # bf16 scale: 1/7 rounds to 0.142578125; 1.0 / that = 7.0137 -> 7.
+    q, sc = O.quantize_q4([[1.0, -1.0, 0.5]], "bf16")
+    assert sc.tolist() == [0.142578125] and q.tolist() == [[7, -7, 4]]   # 0.5 / 0.1426 = 3.507 -> 4
+
+
+def test_q4_matches_plain_python_rule():
+    rng = np.random.default_rng(12)
+    for storage in ("bf16", "f32"):
+        c = rng.standard_normal((300, 32)) * np.exp2(rng.integers(-8, 8, (300, 1)))
+        c[::17] = np.round(c[::17] * 4) / 4          # exact halves and ties appear
+        q, sc = O.quantize_q4(c, storage)
+        for i in range(len(c)):
+            qp, sp = _py_quantize_row(c[i].tolist(), storage)
+            assert q[i].tolist() == qp and sc[i] == sp
+
+
+def test_q4_grid_values_round_trip_and_error_bound():
+    rng = np.random.default_rng(13)
+    k = rng.integers(-7, 8, (50, 16))
+    k[:, 0] = 7                                     # max |k| = 7 fixes the scale exactly
+    c = k * 2.0 ** -5
+    q, sc = O.quantize_q4(c, "bf16")
+    assert np.all(sc == 2.0 ** -5) and np.array_equal(q, k)
+    assert np.array_equal(O.dequantize_q4(q, sc), c)
+    x = rng.standard_normal((400, 48))
+    q, sc = O.quantize_q4(x, "f32")
+    assert np.all(np.abs(O.dequantize_q4(q, sc) - x) <= sc[:, None] * (0.5 + 2 ** -20))
+
+
+@pytest.mark.parametrize("name,total", [("llama8b_32k", 1138944), ("tiny", 2048 // 8 * 256 + 1792 * (8 + 4 + 2) + 256)])
+def test_q4_stream_bytes_closed_form(name, total):
+    """C1 with 4-bit codes, per stream: 2048 reference rows x 256 B, 30720
+    coded tokens x (16 B of codes + 2 B scale + 2 B ordinal), 256 B mean."""
+    c = K.CONFIGS[name]
+    assert O.stream_bytes(c.seq_len, c.stride, c.head_dim, c.code_dim, c.dtype, code_bits=4) == total
+    a = O.cache_array_bytes(1, 1, c.seq_len, c.stride, c.head_dim, c.code_dim, c.dtype, code_bits=4)
+    assert sum(a.values()) // 2 == total
+
+
+def test_q4_compress_stream_uses_unrounded_codes():
+    """The quantizer sees W_down delta before any storage rounding, and the
+    decoder's codes are scale * q."""
+    rng = np.random.default_rng(14)
+    T, d, dc, s = 60, 8, 4, 5
+    k = K.to_storage(rng.standard_normal((T, d)) * 3, "bf16").f64
+    wd = K.to_storage(rng.standard_normal((dc, d)) / 3, "bf16").f64
+    r = O.compress_stream(k, s, wd, "bf16", code_bits=4)
+    toks = O.nonref_positions(T, s)
+    for j, t in enumerate(toks):
+        delta = [(k[t][i] - r["mu"][i]) - r["refs"][r["idx"][j]][i] for i in range(d)]
+        exact = [math.fsum(wd[c][i] * delta[i] for i in range(d)) for c in range(dc)]
+        qp, sp = _py_quantize_row(exact, "bf16")
+        assert r["q"][j].tolist() == qp and r["scales"][j] == sp
+        assert r["codes"][j].tolist() == [x * sp for x in qp]
+
+
+def test_q4_full_rank_code_error_bound():
+    """d_c = d with orthonormal W: k^ - k = W_up (scale q - c), so the
+    reconstruction error is at most the quantization error of the code."""
+    rng = np.random.default_rng(15)
+    T, d, s = 40, 16, 4
+    k = rng.standard_normal((1, 1, T, d)) * 2
+    w = np.linalg.qr(rng.standard_normal((d, d)))[0]
+    c = O.compress(k, k, s, w.T, w.T, "f64", code_bits=4)
+    rec = O.reconstruct_stream(c["mu"][0, 0, 0], c["refs"][0, 0, 0], c["idx"][0, 0, 0], c["codes"][0, 0, 0], w, s, T)
+    toks = O.nonref_positions(T, s)
+    err = np.linalg.norm(rec[toks] - k[0, 0][toks], axis=1)
+    bound = np.sqrt(d) * c["scales"][0, 0, 0] / 2 * (1 + 1e-9)
+    assert np.all(err <= bound)
+    assert np.allclose(rec[O.ref_positions(T, s)], k[0, 0][O.ref_positions(T, s)], atol=1e-12)
+
+
+def test_q4_append_equals_compress():
+    rng = np.random.default_rng(16)
+    T0, n, s, d, dc = 30, 50, 8, 12, 5
+    k = K.to_storage(rng.standard_normal((T0 + n, d)) * 2 + 1, "bf16").f64
+    wd = K.to_storage(rng.standard_normal((dc, d)) / 3, "bf16").f64
+    mu = O.shared_component(k[:T0], "bf16")
+    full = O.compress_stream(k, s, wd, "bf16", mu_in=mu, code_bits=4)
+    refs = list(full["refs"][:O.n_refs(T0, s)])
+    for t in range(T0, T0 + n):
+        a = O.append_token(mu, np.array(refs), k[t], t, s, wd, "bf16", code_bits=4)
+        if "ref" in a:
+            refs.append(a["ref"])
+            continue
+        row = t - t // s - 1
+        assert a["idx"] == full["idx"][row]
+        assert a["q"].tolist() == full["q"][row].tolist() and a["scale"] == full["scales"][row]
