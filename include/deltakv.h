@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define DKV_ABI_VERSION 2u
+#define DKV_ABI_VERSION 3u
 
 typedef enum dkv_status {
   DKV_OK = 0,
@@ -89,6 +89,14 @@ typedef enum dkv_dtype {
  *   seq_len      T >= 1, tokens held in the cache
  *   capacity     tokens the arrays are sized for (T_cap >= T), so that
  *                tokens can be appended in place; 0 means T_cap = T
+ *   code_bits    0: codes in the storage dtype; 4: 4-bit codes, one scale
+ *                per code row (DeltaKV explainer, Portuguese page, Resumo
+ *                Técnico §4: the residuals cluster around zero and suit
+ *                4-bit quantization; the pages give no scheme).  A row's
+ *                code c (computed as for storage-dtype codes, before any
+ *                rounding) is stored as scale = rnd(max_j |c_j| / 7) and
+ *                q_j = clamp(round-half-even(c_j / scale), -8, 7) (q = 0
+ *                when scale = 0); the decoder uses scale * q_j
  * Derived: R = ceil(T / s) references and N = T - R coded tokens per stream
  * are held; the arrays are laid out for R_cap = ceil(T_cap / s) and
  * N_cap = T_cap - R_cap (a cache's layout is fixed by T_cap, so a layout
@@ -105,6 +113,7 @@ typedef struct dkv_layout {
   uint32_t batch;
   uint32_t seq_len;
   uint32_t capacity;
+  uint32_t code_bits;
 } dkv_layout;
 
 /*
@@ -116,9 +125,14 @@ typedef struct dkv_layout {
  *                                 token in position order; token t
  *                                 (t mod s != 0) sits in row
  *                                 t - floor(t / s) - 1 (rows 0 .. N-1 in use)
+ *                                 With code_bits = 4 a row is d_c / 2 bytes:
+ *                                 element 2i in the low nibble of byte i,
+ *                                 2i + 1 in the high nibble, two's complement
  *   idx    [B][H][2][N_cap]       uint16 or uint32 (idx_bytes): reference
  *                                 ordinal r of each row (the token at r*s)
  *   mu     [B][H][2][d]           storage dtype: the shared component
+ *   scales [B][H][2][N_cap]       storage dtype, code_bits = 4 only (else
+ *                                 ignored, may be NULL): scale of each row
  * Each pointer must be 16-byte aligned.
  */
 typedef struct dkv_cache {
@@ -126,6 +140,7 @@ typedef struct dkv_cache {
   void* codes;
   void* idx;
   void* mu;
+  void* scales;
 } dkv_cache;
 
 /*
@@ -249,8 +264,9 @@ dkv_status dkv_layout_check(const dkv_layout* layout);
 size_t dkv_cache_bytes(const dkv_layout* layout);
 
 /* Splits one device buffer of dkv_cache_bytes(layout) bytes starting at
- * `base` (256-byte aligned) into refs, codes, idx and mu, in that order,
- * each at a 256-byte boundary.  Writes only *cache. */
+ * `base` (256-byte aligned) into refs, codes, idx, mu and (code_bits = 4)
+ * scales, in that order, each at a 256-byte boundary; scales is NULL for
+ * storage-dtype codes.  Writes only *cache. */
 dkv_status dkv_cache_carve(const dkv_layout* layout, void* base, dkv_cache* cache);
 
 /* Workspace bytes deltakv_compress needs for this layout (0 if invalid). */

@@ -26,6 +26,7 @@ dkv_status check_layout(const dkv_layout* L, Shape* out) {
   if (cap < L->seq_len) return DKV_ERR_SHAPE;
   if (L->code_dim > L->head_dim) return DKV_ERR_SHAPE;
   if (L->idx_bytes != 2 && L->idx_bytes != 4) return DKV_ERR_SHAPE;
+  if (L->code_bits != 0 && L->code_bits != 4) return DKV_ERR_SHAPE;
   if (L->head_dim != 64 && L->head_dim != 128) return DKV_ERR_UNSUPPORTED;
   if (L->code_dim % 16 != 0) return DKV_ERR_UNSUPPORTED;
   if (cap > (1u << 30) || L->n_kv_heads > 4096 || L->batch > 65535) return DKV_ERR_UNSUPPORTED;
@@ -47,21 +48,23 @@ dkv_status check_layout(const dkv_layout* L, Shape* out) {
     out->B = (int)L->batch;
     out->idx_bytes = (int)L->idx_bytes;
     out->bf16 = L->dtype == DKV_BF16;
+    out->q4 = L->code_bits == 4;
   }
   return DKV_OK;
 }
 
 struct ArrayBytes {
-  size_t refs, codes, idx, mu;
+  size_t refs, codes, idx, mu, scales;
 };
 
 ArrayBytes array_bytes(const Shape& sh) {
   const size_t n = (size_t)sh.n_streams();
   ArrayBytes a;
   a.refs = n * sh.Rc * sh.d * sh.elem();
-  a.codes = n * sh.Nc * sh.dc * sh.elem();
+  a.codes = n * sh.Nc * sh.code_row_bytes();
   a.idx = n * sh.Nc * sh.idx_bytes;
   a.mu = n * sh.d * sh.elem();
+  a.scales = sh.q4 ? n * sh.Nc * sh.elem() : 0;
   return a;
 }
 
@@ -71,7 +74,9 @@ dkv_status check_cache(const dkv_cache* c, const Shape& sh) {
   if (!c) return DKV_ERR_NULL;
   if (!c->refs || !c->mu) return DKV_ERR_NULL;
   if (sh.Nc > 0 && (!c->codes || !c->idx)) return DKV_ERR_NULL;
+  if (sh.q4 && sh.Nc > 0 && !c->scales) return DKV_ERR_NULL;
   if (!aligned16(c->refs) || !aligned16(c->codes) || !aligned16(c->idx) || !aligned16(c->mu)) return DKV_ERR_ALIGN;
+  if (sh.q4 && !aligned16(c->scales)) return DKV_ERR_ALIGN;
   return DKV_OK;
 }
 
@@ -125,7 +130,7 @@ size_t dkv_cache_bytes(const dkv_layout* layout) {
   Shape sh;
   if (check_layout(layout, &sh) != DKV_OK) return 0;
   const ArrayBytes a = array_bytes(sh);
-  return pad(a.refs) + pad(a.codes) + pad(a.idx) + pad(a.mu);
+  return pad(a.refs) + pad(a.codes) + pad(a.idx) + pad(a.mu) + pad(a.scales);
 }
 
 dkv_status dkv_cache_carve(const dkv_layout* layout, void* base, dkv_cache* cache) {
@@ -143,6 +148,8 @@ dkv_status dkv_cache_carve(const dkv_layout* layout, void* base, dkv_cache* cach
   cache->idx = p;
   p += pad(a.idx);
   cache->mu = p;
+  p += pad(a.mu);
+  cache->scales = sh.q4 ? p : nullptr;
   return DKV_OK;
 }
 
@@ -201,6 +208,7 @@ dkv_status deltakv_compress(const dkv_layout* layout, const dkv_compress_in* in,
   a.codes = cache->codes;
   a.idx = cache->idx;
   a.mu = cache->mu;
+  a.scales = sh.q4 ? cache->scales : nullptr;
   a.mean_part = (double*)((char*)ws + dkv::ws_mean_off(sh));
   a.inv_n = (float*)((char*)ws + dkv::ws_invn_off(sh));
   a.events = in->stage_events;
@@ -249,6 +257,7 @@ dkv_status deltakv_append(const dkv_layout* layout, const dkv_append_in* in, con
   a.codes = cache->codes;
   a.idx = cache->idx;
   a.mu = cache->mu;
+  a.scales = sh.q4 ? cache->scales : nullptr;
   a.events = in->stage_events;
   return from_hip(dkv::launch_append(s2, a, ws, (hipStream_t)stream));
 }
@@ -294,6 +303,7 @@ dkv_status decode_setup(const dkv_layout* layout, const dkv_cache* cache, const 
   a->codes = cache->codes;
   a->idx = cache->idx;
   a->mu = cache->mu;
+  a->scales = sh->q4 ? cache->scales : nullptr;
   a->score = (float*)ws;
   a->qp = (float*)((char*)ws + dkv::ws_qp_off(*sh, G));
   a->part = (float*)((char*)ws + dkv::ws_part_off(*sh, G));

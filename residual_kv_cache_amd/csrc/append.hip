@@ -75,7 +75,7 @@ inline size_t pcode_off(int ns, int parts) { return align_up((size_t)ns * parts 
 
 template <class S, int D>
 __global__ __launch_bounds__(256) void k_append_search(AppendArgs a, Shape sh, int chunk, int P, float2* part,
-                                                       typename S::T* pcode) {
+                                                       void* pcode) {
   constexpr int E = D / 16;  // elements per lane of a reference row
   constexpr int Q = D / 4;   // elements per lane of a W_down row
   typedef typename S::T T;
@@ -166,9 +166,11 @@ __global__ __launch_bounds__(256) void k_append_search(AppendArgs a, Shape sh, i
   }
   __syncthreads();
 
-  // The block's candidate code: rnd(W_down (k_t - mu - refs[br])), four
-  // lanes per element, 64 elements per pass.
-  T* out = pcode + ((size_t)stream * P + p) * sh.dc;
+  // The block's candidate code: rnd(W_down (k_t - mu - refs[br])) (for
+  // 4-bit codes the unrounded value, quantized once the winner is known),
+  // four lanes per element, 64 elements per pass.
+  T* out = (T*)pcode + ((size_t)stream * P + p) * sh.dc;
+  float* out32 = (float*)pcode + ((size_t)stream * P + p) * sh.dc;
   for (int j0 = 0; j0 < sh.dc; j0 += 64) {
     const int jj = j0 + j;
     if (j0 > 0) wrow.load(wd + (size_t)min(jj, sh.dc - 1) * D + l4 * Q);
@@ -179,7 +181,12 @@ __global__ __launch_bounds__(256) void k_append_search(AppendArgs a, Shape sh, i
     }
     c += __shfl_xor(c, 1, 64);
     c += __shfl_xor(c, 2, 64);
-    if (jj < sh.dc && l4 == 0) out[jj] = S::from_f32(c);
+    if (jj < sh.dc && l4 == 0) {
+      if (sh.q4)
+        out32[jj] = c;
+      else
+        out[jj] = S::from_f32(c);
+    }
   }
   if (tid == 0) part[(size_t)stream * P + p] = make_float2(bs, __int_as_float(br));
 }
@@ -190,7 +197,7 @@ __global__ __launch_bounds__(256) void k_append_search(AppendArgs a, Shape sh, i
 // position, its centred row.
 template <class S, int D>
 __global__ __launch_bounds__(64) void k_append_finish(AppendArgs a, Shape sh, int P, const float2* part,
-                                                      const typename S::T* pcode) {
+                                                      const void* pcode) {
   typedef typename S::T T;
   const int stream = blockIdx.x;
   const int kv = stream & 1, bh = stream >> 1, b = bh / sh.H, h = bh - b * sh.H;
@@ -225,8 +232,26 @@ __global__ __launch_bounds__(64) void k_append_finish(AppendArgs a, Shape sh, in
     }
   }
   const size_t slot = (size_t)stream * sh.Nc + (size_t)(t - t / sh.s - 1);
-  const T* c = pcode + ((size_t)stream * P + bp) * sh.dc;
-  for (int jj = lane; jj < sh.dc; jj += 64) ((T*)a.codes)[slot * sh.dc + jj] = c[jj];
+  if (!sh.q4) {
+    const T* c = (const T*)pcode + ((size_t)stream * P + bp) * sh.dc;
+    for (int jj = lane; jj < sh.dc; jj += 64) ((T*)a.codes)[slot * sh.dc + jj] = c[jj];
+  } else {
+    // 4-bit codes: the row's scale from its largest magnitude, then each
+    // even lane packs its element with its neighbour's (d_c <= 128).
+    const float* c = (const float*)pcode + ((size_t)stream * P + bp) * sh.dc;
+    const float c0 = lane < sh.dc ? c[lane] : 0.f, c1 = lane + 64 < sh.dc ? c[lane + 64] : 0.f;
+    const float amax = wave_max(fmaxf(fabsf(c0), fabsf(c1)));
+    const T sbits = S::from_f32(amax / 7.0f);
+    const float scale = S::load(sbits);
+    const int q0 = q4_quant(c0, scale), q1 = q4_quant(c1, scale);
+    const int n0 = __shfl_down(q0, 1, 64), n1 = __shfl_down(q1, 1, 64);
+    uint8_t* row = (uint8_t*)a.codes + slot * (sh.dc / 2);
+    if (!(lane & 1)) {
+      if (lane < sh.dc) row[lane >> 1] = (uint8_t)(((uint32_t)q0 & 15u) | (((uint32_t)n0 & 15u) << 4));
+      if (lane + 64 < sh.dc) row[(lane + 64) >> 1] = (uint8_t)(((uint32_t)q1 & 15u) | (((uint32_t)n1 & 15u) << 4));
+    }
+    if (lane == 0) ((T*)a.scales)[slot] = sbits;
+  }
   if (lane == 0) store_idx(a.idx, slot, sh.idx_bytes, (uint32_t)br);
 }
 
@@ -239,7 +264,7 @@ hipError_t launch_append_sd(const Shape& sh, const AppendArgs& a, void* ws, hipS
   const int t = sh.T - 1, ns = sh.n_streams();
   const int P = t % sh.s == 0 ? 0 : append_parts(sh, t / sh.s + 1);
   float2* part = (float2*)ws;
-  typename S::T* pcode = (typename S::T*)((char*)ws + pcode_off(ns, std::max(P, 1)));
+  void* pcode = (char*)ws + pcode_off(ns, std::max(P, 1));
   hipError_t err;
   if (P > 0)
     err = launch(k_append_search<S, D>, dim3(xcd_grid(ns, P)), 256, st, ev[0], ev[1], a, sh,
@@ -248,7 +273,7 @@ hipError_t launch_append_sd(const Shape& sh, const AppendArgs& a, void* ws, hipS
     err = ev[0] ? launch(k_append_empty, dim3(1), 64, st, ev[0], ev[1]) : hipSuccess;
   if (err != hipSuccess) return err;
   return launch(k_append_finish<S, D>, dim3(ns), 64, st, ev[2], ev[3], a, sh, P, (const float2*)part,
-                (const typename S::T*)pcode);
+                (const void*)pcode);
 }
 
 }  // namespace
@@ -269,7 +294,8 @@ size_t append_ws_bytes(const Shape& sh) {
   const int ns = sh.n_streams();
   const int target = (kAppendBlocks + ns - 1) / ns;
   const int most = std::max(1, std::min(target, (sh.Rc + kAppendMinChunk - 1) / kAppendMinChunk));
-  return align_up(pcode_off(ns, most) + (size_t)ns * most * sh.dc * sh.elem(), 256);
+  const size_t code_bytes = sh.q4 ? sizeof(float) : (size_t)sh.elem();   // 4-bit: unrounded candidates
+  return align_up(pcode_off(ns, most) + (size_t)ns * most * sh.dc * code_bytes, 256);
 }
 
 hipError_t launch_append(const Shape& sh, const AppendArgs& a, void* ws, hipStream_t st) {

@@ -439,7 +439,7 @@ __global__ __launch_bounds__(256) void k_search_f32(CompressArgs a, Shape sh) {
 // ---------------------------------------------------------------------------
 
 
-template <int D>
+template <int D, bool Q4>
 __global__ __launch_bounds__(256) void k_encode_mfma(CompressArgs a, Shape sh) {
   constexpr int KS = D / 32;
   constexpr int LDW = D + 8;          // padded LDS row of W_down
@@ -489,21 +489,58 @@ __global__ __launch_bounds__(256) void k_encode_mfma(CompressArgs a, Shape sh) {
   }
   __syncthreads();
 
-  for (int mt = 0; mt < sh.dc / 16; ++mt) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (!Q4) {
+    for (int mt = 0; mt < sh.dc / 16; ++mt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 aw = *reinterpret_cast<const bf16x8*>(&w_lds[(mt * 16 + lrow) * LDW + ks * 32 + lgrp * 8]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bl[ks], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bh[ks], acc, 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 aw = *reinterpret_cast<const bf16x8*>(&w_lds[(mt * 16 + lrow) * LDW + ks * 32 + lgrp * 8]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bl[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bh[ks], acc, 0, 0, 0);
+      }
+      // Lane l holds code elements mt*16 + 4*(l/16) + (0..3) of row l%16.
+      if (valid) {
+        uint2 o;
+        o.x = pk_bf16_rn(acc[0], acc[1]);
+        o.y = pk_bf16_rn(acc[2], acc[3]);
+        *reinterpret_cast<uint2*>(codes + (size_t)n * sh.dc + mt * 16 + lgrp * 4) = o;
+      }
     }
-    // Lane l holds code elements mt*16 + 4*(l/16) + (0..3) of row l%16.
-    if (valid) {
-      uint2 o;
-      o.x = pk_bf16_rn(acc[0], acc[1]);
-      o.y = pk_bf16_rn(acc[2], acc[3]);
-      *reinterpret_cast<uint2*>(codes + (size_t)n * sh.dc + mt * 16 + lgrp * 4) = o;
+  } else {
+    // 4-bit codes: the whole row first (up to D / 16 tiles), then its
+    // maximum magnitude over the row's lanes l, l ^ 16, l ^ 32, l ^ 48, the
+    // scale and the nibbles.
+    const int nmt = sh.dc / 16;
+    f32x4 acc[D / 16];
+    float amax = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) {
+      acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (mt < nmt) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 aw = *reinterpret_cast<const bf16x8*>(&w_lds[(mt * 16 + lrow) * LDW + ks * 32 + lgrp * 8]);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bl[ks], acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bh[ks], acc[mt], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(acc[mt][i]));
+      }
     }
+    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    const uint16_t sbits = f2bf(amax / 7.0f);
+    const float scale = bf2f(sbits);
+    uint8_t* qrow = (uint8_t*)a.codes + ((size_t)stream * sh.Nc + n) * (sh.dc / 2);
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) {
+      if (mt < nmt && valid) {
+        const uint32_t q0 = (uint32_t)q4_quant(acc[mt][0], scale) & 15u, q1 = (uint32_t)q4_quant(acc[mt][1], scale) & 15u;
+        const uint32_t q2 = (uint32_t)q4_quant(acc[mt][2], scale) & 15u, q3 = (uint32_t)q4_quant(acc[mt][3], scale) & 15u;
+        *reinterpret_cast<uint16_t*>(qrow + mt * 8 + lgrp * 2) = (uint16_t)(q0 | (q1 << 4) | (q2 << 8) | (q3 << 12));
+      }
+    }
+    if (valid && lgrp == 0) ((uint16_t*)a.scales)[(size_t)stream * sh.Nc + n] = sbits;
   }
 }
 
@@ -524,13 +561,37 @@ __global__ __launch_bounds__(256) void k_encode_f32(CompressArgs a, Shape sh) {
   float dl[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) dl[i] = (src[(int64_t)t * a.st + i] - mu[i]) - refs[(size_t)r * D + i];
-  float* codes = (float*)a.codes + ((size_t)stream * sh.Nc + n) * sh.dc;
+  if (!sh.q4) {
+    float* codes = (float*)a.codes + ((size_t)stream * sh.Nc + n) * sh.dc;
+    for (int j = 0; j < sh.dc; ++j) {
+      float c = 0.f;
+#pragma unroll
+      for (int i = 0; i < D; ++i) c = fmaf(wd[(size_t)j * D + i], dl[i], c);
+      codes[j] = c;
+    }
+    return;
+  }
+  // 4-bit codes: one pass for the row's maximum magnitude, a second pass
+  // recomputes each code (same order, same value) and quantizes it.
+  float amax = 0.f;
   for (int j = 0; j < sh.dc; ++j) {
     float c = 0.f;
 #pragma unroll
     for (int i = 0; i < D; ++i) c = fmaf(wd[(size_t)j * D + i], dl[i], c);
-    codes[j] = c;
+    amax = fmaxf(amax, fabsf(c));
   }
+  const float scale = amax / 7.0f;
+  uint8_t* qrow = (uint8_t*)a.codes + ((size_t)stream * sh.Nc + n) * (sh.dc / 2);
+  for (int j = 0; j < sh.dc; j += 2) {
+    float c0 = 0.f, c1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      c0 = fmaf(wd[(size_t)j * D + i], dl[i], c0);
+      c1 = fmaf(wd[(size_t)(j + 1) * D + i], dl[i], c1);
+    }
+    qrow[j / 2] = (uint8_t)(((uint32_t)q4_quant(c0, scale) & 15u) | (((uint32_t)q4_quant(c1, scale) & 15u) << 4));
+  }
+  ((float*)a.scales)[(size_t)stream * sh.Nc + n] = scale;
 }
 
 template <int D>
@@ -542,16 +603,23 @@ hipError_t launch_compress_d(const Shape& sh, const CompressArgs& a, hipStream_t
   const dim3 g_enc(xcd_grid(ns, (sh.N + 63) / 64)), g_enc32((sh.N + 255) / 256, ns);
   void* const* ev = a.events;
   hipError_t e;
-#define DKV_TRY(x) \
-  if ((e = (x)) != hipSuccess) return e
+#define DKV_TRY(x)                         \
+  do {                                     \
+    if ((e = (x)) != hipSuccess) return e; \
+  } while (0)
   if (sh.bf16) {
     DKV_TRY(launch(k_mean_partial<BF16>, g_mean, 256, st, ev_start(ev, 0), nullptr, a, sh));
     DKV_TRY(launch(k_mean_final<BF16>, ns, 256, st, nullptr, ev_stop(ev, 0), a, sh, chunks));
     DKV_TRY(launch(k_center_refs<BF16>, g_ref, 256, st, ev_start(ev, 1), ev_stop(ev, 1), a, sh));
     if (sh.N > 0) {
       DKV_TRY(launch(k_search_mfma<D>, g_search, kSearchThreads, st, ev_start(ev, 2), ev_stop(ev, 2), a, sh));
-      DKV_TRY(launch_lds(k_encode_mfma<D>, g_enc, 256, (size_t)sh.dc * (D + 8) * 2, st, ev_start(ev, 3),
-                         ev_stop(ev, 3), a, sh));
+      if (sh.q4) {
+        DKV_TRY(launch_lds(k_encode_mfma<D, true>, g_enc, 256, (size_t)sh.dc * (D + 8) * 2, st, ev_start(ev, 3),
+                           ev_stop(ev, 3), a, sh));
+      } else {
+        DKV_TRY(launch_lds(k_encode_mfma<D, false>, g_enc, 256, (size_t)sh.dc * (D + 8) * 2, st, ev_start(ev, 3),
+                           ev_stop(ev, 3), a, sh));
+      }
     }
   } else {
     DKV_TRY(launch(k_mean_partial<F32>, g_mean, 256, st, ev_start(ev, 0), nullptr, a, sh));

@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256) void k_refscore(DecodeArgs a, Shape sh) {
 // tokens; lanes own head-dim columns (acc_r) and code columns (acc_c).
 // ---------------------------------------------------------------------------
 
-template <class S, int D, int GP>
+template <class S, int D, int GP, bool Q4>
 __global__ __launch_bounds__(256) void k_split_valu(DecodeArgs a, Shape sh) {
   constexpr int RPL = D / 64;            // head-dim columns per lane
   __shared__ float qp_l[GP][D];
@@ -112,6 +112,9 @@ __global__ __launch_bounds__(256) void k_split_valu(DecodeArgs a, Shape sh) {
   const typename S::T* refsV = (const typename S::T*)a.refs + sV * sh.Rc * D;
   const typename S::T* codesK = (const typename S::T*)a.codes + sK * sh.Nc * dc;
   const typename S::T* codesV = (const typename S::T*)a.codes + sV * sh.Nc * dc;
+  // 4-bit codes: rows of d_c / 2 bytes and one scale per row.
+  const uint8_t* qK = (const uint8_t*)a.codes + sK * sh.Nc * (dc / 2);
+  const uint8_t* qV = (const uint8_t*)a.codes + sV * sh.Nc * (dc / 2);
 
   float m[GP], lsum[GP], accr[GP][RPL], accc[GP][2];
 #pragma unroll
@@ -145,10 +148,29 @@ __global__ __launch_bounds__(256) void k_split_valu(DecodeArgs a, Shape sh) {
 #pragma unroll
       for (int g = 0; g < GP; ++g) sc[g] = g < G ? score[(size_t)rk * Gs + g] : -INFINITY;
       if (coded) {
-        for (int j = 0; j < dc; ++j) {
-          const float cj = S::load(codesK[(size_t)u * dc + j]);
+        if constexpr (Q4) {
+          const uint32_t* row = (const uint32_t*)(qK + (size_t)u * (dc / 2));
+          const float scl = ld<S>(a.scales, sK * sh.Nc + u);
+          float cd[GP];
 #pragma unroll
-          for (int g = 0; g < GP; ++g) sc[g] = fmaf(qp_l[g][j], cj, sc[g]);
+          for (int g = 0; g < GP; ++g) cd[g] = 0.f;
+          for (int w = 0; w < dc / 8; ++w) {
+            const uint32_t word = row[w];
+#pragma unroll
+            for (int k2 = 0; k2 < 8; ++k2) {
+              const float cj = q4_at(word, k2);
+#pragma unroll
+              for (int g = 0; g < GP; ++g) cd[g] = fmaf(qp_l[g][8 * w + k2], cj, cd[g]);
+            }
+          }
+#pragma unroll
+          for (int g = 0; g < GP; ++g) sc[g] = fmaf(scl, cd[g], sc[g]);
+        } else {
+          for (int j = 0; j < dc; ++j) {
+            const float cj = S::load(codesK[(size_t)u * dc + j]);
+#pragma unroll
+            for (int g = 0; g < GP; ++g) sc[g] = fmaf(qp_l[g][j], cj, sc[g]);
+          }
         }
       }
     } else {
@@ -176,9 +198,17 @@ __global__ __launch_bounds__(256) void k_split_valu(DecodeArgs a, Shape sh) {
       for (int e = 0; e < RPL; ++e) xr[e] = S::load(refsV[(size_t)r * D + lane * RPL + e]);
       float c0 = 0.f, c1 = 0.f;
       if (coded) {
-        const size_t row = (size_t)(base + k) * dc;
-        if (lane < dc) c0 = S::load(codesV[row + lane]);
-        if (lane + 64 < dc) c1 = S::load(codesV[row + lane + 64]);
+        if constexpr (Q4) {
+          const uint8_t* row = qV + (size_t)(base + k) * (dc / 2);
+          const float scl = ld<S>(a.scales, sV * sh.Nc + base + k);
+          if (lane < dc) c0 = scl * (float)((int32_t)((uint32_t)row[lane >> 1] << (24 + 4 * (1 - (lane & 1)))) >> 28);
+          if (lane + 64 < dc)
+            c1 = scl * (float)((int32_t)((uint32_t)row[(lane + 64) >> 1] << (24 + 4 * (1 - (lane & 1)))) >> 28);
+        } else {
+          const size_t row = (size_t)(base + k) * dc;
+          if (lane < dc) c0 = S::load(codesV[row + lane]);
+          if (lane + 64 < dc) c1 = S::load(codesV[row + lane + 64]);
+        }
       }
 #pragma unroll
       for (int g = 0; g < GP; ++g) {
@@ -269,7 +299,7 @@ __device__ __forceinline__ void load_cols(const typename S::T* p, float (&v)[N])
   }
 }
 
-template <class S, int D, int GP, typename IdxT>
+template <class S, int D, int GP, typename IdxT, bool Q4>
 __global__ __launch_bounds__(256) void k_split_sel(DecodeArgs a, Shape sh) {
   constexpr int RPL = D / 64;            // head-dim columns per lane
   constexpr int UN = 16;                 // entries per accumulate step
@@ -304,6 +334,12 @@ __global__ __launch_bounds__(256) void k_split_sel(DecodeArgs a, Shape sh) {
   const T* codesV = has_codes ? (const T*)a.codes + sV * sh.Nc * dc : (const T*)kZeroRow;
   const IdxT* idxK = has_codes ? (const IdxT*)a.idx + sK * sh.Nc : (const IdxT*)kZeroRow;
   const IdxT* idxV = has_codes ? (const IdxT*)a.idx + sV * sh.Nc : (const IdxT*)kZeroRow;
+  // 4-bit codes: rows of d_c / 2 bytes (stride 0 on the zero row) and scales.
+  const int qstride = has_codes ? dc / 2 : 0;
+  const uint8_t* qK = has_codes ? (const uint8_t*)a.codes + sK * sh.Nc * (dc / 2) : (const uint8_t*)kZeroRow;
+  const uint8_t* qV = has_codes ? (const uint8_t*)a.codes + sV * sh.Nc * (dc / 2) : (const uint8_t*)kZeroRow;
+  const T* sclK = has_codes && Q4 ? (const T*)a.scales + sK * sh.Nc : (const T*)kZeroRow;
+  const T* sclV = has_codes && Q4 ? (const T*)a.scales + sV * sh.Nc : (const T*)kZeroRow;
 
   float m[GP], lsum[GP], accr[GP][RPL], accc[GP][2];
 #pragma unroll
@@ -338,14 +374,27 @@ __global__ __launch_bounds__(256) void k_split_sel(DecodeArgs a, Shape sh) {
     for (int j0 = 0; j0 < dc; j0 += 32) {
       float cv[4][8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        load8<S>(codesK + (size_t)u * cstride + (has_codes ? min(j0 + 8 * q, dc - 8) : 0), cv[q]);
+      for (int q = 0; q < 4; ++q) {
+        const int jj = has_codes ? min(j0 + 8 * q, dc - 8) : 0;
+        if constexpr (Q4) {
+          const uint32_t word = *(const __attribute__((address_space(1))) uint32_t*)(qK + (size_t)u * qstride + jj / 2);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) cv[q][i] = q4_at(word, i);
+        } else {
+          load8<S>(codesK + (size_t)u * cstride + jj, cv[q]);
+        }
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int g = 0; g < GP; ++g)
 #pragma unroll
           for (int i = 0; i < 8; ++i) cd[g] = fmaf(qp_l[g][j0 + 8 * q + i], cv[q][i], cd[g]);
+    }
+    if constexpr (Q4) {
+      const float scl = S::load(sclK[u]);
+#pragma unroll
+      for (int g = 0; g < GP; ++g) cd[g] *= scl;
     }
     const int rk = coded ? ik : r, rv = coded ? iv : r;
     // The entry's S row, four columns per 16-byte load (rows hold Gs >= 4
@@ -386,11 +435,19 @@ __global__ __launch_bounds__(256) void k_split_sel(DecodeArgs a, Shape sh) {
         const int rr = __builtin_amdgcn_readlane(rv, k);
         const int uu = max(__builtin_amdgcn_readlane(ucol, k), 0);
         load_cols<S, RPL>(refsV + (size_t)rr * D + lane * RPL, xr[i]);
-        float t0[1], t1[1];
-        load_cols<S, 1>(codesV + (size_t)uu * cstride + (has_codes ? cl0 : 0), t0);
-        load_cols<S, 1>(codesV + (size_t)uu * cstride + (has_codes ? cl1 : 0), t1);
-        c0[i] = t0[0];
-        c1[i] = t1[0];
+        if constexpr (Q4) {
+          const uint8_t* row = qV + (size_t)uu * qstride;
+          const float scl = S::load(sclV[uu]);
+          const uint32_t b0 = has_codes ? row[cl0 >> 1] : 0u, b1 = has_codes ? row[cl1 >> 1] : 0u;
+          c0[i] = scl * (float)((int32_t)(b0 << (24 + 4 * (1 - (cl0 & 1)))) >> 28);
+          c1[i] = scl * (float)((int32_t)(b1 << (24 + 4 * (1 - (cl1 & 1)))) >> 28);
+        } else {
+          float t0[1], t1[1];
+          load_cols<S, 1>(codesV + (size_t)uu * cstride + (has_codes ? cl0 : 0), t0);
+          load_cols<S, 1>(codesV + (size_t)uu * cstride + (has_codes ? cl1 : 0), t1);
+          c0[i] = t0[0];
+          c1[i] = t1[0];
+        }
       }
 #pragma unroll
       for (int i = 0; i < UN; ++i) {
@@ -516,14 +573,18 @@ __global__ __launch_bounds__(128) void k_combine(DecodeArgs a, Shape sh) {
 
 template <class S, int D, int GP>
 hipError_t launch_split(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
-  return launch(k_split_valu<S, D, GP>, dim3(a.splits, sh.B * sh.H), 256, st, ev_start(a.events, 1),
-                ev_stop(a.events, 1), a, sh);
+  const dim3 grid(a.splits, sh.B * sh.H);
+  return sh.q4 ? launch(k_split_valu<S, D, GP, true>, grid, 256, st, ev_start(a.events, 1), ev_stop(a.events, 1), a, sh)
+               : launch(k_split_valu<S, D, GP, false>, grid, 256, st, ev_start(a.events, 1), ev_stop(a.events, 1), a,
+                        sh);
 }
 
 template <class S, int D>
 hipError_t launch_decode_sd(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
-  hipError_t e = launch(k_refscore<S, D>, dim3((sh.R + 63) / 64, sh.B * sh.H), 256, st, ev_start(a.events, 0),
-                        ev_stop(a.events, 0), a, sh);
+  const bool mfma = mfma_side_kernels_supported(sh, a.G, a.splits);
+  hipError_t e = mfma ? launch_refscore_mfma(sh, a, st)
+                      : launch(k_refscore<S, D>, dim3((sh.R + 63) / 64, sh.B * sh.H), 256, st,
+                               ev_start(a.events, 0), ev_stop(a.events, 0), a, sh);
   if (e != hipSuccess) return e;
   if (a.G <= 1) e = launch_split<S, D, 1>(sh, a, st);
   else if (a.G <= 2) e = launch_split<S, D, 2>(sh, a, st);
@@ -531,23 +592,29 @@ hipError_t launch_decode_sd(const Shape& sh, const DecodeArgs& a, hipStream_t st
   else if (a.G <= 8) e = launch_split<S, D, 8>(sh, a, st);
   else e = launch_split<S, D, 16>(sh, a, st);
   if (e != hipSuccess) return e;
+  if (mfma) return launch_combine_mfma(sh, a, st);
   return launch(k_combine<S, D>, dim3(sh.B * a.Hq), 128, st, ev_start(a.events, 2), ev_stop(a.events, 2), a, sh);
+}
+
+template <class S, int D, typename IdxT, bool Q4>
+hipError_t launch_split_sel_q(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
+  const dim3 grid(a.splits, sh.B * sh.H);
+  const hipEvent_t e0 = ev_start(a.events, 1), e1 = ev_stop(a.events, 1);
+  if (a.G <= 1) return launch(k_split_sel<S, D, 1, IdxT, Q4>, grid, 256, st, e0, e1, a, sh);
+  if (a.G <= 2) return launch(k_split_sel<S, D, 2, IdxT, Q4>, grid, 256, st, e0, e1, a, sh);
+  if (a.G <= 4) return launch(k_split_sel<S, D, 4, IdxT, Q4>, grid, 256, st, e0, e1, a, sh);
+  if (a.G <= 8) return launch(k_split_sel<S, D, 8, IdxT, Q4>, grid, 256, st, e0, e1, a, sh);
+  return launch(k_split_sel<S, D, 16, IdxT, Q4>, grid, 256, st, e0, e1, a, sh);
 }
 
 template <class S, int D, typename IdxT>
 hipError_t launch_split_sel(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
-  const dim3 grid(a.splits, sh.B * sh.H);
-  const hipEvent_t e0 = ev_start(a.events, 1), e1 = ev_stop(a.events, 1);
-  if (a.G <= 1) return launch(k_split_sel<S, D, 1, IdxT>, grid, 256, st, e0, e1, a, sh);
-  if (a.G <= 2) return launch(k_split_sel<S, D, 2, IdxT>, grid, 256, st, e0, e1, a, sh);
-  if (a.G <= 4) return launch(k_split_sel<S, D, 4, IdxT>, grid, 256, st, e0, e1, a, sh);
-  if (a.G <= 8) return launch(k_split_sel<S, D, 8, IdxT>, grid, 256, st, e0, e1, a, sh);
-  return launch(k_split_sel<S, D, 16, IdxT>, grid, 256, st, e0, e1, a, sh);
+  return sh.q4 ? launch_split_sel_q<S, D, IdxT, true>(sh, a, st) : launch_split_sel_q<S, D, IdxT, false>(sh, a, st);
 }
 
 template <class S, int D>
 hipError_t launch_decode_sel_sd(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
-  const bool mfma = decode_fused_supported(sh, a.G, a.splits);
+  const bool mfma = mfma_side_kernels_supported(sh, a.G, a.splits);
   hipError_t e = mfma ? launch_refscore_mfma(sh, a, st)
                       : launch(k_refscore<S, D>, dim3((sh.R + 63) / 64, sh.B * sh.H), 256, st,
                                ev_start(a.events, 0), ev_stop(a.events, 0), a, sh);

@@ -627,8 +627,12 @@ hipError_t launch_split_s(const Shape& sh, const DecodeArgs& a, hipStream_t st, 
 
 }  // namespace
 
-bool decode_fused_supported(const Shape& sh, int G, int splits) {
+bool mfma_side_kernels_supported(const Shape& sh, int G, int splits) {
   return sh.bf16 && sh.d == kD && G <= 4 && sh.dc <= kMaxDc && splits <= kMfmaMaxSplits;
+}
+
+bool decode_fused_supported(const Shape& sh, int G, int splits) {
+  return !sh.q4 && mfma_side_kernels_supported(sh, G, splits);
 }
 
 // The split kernel holds one 512-thread block per CU: about 256 blocks over

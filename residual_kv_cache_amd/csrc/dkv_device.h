@@ -96,6 +96,23 @@ __device__ __forceinline__ void load8(const typename S::T* p, float (&v)[8]) {
 }
 
 // ---------------------------------------------------------------------------
+// 4-bit codes: element e of a row sits in byte e / 2, low nibble for even e,
+// two's complement.
+// ---------------------------------------------------------------------------
+
+// Nibble k (0..7) of a 32-bit word holding elements 8w .. 8w + 7, as float.
+__device__ __forceinline__ float q4_at(uint32_t word, int k) {
+  return (float)((int32_t)(word << (28 - 4 * k)) >> 28);
+}
+
+// Quantized value of code c under `scale` (0 when the scale is 0).
+__device__ __forceinline__ int q4_quant(float c, float scale) {
+  if (!(scale > 0.f)) return 0;
+  const float x = rintf(c / scale);   // IEEE division, ties to even
+  return (int)fminf(fmaxf(x, -8.f), 7.f);
+}
+
+// ---------------------------------------------------------------------------
 // Wave64 reductions (butterfly; every lane ends with the result).
 // ---------------------------------------------------------------------------
 

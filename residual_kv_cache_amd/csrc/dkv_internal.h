@@ -24,8 +24,11 @@ struct Shape {
   int B;        // sequences
   int idx_bytes;
   int bf16;     // 1 = bfloat16 storage, 0 = float32
+  int q4;       // 1 = 4-bit codes with one scale per row
   __host__ __device__ int n_streams() const { return B * H * 2; }
   int elem() const { return bf16 ? 2 : 4; }
+  // Bytes of one code row.
+  __host__ __device__ int code_row_bytes() const { return q4 ? dc / 2 : dc * (bf16 ? 2 : 4); }
 };
 
 // XCD-aware block order: block L runs on XCD L % 8 (workgroups are
@@ -83,6 +86,8 @@ inline size_t decode_ws_bytes(const Shape& sh, int G, int splits) {
 // query heads per KV head, code dim up to 48, at most kMfmaMaxSplits splits.
 constexpr int kMfmaMaxSplits = 256;
 bool decode_fused_supported(const Shape& sh, int G, int splits);
+// The MFMA reference-score and combine kernels alone (any code format).
+bool mfma_side_kernels_supported(const Shape& sh, int G, int splits);
 int decode_fused_auto_splits(const Shape& sh);
 
 struct CompressArgs {
@@ -97,6 +102,7 @@ struct CompressArgs {
   void* codes;
   void* idx;
   void* mu;
+  void* scales;              // 4-bit codes: per-row scales, else NULL
   double* mean_part;
   float* inv_n;
   void* const* events;       // DKV_COMPRESS_EVENTS hipEvent_t or NULL
@@ -116,6 +122,7 @@ struct DecodeArgs {
   const void* codes;
   const void* idx;
   const void* mu;
+  const void* scales;        // 4-bit codes: per-row scales, else NULL
   float* score;              // [B][H][R][score_cols(G)]
   float* qp;                 // [B][H][G][dc]
   float* part;               // [B][H][splits][G][rec]
@@ -157,6 +164,7 @@ struct AppendArgs {
   void* codes;
   void* idx;
   const void* mu;
+  void* scales;              // 4-bit codes: per-row scales, else NULL
   void* const* events;       // DKV_APPEND_EVENTS hipEvent_t or NULL
 };
 

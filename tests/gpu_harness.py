@@ -103,12 +103,53 @@ def gpu_compress(cfg: K.Config, inp: Inputs, k_dev=None, v_dev=None, mu_in=None)
     return lay, cache
 
 
+def unpack_q4(b: np.ndarray) -> np.ndarray:
+    """Packed 4-bit codes [..][dc/2] uint8 -> int64 [..][dc]: element 2i is
+    the low nibble of byte i, two's complement."""
+    b = b.astype(np.int64)
+    lo, hi = b & 15, b >> 4
+    out = np.stack([lo, hi], axis=-1).reshape(*b.shape[:-1], b.shape[-1] * 2)
+    return (out ^ 8) - 8
+
+
 def cache_numpy(cache: D.Cache) -> dict:
+    """Host copies; with 4-bit codes "q" and "scales" are what is stored and
+    "codes" the decoder's values scale * q."""
     a = cache.arrays()
     idx = a["idx"].cpu().numpy()
     idx = idx.view(np.uint16) if idx.dtype == np.int16 else idx.view(np.uint32)
-    return {"refs": f64(a["refs"]), "codes": f64(a["codes"]), "mu": f64(a["mu"]),
-            "idx": idx.astype(np.int64)}
+    out = {"refs": f64(a["refs"]), "mu": f64(a["mu"]), "idx": idx.astype(np.int64)}
+    if "scales" in a:
+        q = unpack_q4(a["codes"].cpu().numpy())
+        sc = f64(a["scales"])
+        out.update(q=q, scales=sc, codes=q * sc[..., None])
+    else:
+        out["codes"] = f64(a["codes"])
+    return out
+
+
+def check_q4_rows(c_exact: np.ndarray, tol: np.ndarray, q_gpu: np.ndarray, s_gpu: np.ndarray, storage: str) -> dict:
+    """4-bit rows against the oracle's quantization of the exact codes.
+    The GPU computes each code to within ``tol``, so its scale may differ
+    from the oracle's by the rounding of a slightly different max|c| / 7
+    (bounded below), and a value may differ, by one step, only where
+    c / scale lies within the combined code and scale error of a
+    half-integer.  Everything else is bit-exact."""
+    q_o, s_o = O.quantize_q4(c_exact, storage)
+    amax = np.abs(c_exact).max(axis=1)
+    amax_tol = tol.max(axis=1)
+    s_lo = O.rnd(np.maximum(amax - amax_tol, 0) / 7 * (1 - 2.0 ** -22), storage)
+    s_hi = O.rnd((amax + amax_tol) / 7 * (1 + 2.0 ** -22), storage)
+    assert np.all((s_gpu >= s_lo) & (s_gpu <= s_hi)), "a scale lies outside the rounding of max|c| / 7"
+    safe = np.where(s_o > 0, s_o, 1.0)[:, None]
+    x = c_exact / safe
+    dx = tol / safe + np.abs(c_exact) * np.abs(s_gpu - s_o)[:, None] / safe ** 2 + 2.0 ** -20 * np.abs(x) + 1e-12
+    near = np.abs(np.abs(x - np.floor(x)) - 0.5) <= dx
+    diff = q_gpu != q_o
+    bad = diff & ~near
+    assert not bad.any(), f"{int(bad.sum())} 4-bit values differ away from a rounding boundary"
+    assert np.all(np.abs(q_gpu - q_o) <= 1)
+    return {"rows": len(c_exact), "scale_differs": int((s_gpu != s_o).sum()), "value_exempt": int(diff.sum())}
 
 
 def gpu_decode(lay, cache, q_raw, inp: Inputs, n_splits=0, scale=0.0) -> np.ndarray:

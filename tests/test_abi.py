@@ -32,7 +32,7 @@ def test_header_declarations_are_exported():
 
 def test_abi_version_and_status_strings():
     lib = _lib()
-    assert lib.dkv_abi_version() == D.ABI_VERSION == 2
+    assert lib.dkv_abi_version() == D.ABI_VERSION == 3
     for code, name in D.STATUS.items():
         assert lib.dkv_status_str(code).decode().startswith(name)
 
@@ -101,6 +101,33 @@ def test_layout_version_and_dtype():
     assert D.lib().dkv_layout_check(None) == 1
 
 
+@pytest.mark.parametrize("name", list(K.CONFIGS))
+def test_q4_cache_bytes_match_oracle_layout(name):
+    _lib()
+    c = K.CONFIGS[name]
+    lay = D.make_layout(c.dtype, c.head_dim, c.code_dim, c.stride, c.n_kv_heads, c.batch, c.seq_len, code_bits=4)
+    assert D.dkv_layout_check(lay) == 0
+    assert D.dkv_cache_bytes(lay) == O.cache_bytes(c.batch, c.n_kv_heads, c.seq_len, c.stride, c.head_dim,
+                                                   c.code_dim, c.dtype, code_bits=4)
+
+
+def test_q4_carve_and_code_bits_check():
+    _lib()
+    lay = L(seq_len=1000, stride=7, code_bits=4)
+    base = 1 << 20
+    c = D.dkv_cache_carve(lay, base)
+    sizes = O.cache_array_bytes(1, 8, 1000, 7, 128, 32, "bf16", code_bits=4)
+    pad = lambda x: -(-x // 256) * 256
+    assert c.codes == base + pad(sizes["refs"])
+    assert c.idx == c.codes + pad(sizes["codes"])
+    assert c.mu == c.idx + pad(sizes["idx"])
+    assert c.scales == c.mu + pad(sizes["mu"])
+    assert c.scales + pad(sizes["scales"]) == base + D.dkv_cache_bytes(lay)
+    assert D.dkv_cache_carve(L(), base).scales is None
+    for bits in (1, 8, 16, 5):
+        assert D.dkv_layout_check(L(code_bits=bits)) == 2
+
+
 def test_idx_width_switch():
     _lib()
     assert D.make_layout("bf16", 128, 32, 2, 1, 1, 131072).idx_bytes == 2
@@ -133,7 +160,7 @@ def _no_device():
 
 class FakeCache:
     def __init__(self, ptr):
-        self.c = D.dkv_cache(ptr, ptr + 4096, ptr + 8192, ptr + 12288)
+        self.c = D.dkv_cache(ptr, ptr + 4096, ptr + 8192, ptr + 12288, ptr + 16384)
 
 
 def _compress_status(lay, k, v, wd, ws, cache, ws_bytes=None):
