@@ -327,7 +327,18 @@ def main():
         for i in range(SEL_STEPS):
             D.deltakv_decode_attn_sel(lay, caches[i % nrep], q_d[i % nsteps], wuk_d, wuv_d, tok_d, outs[i % nsteps],
                                       ws_d)
+        lay4 = D.make_layout(cfg.dtype, cfg.head_dim, cfg.code_dim, cfg.stride, cfg.n_kv_heads, cfg.batch,
+                             cfg.seq_len, code_bits=4)
+        caches4 = [D.Cache(lay4) for _ in range(max(1, math.ceil(2 * MALL_BYTES / D.dkv_cache_bytes(lay4))))]
+        ws_c4 = D.workspace(D.dkv_compress_workspace_bytes(lay4))
+        for c4 in caches4:
+            D.deltakv_compress(lay4, k_d, v_d, wdk_d, wdv_d, c4, ws_c4)
+        ws_d4 = D.workspace(D.dkv_decode_workspace_bytes(lay4, cfg.n_q_heads))
+        for i in range(Q4_STEPS):
+            D.deltakv_decode_attn(lay4, caches4[i % len(caches4)], q_d[i % nsteps], wuk_d, wuv_d, outs[i % nsteps],
+                                  ws_d4)
         torch.cuda.synchronize()
+        del caches4
         lay_a = D.make_layout(cfg.dtype, cfg.head_dim, cfg.code_dim, cfg.stride, cfg.n_kv_heads, cfg.batch,
                               cfg.seq_len, capacity=cfg.seq_len + APPEND_TOKENS)
         cache_a = D.Cache(lay_a)
@@ -339,8 +350,8 @@ def main():
                              wdk_d, wdv_d, cache_a, ws_a)
         torch.cuda.synchronize()
         log(f"[bench] profile driver: calibration copy of {CALIB_BYTES} bytes, {args.steps} decode steps, "
-            f"splits {splits}, {nrep} cache replicas, {SEL_STEPS} selective decode steps, then {APPEND_TOKENS} "
-            f"appends")
+            f"splits {splits}, {nrep} cache replicas, {SEL_STEPS} selective decode steps, {Q4_STEPS} decode steps "
+            f"with 4-bit codes, then {APPEND_TOKENS} appends")
         return
     D.deltakv_decode_attn(lay, caches[0], q_d[0], wuk_d, wuv_d, outs[0], ws_d, n_splits=splits)
     eager0 = outs[0].clone()
