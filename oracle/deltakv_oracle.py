@@ -39,6 +39,10 @@ seedable instance computed here is:
     O11 4-bit codes: O6 without its rounding, then per row
         scale = rnd(max|c| / 7), q = clamp(rne(c / scale), -8, 7); the
         decoder's code is scale * q
+    O12 k references and the L2 metric: O5 keeps the k best earlier
+        references (by cosine, or by smallest ||x~_t - x~_r||), ties to the
+        lower ordinal, all of them when fewer than k are earlier; O6 and O7
+        use their mean in place of the single reference row
 
 ``rnd`` rounds to the storage dtype (nearest, ties to even).  Storage
 "f64" makes rnd the identity; the pins use it to test the mathematics
@@ -237,6 +241,71 @@ def search(xt: np.ndarray, s: int, block: int = 2048, toks=None):
     return idx, top1, margin
 
 
+def ref_count(t, s, top_k):
+    """References a coded token at position t averages: the k nearest, or
+    all earlier ones (floor(t / s) + 1 of them) when fewer than k exist."""
+    return np.minimum(top_k, np.asarray(t) // s + 1)
+
+
+def search_topk(xt: np.ndarray, s: int, top_k: int, metric: str = "cos", toks=None, block: int = 1024):
+    """O12.  The k earlier references nearest to each non-reference token
+    ([en] §3 "Strided Reference Selection": the k nearest neighbours in the
+    strided set by L2 distance; [pt] §2 "Metodologia" and [fr] §2
+    "Méthodologie", the k closest references).  ``metric`` "cos" ranks by
+    cosine (as O5), "l2" by smallest squared distance ||x~_t - x~_r||^2.
+    Ranking ties go to the lower ordinal.
+
+    Returns (idx [n][k] with each token's references in ascending ordinal
+    order, zero past its count; count [n]; margin [n]).  The margin is the
+    gap between the last kept and the first dropped reference: the cosine
+    difference, or for L2 the distance difference over
+    ||x~_t||^2 + ||x~_last||^2 (dimensionless); inf when none is dropped."""
+    T, d = xt.shape
+    R = n_refs(T, s)
+    toks = nonref_positions(T, s) if toks is None else np.asarray(toks, np.int64)
+    refs = xt[ref_positions(T, s)]
+    nr2 = (refs * refs).sum(axis=1)
+    r_pos = np.arange(R, dtype=np.int64) * s
+    idx = np.zeros((len(toks), top_k), np.int64)
+    count = ref_count(toks, s, top_k)
+    margin = np.full(len(toks), np.inf)
+    for a in range(0, len(toks), block):
+        tb = toks[a:a + block]
+        X = xt[tb]
+        nt2 = (X * X).sum(axis=1)
+        dots = X @ refs.T
+        if metric == "cos":
+            den = np.sqrt(nt2)[:, None] * np.sqrt(nr2)[None, :]
+            score = np.where(den > 0, dots / np.where(den > 0, den, 1.0), 0.0)
+        elif metric == "l2":
+            score = -(nt2[:, None] - 2 * dots + nr2[None, :])
+        else:
+            raise ValueError(metric)
+        score = np.where(r_pos[None, :] < tb[:, None], score, -np.inf)
+        order = np.argsort(-score, axis=1, kind="stable")   # stable: equal scores keep ascending ordinals
+        for i in range(len(tb)):
+            c = int(count[a + i])
+            kept = order[i, :c]
+            idx[a + i, :c] = np.sort(kept)
+            if c < len(order[i]) and np.isfinite(score[i, order[i, c]]):
+                gap = score[i, kept[-1]] - score[i, order[i, c]]
+                if metric == "l2":
+                    gap = gap / (nt2[i] + nr2[kept[-1]] + 1e-300)
+                margin[a + i] = gap
+    return idx, count, margin
+
+
+def mean_refs(xt: np.ndarray, s: int, idx, count) -> np.ndarray:
+    """O12.  KV^R: the mean of each token's retrieved reference rows ([en] §3
+    "Residual Encoding"), in fp64, never rounded (it is not stored)."""
+    idx = np.asarray(idx, np.int64)
+    out = np.empty((len(idx), xt.shape[1]))
+    for j in range(len(idx)):
+        c = int(count[j])
+        out[j] = xt[idx[j, :c] * s].sum(axis=0) / c
+    return out
+
+
 def encode(k, mu, xt, s, idx, w_down, storage, toks=None):
     """O6.  Residual of each non-reference token against its reference,
     projected to d_c dimensions and rounded to storage ([en] §3 "Residual
@@ -245,8 +314,17 @@ def encode(k, mu, xt, s, idx, w_down, storage, toks=None):
     d_c-dimensional code)."""
     T = k.shape[0]
     toks = nonref_positions(T, s) if toks is None else np.asarray(toks, np.int64)
-    delta = (k[toks] - mu) - xt[np.asarray(idx, np.int64) * s]
+    delta = (k[toks] - mu) - ref_rows(xt, s, toks, idx)
     return rnd(delta @ w_down.T, storage)
+
+
+def ref_rows(xt, s, toks, idx) -> np.ndarray:
+    """The reference each token's residual is taken against: the row of its
+    single ordinal, or (ordinals [n][k], O12) the mean of its references."""
+    idx = np.asarray(idx, np.int64)
+    if idx.ndim == 1:
+        return xt[idx * s]
+    return mean_refs(xt, s, idx, ref_count(toks, s, idx.shape[1]))
 
 
 def quantize_q4(c, storage):
@@ -279,11 +357,12 @@ def encode_exact(k, mu, xt, s, idx, w_down, toks=None) -> np.ndarray:
     """W_down ((k_t - mu) - x~_ref(t)) before any rounding (fp64)."""
     T = k.shape[0]
     toks = nonref_positions(T, s) if toks is None else np.asarray(toks, np.int64)
-    delta = (k[toks] - mu) - xt[np.asarray(idx, np.int64) * s]
+    delta = (k[toks] - mu) - ref_rows(xt, s, toks, idx)
     return delta @ w_down.T
 
 
-def compress_stream(k, s, w_down, storage, mu_in=None, force_idx=None, code_bits=16) -> dict:
+def compress_stream(k, s, w_down, storage, mu_in=None, force_idx=None, code_bits=16, top_k=1,
+                    metric="cos") -> dict:
     """One stream, steps O2-O6.  ``k`` holds storage-dtype values as float64.
     ``force_idx`` re-encodes with given references (used where several
     references are equally correct within the search tolerance).  With
@@ -294,7 +373,11 @@ def compress_stream(k, s, w_down, storage, mu_in=None, force_idx=None, code_bits
     mu = shared_component(k, storage) if mu_in is None else np.asarray(mu_in, np.float64)
     xt = center(k, mu, storage)
     refs = xt[ref_positions(T, s)]
-    idx, top1, margin = search(xt, s)
+    if top_k == 1 and metric == "cos":
+        idx, top1, margin = search(xt, s)
+    else:   # O12: ordinals [N][k]
+        idx, _, margin = search_topk(xt, s, top_k, metric)
+        top1 = None
     if force_idx is not None:
         idx = np.asarray(force_idx, np.int64)
     out = {"mu": mu, "refs": refs, "idx": idx, "top1": top1, "margin": margin, "xt": xt}
@@ -306,17 +389,18 @@ def compress_stream(k, s, w_down, storage, mu_in=None, force_idx=None, code_bits
     return out
 
 
-def compress(k, v, s, w_down_k, w_down_v, storage, code_bits=16) -> dict:
+def compress(k, v, s, w_down_k, w_down_v, storage, code_bits=16, top_k=1, metric="cos") -> dict:
     """All streams of one layer: k, v are [B][H][T][d].  Returns arrays shaped
     [B][H][2][...] with index 0 = K and 1 = V."""
     B, H, T, d = k.shape
-    names = ("mu", "refs", "idx", "codes", "top1", "margin") + (("q", "scales") if code_bits == 4 else ())
+    names = ("mu", "refs", "idx", "codes", "margin") + (("top1",) if top_k == 1 and metric == "cos" else ()) \
+        + (("q", "scales") if code_bits == 4 else ())
     out = {n: [] for n in names}
     for b in range(B):
         row = {n: [] for n in out}
         for h in range(H):
-            pair = [compress_stream(k[b, h], s, w_down_k, storage, code_bits=code_bits),
-                    compress_stream(v[b, h], s, w_down_v, storage, code_bits=code_bits)]
+            pair = [compress_stream(k[b, h], s, w_down_k, storage, code_bits=code_bits, top_k=top_k, metric=metric),
+                    compress_stream(v[b, h], s, w_down_v, storage, code_bits=code_bits, top_k=top_k, metric=metric)]
             for n in out:
                 row[n].append(np.stack([p[n] for p in pair]))
         for n in out:
@@ -324,7 +408,7 @@ def compress(k, v, s, w_down_k, w_down_v, storage, code_bits=16) -> dict:
     return {n: np.stack(a) for n, a in out.items()}
 
 
-def append_token(mu, refs, k_t, t, s, w_down, storage, code_bits=16) -> dict:
+def append_token(mu, refs, k_t, t, s, w_down, storage, code_bits=16, top_k=1, metric="cos") -> dict:
     """A decode-time token joins a compressed stream ([en] §3 "Strided
     Reference Selection": references sit at a fixed stride and each new
     token retrieves the nearest earlier one; §3 "Residual Encoding").
@@ -341,6 +425,8 @@ def append_token(mu, refs, k_t, t, s, w_down, storage, code_bits=16) -> dict:
     x = rnd(np.asarray(k_t, np.float64) - mu, storage)
     if t % s == 0:
         return {"ref": x}
+    if top_k > 1 or metric != "cos":
+        return _append_topk(mu, refs, k_t, x, t, s, w_down, storage, code_bits, top_k, metric)
     nx = math.sqrt(float(x @ x))
     cands = []
     for r in range(len(refs)):
@@ -364,6 +450,43 @@ def append_token(mu, refs, k_t, t, s, w_down, storage, code_bits=16) -> dict:
     return out
 
 
+def _append_topk(mu, refs, k_t, x, t, s, w_down, storage, code_bits, top_k, metric) -> dict:
+    """O10 with O12: rank the references at positions below t one by one
+    (score, then lower ordinal), keep the first min(k, count), encode
+    against their mean."""
+    cands = []
+    for r in range(len(refs)):
+        if r * s >= t:
+            break
+        y = refs[r]
+        if metric == "cos":
+            den = math.sqrt(float(x @ x)) * math.sqrt(float(y @ y))
+            sc = float(x @ y) / den if den > 0 else 0.0
+        else:
+            sc = -float((x - y) @ (x - y))
+        cands.append((sc, r))
+    ranked = sorted(cands, key=lambda p: (-p[0], p[1]))
+    c = min(top_k, len(ranked))
+    kept = sorted(r for _, r in ranked[:c])
+    m = sum(refs[r] for r in kept) / c
+    resid = (np.asarray(k_t, np.float64) - mu) - m
+    out = {"idx": kept + [0] * (top_k - c), "count": c}
+    if c < len(ranked):
+        gap = ranked[c - 1][0] - ranked[c][0]
+        if metric == "l2":
+            y = refs[ranked[c - 1][1]]
+            gap /= float(x @ x) + float(y @ y) + 1e-300
+        out["margin"] = gap
+    else:
+        out["margin"] = math.inf
+    if code_bits == 4:
+        q, scale = quantize_q4((w_down @ resid)[None], storage)
+        out.update(q=q[0], scale=scale[0], code=q[0] * scale[0])
+    else:
+        out["code"] = rnd(w_down @ resid, storage)
+    return out
+
+
 # ---------------------------------------------------------------------------
 # Decode.
 # ---------------------------------------------------------------------------
@@ -376,7 +499,14 @@ def reconstruct_stream(mu, refs, idx, codes, w_up, s, T) -> np.ndarray:
     out = np.empty((T, d))
     out[ref_positions(T, s)] = mu + refs
     toks = nonref_positions(T, s)
-    out[toks] = mu + refs[np.asarray(idx, np.int64)] + codes @ w_up.T
+    idx = np.asarray(idx, np.int64)
+    if idx.ndim == 1:
+        base = refs[idx]
+    else:   # O12: the mean of the token's references
+        cnt = ref_count(toks, s, idx.shape[1])
+        base = np.stack([refs[idx[j, :cnt[j]]].sum(axis=0) / cnt[j] for j in range(len(toks))]) \
+            if len(toks) else np.zeros((0, d))
+    out[toks] = mu + base + codes @ w_up.T
     return out
 
 

@@ -40,6 +40,12 @@ PINS = [
     P.test_q4_compress_stream_uses_unrounded_codes,
     P.test_q4_full_rank_code_error_bound,
     lambda: P.test_q4_stream_bytes_closed_form("llama8b_32k", 1138944),
+    lambda: P.test_topk_matches_brute_force_integer_data(97, 5, 3, 6, 6, "l2"),
+    lambda: P.test_topk_matches_brute_force_integer_data(60, 2, 4, 3, 8, "cos"),
+    P.test_l2_hand_case,
+    P.test_topk_mean_residual_hand_case,
+    lambda: P.test_topk_full_rank_reconstructs_exactly("l2"),
+    P.test_topk_all_references_is_the_running_mean,
 ]
 
 
@@ -218,6 +224,58 @@ def _sel_off_by_one(cache, q, w_up_k, w_up_v, s, T, sel, scale=None):
     return _ORIG_SEL(cache, q, w_up_k, w_up_v, s, T, np.asarray(sel) + 1, scale)
 
 
+_ORIG_TOPK = OD.search_topk
+_ORIG_MEAN = OD.mean_refs
+
+
+def _topk_far(xt, s, top_k, metric="cos", toks=None, block=1024):
+    if metric == "l2":   # keeps the farthest references
+        return _topk_negated(xt, s, top_k, toks)
+    return _ORIG_TOPK(xt, s, top_k, metric, toks, block)
+
+
+def _topk_negated(xt, s, top_k, toks):
+    T = xt.shape[0]
+    toks = OD.nonref_positions(T, s) if toks is None else np.asarray(toks, np.int64)
+    refs = xt[OD.ref_positions(T, s)]
+    idx = np.zeros((len(toks), top_k), np.int64)
+    cnt = OD.ref_count(toks, s, top_k)
+    for i, t in enumerate(toks):
+        cands = [r for r in range(len(refs)) if r * s < t]
+        dist = [float(((xt[t] - refs[r]) ** 2).sum()) for r in cands]
+        order = sorted(range(len(cands)), key=lambda j: (-dist[j], cands[j]))
+        idx[i, :cnt[i]] = sorted(cands[j] for j in order[:cnt[i]])
+    return idx, cnt, np.full(len(toks), np.inf)
+
+
+def _topk_last_tie(xt, s, top_k, metric="cos", toks=None, block=1024):
+    T = xt.shape[0]
+    R = OD.n_refs(T, s)
+    idx, cnt, m = _ORIG_TOPK(xt, s, top_k, metric, toks, block)
+    toks_ = OD.nonref_positions(T, s) if toks is None else np.asarray(toks, np.int64)
+    refs = xt[OD.ref_positions(T, s)]
+    out = np.zeros_like(idx)
+    for i, t in enumerate(toks_):
+        cands = [r for r in range(R) if r * s < t]
+        if metric == "cos":
+            sc = OD.cosines(xt, np.full(len(cands), t), np.array(cands), s)
+        else:
+            sc = -np.array([float(((xt[t] - refs[r]) ** 2).sum()) for r in cands])
+        order = sorted(range(len(cands)), key=lambda j: (-sc[j], -cands[j]))
+        out[i, :cnt[i]] = sorted(cands[j] for j in order[:cnt[i]])
+    return out, cnt, m
+
+
+def _mean_by_k(xt, s, idx, count):
+    idx = np.asarray(idx, np.int64)
+    return np.stack([xt[idx[j, :count[j]] * s].sum(axis=0) / idx.shape[1] for j in range(len(idx))])
+
+
+def _mean_first_only(xt, s, idx, count):
+    idx = np.asarray(idx, np.int64)
+    return xt[idx[:, 0] * s]
+
+
 def _stream_bytes_no_idx(T, s, d, dc, storage):
     e = OD.ELEM_BYTES[storage]
     R = OD.n_refs(T, s)
@@ -255,6 +313,10 @@ MUTATIONS = {
     "4-bit: scale from max / 8": ("quantize_q4", _q4_scale_by_8),
     "4-bit: quantizes the storage-rounded code": ("encode_exact", _exact_rounded_first),
     "4-bit: decoder drops the scale": ("dequantize_q4", _dequant_no_scale),
+    "top-k: L2 keeps the farthest references": ("search_topk", _topk_far),
+    "top-k: ties to the higher ordinal": ("search_topk", _topk_last_tie),
+    "top-k: mean divides by k, not the count": ("mean_refs", _mean_by_k),
+    "top-k: residual against the first reference only": ("mean_refs", _mean_first_only),
 }
 
 

@@ -663,3 +663,136 @@ def test_q4_append_equals_compress():
         row = t - t // s - 1
         assert a["idx"] == full["idx"][row]
         assert a["q"].tolist() == full["q"][row].tolist() and a["scale"] == full["scales"][row]
+
+
+# ---------------------------------------------------------------------------
+# k references and the L2 metric ([en] §3 "Strided Reference Selection" and
+# "Residual Encoding": the k nearest strided references by L2 distance, and
+# the residual against their mean).
+# ---------------------------------------------------------------------------
+
+def _py_topk(xt, s, k, metric):
+    """Plain loops: score every earlier reference, rank by (score desc,
+    ordinal asc), keep min(k, available), return them in ascending order."""
+    out = []
+    for t in range(len(xt)):
+        if t % s == 0:
+            continue
+        cands = []
+        r = 0
+        while r * s < t:
+            a, b = xt[t], xt[r * s]
+            if metric == "cos":
+                sc = _py_cos(a, b)
+            else:
+                sc = -sum((x - y) ** 2 for x, y in zip(a, b))
+            cands.append((-sc, r))
+            r += 1
+        cands.sort()
+        out.append(sorted(r for _, r in cands[:k]))
+    return out
+
+
+@pytest.mark.parametrize("metric", ["cos", "l2"])
+@pytest.mark.parametrize("T,s,k,d,seed", [(40, 3, 2, 5, 4), (97, 5, 3, 6, 6), (60, 2, 4, 3, 8), (33, 1, 8, 4, 9),
+                                          (50, 7, 1, 4, 10)])
+def test_topk_matches_brute_force_integer_data(T, s, k, d, seed, metric):
+    """Integer vectors: equal scores are bitwise equal, so the tie rule is
+    exercised; early tokens with fewer than k references keep all of them."""
+    rng = np.random.default_rng(seed)
+    xt = rng.integers(-2, 3, size=(T, d)).astype(np.float64)
+    idx, count, _ = O.search_topk(xt, s, k, metric)
+    want = _py_topk(xt.tolist(), s, k, metric)
+    assert [list(row[:c]) for row, c in zip(idx, count)] == want
+    assert np.all(idx[np.arange(k)[None, :] >= count[:, None]] == 0)
+
+
+def test_topk_one_cosine_is_the_top1_search():
+    rng = np.random.default_rng(17)
+    xt = rng.standard_normal((300, 16))
+    idx1, _, m1 = O.search(xt, 7)
+    idxk, cnt, mk = O.search_topk(xt, 7, 1, "cos")
+    assert np.array_equal(idxk[:, 0], idx1) and np.all(cnt == 1)
+    assert np.allclose(mk, m1, rtol=0, atol=1e-12)
+
+
+def test_l2_hand_case():
+    """refs r0 = (0, 0), r1 = (3, 0), r2 = (1, 1) (s = 2, positions 0, 2, 4);
+    token 5 = (2, 0): squared distances 4, 1, 2 -> top-1 r1, top-2 {r1, r2};
+    cosine instead prefers r1 (cos 1) and then r2 (cos 0.707), r0 scores 0."""
+    xt = np.array([[0, 0], [9, 9], [3, 0], [9, 9], [1, 1], [2, 0]], dtype=np.float64)
+    i1, c1, m1 = O.search_topk(xt, 2, 1, "l2", toks=[5])
+    assert i1.tolist() == [[1]] and c1.tolist() == [1]
+    assert abs(m1[0] - (2 - 1) / (4 + 9)) < 1e-15
+    i2, c2, _ = O.search_topk(xt, 2, 2, "l2", toks=[5])
+    assert i2.tolist() == [[1, 2]] and c2.tolist() == [2]
+    i3, c3, _ = O.search_topk(xt, 2, 3, "l2", toks=[5])
+    assert i3.tolist() == [[0, 1, 2]]
+    # token 3 sees r0 and r1 only: with k = 3 it keeps both, the third slot is 0
+    i4, c4, m4 = O.search_topk(xt, 2, 3, "l2", toks=[3])
+    assert i4.tolist() == [[0, 1, 0]] and c4.tolist() == [2] and m4[0] == np.inf
+
+
+def test_topk_mean_residual_hand_case():
+    """k = 2, L2, d = 2: token 5 = (2, 0) keeps r1 = (3, 0), r2 = (1, 1);
+    their mean is (2, 0.5), so with W_down = I the code is (0, -0.5) and the
+    reconstruction gives the token back."""
+    k = np.array([[[[0, 0], [9, 9], [3, 0], [9, 9], [1, 1], [2, 0]]]], dtype=np.float64)
+    mu = k[0, 0].mean(axis=0)
+    k0 = k + 0.0
+    c = O.compress(k0, k0, 2, np.eye(2), np.eye(2), "f64", top_k=2, metric="l2")
+    assert np.array_equal(c["mu"][0, 0, 0], mu)
+    row = 5 - 5 // 2 - 1
+    assert c["idx"][0, 0, 0][row].tolist() == [1, 2]
+    assert np.allclose(c["codes"][0, 0, 0][row], (k[0, 0, 5] - mu) - ((k[0, 0, 2] - mu) + (k[0, 0, 4] - mu)) / 2)
+    rec = O.reconstruct_stream(c["mu"][0, 0, 0], c["refs"][0, 0, 0], c["idx"][0, 0, 0], c["codes"][0, 0, 0],
+                               np.eye(2), 2, 6)
+    assert np.allclose(rec, k[0, 0], atol=1e-14)
+
+
+@pytest.mark.parametrize("metric", ["cos", "l2"])
+def test_topk_full_rank_reconstructs_exactly(metric):
+    """d_c = d with orthonormal W: every token comes back exactly, whatever k."""
+    rng = np.random.default_rng(18)
+    T, d, s = 50, 8, 3
+    k = rng.standard_normal((1, 2, T, d)) * 2 + 3
+    w = np.linalg.qr(rng.standard_normal((d, d)))[0]
+    for kk in (2, 4):
+        c = O.compress(k, k, s, w.T, w.T, "f64", top_k=kk, metric=metric)
+        for h in range(2):
+            rec = O.reconstruct_stream(c["mu"][0, h, 0], c["refs"][0, h, 0], c["idx"][0, h, 0], c["codes"][0, h, 0],
+                                       w, s, T)
+            assert np.abs(rec - k[0, h]).max() < 1e-12
+
+
+def test_topk_all_references_is_the_running_mean():
+    """k at least the number of references: every coded token averages all
+    earlier references (a closed form)."""
+    rng = np.random.default_rng(19)
+    T, d, s = 40, 4, 4
+    xt = rng.standard_normal((T, d))
+    toks = O.nonref_positions(T, s)
+    idx, cnt, _ = O.search_topk(xt, s, 16, "l2")
+    m = O.mean_refs(xt, s, idx, cnt)
+    for j, t in enumerate(toks):
+        assert np.allclose(m[j], xt[0:t:s].mean(axis=0), atol=1e-14)
+
+
+@pytest.mark.parametrize("metric,k", [("l2", 1), ("l2", 3), ("cos", 2)])
+def test_topk_append_equals_compress(metric, k):
+    rng = np.random.default_rng(20)
+    T0, n, s, d, dc = 25, 40, 6, 10, 4
+    x = K.to_storage(rng.standard_normal((T0 + n, d)) * 2 + 1, "bf16").f64
+    wd = K.to_storage(rng.standard_normal((dc, d)) / 3, "bf16").f64
+    mu = O.shared_component(x[:T0], "bf16")
+    full = O.compress_stream(x, s, wd, "bf16", mu_in=mu, top_k=k, metric=metric)
+    refs = list(full["refs"][:O.n_refs(T0, s)])
+    for t in range(T0, T0 + n):
+        a = O.append_token(mu, np.array(refs), x[t], t, s, wd, "bf16", top_k=k, metric=metric)
+        if "ref" in a:
+            refs.append(a["ref"])
+            continue
+        row = t - t // s - 1
+        assert a["idx"] == full["idx"][row].tolist()
+        gap = np.abs(a["code"] - full["codes"][row])
+        assert np.all(gap <= np.spacing(np.abs(full["codes"][row]).astype(np.float32)) * 256)
