@@ -19,6 +19,8 @@
  *   refs[r] = x~_{r*s}            r = 0 .. R-1, R = ceil(T / s)
  *   ref(t)  = argmax over r with r*s < t of cos(x~_t, refs[r]),
  *             lowest r on exact ties, cos = 0 for a zero vector
+ *             (top_k > 1 or metric = L2: the k best by that metric, and
+ *             refs[ref(t)] below stands for their mean)
  *   code_t  = rnd(W_down ((k_t - mu) - refs[ref(t)]))   d_c values
  *   decode: k^_t = mu + refs[ref(t)] + W_up code_t (refs are tokens too:
  *           k^_{r*s} = mu + refs[r]); out_g = softmax_t(q_g . k^_t * scale) V^
@@ -57,7 +59,7 @@
 extern "C" {
 #endif
 
-#define DKV_ABI_VERSION 3u
+#define DKV_ABI_VERSION 4u
 
 typedef enum dkv_status {
   DKV_OK = 0,
@@ -97,6 +99,15 @@ typedef enum dkv_dtype {
  *                rounding) is stored as scale = rnd(max_j |c_j| / 7) and
  *                q_j = clamp(round-half-even(c_j / scale), -8, 7) (q = 0
  *                when scale = 0); the decoder uses scale * q_j
+ *   top_k        references each coded token keeps, 1 .. 8 (0 means 1):
+ *                the k best earlier references, ties to the lower ordinal
+ *                (all earlier ones when fewer than k exist); the residual
+ *                and the reconstruction use their mean (English page,
+ *                Technical Summary §3 "Strided Reference Selection" and
+ *                "Residual Encoding": the k nearest references and their
+ *                mean KV^R)
+ *   metric       DKV_METRIC_COS (0): rank by cosine; DKV_METRIC_L2 (1): by
+ *                smallest ||x~_t - refs[r]|| (the English page's L2 distance)
  * Derived: R = ceil(T / s) references and N = T - R coded tokens per stream
  * are held; the arrays are laid out for R_cap = ceil(T_cap / s) and
  * N_cap = T_cap - R_cap (a cache's layout is fixed by T_cap, so a layout
@@ -114,7 +125,12 @@ typedef struct dkv_layout {
   uint32_t seq_len;
   uint32_t capacity;
   uint32_t code_bits;
+  uint32_t top_k;
+  uint32_t metric;
 } dkv_layout;
+
+#define DKV_METRIC_COS 0u
+#define DKV_METRIC_L2 1u
 
 /*
  * Device pointers of a compressed cache.  All arrays are dense, row-major,
@@ -128,8 +144,11 @@ typedef struct dkv_layout {
  *                                 With code_bits = 4 a row is d_c / 2 bytes:
  *                                 element 2i in the low nibble of byte i,
  *                                 2i + 1 in the high nibble, two's complement
- *   idx    [B][H][2][N_cap]       uint16 or uint32 (idx_bytes): reference
- *                                 ordinal r of each row (the token at r*s)
+ *   idx    [B][H][2][N_cap][k]    uint16 or uint32 (idx_bytes): reference
+ *                                 ordinals r of each row (the token at r*s),
+ *                                 k = top_k, in ascending order; a token with
+ *                                 c < k earlier references fills slots
+ *                                 c .. k-1 with 0
  *   mu     [B][H][2][d]           storage dtype: the shared component
  *   scales [B][H][2][N_cap]       storage dtype, code_bits = 4 only (else
  *                                 ignored, may be NULL): scale of each row

@@ -123,17 +123,19 @@ def idx_bytes_for(R: int) -> int:
     return 2 if R <= 65536 else 4
 
 
-def stream_bytes(T: int, s: int, d: int, dc: int, storage: str, code_bits: int = 16) -> int:
+def stream_bytes(T: int, s: int, d: int, dc: int, storage: str, code_bits: int = 16, top_k: int = 1) -> int:
     """Bytes one compressed stream occupies: references, codes, indices, mean
-    (with 4-bit codes: d_c / 2 bytes and one scale per coded token)."""
+    (with 4-bit codes: d_c / 2 bytes and one scale per coded token; with k
+    references: k ordinals per coded token)."""
     e = ELEM_BYTES[storage]
     R = n_refs(T, s)
     N = T - R
     code = dc // 2 + e if code_bits == 4 else dc * e
-    return R * d * e + N * (code + idx_bytes_for(R)) + d * e
+    return R * d * e + N * (code + top_k * idx_bytes_for(R)) + d * e
 
 
-def cache_array_bytes(B: int, H: int, T: int, s: int, d: int, dc: int, storage: str, code_bits: int = 16) -> dict:
+def cache_array_bytes(B: int, H: int, T: int, s: int, d: int, dc: int, storage: str, code_bits: int = 16,
+                      top_k: int = 1) -> dict:
     """Unpadded size of each cache array over B sequences x H heads x {K, V}."""
     e = ELEM_BYTES[storage]
     R = n_refs(T, s)
@@ -142,7 +144,7 @@ def cache_array_bytes(B: int, H: int, T: int, s: int, d: int, dc: int, storage: 
     out = {
         "refs": n * R * d * e,
         "codes": n * N * (dc // 2 if code_bits == 4 else dc * e),
-        "idx": n * N * idx_bytes_for(R),
+        "idx": n * N * top_k * idx_bytes_for(R),
         "mu": n * d * e,
     }
     if code_bits == 4:
@@ -150,9 +152,10 @@ def cache_array_bytes(B: int, H: int, T: int, s: int, d: int, dc: int, storage: 
     return out
 
 
-def cache_bytes(B, H, T, s, d, dc, storage, align: int = ALIGN, code_bits: int = 16) -> int:
+def cache_bytes(B, H, T, s, d, dc, storage, align: int = ALIGN, code_bits: int = 16, top_k: int = 1) -> int:
     """Total carved cache size: each array padded to ``align`` bytes."""
-    return sum(-(-v // align) * align for v in cache_array_bytes(B, H, T, s, d, dc, storage, code_bits).values())
+    return sum(-(-v // align) * align
+               for v in cache_array_bytes(B, H, T, s, d, dc, storage, code_bits, top_k).values())
 
 
 def dense_kv_bytes(n_layers, n_kv_heads, head_dim, seq_len, batch, elem_bytes=2) -> int:

@@ -17,7 +17,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdeltakv.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 F32, BF16 = 0, 1
 STATUS = {0: "DKV_OK", 1: "DKV_ERR_NULL", 2: "DKV_ERR_SHAPE", 3: "DKV_ERR_DTYPE", 4: "DKV_ERR_ALIGN",
           5: "DKV_ERR_WORKSPACE", 6: "DKV_ERR_UNSUPPORTED", 7: "DKV_ERR_VERSION", 8: "DKV_ERR_DEVICE"}
@@ -36,7 +36,7 @@ class DeltaKVError(RuntimeError):
 class dkv_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint32) for n in ("abi_version", "dtype", "head_dim", "code_dim", "stride",
                                               "idx_bytes", "n_kv_heads", "batch", "seq_len", "capacity",
-                                              "code_bits")]
+                                              "code_bits", "top_k", "metric")]
 
     @property
     def n_refs(self) -> int:
@@ -139,16 +139,21 @@ def _check(status: int, what: str):
 # Layout and cache.
 # ---------------------------------------------------------------------------
 
+METRICS = {"cos": 0, "l2": 1}
+
+
 def make_layout(dtype: str, head_dim: int, code_dim: int, stride: int, n_kv_heads: int, batch: int,
-                seq_len: int, idx_bytes: int | None = None, capacity: int = 0, code_bits: int = 0) -> dkv_layout:
+                seq_len: int, idx_bytes: int | None = None, capacity: int = 0, code_bits: int = 0, top_k: int = 1,
+                metric: str = "cos") -> dkv_layout:
     """capacity: tokens the cache arrays are sized for (0 = seq_len);
-    code_bits: 0 = codes in the storage dtype, 4 = 4-bit codes with scales."""
+    code_bits: 0 = codes in the storage dtype, 4 = 4-bit codes with scales;
+    top_k: references per coded token; metric: "cos" or "l2"."""
     cap = capacity or seq_len
     R = -(-cap // stride) if stride > 0 else 0
     if idx_bytes is None:
         idx_bytes = 2 if R <= 65536 else 4
     return dkv_layout(ABI_VERSION, {"f32": F32, "bf16": BF16}[dtype], head_dim, code_dim, stride, idx_bytes,
-                      n_kv_heads, batch, seq_len, capacity, code_bits)
+                      n_kv_heads, batch, seq_len, capacity, code_bits, top_k, METRICS[metric])
 
 
 def with_seq_len(layout: dkv_layout, seq_len: int) -> dkv_layout:
@@ -156,7 +161,8 @@ def with_seq_len(layout: dkv_layout, seq_len: int) -> dkv_layout:
     capacity, and with it the array layout, stays fixed)."""
     cap = layout.cap_tokens
     return dkv_layout(layout.abi_version, layout.dtype, layout.head_dim, layout.code_dim, layout.stride,
-                      layout.idx_bytes, layout.n_kv_heads, layout.batch, seq_len, cap, layout.code_bits)
+                      layout.idx_bytes, layout.n_kv_heads, layout.batch, seq_len, cap, layout.code_bits,
+                      layout.top_k, layout.metric)
 
 
 def dkv_layout_check(layout: dkv_layout) -> int:
@@ -213,8 +219,9 @@ class Cache:
         dt = storage_torch_dtype(L)
         B, H, R, N, d, dc = L.batch, L.n_kv_heads, L.cap_refs, L.cap_codes, L.head_dim, L.code_dim
         it = torch.int16 if L.idx_bytes == 2 else torch.int32
+        kk = max(L.top_k, 1)
         out = {"refs": self._view(self.c.refs, (B, H, 2, R, d), dt),
-               "idx": self._view(self.c.idx, (B, H, 2, N), it),
+               "idx": self._view(self.c.idx, (B, H, 2, N) if kk == 1 else (B, H, 2, N, kk), it),
                "mu": self._view(self.c.mu, (B, H, 2, d), dt)}
         if L.code_bits == 4:   # packed nibbles (uint8) and one scale per row
             out["codes"] = self._view(self.c.codes, (B, H, 2, N, dc // 2), torch.uint8)

@@ -27,6 +27,8 @@ dkv_status check_layout(const dkv_layout* L, Shape* out) {
   if (L->code_dim > L->head_dim) return DKV_ERR_SHAPE;
   if (L->idx_bytes != 2 && L->idx_bytes != 4) return DKV_ERR_SHAPE;
   if (L->code_bits != 0 && L->code_bits != 4) return DKV_ERR_SHAPE;
+  if (L->metric != DKV_METRIC_COS && L->metric != DKV_METRIC_L2) return DKV_ERR_SHAPE;
+  if (L->top_k > 8) return DKV_ERR_UNSUPPORTED;
   if (L->head_dim != 64 && L->head_dim != 128) return DKV_ERR_UNSUPPORTED;
   if (L->code_dim % 16 != 0) return DKV_ERR_UNSUPPORTED;
   if (cap > (1u << 30) || L->n_kv_heads > 4096 || L->batch > 65535) return DKV_ERR_UNSUPPORTED;
@@ -49,6 +51,8 @@ dkv_status check_layout(const dkv_layout* L, Shape* out) {
     out->idx_bytes = (int)L->idx_bytes;
     out->bf16 = L->dtype == DKV_BF16;
     out->q4 = L->code_bits == 4;
+    out->K = L->top_k ? (int)L->top_k : 1;
+    out->l2 = L->metric == DKV_METRIC_L2;
   }
   return DKV_OK;
 }
@@ -62,7 +66,7 @@ ArrayBytes array_bytes(const Shape& sh) {
   ArrayBytes a;
   a.refs = n * sh.Rc * sh.d * sh.elem();
   a.codes = n * sh.Nc * sh.code_row_bytes();
-  a.idx = n * sh.Nc * sh.idx_bytes;
+  a.idx = n * sh.Nc * sh.K * sh.idx_bytes;
   a.mu = n * sh.d * sh.elem();
   a.scales = sh.q4 ? n * sh.Nc * sh.elem() : 0;
   return a;

@@ -255,6 +255,170 @@ __global__ __launch_bounds__(64) void k_append_finish(AppendArgs a, Shape sh, in
   if (lane == 0) store_idx(a.idx, slot, sh.idx_bytes, (uint32_t)br);
 }
 
+// ---------------------------------------------------------------------------
+// k references or the L2 metric: the search blocks keep the best k of their
+// chunk (per 16-lane group, then merged in the block), and one 256-thread
+// block per stream merges the blocks' lists, averages the kept references
+// and encodes against the mean.
+// ---------------------------------------------------------------------------
+
+template <class S, int D>
+__global__ __launch_bounds__(256) void k_append_search_topk(AppendArgs a, Shape sh, int chunk, int P, float2* part) {
+  constexpr int E = D / 16;
+  const XcdItem xi = xcd_item(sh.n_streams());
+  if (xi.stream < 0) return;
+  const int stream = xi.stream, p = xi.item;
+  const int kv = stream & 1, bh = stream >> 1, b = bh / sh.H, h = bh - b * sh.H;
+  const int t = sh.T - 1;
+  const int nref = t / sh.s + 1;
+  const int r0 = p * chunk, r1 = min(nref, r0 + chunk);
+  const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15;
+  const int K = sh.K;
+  constexpr size_t e = sizeof(typename S::T);
+  const char* refs = (const char*)a.refs + ((size_t)stream * sh.Rc * D + l16 * E) * e;
+  RowSlice<S, E> row[kUnroll];
+  int r = r0 + grp;
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) row[u].load(refs + (size_t)min(r + 16 * u, r1 - 1) * D * e);
+  const char* src = (const char*)(kv ? a.v : a.k) + ((int64_t)b * a.sb + (int64_t)h * a.sh + l16 * E) * e;
+  RowSlice<S, E> ks, ms;
+  ks.load(src);
+  ms.load((const char*)a.mu + ((size_t)stream * D + l16 * E) * e);
+  float x[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) x[i] = S::load(S::sub_rn(ks.at(i), ms.at(i)));
+
+  TopK top;
+  top.init();
+  for (;;) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      float dot = 0.f, n2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const float v = row[u].at(i);
+        dot = fmaf(x[i], v, dot);
+        n2 = fmaf(v, v, n2);
+      }
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) {
+        dot += __shfl_xor(dot, o, 64);
+        n2 += __shfl_xor(n2, o, 64);
+      }
+      const float sc = sh.l2 ? 2.f * dot - n2 : (n2 > 0.f ? dot * (1.0f / sqrtf(n2)) : 0.f);
+      const int ru = r + 16 * u;
+      if (ru < r1) top.insert(sc, ru, K);   // the group's lanes hold the same list
+    }
+    r += 16 * kUnroll;
+    if (r >= r1) break;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) row[u].load(refs + (size_t)min(r + 16 * u, r1 - 1) * D * e);
+  }
+  __shared__ float red_s[16][kTopMax];
+  __shared__ int red_r[16][kTopMax];
+  if (l16 == 0) {
+#pragma unroll
+    for (int j = 0; j < kTopMax; ++j) {
+      red_s[grp][j] = top.s[j];
+      red_r[grp][j] = top.r[j];
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    TopK all;
+    all.init();
+    for (int g = 0; g < 16; ++g)
+      for (int j = 0; j < K; ++j) all.insert(red_s[g][j], red_r[g][j], K);
+    float2* out = part + ((size_t)stream * P + p) * K;
+#pragma unroll
+    for (int j = 0; j < kTopMax; ++j)
+      if (j < K) out[j] = make_float2(all.s[j], __int_as_float(all.r[j]));
+  }
+}
+
+template <class S, int D>
+__global__ __launch_bounds__(256) void k_append_finish_topk(AppendArgs a, Shape sh, int P, const float2* part) {
+  typedef typename S::T T;
+  const int stream = blockIdx.x;
+  const int kv = stream & 1, bh = stream >> 1, b = bh / sh.H, h = bh - b * sh.H;
+  const int t = sh.T - 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int K = sh.K;
+  const T* src = (const T*)(kv ? a.v : a.k) + (int64_t)b * a.sb + (int64_t)h * a.sh;
+  const T* mu = (const T*)a.mu + (size_t)stream * D;
+  T* refs = (T*)a.refs + (size_t)stream * sh.Rc * D;
+  if (t % sh.s == 0) {
+    if (tid < D) refs[(size_t)(t / sh.s) * D + tid] = S::sub_rn(S::load(src[tid]), S::load(mu[tid]));
+    return;
+  }
+  __shared__ int s_ord[kTopMax];
+  __shared__ float diff[D];
+  __shared__ float red[8];
+  const int cnt = min(K, t / sh.s + 1);
+  if (tid < 64) {
+    TopK top;
+    top.init();
+    for (int i = lane; i < P * K; i += 64) {
+      const float2 v = part[(size_t)stream * P * K + i];
+      top.insert(v.x, __float_as_int(v.y), K);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) top.merge_xor(o, K);
+    if (lane == 0) {
+      int o[kTopMax];
+      top.sorted_ordinals(cnt, o);
+#pragma unroll
+      for (int j = 0; j < kTopMax; ++j) s_ord[j] = o[j];
+    }
+  }
+  __syncthreads();
+  if (tid < D) {
+    float m = 0.f;
+    for (int j = 0; j < cnt; ++j) m += S::load(refs[(size_t)min(s_ord[j], sh.R - 1) * D + tid]);
+    m = cnt > 1 ? m * (1.0f / (float)cnt) : m;
+    diff[tid] = (S::load(src[tid]) - S::load(mu[tid])) - m;
+  }
+  __syncthreads();
+  const size_t slot = (size_t)stream * sh.Nc + (size_t)(t - t / sh.s - 1);
+  const T* w = (const T*)(kv ? a.wdv : a.wdk) + (size_t)h * a.w_hs;
+  constexpr int Q = D / 4;
+  const int l4 = tid & 3;
+  // Code element j = j0 + tid / 4 from four lanes' partial dot products.
+  float cv[2] = {0.f, 0.f};   // this lane's elements of the two 64-element passes (d_c <= 128)
+  for (int pass = 0; pass * 64 < sh.dc; ++pass) {
+    const int jj = pass * 64 + (tid >> 2);
+    float c = 0.f;
+    if (jj < sh.dc) {
+      const T* wr = w + (size_t)jj * D + l4 * Q;
+#pragma unroll 8
+      for (int i = 0; i < Q; ++i) c = fmaf(S::load(wr[i]), diff[l4 * Q + i], c);
+    }
+    c += __shfl_xor(c, 1, 64);
+    c += __shfl_xor(c, 2, 64);
+    cv[pass] = c;
+    if (!sh.q4 && jj < sh.dc && l4 == 0) ((T*)a.codes)[slot * sh.dc + jj] = S::from_f32(c);
+  }
+  if (sh.q4) {
+    float am = fmaxf(fabsf(cv[0]), fabsf(cv[1]));
+    am = wave_max(am);
+    if (lane == 0) red[tid >> 6] = am;
+    __syncthreads();
+    const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const T sbits = S::from_f32(amax / 7.0f);
+    const float scale = S::load(sbits);
+    uint8_t* row = (uint8_t*)a.codes + slot * (sh.dc / 2);
+    for (int pass = 0; pass * 64 < sh.dc; ++pass) {
+      const int jj = pass * 64 + (tid >> 2);
+      const int q = q4_quant(cv[pass], scale);
+      const int qn = __shfl_down(q, 4, 64);   // element jj + 1 sits four lanes up
+      if (l4 == 0 && !(jj & 1) && jj < sh.dc)
+        row[jj >> 1] = (uint8_t)(((uint32_t)q & 15u) | (((uint32_t)qn & 15u) << 4));
+    }
+    if (tid == 0) ((T*)a.scales)[slot] = sbits;
+  }
+  if (tid < K) store_idx(a.idx, slot * K + tid, sh.idx_bytes, (uint32_t)s_ord[tid]);
+}
+
 __global__ void k_append_empty() {}
 
 template <class S, int D>
@@ -263,6 +427,17 @@ hipError_t launch_append_sd(const Shape& sh, const AppendArgs& a, void* ws, hipS
                             ev_stop(a.events, 1)};
   const int t = sh.T - 1, ns = sh.n_streams();
   const int P = t % sh.s == 0 ? 0 : append_parts(sh, t / sh.s + 1);
+  if (sh.topk_search()) {
+    float2* part = (float2*)ws;
+    hipError_t err;
+    if (P > 0)
+      err = launch(k_append_search_topk<S, D>, dim3(xcd_grid(ns, P)), 256, st, ev[0], ev[1], a, sh,
+                   append_chunk(sh, t / sh.s + 1), P, part);
+    else
+      err = ev[0] ? launch(k_append_empty, dim3(1), 64, st, ev[0], ev[1]) : hipSuccess;
+    if (err != hipSuccess) return err;
+    return launch(k_append_finish_topk<S, D>, dim3(ns), 256, st, ev[2], ev[3], a, sh, P, (const float2*)part);
+  }
   float2* part = (float2*)ws;
   void* pcode = (char*)ws + pcode_off(ns, std::max(P, 1));
   hipError_t err;
@@ -295,7 +470,9 @@ size_t append_ws_bytes(const Shape& sh) {
   const int target = (kAppendBlocks + ns - 1) / ns;
   const int most = std::max(1, std::min(target, (sh.Rc + kAppendMinChunk - 1) / kAppendMinChunk));
   const size_t code_bytes = sh.q4 ? sizeof(float) : (size_t)sh.elem();   // 4-bit: unrounded candidates
-  return align_up(pcode_off(ns, most) + (size_t)ns * most * sh.dc * code_bytes, 256);
+  const size_t one = align_up(pcode_off(ns, most) + (size_t)ns * most * sh.dc * code_bytes, 256);
+  const size_t lists = align_up((size_t)ns * most * sh.K * sizeof(float2), 256);   // k references / L2
+  return sh.topk_search() ? lists : one;
 }
 
 hipError_t launch_append(const Shape& sh, const AppendArgs& a, void* ws, hipStream_t st) {

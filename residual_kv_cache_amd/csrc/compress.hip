@@ -439,6 +439,181 @@ __global__ __launch_bounds__(256) void k_search_f32(CompressArgs a, Shape sh) {
 // ---------------------------------------------------------------------------
 
 
+// ---------------------------------------------------------------------------
+// Search for k references, or by L2 distance (top_k > 1 or metric = L2).
+// Each candidate (score, ordinal) enters a sorted list of the best k under
+// the total order "higher score, then lower ordinal"; the lists of a token
+// are merged at the end, and the kept ordinals written in ascending order,
+// zero past the token's count min(k, floor(t / s) + 1).
+// Scores: cosine order is dot / ||r|| (0 for a zero reference); L2 order is
+// 2 dot - ||r||^2 (= ||x||^2 - ||x - r||^2, the token's norm being common).
+// ---------------------------------------------------------------------------
+
+// bfloat16: 64 coded rows per block, 16 per wave.  A = 16 reference rows
+// (lane n16 holds row n16, dims 8 q4 ..), B = the wave's 16 tokens, so lane
+// (n16, q4) gets the dots of references 4 q4 + i with token n16; the
+// reference norms come from the A fragments themselves.  The next tile's
+// rows are loaded while the current one is scored.  Insertion runs only
+// when some lane of the wave has a candidate that beats its k-th best.
+template <int D>
+__global__ __launch_bounds__(256) void k_search_topk_mfma(CompressArgs a, Shape sh) {
+  constexpr int KS = D / 32;
+  typedef uint32_t Frag __attribute__((ext_vector_type(4)));
+  const XcdItem xi = xcd_item(sh.n_streams());
+  if (xi.stream < 0) return;
+  const int stream = xi.stream;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n16 = lane & 15, q4 = lane >> 4;
+  const int K = sh.K;
+  const StreamId id = decode_stream(stream, sh.H);
+  const uint16_t* src = stream_src<BF16>(a, id);
+  const uint16_t* mu = (const uint16_t*)a.mu + (size_t)stream * D;
+  const uint16_t* refs = (const uint16_t*)a.refs + (size_t)stream * sh.Rc * D;
+
+  const int nbase = xi.item * 64 + wave * 16;
+  if (nbase >= sh.N) return;
+  const int n = nbase + n16;
+  const bool valid = n < sh.N;
+  const int t = valid ? slot_to_pos(n, sh.s) : 0;
+  const int tmax = slot_to_pos(min(nbase + 15, sh.N - 1), sh.s);
+  const int nref = (tmax - 1) / sh.s + 1;   // references any token of the wave may use
+
+  Frag bt[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int c = ks * 32 + q4 * 8;
+    float x[8], m[8];
+    load8(src + (int64_t)t * a.st + c, x);
+    load8(mu + c, m);
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = valid ? ((uint32_t)f2bf(x[2 * e] - m[2 * e]) | ((uint32_t)f2bf(x[2 * e + 1] - m[2 * e + 1]) << 16)) : 0u;
+    bt[ks] = Frag{w[0], w[1], w[2], w[3]};
+  }
+
+  TopK top;
+  top.init();
+  Frag ar[KS], an[KS];
+  {
+    const int rr = min(n16, nref - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) ar[ks] = *(const Frag*)(refs + (size_t)rr * D + ks * 32 + q4 * 8);
+  }
+  for (int r0 = 0; r0 < nref; r0 += 16) {
+    const int rn = min(r0 + 16 + n16, nref - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) an[ks] = *(const Frag*)(refs + (size_t)rn * D + ks * 32 + q4 * 8);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float n2 = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ar[ks]), __builtin_bit_cast(bf16x8, bt[ks]),
+                                                    acc, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = __uint_as_float(ar[ks][e] << 16), hi = __uint_as_float(ar[ks][e] & 0xFFFF0000u);
+        n2 = fmaf(lo, lo, n2);
+        n2 = fmaf(hi, hi, n2);
+      }
+    }
+    n2 += __shfl_xor(n2, 16, 64);
+    n2 += __shfl_xor(n2, 32, 64);   // every lane of row n16: ||refs[r0 + n16]||^2
+    float sc[4];
+    int rc[4];
+    bool want = false;
+    float ths;
+    int thr;
+    top.kth(K, ths, thr);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float nn = __shfl(n2, 4 * q4 + i, 64);
+      const int r = r0 + 4 * q4 + i;
+      float v;
+      if (sh.l2)
+        v = 2.f * acc[i] - nn;
+      else
+        v = nn > 0.f ? acc[i] / sqrtf(nn) : 0.f;
+      const bool ok = valid && r < nref && r * sh.s < t;
+      sc[i] = ok ? v : -INFINITY;
+      rc[i] = r;
+      want |= ok && ranks_before(v, r, ths, thr);
+    }
+    if (__ballot(want) != 0ull) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (sc[i] != -INFINITY) top.insert(sc[i], rc[i], K);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) ar[ks] = an[ks];
+  }
+  top.merge_xor(16, K);
+  top.merge_xor(32, K);
+  if (valid && q4 == 0) {
+    int o[kTopMax];
+    top.sorted_ordinals(min(K, t / sh.s + 1), o);
+    const size_t base = ((size_t)stream * sh.Nc + n) * K;
+    for (int j = 0; j < K; ++j) store_idx(a.idx, base + j, sh.idx_bytes, (uint32_t)o[j]);
+  }
+}
+
+// float32 storage: one thread per token, references staged through LDS.
+template <int D>
+__global__ __launch_bounds__(256) void k_search_topk_f32(CompressArgs a, Shape sh) {
+  constexpr int CH = 32;
+  __shared__ float lds_ref[CH][D];
+  __shared__ float lds_n2[CH];
+  const int stream = blockIdx.y;
+  const int K = sh.K;
+  const StreamId id = decode_stream(stream, sh.H);
+  const float* src = stream_src<F32>(a, id);
+  const float* mu = (const float*)a.mu + (size_t)stream * D;
+  const float* refs = (const float*)a.refs + (size_t)stream * sh.Rc * D;
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  const bool valid = n < sh.N;
+  const int t = valid ? slot_to_pos(n, sh.s) : 0;
+  const int nlast = min(sh.N - 1, (int)blockIdx.x * 256 + 255);
+  const int nref = (slot_to_pos(nlast, sh.s) - 1) / sh.s + 1;
+  float x[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) x[i] = valid ? src[(int64_t)t * a.st + i] - mu[i] : 0.f;
+  TopK top;
+  top.init();
+  for (int rc = 0; rc < nref; rc += CH) {
+    __syncthreads();
+    for (int p = threadIdx.x; p < CH * D; p += 256) {
+      const int row = p / D, col = p % D;
+      lds_ref[row][col] = rc + row < nref ? refs[(size_t)(rc + row) * D + col] : 0.f;
+    }
+    __syncthreads();
+    if (threadIdx.x < CH) {
+      float q = 0.f;
+      for (int i = 0; i < D; ++i) q = fmaf(lds_ref[threadIdx.x][i], lds_ref[threadIdx.x][i], q);
+      lds_n2[threadIdx.x] = q;
+    }
+    __syncthreads();
+    for (int j = 0; j < CH; ++j) {
+      const int r = rc + j;
+      if (!valid || r >= nref || r * sh.s >= t) break;
+      float dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < D; ++i) dot = fmaf(x[i], lds_ref[j][i], dot);
+      const float nn = lds_n2[j];
+      const float v = sh.l2 ? 2.f * dot - nn : (nn > 0.f ? dot / sqrtf(nn) : 0.f);
+      float ths;
+      int thr;
+      top.kth(K, ths, thr);
+      if (ranks_before(v, r, ths, thr)) top.insert(v, r, K);
+    }
+  }
+  if (valid) {
+    int o[kTopMax];
+    top.sorted_ordinals(min(K, t / sh.s + 1), o);
+    const size_t base = ((size_t)stream * sh.Nc + n) * K;
+    for (int j = 0; j < K; ++j) store_idx(a.idx, base + j, sh.idx_bytes, (uint32_t)o[j]);
+  }
+}
+
 template <int D, bool Q4>
 __global__ __launch_bounds__(256) void k_encode_mfma(CompressArgs a, Shape sh) {
   constexpr int KS = D / 32;
@@ -459,7 +634,12 @@ __global__ __launch_bounds__(256) void k_encode_mfma(CompressArgs a, Shape sh) {
   const int n = xi.item * 64 + wave * 16 + lrow;   // this lane's coded row
   const bool valid = n < sh.N;
   const int t = valid ? slot_to_pos(n, sh.s) : 0;
-  const int r = valid ? min((int)load_idx(a.idx, (size_t)stream * sh.Nc + n, sh.idx_bytes), sh.R - 1) : 0;
+  // The row's references: one ordinal, or (top_k > 1) the first
+  // c = min(k, floor(t / s) + 1) of its k, whose mean is the reference.
+  const int K = sh.K;
+  const int cnt = valid ? min(K, t / sh.s + 1) : 1;
+  const size_t ibase = ((size_t)stream * sh.Nc + (valid ? n : 0)) * K;
+  const int r = valid ? min((int)load_idx(a.idx, ibase, sh.idx_bytes), sh.R - 1) : 0;
 
   for (int p = threadIdx.x; p < sh.dc * (D / 8); p += 256) {
     const int row = p / (D / 8), col = (p % (D / 8)) * 8;
@@ -476,6 +656,17 @@ __global__ __launch_bounds__(256) void k_encode_mfma(CompressArgs a, Shape sh) {
       load8(src + (int64_t)t * a.st + c, x);
       load8(mu + c, m);
       load8(refs + (size_t)r * D + c, rf);
+      if (K > 1) {
+        for (int j = 1; j < cnt; ++j) {
+          float rj[8];
+          load8(refs + (size_t)min((int)load_idx(a.idx, ibase + j, sh.idx_bytes), sh.R - 1) * D + c, rj);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) rf[e] += rj[e];
+        }
+        const float inv = 1.0f / (float)cnt;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rf[e] = cnt > 1 ? rf[e] * inv : rf[e];
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float d0 = (x[2 * e] - m[2 * e]) - rf[2 * e];
@@ -557,10 +748,20 @@ __global__ __launch_bounds__(256) void k_encode_f32(CompressArgs a, Shape sh) {
   const float* mu = (const float*)a.mu + (size_t)stream * D;
   const float* refs = (const float*)a.refs + (size_t)stream * sh.Rc * D;
   const int t = slot_to_pos(n, sh.s);
-  const int r = min((int)load_idx(a.idx, (size_t)stream * sh.Nc + n, sh.idx_bytes), sh.R - 1);
+  const int K = sh.K;
+  const int cnt = min(K, t / sh.s + 1);
+  const size_t ibase = ((size_t)stream * sh.Nc + n) * K;
   float dl[D];
 #pragma unroll
-  for (int i = 0; i < D; ++i) dl[i] = (src[(int64_t)t * a.st + i] - mu[i]) - refs[(size_t)r * D + i];
+  for (int i = 0; i < D; ++i) dl[i] = 0.f;
+  for (int j = 0; j < cnt; ++j) {   // sum of the row's references (one when top_k = 1)
+    const int r = min((int)load_idx(a.idx, ibase + j, sh.idx_bytes), sh.R - 1);
+#pragma unroll
+    for (int i = 0; i < D; ++i) dl[i] += refs[(size_t)r * D + i];
+  }
+  const float inv = 1.0f / (float)cnt;
+#pragma unroll
+  for (int i = 0; i < D; ++i) dl[i] = (src[(int64_t)t * a.st + i] - mu[i]) - (cnt > 1 ? dl[i] * inv : dl[i]);
   if (!sh.q4) {
     float* codes = (float*)a.codes + ((size_t)stream * sh.Nc + n) * sh.dc;
     for (int j = 0; j < sh.dc; ++j) {
@@ -612,7 +813,12 @@ hipError_t launch_compress_d(const Shape& sh, const CompressArgs& a, hipStream_t
     DKV_TRY(launch(k_mean_final<BF16>, ns, 256, st, nullptr, ev_stop(ev, 0), a, sh, chunks));
     DKV_TRY(launch(k_center_refs<BF16>, g_ref, 256, st, ev_start(ev, 1), ev_stop(ev, 1), a, sh));
     if (sh.N > 0) {
-      DKV_TRY(launch(k_search_mfma<D>, g_search, kSearchThreads, st, ev_start(ev, 2), ev_stop(ev, 2), a, sh));
+      if (sh.topk_search()) {
+        DKV_TRY(launch(k_search_topk_mfma<D>, dim3(xcd_grid(ns, (sh.N + 63) / 64)), 256, st, ev_start(ev, 2),
+                       ev_stop(ev, 2), a, sh));
+      } else {
+        DKV_TRY(launch(k_search_mfma<D>, g_search, kSearchThreads, st, ev_start(ev, 2), ev_stop(ev, 2), a, sh));
+      }
       if (sh.q4) {
         DKV_TRY(launch_lds(k_encode_mfma<D, true>, g_enc, 256, (size_t)sh.dc * (D + 8) * 2, st, ev_start(ev, 3),
                            ev_stop(ev, 3), a, sh));
@@ -626,7 +832,12 @@ hipError_t launch_compress_d(const Shape& sh, const CompressArgs& a, hipStream_t
     DKV_TRY(launch(k_mean_final<F32>, ns, 256, st, nullptr, ev_stop(ev, 0), a, sh, chunks));
     DKV_TRY(launch(k_center_refs<F32>, g_ref, 256, st, ev_start(ev, 1), ev_stop(ev, 1), a, sh));
     if (sh.N > 0) {
-      DKV_TRY(launch(k_search_f32<D>, g_search32, 256, st, ev_start(ev, 2), ev_stop(ev, 2), a, sh));
+      if (sh.topk_search()) {
+        DKV_TRY(launch(k_search_topk_f32<D>, dim3((sh.N + 255) / 256, ns), 256, st, ev_start(ev, 2), ev_stop(ev, 2),
+                       a, sh));
+      } else {
+        DKV_TRY(launch(k_search_f32<D>, g_search32, 256, st, ev_start(ev, 2), ev_stop(ev, 2), a, sh));
+      }
       DKV_TRY(launch(k_encode_f32<D>, g_enc32, 256, st, ev_start(ev, 3), ev_stop(ev, 3), a, sh));
     }
   }

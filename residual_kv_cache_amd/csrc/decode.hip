@@ -90,8 +90,11 @@ __global__ __launch_bounds__(256) void k_refscore(DecodeArgs a, Shape sh) {
 // tokens; lanes own head-dim columns (acc_r) and code columns (acc_c).
 // ---------------------------------------------------------------------------
 
-template <class S, int D, int GP, bool Q4>
+// MK: several references per coded token (top_k > 1): the key score takes
+// the mean of their S rows and the value side the mean of their rows.
+template <class S, int D, int GP, bool Q4, bool MK>
 __global__ __launch_bounds__(256) void k_split_valu(DecodeArgs a, Shape sh) {
+  constexpr int KM = MK ? 8 : 1;         // ordinals held per lane
   constexpr int RPL = D / 64;            // head-dim columns per lane
   __shared__ float qp_l[GP][D];
   __shared__ float mw[4][GP];
@@ -135,18 +138,46 @@ __global__ __launch_bounds__(256) void k_split_valu(DecodeArgs a, Shape sh) {
     const int u = base + lane;
     const bool valid = lane < cnt;
     int rk = 0, rv = 0;
+    int rvs[KM];   // MK: the token's value ordinals
+    int nref = 1;  // references the token averages
     float sc[GP];
     if (valid) {
-      if (coded) {
+      if (coded && !MK) {
         // Ordinals come from caller memory: clamp so a corrupt cache can never
         // address outside the reference arrays.
         rk = min((int)load_idx(a.idx, sK * sh.Nc + u, sh.idx_bytes), sh.R - 1);
         rv = min((int)load_idx(a.idx, sV * sh.Nc + u, sh.idx_bytes), sh.R - 1);
-      } else {
+      } else if (!coded) {
         rk = rv = u;
       }
+      if constexpr (MK) {
+        rvs[0] = rv;
 #pragma unroll
-      for (int g = 0; g < GP; ++g) sc[g] = g < G ? score[(size_t)rk * Gs + g] : -INFINITY;
+        for (int j = 1; j < KM; ++j) rvs[j] = 0;
+      }
+      if (coded && MK) {
+        const int t = slot_to_pos(u, sh.s);
+        nref = min(sh.K, t / sh.s + 1);
+        const size_t ib = (sK * sh.Nc + u) * sh.K, jb = (sV * sh.Nc + u) * sh.K;
+        float ssum[GP];
+#pragma unroll
+        for (int g = 0; g < GP; ++g) ssum[g] = 0.f;
+#pragma unroll
+        for (int j = 0; j < KM; ++j) {
+          if (j < nref) {
+            const int kj = min((int)load_idx(a.idx, ib + j, sh.idx_bytes), sh.R - 1);
+            rvs[j] = min((int)load_idx(a.idx, jb + j, sh.idx_bytes), sh.R - 1);
+#pragma unroll
+            for (int g = 0; g < GP; ++g) ssum[g] += g < G ? score[(size_t)kj * Gs + g] : 0.f;
+          }
+        }
+        const float inv = 1.0f / (float)nref;
+#pragma unroll
+        for (int g = 0; g < GP; ++g) sc[g] = g < G ? ssum[g] * inv : -INFINITY;
+      } else {
+#pragma unroll
+        for (int g = 0; g < GP; ++g) sc[g] = g < G ? score[(size_t)rk * Gs + g] : -INFINITY;
+      }
       if (coded) {
         if constexpr (Q4) {
           const uint32_t* row = (const uint32_t*)(qK + (size_t)u * (dc / 2));
@@ -192,10 +223,28 @@ __global__ __launch_bounds__(256) void k_split_valu(DecodeArgs a, Shape sh) {
       accc[g][1] *= alpha;
     }
     for (int k = 0; k < cnt; ++k) {
-      const int r = __builtin_amdgcn_readlane(rv, k);
       float xr[RPL];
+      if constexpr (MK) {
+        // the mean of the token's value references
+        const int nk = __builtin_amdgcn_readlane(nref, k);
 #pragma unroll
-      for (int e = 0; e < RPL; ++e) xr[e] = S::load(refsV[(size_t)r * D + lane * RPL + e]);
+        for (int e = 0; e < RPL; ++e) xr[e] = 0.f;
+#pragma unroll
+        for (int j = 0; j < KM; ++j) {
+          if (j < nk) {
+            const int r = __builtin_amdgcn_readlane(rvs[j], k);
+#pragma unroll
+            for (int e = 0; e < RPL; ++e) xr[e] += S::load(refsV[(size_t)r * D + lane * RPL + e]);
+          }
+        }
+        const float inv = 1.0f / (float)nk;
+#pragma unroll
+        for (int e = 0; e < RPL; ++e) xr[e] = nk > 1 ? xr[e] * inv : xr[e];
+      } else {
+        const int r = __builtin_amdgcn_readlane(rv, k);
+#pragma unroll
+        for (int e = 0; e < RPL; ++e) xr[e] = S::load(refsV[(size_t)r * D + lane * RPL + e]);
+      }
       float c0 = 0.f, c1 = 0.f;
       if (coded) {
         if constexpr (Q4) {
@@ -299,10 +348,11 @@ __device__ __forceinline__ void load_cols(const typename S::T* p, float (&v)[N])
   }
 }
 
-template <class S, int D, int GP, typename IdxT, bool Q4>
+template <class S, int D, int GP, typename IdxT, bool Q4, bool MK>
 __global__ __launch_bounds__(256) void k_split_sel(DecodeArgs a, Shape sh) {
   constexpr int RPL = D / 64;            // head-dim columns per lane
-  constexpr int UN = 16;                 // entries per accumulate step
+  constexpr int UN = MK ? 8 : 16;        // entries per accumulate step
+  constexpr int KM = MK ? 8 : 1;         // ordinals held per lane (MK: top_k > 1)
   typedef typename S::T T;
   __shared__ float qp_l[GP][128];
   __shared__ float mw[4][GP];
@@ -332,8 +382,8 @@ __global__ __launch_bounds__(256) void k_split_sel(DecodeArgs a, Shape sh) {
   const int cstride = has_codes ? dc : 0;
   const T* codesK = has_codes ? (const T*)a.codes + sK * sh.Nc * dc : (const T*)kZeroRow;
   const T* codesV = has_codes ? (const T*)a.codes + sV * sh.Nc * dc : (const T*)kZeroRow;
-  const IdxT* idxK = has_codes ? (const IdxT*)a.idx + sK * sh.Nc : (const IdxT*)kZeroRow;
-  const IdxT* idxV = has_codes ? (const IdxT*)a.idx + sV * sh.Nc : (const IdxT*)kZeroRow;
+  const IdxT* idxK = has_codes ? (const IdxT*)a.idx + sK * sh.Nc * sh.K : (const IdxT*)kZeroRow;
+  const IdxT* idxV = has_codes ? (const IdxT*)a.idx + sV * sh.Nc * sh.K : (const IdxT*)kZeroRow;
   // 4-bit codes: rows of d_c / 2 bytes (stride 0 on the zero row) and scales.
   const int qstride = has_codes ? dc / 2 : 0;
   const uint8_t* qK = has_codes ? (const uint8_t*)a.codes + sK * sh.Nc * (dc / 2) : (const uint8_t*)kZeroRow;
@@ -364,7 +414,15 @@ __global__ __launch_bounds__(256) void k_split_sel(DecodeArgs a, Shape sh) {
     const int u = coded ? tt - r - 1 : 0;     // coded row (0 when unused)
     // Ordinals come from caller memory: clamp so a corrupt cache can never
     // address outside the reference arrays.
-    const int ik = min((int)idxK[u], sh.R - 1), iv = min((int)idxV[u], sh.R - 1);
+    const int KK = MK ? sh.K : 1;
+    const int nref = coded && MK ? min(sh.K, tt / sh.s + 1) : 1;
+    int iks[KM], ivs[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      iks[j] = min((int)idxK[(size_t)u * KK + (j < nref ? j : 0)], sh.R - 1);
+      ivs[j] = min((int)idxV[(size_t)u * KK + (j < nref ? j : 0)], sh.R - 1);
+    }
+    const int ik = iks[0], iv = ivs[0];
     float cd[GP];
 #pragma unroll
     for (int g = 0; g < GP; ++g) cd[g] = 0.f;
@@ -404,6 +462,20 @@ __global__ __launch_bounds__(256) void k_split_sel(DecodeArgs a, Shape sh) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q)
       srow[q] = *(const __attribute__((address_space(1))) f32x4*)(score + (size_t)rk * Gs + min(4 * q, Gs - 4));
+    if constexpr (MK) {   // the mean of the entry's S rows
+#pragma unroll
+      for (int j = 1; j < KM; ++j) {
+        if (j < nref) {
+#pragma unroll
+          for (int q = 0; q < NQ; ++q)
+            srow[q] += *(const __attribute__((address_space(1))) f32x4*)(score + (size_t)iks[j] * Gs +
+                                                                         min(4 * q, Gs - 4));
+        }
+      }
+      const float inv = 1.0f / (float)nref;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) srow[q] = nref > 1 ? srow[q] * inv : srow[q];
+    }
     float sc[GP];
 #pragma unroll
     for (int g = 0; g < GP; ++g)
@@ -435,6 +507,21 @@ __global__ __launch_bounds__(256) void k_split_sel(DecodeArgs a, Shape sh) {
         const int rr = __builtin_amdgcn_readlane(rv, k);
         const int uu = max(__builtin_amdgcn_readlane(ucol, k), 0);
         load_cols<S, RPL>(refsV + (size_t)rr * D + lane * RPL, xr[i]);
+        if constexpr (MK) {   // the mean of the entry's value references
+          const int nk = __builtin_amdgcn_readlane(nref, k);
+#pragma unroll
+          for (int j = 1; j < KM; ++j) {
+            if (j < nk) {
+              float xj[RPL];
+              load_cols<S, RPL>(refsV + (size_t)__builtin_amdgcn_readlane(ivs[j], k) * D + lane * RPL, xj);
+#pragma unroll
+              for (int e = 0; e < RPL; ++e) xr[i][e] += xj[e];
+            }
+          }
+          const float inv = 1.0f / (float)nk;
+#pragma unroll
+          for (int e = 0; e < RPL; ++e) xr[i][e] = nk > 1 ? xr[i][e] * inv : xr[i][e];
+        }
         if constexpr (Q4) {
           const uint8_t* row = qV + (size_t)uu * qstride;
           const float scl = S::load(sclV[uu]);
@@ -574,9 +661,12 @@ __global__ __launch_bounds__(128) void k_combine(DecodeArgs a, Shape sh) {
 template <class S, int D, int GP>
 hipError_t launch_split(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.splits, sh.B * sh.H);
-  return sh.q4 ? launch(k_split_valu<S, D, GP, true>, grid, 256, st, ev_start(a.events, 1), ev_stop(a.events, 1), a, sh)
-               : launch(k_split_valu<S, D, GP, false>, grid, 256, st, ev_start(a.events, 1), ev_stop(a.events, 1), a,
-                        sh);
+  const hipEvent_t e0 = ev_start(a.events, 1), e1 = ev_stop(a.events, 1);
+  if (sh.K > 1)
+    return sh.q4 ? launch(k_split_valu<S, D, GP, true, true>, grid, 256, st, e0, e1, a, sh)
+                 : launch(k_split_valu<S, D, GP, false, true>, grid, 256, st, e0, e1, a, sh);
+  return sh.q4 ? launch(k_split_valu<S, D, GP, true, false>, grid, 256, st, e0, e1, a, sh)
+               : launch(k_split_valu<S, D, GP, false, false>, grid, 256, st, e0, e1, a, sh);
 }
 
 template <class S, int D>
@@ -596,20 +686,24 @@ hipError_t launch_decode_sd(const Shape& sh, const DecodeArgs& a, hipStream_t st
   return launch(k_combine<S, D>, dim3(sh.B * a.Hq), 128, st, ev_start(a.events, 2), ev_stop(a.events, 2), a, sh);
 }
 
-template <class S, int D, typename IdxT, bool Q4>
+template <class S, int D, typename IdxT, bool Q4, bool MK>
 hipError_t launch_split_sel_q(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.splits, sh.B * sh.H);
   const hipEvent_t e0 = ev_start(a.events, 1), e1 = ev_stop(a.events, 1);
-  if (a.G <= 1) return launch(k_split_sel<S, D, 1, IdxT, Q4>, grid, 256, st, e0, e1, a, sh);
-  if (a.G <= 2) return launch(k_split_sel<S, D, 2, IdxT, Q4>, grid, 256, st, e0, e1, a, sh);
-  if (a.G <= 4) return launch(k_split_sel<S, D, 4, IdxT, Q4>, grid, 256, st, e0, e1, a, sh);
-  if (a.G <= 8) return launch(k_split_sel<S, D, 8, IdxT, Q4>, grid, 256, st, e0, e1, a, sh);
-  return launch(k_split_sel<S, D, 16, IdxT, Q4>, grid, 256, st, e0, e1, a, sh);
+  if (a.G <= 1) return launch(k_split_sel<S, D, 1, IdxT, Q4, MK>, grid, 256, st, e0, e1, a, sh);
+  if (a.G <= 2) return launch(k_split_sel<S, D, 2, IdxT, Q4, MK>, grid, 256, st, e0, e1, a, sh);
+  if (a.G <= 4) return launch(k_split_sel<S, D, 4, IdxT, Q4, MK>, grid, 256, st, e0, e1, a, sh);
+  if (a.G <= 8) return launch(k_split_sel<S, D, 8, IdxT, Q4, MK>, grid, 256, st, e0, e1, a, sh);
+  return launch(k_split_sel<S, D, 16, IdxT, Q4, MK>, grid, 256, st, e0, e1, a, sh);
 }
 
 template <class S, int D, typename IdxT>
 hipError_t launch_split_sel(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
-  return sh.q4 ? launch_split_sel_q<S, D, IdxT, true>(sh, a, st) : launch_split_sel_q<S, D, IdxT, false>(sh, a, st);
+  if (sh.K > 1)
+    return sh.q4 ? launch_split_sel_q<S, D, IdxT, true, true>(sh, a, st)
+                 : launch_split_sel_q<S, D, IdxT, false, true>(sh, a, st);
+  return sh.q4 ? launch_split_sel_q<S, D, IdxT, true, false>(sh, a, st)
+               : launch_split_sel_q<S, D, IdxT, false, false>(sh, a, st);
 }
 
 template <class S, int D>

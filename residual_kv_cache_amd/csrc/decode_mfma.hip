@@ -632,7 +632,7 @@ bool mfma_side_kernels_supported(const Shape& sh, int G, int splits) {
 }
 
 bool decode_fused_supported(const Shape& sh, int G, int splits) {
-  return !sh.q4 && mfma_side_kernels_supported(sh, G, splits);
+  return !sh.q4 && sh.K == 1 && mfma_side_kernels_supported(sh, G, splits);
 }
 
 // The split kernel holds one 512-thread block per CU: about 256 blocks over

@@ -113,6 +113,84 @@ __device__ __forceinline__ int q4_quant(float c, float scale) {
 }
 
 // ---------------------------------------------------------------------------
+// Sorted lists of the best k candidates (score, ordinal) under the total
+// order "higher score, then lower ordinal".
+// ---------------------------------------------------------------------------
+
+constexpr int kTopMax = 8;
+
+__device__ __forceinline__ bool ranks_before(float s1, int r1, float s2, int r2) {
+  return s1 > s2 || (s1 == s2 && r1 < r2);
+}
+
+struct TopK {
+  float s[kTopMax];
+  int r[kTopMax];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int j = 0; j < kTopMax; ++j) {
+      s[j] = -INFINITY;
+      r[j] = 0x7FFFFFFF;
+    }
+  }
+  // Insertion by compare-and-swap down the list (branch-free).
+  __device__ __forceinline__ void insert(float cs, int cr, int K) {
+#pragma unroll
+    for (int j = 0; j < kTopMax; ++j) {
+      if (j < K) {
+        const bool take = ranks_before(cs, cr, s[j], r[j]);
+        const float ts = s[j];
+        const int tr = r[j];
+        s[j] = take ? cs : s[j];
+        r[j] = take ? cr : r[j];
+        cs = take ? ts : cs;
+        cr = take ? tr : cr;
+      }
+    }
+  }
+  // The k-th entry (selects over the fixed-size arrays: no dynamic
+  // register indexing).
+  __device__ __forceinline__ void kth(int K, float& ks, int& kr) const {
+    ks = s[0];
+    kr = r[0];
+#pragma unroll
+    for (int j = 1; j < kTopMax; ++j) {
+      ks = j == K - 1 ? s[j] : ks;
+      kr = j == K - 1 ? r[j] : kr;
+    }
+  }
+  // Merge with the list of lane (lane ^ mask).
+  __device__ __forceinline__ void merge_xor(int mask, int K) {
+    float os[kTopMax];
+    int orr[kTopMax];
+#pragma unroll
+    for (int j = 0; j < kTopMax; ++j) {
+      os[j] = __shfl_xor(s[j], mask, 64);
+      orr[j] = __shfl_xor(r[j], mask, 64);
+    }
+#pragma unroll
+    for (int j = 0; j < kTopMax; ++j)
+      if (j < K) insert(os[j], orr[j], K);
+  }
+  // The first c ordinals in ascending order (c <= K), zero after.
+  __device__ __forceinline__ void sorted_ordinals(int c, int* out) const {
+    int v[kTopMax];
+#pragma unroll
+    for (int j = 0; j < kTopMax; ++j) v[j] = j < c ? r[j] : 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < kTopMax; ++i)
+#pragma unroll
+      for (int j = 0; j + 1 < kTopMax - i; ++j) {
+        const int lo = min(v[j], v[j + 1]), hi = max(v[j], v[j + 1]);
+        v[j] = lo;
+        v[j + 1] = hi;
+      }
+#pragma unroll
+    for (int j = 0; j < kTopMax; ++j) out[j] = j < c ? v[j] : 0;
+  }
+};
+
+// ---------------------------------------------------------------------------
 // Wave64 reductions (butterfly; every lane ends with the result).
 // ---------------------------------------------------------------------------
 

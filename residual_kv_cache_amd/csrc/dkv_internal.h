@@ -25,6 +25,10 @@ struct Shape {
   int idx_bytes;
   int bf16;     // 1 = bfloat16 storage, 0 = float32
   int q4;       // 1 = 4-bit codes with one scale per row
+  int K;        // references per coded token (top_k)
+  int l2;       // 1 = references ranked by L2 distance, 0 = by cosine
+  // The fast paths (top-1 cosine search; token-tile decode) serve K = 1.
+  __host__ __device__ bool topk_search() const { return K > 1 || l2; }
   __host__ __device__ int n_streams() const { return B * H * 2; }
   int elem() const { return bf16 ? 2 : 4; }
   // Bytes of one code row.

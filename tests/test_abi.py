@@ -32,7 +32,7 @@ def test_header_declarations_are_exported():
 
 def test_abi_version_and_status_strings():
     lib = _lib()
-    assert lib.dkv_abi_version() == D.ABI_VERSION == 3
+    assert lib.dkv_abi_version() == D.ABI_VERSION == 4
     for code, name in D.STATUS.items():
         assert lib.dkv_status_str(code).decode().startswith(name)
 
@@ -126,6 +126,26 @@ def test_q4_carve_and_code_bits_check():
     assert D.dkv_cache_carve(L(), base).scales is None
     for bits in (1, 8, 16, 5):
         assert D.dkv_layout_check(L(code_bits=bits)) == 2
+
+
+@pytest.mark.parametrize("k,metric", [(1, "l2"), (2, "cos"), (3, "l2"), (8, "cos")])
+def test_topk_cache_bytes(k, metric):
+    _lib()
+    lay = L(seq_len=1000, stride=7, top_k=k, metric=metric)
+    assert D.dkv_layout_check(lay) == 0
+    assert D.dkv_cache_bytes(lay) == O.cache_bytes(1, 8, 1000, 7, 128, 32, "bf16", top_k=k)
+    lay4 = L(seq_len=1000, stride=7, top_k=k, metric=metric, code_bits=4)
+    assert D.dkv_cache_bytes(lay4) == O.cache_bytes(1, 8, 1000, 7, 128, 32, "bf16", code_bits=4, top_k=k)
+
+
+def test_topk_layout_checks():
+    _lib()
+    assert D.dkv_layout_check(L(top_k=9)) == 6
+    lay = L()
+    lay.top_k = 0            # 0 means one reference
+    assert D.dkv_layout_check(lay) == 0 and D.dkv_cache_bytes(lay) == D.dkv_cache_bytes(L())
+    lay.metric = 2
+    assert D.dkv_layout_check(lay) == 2
 
 
 def test_idx_width_switch():
