@@ -25,9 +25,9 @@ baseline.
 Further operations are reported beside it (not part of `value`), each with
 stage events per kernel: selective decode (each step attends over a quarter
 of the tokens, in random 64-token blocks, over the cache replicas in turn,
-whole steps timed by graph replay), the layer with 4-bit codes (compress,
-and decode steps by graph replay over its own replicas), and decode-time
-append (32 tokens appended one at a time to a cache sized for them, each
+whole steps timed by graph replay), the layer with 4-bit codes and the layer
+with 4 references per token by L2 distance (compress, and decode steps by
+graph replay over their own replicas), and decode-time append (32 tokens appended one at a time to a cache sized for them, each
 after a copy that evicts the references from the Infinity Cache).
 """
 from __future__ import annotations
@@ -53,6 +53,8 @@ SEL_BLOCK = 64
 SEL_SEED = 77
 SEL_REPLAYS = 5
 Q4_STEPS = 64
+VARIANT_STEPS = 64
+TOPK_K = 4
 MALL_BYTES = 256 << 20
 
 
@@ -148,17 +150,17 @@ class Hip:
         self.ok(self.h.hipStreamSynchronize(ctypes.c_void_p(stream)), "hipStreamSynchronize")
 
 
-def effective_decode_bytes(cfg, code_bits: int = 0) -> int:
+def effective_decode_bytes(cfg, code_bits: int = 0, top_k: int = 1) -> int:
     """Bytes one decode step must move once: references, codes (with 4-bit
-    codes: d_c / 2 bytes and a scale per row) and ordinals of K and V, V's
-    mean, W_up of K and V, the queries and the fp32 outputs."""
+    codes: d_c / 2 bytes and a scale per row) and ordinals (k per row) of K
+    and V, V's mean, W_up of K and V, the queries and the fp32 outputs."""
     e = 2 if cfg.dtype == "bf16" else 4
     R = -(-cfg.seq_len // cfg.stride)
     N = cfg.seq_len - R
     ib = 2 if R <= 65536 else 4
     n = cfg.batch * cfg.n_kv_heads * 2
     row = cfg.code_dim // 2 + e if code_bits == 4 else cfg.code_dim * e
-    cache = n * (R * cfg.head_dim * e + N * (row + ib))
+    cache = n * (R * cfg.head_dim * e + N * (row + top_k * ib))
     mu_v = cfg.batch * cfg.n_kv_heads * cfg.head_dim * e
     w = 2 * cfg.head_dim * cfg.code_dim * e
     q_out = cfg.batch * cfg.n_q_heads * cfg.head_dim * (e + 4)
@@ -469,49 +471,66 @@ def main():
             rv = np.unique(np.concatenate([idx_np[b, h, 1][slots], (t // cfg.stride)[~coded]]))
             sel_bytes += n_sel * 4 + len(slots) * 2 * (cfg.code_dim * elem + lay.idx_bytes) + len(rv) * cfg.head_dim * elem
 
-    # 4-bit codes: the same layer compressed with code_bits = 4 into enough
-    # replicas to exceed the Infinity Cache, decode steps replayed from a
-    # graph, stage events for the kernels.
-    lay4 = D.make_layout(cfg.dtype, cfg.head_dim, cfg.code_dim, cfg.stride, cfg.n_kv_heads, cfg.batch, cfg.seq_len,
-                         code_bits=4)
-    cache4_bytes = D.dkv_cache_bytes(lay4)
-    nrep4 = max(1, math.ceil(2 * MALL_BYTES / cache4_bytes))
-    caches4 = [D.Cache(lay4) for _ in range(nrep4)]
-    ws_c4 = D.workspace(D.dkv_compress_workspace_bytes(lay4))
-    ev_c4 = hip.events(8)
-    for c4 in caches4:
-        D.deltakv_compress(lay4, k_d, v_d, wdk_d, wdv_d, c4, ws_c4, stream=s_h, stage_events=ev_c4)
-    hip.sync(s_h)
-    q4_compress_ms = sum(hip.elapsed_ms(ev_c4[2 * j], ev_c4[2 * j + 1]) for j in range(4))
-    splits4 = D.dkv_decode_auto_splits(lay4, cfg.n_q_heads)
-    ws_d4 = D.workspace(D.dkv_decode_workspace_bytes(lay4, cfg.n_q_heads))
-    ev_4 = [hip.events(6) for _ in range(Q4_STEPS)]
-    q4_stage = []
-    for rep in range(2):
-        for i in range(Q4_STEPS):
-            D.deltakv_decode_attn(lay4, caches4[i % nrep4], q_d[i % nsteps], wuk_d, wuv_d, outs[i % nsteps], ws_d4,
-                                  stream=s_h, stage_events=ev_4[i])
+    def variant(**kw):
+        """The same layer under another layout (4-bit codes, k references,
+        L2): compress into enough replicas to exceed the Infinity Cache,
+        decode steps replayed from a graph, stage events for the kernels."""
+        layv = D.make_layout(cfg.dtype, cfg.head_dim, cfg.code_dim, cfg.stride, cfg.n_kv_heads, cfg.batch,
+                             cfg.seq_len, **kw)
+        nbytes = D.dkv_cache_bytes(layv)
+        nrepv = max(1, math.ceil(2 * MALL_BYTES / nbytes))
+        cv = [D.Cache(layv) for _ in range(nrepv)]
+        ws_cv = D.workspace(D.dkv_compress_workspace_bytes(layv))
+        ev_cv = hip.events(8)
+        comp = []
+        for c in cv:
+            D.deltakv_compress(layv, k_d, v_d, wdk_d, wdv_d, c, ws_cv, stream=s_h, stage_events=ev_cv)
+            hip.sync(s_h)
+            comp.append([hip.elapsed_ms(ev_cv[2 * j], ev_cv[2 * j + 1]) for j in range(4)])
+        comp = np.mean(np.array(comp), axis=0)
+        ws_dv = D.workspace(D.dkv_decode_workspace_bytes(layv, cfg.n_q_heads))
+        ev_v = [hip.events(6) for _ in range(VARIANT_STEPS)]
+        stage = []
+        for rep in range(2):
+            for i in range(VARIANT_STEPS):
+                D.deltakv_decode_attn(layv, cv[i % nrepv], q_d[i % nsteps], wuk_d, wuv_d, outs[i % nsteps], ws_dv,
+                                      stream=s_h, stage_events=ev_v[i])
+            hip.sync(s_h)
+            stage.extend([[hip.elapsed_ms(e[2 * j], e[2 * j + 1]) for j in range(3)] for e in ev_v])
+        stage = np.array(stage)
+        hip.begin_capture(s_h)
+        try:
+            for i in range(VARIANT_STEPS):
+                D.deltakv_decode_attn(layv, cv[i % nrepv], q_d[i % nsteps], wuk_d, wuv_d, outs[i % nsteps], ws_dv,
+                                      stream=s_h)
+        finally:
+            _, g_v = hip.end_capture(s_h)
+        hip.launch(g_v, s_h)
         hip.sync(s_h)
-        q4_stage.extend([[hip.elapsed_ms(e[2 * j], e[2 * j + 1]) for j in range(3)] for e in ev_4])
-    q4_stage = np.array(q4_stage)
-    hip.begin_capture(s_h)
-    try:
-        for i in range(Q4_STEPS):
-            D.deltakv_decode_attn(lay4, caches4[i % nrep4], q_d[i % nsteps], wuk_d, wuv_d, outs[i % nsteps], ws_d4,
-                                  stream=s_h)
-    finally:
-        _, g_q4 = hip.end_capture(s_h)
-    hip.launch(g_q4, s_h)
-    hip.sync(s_h)
-    ev_g4 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev_g4[0].record(stream)
-    for _ in range(SEL_REPLAYS):
-        hip.launch(g_q4, s_h)
-    ev_g4[1].record(stream)
-    hip.sync(s_h)
-    q4_step_us = ev_g4[0].elapsed_time(ev_g4[1]) * 1e3 / (SEL_REPLAYS * Q4_STEPS)
-    eff4 = effective_decode_bytes(cfg, code_bits=4)
-    del caches4
+        ev_g = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev_g[0].record(stream)
+        for _ in range(SEL_REPLAYS):
+            hip.launch(g_v, s_h)
+        ev_g[1].record(stream)
+        hip.sync(s_h)
+        step_us = ev_g[0].elapsed_time(ev_g[1]) * 1e3 / (SEL_REPLAYS * VARIANT_STEPS)
+        effv = effective_decode_bytes(cfg, code_bits=kw.get("code_bits", 0), top_k=kw.get("top_k", 1))
+        return {"layout": {k2: v2 for k2, v2 in kw.items()}, "cache_mb": round(nbytes / 1e6, 2),
+                "cache_replicas": nrepv, "splits": D.dkv_decode_auto_splits(layv, cfg.n_q_heads),
+                "compress_ms": round(float(comp.sum()), 4),
+                "compress_stage_ms": {"mean": round(comp[0], 4), "center": round(comp[1], 4),
+                                      "search": round(comp[2], 4), "encode": round(comp[3], 4)},
+                "decode_us_per_step": round(step_us, 3),
+                "decode_gbs_effective": round(effv / (step_us * 1e-6) / 1e9, 2),
+                "effective_bytes_per_step": effv,
+                "stage_us": {"refscore": round(float(stage[:, 0].mean()) * 1e3, 3),
+                             "split": round(float(stage[:, 1].mean()) * 1e3, 3),
+                             "combine": round(float(stage[:, 2].mean()) * 1e3, 3)}}
+
+    int4 = variant(code_bits=4)
+    topk = variant(top_k=TOPK_K, metric="l2")
+    topk["search_gflops_per_s"] = round(search_flops_per_stream(cfg) * cfg.batch * cfg.n_kv_heads * 2
+                                        / (topk["compress_stage_ms"]["search"] * 1e-3) / 1e9, 1)
 
     # Decode-time append: a cache sized for APPEND_TOKENS more tokens takes
     # them one at a time after the prefill (each new token of every stream is
@@ -601,14 +620,8 @@ def main():
                                "unit": "GB/s",
                                "frac": round(sel_bytes / (sel_split_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                                "bytes_per_launch": int(sel_bytes), "launch_us": round(sel_split_us, 3)},
-        "int4_codes": {"cache_mb": round(cache4_bytes / 1e6, 2), "cache_replicas": nrep4, "splits": splits4,
-                       "compress_ms": round(q4_compress_ms, 4),
-                       "decode_us_per_step": round(q4_step_us, 3),
-                       "decode_gbs_effective": round(eff4 / (q4_step_us * 1e-6) / 1e9, 2),
-                       "effective_bytes_per_step": eff4,
-                       "stage_us": {"refscore": round(float(q4_stage[:, 0].mean()) * 1e3, 3),
-                                    "split": round(float(q4_stage[:, 1].mean()) * 1e3, 3),
-                                    "combine": round(float(q4_stage[:, 2].mean()) * 1e3, 3)}},
+        "int4_codes": int4,
+        "topk_l2": topk,
         "append_kernel_us_per_token": round(append_us, 3),
         "roofline_append": {"kernel": "k_append_search", "bound": "hbm",
                             "achieved": round(append_bytes / (search_us * 1e-6) / 1e9, 2), "peak": HBM_PEAK_GBS,
