@@ -163,6 +163,10 @@ struct Tile {
   Frag xv[2][2];   // value B [group][half]: tokens 4 q4 + 2 group + {0, 1}
   Frag bc[2];      // value-code B [group] (+ the 1.0 column); d_c > 32
   Frag cv;         // d_c <= 32: the tile's value codes, one 16-byte load per lane
+  uint32_t ckq;    // 4-bit codes: the key code nibbles of token n16 (columns 8 q4 ..)
+  uint32_t cvq;    // 4-bit codes: the value code nibbles the lane would load as cv
+  uint32_t scl;    // 4-bit codes: bits of the key scale of token n16
+  uint32_t sclv;   // 4-bit codes: bits of the value scale of the token of cvq
   int cnt;
 };
 
@@ -171,6 +175,10 @@ struct Args {
   const uint16_t* refsV;
   const uint16_t* codesK;
   const uint16_t* codesV;
+  const uint8_t* qK;      // 4-bit codes: rows of d_c / 2 bytes
+  const uint8_t* qV;
+  const uint16_t* sclK;   // 4-bit codes: per-row scales
+  const uint16_t* sclV;
   const void* idxK;       // uint16_t or uint32_t ordinals
   const void* idxV;
   const float* score;     // S rows of this (b, h), 4 floats each
@@ -209,7 +217,7 @@ __device__ __forceinline__ float s_lookup(const Args& p, const float* s_lds, int
   return SLDS ? s_lds[rk * 4 + gl] : ldg<float>(p.score, (rk * 4 + gl) * 4u);
 }
 
-template <bool CODED, int DCK, bool SLDS>
+template <bool CODED, int DCK, bool SLDS, bool Q4>
 __device__ __forceinline__ void load_data(const Args& p, const Shape& sh, const float* s_lds, const TileIdx& ti,
                                           int n16, int q4, Tile& td) {
   const int dc = sh.dc;
@@ -237,7 +245,20 @@ __device__ __forceinline__ void load_data(const Args& p, const Shape& sh, const 
     td.xv[1][0] = Frag{a.x, a.y, b.x, b.y};
     td.xv[1][1] = Frag{a.z, a.w, b.z, b.w};
   }
-  if (CODED) {
+  if (CODED && Q4) {
+    // 4-bit codes (d_c <= 32): raw nibbles and the token's scale; the
+    // operands are built in compute_tile, once the words have arrived.
+    const int cnt = max(ti.cnt, 1);
+    const uint32_t ua = ti.base + min(n16, cnt - 1);
+    const int c = q4 * 8;
+    td.ckq = ldg<uint32_t>(p.qK, ua * (uint32_t)(dc / 2) + (uint32_t)(c < dc ? c : 0) / 2u);
+    td.scl = ldg<uint16_t>(p.sclK, ua * 2u);
+    const int g2 = n16 >> 3, cc = n16 & 7;
+    const int col = 4 * (cc & ~1);
+    const uint32_t u = ti.base + min(q4 * 4 + 2 * g2 + (cc & 1), cnt - 1);
+    td.cvq = ldg<uint32_t>(p.qV, u * (uint32_t)(dc / 2) + (uint32_t)(col < dc ? col : 0) / 2u);
+    td.sclv = ldg<uint16_t>(p.sclV, u * 2u);
+  } else if (CODED) {
     const int cnt = max(ti.cnt, 1);
     const uint32_t ua = ti.base + min(n16, cnt - 1);
 #pragma unroll
@@ -298,23 +319,42 @@ __device__ __forceinline__ uint32_t ror8(uint32_t v) {
 // c + 1 columns 4c + 4 .. 4c + 7 of both tokens, and group 1 sits 8 lanes
 // up.  Lanes at or past column d_c get the 1.0 column (only the lane at d_c
 // is read).
-__device__ __forceinline__ void value_code_operands(const Frag& x, int n16, int dc, Frag* bc) {
+__device__ __forceinline__ void value_code_operands(const Frag& x, int n16, int dc, Frag* bc,
+                                                    uint32_t one_bits = 0x3F80u) {
   const bool odd = n16 & 1;
   const uint32_t r0 = swap_pairs(odd ? x.x : x.z), r1 = swap_pairs(odd ? x.y : x.w);
   const Frag mine = odd ? Frag{r0, r1, x.z, x.w} : Frag{x.x, x.y, r0, r1};
   const Frag up = Frag{ror8(mine.x), ror8(mine.y), ror8(mine.z), ror8(mine.w)};
   const bool data = n16 * 4 < dc;
-  const uint32_t one = n16 * 4 == dc ? 0x3F80u : 0u;
+  const uint32_t one = n16 * 4 == dc ? one_bits : 0u;
   const Frag ones = Frag{one, 0u, one, 0u};
   bc[0] = data ? mine : ones;
   bc[1] = data ? up : ones;
 }
 
-template <bool CODED, int DCK>
+// 4-bit codes: elements 2j and 2j + 1 of a nibble word as a bf16 pair
+// (small integers are exact in bf16: the top half of their fp32 bits).
+__device__ __forceinline__ uint32_t q4_pair_bf16(uint32_t w, int j) {
+  const float a = (float)((int32_t)(w << (28 - 8 * j)) >> 28);
+  const float b = (float)((int32_t)(w << (24 - 8 * j)) >> 28);
+  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
+}
+
+template <bool CODED, int DCK, bool Q4>
 __device__ __forceinline__ void compute_tile(const Tile& td, const Frag* qh, const Frag* ql, int n16, int q4, int dc,
                                              const uint32_t* sel, State& st) {
   float s[4] = {td.sb[0], td.sb[1], td.sb[2], td.sb[3]};
-  if (CODED) {
+  if (CODED && Q4) {
+    // Key codes: integer values as the A operand, the token's scale applied
+    // to the fp32 product (exact operands, one rounding).
+    const Frag ck = Frag{q4_pair_bf16(td.ckq, 0), q4_pair_bf16(td.ckq, 1), q4_pair_bf16(td.ckq, 2),
+                         q4_pair_bf16(td.ckq, 3)};
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+    c = mfma16(ck, qh[0], c);
+    c = mfma16(ck, ql[0], c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] += bf2f((uint16_t)__shfl((int)td.scl, 4 * q4 + i, 64)) * c[i];
+  } else if (CODED) {
     f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < DCK; ++ks) {
@@ -339,7 +379,24 @@ __device__ __forceinline__ void compute_tile(const Tile& td, const Frag* qh, con
     st.accc *= aa;
   }
   Frag bc[2] = {td.bc[0], td.bc[1]};
-  if (CODED && DCK == 1) value_code_operands(td.cv, n16, dc, bc);
+  Frag bl[2];   // 4-bit codes: low bf16 parts of the dequantized value codes
+  if (CODED && Q4) {
+    // Value codes scale * q (at most 12 significant bits) as exact bf16
+    // hi + lo parts; the weight-sum column rides on the hi operand only.
+    const float sv = bf2f((uint16_t)td.sclv);
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = sv * (float)((int32_t)(td.cvq << (28 - 8 * j)) >> 28);
+      const float b = sv * (float)((int32_t)(td.cvq << (24 - 8 * j)) >> 28);
+      hw[j] = pk_bf16(a, b);
+      lw[j] = pk_bf16(a - __uint_as_float(hw[j] << 16), b - __uint_as_float(hw[j] & 0xFFFF0000u));
+    }
+    value_code_operands(Frag{hw[0], hw[1], hw[2], hw[3]}, n16, dc, bc);
+    value_code_operands(Frag{lw[0], lw[1], lw[2], lw[3]}, n16, dc, bl, 0u);
+  } else if (CODED && DCK == 1) {
+    value_code_operands(td.cv, n16, dc, bc);
+  }
   float p[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(s[i] - st.m);
@@ -359,6 +416,7 @@ __device__ __forceinline__ void compute_tile(const Tile& td, const Frag* qh, con
     st.accr[1] = mfma16(al, td.xv[g2][1], st.accr[1]);
     st.accc = mfma16(ah, bc[g2], st.accc);
     st.accc = mfma16(al, bc[g2], st.accc);
+    if (CODED && Q4) st.accc = mfma16(ah, bl[g2], st.accc);
   }
 }
 
@@ -366,7 +424,7 @@ __device__ __forceinline__ void compute_tile(const Tile& td, const Frag* qh, con
 // (buffers A and B); the ordinals of tile t+2 and the data of tile t+1 are
 // in flight while tile t computes.  The scheduling barriers keep the
 // compiler from hoisting a tile's arithmetic above the next tile's loads.
-template <bool CODED, int DCK, typename IdxT, bool SLDS>
+template <bool CODED, int DCK, typename IdxT, bool SLDS, bool Q4>
 __device__ __forceinline__ void run_tiles(const Args& p, const Shape& sh, const float* s_lds, int t0, int t1,
                                           int first, int last, int n16, int q4, const Frag* qh, const Frag* ql,
                                           const uint32_t* sel, State& st) {
@@ -375,17 +433,17 @@ __device__ __forceinline__ void run_tiles(const Args& p, const Shape& sh, const 
   Tile da, db;
   load_idx<CODED, IdxT>(p, t0, t1, first, last, n16, q4, ia);
   load_idx<CODED, IdxT>(p, t0 + 1, t1, first, last, n16, q4, ib);
-  load_data<CODED, DCK, SLDS>(p, sh, s_lds, ia, n16, q4, da);
+  load_data<CODED, DCK, SLDS, Q4>(p, sh, s_lds, ia, n16, q4, da);
   for (int tt = t0; tt < t1; tt += 2) {
     load_idx<CODED, IdxT>(p, tt + 2, t1, first, last, n16, q4, ia);
-    load_data<CODED, DCK, SLDS>(p, sh, s_lds, ib, n16, q4, db);
+    load_data<CODED, DCK, SLDS, Q4>(p, sh, s_lds, ib, n16, q4, db);
     __builtin_amdgcn_sched_barrier(0);
-    compute_tile<CODED, DCK>(da, qh, ql, n16, q4, sh.dc, sel, st);
+    compute_tile<CODED, DCK, Q4>(da, qh, ql, n16, q4, sh.dc, sel, st);
     __builtin_amdgcn_sched_barrier(0);
     load_idx<CODED, IdxT>(p, tt + 3, t1, first, last, n16, q4, ib);
-    load_data<CODED, DCK, SLDS>(p, sh, s_lds, ia, n16, q4, da);
+    load_data<CODED, DCK, SLDS, Q4>(p, sh, s_lds, ia, n16, q4, da);
     __builtin_amdgcn_sched_barrier(0);
-    compute_tile<CODED, DCK>(db, qh, ql, n16, q4, sh.dc, sel, st);
+    compute_tile<CODED, DCK, Q4>(db, qh, ql, n16, q4, sh.dc, sel, st);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -398,7 +456,7 @@ __device__ __forceinline__ int split_lo(int n, int sp, int splits, int align) {
 
 // Dynamic LDS: the S table (SLDS) and, after the tile loop, the wave-merge
 // buffer in the same bytes.
-template <int DCK, typename IdxT, bool SLDS>
+template <int DCK, typename IdxT, bool SLDS, bool Q4>
 __global__ __launch_bounds__(kThreads) void k_split_mfma(DecodeArgs a, Shape sh) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   __shared__ float red_m[kWaves][4];
@@ -425,6 +483,10 @@ __global__ __launch_bounds__(kThreads) void k_split_mfma(DecodeArgs a, Shape sh)
   p.idxK = (const IdxT*)a.idx + sK * sh.Nc;
   p.idxV = (const IdxT*)a.idx + sV * sh.Nc;
   p.score = a.score + (size_t)bh * sh.R * 4;
+  p.qK = (const uint8_t*)a.codes + sK * sh.Nc * (dc / 2);
+  p.qV = (const uint8_t*)a.codes + sV * sh.Nc * (dc / 2);
+  p.sclK = Q4 ? (const uint16_t*)a.scales + sK * sh.Nc : kOnePair;
+  p.sclV = Q4 ? (const uint16_t*)a.scales + sV * sh.Nc : kOnePair;
 
   // The head's S table into LDS.
   if (SLDS) {
@@ -472,8 +534,8 @@ __global__ __launch_bounds__(kThreads) void k_split_mfma(DecodeArgs a, Shape sh)
   st.m = -INFINITY;
   st.accr[0] = st.accr[1] = st.accc = f32x4{0.f, 0.f, 0.f, 0.f};
   // The wave's tiles: coded tiles [0, nct) then reference tiles [nct, nt).
-  run_tiles<true, DCK, IdxT, SLDS>(p, sh, lds, t_beg, min(t_end, nct), n0, n1, n16, q4, qh, ql, sel, st);
-  run_tiles<false, DCK, IdxT, SLDS>(p, sh, lds, max(t_beg, nct) - nct, t_end - nct, r0, r1, n16, q4, qh, ql, sel,
+  run_tiles<true, DCK, IdxT, SLDS, Q4>(p, sh, lds, t_beg, min(t_end, nct), n0, n1, n16, q4, qh, ql, sel, st);
+  run_tiles<false, DCK, IdxT, SLDS, Q4>(p, sh, lds, max(t_beg, nct) - nct, t_end - nct, r0, r1, n16, q4, qh, ql, sel,
                                     st);
 
   // ---- merge the block's waves (fixed order) ----
@@ -614,8 +676,11 @@ size_t split_lds_bytes(const Shape& sh, bool slds) {
 template <int DCK, typename IdxT, bool SLDS>
 hipError_t launch_split(const Shape& sh, const DecodeArgs& a, hipStream_t st, dim3 grid) {
   // gfx950 gives a workgroup up to 160 KB of LDS; dynamic sizes above 64 KB
-  // need no opt-in attribute on this runtime.
-  return launch_lds(k_split_mfma<DCK, IdxT, SLDS>, grid, kThreads, split_lds_bytes(sh, SLDS), st,
+  // need no opt-in attribute on this runtime.  4-bit codes: d_c <= 32 only.
+  if (DCK == 1 && sh.q4)
+    return launch_lds(k_split_mfma<1, IdxT, SLDS, true>, grid, kThreads, split_lds_bytes(sh, SLDS), st,
+                      ev_start(a.events, 1), ev_stop(a.events, 1), a, sh);
+  return launch_lds(k_split_mfma<DCK, IdxT, SLDS, false>, grid, kThreads, split_lds_bytes(sh, SLDS), st,
                     ev_start(a.events, 1), ev_stop(a.events, 1), a, sh);
 }
 
@@ -632,7 +697,7 @@ bool mfma_side_kernels_supported(const Shape& sh, int G, int splits) {
 }
 
 bool decode_fused_supported(const Shape& sh, int G, int splits) {
-  return !sh.q4 && sh.K == 1 && mfma_side_kernels_supported(sh, G, splits);
+  return (!sh.q4 || sh.dc <= 32) && sh.K == 1 && mfma_side_kernels_supported(sh, G, splits);
 }
 
 // The split kernel holds one 512-thread block per CU: about 256 blocks over
