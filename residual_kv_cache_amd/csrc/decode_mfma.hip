@@ -424,15 +424,14 @@ __device__ __forceinline__ void compute_tile(const Tile& td, const Frag* qh, con
 // (buffers A and B); the ordinals of tile t+2 and the data of tile t+1 are
 // in flight while tile t computes.  The scheduling barriers keep the
 // compiler from hoisting a tile's arithmetic above the next tile's loads.
+// The ordinals of the first two tiles (ia, ib) come from the caller, which
+// issues them early.
 template <bool CODED, int DCK, typename IdxT, bool SLDS, bool Q4>
 __device__ __forceinline__ void run_tiles(const Args& p, const Shape& sh, const float* s_lds, int t0, int t1,
                                           int first, int last, int n16, int q4, const Frag* qh, const Frag* ql,
-                                          const uint32_t* sel, State& st) {
+                                          const uint32_t* sel, TileIdx ia, TileIdx ib, State& st) {
   if (t0 >= t1) return;
-  TileIdx ia, ib;
   Tile da, db;
-  load_idx<CODED, IdxT>(p, t0, t1, first, last, n16, q4, ia);
-  load_idx<CODED, IdxT>(p, t0 + 1, t1, first, last, n16, q4, ib);
   load_data<CODED, DCK, SLDS, Q4>(p, sh, s_lds, ia, n16, q4, da);
   for (int tt = t0; tt < t1; tt += 2) {
     load_idx<CODED, IdxT>(p, tt + 2, t1, first, last, n16, q4, ia);
@@ -488,11 +487,27 @@ __global__ __launch_bounds__(kThreads) void k_split_mfma(DecodeArgs a, Shape sh)
   p.sclK = Q4 ? (const uint16_t*)a.scales + sK * sh.Nc : kOnePair;
   p.sclV = Q4 ? (const uint16_t*)a.scales + sV * sh.Nc : kOnePair;
 
-  // The head's S table into LDS.
+  // Ordinals of the wave's first two coded tiles: issued first, so that
+  // their HBM round trip overlaps the S-table copy.
+  const int c1 = min(t_end, nct);
+  TileIdx ia = {0, 0, 0}, ib = {0, 0, 0};
+  if (t_beg < c1) {
+    load_idx<true, IdxT>(p, t_beg, c1, n0, n1, n16, q4, ia);
+    load_idx<true, IdxT>(p, t_beg + 1, c1, n0, n1, n16, q4, ib);
+  }
+  // The head's S table into LDS, four rows per thread in flight at once.
   if (SLDS) {
     const f32x4* src = reinterpret_cast<const f32x4*>(p.score);
     f32x4* dst = reinterpret_cast<f32x4*>(lds);
-    for (int i = tid; i < sh.R; i += kThreads) dst[i] = src[i];
+    int i = tid;
+    for (; i + 3 * kThreads < sh.R; i += 4 * kThreads) {
+      const f32x4 v0 = src[i], v1 = src[i + kThreads], v2 = src[i + 2 * kThreads], v3 = src[i + 3 * kThreads];
+      dst[i] = v0;
+      dst[i + kThreads] = v1;
+      dst[i + 2 * kThreads] = v2;
+      dst[i + 3 * kThreads] = v3;
+    }
+    for (; i < sh.R; i += kThreads) dst[i] = src[i];
   }
   // Score B operands: q'_g (g = n16 / 4) split into bf16 hi + lo parts.
   Frag qh[DCK], ql[DCK];
@@ -534,9 +549,16 @@ __global__ __launch_bounds__(kThreads) void k_split_mfma(DecodeArgs a, Shape sh)
   st.m = -INFINITY;
   st.accr[0] = st.accr[1] = st.accc = f32x4{0.f, 0.f, 0.f, 0.f};
   // The wave's tiles: coded tiles [0, nct) then reference tiles [nct, nt).
-  run_tiles<true, DCK, IdxT, SLDS, Q4>(p, sh, lds, t_beg, min(t_end, nct), n0, n1, n16, q4, qh, ql, sel, st);
-  run_tiles<false, DCK, IdxT, SLDS, Q4>(p, sh, lds, max(t_beg, nct) - nct, t_end - nct, r0, r1, n16, q4, qh, ql, sel,
-                                    st);
+  run_tiles<true, DCK, IdxT, SLDS, Q4>(p, sh, lds, t_beg, c1, n0, n1, n16, q4, qh, ql, sel, ia, ib, st);
+  {
+    const int rt0 = max(t_beg, nct) - nct, rt1 = t_end - nct;
+    TileIdx ra = {0, 0, 0}, rb = {0, 0, 0};
+    if (rt0 < rt1) {
+      load_idx<false, IdxT>(p, rt0, rt1, r0, r1, n16, q4, ra);
+      load_idx<false, IdxT>(p, rt0 + 1, rt1, r0, r1, n16, q4, rb);
+    }
+    run_tiles<false, DCK, IdxT, SLDS, Q4>(p, sh, lds, rt0, rt1, r0, r1, n16, q4, qh, ql, sel, ra, rb, st);
+  }
 
   // ---- merge the block's waves (fixed order) ----
   if (lane < 16 && (n16 & 3) == 0) red_m[wave][n16 >> 2] = st.m;
