@@ -307,6 +307,10 @@ def main():
 
     lay = D.make_layout(cfg.dtype, cfg.head_dim, cfg.code_dim, cfg.stride, cfg.n_kv_heads, cfg.batch, cfg.seq_len)
     cache_bytes = D.dkv_cache_bytes(lay)
+    # Shapes the MFMA token-tile decode serves (bfloat16, d = 128, up to 4
+    # query heads per KV head, code dim up to 48; token lists up to 32).
+    mfma_shape = (cfg.dtype == "bf16" and cfg.head_dim == 128 and cfg.n_q_heads // cfg.n_kv_heads <= 4
+                  and cfg.code_dim <= 48)
     nrep = max(1, math.ceil(2 * MALL_BYTES / cache_bytes))
     caches = [D.Cache(lay) for _ in range(nrep)]
     splits = args.splits or D.dkv_decode_auto_splits(lay, cfg.n_q_heads)
@@ -605,7 +609,7 @@ def main():
         "decode_stage_us": {"refscore": round(float(d_stage[:, 0].mean()) * 1e3, 3),
                             "split": round(split_ms * 1e3, 3),
                             "combine": round(float(d_stage[:, 2].mean()) * 1e3, 3)},
-        "roofline": {"kernel": "k_split_mfma (decode token stream)", "bound": "hbm",
+        "roofline": {"kernel": "k_split_mfma (decode token stream)" if mfma_shape else "k_split_valu", "bound": "hbm",
                      "achieved": round(split_bytes / (split_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(split_bytes / (split_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": stored_traffic(cfg.name, splits), "bytes_per_launch": split_bytes,
@@ -615,7 +619,8 @@ def main():
                              "stage_us": {"refscore": round(float(s_stage[:, 0].mean()) * 1e3, 3),
                                           "split": round(sel_split_us, 3),
                                           "combine": round(float(s_stage[:, 2].mean()) * 1e3, 3)}},
-        "roofline_selective": {"kernel": "k_split_sel", "bound": "hbm",
+        "roofline_selective": {"kernel": "k_split_mfma (token list)" if mfma_shape and cfg.code_dim <= 32
+                               else "k_split_sel", "bound": "hbm",
                                "achieved": round(sel_bytes / (sel_split_us * 1e-6) / 1e9, 2), "peak": HBM_PEAK_GBS,
                                "unit": "GB/s",
                                "frac": round(sel_bytes / (sel_split_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),

@@ -722,6 +722,7 @@ hipError_t launch_decode_sel_sd(const Shape& sh, const DecodeArgs& a, hipStream_
 }  // namespace
 
 hipError_t launch_decode_sel(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
+  if (decode_sel_fused_supported(sh, a.G, a.splits)) return launch_decode_sel_fused(sh, a, st);
   if (sh.bf16)
     return sh.d == 128 ? launch_decode_sel_sd<BF16, 128>(sh, a, st) : launch_decode_sel_sd<BF16, 64>(sh, a, st);
   return sh.d == 128 ? launch_decode_sel_sd<F32, 128>(sh, a, st) : launch_decode_sel_sd<F32, 64>(sh, a, st);

@@ -153,8 +153,13 @@ __global__ __launch_bounds__(256) void k_refscore_mfma(DecodeArgs a, Shape sh, i
 // loop bodies have no control flow (a branch merge would make the compiler
 // drain every outstanding load).
 struct TileIdx {
-  int base, cnt;   // first token (coded row or reference ordinal); valid tokens (0 = dead tile)
+  int base, cnt;   // first token (coded row or reference ordinal); valid tokens (0 = dead tile);
+                   // token lists: cnt is the tile's validity mask (bit j = token j)
   int raw;
+  // Token lists only: the ordinal of a reference or invalid position (used
+  // instead of raw when use_alt), and the code rows of the lane's key-code
+  // and value-code tokens (-1: zero row).
+  int alt, use_alt, rb, rc;
 };
 
 struct Tile {
@@ -182,7 +187,19 @@ struct Args {
   const void* idxK;       // uint16_t or uint32_t ordinals
   const void* idxV;
   const float* score;     // S rows of this (b, h), 4 floats each
+  const uint32_t* list;   // token lists: the positions of sequence b
+  uint32_t magic;         // token lists: floor((2^32 - 1) / s)
 };
+
+// 256 zero bytes: the code row of a reference position in a token list.
+__device__ const uint32_t kZeroCodes[64] __attribute__((aligned(16))) = {0u};
+
+// floor(t / s) from magic = floor((2^32 - 1) / s): the high product is
+// floor(t / s) or one less, and one correction step fixes it.
+__device__ __forceinline__ uint32_t div_s(uint32_t t, uint32_t s, uint32_t magic) {
+  const uint32_t q = __umulhi(t, magic);
+  return q + (uint32_t)(t - q * s >= s);
+}
 
 // Lane k of each 16-lane row, broadcast over the row.
 template <int K>
@@ -211,28 +228,74 @@ __device__ __forceinline__ void load_idx(const Args& p, int tt, int t1, int firs
   }
 }
 
+// Token-list mode: tile tt of the list entries [first, last) of the block.
+// A lane reads the positions of three of the tile's tokens: j_a, whose
+// ordinal it contributes to the row broadcast (lanes n16 < 8: key ordinal of
+// token 4 q4 + n16, value ordinal of token 4 q4 + n16 - 4), j_b = n16 (its
+// key-code row) and j_c (its value-code row, the token load_data pairs it
+// with).  A reference position acts as a coded token with a zero code row and
+// its own ordinal in both streams, so its score is S[t / s] and its value the
+// reference row; a position at or past T is cleared by the validity mask.
+template <typename IdxT>
+__device__ __forceinline__ void load_idx_sel(const Args& p, const Shape& sh, int tt, int t1, int first, int last,
+                                             int n16, int q4, TileIdx& ti) {
+  const bool live = tt < t1;
+  tt = min(tt, t1 - 1);
+  const int base = first + tt * 16;
+  const int cnt = min(16, last - base);
+  const int ja = q4 * 4 + (n16 & 3), jb = n16, jc = q4 * 4 + 2 * (n16 >> 3) + (n16 & 1);
+  const uint32_t pa = p.list[base + min(ja, cnt - 1)];
+  const uint32_t pb = p.list[base + min(jb, cnt - 1)];
+  const uint32_t pc = p.list[base + min(jc, cnt - 1)];
+  const uint32_t T = (uint32_t)sh.T, s = (uint32_t)sh.s;
+  const uint32_t qa = div_s(pa, s, p.magic), qb = div_s(pb, s, p.magic), qc = div_s(pc, s, p.magic);
+  const bool coded_a = pa < T && pa != qa * s;
+  const bool coded_b = pb < T && pb != qb * s;
+  const bool coded_c = pc < T && pc != qc * s;
+  // Not coded: read the zero row (a layout may hold no coded rows at all).
+  const IdxT* src = coded_a ? (const IdxT*)(n16 < 4 ? p.idxK : p.idxV) + (pa - qa - 1) : (const IdxT*)kZeroCodes;
+  ti.raw = (int)ldg<IdxT>(src, 0u);
+  ti.alt = pa < T ? (int)qa : 0;
+  ti.use_alt = !coded_a;
+  ti.rb = coded_b ? (int)(pb - qb - 1) : -1;
+  ti.rc = coded_c ? (int)(pc - qc - 1) : -1;
+  const uint64_t vb = __ballot(live && jb < cnt && pb < T);
+  ti.cnt = (int)(vb & 0xFFFFull);
+  ti.base = 0;
+}
+
+template <bool CODED, bool SEL, typename IdxT>
+__device__ __forceinline__ void load_tile_idx(const Args& p, const Shape& sh, int tt, int t1, int first, int last,
+                                              int n16, int q4, TileIdx& ti) {
+  if constexpr (SEL)
+    load_idx_sel<IdxT>(p, sh, tt, t1, first, last, n16, q4, ti);
+  else
+    load_idx<CODED, IdxT>(p, tt, t1, first, last, n16, q4, ti);
+}
+
 template <int I, bool SLDS>
 __device__ __forceinline__ float s_lookup(const Args& p, const float* s_lds, int raw, int R, int gl) {
   const uint32_t rk = (uint32_t)min(row_bcast<I>(raw), R - 1);
   return SLDS ? s_lds[rk * 4 + gl] : ldg<float>(p.score, (rk * 4 + gl) * 4u);
 }
 
-template <bool CODED, int DCK, bool SLDS, bool Q4>
+template <bool CODED, int DCK, bool SLDS, bool Q4, bool SEL = false>
 __device__ __forceinline__ void load_data(const Args& p, const Shape& sh, const float* s_lds, const TileIdx& ti,
                                           int n16, int q4, Tile& td) {
   const int dc = sh.dc;
   const int gl = n16 >> 2;
   td.cnt = ti.cnt;
+  const int raw = SEL ? (ti.use_alt ? ti.alt : ti.raw) : ti.raw;
   // Ordinals come from caller memory: clamp so that a corrupt cache can never
   // address outside the reference arrays or the S table.
-  td.sb[0] = s_lookup<0, SLDS>(p, s_lds, ti.raw, sh.R, gl);
-  td.sb[1] = s_lookup<1, SLDS>(p, s_lds, ti.raw, sh.R, gl);
-  td.sb[2] = s_lookup<2, SLDS>(p, s_lds, ti.raw, sh.R, gl);
-  td.sb[3] = s_lookup<3, SLDS>(p, s_lds, ti.raw, sh.R, gl);
-  const uint32_t rv0 = (uint32_t)min(row_bcast<4>(ti.raw), sh.R - 1);
-  const uint32_t rv1 = (uint32_t)min(row_bcast<5>(ti.raw), sh.R - 1);
-  const uint32_t rv2 = (uint32_t)min(row_bcast<6>(ti.raw), sh.R - 1);
-  const uint32_t rv3 = (uint32_t)min(row_bcast<7>(ti.raw), sh.R - 1);
+  td.sb[0] = s_lookup<0, SLDS>(p, s_lds, raw, sh.R, gl);
+  td.sb[1] = s_lookup<1, SLDS>(p, s_lds, raw, sh.R, gl);
+  td.sb[2] = s_lookup<2, SLDS>(p, s_lds, raw, sh.R, gl);
+  td.sb[3] = s_lookup<3, SLDS>(p, s_lds, raw, sh.R, gl);
+  const uint32_t rv0 = (uint32_t)min(row_bcast<4>(raw), sh.R - 1);
+  const uint32_t rv1 = (uint32_t)min(row_bcast<5>(raw), sh.R - 1);
+  const uint32_t rv2 = (uint32_t)min(row_bcast<6>(raw), sh.R - 1);
+  const uint32_t rv3 = (uint32_t)min(row_bcast<7>(raw), sh.R - 1);
   {
     const Frag a = ldg<Frag>(p.refsV, (rv0 * kD + n16 * 8) * 2u);
     const Frag b = ldg<Frag>(p.refsV, (rv1 * kD + n16 * 8) * 2u);
@@ -245,7 +308,29 @@ __device__ __forceinline__ void load_data(const Args& p, const Shape& sh, const 
     td.xv[1][0] = Frag{a.x, a.y, b.x, b.y};
     td.xv[1][1] = Frag{a.z, a.w, b.z, b.w};
   }
-  if (CODED && Q4) {
+  if (CODED && Q4 && SEL) {
+    // Token lists: rows from the list; a reference position reads zeros.
+    const int c = q4 * 8;
+    const int col = 4 * ((n16 & 7) & ~1);
+    const bool kb = ti.rb >= 0, vb = ti.rc >= 0;
+    const uint32_t ua = (uint32_t)ti.rb, u = (uint32_t)ti.rc;
+    td.ckq = ldg<uint32_t>(kb ? (const void*)p.qK : (const void*)kZeroCodes,
+                           kb ? ua * (uint32_t)(dc / 2) + (uint32_t)(c < dc ? c : 0) / 2u : 0u);
+    td.scl = ldg<uint16_t>(kb ? (const void*)p.sclK : (const void*)kOnePair, kb ? ua * 2u : 0u);
+    td.cvq = ldg<uint32_t>(vb ? (const void*)p.qV : (const void*)kZeroCodes,
+                           vb ? u * (uint32_t)(dc / 2) + (uint32_t)(col < dc ? col : 0) / 2u : 0u);
+    td.sclv = ldg<uint16_t>(vb ? (const void*)p.sclV : (const void*)kOnePair, vb ? u * 2u : 0u);
+  } else if (CODED && SEL) {
+    const int c = q4 * 8;
+    const bool kb = ti.rb >= 0;
+    td.ck[0] = ldg<Frag>(kb ? (const void*)p.codesK : (const void*)kZeroCodes,
+                         kb ? ((uint32_t)ti.rb * dc + (c < dc ? c : 0)) * 2u : 0u);
+    const int g2 = n16 >> 3, cc = n16 & 7;
+    const int col = 4 * (cc & ~1);
+    const bool in_code = col < dc, vb = ti.rc >= 0;
+    const void* vbase = in_code ? (vb ? (const void*)p.codesV : (const void*)kZeroCodes) : (const void*)kOnePair;
+    td.cv = ldg<Frag>(vbase, in_code && vb ? ((uint32_t)ti.rc * dc + col) * 2u : 0u);
+  } else if (CODED && Q4) {
     // 4-bit codes (d_c <= 32): raw nibbles and the token's scale; the
     // operands are built in compute_tile, once the words have arrived.
     const int cnt = max(ti.cnt, 1);
@@ -340,7 +425,7 @@ __device__ __forceinline__ uint32_t q4_pair_bf16(uint32_t w, int j) {
   return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
 }
 
-template <bool CODED, int DCK, bool Q4>
+template <bool CODED, int DCK, bool Q4, bool SEL = false>
 __device__ __forceinline__ void compute_tile(const Tile& td, const Frag* qh, const Frag* ql, int n16, int q4, int dc,
                                              const uint32_t* sel, State& st) {
   float s[4] = {td.sb[0], td.sb[1], td.sb[2], td.sb[3]};
@@ -364,8 +449,14 @@ __device__ __forceinline__ void compute_tile(const Tile& td, const Frag* qh, con
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[i] += c[i];
   }
+  if constexpr (SEL) {
+    const uint32_t vm = (uint32_t)td.cnt >> (q4 * 4);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) s[i] = q4 * 4 + i < td.cnt ? s[i] : -INFINITY;
+    for (int i = 0; i < 4; ++i) s[i] = (vm >> i) & 1u ? s[i] : -INFINITY;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = q4 * 4 + i < td.cnt ? s[i] : -INFINITY;
+  }
   const float tmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
   if (__ballot(tmax > st.m + kTau) != 0ull) {
     float t2 = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
@@ -426,23 +517,23 @@ __device__ __forceinline__ void compute_tile(const Tile& td, const Frag* qh, con
 // compiler from hoisting a tile's arithmetic above the next tile's loads.
 // The ordinals of the first two tiles (ia, ib) come from the caller, which
 // issues them early.
-template <bool CODED, int DCK, typename IdxT, bool SLDS, bool Q4>
+template <bool CODED, int DCK, typename IdxT, bool SLDS, bool Q4, bool SEL>
 __device__ __forceinline__ void run_tiles(const Args& p, const Shape& sh, const float* s_lds, int t0, int t1,
                                           int first, int last, int n16, int q4, const Frag* qh, const Frag* ql,
                                           const uint32_t* sel, TileIdx ia, TileIdx ib, State& st) {
   if (t0 >= t1) return;
   Tile da, db;
-  load_data<CODED, DCK, SLDS, Q4>(p, sh, s_lds, ia, n16, q4, da);
+  load_data<CODED, DCK, SLDS, Q4, SEL>(p, sh, s_lds, ia, n16, q4, da);
   for (int tt = t0; tt < t1; tt += 2) {
-    load_idx<CODED, IdxT>(p, tt + 2, t1, first, last, n16, q4, ia);
-    load_data<CODED, DCK, SLDS, Q4>(p, sh, s_lds, ib, n16, q4, db);
+    load_tile_idx<CODED, SEL, IdxT>(p, sh, tt + 2, t1, first, last, n16, q4, ia);
+    load_data<CODED, DCK, SLDS, Q4, SEL>(p, sh, s_lds, ib, n16, q4, db);
     __builtin_amdgcn_sched_barrier(0);
-    compute_tile<CODED, DCK, Q4>(da, qh, ql, n16, q4, sh.dc, sel, st);
+    compute_tile<CODED, DCK, Q4, SEL>(da, qh, ql, n16, q4, sh.dc, sel, st);
     __builtin_amdgcn_sched_barrier(0);
-    load_idx<CODED, IdxT>(p, tt + 3, t1, first, last, n16, q4, ib);
-    load_data<CODED, DCK, SLDS, Q4>(p, sh, s_lds, ia, n16, q4, da);
+    load_tile_idx<CODED, SEL, IdxT>(p, sh, tt + 3, t1, first, last, n16, q4, ib);
+    load_data<CODED, DCK, SLDS, Q4, SEL>(p, sh, s_lds, ia, n16, q4, da);
     __builtin_amdgcn_sched_barrier(0);
-    compute_tile<CODED, DCK, Q4>(db, qh, ql, n16, q4, sh.dc, sel, st);
+    compute_tile<CODED, DCK, Q4, SEL>(db, qh, ql, n16, q4, sh.dc, sel, st);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -454,8 +545,9 @@ __device__ __forceinline__ int split_lo(int n, int sp, int splits, int align) {
 }
 
 // Dynamic LDS: the S table (SLDS) and, after the tile loop, the wave-merge
-// buffer in the same bytes.
-template <int DCK, typename IdxT, bool SLDS, bool Q4>
+// buffer in the same bytes.  SEL: the block's tiles are 16-entry runs of the
+// sequence's token list (a.sel) instead of coded rows and references.
+template <int DCK, typename IdxT, bool SLDS, bool Q4, bool SEL>
 __global__ __launch_bounds__(kThreads) void k_split_mfma(DecodeArgs a, Shape sh) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   __shared__ float red_m[kWaves][4];
@@ -468,8 +560,10 @@ __global__ __launch_bounds__(kThreads) void k_split_mfma(DecodeArgs a, Shape sh)
   const int n16 = lane & 15, q4 = lane >> 4;
   const int G = a.G, dc = sh.dc;
 
-  const int n0 = split_lo(sh.N, sp, a.splits, 16), n1 = split_lo(sh.N, sp + 1, a.splits, 16);
-  const int r0 = split_lo(sh.R, sp, a.splits, 1), r1 = split_lo(sh.R, sp + 1, a.splits, 1);
+  // Coded rows [n0, n1) and references [r0, r1); token lists: entries [n0, n1).
+  const int nrow = SEL ? a.n_sel : sh.N;
+  const int n0 = split_lo(nrow, sp, a.splits, 16), n1 = split_lo(nrow, sp + 1, a.splits, 16);
+  const int r0 = SEL ? 0 : split_lo(sh.R, sp, a.splits, 1), r1 = SEL ? 0 : split_lo(sh.R, sp + 1, a.splits, 1);
   const int nct = (n1 - n0 + 15) / 16, nrt = (r1 - r0 + 15) / 16;
   const int nt = nct + nrt;
   const int t_beg = (int)((int64_t)nt * wave / kWaves), t_end = (int)((int64_t)nt * (wave + 1) / kWaves);
@@ -486,14 +580,16 @@ __global__ __launch_bounds__(kThreads) void k_split_mfma(DecodeArgs a, Shape sh)
   p.qV = (const uint8_t*)a.codes + sV * sh.Nc * (dc / 2);
   p.sclK = Q4 ? (const uint16_t*)a.scales + sK * sh.Nc : kOnePair;
   p.sclV = Q4 ? (const uint16_t*)a.scales + sV * sh.Nc : kOnePair;
+  p.list = SEL ? a.sel + (size_t)(bh / sh.H) * a.n_sel : nullptr;
+  p.magic = SEL ? 0xFFFFFFFFu / (uint32_t)sh.s : 0u;
 
   // Ordinals of the wave's first two coded tiles: issued first, so that
   // their HBM round trip overlaps the S-table copy.
   const int c1 = min(t_end, nct);
-  TileIdx ia = {0, 0, 0}, ib = {0, 0, 0};
+  TileIdx ia = {0, 0, 0, 0, 0, 0, 0}, ib = {0, 0, 0, 0, 0, 0, 0};
   if (t_beg < c1) {
-    load_idx<true, IdxT>(p, t_beg, c1, n0, n1, n16, q4, ia);
-    load_idx<true, IdxT>(p, t_beg + 1, c1, n0, n1, n16, q4, ib);
+    load_tile_idx<true, SEL, IdxT>(p, sh, t_beg, c1, n0, n1, n16, q4, ia);
+    load_tile_idx<true, SEL, IdxT>(p, sh, t_beg + 1, c1, n0, n1, n16, q4, ib);
   }
   // The head's S table into LDS, four rows per thread in flight at once.
   if (SLDS) {
@@ -546,18 +642,21 @@ __global__ __launch_bounds__(kThreads) void k_split_mfma(DecodeArgs a, Shape sh)
   if (SLDS) __syncthreads();
 
   State st;
-  st.m = -INFINITY;
+  // Token lists may leave a wave (or a whole split) with no valid token: a
+  // finite initial maximum keeps every weight 2^(s - m) at 0 rather than NaN
+  // there, and is replaced by the first real score.
+  st.m = SEL ? -3.0e38f : -INFINITY;
   st.accr[0] = st.accr[1] = st.accc = f32x4{0.f, 0.f, 0.f, 0.f};
   // The wave's tiles: coded tiles [0, nct) then reference tiles [nct, nt).
-  run_tiles<true, DCK, IdxT, SLDS, Q4>(p, sh, lds, t_beg, c1, n0, n1, n16, q4, qh, ql, sel, ia, ib, st);
-  {
+  run_tiles<true, DCK, IdxT, SLDS, Q4, SEL>(p, sh, lds, t_beg, c1, n0, n1, n16, q4, qh, ql, sel, ia, ib, st);
+  if (!SEL) {
     const int rt0 = max(t_beg, nct) - nct, rt1 = t_end - nct;
-    TileIdx ra = {0, 0, 0}, rb = {0, 0, 0};
+    TileIdx ra = {0, 0, 0, 0, 0, 0, 0}, rb = {0, 0, 0, 0, 0, 0, 0};
     if (rt0 < rt1) {
       load_idx<false, IdxT>(p, rt0, rt1, r0, r1, n16, q4, ra);
       load_idx<false, IdxT>(p, rt0 + 1, rt1, r0, r1, n16, q4, rb);
     }
-    run_tiles<false, DCK, IdxT, SLDS, Q4>(p, sh, lds, rt0, rt1, r0, r1, n16, q4, qh, ql, sel, ra, rb, st);
+    run_tiles<false, DCK, IdxT, SLDS, Q4, false>(p, sh, lds, rt0, rt1, r0, r1, n16, q4, qh, ql, sel, ra, rb, st);
   }
 
   // ---- merge the block's waves (fixed order) ----
@@ -695,21 +794,22 @@ size_t split_lds_bytes(const Shape& sh, bool slds) {
   return s > red ? s : red;
 }
 
-template <int DCK, typename IdxT, bool SLDS>
+template <int DCK, typename IdxT, bool SLDS, bool SEL>
 hipError_t launch_split(const Shape& sh, const DecodeArgs& a, hipStream_t st, dim3 grid) {
   // gfx950 gives a workgroup up to 160 KB of LDS; dynamic sizes above 64 KB
-  // need no opt-in attribute on this runtime.  4-bit codes: d_c <= 32 only.
+  // need no opt-in attribute on this runtime.  4-bit codes and token lists:
+  // d_c <= 32 only.
   if (DCK == 1 && sh.q4)
-    return launch_lds(k_split_mfma<1, IdxT, SLDS, true>, grid, kThreads, split_lds_bytes(sh, SLDS), st,
+    return launch_lds(k_split_mfma<1, IdxT, SLDS, true, SEL>, grid, kThreads, split_lds_bytes(sh, SLDS), st,
                       ev_start(a.events, 1), ev_stop(a.events, 1), a, sh);
-  return launch_lds(k_split_mfma<DCK, IdxT, SLDS, false>, grid, kThreads, split_lds_bytes(sh, SLDS), st,
-                    ev_start(a.events, 1), ev_stop(a.events, 1), a, sh);
+  return launch_lds(k_split_mfma<DCK, IdxT, SLDS, false, SEL && DCK == 1>, grid, kThreads,
+                    split_lds_bytes(sh, SLDS), st, ev_start(a.events, 1), ev_stop(a.events, 1), a, sh);
 }
 
-template <int DCK, typename IdxT>
+template <int DCK, typename IdxT, bool SEL = false>
 hipError_t launch_split_s(const Shape& sh, const DecodeArgs& a, hipStream_t st, dim3 grid) {
-  return split_lds_bytes(sh, true) <= kSplitLdsMax ? launch_split<DCK, IdxT, true>(sh, a, st, grid)
-                                                   : launch_split<DCK, IdxT, false>(sh, a, st, grid);
+  return split_lds_bytes(sh, true) <= kSplitLdsMax ? launch_split<DCK, IdxT, true, SEL>(sh, a, st, grid)
+                                                   : launch_split<DCK, IdxT, false, SEL>(sh, a, st, grid);
 }
 
 }  // namespace
@@ -720,6 +820,10 @@ bool mfma_side_kernels_supported(const Shape& sh, int G, int splits) {
 
 bool decode_fused_supported(const Shape& sh, int G, int splits) {
   return (!sh.q4 || sh.dc <= 32) && sh.K == 1 && mfma_side_kernels_supported(sh, G, splits);
+}
+
+bool decode_sel_fused_supported(const Shape& sh, int G, int splits) {
+  return sh.dc <= 32 && decode_fused_supported(sh, G, splits);
 }
 
 // The split kernel holds one 512-thread block per CU: about 256 blocks over
@@ -756,6 +860,17 @@ hipError_t launch_decode_fused(const Shape& sh, const DecodeArgs& a, hipStream_t
     e = i16 ? launch_split_s<1, uint16_t>(sh, a, st, grid) : launch_split_s<1, uint32_t>(sh, a, st, grid);
   else
     e = i16 ? launch_split_s<2, uint16_t>(sh, a, st, grid) : launch_split_s<2, uint32_t>(sh, a, st, grid);
+  if (e != hipSuccess) return e;
+  return launch(k_combine, dim3(BH8 * a.G), 256, st, ev_start(a.events, 2), ev_stop(a.events, 2), a, sh);
+}
+
+hipError_t launch_decode_sel_fused(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
+  const int BH8 = 8 * ((sh.B * sh.H + 7) / 8);
+  hipError_t e = launch_refscore_mfma(sh, a, st);
+  if (e != hipSuccess) return e;
+  const dim3 grid(BH8 * a.splits);
+  e = sh.idx_bytes == 2 ? launch_split_s<1, uint16_t, true>(sh, a, st, grid)
+                        : launch_split_s<1, uint32_t, true>(sh, a, st, grid);
   if (e != hipSuccess) return e;
   return launch(k_combine, dim3(BH8 * a.G), 256, st, ev_start(a.events, 2), ev_stop(a.events, 2), a, sh);
 }

@@ -90,6 +90,8 @@ inline size_t decode_ws_bytes(const Shape& sh, int G, int splits) {
 // query heads per KV head, code dim up to 48, at most kMfmaMaxSplits splits.
 constexpr int kMfmaMaxSplits = 256;
 bool decode_fused_supported(const Shape& sh, int G, int splits);
+// The same path over a token list (d_c <= 32).
+bool decode_sel_fused_supported(const Shape& sh, int G, int splits);
 // The MFMA reference-score and combine kernels alone (any code format).
 bool mfma_side_kernels_supported(const Shape& sh, int G, int splits);
 int decode_fused_auto_splits(const Shape& sh);
@@ -185,6 +187,7 @@ hipError_t launch_compress(const Shape& sh, const CompressArgs& a, hipStream_t s
 hipError_t launch_append(const Shape& sh, const AppendArgs& a, void* ws, hipStream_t st);
 hipError_t launch_decode(const Shape& sh, const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_fused(const Shape& sh, const DecodeArgs& a, hipStream_t st);
+hipError_t launch_decode_sel_fused(const Shape& sh, const DecodeArgs& a, hipStream_t st);
 // Decode over a token list (a.sel): reference scores, the list's split, combine.
 hipError_t launch_decode_sel(const Shape& sh, const DecodeArgs& a, hipStream_t st);
 // The MFMA reference-score kernel alone (shapes decode_fused_supported accepts).

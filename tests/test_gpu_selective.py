@@ -23,6 +23,8 @@ CASES = {
                                              code_dim=64, stride=5, batch=2),
     "bf16_g16_full_code_s2": BASE.replace(name="sel_d", stride=2, code_dim=128, seq_len=900, n_kv_heads=1,
                                           n_q_heads=16, batch=2),
+    # Stride 1: every position is a reference and the layout holds no coded rows.
+    "bf16_mfma_shape_s1": BASE.replace(name="sel_e", stride=1, seq_len=300, n_kv_heads=1, n_q_heads=4, batch=2),
 }
 
 
