@@ -160,6 +160,9 @@ struct TileIdx {
   // instead of raw when use_alt), and the code rows of the lane's key-code
   // and value-code tokens (-1: zero row).
   int alt, use_alt, rb, rc;
+  // k references per token (KT > 1): the lane's token's ordinals 1 .. KT - 1
+  // (ordinal 0 is raw).
+  int rk[kTopMax];
 };
 
 struct Tile {
@@ -173,6 +176,12 @@ struct Tile {
   uint32_t scl;    // 4-bit codes: bits of the key scale of token n16
   uint32_t sclv;   // 4-bit codes: bits of the value scale of the token of cvq
   int cnt;
+  // k references per token (KT > 1): value ordinals 1 .. KT - 1 of the lane's
+  // broadcast token, the reference counts of tokens 4 q4 + j (4 bits each),
+  // and their reciprocals.
+  int rk[kTopMax];
+  uint32_t cnt4;
+  float invc[4];
 };
 
 struct Args {
@@ -210,9 +219,9 @@ __device__ __forceinline__ int row_bcast(int v) {
 // Tile tt of a run [t0, t1) of 16-token tiles starting at token `first`
 // and ending at token `last` (exclusive).  Tiles past t1 are dead: they
 // repeat the run's last tile with cnt = 0.
-template <bool CODED, typename IdxT>
+template <bool CODED, typename IdxT, int KT = 1>
 __device__ __forceinline__ void load_idx(const Args& p, int tt, int t1, int first, int last, int n16, int q4,
-                                         TileIdx& ti) {
+                                         TileIdx& ti, int K = 1) {
   const bool live = tt < t1;
   tt = min(tt, t1 - 1);
   const int base = first + tt * 16;
@@ -220,7 +229,13 @@ __device__ __forceinline__ void load_idx(const Args& p, int tt, int t1, int firs
   ti.base = base;
   ti.cnt = live ? cnt : 0;
   const int u = base + min(q4 * 4 + (n16 & 3), cnt - 1);
-  if (CODED) {
+  if (CODED && KT > 1) {
+    // Rows of K ordinals; slots past K repeat the last one (never used).
+    const IdxT* src = (const IdxT*)(n16 < 4 ? p.idxK : p.idxV) + (size_t)u * K;
+    ti.raw = (int)src[0];
+#pragma unroll
+    for (int k = 1; k < KT; ++k) ti.rk[k] = (int)src[min(k, K - 1)];
+  } else if (CODED) {
     const IdxT* src = (const IdxT*)(n16 < 4 ? p.idxK : p.idxV);
     ti.raw = (int)src[u];
   } else {
@@ -264,13 +279,13 @@ __device__ __forceinline__ void load_idx_sel(const Args& p, const Shape& sh, int
   ti.base = 0;
 }
 
-template <bool CODED, bool SEL, typename IdxT>
+template <bool CODED, bool SEL, typename IdxT, int KT = 1>
 __device__ __forceinline__ void load_tile_idx(const Args& p, const Shape& sh, int tt, int t1, int first, int last,
                                               int n16, int q4, TileIdx& ti) {
   if constexpr (SEL)
     load_idx_sel<IdxT>(p, sh, tt, t1, first, last, n16, q4, ti);
   else
-    load_idx<CODED, IdxT>(p, tt, t1, first, last, n16, q4, ti);
+    load_idx<CODED, IdxT, KT>(p, tt, t1, first, last, n16, q4, ti, sh.K);
 }
 
 template <int I, bool SLDS>
@@ -279,7 +294,7 @@ __device__ __forceinline__ float s_lookup(const Args& p, const float* s_lds, int
   return SLDS ? s_lds[rk * 4 + gl] : ldg<float>(p.score, (rk * 4 + gl) * 4u);
 }
 
-template <bool CODED, int DCK, bool SLDS, bool Q4, bool SEL = false>
+template <bool CODED, int DCK, bool SLDS, bool Q4, bool SEL = false, int KT = 1>
 __device__ __forceinline__ void load_data(const Args& p, const Shape& sh, const float* s_lds, const TileIdx& ti,
                                           int n16, int q4, Tile& td) {
   const int dc = sh.dc;
@@ -292,6 +307,37 @@ __device__ __forceinline__ void load_data(const Args& p, const Shape& sh, const 
   td.sb[1] = s_lookup<1, SLDS>(p, s_lds, raw, sh.R, gl);
   td.sb[2] = s_lookup<2, SLDS>(p, s_lds, raw, sh.R, gl);
   td.sb[3] = s_lookup<3, SLDS>(p, s_lds, raw, sh.R, gl);
+  if constexpr (CODED && KT > 1) {
+    // Token 4 q4 + j (coded row n) averages cnt = min(K, n / (s - 1) + 1)
+    // references: its position t has t / s = n / (s - 1) earlier references
+    // besides its own block's.  The key score takes the mean of their S rows.
+    const int s1 = sh.s - 1;
+    uint32_t cnt4 = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = ti.base + q4 * 4 + j;
+      int c = 1;
+#pragma unroll
+      for (int k = 1; k < KT; ++k) c += (k < sh.K && n >= k * s1) ? 1 : 0;
+      cnt4 |= (uint32_t)c << (4 * j);
+      td.invc[j] = 1.0f / (float)c;
+    }
+    td.cnt4 = cnt4;
+#pragma unroll
+    for (int k = 1; k < KT; ++k) {
+      td.rk[k] = ti.rk[k];
+      const float s0 = s_lookup<0, SLDS>(p, s_lds, ti.rk[k], sh.R, gl);
+      const float s1v = s_lookup<1, SLDS>(p, s_lds, ti.rk[k], sh.R, gl);
+      const float s2 = s_lookup<2, SLDS>(p, s_lds, ti.rk[k], sh.R, gl);
+      const float s3 = s_lookup<3, SLDS>(p, s_lds, ti.rk[k], sh.R, gl);
+      td.sb[0] += k < (int)(cnt4 & 15u) ? s0 : 0.f;
+      td.sb[1] += k < (int)((cnt4 >> 4) & 15u) ? s1v : 0.f;
+      td.sb[2] += k < (int)((cnt4 >> 8) & 15u) ? s2 : 0.f;
+      td.sb[3] += k < (int)((cnt4 >> 12) & 15u) ? s3 : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) td.sb[j] *= td.invc[j];
+  }
   const uint32_t rv0 = (uint32_t)min(row_bcast<4>(raw), sh.R - 1);
   const uint32_t rv1 = (uint32_t)min(row_bcast<5>(raw), sh.R - 1);
   const uint32_t rv2 = (uint32_t)min(row_bcast<6>(raw), sh.R - 1);
@@ -425,9 +471,25 @@ __device__ __forceinline__ uint32_t q4_pair_bf16(uint32_t w, int j) {
   return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
 }
 
-template <bool CODED, int DCK, bool Q4, bool SEL = false>
+// k references per token: value rows of reference slot k of the tile's
+// tokens 4 q4 + 2 G2 + {0, 1}, as the B operands of group G2 (a slot past a
+// token's count reads the zero row).
+template <int G2>
+__device__ __forceinline__ void gather_refs(const Args& p, int R, const Tile& td, int k, int n16, Frag* x) {
+  const int ca = (int)((td.cnt4 >> (8 * G2)) & 15u), cb = (int)((td.cnt4 >> (8 * G2 + 4)) & 15u);
+  const int rw = k == 0 ? 0 : td.rk[k];
+  const uint32_t ra = (uint32_t)min(row_bcast<4 + 2 * G2>(rw), R - 1);
+  const uint32_t rb = (uint32_t)min(row_bcast<5 + 2 * G2>(rw), R - 1);
+  const bool va = k < ca, vb = k < cb;
+  const Frag a = ldg<Frag>(va ? (const void*)p.refsV : (const void*)kZeroCodes, va ? (ra * kD + n16 * 8) * 2u : n16 * 16u);
+  const Frag b = ldg<Frag>(vb ? (const void*)p.refsV : (const void*)kZeroCodes, vb ? (rb * kD + n16 * 8) * 2u : n16 * 16u);
+  x[0] = Frag{a.x, a.y, b.x, b.y};
+  x[1] = Frag{a.z, a.w, b.z, b.w};
+}
+
+template <bool CODED, int DCK, bool Q4, bool SEL = false, int KT = 1>
 __device__ __forceinline__ void compute_tile(const Tile& td, const Frag* qh, const Frag* ql, int n16, int q4, int dc,
-                                             const uint32_t* sel, State& st) {
+                                             const uint32_t* sel, State& st, const Args& pa, int R) {
   float s[4] = {td.sb[0], td.sb[1], td.sb[2], td.sb[3]};
   if (CODED && Q4) {
     // Key codes: integer values as the A operand, the token's scale applied
@@ -494,6 +556,8 @@ __device__ __forceinline__ void compute_tile(const Tile& td, const Frag* qh, con
   const uint32_t h01 = pk_bf16(p[0], p[1]), h23 = pk_bf16(p[2], p[3]);
   const uint32_t l01 = pk_bf16(p[0] - __uint_as_float(h01 << 16), p[1] - __uint_as_float(h01 & 0xFFFF0000u));
   const uint32_t l23 = pk_bf16(p[2] - __uint_as_float(h23 << 16), p[3] - __uint_as_float(h23 & 0xFFFF0000u));
+  constexpr bool MK = CODED && KT > 1;
+  Frag ahk[2], alk[2];   // MK: A operands of the weights p / cnt (reference part)
 #pragma unroll
   for (int g2 = 0; g2 < 2; ++g2) {
     const uint32_t hp = g2 ? h23 : h01, lp = g2 ? l23 : l01;
@@ -501,13 +565,57 @@ __device__ __forceinline__ void compute_tile(const Tile& td, const Frag* qh, con
                          __builtin_amdgcn_perm(hp, hp, sel[2]), __builtin_amdgcn_perm(hp, hp, sel[3])};
     const Frag al = Frag{__builtin_amdgcn_perm(lp, lp, sel[0]), __builtin_amdgcn_perm(lp, lp, sel[1]),
                          __builtin_amdgcn_perm(lp, lp, sel[2]), __builtin_amdgcn_perm(lp, lp, sel[3])};
-    st.accr[0] = mfma16(ah, td.xv[g2][0], st.accr[0]);
-    st.accr[0] = mfma16(al, td.xv[g2][0], st.accr[0]);
-    st.accr[1] = mfma16(ah, td.xv[g2][1], st.accr[1]);
-    st.accr[1] = mfma16(al, td.xv[g2][1], st.accr[1]);
+    if constexpr (!MK) {
+      st.accr[0] = mfma16(ah, td.xv[g2][0], st.accr[0]);
+      st.accr[0] = mfma16(al, td.xv[g2][0], st.accr[0]);
+      st.accr[1] = mfma16(ah, td.xv[g2][1], st.accr[1]);
+      st.accr[1] = mfma16(al, td.xv[g2][1], st.accr[1]);
+    }
     st.accc = mfma16(ah, bc[g2], st.accc);
     st.accc = mfma16(al, bc[g2], st.accc);
     if (CODED && Q4) st.accc = mfma16(ah, bl[g2], st.accc);
+  }
+  if constexpr (MK) {
+    // The reference part averages each token's references: weights p / cnt,
+    // one pass of value-reference MFMAs per reference slot, the next slot's
+    // rows gathered before the current slot's products.
+    float q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = p[i] * td.invc[i];
+    const uint32_t k01 = pk_bf16(q[0], q[1]), k23 = pk_bf16(q[2], q[3]);
+    const uint32_t m01 = pk_bf16(q[0] - __uint_as_float(k01 << 16), q[1] - __uint_as_float(k01 & 0xFFFF0000u));
+    const uint32_t m23 = pk_bf16(q[2] - __uint_as_float(k23 << 16), q[3] - __uint_as_float(k23 & 0xFFFF0000u));
+#pragma unroll
+    for (int g2 = 0; g2 < 2; ++g2) {
+      const uint32_t hp = g2 ? k23 : k01, lp = g2 ? m23 : m01;
+      ahk[g2] = Frag{__builtin_amdgcn_perm(hp, hp, sel[0]), __builtin_amdgcn_perm(hp, hp, sel[1]),
+                     __builtin_amdgcn_perm(hp, hp, sel[2]), __builtin_amdgcn_perm(hp, hp, sel[3])};
+      alk[g2] = Frag{__builtin_amdgcn_perm(lp, lp, sel[0]), __builtin_amdgcn_perm(lp, lp, sel[1]),
+                     __builtin_amdgcn_perm(lp, lp, sel[2]), __builtin_amdgcn_perm(lp, lp, sel[3])};
+    }
+    Frag cur[2][2] = {{td.xv[0][0], td.xv[0][1]}, {td.xv[1][0], td.xv[1][1]}};
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+      Frag nxt[2][2];
+      if (k + 1 < KT) {
+        gather_refs<0>(pa, R, td, k + 1, n16, nxt[0]);
+        gather_refs<1>(pa, R, td, k + 1, n16, nxt[1]);
+      }
+#pragma unroll
+      for (int g2 = 0; g2 < 2; ++g2) {
+        st.accr[0] = mfma16(ahk[g2], cur[g2][0], st.accr[0]);
+        st.accr[0] = mfma16(alk[g2], cur[g2][0], st.accr[0]);
+        st.accr[1] = mfma16(ahk[g2], cur[g2][1], st.accr[1]);
+        st.accr[1] = mfma16(alk[g2], cur[g2][1], st.accr[1]);
+      }
+      if (k + 1 < KT) {
+#pragma unroll
+        for (int g2 = 0; g2 < 2; ++g2) {
+          cur[g2][0] = nxt[g2][0];
+          cur[g2][1] = nxt[g2][1];
+        }
+      }
+    }
   }
 }
 
@@ -517,23 +625,23 @@ __device__ __forceinline__ void compute_tile(const Tile& td, const Frag* qh, con
 // compiler from hoisting a tile's arithmetic above the next tile's loads.
 // The ordinals of the first two tiles (ia, ib) come from the caller, which
 // issues them early.
-template <bool CODED, int DCK, typename IdxT, bool SLDS, bool Q4, bool SEL>
+template <bool CODED, int DCK, typename IdxT, bool SLDS, bool Q4, bool SEL, int KT = 1>
 __device__ __forceinline__ void run_tiles(const Args& p, const Shape& sh, const float* s_lds, int t0, int t1,
                                           int first, int last, int n16, int q4, const Frag* qh, const Frag* ql,
                                           const uint32_t* sel, TileIdx ia, TileIdx ib, State& st) {
   if (t0 >= t1) return;
   Tile da, db;
-  load_data<CODED, DCK, SLDS, Q4, SEL>(p, sh, s_lds, ia, n16, q4, da);
+  load_data<CODED, DCK, SLDS, Q4, SEL, KT>(p, sh, s_lds, ia, n16, q4, da);
   for (int tt = t0; tt < t1; tt += 2) {
-    load_tile_idx<CODED, SEL, IdxT>(p, sh, tt + 2, t1, first, last, n16, q4, ia);
-    load_data<CODED, DCK, SLDS, Q4, SEL>(p, sh, s_lds, ib, n16, q4, db);
+    load_tile_idx<CODED, SEL, IdxT, KT>(p, sh, tt + 2, t1, first, last, n16, q4, ia);
+    load_data<CODED, DCK, SLDS, Q4, SEL, KT>(p, sh, s_lds, ib, n16, q4, db);
     __builtin_amdgcn_sched_barrier(0);
-    compute_tile<CODED, DCK, Q4, SEL>(da, qh, ql, n16, q4, sh.dc, sel, st);
+    compute_tile<CODED, DCK, Q4, SEL, KT>(da, qh, ql, n16, q4, sh.dc, sel, st, p, sh.R);
     __builtin_amdgcn_sched_barrier(0);
-    load_tile_idx<CODED, SEL, IdxT>(p, sh, tt + 3, t1, first, last, n16, q4, ib);
-    load_data<CODED, DCK, SLDS, Q4, SEL>(p, sh, s_lds, ia, n16, q4, da);
+    load_tile_idx<CODED, SEL, IdxT, KT>(p, sh, tt + 3, t1, first, last, n16, q4, ib);
+    load_data<CODED, DCK, SLDS, Q4, SEL, KT>(p, sh, s_lds, ia, n16, q4, da);
     __builtin_amdgcn_sched_barrier(0);
-    compute_tile<CODED, DCK, Q4, SEL>(db, qh, ql, n16, q4, sh.dc, sel, st);
+    compute_tile<CODED, DCK, Q4, SEL, KT>(db, qh, ql, n16, q4, sh.dc, sel, st, p, sh.R);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -547,7 +655,7 @@ __device__ __forceinline__ int split_lo(int n, int sp, int splits, int align) {
 // Dynamic LDS: the S table (SLDS) and, after the tile loop, the wave-merge
 // buffer in the same bytes.  SEL: the block's tiles are 16-entry runs of the
 // sequence's token list (a.sel) instead of coded rows and references.
-template <int DCK, typename IdxT, bool SLDS, bool Q4, bool SEL>
+template <int DCK, typename IdxT, bool SLDS, bool Q4, bool SEL, int KT = 1>
 __global__ __launch_bounds__(kThreads) void k_split_mfma(DecodeArgs a, Shape sh) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   __shared__ float red_m[kWaves][4];
@@ -573,8 +681,8 @@ __global__ __launch_bounds__(kThreads) void k_split_mfma(DecodeArgs a, Shape sh)
   p.refsV = (const uint16_t*)a.refs + sV * sh.Rc * kD;
   p.codesK = (const uint16_t*)a.codes + sK * sh.Nc * dc;
   p.codesV = (const uint16_t*)a.codes + sV * sh.Nc * dc;
-  p.idxK = (const IdxT*)a.idx + sK * sh.Nc;
-  p.idxV = (const IdxT*)a.idx + sV * sh.Nc;
+  p.idxK = (const IdxT*)a.idx + sK * sh.Nc * sh.K;   // rows of K ordinals
+  p.idxV = (const IdxT*)a.idx + sV * sh.Nc * sh.K;
   p.score = a.score + (size_t)bh * sh.R * 4;
   p.qK = (const uint8_t*)a.codes + sK * sh.Nc * (dc / 2);
   p.qV = (const uint8_t*)a.codes + sV * sh.Nc * (dc / 2);
@@ -588,8 +696,8 @@ __global__ __launch_bounds__(kThreads) void k_split_mfma(DecodeArgs a, Shape sh)
   const int c1 = min(t_end, nct);
   TileIdx ia = {0, 0, 0, 0, 0, 0, 0}, ib = {0, 0, 0, 0, 0, 0, 0};
   if (t_beg < c1) {
-    load_tile_idx<true, SEL, IdxT>(p, sh, t_beg, c1, n0, n1, n16, q4, ia);
-    load_tile_idx<true, SEL, IdxT>(p, sh, t_beg + 1, c1, n0, n1, n16, q4, ib);
+    load_tile_idx<true, SEL, IdxT, KT>(p, sh, t_beg, c1, n0, n1, n16, q4, ia);
+    load_tile_idx<true, SEL, IdxT, KT>(p, sh, t_beg + 1, c1, n0, n1, n16, q4, ib);
   }
   // The head's S table into LDS, four rows per thread in flight at once.
   if (SLDS) {
@@ -648,7 +756,7 @@ __global__ __launch_bounds__(kThreads) void k_split_mfma(DecodeArgs a, Shape sh)
   st.m = SEL ? -3.0e38f : -INFINITY;
   st.accr[0] = st.accr[1] = st.accc = f32x4{0.f, 0.f, 0.f, 0.f};
   // The wave's tiles: coded tiles [0, nct) then reference tiles [nct, nt).
-  run_tiles<true, DCK, IdxT, SLDS, Q4, SEL>(p, sh, lds, t_beg, c1, n0, n1, n16, q4, qh, ql, sel, ia, ib, st);
+  run_tiles<true, DCK, IdxT, SLDS, Q4, SEL, KT>(p, sh, lds, t_beg, c1, n0, n1, n16, q4, qh, ql, sel, ia, ib, st);
   if (!SEL) {
     const int rt0 = max(t_beg, nct) - nct, rt1 = t_end - nct;
     TileIdx ra = {0, 0, 0, 0, 0, 0, 0}, rb = {0, 0, 0, 0, 0, 0, 0};
@@ -812,6 +920,24 @@ hipError_t launch_split_s(const Shape& sh, const DecodeArgs& a, hipStream_t st, 
                                                    : launch_split<DCK, IdxT, false, SEL>(sh, a, st, grid);
 }
 
+// k references per token (storage-dtype codes, d_c <= 32): KT = 4 serves
+// k <= 4, KT = 8 the rest.
+template <typename IdxT, bool SLDS>
+hipError_t launch_split_topk(const Shape& sh, const DecodeArgs& a, hipStream_t st, dim3 grid) {
+  const size_t lds = split_lds_bytes(sh, SLDS);
+  if (sh.K <= 4)
+    return launch_lds(k_split_mfma<1, IdxT, SLDS, false, false, 4>, grid, kThreads, lds, st, ev_start(a.events, 1),
+                      ev_stop(a.events, 1), a, sh);
+  return launch_lds(k_split_mfma<1, IdxT, SLDS, false, false, 8>, grid, kThreads, lds, st, ev_start(a.events, 1),
+                    ev_stop(a.events, 1), a, sh);
+}
+
+template <typename IdxT>
+hipError_t launch_split_topk_s(const Shape& sh, const DecodeArgs& a, hipStream_t st, dim3 grid) {
+  return split_lds_bytes(sh, true) <= kSplitLdsMax ? launch_split_topk<IdxT, true>(sh, a, st, grid)
+                                                   : launch_split_topk<IdxT, false>(sh, a, st, grid);
+}
+
 }  // namespace
 
 bool mfma_side_kernels_supported(const Shape& sh, int G, int splits) {
@@ -819,11 +945,12 @@ bool mfma_side_kernels_supported(const Shape& sh, int G, int splits) {
 }
 
 bool decode_fused_supported(const Shape& sh, int G, int splits) {
-  return (!sh.q4 || sh.dc <= 32) && sh.K == 1 && mfma_side_kernels_supported(sh, G, splits);
+  const bool codes_ok = sh.K == 1 ? (!sh.q4 || sh.dc <= 32) : (!sh.q4 && sh.dc <= 32);
+  return codes_ok && mfma_side_kernels_supported(sh, G, splits);
 }
 
 bool decode_sel_fused_supported(const Shape& sh, int G, int splits) {
-  return sh.dc <= 32 && decode_fused_supported(sh, G, splits);
+  return sh.K == 1 && sh.dc <= 32 && decode_fused_supported(sh, G, splits);
 }
 
 // The split kernel holds one 512-thread block per CU: about 256 blocks over
@@ -856,7 +983,9 @@ hipError_t launch_decode_fused(const Shape& sh, const DecodeArgs& a, hipStream_t
   if (e != hipSuccess) return e;
   const dim3 grid(BH8 * a.splits);
   const bool i16 = sh.idx_bytes == 2;
-  if (sh.dc <= 32)
+  if (sh.K > 1)
+    e = i16 ? launch_split_topk_s<uint16_t>(sh, a, st, grid) : launch_split_topk_s<uint32_t>(sh, a, st, grid);
+  else if (sh.dc <= 32)
     e = i16 ? launch_split_s<1, uint16_t>(sh, a, st, grid) : launch_split_s<1, uint32_t>(sh, a, st, grid);
   else
     e = i16 ? launch_split_s<2, uint16_t>(sh, a, st, grid) : launch_split_s<2, uint32_t>(sh, a, st, grid);

@@ -25,6 +25,10 @@ CASES = {
     "f32_k2_l2": (TINY.replace(name="tk_e", seq_len=1200, n_kv_heads=2, n_q_heads=4, head_dim=128, code_dim=32,
                                stride=5), 2, "l2", 0),
     "bf16_k8_cos_q4": (BASE.replace(name="tk_f", seq_len=1800, n_kv_heads=1, n_q_heads=4, stride=4), 8, "cos", 4),
+    # k > 4 with storage-dtype codes (decode tiles for up to 8 references); stride 3 gives many early tokens
+    # with fewer than k earlier references.
+    "bf16_k8_l2_s3": (BASE.replace(name="tk_g", seq_len=1300, n_kv_heads=1, n_q_heads=4, stride=3), 8, "l2", 0),
+    "bf16_k5_cos_b2": (BASE.replace(name="tk_h", seq_len=2500, n_kv_heads=2, n_q_heads=8, batch=2), 5, "cos", 0),
 }
 
 
