@@ -169,7 +169,9 @@ __global__ __launch_bounds__(256) void k_center_refs(CompressArgs a, Shape sh) {
     n2 += f * f;
   }
   n2 = wave_sum(n2);
-  if (lane == 0) a.inv_n[(size_t)stream * sh.R + r] = n2 > 0.f ? 1.0f / sqrtf(n2) : 0.0f;
+  // Norm term of the search: 1 / ||r|| (cosine; 0 for a zero reference) or
+  // ||r||^2 (L2).
+  if (lane == 0) a.inv_n[(size_t)stream * sh.R + r] = sh.l2 ? n2 : n2 > 0.f ? 1.0f / sqrtf(n2) : 0.0f;
 }
 
 // ---------------------------------------------------------------------------
@@ -449,111 +451,168 @@ __global__ __launch_bounds__(256) void k_search_f32(CompressArgs a, Shape sh) {
 // 2 dot - ||r||^2 (= ||x||^2 - ||x - r||^2, the token's norm being common).
 // ---------------------------------------------------------------------------
 
-// bfloat16: 64 coded rows per block, 16 per wave.  A = 16 reference rows
-// (lane n16 holds row n16, dims 8 q4 ..), B = the wave's 16 tokens, so lane
-// (n16, q4) gets the dots of references 4 q4 + i with token n16; the
-// reference norms come from the A fragments themselves.  The next tile's
-// rows are loaded while the current one is scored.  Insertion runs only
-// when some lane of the wave has a candidate that beats its k-th best.
-template <int D>
-__global__ __launch_bounds__(256) void k_search_topk_mfma(CompressArgs a, Shape sh) {
+// bfloat16: the block and chunk structure of k_search_mfma (256 positions
+// per block, two 16-token MFMA tiles per wave, references staged through LDS
+// in double-buffered chunks of 64 with their norm terms), with a sorted list
+// of the best k per lane and token tile in place of the running maximum.
+// The norm term of a reference is 1 / ||r|| (cosine) or ||r||^2 (L2), written
+// by k_center_refs.  A candidate costs one multiply or FMA and a comparison
+// with the lane's k-th score (cached, refreshed after insertions; a tie passes
+// the test and the insertion applies the exact order); insertion runs, per
+// candidate slot, only when some lane of the wave has a candidate that
+// passes.  Lists hold KT >= k entries (4 or 8).  At the end the four lane
+// groups of a token merge their lists and lane group 0 writes the ordinals.
+template <int D, int KT>
+__global__ __launch_bounds__(kSearchThreads) void k_search_topk_mfma(CompressArgs a, Shape sh) {
   constexpr int KS = D / 32;
-  typedef uint32_t Frag __attribute__((ext_vector_type(4)));
+  constexpr int LDR = D + 8;
+  constexpr int PER = kSearchRefs * (D / 8) / kSearchThreads;
+  __shared__ __attribute__((aligned(16))) uint16_t lds_ref[2][kSearchRefs * LDR];
+  __shared__ float lds_nrm[2][kSearchRefs];
+
   const XcdItem xi = xcd_item(sh.n_streams());
   if (xi.stream < 0) return;
   const int stream = xi.stream;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int n16 = lane & 15, q4 = lane >> 4;
+  const int tile = (sh.T + kSearchTok - 1) / kSearchTok - 1 - xi.item;   // heavy (late) tiles first
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int lrow = lane & 15, lgrp = lane >> 4;
   const int K = sh.K;
+  const bool l2 = sh.l2 != 0;
   const StreamId id = decode_stream(stream, sh.H);
   const uint16_t* src = stream_src<BF16>(a, id);
   const uint16_t* mu = (const uint16_t*)a.mu + (size_t)stream * D;
   const uint16_t* refs = (const uint16_t*)a.refs + (size_t)stream * sh.Rc * D;
+  const float* nrm = a.inv_n + (size_t)stream * sh.R;
 
-  const int nbase = xi.item * 64 + wave * 16;
-  if (nbase >= sh.N) return;
-  const int n = nbase + n16;
-  const bool valid = n < sh.N;
-  const int t = valid ? slot_to_pos(n, sh.s) : 0;
-  const int tmax = slot_to_pos(min(nbase + 15, sh.N - 1), sh.s);
-  const int nref = (tmax - 1) / sh.s + 1;   // references any token of the wave may use
+  const int tb = tile * kSearchTok;
+  const int tw = tb + wave * 16 * kSearchNT;
+  const int tmax_b = min(sh.T - 1, tb + kSearchTok - 1);
+  const int rend_b = (tmax_b + sh.s - 1) / sh.s;
+  const int tmax_w = min(sh.T - 1, tw + 16 * kSearchNT - 1);
+  const int rend_w = tw < sh.T ? (tmax_w + sh.s - 1) / sh.s : 0;
+  const int nchunks = (rend_b + kSearchRefs - 1) / kSearchRefs;
 
-  Frag bt[KS];
+  uint4 pre[PER];
+  float pn = 0.f;
+  auto fetch = [&](int ch) {
+    const int rc = ch * kSearchRefs;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int q = tid + j * kSearchThreads;
+      const int row = q / (D / 8), col = (q % (D / 8)) * 8;
+      pre[j] = rc + row < rend_b ? *reinterpret_cast<const uint4*>(refs + (size_t)(rc + row) * D + col)
+                                 : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < kSearchRefs) pn = rc + tid < rend_b ? nrm[rc + tid] : 0.f;
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int q = tid + j * kSearchThreads;
+      const int row = q / (D / 8), col = (q % (D / 8)) * 8;
+      *reinterpret_cast<uint4*>(&lds_ref[buf][row * LDR + col]) = pre[j];
+    }
+    if (tid < kSearchRefs) lds_nrm[buf][tid] = pn;
+  };
+  if (nchunks > 0) fetch(0);
+
+  // B operands: the centred tokens rnd(x - mu), as in k_search_mfma.
+  bf16x8 bt[kSearchNT][KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    const int c = ks * 32 + q4 * 8;
-    float x[8], m[8];
-    load8(src + (int64_t)t * a.st + c, x);
+    const int c = ks * 32 + lgrp * 8;
+    float m[8];
     load8(mu + c, m);
-    uint32_t w[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = valid ? ((uint32_t)f2bf(x[2 * e] - m[2 * e]) | ((uint32_t)f2bf(x[2 * e + 1] - m[2 * e + 1]) << 16)) : 0u;
-    bt[ks] = Frag{w[0], w[1], w[2], w[3]};
+    for (int nt = 0; nt < kSearchNT; ++nt) {
+      const int t = tw + nt * 16 + lrow;
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+      if (t < sh.T) {
+        float x[8];
+        load8(src + (int64_t)t * a.st + c, x);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = pk_bf16_rn(x[2 * e] - m[2 * e], x[2 * e + 1] - m[2 * e + 1]);
+      }
+      bt[nt][ks] = __builtin_bit_cast(bf16x8, w);
+    }
   }
 
-  TopK top;
-  top.init();
-  Frag ar[KS], an[KS];
-  {
-    const int rr = min(n16, nref - 1);
+  TopKN<KT> top[kSearchNT];
+  float ths[kSearchNT];
+  int thr[kSearchNT];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) ar[ks] = *(const Frag*)(refs + (size_t)rr * D + ks * 32 + q4 * 8);
+  for (int nt = 0; nt < kSearchNT; ++nt) {
+    top[nt].init();
+    top[nt].kth(K, ths[nt], thr[nt]);
   }
-  for (int r0 = 0; r0 < nref; r0 += 16) {
-    const int rn = min(r0 + 16 + n16, nref - 1);
+
+  if (nchunks > 0) stash(0);
+  __syncthreads();
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int rc = ch * kSearchRefs;
+    const int buf = ch & 1;
+    if (ch + 1 < nchunks) fetch(ch + 1);
+    if (rc < rend_w) {
+      const int nmt = min(kSearchRefs / 16, (rend_w - rc + 15) / 16);
+      for (int mt = 0; mt < nmt; ++mt) {
+        const int rbase = rc + mt * 16;
+        bf16x8 ar[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) an[ks] = *(const Frag*)(refs + (size_t)rn * D + ks * 32 + q4 * 8);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float n2 = 0.f;
+        for (int ks = 0; ks < KS; ++ks)
+          ar[ks] = *reinterpret_cast<const bf16x8*>(&lds_ref[buf][(mt * 16 + lrow) * LDR + ks * 32 + lgrp * 8]);
+        f32x4 acc[kSearchNT];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ar[ks]), __builtin_bit_cast(bf16x8, bt[ks]),
-                                                    acc, 0, 0, 0);
+        for (int nt = 0; nt < kSearchNT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lo = __uint_as_float(ar[ks][e] << 16), hi = __uint_as_float(ar[ks][e] & 0xFFFF0000u);
-        n2 = fmaf(lo, lo, n2);
-        n2 = fmaf(hi, hi, n2);
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int nt = 0; nt < kSearchNT; ++nt)
+            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar[ks], bt[nt][ks], acc[nt], 0, 0, 0);
+        float nr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) nr[i] = lds_nrm[buf][mt * 16 + lgrp * 4 + i];
+        const int r0 = rbase + lgrp * 4;
+        const bool masked = (rbase + 15) * sh.s >= tw;
+#pragma unroll
+        for (int nt = 0; nt < kSearchNT; ++nt) {
+          const int t = tw + nt * 16 + lrow;
+          float v[4];
+          bool want[4];
+          (void)thr;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[i] = l2 ? fmaf(2.f, acc[nt][i], -nr[i]) : acc[nt][i] * nr[i];
+            const bool ok = !masked || ((r0 + i) * sh.s < t && t < sh.T);
+            want[i] = ok && v[i] >= ths[nt];
+          }
+          bool any = false;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (__ballot(want[i]) != 0ull) {
+              top[nt].insert(want[i] ? v[i] : -INFINITY, want[i] ? r0 + i : 0x7FFFFFFF, K);
+              any = true;
+            }
+          }
+          if (any) top[nt].kth(K, ths[nt], thr[nt]);
+        }
       }
     }
-    n2 += __shfl_xor(n2, 16, 64);
-    n2 += __shfl_xor(n2, 32, 64);   // every lane of row n16: ||refs[r0 + n16]||^2
-    float sc[4];
-    int rc[4];
-    bool want = false;
-    float ths;
-    int thr;
-    top.kth(K, ths, thr);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float nn = __shfl(n2, 4 * q4 + i, 64);
-      const int r = r0 + 4 * q4 + i;
-      float v;
-      if (sh.l2)
-        v = 2.f * acc[i] - nn;
-      else
-        v = nn > 0.f ? acc[i] / sqrtf(nn) : 0.f;
-      const bool ok = valid && r < nref && r * sh.s < t;
-      sc[i] = ok ? v : -INFINITY;
-      rc[i] = r;
-      want |= ok && ranks_before(v, r, ths, thr);
-    }
-    if (__ballot(want) != 0ull) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (sc[i] != -INFINITY) top.insert(sc[i], rc[i], K);
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) ar[ks] = an[ks];
+    if (ch + 1 < nchunks) stash(buf ^ 1);
+    __syncthreads();
   }
-  top.merge_xor(16, K);
-  top.merge_xor(32, K);
-  if (valid && q4 == 0) {
-    int o[kTopMax];
-    top.sorted_ordinals(min(K, t / sh.s + 1), o);
-    const size_t base = ((size_t)stream * sh.Nc + n) * K;
-    for (int j = 0; j < K; ++j) store_idx(a.idx, base + j, sh.idx_bytes, (uint32_t)o[j]);
+
+#pragma unroll
+  for (int nt = 0; nt < kSearchNT; ++nt) {
+    top[nt].merge_xor(16, K);
+    top[nt].merge_xor(32, K);
+    const int t = tw + nt * 16 + lrow;
+    if (lgrp == 0 && t < sh.T && t % sh.s != 0) {
+      int o[kTopMax];
+      top[nt].sorted_ordinals(min(K, t / sh.s + 1), o);
+      const size_t base = ((size_t)stream * sh.Nc + pos_to_slot(t, sh.s)) * K;
+      for (int j = 0; j < K; ++j) store_idx(a.idx, base + j, sh.idx_bytes, (uint32_t)o[j]);
+    }
   }
 }
 
@@ -814,8 +873,12 @@ hipError_t launch_compress_d(const Shape& sh, const CompressArgs& a, hipStream_t
     DKV_TRY(launch(k_center_refs<BF16>, g_ref, 256, st, ev_start(ev, 1), ev_stop(ev, 1), a, sh));
     if (sh.N > 0) {
       if (sh.topk_search()) {
-        DKV_TRY(launch(k_search_topk_mfma<D>, dim3(xcd_grid(ns, (sh.N + 63) / 64)), 256, st, ev_start(ev, 2),
-                       ev_stop(ev, 2), a, sh));
+        if (sh.K <= 4)
+          DKV_TRY(launch(k_search_topk_mfma<D, 4>, g_search, kSearchThreads, st, ev_start(ev, 2), ev_stop(ev, 2), a,
+                         sh));
+        else
+          DKV_TRY(launch(k_search_topk_mfma<D, 8>, g_search, kSearchThreads, st, ev_start(ev, 2), ev_stop(ev, 2), a,
+                         sh));
       } else {
         DKV_TRY(launch(k_search_mfma<D>, g_search, kSearchThreads, st, ev_start(ev, 2), ev_stop(ev, 2), a, sh));
       }

@@ -123,12 +123,13 @@ __device__ __forceinline__ bool ranks_before(float s1, int r1, float s2, int r2)
   return s1 > s2 || (s1 == s2 && r1 < r2);
 }
 
-struct TopK {
-  float s[kTopMax];
-  int r[kTopMax];
+template <int KM>
+struct TopKN {
+  float s[KM];
+  int r[KM];
   __device__ __forceinline__ void init() {
 #pragma unroll
-    for (int j = 0; j < kTopMax; ++j) {
+    for (int j = 0; j < KM; ++j) {
       s[j] = -INFINITY;
       r[j] = 0x7FFFFFFF;
     }
@@ -136,7 +137,7 @@ struct TopK {
   // Insertion by compare-and-swap down the list (branch-free).
   __device__ __forceinline__ void insert(float cs, int cr, int K) {
 #pragma unroll
-    for (int j = 0; j < kTopMax; ++j) {
+    for (int j = 0; j < KM; ++j) {
       if (j < K) {
         const bool take = ranks_before(cs, cr, s[j], r[j]);
         const float ts = s[j];
@@ -154,41 +155,42 @@ struct TopK {
     ks = s[0];
     kr = r[0];
 #pragma unroll
-    for (int j = 1; j < kTopMax; ++j) {
+    for (int j = 1; j < KM; ++j) {
       ks = j == K - 1 ? s[j] : ks;
       kr = j == K - 1 ? r[j] : kr;
     }
   }
   // Merge with the list of lane (lane ^ mask).
   __device__ __forceinline__ void merge_xor(int mask, int K) {
-    float os[kTopMax];
-    int orr[kTopMax];
+    float os[KM];
+    int orr[KM];
 #pragma unroll
-    for (int j = 0; j < kTopMax; ++j) {
+    for (int j = 0; j < KM; ++j) {
       os[j] = __shfl_xor(s[j], mask, 64);
       orr[j] = __shfl_xor(r[j], mask, 64);
     }
 #pragma unroll
-    for (int j = 0; j < kTopMax; ++j)
+    for (int j = 0; j < KM; ++j)
       if (j < K) insert(os[j], orr[j], K);
   }
   // The first c ordinals in ascending order (c <= K), zero after.
   __device__ __forceinline__ void sorted_ordinals(int c, int* out) const {
-    int v[kTopMax];
+    int v[KM];
 #pragma unroll
-    for (int j = 0; j < kTopMax; ++j) v[j] = j < c ? r[j] : 0x7FFFFFFF;
+    for (int j = 0; j < KM; ++j) v[j] = j < c ? r[j] : 0x7FFFFFFF;
 #pragma unroll
-    for (int i = 0; i < kTopMax; ++i)
+    for (int i = 0; i < KM; ++i)
 #pragma unroll
-      for (int j = 0; j + 1 < kTopMax - i; ++j) {
+      for (int j = 0; j + 1 < KM - i; ++j) {
         const int lo = min(v[j], v[j + 1]), hi = max(v[j], v[j + 1]);
         v[j] = lo;
         v[j + 1] = hi;
       }
 #pragma unroll
-    for (int j = 0; j < kTopMax; ++j) out[j] = j < c ? v[j] : 0;
+    for (int j = 0; j < KM; ++j) out[j] = j < c ? v[j] : 0;
   }
 };
+typedef TopKN<kTopMax> TopK;
 
 // ---------------------------------------------------------------------------
 // Wave64 reductions (butterfly; every lane ends with the result).
