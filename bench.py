@@ -651,6 +651,44 @@ def main():
 PREFILL_INPUT_LAYERS = 4   # distinct synthetic layers resident in HBM for the compress-only workload
 
 
+def causal_pairs(T: int, s: int) -> int:
+    """(token, earlier reference) pairs of one stream: the search's work."""
+    return sum(-(-t // s) for t in range(T) if t % s)
+
+
+def cpu_baseline_prefill(cfg, budget_s: float = 20.0) -> dict:
+    """Time the fp64 oracle's compress of the first K stream on the host, on
+    prefixes of doubling length until about 30% of the budget is spent, and
+    extrapolate to a whole stream by causal pairs (the search dominates);
+    tokens/s count each position once over all K and V streams of a layer."""
+    from threadpoolctl import threadpool_info
+
+    import kvsynth as K
+    import oracle as O
+
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    k = K.gen_stream(cfg, 0, 0, 0, 0).f64
+    w = K.gen_w(cfg, 0, 0)[1].f64
+    tp = min(2048, cfg.seq_len)
+    while True:
+        t0 = time.perf_counter()
+        O.compress_stream(k[:tp], cfg.stride, w, cfg.dtype)
+        dt = time.perf_counter() - t0
+        if dt > budget_s * 0.3 or tp >= cfg.seq_len:
+            break
+        tp = min(2 * tp, cfg.seq_len)
+    t_stream = dt * causal_pairs(cfg.seq_len, cfg.stride) / causal_pairs(tp, cfg.stride)
+    return {
+        "value": cfg.seq_len / (2 * cfg.n_kv_heads * cfg.batch * t_stream),
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle: compress of the first {tp} tokens of one K stream in {dt:.1f} s, "
+                   f"scaled by causal (token, reference) pairs to a {cfg.seq_len}-token stream and over the "
+                   f"{2 * cfg.n_kv_heads * cfg.batch} K and V streams of a layer"),
+    }
+
+
 def prefill(cfg, args, np, torch, K, D):
     """Compress-only workload (a prefill with no decode steps): one step is
     the compress of every layer of the configuration, graph-replayed over
@@ -738,8 +776,11 @@ def prefill(cfg, args, np, torch, K, D):
                      "achieved": round(search_flops / (st[2] * 1e-3) / 1e12, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(search_flops / (st[2] * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                      "traffic": None, "flops_per_launch": search_flops},
-        "cpu_baseline": None,
     }
+    log(f"[bench] gpu done: {json.dumps(res)}")
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host")
+        res["cpu_baseline"] = cpu_baseline_prefill(cfg, args.cpu_budget)
     print(json.dumps(res), flush=True)
 
 
