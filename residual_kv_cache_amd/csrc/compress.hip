@@ -306,9 +306,42 @@ __global__ __launch_bounds__(kSearchThreads) void k_search_mfma(CompressArgs a, 
     const int rc = ch * kSearchRefs;
     const int buf = ch & 1;
     if (ch + 1 < nchunks) fetch(ch + 1);
-    if (rc < rend_w) {
-      uint32_t ckey[kSearchNT] = {};
-      const int nmt = min(kSearchRefs / 16, (rend_w - rc + 15) / 16);
+    uint32_t ckey[kSearchNT] = {};
+    const int nmt = min(kSearchRefs / 16, (rend_w - rc + 15) / 16);
+    if (rc < rend_w && nmt == kSearchRefs / 16 && (rc + kSearchRefs - 1) * sh.s < tw) {
+      // Fast path: a full chunk entirely before the wave's first position
+      // needs no causal mask.  With no branch inside, the next tile's MFMAs
+      // are issued before this tile's keys are extracted, so the matrix
+      // core and the VALU work at the same time.
+      f32x4 acc[2][kSearchNT];
+      auto tile_mfma = [&](int mt, f32x4* out) {
+        bf16x8 ar[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          ar[ks] = *reinterpret_cast<const bf16x8*>(&lds_ref[buf][(mt * 16 + lrow) * LDR + ks * 32 + lgrp * 8]);
+#pragma unroll
+        for (int nt = 0; nt < kSearchNT; ++nt) out[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int nt = 0; nt < kSearchNT; ++nt)
+            out[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar[ks], bt[nt][ks], out[nt], 0, 0, 0);
+      };
+      tile_mfma(0, acc[0]);
+#pragma unroll
+      for (int mt = 0; mt < kSearchRefs / 16; ++mt) {
+        if (mt + 1 < kSearchRefs / 16) tile_mfma(mt + 1, acc[(mt + 1) & 1]);
+        const f32x4 inv4 = *reinterpret_cast<const f32x4*>(&lds_inv[buf][mt * 16 + lgrp * 4]);
+#pragma unroll
+        for (int nt = 0; nt < kSearchNT; ++nt) {
+          uint32_t k[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            k[i] = (__float_as_uint(fmaf(acc[mt & 1][nt][i], inv4[i], off[nt])) & ~15u) | (uint32_t)(15 - (4 * mt + i));
+          ckey[nt] = max(max(max(k[0], k[1]), max(k[2], k[3])), ckey[nt]);
+        }
+      }
+    } else if (rc < rend_w) {
 #pragma unroll
       for (int mt = 0; mt < kSearchRefs / 16; ++mt) {
         if (mt < nmt) {
@@ -347,12 +380,13 @@ __global__ __launch_bounds__(kSearchThreads) void k_search_mfma(CompressArgs a, 
           }
         }
       }
+    }
+    // A chunk without keys leaves ckey = 0, which never replaces the best.
 #pragma unroll
-      for (int nt = 0; nt < kSearchNT; ++nt) {
-        const bool g = (ckey[nt] & ~15u) > (bkey[nt] & ~15u);
-        bkey[nt] = g ? ckey[nt] : bkey[nt];
-        bch[nt] = g ? ch : bch[nt];
-      }
+    for (int nt = 0; nt < kSearchNT; ++nt) {
+      const bool g = (ckey[nt] & ~15u) > (bkey[nt] & ~15u);
+      bkey[nt] = g ? ckey[nt] : bkey[nt];
+      bch[nt] = g ? ch : bch[nt];
     }
     if (ch + 1 < nchunks) stash(buf ^ 1);
     __syncthreads();
