@@ -577,6 +577,15 @@ def main():
 
     eff = effective_decode_bytes(cfg)
     value = nsteps * eff / (decode_window_ms * 1e-3) / 1e9
+    # The library's choice of split kernel for this shape: the histogram form
+    # when a split holds at least four coded tokens per reference and its
+    # S table (or the 24 KB wave-merge buffer) and the 64-bit histogram fit
+    # in 159 KB of LDS.
+    n_refs = -(-cfg.seq_len // cfg.stride)
+    hist = (mfma_shape and cfg.code_dim <= 32 and cfg.seq_len - n_refs >= 4 * n_refs * splits
+            and max(16 * n_refs, 24576) + 32 * n_refs <= 159 * 1024)
+    split_kernel_name = ("k_split_hist (reference-weight histogram)" if hist else
+                         "k_split_mfma (decode token stream)" if mfma_shape else "k_split_valu")
     split_ms = float(d_stage[:, 1].mean())
     split_bytes = split_kernel_bytes_per_head(cfg, splits) * cfg.batch * cfg.n_kv_heads
     n_streams = cfg.batch * cfg.n_kv_heads * 2
@@ -610,7 +619,7 @@ def main():
         "decode_stage_us": {"refscore": round(float(d_stage[:, 0].mean()) * 1e3, 3),
                             "split": round(split_ms * 1e3, 3),
                             "combine": round(float(d_stage[:, 2].mean()) * 1e3, 3)},
-        "roofline": {"kernel": "k_split_mfma (decode token stream)" if mfma_shape else "k_split_valu", "bound": "hbm",
+        "roofline": {"kernel": split_kernel_name, "bound": "hbm",
                      "achieved": round(split_bytes / (split_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(split_bytes / (split_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": stored_traffic(cfg.name, splits), "bytes_per_launch": split_bytes,

@@ -808,6 +808,368 @@ __global__ __launch_bounds__(kThreads) void k_split_mfma(DecodeArgs a, Shape sh)
   }
 }
 
+// ---------------------------------------------------------------------------
+// split, histogram form, for splits that hold many more tokens than the head
+// has references (batched decode: a few long splits per head).  The value
+// side sum_t p_t x~V[ref(t)] equals sum_r w_r x~V[r] with w_r the summed
+// weights of the tokens whose value reference is r, so each token adds its
+// weight to an LDS histogram instead of gathering its reference row, and
+// every reference row is read once at the end.
+//
+// All waves must then weight against one maximum per query head: the block
+// works through its tiles in chunks of kHistTiles per wave.  Pass A scores a
+// chunk (its ordinals and codes were loaded one chunk ahead) and publishes
+// each wave's maxima; after a barrier every thread forms the same block
+// maxima, and when one grew by more than kTau the histogram and the code
+// accumulators are rescaled by the same factor; pass B then adds the weights
+// 2^(s - M) to the histogram and runs the value-code MFMAs (with the weight
+// sum column), as the token-tile split does.  The block's own reference
+// positions are tokens with a zero code row and their own ordinal in both
+// streams.  The histogram holds 64-bit fixed-point weights (scale 2^32,
+// added with integer LDS atomics, so the sums do not depend on the order of
+// the additions and the output stays deterministic).  A dense pass over the
+// references then applies the weights with the token-tile split's
+// value-reference MFMAs.
+// ---------------------------------------------------------------------------
+
+constexpr int kHistTiles = 4;   // tiles per wave per chunk
+
+// v[i] of a four-entry register array for a run-time i (selects, so that the
+// array stays in registers).
+__device__ __forceinline__ float pick4(const float (&v)[4], int i) {
+  return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
+}
+
+struct HChunk {
+  int ld[kHistTiles];     // loaded ordinal (coded tiles)
+  Frag ck[kHistTiles];    // key-code A operand rows (zero rows for references)
+  Frag cv[kHistTiles];    // value-code pieces, as Tile::cv
+};
+
+// p (0 <= p <= 2^kTau) as a fixed-point integer at scale 2^32, truncated,
+// in two exact 16-bit steps.
+__device__ __forceinline__ unsigned long long fix32(float p) {
+  const float t = p * 65536.f;
+  const uint32_t hi = (uint32_t)t;
+  const uint32_t lo = (uint32_t)((t - (float)hi) * 65536.f);
+  return ((unsigned long long)hi << 16) + lo;
+}
+
+size_t hist_lds_bytes(const Shape& sh) {
+  const size_t front = (size_t)sh.R * 4 * sizeof(float);
+  const size_t red = (size_t)kRedFloats * sizeof(float);
+  return (front > red ? front : red) + (size_t)4 * sh.R * sizeof(unsigned long long);
+}
+
+template <typename IdxT>
+__global__ __launch_bounds__(kThreads) void k_split_hist(DecodeArgs a, Shape sh) {
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  __shared__ __attribute__((aligned(16))) float red_m[kWaves][4];
+  __shared__ __attribute__((aligned(16))) float chunk_m[2][kWaves][4];   // by chunk parity
+
+  const int BH = sh.B * sh.H;
+  const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
+  const int bh = xcd + 8 * (kx / a.splits), sp = kx % a.splits;
+  if (bh >= BH) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n16 = lane & 15, q4 = lane >> 4;
+  const int G = a.G, dc = sh.dc, R = sh.R;
+  const int gl = n16 >> 2;
+
+  const int n0 = split_lo(sh.N, sp, a.splits, 16), n1 = split_lo(sh.N, sp + 1, a.splits, 16);
+  const int r0 = split_lo(sh.R, sp, a.splits, 1), r1 = split_lo(sh.R, sp + 1, a.splits, 1);
+  const int nct = (n1 - n0 + 15) / 16, nrt = (r1 - r0 + 15) / 16;
+  const int nt = nct + nrt;
+  const int t_beg = (int)((int64_t)nt * wave / kWaves), t_end = (int)((int64_t)nt * (wave + 1) / kWaves);
+  const int nchunk = ((nt + kWaves - 1) / kWaves + kHistTiles - 1) / kHistTiles;
+
+  Args p;
+  const size_t sK = (size_t)bh * 2, sV = sK + 1;
+  p.refsV = (const uint16_t*)a.refs + sV * sh.Rc * kD;
+  p.codesK = (const uint16_t*)a.codes + sK * sh.Nc * dc;
+  p.codesV = (const uint16_t*)a.codes + sV * sh.Nc * dc;
+  p.idxK = (const IdxT*)a.idx + sK * sh.Nc;
+  p.idxV = (const IdxT*)a.idx + sV * sh.Nc;
+  p.score = a.score + (size_t)bh * sh.R * 4;
+
+  float* s_tab = lds;   // [R][4]; the wave-merge buffer after the dense pass
+  unsigned long long* hist = (unsigned long long*)(lds + max(R * 4, kRedFloats));   // [4][R]
+
+  // Chunk loads: the wave's tile t = t_beg + kHistTiles c + k (clamped to a
+  // tile of the block, masked when past the wave's range).
+  auto tile_of = [&](int c, int k, int& tb, int& cnt, bool& coded, bool& live) {
+    const int t = t_beg + c * kHistTiles + k;
+    live = t < t_end;
+    const int tc = min(t, nt - 1);
+    coded = tc < nct;
+    tb = coded ? n0 + 16 * tc : r0 + 16 * (tc - nct);
+    cnt = coded ? min(16, n1 - tb) : min(16, r1 - tb);
+  };
+  auto issue = [&](int c, HChunk& L) {
+#pragma unroll
+    for (int k = 0; k < kHistTiles; ++k) {
+      int tb, cnt;
+      bool coded, live;
+      tile_of(c, k, tb, cnt, coded, live);
+      const int ua = tb + min(q4 * 4 + (n16 & 3), cnt - 1);
+      const void* ip = coded ? (const void*)((const IdxT*)(n16 < 4 ? p.idxK : p.idxV) + ua) : (const void*)kZeroCodes;
+      L.ld[k] = (int)ldg<IdxT>(ip, 0u);
+      const int ub = tb + min(n16, cnt - 1);
+      const int cc = q4 * 8;
+      L.ck[k] = ldg<Frag>(coded ? (const void*)p.codesK : (const void*)kZeroCodes,
+                          coded ? ((uint32_t)ub * dc + (cc < dc ? cc : 0)) * 2u : 0u);
+      const int g2 = n16 >> 3, c7 = n16 & 7;
+      const int col = 4 * (c7 & ~1);
+      const int uc = tb + min(q4 * 4 + 2 * g2 + (c7 & 1), cnt - 1);
+      const bool in_code = col < dc;
+      L.cv[k] = ldg<Frag>(in_code ? (coded ? (const void*)p.codesV : (const void*)kZeroCodes) : (const void*)kOnePair,
+                          in_code && coded ? ((uint32_t)uc * dc + col) * 2u : 0u);
+    }
+  };
+
+  HChunk LA, LB;
+  if (nchunk > 0) issue(0, LA);
+
+  // S table into LDS; histogram cleared.
+  {
+    const f32x4* src = reinterpret_cast<const f32x4*>(p.score);
+    f32x4* dst = reinterpret_cast<f32x4*>(s_tab);
+    int i = tid;
+    for (; i + 3 * kThreads < R; i += 4 * kThreads) {
+      const f32x4 v0 = src[i], v1 = src[i + kThreads], v2 = src[i + 2 * kThreads], v3 = src[i + 3 * kThreads];
+      dst[i] = v0;
+      dst[i + kThreads] = v1;
+      dst[i + 2 * kThreads] = v2;
+      dst[i + 3 * kThreads] = v3;
+    }
+    for (; i < R; i += kThreads) dst[i] = src[i];
+    for (int j = tid; j < 4 * R; j += kThreads) hist[j] = 0ull;
+  }
+  Frag qh[1], ql[1];
+  {
+    const int g = n16 >> 2;
+    const float* qp = a.qp + ((size_t)bh * G + min(g, G - 1)) * dc;
+    const int k0 = q4 * 8;
+    const bool live = g < G && k0 < dc;
+    const f32x4 v0 = live ? *reinterpret_cast<const f32x4*>(qp + k0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const f32x4 v1 = live ? *reinterpret_cast<const f32x4*>(qp + k0 + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) {
+      const uint32_t hp = pk_bf16(v[2 * k2], v[2 * k2 + 1]);
+      qh[0][k2] = hp;
+      ql[0][k2] = pk_bf16(v[2 * k2] - __uint_as_float(hp << 16), v[2 * k2 + 1] - __uint_as_float(hp & 0xFFFF0000u));
+    }
+  }
+  uint32_t sel[4];
+  {
+    const int el = n16 & 3;
+    const uint32_t lo_a = (el & 1) ? 0x01000c0cu : 0x0c0c0100u;
+    const uint32_t lo_b = (el & 1) ? 0x03020c0cu : 0x0c0c0302u;
+    const int dw = el >> 1;
+    sel[0] = dw == 0 ? lo_a : 0x0c0c0c0cu;
+    sel[1] = dw == 1 ? lo_a : 0x0c0c0c0cu;
+    sel[2] = dw == 0 ? lo_b : 0x0c0c0c0cu;
+    sel[3] = dw == 1 ? lo_b : 0x0c0c0c0cu;
+  }
+  __syncthreads();
+
+  float M[4] = {-3.0e38f, -3.0e38f, -3.0e38f, -3.0e38f};   // block maxima per query head (base 2)
+  f32x4 accc = {0.f, 0.f, 0.f, 0.f};                         // value codes + weight sum, query head q4
+
+  auto chunk = [&](int c, const HChunk& L, HChunk& Lnext) {
+    // ---- pass A: scores ----
+    float sc[kHistTiles][4];
+    int rw[kHistTiles];
+    float wmax = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kHistTiles; ++k) {
+      int tb, cnt;
+      bool coded, live;
+      tile_of(c, k, tb, cnt, coded, live);
+      const int ua = tb + min(q4 * 4 + (n16 & 3), cnt - 1);
+      const int raw = coded ? L.ld[k] : ua;
+      rw[k] = raw;
+      f32x4 cs = {0.f, 0.f, 0.f, 0.f};
+      cs = mfma16(L.ck[k], qh[0], cs);
+      cs = mfma16(L.ck[k], ql[0], cs);
+      float sb[4];
+      sb[0] = s_tab[(uint32_t)min(row_bcast<0>(raw), R - 1) * 4 + gl];
+      sb[1] = s_tab[(uint32_t)min(row_bcast<1>(raw), R - 1) * 4 + gl];
+      sb[2] = s_tab[(uint32_t)min(row_bcast<2>(raw), R - 1) * 4 + gl];
+      sb[3] = s_tab[(uint32_t)min(row_bcast<3>(raw), R - 1) * 4 + gl];
+      const int vm = live ? cnt : 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sv = q4 * 4 + i < vm ? sb[i] + cs[i] : -INFINITY;
+        sc[k][i] = sv;
+        wmax = fmaxf(wmax, sv);
+      }
+    }
+    // The next chunk's loads fly through the barriers and pass B (issued
+    // once this chunk's ordinals and key codes are consumed).
+    if (c + 1 < nchunk) issue(c + 1, Lnext);
+    wmax = fmaxf(wmax, __shfl_xor(wmax, 16, 64));
+    wmax = fmaxf(wmax, __shfl_xor(wmax, 32, 64));
+    // Maxima slots alternate with the chunk's parity: a wave may write the
+    // next chunk's while a slower one still reads these.
+    if (lane < 16 && (n16 & 3) == 0) chunk_m[c & 1][wave][gl] = wmax;
+    __syncthreads();
+    // ---- block maxima and lazy rescale (the same decision in every thread) ----
+    f32x4 mx4 = {M[0], M[1], M[2], M[3]};
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(&chunk_m[c & 1][w][0]);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) mx4[g] = fmaxf(mx4[g], v[g]);
+    }
+    float alpha[4];
+    bool grow_any = false;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const bool grow = mx4[g] > M[g] + kTau;
+      alpha[g] = grow ? __builtin_amdgcn_exp2f(M[g] - mx4[g]) : 1.f;
+      M[g] = grow ? mx4[g] : M[g];
+      grow_any |= grow;
+    }
+    // Block-uniform (every thread computed the same maxima).  The barrier
+    // above already follows every wave's adds of the earlier chunks.
+    if (grow_any) {
+      for (int j = tid; j < 4 * R; j += kThreads) {
+        const float al = pick4(alpha, j / R);
+        hist[j] = (unsigned long long)((double)hist[j] * (double)al);
+      }
+      accc *= pick4(alpha, q4);
+      __syncthreads();
+    }
+    // ---- pass B: histogram weights and value-code MFMAs ----
+    const float mg = pick4(M, gl);
+#pragma unroll
+    for (int k = 0; k < kHistTiles; ++k) {
+      float pw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pw[i] = __builtin_amdgcn_exp2f(sc[k][i] - mg);
+      const int rv0 = min(row_bcast<4>(rw[k]), R - 1), rv1 = min(row_bcast<5>(rw[k]), R - 1);
+      const int rv2 = min(row_bcast<6>(rw[k]), R - 1), rv3 = min(row_bcast<7>(rw[k]), R - 1);
+      if ((n16 & 3) == 0 && gl < G) {   // one lane of the four that share (token, query head)
+        unsigned long long* hg = hist + (size_t)gl * R;
+        atomicAdd(hg + rv0, fix32(pw[0]));
+        atomicAdd(hg + rv1, fix32(pw[1]));
+        atomicAdd(hg + rv2, fix32(pw[2]));
+        atomicAdd(hg + rv3, fix32(pw[3]));
+      }
+      Frag bc[2];
+      value_code_operands(L.cv[k], n16, dc, bc);
+      const uint32_t h01 = pk_bf16(pw[0], pw[1]), h23 = pk_bf16(pw[2], pw[3]);
+      const uint32_t l01 = pk_bf16(pw[0] - __uint_as_float(h01 << 16), pw[1] - __uint_as_float(h01 & 0xFFFF0000u));
+      const uint32_t l23 = pk_bf16(pw[2] - __uint_as_float(h23 << 16), pw[3] - __uint_as_float(h23 & 0xFFFF0000u));
+#pragma unroll
+      for (int g2 = 0; g2 < 2; ++g2) {
+        const uint32_t hp = g2 ? h23 : h01, lp = g2 ? l23 : l01;
+        const Frag ah = Frag{__builtin_amdgcn_perm(hp, hp, sel[0]), __builtin_amdgcn_perm(hp, hp, sel[1]),
+                             __builtin_amdgcn_perm(hp, hp, sel[2]), __builtin_amdgcn_perm(hp, hp, sel[3])};
+        const Frag al = Frag{__builtin_amdgcn_perm(lp, lp, sel[0]), __builtin_amdgcn_perm(lp, lp, sel[1]),
+                             __builtin_amdgcn_perm(lp, lp, sel[2]), __builtin_amdgcn_perm(lp, lp, sel[3])};
+        accc = mfma16(ah, bc[g2], accc);
+        accc = mfma16(al, bc[g2], accc);
+      }
+    }
+  };
+  for (int c = 0; c < nchunk; c += 2) {
+    chunk(c, LA, LB);
+    if (c + 1 < nchunk) chunk(c + 1, LB, LA);
+  }
+  __syncthreads();   // every weight is in the histogram
+
+  // ---- dense pass: the reference part from the weighted rows ----
+  f32x4 accr[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  {
+    const int rt = (R + 15) / 16;
+    const int rt0 = (int)((int64_t)rt * wave / kWaves), rt1 = (int)((int64_t)rt * (wave + 1) / kWaves);
+    auto load_rows = [&](int t, Frag (&x)[2][2]) {
+      const int base = 16 * min(t, rt - 1) + 4 * q4;
+      const uint32_t ra = (uint32_t)min(base + 0, R - 1), rb = (uint32_t)min(base + 1, R - 1);
+      const uint32_t rc = (uint32_t)min(base + 2, R - 1), rd = (uint32_t)min(base + 3, R - 1);
+      const Frag fa = ldg<Frag>(p.refsV, (ra * kD + n16 * 8) * 2u), fb = ldg<Frag>(p.refsV, (rb * kD + n16 * 8) * 2u);
+      const Frag fc = ldg<Frag>(p.refsV, (rc * kD + n16 * 8) * 2u), fd = ldg<Frag>(p.refsV, (rd * kD + n16 * 8) * 2u);
+      x[0][0] = Frag{fa.x, fa.y, fb.x, fb.y};
+      x[0][1] = Frag{fa.z, fa.w, fb.z, fb.w};
+      x[1][0] = Frag{fc.x, fc.y, fd.x, fd.y};
+      x[1][1] = Frag{fc.z, fc.w, fd.z, fd.w};
+    };
+    // One reference tile: weights of references 16 t + 4 q4 + i for query
+    // head gl (zero past R, past the wave's range, or for unused heads).
+    auto dense_tile = [&](int t, const Frag (&x)[2][2]) {
+      const int base = 16 * t + 4 * q4;
+      float w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = min(base + i, R - 1);
+        const float v = (float)((double)hist[(size_t)min(gl, 3) * R + r] * 0x1p-32);
+        w[i] = t < rt1 && base + i < R && gl < G ? v : 0.f;
+      }
+      const uint32_t h01 = pk_bf16(w[0], w[1]), h23 = pk_bf16(w[2], w[3]);
+      const uint32_t l01 = pk_bf16(w[0] - __uint_as_float(h01 << 16), w[1] - __uint_as_float(h01 & 0xFFFF0000u));
+      const uint32_t l23 = pk_bf16(w[2] - __uint_as_float(h23 << 16), w[3] - __uint_as_float(h23 & 0xFFFF0000u));
+#pragma unroll
+      for (int g2 = 0; g2 < 2; ++g2) {
+        const uint32_t hp = g2 ? h23 : h01, lp = g2 ? l23 : l01;
+        const Frag ah = Frag{__builtin_amdgcn_perm(hp, hp, sel[0]), __builtin_amdgcn_perm(hp, hp, sel[1]),
+                             __builtin_amdgcn_perm(hp, hp, sel[2]), __builtin_amdgcn_perm(hp, hp, sel[3])};
+        const Frag al = Frag{__builtin_amdgcn_perm(lp, lp, sel[0]), __builtin_amdgcn_perm(lp, lp, sel[1]),
+                             __builtin_amdgcn_perm(lp, lp, sel[2]), __builtin_amdgcn_perm(lp, lp, sel[3])};
+        accr[0] = mfma16(ah, x[g2][0], accr[0]);
+        accr[0] = mfma16(al, x[g2][0], accr[0]);
+        accr[1] = mfma16(ah, x[g2][1], accr[1]);
+        accr[1] = mfma16(al, x[g2][1], accr[1]);
+      }
+    };
+    // Two row buffers in turn; loads past the range are clamped and their
+    // weights are zero, so the loop body has no branch.
+    Frag xa[2][2], xb[2][2];
+    if (rt0 < rt1) load_rows(rt0, xa);
+    for (int t = rt0; t < rt1; t += 2) {
+      load_rows(min(t + 1, rt1 - 1), xb);
+      dense_tile(t, xa);
+      load_rows(min(t + 2, rt1 - 1), xa);
+      dense_tile(t + 1, xb);
+    }
+  }
+
+  // ---- merge the block's waves: one maximum per query head, plain sums ----
+  if (lane < 16 && (n16 & 3) == 0) red_m[wave][gl] = pick4(M, gl);
+  __syncthreads();   // also: the S table is no longer read
+  float* red_acc = lds;
+  float* mine_acc = red_acc + (wave * 4 + q4) * (kD + 64);
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mine_acc[n16 * 8 + hh * 4 + i] = accr[hh][i];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (n16 * 4 + i <= dc) mine_acc[kD + n16 * 4 + i] = accc[i];
+  __syncthreads();
+  const int rec = partial_rec(sh);
+  float* part = a.part + ((size_t)bh * a.splits + sp) * G * rec;
+  for (int i = tid; i < G * rec; i += kThreads) {
+    const int g = i / rec, f = i % rec;
+    float v = 0.f;
+    if (f == 0) {
+      v = red_m[0][g];
+    } else if (f == 1) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) v += red_acc[(w * 4 + g) * (kD + 64) + kD + dc];
+    } else if (f < 2 + dc) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) v += red_acc[(w * 4 + g) * (kD + 64) + kD + f - 2];
+    } else if (f < 2 + dc + kD) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) v += red_acc[(w * 4 + g) * (kD + 64) + f - 2 - dc];
+    }
+    part[i] = v;
+  }
+}
+
 // combine: merges the splits of one (b, query head) and applies mu_V and
 // W_up_V.  Block L (256 threads) runs on XCD L % 8, the XCD of its head's
 // split blocks; thread t owns column t of the partial records (code columns,
@@ -949,6 +1311,15 @@ bool decode_fused_supported(const Shape& sh, int G, int splits) {
   return codes_ok && mfma_side_kernels_supported(sh, G, splits);
 }
 
+// The histogram split serves storage-dtype codes with d_c <= 32 and one
+// reference when each split holds at least four times as many coded tokens
+// as the head has references (there the one pass over the references is far
+// cheaper than a gather per token) and the S table and histogram fit in LDS.
+bool decode_hist_supported(const Shape& sh, int G, int splits) {
+  return sh.K == 1 && !sh.q4 && sh.dc <= 32 && mfma_side_kernels_supported(sh, G, splits) &&
+         (int64_t)sh.N >= (int64_t)4 * sh.R * splits && hist_lds_bytes(sh) <= kSplitLdsMax;
+}
+
 bool decode_sel_fused_supported(const Shape& sh, int G, int splits) {
   return sh.K == 1 && sh.dc <= 32 && decode_fused_supported(sh, G, splits);
 }
@@ -983,7 +1354,12 @@ hipError_t launch_decode_fused(const Shape& sh, const DecodeArgs& a, hipStream_t
   if (e != hipSuccess) return e;
   const dim3 grid(BH8 * a.splits);
   const bool i16 = sh.idx_bytes == 2;
-  if (sh.K > 1)
+  if (decode_hist_supported(sh, a.G, a.splits))
+    e = i16 ? launch_lds(k_split_hist<uint16_t>, grid, kThreads, hist_lds_bytes(sh), st, ev_start(a.events, 1),
+                         ev_stop(a.events, 1), a, sh)
+            : launch_lds(k_split_hist<uint32_t>, grid, kThreads, hist_lds_bytes(sh), st, ev_start(a.events, 1),
+                         ev_stop(a.events, 1), a, sh);
+  else if (sh.K > 1)
     e = i16 ? launch_split_topk_s<uint16_t>(sh, a, st, grid) : launch_split_topk_s<uint32_t>(sh, a, st, grid);
   else if (sh.dc <= 32)
     e = i16 ? launch_split_s<1, uint16_t>(sh, a, st, grid) : launch_split_s<1, uint32_t>(sh, a, st, grid);

@@ -96,6 +96,29 @@ def test_split_count_invariance(splits, small_runs):
     assert np.abs(out - base).max() <= 1e-5
 
 
+def test_histogram_split_deterministic(small_runs):
+    """One split over 3001 tokens (2813 coded rows, at least four per
+    reference per split) takes the histogram form of the split: identical
+    bytes on repeated calls (its weight sums are integer), oracle parity,
+    and agreement with the token-tile form at 64 splits."""
+    inp, lay, cache, gc = _run("bf16_ragged", small_runs)
+    cfg = inp.cfg
+    assert lay.n_codes >= 4 * lay.n_refs
+    q = inp.q(5)
+    outs = []
+    for _ in range(3):
+        out = torch.empty((cfg.batch, cfg.n_q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
+        ws = D.workspace(D.dkv_decode_workspace_bytes(lay, cfg.n_q_heads, 1))
+        D.deltakv_decode_attn(lay, cache, GH.dev(q.raw), GH.dev(inp.wuk.raw), GH.dev(inp.wuv.raw), out, ws,
+                              n_splits=1)
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    o = outs[0].cpu().numpy().astype(np.float64)
+    assert np.abs(o - GH.oracle_decode_on(gc, q.f64, inp)).max() <= GH.OUT_TOL[cfg.dtype]
+    assert np.abs(o - GH.gpu_decode(lay, cache, q.raw, inp, n_splits=64)).max() <= 1e-5
+
+
 def test_softmax_scale_argument(small_runs):
     inp, lay, cache, gc = _run("bf16_ragged", small_runs)
     q = inp.q(0)
