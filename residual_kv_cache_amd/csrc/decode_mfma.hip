@@ -110,34 +110,58 @@ __global__ __launch_bounds__(256) void k_refscore_mfma(DecodeArgs a, Shape sh, i
   const int r = c * kRsRefs + wave * 16 + n16;
   const uint32_t rr = (uint32_t)min(r, sh.R - 1);
   const uint16_t* refsK = (const uint16_t*)a.refs + (size_t)bh * 2 * sh.Rc * kD;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const uint16_t* wu = (const uint16_t*)a.wuk + (size_t)h * a.w_hs;
+  const int quarter = wave * 4 + q4;
+  // Every load of the block is issued before the first wait (one round
+  // trip): the query rows (row clamped; heads past G are zeroed after), the
+  // reference rows, and the first q' output's query slice and W_up column.
+  Frag aq[4], br[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const uint32_t col = ks * 32 + q4 * 8;
-    const Frag aq = n16 < G ? ldg<Frag>(q, ((uint32_t)n16 * kD + col) * 2u) : Frag{0u, 0u, 0u, 0u};
-    const Frag br = ldg<Frag>(refsK, (rr * kD + col) * 2u);
-    acc = mfma16(aq, br, acc);
+    aq[ks] = ldg<Frag>(q, ((uint32_t)min(n16, G - 1) * kD + col) * 2u);
+    br[ks] = ldg<Frag>(refsK, (rr * kD + col) * 2u);
+  }
+  const int o0 = c + chunks * quarter;
+  const int oc = min(o0, G * dc - 1);
+  const Frag qv0 = ldg<Frag>(q, ((uint32_t)(oc / dc) * kD + n16 * 8) * 2u);
+  uint16_t w0[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) w0[t] = ldg<uint16_t>(wu, ((uint32_t)(n16 * 8 + t) * dc + oc % dc) * 2u);
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const Frag a0 = n16 < G ? aq[ks] : Frag{0u, 0u, 0u, 0u};
+    acc = mfma16(a0, br[ks], acc);
   }
   if (q4 == 0 && r < sh.R)
     *reinterpret_cast<f32x4*>(a.score + ((size_t)bh * sh.R + r) * 4) = acc * cs;
 
-  const int quarter = wave * 4 + q4;
-  const uint16_t* wu = (const uint16_t*)a.wuk + (size_t)h * a.w_hs;
-  for (int o = c + chunks * quarter; o < G * dc; o += chunks * 16) {
-    const int g = o / dc, j = o % dc;
-    const Frag qv = ldg<Frag>(q, ((uint32_t)g * kD + n16 * 8) * 2u);
-    float s = 0.f;
+  // q' = W_up_K^T q (scaled): 16 lanes per output, 8 products each, summed
+  // by a fixed butterfly.
+  auto qprime = [&](int o, const Frag& qv, const uint16_t* w) {
+    float sacc = 0.f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const uint32_t qw = qv[t >> 1];
       const float qf = __uint_as_float((t & 1) ? (qw & 0xFFFF0000u) : (qw << 16));
-      s = fmaf(qf, bf2f(wu[(size_t)(n16 * 8 + t) * dc + j]), s);
+      sacc = fmaf(qf, bf2f(w[t]), sacc);
     }
-    s += __shfl_xor(s, 8, 64);
-    s += __shfl_xor(s, 4, 64);
-    s += __shfl_xor(s, 2, 64);
-    s += __shfl_xor(s, 1, 64);
-    if (n16 == 0) a.qp[((size_t)bh * G + g) * dc + j] = s * cs;
+    sacc += __shfl_xor(sacc, 8, 64);
+    sacc += __shfl_xor(sacc, 4, 64);
+    sacc += __shfl_xor(sacc, 2, 64);
+    sacc += __shfl_xor(sacc, 1, 64);
+    if (n16 == 0) a.qp[((size_t)bh * G + o / dc) * dc + o % dc] = sacc * cs;
+  };
+  if (o0 < G * dc) qprime(o0, qv0, w0);
+  // Further outputs (only when there are fewer than G d_c / 16 chunks).
+  for (int o = o0 + chunks * 16; o < G * dc; o += chunks * 16) {
+    const Frag qv = ldg<Frag>(q, ((uint32_t)(o / dc) * kD + n16 * 8) * 2u);
+    uint16_t w[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) w[t] = ldg<uint16_t>(wu, ((uint32_t)(n16 * 8 + t) * dc + o % dc) * 2u);
+    qprime(o, qv, w);
   }
 }
 
