@@ -1220,14 +1220,28 @@ __global__ __launch_bounds__(256) void k_combine(DecodeArgs a, Shape sh) {
   const int i_out = t - dc;
   const bool is_out = i_out >= 0 && has_col;
   const uint16_t* wuv = (const uint16_t*)a.wuv + (size_t)h * a.w_hs;
+  // Every load is unconditional (clamped addresses) and masked afterwards
+  // with arithmetic, so the compiler cannot turn a select into a branch that
+  // waits: the W_up row, mu_V and the first 32 records arrive in one round
+  // trip.
+  const uint32_t io = is_out ? (uint32_t)i_out : 0u;
   U32x2 wrow[kMaxDc / 4];
 #pragma unroll
   for (int j = 0; j < kMaxDc / 4; ++j)
-    wrow[j] = (is_out && j * 4 < dc) ? ldg<U32x2>(wuv, ((uint32_t)i_out * dc + j * 4) * 2u) : U32x2{0u, 0u};
-  const float muv = is_out ? bf2f(((const uint16_t*)a.mu)[((size_t)bh * 2 + 1) * kD + i_out]) : 0.f;
+    wrow[j] = ldg<U32x2>(wuv, (io * dc + (uint32_t)min(j * 4, dc - 4)) * 2u);
+  const uint16_t mu_bits = ldg<uint16_t>(a.mu, ((uint32_t)(bh * 2 + 1) * kD + io) * 2u);
   float v[kCombineBatch];
 #pragma unroll
-  for (int k = 0; k < kCombineBatch; ++k) v[k] = (has_col && k < ns) ? pc[(size_t)k * pstride] : 0.f;
+  for (int k = 0; k < kCombineBatch; ++k) v[k] = pc[(size_t)min(k, ns - 1) * pstride];
+  const float col_on = has_col ? 1.f : 0.f;
+#pragma unroll
+  for (int k = 0; k < kCombineBatch; ++k) v[k] *= k < ns ? col_on : 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxDc / 4; ++j) {
+    const uint32_t m = 0u - (uint32_t)(is_out && j * 4 < dc);
+    wrow[j] = U32x2{wrow[j].x & m, wrow[j].y & m};
+  }
+  const float muv = is_out ? bf2f(mu_bits) : 0.f;
   for (int s2 = t; s2 < ns; s2 += 256) {
     mls[0][s2] = part[s2 * pstride];
     mls[1][s2] = part[s2 * pstride + 1];
