@@ -715,6 +715,19 @@ __global__ __launch_bounds__(kThreads) void k_split_mfma(DecodeArgs a, Shape sh)
   p.list = SEL ? a.sel + (size_t)(bh / sh.H) * a.n_sel : nullptr;
   p.magic = SEL ? 0xFFFFFFFFu / (uint32_t)sh.s : 0u;
 
+  // q'_g (g = n16 / 4) for the score B operands: loaded first and
+  // unconditionally (clamped column, masked later by a 0/1 factor), so that
+  // this load, the first ordinals and the S-table copy share one round trip.
+  f32x4 qv[DCK][2];
+  {
+    const float* qp = a.qp + ((size_t)bh * G + min(n16 >> 2, G - 1)) * dc;
+#pragma unroll
+    for (int ks = 0; ks < DCK; ++ks) {
+      const int k0 = min(ks * 32 + q4 * 8, dc - 8);
+      qv[ks][0] = *reinterpret_cast<const f32x4*>(qp + k0);
+      qv[ks][1] = *reinterpret_cast<const f32x4*>(qp + k0 + 4);
+    }
+  }
   // Ordinals of the wave's first two coded tiles: issued first, so that
   // their HBM round trip overlaps the S-table copy.
   const int c1 = min(t_end, nct);
@@ -737,24 +750,18 @@ __global__ __launch_bounds__(kThreads) void k_split_mfma(DecodeArgs a, Shape sh)
     }
     for (; i < sh.R; i += kThreads) dst[i] = src[i];
   }
-  // Score B operands: q'_g (g = n16 / 4) split into bf16 hi + lo parts.
+  // Score B operands: q' split into bf16 hi + lo parts.
   Frag qh[DCK], ql[DCK];
-  {
-    const int g = n16 >> 2;
-    const float* qp = a.qp + ((size_t)bh * G + min(g, G - 1)) * dc;
 #pragma unroll
-    for (int ks = 0; ks < DCK; ++ks) {
-      const int k0 = ks * 32 + q4 * 8;
-      const bool live = g < G && k0 < dc;
-      const f32x4 v0 = live ? *reinterpret_cast<const f32x4*>(qp + k0) : f32x4{0.f, 0.f, 0.f, 0.f};
-      const f32x4 v1 = live ? *reinterpret_cast<const f32x4*>(qp + k0 + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
-      const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+  for (int ks = 0; ks < DCK; ++ks) {
+    const float on = ((n16 >> 2) < G && ks * 32 + q4 * 8 < dc) ? 1.f : 0.f;
+    const f32x4 v0 = qv[ks][0] * on, v1 = qv[ks][1] * on;
+    const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
 #pragma unroll
-      for (int k2 = 0; k2 < 4; ++k2) {
-        const uint32_t hp = pk_bf16(v[2 * k2], v[2 * k2 + 1]);
-        qh[ks][k2] = hp;
-        ql[ks][k2] = pk_bf16(v[2 * k2] - __uint_as_float(hp << 16), v[2 * k2 + 1] - __uint_as_float(hp & 0xFFFF0000u));
-      }
+    for (int k2 = 0; k2 < 4; ++k2) {
+      const uint32_t hp = pk_bf16(v[2 * k2], v[2 * k2 + 1]);
+      qh[ks][k2] = hp;
+      ql[ks][k2] = pk_bf16(v[2 * k2] - __uint_as_float(hp << 16), v[2 * k2 + 1] - __uint_as_float(hp & 0xFFFF0000u));
     }
   }
   // v_perm selectors that place a packed pair (p_a low, p_b high) at
