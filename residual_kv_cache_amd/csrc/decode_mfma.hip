@@ -110,11 +110,8 @@ __global__ __launch_bounds__(256) void k_refscore_mfma(DecodeArgs a, Shape sh, i
   const int r = c * kRsRefs + wave * 16 + n16;
   const uint32_t rr = (uint32_t)min(r, sh.R - 1);
   const uint16_t* refsK = (const uint16_t*)a.refs + (size_t)bh * 2 * sh.Rc * kD;
-  const uint16_t* wu = (const uint16_t*)a.wuk + (size_t)h * a.w_hs;
-  const int quarter = wave * 4 + q4;
-  // Every load of the block is issued before the first wait (one round
-  // trip): the query rows (row clamped; heads past G are zeroed after), the
-  // reference rows, and the first q' output's query slice and W_up column.
+  // The S part's loads are unconditional (query row clamped, heads past G
+  // zeroed after the loads), so all eight are in flight at once.
   Frag aq[4], br[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
@@ -122,13 +119,6 @@ __global__ __launch_bounds__(256) void k_refscore_mfma(DecodeArgs a, Shape sh, i
     aq[ks] = ldg<Frag>(q, ((uint32_t)min(n16, G - 1) * kD + col) * 2u);
     br[ks] = ldg<Frag>(refsK, (rr * kD + col) * 2u);
   }
-  const int o0 = c + chunks * quarter;
-  const int oc = min(o0, G * dc - 1);
-  const Frag qv0 = ldg<Frag>(q, ((uint32_t)(oc / dc) * kD + n16 * 8) * 2u);
-  uint16_t w0[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) w0[t] = ldg<uint16_t>(wu, ((uint32_t)(n16 * 8 + t) * dc + oc % dc) * 2u);
-
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
@@ -138,30 +128,25 @@ __global__ __launch_bounds__(256) void k_refscore_mfma(DecodeArgs a, Shape sh, i
   if (q4 == 0 && r < sh.R)
     *reinterpret_cast<f32x4*>(a.score + ((size_t)bh * sh.R + r) * 4) = acc * cs;
 
-  // q' = W_up_K^T q (scaled): 16 lanes per output, 8 products each, summed
-  // by a fixed butterfly.
-  auto qprime = [&](int o, const Frag& qv, const uint16_t* w) {
+  // q' outputs o = chunk + chunks * (16 t + quarter): 16 lanes per output, 8
+  // products each, summed by a fixed butterfly.
+  const int quarter = wave * 4 + q4;
+  const uint16_t* wu = (const uint16_t*)a.wuk + (size_t)h * a.w_hs;
+  for (int o = c + chunks * quarter; o < G * dc; o += chunks * 16) {
+    const int g = o / dc, j = o % dc;
+    const Frag qv = ldg<Frag>(q, ((uint32_t)g * kD + n16 * 8) * 2u);
     float sacc = 0.f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const uint32_t qw = qv[t >> 1];
       const float qf = __uint_as_float((t & 1) ? (qw & 0xFFFF0000u) : (qw << 16));
-      sacc = fmaf(qf, bf2f(w[t]), sacc);
+      sacc = fmaf(qf, bf2f(wu[(size_t)(n16 * 8 + t) * dc + j]), sacc);
     }
     sacc += __shfl_xor(sacc, 8, 64);
     sacc += __shfl_xor(sacc, 4, 64);
     sacc += __shfl_xor(sacc, 2, 64);
     sacc += __shfl_xor(sacc, 1, 64);
-    if (n16 == 0) a.qp[((size_t)bh * G + o / dc) * dc + o % dc] = sacc * cs;
-  };
-  if (o0 < G * dc) qprime(o0, qv0, w0);
-  // Further outputs (only when there are fewer than G d_c / 16 chunks).
-  for (int o = o0 + chunks * 16; o < G * dc; o += chunks * 16) {
-    const Frag qv = ldg<Frag>(q, ((uint32_t)(o / dc) * kD + n16 * 8) * 2u);
-    uint16_t w[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) w[t] = ldg<uint16_t>(wu, ((uint32_t)(n16 * 8 + t) * dc + o % dc) * 2u);
-    qprime(o, qv, w);
+    if (n16 == 0) a.qp[((size_t)bh * G + g) * dc + j] = sacc * cs;
   }
 }
 
@@ -1237,12 +1222,13 @@ __global__ __launch_bounds__(256) void k_combine(DecodeArgs a, Shape sh) {
   for (int j = 0; j < kMaxDc / 4; ++j)
     wrow[j] = ldg<U32x2>(wuv, (io * dc + (uint32_t)min(j * 4, dc - 4)) * 2u);
   const uint16_t mu_bits = ldg<uint16_t>(a.mu, ((uint32_t)(bh * 2 + 1) * kD + io) * 2u);
+  // Records past the split count are not loaded (a uniform condition).
   float v[kCombineBatch];
 #pragma unroll
-  for (int k = 0; k < kCombineBatch; ++k) v[k] = pc[(size_t)min(k, ns - 1) * pstride];
+  for (int k = 0; k < kCombineBatch; ++k) v[k] = k < ns ? pc[(size_t)k * pstride] : 0.f;
   const float col_on = has_col ? 1.f : 0.f;
 #pragma unroll
-  for (int k = 0; k < kCombineBatch; ++k) v[k] *= k < ns ? col_on : 0.f;
+  for (int k = 0; k < kCombineBatch; ++k) v[k] *= col_on;
 #pragma unroll
   for (int j = 0; j < kMaxDc / 4; ++j) {
     const uint32_t m = 0u - (uint32_t)(is_out && j * 4 < dc);
