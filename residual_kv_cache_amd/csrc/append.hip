@@ -204,20 +204,41 @@ __global__ __launch_bounds__(64) void k_append_finish(AppendArgs a, Shape sh, in
   const int t = sh.T - 1;
   const int lane = threadIdx.x;
   if (t % sh.s == 0) {
+    // The token's centred row becomes a reference (both elements of a lane
+    // loaded before either is stored).
     const T* src = (const T*)(kv ? a.v : a.k) + (int64_t)b * a.sb + (int64_t)h * a.sh;
     const T* mu = (const T*)a.mu + (size_t)stream * D;
     T* row = (T*)a.refs + ((size_t)stream * sh.Rc + t / sh.s) * D;
-    for (int i = lane; i < D; i += 64) row[i] = S::sub_rn(S::load(src[i]), S::load(mu[i]));
+    constexpr int PER = D / 64;
+    T x[PER], m[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      x[j] = src[lane + 64 * j];
+      m[j] = mu[lane + 64 * j];
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) row[lane + 64 * j] = S::sub_rn(S::load(x[j]), S::load(m[j]));
     return;
   }
+  // Merge the blocks' candidates.  A lane loads up to kMergeLoads of them at
+  // once (clamped addresses; duplicates of the last one cannot change the
+  // maximum), then compares; larger P loops.
+  constexpr int kMergeLoads = 4;
   float bs = -INFINITY;
   int br = 0x7FFFFFFF, bp = 0;
-  for (int i = lane; i < P; i += 64) {
-    const float2 v = part[(size_t)stream * P + i];
-    if (better(v.x, __float_as_int(v.y), bs, br)) {
-      bs = v.x;
-      br = __float_as_int(v.y);
-      bp = i;
+  const float2* pp = part + (size_t)stream * P;
+  for (int i0 = 0; i0 < P; i0 += 64 * kMergeLoads) {
+    float2 v[kMergeLoads];
+#pragma unroll
+    for (int u = 0; u < kMergeLoads; ++u) v[u] = pp[min(i0 + lane + 64 * u, P - 1)];
+#pragma unroll
+    for (int u = 0; u < kMergeLoads; ++u) {
+      const int i = min(i0 + lane + 64 * u, P - 1);
+      if (better(v[u].x, __float_as_int(v[u].y), bs, br)) {
+        bs = v[u].x;
+        br = __float_as_int(v[u].y);
+        bp = i;
+      }
     }
   }
 #pragma unroll
@@ -239,7 +260,9 @@ __global__ __launch_bounds__(64) void k_append_finish(AppendArgs a, Shape sh, in
     // 4-bit codes: the row's scale from its largest magnitude, then each
     // even lane packs its element with its neighbour's (d_c <= 128).
     const float* c = (const float*)pcode + ((size_t)stream * P + bp) * sh.dc;
-    const float c0 = lane < sh.dc ? c[lane] : 0.f, c1 = lane + 64 < sh.dc ? c[lane + 64] : 0.f;
+    // Both loads unconditional (clamped), masked after: one round trip.
+    const float l0 = c[min(lane, sh.dc - 1)], l1 = c[min(lane + 64, sh.dc - 1)];
+    const float c0 = lane < sh.dc ? l0 : 0.f, c1 = lane + 64 < sh.dc ? l1 : 0.f;
     const float amax = wave_max(fmaxf(fabsf(c0), fabsf(c1)));
     const T sbits = S::from_f32(amax / 7.0f);
     const float scale = S::load(sbits);
@@ -358,9 +381,17 @@ __global__ __launch_bounds__(256) void k_append_finish_topk(AppendArgs a, Shape 
   if (tid < 64) {
     TopK top;
     top.init();
-    for (int i = lane; i < P * K; i += 64) {
-      const float2 v = part[(size_t)stream * P * K + i];
-      top.insert(v.x, __float_as_int(v.y), K);
+    // Up to 8 list entries per lane in flight at once (clamped; a repeated
+    // entry is masked out), then inserted.
+    const float2* pp = part + (size_t)stream * P * K;
+    const int n = P * K;
+    for (int i0 = 0; i0 < n; i0 += 64 * 8) {
+      float2 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = pp[min(i0 + lane + 64 * u, n - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (i0 + lane + 64 * u < n) top.insert(v[u].x, __float_as_int(v[u].y), K);
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) top.merge_xor(o, K);
@@ -373,10 +404,17 @@ __global__ __launch_bounds__(256) void k_append_finish_topk(AppendArgs a, Shape 
   }
   __syncthreads();
   if (tid < D) {
+    // Every kept reference row loaded at once (slots past the count read a
+    // valid row and are masked), summed in slot order.
+    T rv[kTopMax];
+#pragma unroll
+    for (int j = 0; j < kTopMax; ++j) rv[j] = refs[(size_t)min(s_ord[min(j, cnt - 1)], sh.R - 1) * D + tid];
+    const T xk = src[tid], xm = mu[tid];
     float m = 0.f;
-    for (int j = 0; j < cnt; ++j) m += S::load(refs[(size_t)min(s_ord[j], sh.R - 1) * D + tid]);
+#pragma unroll
+    for (int j = 0; j < kTopMax; ++j) m += j < cnt ? S::load(rv[j]) : 0.f;
     m = cnt > 1 ? m * (1.0f / (float)cnt) : m;
-    diff[tid] = (S::load(src[tid]) - S::load(mu[tid])) - m;
+    diff[tid] = (S::load(xk) - S::load(xm)) - m;
   }
   __syncthreads();
   const size_t slot = (size_t)stream * sh.Nc + (size_t)(t - t / sh.s - 1);
