@@ -197,12 +197,57 @@ constexpr int kSearchNT = 2;                    // 16-token MFMA tiles per wave
 constexpr int kSearchThreads = 64 * kSearchWaves;
 constexpr int kSearchTok = 16 * kSearchNT * kSearchWaves;   // positions per block
 
+// Token and mean pieces of a wave's MFMA B operands: token tiles of 16
+// positions from tw, lane (lrow, lgrp) holding elements ks * 32 + lgrp * 8 ..
+// + 7 of position tw + 16 nt + lrow.  Every load is issued before any is used.
+// Positions past the end read the last row: their columns only produce keys
+// of positions that are never stored.
 template <int D>
-__global__ __launch_bounds__(kSearchThreads) void k_search_mfma(CompressArgs a, Shape sh) {
+__device__ __forceinline__ void load_tokens(const uint16_t* src, int64_t st, const uint16_t* mu, int tw, int T,
+                                            int lrow, int lgrp, uint4 (*xr)[D / 32], uint4* mr) {
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) mr[ks] = *reinterpret_cast<const uint4*>(mu + ks * 32 + lgrp * 8);
+#pragma unroll
+  for (int nt = 0; nt < kSearchNT; ++nt) {
+    const int t = min(tw + nt * 16 + lrow, T - 1);
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+      xr[nt][ks] = *reinterpret_cast<const uint4*>(src + (int64_t)t * st + ks * 32 + lgrp * 8);
+  }
+}
+
+// rnd(x - mu) of 8 bfloat16 elements as 4 packed pairs: x - mu of two bf16
+// values is exact in fp32 or too far from a bf16 tie to round differently,
+// so one fp32 subtraction and one rounding give rnd(x - mu).
+__device__ __forceinline__ void centre8(uint4 x, uint4 m, uint32_t* w) {
+  const uint32_t xv[4] = {x.x, x.y, x.z, x.w}, mv[4] = {m.x, m.y, m.z, m.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    w[e] = pk_bf16_rn(__uint_as_float(xv[e] << 16) - __uint_as_float(mv[e] << 16),
+                      __uint_as_float(xv[e] & 0xFFFF0000u) - __uint_as_float(mv[e] & 0xFFFF0000u));
+}
+
+// Word 3 of a raw buffer descriptor (gfx9 family): 32-bit data format, so
+// untyped loads return the bytes as stored; a load at or past the size in
+// word 2 (bytes, for stride 0) returns zeros.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+// Element offset of 16-byte piece pc of row `row` in an LDS reference chunk
+// (unpadded rows of D / 8 pieces).  The piece index is XORed with the row
+// (with the row pair for d = 64, whose rows are half as long), so the lanes
+// of an MFMA A-fragment read, which take the same piece of 16 consecutive
+// rows, fall on distinct LDS banks.
+template <int D>
+__device__ __forceinline__ int chunk_off(int row, int pc) {
+  constexpr int SH = D == 128 ? 0 : 1;
+  return row * D + ((pc ^ ((row >> SH) & (D / 8 - 1))) << 3);
+}
+
+template <int D>
+__global__ __launch_bounds__(kSearchThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_search_mfma(CompressArgs a, Shape sh) {
   constexpr int KS = D / 32;      // MFMA K-steps over the head dim
-  constexpr int LDR = D + 8;      // padded LDS row (elements)
   constexpr int PER = kSearchRefs * (D / 8) / kSearchThreads;   // 16-byte pieces per thread per chunk
-  __shared__ __attribute__((aligned(16))) uint16_t lds_ref[2][kSearchRefs * LDR];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_ref[2][kSearchRefs * D];
   __shared__ float lds_inv[2][kSearchRefs];
 
   const XcdItem xi = xcd_item(sh.n_streams());
@@ -228,56 +273,59 @@ __global__ __launch_bounds__(kSearchThreads) void k_search_mfma(CompressArgs a, 
   const int nchunks = (rend_b + kSearchRefs - 1) / kSearchRefs;
 
   // Chunk staging: global -> registers (one chunk ahead) -> LDS.
+  // Chunk loads through buffer descriptors whose base is the chunk's first
+  // row and whose size covers the rows that exist (r < rend_b): rows past
+  // the end read as zeros with no compare or branch, and each thread's byte
+  // offsets are the same for every chunk.
   uint4 pre[PER];
   float pinv = 0.f;
   auto fetch = [&](int ch) {
     const int rc = ch * kSearchRefs;
+    const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(refs + (size_t)rc * D), (short)0, (rend_b - rc) * D * 2, kBufferRsrcWord3);
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int p = tid + j * kSearchThreads;
-      const int row = p / (D / 8), col = (p % (D / 8)) * 8;
-      pre[j] = rc + row < rend_b ? *reinterpret_cast<const uint4*>(refs + (size_t)(rc + row) * D + col)
-                                 : make_uint4(0, 0, 0, 0);
+      pre[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, p * 16, 0, 0));
     }
-    if (tid < kSearchRefs) pinv = rc + tid < rend_b ? inv_n[rc + tid] : 0.f;
+    if (tid < kSearchRefs) {
+      const __amdgpu_buffer_rsrc_t rn = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(inv_n + rc), (short)0, (rend_b - rc) * 4, kBufferRsrcWord3);
+      pinv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rn, tid * 4, 0, 0));
+    }
   };
   auto stash = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int p = tid + j * kSearchThreads;
       const int row = p / (D / 8), col = (p % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(&lds_ref[buf][row * LDR + col]) = pre[j];
+      *reinterpret_cast<uint4*>(&lds_ref[buf][chunk_off<D>(row, col >> 3)]) = pre[j];
     }
     if (tid < kSearchRefs) lds_inv[buf][tid] = pinv;
   };
   if (nchunks > 0) fetch(0);
 
-  // B operands: centred tokens, [N-tile][K-step].  x - mu of two bf16
-  // values is exact in fp32 or too far from a bf16 tie to round
-  // differently, so one fp32 subtraction and one rounding give rnd(x - mu).
+  // B operands: centred tokens rnd(x - mu), [N-tile][K-step], and their
+  // squared norms.
   bf16x8 bt[kSearchNT][KS];
   float n2[kSearchNT] = {};
+  {
+    uint4 xr[kSearchNT][KS], mr[KS];
+    load_tokens<D>(src, a.st, mu, tw, sh.T, lrow, lgrp, xr, mr);
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const int c = ks * 32 + lgrp * 8;
-    float m[8];
-    load8(mu + c, m);
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-    for (int nt = 0; nt < kSearchNT; ++nt) {
-      const int t = tw + nt * 16 + lrow;
-      uint32_t w[4] = {0u, 0u, 0u, 0u};
-      if (t < sh.T) {
-        float x[8];
-        load8(src + (int64_t)t * a.st + c, x);
+      for (int nt = 0; nt < kSearchNT; ++nt) {
+        uint32_t w[4];
+        centre8(xr[nt][ks], mr[ks], w);
+        // Squared norm by bf16 pair dot products: it only sets the key
+        // offset below, which needs no particular rounding.
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          w[e] = pk_bf16_rn(x[2 * e] - m[2 * e], x[2 * e + 1] - m[2 * e + 1]);
-          const float lo = __uint_as_float(w[e] << 16), hi = __uint_as_float(w[e] & 0xFFFF0000u);
-          n2[nt] = fmaf(lo, lo, fmaf(hi, hi, n2[nt]));
-        }
+        for (int e = 0; e < 4; ++e)
+          n2[nt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[e]),
+                                                   __builtin_bit_cast(bf16x2_t, w[e]), n2[nt], false);
+        bt[nt][ks] = __builtin_bit_cast(bf16x8, w);
       }
-      bt[nt][ks] = __builtin_bit_cast(bf16x8, w);
-    }
   }
   // Selection keys.  A candidate's score <x~_t, x~_r> / ||x~_r|| lies in
   // [-||x~_t||, ||x~_t||]; adding off = 2 ||x~_t|| (+ a tiny constant, so that
@@ -299,6 +347,10 @@ __global__ __launch_bounds__(kSearchThreads) void k_search_mfma(CompressArgs a, 
   }
   uint32_t bkey[kSearchNT] = {};
   int bch[kSearchNT] = {};
+  // Number of references before the lane's token t (those with r s < t).
+  int nprev[kSearchNT];
+#pragma unroll
+  for (int nt = 0; nt < kSearchNT; ++nt) nprev[nt] = (tw + nt * 16 + lrow + sh.s - 1) / sh.s;
 
   if (nchunks > 0) stash(0);
   __syncthreads();
@@ -310,35 +362,47 @@ __global__ __launch_bounds__(kSearchThreads) void k_search_mfma(CompressArgs a, 
     const int nmt = min(kSearchRefs / 16, (rend_w - rc + 15) / 16);
     if (rc < rend_w && nmt == kSearchRefs / 16 && (rc + kSearchRefs - 1) * sh.s < tw) {
       // Fast path: a full chunk entirely before the wave's first position
-      // needs no causal mask.  With no branch inside, the next tile's MFMAs
-      // are issued before this tile's keys are extracted, so the matrix
-      // core and the VALU work at the same time.
+      // needs no causal mask.  The issue order is fixed by hand: K-step ks of
+      // tile mt issues its two MFMAs, refills the A-fragment register it has
+      // just consumed with tile mt + 1's piece (three K-steps of LDS latency
+      // cover), then computes the keys of element ks of tile mt - 1 (three
+      // VALU operations per token tile), so one wave keeps the matrix core
+      // and the VALU busy together.
+      constexpr int MT = kSearchRefs / 16;
+      bf16x8 ar[KS];
       f32x4 acc[2][kSearchNT];
-      auto tile_mfma = [&](int mt, f32x4* out) {
-        bf16x8 ar[KS];
+      f32x4 inv4;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          ar[ks] = *reinterpret_cast<const bf16x8*>(&lds_ref[buf][(mt * 16 + lrow) * LDR + ks * 32 + lgrp * 8]);
+      for (int ks = 0; ks < KS; ++ks)
+        ar[ks] = *reinterpret_cast<const bf16x8*>(&lds_ref[buf][chunk_off<D>(lrow, ks * 4 + lgrp)]);
 #pragma unroll
-        for (int nt = 0; nt < kSearchNT; ++nt) out[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int mt = 0; mt <= MT; ++mt) {
+        if (mt > 0) inv4 = *reinterpret_cast<const f32x4*>(&lds_inv[buf][(mt - 1) * 16 + lgrp * 4]);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int ks = 0; ks < KS; ++ks) {
+          if (mt < MT) {
 #pragma unroll
-          for (int nt = 0; nt < kSearchNT; ++nt)
-            out[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar[ks], bt[nt][ks], out[nt], 0, 0, 0);
-      };
-      tile_mfma(0, acc[0]);
+            for (int nt = 0; nt < kSearchNT; ++nt)
+              acc[mt & 1][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  ar[ks], bt[nt][ks], ks ? acc[mt & 1][nt] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            if (mt + 1 < MT)
+              ar[ks] = *reinterpret_cast<const bf16x8*>(
+                  &lds_ref[buf][chunk_off<D>((mt + 1) * 16 + lrow, ks * 4 + lgrp)]);
+          }
+          if (mt > 0) {
+            // Elements of the C fragment spread over the K-steps (one per
+            // step for d = 128, two for d = 64).
+            const int pm = mt - 1;
 #pragma unroll
-      for (int mt = 0; mt < kSearchRefs / 16; ++mt) {
-        if (mt + 1 < kSearchRefs / 16) tile_mfma(mt + 1, acc[(mt + 1) & 1]);
-        const f32x4 inv4 = *reinterpret_cast<const f32x4*>(&lds_inv[buf][mt * 16 + lgrp * 4]);
+            for (int i = ks * 4 / KS; i < (ks + 1) * 4 / KS; ++i)
 #pragma unroll
-        for (int nt = 0; nt < kSearchNT; ++nt) {
-          uint32_t k[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            k[i] = (__float_as_uint(fmaf(acc[mt & 1][nt][i], inv4[i], off[nt])) & ~15u) | (uint32_t)(15 - (4 * mt + i));
-          ckey[nt] = max(max(max(k[0], k[1]), max(k[2], k[3])), ckey[nt]);
+              for (int nt = 0; nt < kSearchNT; ++nt) {
+                const uint32_t k = (__float_as_uint(fmaf(acc[pm & 1][nt][i], inv4[i], off[nt])) & ~15u) |
+                                   (uint32_t)(15 - (4 * pm + i));
+                ckey[nt] = max(ckey[nt], k);
+              }
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     } else if (rc < rend_w) {
@@ -349,7 +413,7 @@ __global__ __launch_bounds__(kSearchThreads) void k_search_mfma(CompressArgs a, 
           bf16x8 ar[KS];
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks)
-            ar[ks] = *reinterpret_cast<const bf16x8*>(&lds_ref[buf][(mt * 16 + lrow) * LDR + ks * 32 + lgrp * 8]);
+            ar[ks] = *reinterpret_cast<const bf16x8*>(&lds_ref[buf][chunk_off<D>(mt * 16 + lrow, ks * 4 + lgrp)]);
           f32x4 acc[kSearchNT];
 #pragma unroll
           for (int nt = 0; nt < kSearchNT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -367,14 +431,15 @@ __global__ __launch_bounds__(kSearchThreads) void k_search_mfma(CompressArgs a, 
           const int r0 = rbase + lgrp * 4;
 #pragma unroll
           for (int nt = 0; nt < kSearchNT; ++nt) {
-            const int t = tw + nt * 16 + lrow;
             uint32_t k[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
               k[i] = (__float_as_uint(fmaf(acc[nt][i], inv[i], off[nt])) & ~15u) | (uint32_t)(15 - (4 * mt + i));
             if (masked) {
+              // Reference r0 + i precedes the token iff r0 + i < nprev.
+              const int lim = nprev[nt] - r0;
 #pragma unroll
-              for (int i = 0; i < 4; ++i) k[i] = (r0 + i) * sh.s < t ? k[i] : 0u;
+              for (int i = 0; i < 4; ++i) k[i] = i < lim ? k[i] : 0u;
             }
             ckey[nt] = max(max(max(k[0], k[1]), max(k[2], k[3])), ckey[nt]);
           }
@@ -538,7 +603,10 @@ __global__ __launch_bounds__(kSearchThreads) void k_search_topk_mfma(CompressArg
       pre[j] = rc + row < rend_b ? *reinterpret_cast<const uint4*>(refs + (size_t)(rc + row) * D + col)
                                  : make_uint4(0, 0, 0, 0);
     }
-    if (tid < kSearchRefs) pn = rc + tid < rend_b ? nrm[rc + tid] : 0.f;
+    if (tid < kSearchRefs) {
+      const float v = nrm[min(rc + tid, rend_b - 1)];
+      pn = rc + tid < rend_b ? v : 0.f;
+    }
   };
   auto stash = [&](int buf) {
 #pragma unroll
@@ -553,23 +621,17 @@ __global__ __launch_bounds__(kSearchThreads) void k_search_topk_mfma(CompressArg
 
   // B operands: the centred tokens rnd(x - mu), as in k_search_mfma.
   bf16x8 bt[kSearchNT][KS];
+  {
+    uint4 xr[kSearchNT][KS], mr[KS];
+    load_tokens<D>(src, a.st, mu, tw, sh.T, lrow, lgrp, xr, mr);
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const int c = ks * 32 + lgrp * 8;
-    float m[8];
-    load8(mu + c, m);
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-    for (int nt = 0; nt < kSearchNT; ++nt) {
-      const int t = tw + nt * 16 + lrow;
-      uint32_t w[4] = {0u, 0u, 0u, 0u};
-      if (t < sh.T) {
-        float x[8];
-        load8(src + (int64_t)t * a.st + c, x);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = pk_bf16_rn(x[2 * e] - m[2 * e], x[2 * e + 1] - m[2 * e + 1]);
+      for (int nt = 0; nt < kSearchNT; ++nt) {
+        uint32_t w[4];
+        centre8(xr[nt][ks], mr[ks], w);
+        bt[nt][ks] = __builtin_bit_cast(bf16x8, w);
       }
-      bt[nt][ks] = __builtin_bit_cast(bf16x8, w);
-    }
   }
 
   TopKN<KT> top[kSearchNT];
