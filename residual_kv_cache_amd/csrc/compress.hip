@@ -180,7 +180,7 @@ __global__ __launch_bounds__(256) void k_center_refs(CompressArgs a, Shape sh) {
 // Block = 8 waves = 256 consecutive positions of one stream; wave w owns 32
 // of them (2 MFMA N-tiles of 16 tokens).  The centred tokens x~_t are built
 // once in registers as MFMA B operands (exact bf16).  References stream
-// through LDS in double-buffered chunks of 64 (4 M-tiles of 16; the next
+// through LDS in double-buffered chunks of 128 (8 M-tiles of 16; the next
 // chunk is fetched into registers while the current one is used); each
 // M-tile x N-tile block of scores is an MFMA 16x16x32 chain over the head
 // dim.  The C fragment of lane l holds references 4*(l/16)+i (i = 0..3) for
@@ -191,7 +191,11 @@ __global__ __launch_bounds__(256) void k_center_refs(CompressArgs a, Shape sh) {
 // token merge at the end (larger key, then lower ordinal).
 // ---------------------------------------------------------------------------
 
-constexpr int kSearchRefs = 64;   // references per LDS chunk
+constexpr int kSearchRefs = 64;   // references per LDS chunk (k references)
+constexpr int kTop1Refs = 128;    // references per LDS chunk (top-1 search)
+// Low key bits that hold a candidate's place in its top-1 chunk: each lane
+// sees 4 of every 16 references, kTop1Refs / 4 places.
+constexpr uint32_t kPlaceMask = kTop1Refs / 4 - 1;
 constexpr int kSearchWaves = 8;
 constexpr int kSearchNT = 2;                    // 16-token MFMA tiles per wave
 constexpr int kSearchThreads = 64 * kSearchWaves;
@@ -231,6 +235,17 @@ __device__ __forceinline__ void centre8(uint4 x, uint4 m, uint32_t* w) {
 // untyped loads return the bytes as stored; a load at or past the size in
 // word 2 (bytes, for stride 0) returns zeros.
 constexpr int kBufferRsrcWord3 = 0x00020000;
+// Buffer load of 16 bytes per lane straight into LDS: lane l's bytes land
+// at lds + 16 l; lds is wave-uniform and below 64 KB (the load takes its LDS
+// address from the low 16 bits of M0).
+__device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
+
+// s_waitcnt operand that waits for every vector memory operation (vmcnt 0)
+// and leaves the export and LDS counters free (gfx9 encoding).
+constexpr int kWaitVm0 = 0x0F70;
 
 // Element offset of 16-byte piece pc of row `row` in an LDS reference chunk
 // (unpadded rows of D / 8 pieces).  The piece index is XORed with the row
@@ -246,9 +261,11 @@ __device__ __forceinline__ int chunk_off(int row, int pc) {
 template <int D>
 __global__ __launch_bounds__(kSearchThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_search_mfma(CompressArgs a, Shape sh) {
   constexpr int KS = D / 32;      // MFMA K-steps over the head dim
-  constexpr int PER = kSearchRefs * (D / 8) / kSearchThreads;   // 16-byte pieces per thread per chunk
-  __shared__ __attribute__((aligned(16))) uint16_t lds_ref[2][kSearchRefs * D];
-  __shared__ float lds_inv[2][kSearchRefs];
+  // Two chunk buffers as separate arrays: the loop below alternates them
+  // statically, so the compiler sees that reads of one never wait for the
+  // LDS loads into the other.
+  __shared__ __attribute__((aligned(16))) uint16_t lds_ref0[kTop1Refs * D], lds_ref1[kTop1Refs * D];
+  __shared__ float lds_inv0[kTop1Refs], lds_inv1[kTop1Refs];
 
   const XcdItem xi = xcd_item(sh.n_streams());
   if (xi.stream < 0) return;
@@ -270,40 +287,45 @@ __global__ __launch_bounds__(kSearchThreads) __attribute__((amdgpu_waves_per_eu(
   const int rend_b = (tmax_b + sh.s - 1) / sh.s;
   const int tmax_w = min(sh.T - 1, tw + 16 * kSearchNT - 1);
   const int rend_w = tw < sh.T ? (tmax_w + sh.s - 1) / sh.s : 0;
-  const int nchunks = (rend_b + kSearchRefs - 1) / kSearchRefs;
+  const int nchunks = (rend_b + kTop1Refs - 1) / kTop1Refs;
 
-  // Chunk staging: global -> registers (one chunk ahead) -> LDS.
-  // Chunk loads through buffer descriptors whose base is the chunk's first
-  // row and whose size covers the rows that exist (r < rend_b): rows past
-  // the end read as zeros with no compare or branch, and each thread's byte
-  // offsets are the same for every chunk.
-  uint4 pre[PER];
+  // Chunk loads go straight from global memory to LDS (buffer loads with
+  // the LDS flag, issued one chunk ahead): each wave instruction fills 1 KB of
+  // the chunk, lane l its 16-byte piece l, so lane l reads the global piece
+  // that the swizzle places there (the XOR swizzle is its own inverse).  The
+  // buffer descriptor's base is the chunk's first row and its size covers the
+  // rows that exist (r < rend_b), so rows past the end read as zeros with no
+  // compare or branch; each lane's offsets are the same for every chunk.
+  constexpr int NI = kTop1Refs * D * 2 / (kSearchWaves * 1024);   // 1 KB loads per wave per chunk
+  uint32_t voff[NI];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int q = (wave * NI + j) * 64 + lane;   // 16-byte piece of the chunk in LDS order
+    voff[j] = (uint32_t)chunk_off<D>(q / (D / 8), q % (D / 8)) * 2;
+  }
   float pinv = 0.f;
-  auto fetch = [&](int ch) {
-    const int rc = ch * kSearchRefs;
+  auto fetch = [&](int ch, uint16_t* dref, float* dinv) {
+    const int rc = ch * kTop1Refs;
     const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(refs + (size_t)rc * D), (short)0, (rend_b - rc) * D * 2, kBufferRsrcWord3);
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int p = tid + j * kSearchThreads;
-      pre[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, p * 16, 0, 0));
-    }
-    if (tid < kSearchRefs) {
+    for (int j = 0; j < NI; ++j)
+      load_to_lds16(rr, dref + (wave * NI + j) * 512, voff[j]);
+    if (tid < kTop1Refs) {
       const __amdgpu_buffer_rsrc_t rn = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(inv_n + rc), (short)0, (rend_b - rc) * 4, kBufferRsrcWord3);
       pinv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rn, tid * 4, 0, 0));
     }
+    (void)dinv;
   };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int p = tid + j * kSearchThreads;
-      const int row = p / (D / 8), col = (p % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(&lds_ref[buf][chunk_off<D>(row, col >> 3)]) = pre[j];
-    }
-    if (tid < kSearchRefs) lds_inv[buf][tid] = pinv;
+  // The norm terms go through a register and an LDS store (placed before
+  // the barrier that publishes the chunk): the direct LDS loads take their
+  // LDS address from the low 16 bits of M0, so only the two reference
+  // buffers, the first 64 KB of the block's LDS, are filled that way.
+  auto stash_inv = [&](float* dinv) {
+    if (tid < kTop1Refs) dinv[tid] = pinv;
   };
-  if (nchunks > 0) fetch(0);
+  if (nchunks > 0) fetch(0, lds_ref0, lds_inv0);
 
   // B operands: centred tokens rnd(x - mu), [N-tile][K-step], and their
   // squared norms.
@@ -330,13 +352,14 @@ __global__ __launch_bounds__(kSearchThreads) __attribute__((amdgpu_waves_per_eu(
   // Selection keys.  A candidate's score <x~_t, x~_r> / ||x~_r|| lies in
   // [-||x~_t||, ||x~_t||]; adding off = 2 ||x~_t|| (+ a tiny constant, so that
   // keys of a zero token stay positive) makes every key a positive float, so
-  // keys order as unsigned integers.  The low 4 bits of a key are replaced by
-  // 15 - (4 mt + i), the candidate's place in its 64-reference chunk, so an
+  // keys order as unsigned integers.  The low 5 bits of a key are replaced by
+  // 31 - (4 mt + i), the candidate's place in its 128-reference chunk, so an
   // integer max picks the best score and, among equal scores, the lowest
-  // ordinal; the change is below 2^-19 relative to the key, far inside the
-  // 1e-4 cosine margin within which any near-best reference is accepted.
-  // Across chunks a lane keeps the earlier chunk unless the new chunk's key
-  // is strictly larger above those 4 bits.
+  // ordinal; the change is below 2^-18 relative to the key (below 1.2e-5 in
+  // cosine, as keys are at most 3 ||x~_t||), inside the 1e-4 cosine margin
+  // within which any near-best reference is accepted.  Across chunks a lane
+  // keeps the earlier chunk unless the new chunk's key is strictly larger
+  // above those 5 bits.
   float off[kSearchNT];
 #pragma unroll
   for (int nt = 0; nt < kSearchNT; ++nt) {
@@ -352,15 +375,18 @@ __global__ __launch_bounds__(kSearchThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
   for (int nt = 0; nt < kSearchNT; ++nt) nprev[nt] = (tw + nt * 16 + lrow + sh.s - 1) / sh.s;
 
-  if (nchunks > 0) stash(0);
+  // The chunk's LDS loads have landed (vmcnt 0) before the barrier.
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  if (nchunks > 0) stash_inv(lds_inv0);
   __syncthreads();
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const int rc = ch * kSearchRefs;
-    const int buf = ch & 1;
-    if (ch + 1 < nchunks) fetch(ch + 1);
+  // One chunk: fetch the next one into (nref, ninv) while this one (cref,
+  // cinv) is scored.
+  auto chunk = [&](int ch, const uint16_t* cref, const float* cinv, uint16_t* nref, float* ninv) {
+    const int rc = ch * kTop1Refs;
+    if (ch + 1 < nchunks) fetch(ch + 1, nref, ninv);
     uint32_t ckey[kSearchNT] = {};
-    const int nmt = min(kSearchRefs / 16, (rend_w - rc + 15) / 16);
-    if (rc < rend_w && nmt == kSearchRefs / 16 && (rc + kSearchRefs - 1) * sh.s < tw) {
+    const int nmt = min(kTop1Refs / 16, (rend_w - rc + 15) / 16);
+    if (rc < rend_w && nmt == kTop1Refs / 16 && (rc + kTop1Refs - 1) * sh.s < tw) {
       // Fast path: a full chunk entirely before the wave's first position
       // needs no causal mask.  The issue order is fixed by hand: K-step ks of
       // tile mt issues its two MFMAs, refills the A-fragment register it has
@@ -368,16 +394,16 @@ __global__ __launch_bounds__(kSearchThreads) __attribute__((amdgpu_waves_per_eu(
       // cover), then computes the keys of element ks of tile mt - 1 (three
       // VALU operations per token tile), so one wave keeps the matrix core
       // and the VALU busy together.
-      constexpr int MT = kSearchRefs / 16;
+      constexpr int MT = kTop1Refs / 16;
       bf16x8 ar[KS];
       f32x4 acc[2][kSearchNT];
       f32x4 inv4;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        ar[ks] = *reinterpret_cast<const bf16x8*>(&lds_ref[buf][chunk_off<D>(lrow, ks * 4 + lgrp)]);
+        ar[ks] = *reinterpret_cast<const bf16x8*>(&cref[chunk_off<D>(lrow, ks * 4 + lgrp)]);
 #pragma unroll
       for (int mt = 0; mt <= MT; ++mt) {
-        if (mt > 0) inv4 = *reinterpret_cast<const f32x4*>(&lds_inv[buf][(mt - 1) * 16 + lgrp * 4]);
+        if (mt > 0) inv4 = *reinterpret_cast<const f32x4*>(&cinv[(mt - 1) * 16 + lgrp * 4]);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           if (mt < MT) {
@@ -387,7 +413,7 @@ __global__ __launch_bounds__(kSearchThreads) __attribute__((amdgpu_waves_per_eu(
                   ar[ks], bt[nt][ks], ks ? acc[mt & 1][nt] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
             if (mt + 1 < MT)
               ar[ks] = *reinterpret_cast<const bf16x8*>(
-                  &lds_ref[buf][chunk_off<D>((mt + 1) * 16 + lrow, ks * 4 + lgrp)]);
+                  &cref[chunk_off<D>((mt + 1) * 16 + lrow, ks * 4 + lgrp)]);
           }
           if (mt > 0) {
             // Elements of the C fragment spread over the K-steps (one per
@@ -397,8 +423,8 @@ __global__ __launch_bounds__(kSearchThreads) __attribute__((amdgpu_waves_per_eu(
             for (int i = ks * 4 / KS; i < (ks + 1) * 4 / KS; ++i)
 #pragma unroll
               for (int nt = 0; nt < kSearchNT; ++nt) {
-                const uint32_t k = (__float_as_uint(fmaf(acc[pm & 1][nt][i], inv4[i], off[nt])) & ~15u) |
-                                   (uint32_t)(15 - (4 * pm + i));
+                const uint32_t k = (__float_as_uint(fmaf(acc[pm & 1][nt][i], inv4[i], off[nt])) & ~kPlaceMask) |
+                                   (uint32_t)(kPlaceMask - (4 * pm + i));
                 ckey[nt] = max(ckey[nt], k);
               }
           }
@@ -407,13 +433,13 @@ __global__ __launch_bounds__(kSearchThreads) __attribute__((amdgpu_waves_per_eu(
       }
     } else if (rc < rend_w) {
 #pragma unroll
-      for (int mt = 0; mt < kSearchRefs / 16; ++mt) {
+      for (int mt = 0; mt < kTop1Refs / 16; ++mt) {
         if (mt < nmt) {
           const int rbase = rc + mt * 16;
           bf16x8 ar[KS];
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks)
-            ar[ks] = *reinterpret_cast<const bf16x8*>(&lds_ref[buf][chunk_off<D>(mt * 16 + lrow, ks * 4 + lgrp)]);
+            ar[ks] = *reinterpret_cast<const bf16x8*>(&cref[chunk_off<D>(mt * 16 + lrow, ks * 4 + lgrp)]);
           f32x4 acc[kSearchNT];
 #pragma unroll
           for (int nt = 0; nt < kSearchNT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -424,7 +450,7 @@ __global__ __launch_bounds__(kSearchThreads) __attribute__((amdgpu_waves_per_eu(
               acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar[ks], bt[nt][ks], acc[nt], 0, 0, 0);
           float inv[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) inv[i] = lds_inv[buf][mt * 16 + lgrp * 4 + i];
+          for (int i = 0; i < 4; ++i) inv[i] = cinv[mt * 16 + lgrp * 4 + i];
           // A tile needs the causal mask when its last reference is not
           // earlier than the wave's first position.
           const bool masked = (rbase + 15) * sh.s >= tw;
@@ -434,7 +460,7 @@ __global__ __launch_bounds__(kSearchThreads) __attribute__((amdgpu_waves_per_eu(
             uint32_t k[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              k[i] = (__float_as_uint(fmaf(acc[nt][i], inv[i], off[nt])) & ~15u) | (uint32_t)(15 - (4 * mt + i));
+              k[i] = (__float_as_uint(fmaf(acc[nt][i], inv[i], off[nt])) & ~kPlaceMask) | (uint32_t)(kPlaceMask - (4 * mt + i));
             if (masked) {
               // Reference r0 + i precedes the token iff r0 + i < nprev.
               const int lim = nprev[nt] - r0;
@@ -449,21 +475,26 @@ __global__ __launch_bounds__(kSearchThreads) __attribute__((amdgpu_waves_per_eu(
     // A chunk without keys leaves ckey = 0, which never replaces the best.
 #pragma unroll
     for (int nt = 0; nt < kSearchNT; ++nt) {
-      const bool g = (ckey[nt] & ~15u) > (bkey[nt] & ~15u);
+      const bool g = (ckey[nt] & ~kPlaceMask) > (bkey[nt] & ~kPlaceMask);
       bkey[nt] = g ? ckey[nt] : bkey[nt];
       bch[nt] = g ? ch : bch[nt];
     }
-    if (ch + 1 < nchunks) stash(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    if (ch + 1 < nchunks) stash_inv(ninv);
     __syncthreads();
+  };
+  for (int ch = 0; ch < nchunks; ch += 2) {
+    chunk(ch, lds_ref0, lds_inv0, lds_ref1, lds_inv1);
+    if (ch + 1 < nchunks) chunk(ch + 1, lds_ref1, lds_inv1, lds_ref0, lds_inv0);
   }
 
   // Merge the four lane groups of each token (larger key above the place
   // bits, then lower ordinal); lanes 0..15 write.
 #pragma unroll
   for (int nt = 0; nt < kSearchNT; ++nt) {
-    const int q = 15 - (int)(bkey[nt] & 15u);
-    uint32_t v = bkey[nt] & ~15u;
-    int r = bch[nt] * kSearchRefs + (q >> 2) * 16 + lgrp * 4 + (q & 3);
+    const int q = (int)kPlaceMask - (int)(bkey[nt] & kPlaceMask);
+    uint32_t v = bkey[nt] & ~kPlaceMask;
+    int r = bch[nt] * kTop1Refs + (q >> 2) * 16 + lgrp * 4 + (q & 3);
 #pragma unroll
     for (int o = 16; o <= 32; o <<= 1) {
       const uint32_t v2 = (uint32_t)__shfl_xor((int)v, o, 64);
