@@ -721,7 +721,15 @@ __global__ __launch_bounds__(kSearchThreads) void k_search_topk_mfma(CompressArg
               any = true;
             }
           }
-          if (any) top[nt].kth(K, ths[nt], thr[nt]);
+          if (any) {
+            // Pass threshold: the largest k-th score of the token's four
+            // lane lists.  The token's k best over all references score at
+            // least that much, so a candidate below it can never be kept;
+            // ties pass and the insertion applies the exact order.
+            top[nt].kth(K, ths[nt], thr[nt]);
+            ths[nt] = fmaxf(ths[nt], __shfl_xor(ths[nt], 16, 64));
+            ths[nt] = fmaxf(ths[nt], __shfl_xor(ths[nt], 32, 64));
+          }
         }
       }
     }
