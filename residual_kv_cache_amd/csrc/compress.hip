@@ -304,7 +304,7 @@ __global__ __launch_bounds__(kSearchThreads) __attribute__((amdgpu_waves_per_eu(
     voff[j] = (uint32_t)chunk_off<D>(q / (D / 8), q % (D / 8)) * 2;
   }
   float pinv = 0.f;
-  auto fetch = [&](int ch, uint16_t* dref, float* dinv) {
+  auto fetch = [&](int ch, uint16_t* dref) {
     const int rc = ch * kTop1Refs;
     const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(refs + (size_t)rc * D), (short)0, (rend_b - rc) * D * 2, kBufferRsrcWord3);
@@ -316,7 +316,6 @@ __global__ __launch_bounds__(kSearchThreads) __attribute__((amdgpu_waves_per_eu(
           (void*)(inv_n + rc), (short)0, (rend_b - rc) * 4, kBufferRsrcWord3);
       pinv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rn, tid * 4, 0, 0));
     }
-    (void)dinv;
   };
   // The norm terms go through a register and an LDS store (placed before
   // the barrier that publishes the chunk): the direct LDS loads take their
@@ -325,7 +324,7 @@ __global__ __launch_bounds__(kSearchThreads) __attribute__((amdgpu_waves_per_eu(
   auto stash_inv = [&](float* dinv) {
     if (tid < kTop1Refs) dinv[tid] = pinv;
   };
-  if (nchunks > 0) fetch(0, lds_ref0, lds_inv0);
+  if (nchunks > 0) fetch(0, lds_ref0);
 
   // B operands: centred tokens rnd(x - mu), [N-tile][K-step], and their
   // squared norms.
@@ -383,7 +382,7 @@ __global__ __launch_bounds__(kSearchThreads) __attribute__((amdgpu_waves_per_eu(
   // cinv) is scored.
   auto chunk = [&](int ch, const uint16_t* cref, const float* cinv, uint16_t* nref, float* ninv) {
     const int rc = ch * kTop1Refs;
-    if (ch + 1 < nchunks) fetch(ch + 1, nref, ninv);
+    if (ch + 1 < nchunks) fetch(ch + 1, nref);
     uint32_t ckey[kSearchNT] = {};
     const int nmt = min(kTop1Refs / 16, (rend_w - rc + 15) / 16);
     if (rc < rend_w && nmt == kTop1Refs / 16 && (rc + kTop1Refs - 1) * sh.s < tw) {

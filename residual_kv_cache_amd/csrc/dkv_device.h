@@ -119,8 +119,11 @@ __device__ __forceinline__ int q4_quant(float c, float scale) {
 
 constexpr int kTopMax = 8;
 
+// (s1, r1) ranks before (s2, r2): larger score, then lower ordinal.  Bitwise
+// operators, so all three comparisons are evaluated and combined as lane
+// masks (short-circuit forms become divergent branches).
 __device__ __forceinline__ bool ranks_before(float s1, int r1, float s2, int r2) {
-  return s1 > s2 || (s1 == s2 && r1 < r2);
+  return (s1 > s2) | ((s1 == s2) & (r1 < r2));
 }
 
 template <int KM>
