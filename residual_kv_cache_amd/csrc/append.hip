@@ -64,7 +64,7 @@ struct RowSlice {
 };
 
 __device__ __forceinline__ bool better(float s1, int r1, float s2, int r2) {
-  return s1 > s2 || (s1 == s2 && r1 < r2);
+  return (s1 > s2) | ((s1 == s2) & (r1 < r2));   // bitwise: no divergent branches
 }
 
 constexpr int kUnroll = 4;

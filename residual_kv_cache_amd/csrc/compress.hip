@@ -709,8 +709,8 @@ __global__ __launch_bounds__(kSearchThreads) void k_search_topk_mfma(CompressArg
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             v[i] = l2 ? fmaf(2.f, acc[nt][i], -nr[i]) : acc[nt][i] * nr[i];
-            const bool ok = !masked || ((r0 + i) * sh.s < t && t < sh.T);
-            want[i] = ok && v[i] >= ths[nt];
+            const bool ok = !masked | (((r0 + i) * sh.s < t) & (t < sh.T));
+            want[i] = ok & (v[i] >= ths[nt]);
           }
           bool any = false;
 #pragma unroll
