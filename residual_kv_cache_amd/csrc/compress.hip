@@ -591,7 +591,7 @@ __global__ __launch_bounds__(256) void k_search_f32(CompressArgs a, Shape sh) {
 // candidate slot, only when some lane of the wave has a candidate that
 // passes.  Lists hold KT >= k entries (4 or 8).  At the end the four lane
 // groups of a token merge their lists and lane group 0 writes the ordinals.
-template <int D, int KT>
+template <int D, int KT, bool KFULL>
 __global__ __launch_bounds__(kSearchThreads) void k_search_topk_mfma(CompressArgs a, Shape sh) {
   constexpr int KS = D / 32;
   constexpr int LDR = D + 8;
@@ -606,7 +606,7 @@ __global__ __launch_bounds__(kSearchThreads) void k_search_topk_mfma(CompressArg
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lrow = lane & 15, lgrp = lane >> 4;
-  const int K = sh.K;
+  const int K = KFULL ? KT : sh.K;   // k equal to the list length: a compile-time constant
   const bool l2 = sh.l2 != 0;
   const StreamId id = decode_stream(stream, sh.H);
   const uint16_t* src = stream_src<BF16>(a, id);
@@ -1007,12 +1007,11 @@ hipError_t launch_compress_d(const Shape& sh, const CompressArgs& a, hipStream_t
     DKV_TRY(launch(k_center_refs<BF16>, g_ref, 256, st, ev_start(ev, 1), ev_stop(ev, 1), a, sh));
     if (sh.N > 0) {
       if (sh.topk_search()) {
-        if (sh.K <= 4)
-          DKV_TRY(launch(k_search_topk_mfma<D, 4>, g_search, kSearchThreads, st, ev_start(ev, 2), ev_stop(ev, 2), a,
-                         sh));
-        else
-          DKV_TRY(launch(k_search_topk_mfma<D, 8>, g_search, kSearchThreads, st, ev_start(ev, 2), ev_stop(ev, 2), a,
-                         sh));
+        auto kern = sh.K == 4   ? k_search_topk_mfma<D, 4, true>
+                    : sh.K < 4  ? k_search_topk_mfma<D, 4, false>
+                    : sh.K == 8 ? k_search_topk_mfma<D, 8, true>
+                                : k_search_topk_mfma<D, 8, false>;
+        DKV_TRY(launch(kern, g_search, kSearchThreads, st, ev_start(ev, 2), ev_stop(ev, 2), a, sh));
       } else {
         DKV_TRY(launch(k_search_mfma<D>, g_search, kSearchThreads, st, ev_start(ev, 2), ev_stop(ev, 2), a, sh));
       }
