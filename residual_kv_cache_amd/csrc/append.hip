@@ -285,7 +285,7 @@ __global__ __launch_bounds__(64) void k_append_finish(AppendArgs a, Shape sh, in
 // and encodes against the mean.
 // ---------------------------------------------------------------------------
 
-template <class S, int D>
+template <class S, int D, int KT, bool KFULL>
 __global__ __launch_bounds__(256) void k_append_search_topk(AppendArgs a, Shape sh, int chunk, int P, float2* part) {
   constexpr int E = D / 16;
   const XcdItem xi = xcd_item(sh.n_streams());
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(256) void k_append_search_topk(AppendArgs a, Shape 
   const int nref = t / sh.s + 1;
   const int r0 = p * chunk, r1 = min(nref, r0 + chunk);
   const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15;
-  const int K = sh.K;
+  const int K = KFULL ? KT : sh.K;   // k equal to the list length: a compile-time constant
   constexpr size_t e = sizeof(typename S::T);
   const char* refs = (const char*)a.refs + ((size_t)stream * sh.Rc * D + l16 * E) * e;
   RowSlice<S, E> row[kUnroll];
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(256) void k_append_search_topk(AppendArgs a, Shape 
 #pragma unroll
   for (int i = 0; i < E; ++i) x[i] = S::load(S::sub_rn(ks.at(i), ms.at(i)));
 
-  TopK top;
+  TopKN<KT> top;
   top.init();
   for (;;) {
 #pragma unroll
@@ -337,36 +337,36 @@ __global__ __launch_bounds__(256) void k_append_search_topk(AppendArgs a, Shape 
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) row[u].load(refs + (size_t)min(r + 16 * u, r1 - 1) * D * e);
   }
-  __shared__ float red_s[16][kTopMax];
-  __shared__ int red_r[16][kTopMax];
+  __shared__ float red_s[16][KT];
+  __shared__ int red_r[16][KT];
   if (l16 == 0) {
 #pragma unroll
-    for (int j = 0; j < kTopMax; ++j) {
+    for (int j = 0; j < KT; ++j) {
       red_s[grp][j] = top.s[j];
       red_r[grp][j] = top.r[j];
     }
   }
   __syncthreads();
   if (tid == 0) {
-    TopK all;
+    TopKN<KT> all;
     all.init();
     for (int g = 0; g < 16; ++g)
       for (int j = 0; j < K; ++j) all.insert(red_s[g][j], red_r[g][j], K);
     float2* out = part + ((size_t)stream * P + p) * K;
 #pragma unroll
-    for (int j = 0; j < kTopMax; ++j)
+    for (int j = 0; j < KT; ++j)
       if (j < K) out[j] = make_float2(all.s[j], __int_as_float(all.r[j]));
   }
 }
 
-template <class S, int D>
+template <class S, int D, int KT, bool KFULL>
 __global__ __launch_bounds__(256) void k_append_finish_topk(AppendArgs a, Shape sh, int P, const float2* part) {
   typedef typename S::T T;
   const int stream = blockIdx.x;
   const int kv = stream & 1, bh = stream >> 1, b = bh / sh.H, h = bh - b * sh.H;
   const int t = sh.T - 1;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int K = sh.K;
+  const int K = KFULL ? KT : sh.K;
   const T* src = (const T*)(kv ? a.v : a.k) + (int64_t)b * a.sb + (int64_t)h * a.sh;
   const T* mu = (const T*)a.mu + (size_t)stream * D;
   T* refs = (T*)a.refs + (size_t)stream * sh.Rc * D;
@@ -374,12 +374,12 @@ __global__ __launch_bounds__(256) void k_append_finish_topk(AppendArgs a, Shape 
     if (tid < D) refs[(size_t)(t / sh.s) * D + tid] = S::sub_rn(S::load(src[tid]), S::load(mu[tid]));
     return;
   }
-  __shared__ int s_ord[kTopMax];
+  __shared__ int s_ord[KT];
   __shared__ float diff[D];
   __shared__ float red[8];
   const int cnt = min(K, t / sh.s + 1);
   if (tid < 64) {
-    TopK top;
+    TopKN<KT> top;
     top.init();
     // Up to 8 list entries per lane in flight at once (clamped; a repeated
     // entry is masked out), then inserted.
@@ -396,23 +396,23 @@ __global__ __launch_bounds__(256) void k_append_finish_topk(AppendArgs a, Shape 
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) top.merge_xor(o, K);
     if (lane == 0) {
-      int o[kTopMax];
+      int o[KT];
       top.sorted_ordinals(cnt, o);
 #pragma unroll
-      for (int j = 0; j < kTopMax; ++j) s_ord[j] = o[j];
+      for (int j = 0; j < KT; ++j) s_ord[j] = o[j];
     }
   }
   __syncthreads();
   if (tid < D) {
     // Every kept reference row loaded at once (slots past the count read a
     // valid row and are masked), summed in slot order.
-    T rv[kTopMax];
+    T rv[KT];
 #pragma unroll
-    for (int j = 0; j < kTopMax; ++j) rv[j] = refs[(size_t)min(s_ord[min(j, cnt - 1)], sh.R - 1) * D + tid];
+    for (int j = 0; j < KT; ++j) rv[j] = refs[(size_t)min(s_ord[min(j, cnt - 1)], sh.R - 1) * D + tid];
     const T xk = src[tid], xm = mu[tid];
     float m = 0.f;
 #pragma unroll
-    for (int j = 0; j < kTopMax; ++j) m += j < cnt ? S::load(rv[j]) : 0.f;
+    for (int j = 0; j < KT; ++j) m += j < cnt ? S::load(rv[j]) : 0.f;
     m = cnt > 1 ? m * (1.0f / (float)cnt) : m;
     diff[tid] = (S::load(xk) - S::load(xm)) - m;
   }
@@ -468,13 +468,22 @@ hipError_t launch_append_sd(const Shape& sh, const AppendArgs& a, void* ws, hipS
   if (sh.topk_search()) {
     float2* part = (float2*)ws;
     hipError_t err;
+    // Lists of 4 or 8; k equal to the list length is a compile-time constant.
+    auto search = sh.K == 4   ? k_append_search_topk<S, D, 4, true>
+                  : sh.K < 4  ? k_append_search_topk<S, D, 4, false>
+                  : sh.K == 8 ? k_append_search_topk<S, D, 8, true>
+                              : k_append_search_topk<S, D, 8, false>;
+    auto finish = sh.K == 4   ? k_append_finish_topk<S, D, 4, true>
+                  : sh.K < 4  ? k_append_finish_topk<S, D, 4, false>
+                  : sh.K == 8 ? k_append_finish_topk<S, D, 8, true>
+                              : k_append_finish_topk<S, D, 8, false>;
     if (P > 0)
-      err = launch(k_append_search_topk<S, D>, dim3(xcd_grid(ns, P)), 256, st, ev[0], ev[1], a, sh,
-                   append_chunk(sh, t / sh.s + 1), P, part);
+      err = launch(search, dim3(xcd_grid(ns, P)), 256, st, ev[0], ev[1], a, sh, append_chunk(sh, t / sh.s + 1), P,
+                   part);
     else
       err = ev[0] ? launch(k_append_empty, dim3(1), 64, st, ev[0], ev[1]) : hipSuccess;
     if (err != hipSuccess) return err;
-    return launch(k_append_finish_topk<S, D>, dim3(ns), 256, st, ev[2], ev[3], a, sh, P, (const float2*)part);
+    return launch(finish, dim3(ns), 256, st, ev[2], ev[3], a, sh, P, (const float2*)part);
   }
   float2* part = (float2*)ws;
   void* pcode = (char*)ws + pcode_off(ns, std::max(P, 1));

@@ -41,7 +41,10 @@ def dev(raw: np.ndarray) -> torch.Tensor:
 
 
 def f64(t: torch.Tensor) -> np.ndarray:
-    return t.detach().float().cpu().numpy().astype(np.float64)
+    # Capacity rows past the written ones hold whatever the allocation held
+    # (possibly signalling-NaN bit patterns, which make the cast warn).
+    with np.errstate(invalid="ignore"):
+        return t.detach().float().cpu().numpy().astype(np.float64)
 
 
 def layout_of(cfg: K.Config) -> D.dkv_layout:

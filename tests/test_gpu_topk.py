@@ -172,7 +172,7 @@ def test_topk_selective(runs):
 
 
 @pytest.mark.parametrize("k,metric,bits,dtype", [(3, "l2", 0, "bf16"), (2, "cos", 4, "bf16"), (1, "l2", 0, "bf16"),
-                                                 (2, "l2", 0, "f32")])
+                                                 (2, "l2", 0, "f32"), (4, "l2", 0, "bf16"), (8, "cos", 0, "bf16")])
 def test_topk_append(k, metric, bits, dtype):
     base = BASE if dtype == "bf16" else TINY.replace(head_dim=128, code_dim=32)
     cfg = base.replace(name=f"tk_app_{k}{metric}{bits}{dtype}", seq_len=440, n_kv_heads=2, n_q_heads=4, stride=8)
