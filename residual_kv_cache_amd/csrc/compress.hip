@@ -181,9 +181,9 @@ __global__ __launch_bounds__(256) void k_center_refs(CompressArgs a, Shape sh) {
 // of them (2 MFMA N-tiles of 16 tokens).  The centred tokens x~_t are built
 // once in registers as MFMA B operands (exact bf16).  References stream
 // through LDS in double-buffered chunks of 128 (8 M-tiles of 16; the next
-// chunk is fetched into registers while the current one is used); each
-// M-tile x N-tile block of scores is an MFMA 16x16x32 chain over the head
-// dim.  The C fragment of lane l holds references 4*(l/16)+i (i = 0..3) for
+// chunk is loaded straight into the other LDS buffer while the current one
+// is used); each M-tile x N-tile block of scores is an MFMA 16x16x32 chain
+// over the head dim.  The C fragment of lane l holds references 4*(l/16)+i (i = 0..3) for
 // token l%16.  Scores are <x~_t, x~_r> / ||x~_r||: the token's own norm is
 // the same for every candidate and does not change the argmax.  Each score
 // becomes an integer selection key (see below) so that a lane's running
