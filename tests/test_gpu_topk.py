@@ -29,6 +29,9 @@ CASES = {
     # with fewer than k earlier references.
     "bf16_k8_l2_s3": (BASE.replace(name="tk_g", seq_len=1300, n_kv_heads=1, n_q_heads=4, stride=3), 8, "l2", 0),
     "bf16_k5_cos_b2": (BASE.replace(name="tk_h", seq_len=2500, n_kv_heads=2, n_q_heads=8, batch=2), 5, "cos", 0),
+    # d = 64 with k equal to the list length (the search's compile-time-k instantiation at this head size).
+    "bf16_d64_k4_cos": (BASE.replace(name="tk_i", head_dim=64, code_dim=16, stride=6, seq_len=1700, n_kv_heads=2,
+                                     n_q_heads=4), 4, "cos", 0),
 }
 
 
@@ -171,11 +174,15 @@ def test_topk_selective(runs):
     assert np.abs(out.cpu().numpy() - ref).max() <= GH.OUT_TOL[cfg.dtype]
 
 
-@pytest.mark.parametrize("k,metric,bits,dtype", [(3, "l2", 0, "bf16"), (2, "cos", 4, "bf16"), (1, "l2", 0, "bf16"),
-                                                 (2, "l2", 0, "f32"), (4, "l2", 0, "bf16"), (8, "cos", 0, "bf16")])
-def test_topk_append(k, metric, bits, dtype):
+@pytest.mark.parametrize("k,metric,bits,dtype,d", [(3, "l2", 0, "bf16", 128), (2, "cos", 4, "bf16", 128),
+                                                   (1, "l2", 0, "bf16", 128), (2, "l2", 0, "f32", 128),
+                                                   (4, "l2", 0, "bf16", 128), (8, "cos", 0, "bf16", 128),
+                                                   (4, "cos", 0, "bf16", 64)])
+def test_topk_append(k, metric, bits, dtype, d):
     base = BASE if dtype == "bf16" else TINY.replace(head_dim=128, code_dim=32)
-    cfg = base.replace(name=f"tk_app_{k}{metric}{bits}{dtype}", seq_len=440, n_kv_heads=2, n_q_heads=4, stride=8)
+    if d != base.head_dim:
+        base = base.replace(head_dim=d, code_dim=16)
+    cfg = base.replace(name=f"tk_app_{k}{metric}{bits}{dtype}{d}", seq_len=440, n_kv_heads=2, n_q_heads=4, stride=8)
     T0 = 400
     inp = GH.Inputs(cfg)
     lay0 = layout_of(cfg, k, metric, bits, seq_len=T0, capacity=cfg.seq_len + 5)
