@@ -219,10 +219,12 @@ __device__ __forceinline__ uint32_t div_s(uint32_t t, uint32_t s, uint32_t magic
   return q + (uint32_t)(t - q * s >= s);
 }
 
-// Lane k of each 16-lane row, broadcast over the row.
+// Lane k of each 16-lane row, broadcast over the row.  Every lane has a
+// valid source in these DPP patterns, so no "old" value is needed (plain DPP
+// moves with bound_ctrl: no initialising copy of the destination).
 template <int K>
 __device__ __forceinline__ int row_bcast(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, 0x150 + K, 0xF, 0xF, false);
+  return __builtin_amdgcn_mov_dpp(v, 0x150 + K, 0xF, 0xF, true);
 }
 
 // Tile tt of a run [t0, t1) of 16-token tiles starting at token `first`
@@ -447,10 +449,10 @@ struct State {
 // DPP lane moves within 16-lane rows: swap neighbours (quad_perm 1,0,3,2)
 // and rotate by 8.
 __device__ __forceinline__ uint32_t swap_pairs(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
 }
 __device__ __forceinline__ uint32_t ror8(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true);
 }
 
 // Value-code B operands of both groups from the one 16-byte load per lane
