@@ -84,13 +84,15 @@ typedef enum dkv_dtype {
  *   dtype        dkv_dtype of K, V, queries, W matrices and of refs/codes/mu
  *   head_dim     d; supported: 64 or 128
  *   code_dim     d_c; supported: a multiple of 16 with 16 <= d_c <= d
- *   stride       s >= 1 (s = 1 stores every token whole)
+ *   stride       s >= 1 (s = 1 stores every token whole); supported up
+ *                to 2^30
  *   idx_bytes    width of a stored reference ordinal: 2 (requires
  *                R_cap <= 65536) or 4
  *   n_kv_heads   H >= 1;  batch  B >= 1
  *   seq_len      T >= 1, tokens held in the cache
  *   capacity     tokens the arrays are sized for (T_cap >= T), so that
- *                tokens can be appended in place; 0 means T_cap = T
+ *                tokens can be appended in place; 0 means T_cap = T;
+ *                supported up to 2^30
  *   code_bits    0: codes in the storage dtype; 4: 4-bit codes, one scale
  *                per code row (DeltaKV explainer, Portuguese page, Resumo
  *                Técnico §4: the residuals cluster around zero and suit

@@ -58,9 +58,13 @@ design notes of the repository):
   * K and V search independently, each with its own mean and references.
 
 Parity status.  Every function here is pinned by a CPU test against
-something other than itself (brute force on tiny inputs, exact
-reconstruction when d_c = d, dense attention when s = 1, closed forms and
-invariants).  No function is "parity unpinned".
+something other than itself: brute force in plain Python loops on tiny
+inputs (search, top-k search, append, cosines, 4-bit quantization), exact
+reconstruction when d_c = d, dense attention when s = 1, closed forms
+(bytes per token and per decode step, counted from the arrays the oracle
+itself returns and from the workload shapes) and invariants.  The pins are
+listed in tests/test_oracle_pins.py; tests/test_oracle_mutations.py plants
+a plausible mistake in each function and checks that a pin catches it.
 """
 from __future__ import annotations
 
@@ -163,13 +167,13 @@ def dense_kv_bytes(n_layers, n_kv_heads, head_dim, seq_len, batch, elem_bytes=2)
     return 2 * n_layers * n_kv_heads * head_dim * elem_bytes * seq_len * batch
 
 
-def decode_effective_bytes(B, H, Hq, T, s, d, dc, storage, code_bits: int = 16) -> int:
+def decode_effective_bytes(B, H, Hq, T, s, d, dc, storage, code_bits: int = 16, top_k: int = 1) -> int:
     """Bytes one decode step must move at least once: both tensors' references,
     codes (and scales) and indices, V's mean, W_up of K and V, the query and
     the fp32 output.  K's mean is never needed (it shifts every score
     equally)."""
     e = ELEM_BYTES[storage]
-    a = cache_array_bytes(B, H, T, s, d, dc, storage, code_bits)
+    a = cache_array_bytes(B, H, T, s, d, dc, storage, code_bits, top_k)
     mu_v = B * H * d * e
     return (a["refs"] + a["codes"] + a.get("scales", 0) + a["idx"] + mu_v + 2 * d * dc * e + B * Hq * d * e
             + B * Hq * d * 4)

@@ -31,9 +31,12 @@ dkv_status check_layout(const dkv_layout* L, Shape* out) {
   if (L->top_k > 8) return DKV_ERR_UNSUPPORTED;
   if (L->head_dim != 64 && L->head_dim != 128) return DKV_ERR_UNSUPPORTED;
   if (L->code_dim % 16 != 0) return DKV_ERR_UNSUPPORTED;
-  if (cap > (1u << 30) || L->n_kv_heads > 4096 || L->batch > 65535) return DKV_ERR_UNSUPPORTED;
-  const uint32_t R = (L->seq_len + L->stride - 1) / L->stride;
-  const uint32_t Rc = (cap + L->stride - 1) / L->stride;
+  // Strides up to 2^30 (one reference per 2^30 tokens) keep every
+  // position and slot computation of the kernels inside int32.
+  if (cap > (1u << 30) || L->stride > (1u << 30) || L->n_kv_heads > 4096 || L->batch > 65535)
+    return DKV_ERR_UNSUPPORTED;
+  const uint64_t R = ((uint64_t)L->seq_len + L->stride - 1) / L->stride;
+  const uint64_t Rc = ((uint64_t)cap + L->stride - 1) / L->stride;
   if (L->idx_bytes == 2 && Rc > 65536) return DKV_ERR_UNSUPPORTED;
   const uint64_t streams = 2ull * L->batch * L->n_kv_heads;
   if (streams > 65535) return DKV_ERR_UNSUPPORTED;  // grid y limit of the stream axis

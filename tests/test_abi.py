@@ -79,10 +79,24 @@ def test_carve_offsets():
     (dict(head_dim=96), 6), (dict(code_dim=24), 6), (dict(code_dim=256), 2), (dict(stride=0), 2),
     (dict(seq_len=0), 2), (dict(n_kv_heads=0), 2), (dict(batch=0), 2), (dict(idx_bytes=3), 2),
     (dict(seq_len=65537 * 2, stride=2, idx_bytes=2), 6), (dict(dtype="f32"), 0),
+    (dict(stride=1 << 30), 0), (dict(stride=(1 << 30) + 1), 6), (dict(stride=1 << 31), 6),
+    (dict(stride=(1 << 32) - 1), 6), (dict(seq_len=(1 << 30) + 1, idx_bytes=4), 6),
 ])
 def test_layout_check(kw, code):
     _lib()
     assert D.dkv_layout_check(L(**kw)) == code
+
+
+@pytest.mark.parametrize("stride", [1 << 31, (1 << 32) - 1, (1 << 30) + 1])
+def test_huge_stride_is_rejected_everywhere(stride):
+    """A stride past 2^30 would wrap the reference count or turn negative
+    in the kernels' int arithmetic: every entry point rejects the layout."""
+    _lib()
+    lay = L(stride=stride)
+    assert D.dkv_layout_check(lay) == 6
+    assert D.dkv_cache_bytes(lay) == 0
+    assert D.dkv_compress_workspace_bytes(lay) == 0
+    assert D.dkv_decode_workspace_bytes(lay, 32) == 0
 
 
 def test_layout_version_and_dtype():

@@ -46,6 +46,13 @@ PINS = [
     P.test_topk_mean_residual_hand_case,
     lambda: P.test_topk_full_rank_reconstructs_exactly("l2"),
     P.test_topk_all_references_is_the_running_mean,
+    P.test_cosines_matches_plain_loop_integer_data,
+    P.test_cosines_matches_plain_loop_real_data_and_search,
+    lambda: P.test_decode_effective_bytes_counts_the_arrays("bf16", 16, 1),
+    lambda: P.test_decode_effective_bytes_counts_the_arrays("bf16", 4, 1),
+    lambda: P.test_decode_effective_bytes_counts_the_arrays("bf16", 16, 3),
+    P.test_decode_effective_bytes_llama8b_32k,
+    lambda: P.test_topk_ordinal_bytes_count_the_arrays(4),
 ]
 
 
@@ -282,6 +289,57 @@ def _stream_bytes_no_idx(T, s, d, dc, storage):
     return R * d * e + (T - R) * dc * e + d * e
 
 
+def _cos_raw_dot(xt, tok, ref, s):
+    return np.einsum("ij,ij->i", xt[tok], xt[ref * s])
+
+
+def _cos_one_norm(xt, tok, ref, s):
+    a, b = xt[tok], xt[ref * s]
+    den = np.sqrt(np.einsum("ij,ij->i", a, a))
+    return np.where(den > 0, np.einsum("ij,ij->i", a, b) / np.where(den > 0, den, 1.0), 0.0)
+
+
+def _cos_zero_is_one(xt, tok, ref, s):
+    a, b = xt[tok], xt[ref * s]
+    den = np.sqrt(np.einsum("ij,ij->i", a, a)) * np.sqrt(np.einsum("ij,ij->i", b, b))
+    return np.where(den > 0, np.einsum("ij,ij->i", a, b) / np.where(den > 0, den, 1.0), 1.0)
+
+
+def _cos_ref_is_token(xt, tok, ref, s):
+    a, b = xt[tok], xt[ref]          # ordinal used as a position
+    den = np.sqrt(np.einsum("ij,ij->i", a, a)) * np.sqrt(np.einsum("ij,ij->i", b, b))
+    return np.where(den > 0, np.einsum("ij,ij->i", a, b) / np.where(den > 0, den, 1.0), 0.0)
+
+
+_ORIG_DEB = OD.decode_effective_bytes
+_ORIG_CAB = OD.cache_array_bytes
+_ORIG_SB = OD.stream_bytes
+
+
+def _deb_zero(*a, **kw):
+    return 0
+
+
+def _deb_no_output(B, H, Hq, T, s, d, dc, storage, code_bits=16, top_k=1):
+    return _ORIG_DEB(B, H, Hq, T, s, d, dc, storage, code_bits, top_k) - B * Hq * d * 4
+
+
+def _deb_key_mean_too(B, H, Hq, T, s, d, dc, storage, code_bits=16, top_k=1):
+    return _ORIG_DEB(B, H, Hq, T, s, d, dc, storage, code_bits, top_k) + B * H * d * OD.ELEM_BYTES[storage]
+
+
+def _deb_one_ordinal(B, H, Hq, T, s, d, dc, storage, code_bits=16, top_k=1):
+    return _ORIG_DEB(B, H, Hq, T, s, d, dc, storage, code_bits, 1)
+
+
+def _cab_one_ordinal(B, H, T, s, d, dc, storage, code_bits=16, top_k=1):
+    return _ORIG_CAB(B, H, T, s, d, dc, storage, code_bits, 1)
+
+
+def _sb_one_ordinal(T, s, d, dc, storage, code_bits=16, top_k=1):
+    return _ORIG_SB(T, s, d, dc, storage, code_bits, 1)
+
+
 MUTATIONS = {
     "search: also sees the next (later) reference": ("search", _search_factory(see_next=True)),
     "search: ties to highest ordinal": ("search", _search_factory(last_tie=True)),
@@ -317,6 +375,16 @@ MUTATIONS = {
     "top-k: ties to the higher ordinal": ("search_topk", _topk_last_tie),
     "top-k: mean divides by k, not the count": ("mean_refs", _mean_by_k),
     "top-k: residual against the first reference only": ("mean_refs", _mean_first_only),
+    "cosines: raw dot product, no normalisation": ("cosines", _cos_raw_dot),
+    "cosines: only the token's norm": ("cosines", _cos_one_norm),
+    "cosines: a zero vector gives 1": ("cosines", _cos_zero_is_one),
+    "cosines: ordinal read as a position": ("cosines", _cos_ref_is_token),
+    "decode bytes: zero": ("decode_effective_bytes", _deb_zero),
+    "decode bytes: output forgotten": ("decode_effective_bytes", _deb_no_output),
+    "decode bytes: K's mean counted": ("decode_effective_bytes", _deb_key_mean_too),
+    "decode bytes: one ordinal per row whatever k": ("decode_effective_bytes", _deb_one_ordinal),
+    "array bytes: one ordinal per row whatever k": ("cache_array_bytes", _cab_one_ordinal),
+    "stream bytes: one ordinal per row whatever k": ("stream_bytes", _sb_one_ordinal),
 }
 
 

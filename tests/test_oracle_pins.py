@@ -796,3 +796,125 @@ def test_topk_append_equals_compress(metric, k):
         assert a["idx"] == full["idx"][row].tolist()
         gap = np.abs(a["code"] - full["codes"][row])
         assert np.all(gap <= np.spacing(np.abs(full["codes"][row]).astype(np.float32)) * 256)
+
+
+# ---------------------------------------------------------------------------
+# Cosines of given (token, reference) pairs: the GPU checks accept a differing
+# ordinal only when its cosine, computed here, is within the margin of the
+# best, so this helper is pinned on its own against plain loops.
+# ---------------------------------------------------------------------------
+
+def test_cosines_matches_plain_loop_integer_data():
+    """Small integer vectors: every pair's dot product and norms are exact,
+    so the helper must equal the plain-loop cosine to the last bit of the
+    final division, including a token against itself (1) and zero rows (0)."""
+    rng = np.random.default_rng(31)
+    T, s, d = 60, 3, 5
+    xt = rng.integers(-2, 3, size=(T, d)).astype(np.float64)
+    xt[7] = 0.0    # a zero token
+    xt[9] = 0.0    # a zero reference (position 9 = ordinal 3)
+    toks = np.array([t for t in range(T) for r in range(-(-T // s))], np.int64)
+    refs = np.array([r for t in range(T) for r in range(-(-T // s))], np.int64)
+    got = O.cosines(xt, toks, refs, s)
+    want = [_py_cos(xt[t].tolist(), xt[r * s].tolist()) for t, r in zip(toks, refs)]
+    assert np.allclose(got, want, rtol=0, atol=1e-15)
+    assert np.all(got[(toks == 7) | (refs == 3)] == 0.0)
+    self_pairs = (toks == refs * s) & (toks != 9)
+    assert np.allclose(got[self_pairs], 1.0, rtol=0, atol=1e-15)
+
+
+def test_cosines_matches_plain_loop_real_data_and_search():
+    """Real vectors: the helper equals the plain-loop cosine, and for the
+    search's own choice it equals the search's reported best cosine; scaling
+    a token or a reference by a positive factor leaves it unchanged, and a
+    negated reference flips its sign."""
+    rng = np.random.default_rng(32)
+    T, s, d = 200, 7, 16
+    xt = rng.standard_normal((T, d))
+    toks = rng.integers(0, T, size=300)
+    refs = rng.integers(0, -(-T // s), size=300)
+    got = O.cosines(xt, toks, refs, s)
+    want = [_py_cos(xt[t].tolist(), xt[r * s].tolist()) for t, r in zip(toks, refs)]
+    assert np.allclose(got, want, rtol=0, atol=1e-14)
+    idx, top1, _ = O.search(xt, s)
+    nr = O.nonref_positions(T, s)
+    assert np.allclose(O.cosines(xt, nr, idx, s), top1, rtol=0, atol=1e-14)
+    y = xt.copy()
+    y[toks] *= 3.5
+    assert np.allclose(O.cosines(y, toks, refs, s), got, rtol=0, atol=1e-14)
+    z = xt.copy()
+    z[np.arange(-(-T // s)) * s] *= -1.0
+    flip = O.cosines(z, toks, refs, s)
+    same = toks % s != 0         # a token at a reference position is negated too
+    assert np.allclose(flip[same], -got[same], rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Bytes of one decode step and ordinal bytes with k references: counted from
+# the arrays the oracle returns and from the workload's sizes.
+# ---------------------------------------------------------------------------
+
+def _decode_inputs_bytes(cache, storage, q_shape, d, dc, code_bits):
+    """Bytes of what a decode step reads and writes, counted from the arrays
+    themselves: refs, codes (4-bit: d_c / 2 bytes per row and the scales)
+    and ordinals of K and V, V's shared component only, both W_up, the
+    query in the storage dtype and the fp32 output."""
+    e = O.ELEM_BYTES[storage]
+    R = cache["refs"].shape[-2]
+    n = cache["refs"].size
+    nb = n * e
+    nb += (cache["q"].size // 2 + cache["scales"].size * e) if code_bits == 4 else cache["codes"].size * e
+    nb += cache["idx"].size * O.idx_bytes_for(R)
+    nb += cache["mu"][:, :, 1].size * e
+    nb += 2 * d * dc * e
+    nb += int(np.prod(q_shape)) * (e + 4)
+    return nb
+
+
+@pytest.mark.parametrize("storage,code_bits,top_k", [("f32", 16, 1), ("bf16", 16, 1), ("bf16", 4, 1),
+                                                     ("bf16", 16, 3), ("f32", 16, 4)])
+def test_decode_effective_bytes_counts_the_arrays(storage, code_bits, top_k):
+    rng = np.random.default_rng(33)
+    B, H, Hq, T, s, d, dc = 2, 2, 6, 203, 8, 64, 16
+    k = O.rnd(rng.standard_normal((B, H, T, d)), storage)
+    v = O.rnd(rng.standard_normal((B, H, T, d)), storage)
+    w = np.linalg.qr(rng.standard_normal((d, dc)))[0]
+    cache = O.compress(k, v, s, w.T, w.T, storage, code_bits=code_bits, top_k=top_k)
+    want = _decode_inputs_bytes(cache, storage, (B, Hq, d), d, dc, code_bits)
+    assert O.decode_effective_bytes(B, H, Hq, T, s, d, dc, storage, code_bits=code_bits, top_k=top_k) == want
+
+
+def test_decode_effective_bytes_llama8b_32k():
+    """One Llama-3-8B-shaped layer at 32768 tokens (8 KV / 32 query heads,
+    d 128, s 16, d_c 32, bf16): 16 streams x 2048 reference rows x 256 B,
+    16 x 30720 coded rows x (64 B + 2 B), V's 8 means x 256 B, two 128 x 32
+    bf16 matrices, 32 bf16 query rows and 32 fp32 output rows."""
+    want = 16 * 2048 * 256 + 16 * 30720 * 66 + 8 * 256 + 2 * 128 * 32 * 2 + 32 * 128 * 2 + 32 * 128 * 4
+    assert want == 40_871_936
+    assert O.decode_effective_bytes(1, 8, 32, 32768, 16, 128, 32, "bf16") == want
+    # 4-bit codes: 16 B of nibbles and a 2-byte scale per coded row.
+    want4 = 16 * 2048 * 256 + 16 * 30720 * (16 + 2 + 2) + 8 * 256 + 2 * 128 * 32 * 2 + 32 * 128 * 6
+    assert O.decode_effective_bytes(1, 8, 32, 32768, 16, 128, 32, "bf16", code_bits=4) == want4
+    # 4 references per coded row: 4 ordinals of 2 bytes.
+    want_k4 = want + 16 * 30720 * 3 * 2
+    assert O.decode_effective_bytes(1, 8, 32, 32768, 16, 128, 32, "bf16", top_k=4) == want_k4
+
+
+@pytest.mark.parametrize("top_k", [2, 4, 8])
+def test_topk_ordinal_bytes_count_the_arrays(top_k):
+    """With k references every coded row stores k ordinals: the byte count
+    equals the size of the ordinal array the oracle returns, and per token
+    of a 32768-token stream (s 16, d 128, d_c 32, bf16) it is
+    16 + 60 + k * 1.875 bytes."""
+    rng = np.random.default_rng(34)
+    B, H, T, s, d, dc = 1, 2, 150, 5, 64, 16
+    k = rng.standard_normal((B, H, T, d))
+    v = rng.standard_normal((B, H, T, d))
+    w = np.linalg.qr(rng.standard_normal((d, dc)))[0]
+    cache = O.compress(k, v, s, w.T, w.T, "f32", top_k=top_k)
+    a = O.cache_array_bytes(B, H, T, s, d, dc, "f32", top_k=top_k)
+    assert cache["idx"].shape == (B, H, 2, T - O.n_refs(T, s), top_k)
+    assert a["idx"] == cache["idx"].size * 2
+    assert sum(a.values()) == B * H * 2 * O.stream_bytes(T, s, d, dc, "f32", top_k=top_k)
+    per_tok = (O.stream_bytes(32768, 16, 128, 32, "bf16", top_k=top_k) - 256) / 32768
+    assert per_tok == 16 + 60 + top_k * 1.875
