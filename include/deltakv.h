@@ -342,6 +342,25 @@ dkv_status deltakv_decode_attn(const dkv_layout* layout, const dkv_cache* cache,
                                void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * deltakv_decode_attn with its workspace taken from a device array the
+ * library holds, DKV_NOALLOC_SCRATCH_BYTES bytes on each GPU it runs on
+ * (created with the library's device code on that GPU and kept until the
+ * process ends).  The call allocates nothing.  Returns DKV_ERR_WORKSPACE,
+ * before touching the device, when dkv_decode_workspace_bytes(layout,
+ * n_q_heads, n_splits) exceeds that size (16 MiB covers, for example, 16
+ * sequences x 8 KV heads x 32768 tokens at stride 16).  Every call on a GPU
+ * uses that GPU's one array: calls that overlap on one GPU (different
+ * streams, or several threads) race and must not be issued; calls ordered
+ * on one stream are fine.  Arguments (no workspace) and results as
+ * deltakv_decode_attn, on the current device.
+ */
+#define DKV_NOALLOC_SCRATCH_BYTES (16u << 20)
+dkv_status deltakv_decode_attn_noalloc(const dkv_layout* layout, const dkv_cache* cache, const dkv_decode_in* in,
+                                       void* stream);
+
+/*
  * Decode attention over a chosen subset of the cached tokens: for each
  * sequence b, softmax(q k^_t^T * scale) v^_t over the entries t of row b of
  * sel->tokens, every other token left untouched (DeltaKV explainer, Spanish

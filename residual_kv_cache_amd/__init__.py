@@ -24,7 +24,8 @@ STATUS = {0: "DKV_OK", 1: "DKV_ERR_NULL", 2: "DKV_ERR_SHAPE", 3: "DKV_ERR_DTYPE"
 EXPORTS = ["dkv_abi_version", "dkv_status_str", "dkv_layout_check", "dkv_cache_bytes", "dkv_cache_carve",
            "dkv_compress_workspace_bytes", "dkv_decode_auto_splits", "dkv_decode_workspace_bytes",
            "dkv_append_workspace_bytes", "deltakv_compress", "deltakv_append", "deltakv_decode_attn",
-           "dkv_decode_sel_auto_splits", "deltakv_decode_attn_sel"]
+           "dkv_decode_sel_auto_splits", "deltakv_decode_attn_sel", "deltakv_decode_attn_noalloc"]
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class DeltaKVError(RuntimeError):
@@ -122,6 +123,7 @@ def lib() -> ctypes.CDLL:
                                      ctypes.c_size_t, ctypes.c_void_p]
         h.dkv_decode_sel_auto_splits.restype = ctypes.c_uint32
         h.dkv_decode_sel_auto_splits.argtypes = [P(dkv_layout), ctypes.c_uint32, ctypes.c_uint32]
+        h.deltakv_decode_attn_noalloc.argtypes = [P(dkv_layout), P(dkv_cache), P(dkv_decode_in), ctypes.c_void_p]
         h.deltakv_decode_attn_sel.argtypes = [P(dkv_layout), P(dkv_cache), P(dkv_decode_in), P(dkv_token_sel),
                                               ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         if h.dkv_abi_version() != ABI_VERSION:
@@ -279,6 +281,19 @@ def deltakv_decode_attn(layout: dkv_layout, cache: Cache, q: torch.Tensor, w_up_
                                      ctypes.c_void_p(_stream(stream))), "deltakv_decode_attn")
 
 
+def deltakv_decode_attn_noalloc(layout: dkv_layout, cache: Cache, q: torch.Tensor, w_up_k: torch.Tensor,
+                                w_up_v: torch.Tensor, out: torch.Tensor, n_splits: int = 0, softmax_scale: float = 0.0,
+                                w_head_stride: int = 0, stream=None, stage_events=None) -> None:
+    """deltakv_decode_attn on the library's own device scratch (no workspace
+    argument; nothing is allocated)."""
+    if not q.is_contiguous() or not out.is_contiguous() or out.dtype != torch.float32:
+        raise ValueError("q and out must be contiguous; out must be float32")
+    a = dkv_decode_in(_ptr(q), _ptr(w_up_k), _ptr(w_up_v), w_head_stride, q.shape[1], n_splits,
+                      softmax_scale, 0, _ptr(out), _events(stage_events))
+    _check(lib().deltakv_decode_attn_noalloc(ctypes.byref(layout), ctypes.byref(cache.c), ctypes.byref(a),
+                                             ctypes.c_void_p(_stream(stream))), "deltakv_decode_attn_noalloc")
+
+
 def deltakv_decode_attn_sel(layout: dkv_layout, cache: Cache, q: torch.Tensor, w_up_k: torch.Tensor,
                             w_up_v: torch.Tensor, tokens: torch.Tensor, out: torch.Tensor, ws: torch.Tensor,
                             n_splits: int = 0, softmax_scale: float = 0.0, w_head_stride: int = 0, stream=None,
@@ -329,7 +344,8 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
 
 __all__ = ["lib", "make_layout", "with_seq_len", "dkv_layout", "dkv_cache", "dkv_compress_in", "dkv_append_in",
            "dkv_decode_in", "dkv_token_sel", "Cache", "deltakv_append", "dkv_append_workspace_bytes",
-           "deltakv_decode_attn_sel", "dkv_decode_sel_auto_splits",
+           "deltakv_decode_attn_sel", "dkv_decode_sel_auto_splits", "deltakv_decode_attn_noalloc",
+           "NOALLOC_SCRATCH_BYTES",
            "DeltaKVError", "dkv_layout_check", "dkv_cache_bytes", "dkv_cache_carve", "dkv_compress_workspace_bytes",
            "dkv_decode_auto_splits", "dkv_decode_workspace_bytes", "deltakv_compress", "deltakv_decode_attn",
            "workspace", "storage_torch_dtype", "EXPORTS", "LIB_PATH"]

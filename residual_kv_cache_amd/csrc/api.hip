@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "dkv_internal.h"
 
 using dkv::Shape;
@@ -339,6 +341,64 @@ dkv_status deltakv_decode_attn(const dkv_layout* layout, const dkv_cache* cache,
   Shape sh;
   dkv::DecodeArgs a;
   const dkv_status st = decode_setup(layout, cache, in, ws, ws_bytes, stream, 0, &sh, &a);
+  if (st != DKV_OK) return st;
+  return from_hip(dkv::launch_decode(sh, a, (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of deltakv_decode_attn_noalloc: one array per GPU, part of the
+// library's device code, so it exists on every GPU the library runs on from
+// the time the code is loaded there until the process ends.  Host code uses
+// its device address from hipGetSymbolAddress (kept per device below), never
+// the array's name, which on the host is only a stand-in.  The decode
+// kernels write every byte they read in a call (scores, projected queries,
+// split records), so nothing in it has to start at zero.
+static __device__ __align__(256) unsigned char scratch[DKV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];   // device address of `scratch` on each device, once looked up
+
+// The current device's scratch address: looked up on the device's first
+// call (with that device current), then reused.
+dkv_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DKV_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DKV_ERR_DEVICE;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return DKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dkv_status deltakv_decode_attn_noalloc(const dkv_layout* layout, const dkv_cache* cache, const dkv_decode_in* in,
+                                       void* stream) {
+  // The shape's workspace must fit the scratch array; checked before the
+  // device is touched.
+  Shape sh;
+  dkv_status st = check_layout(layout, &sh);
+  if (st != DKV_OK) return st;
+  if (!in) return DKV_ERR_NULL;
+  if (in->n_q_heads == 0 || in->n_q_heads % sh.H != 0) return DKV_ERR_SHAPE;
+  if (in->n_q_heads / sh.H > 16) return DKV_ERR_UNSUPPORTED;
+  if (in->n_splits > 1024) return DKV_ERR_UNSUPPORTED;
+  const int G = (int)(in->n_q_heads / sh.H);
+  const int splits = in->n_splits ? (int)in->n_splits : (int)auto_splits(sh, G);
+  if (dkv::decode_ws_bytes(sh, G, splits) > (size_t)DKV_NOALLOC_SCRATCH_BYTES) return DKV_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != DKV_OK) return st;
+  dkv::DecodeArgs a;
+  st = decode_setup(layout, cache, in, ws, (size_t)DKV_NOALLOC_SCRATCH_BYTES, stream, 0, &sh, &a);
   if (st != DKV_OK) return st;
   return from_hip(dkv::launch_decode(sh, a, (hipStream_t)stream));
 }

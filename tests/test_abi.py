@@ -373,3 +373,19 @@ def test_selective_auto_splits_fit_the_decode_workspace(B, H, T, n_sel):
     assert 1 <= s <= D.dkv_decode_auto_splits(lay, 4 * H)
     assert s <= max(1, -(-n_sel // 256))
     assert D.dkv_decode_workspace_bytes(lay, 4 * H, s) <= D.dkv_decode_workspace_bytes(lay, 4 * H, 0)
+
+
+def test_noalloc_decode_rejects_oversized_shapes_before_the_device():
+    """The no-allocation decode refuses, before touching a device, a shape
+    whose workspace exceeds its fixed scratch (64 sequences x 8 heads x
+    32768 tokens need about 17 MB of reference scores alone)."""
+    _lib()
+    lay = L(batch=64)
+    assert D.dkv_decode_workspace_bytes(lay, 32) > D.NOALLOC_SCRATCH_BYTES
+    fake = ctypes.c_void_p(1 << 20)
+    cache = D.dkv_cache(fake, fake, fake, fake, None)
+    a = D.dkv_decode_in(fake, fake, fake, 0, 32, 0, 0.0, 0, fake, None)
+    st = D.lib().deltakv_decode_attn_noalloc(ctypes.byref(lay), ctypes.byref(cache), ctypes.byref(a), None)
+    assert st == 5   # DKV_ERR_WORKSPACE
+    lay.abi_version = 1
+    assert D.lib().deltakv_decode_attn_noalloc(ctypes.byref(lay), ctypes.byref(cache), ctypes.byref(a), None) == 7
