@@ -104,8 +104,9 @@ def test_append_matches_oracle(name):
     out = GH.gpu_decode(D.with_seq_len(lay0, T), cache, q.raw, inp)
     for b in range(cfg.batch):
         sub = {n: g[n][b:b + 1] for n in g}
-        ref = O.decode(_held_seq(sub, T, cfg.stride), q.f64[b:b + 1], inp.wuk.f64, inp.wuv.f64, cfg.stride, T)[0]
-        assert np.abs(out[b] - ref).max() <= GH.OUT_TOL[cfg.dtype]
+        held = _held_seq(sub, T, cfg.stride)
+        ref = O.decode(held, q.f64[b:b + 1], inp.wuk.f64, inp.wuv.f64, cfg.stride, T)[0]
+        GH.check_same_cache(out[b], ref, cfg.dtype, f"append {name} seq {b}", codes=held["codes"], n_tokens=T)
     GH.say(f"[gpu] append {name}: {T - T0} tokens appended, {exempt} inside the cosine margin; decode ok")
 
 
@@ -127,7 +128,8 @@ def test_decode_between_appends():
         for b in range(cfg.batch):
             sub = _held_seq({n: g[n][b:b + 1] for n in g}, T, cfg.stride)
             ref = O.decode(sub, q.f64[b:b + 1], inp.wuk.f64, inp.wuv.f64, cfg.stride, T)[0]
-            assert np.abs(outs[T][b] - ref).max() <= GH.OUT_TOL[cfg.dtype], (T, b)
+            GH.check_same_cache(outs[T][b], ref, cfg.dtype, f"after append T={T} seq {b}", codes=sub["codes"],
+                                n_tokens=T)
     GH.say(f"[gpu] decode between appends at {at}: ok")
 
 

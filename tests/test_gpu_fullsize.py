@@ -77,14 +77,16 @@ class Layer:
         cfg = self.cfg
         q = self.inp.q(step)
         out = GH.gpu_decode(self.lay, self.cache, q.raw, self.inp)
-        worst = 0.0
+        worst, bar = 0.0, GH.SAME_CACHE_TOL
         for b in seqs:
             ref = O.decode(seq_arrays(self.cache, b), q.f64[b:b + 1], self.inp.wuk.f64, self.inp.wuv.f64,
                            cfg.stride, cfg.seq_len)[0]
             worst = max(worst, float(np.abs(out[b] - ref).max()))
+            bar = max(bar, GH.same_cache_bar(ref))
         GH.say(f"[gpu] {cfg.name} decode step {step} seqs {list(seqs)}: max-abs {worst:.3g} "
                f"(splits {D.dkv_decode_auto_splits(self.lay, cfg.n_q_heads)})")
         assert worst <= GH.OUT_TOL[cfg.dtype]
+        assert worst <= bar, f"same-cache max-abs {worst:.3g} above {bar:.3g}"
 
 
 @pytest.fixture(scope="module")

@@ -66,9 +66,8 @@ def test_decode_on_same_cache_matches_oracle(name, small_runs):
         q = inp.q(step)
         out = GH.gpu_decode(lay, cache, q.raw, inp)
         ref = GH.oracle_decode_on(gc, q.f64, inp)
-        err = np.abs(out - ref).max()
-        GH.say(f"[gpu] {name} decode step {step}: max-abs {err:.3g}")
-        assert err <= GH.OUT_TOL[cfg.dtype]
+        GH.check_same_cache(out, ref, cfg.dtype, f"{name} decode step {step}", codes=gc["codes"],
+                            n_tokens=cfg.seq_len)
 
 
 @pytest.mark.parametrize("name", ["tiny", "bf16_ragged", "bf16_g3"])
@@ -92,7 +91,7 @@ def test_split_count_invariance(splits, small_runs):
     base = GH.gpu_decode(lay, cache, q.raw, inp, n_splits=1)
     out = GH.gpu_decode(lay, cache, q.raw, inp, n_splits=splits)
     ref = GH.oracle_decode_on(gc, q.f64, inp)
-    assert np.abs(out - ref).max() <= GH.OUT_TOL["bf16"]
+    GH.check_same_cache(out, ref, "bf16", f"splits {splits}", codes=gc["codes"])
     assert np.abs(out - base).max() <= 1e-5
 
 
@@ -115,7 +114,7 @@ def test_histogram_split_deterministic(small_runs):
         outs.append(out)
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
     o = outs[0].cpu().numpy().astype(np.float64)
-    assert np.abs(o - GH.oracle_decode_on(gc, q.f64, inp)).max() <= GH.OUT_TOL[cfg.dtype]
+    GH.check_same_cache(o, GH.oracle_decode_on(gc, q.f64, inp), cfg.dtype, "histogram split", codes=gc["codes"])
     assert np.abs(o - GH.gpu_decode(lay, cache, q.raw, inp, n_splits=64)).max() <= 1e-5
 
 
@@ -124,7 +123,7 @@ def test_softmax_scale_argument(small_runs):
     q = inp.q(0)
     out = GH.gpu_decode(lay, cache, q.raw, inp, scale=0.05)
     ref = GH.oracle_decode_on(gc, q.f64, inp, scale=0.05)
-    assert np.abs(out - ref).max() <= GH.OUT_TOL["bf16"]
+    GH.check_same_cache(out, ref, "bf16", "softmax scale 0.05", codes=gc["codes"])
 
 
 def test_deterministic_and_overwrites_everything(small_runs):
@@ -216,7 +215,7 @@ def test_per_head_matrices():
     vh = np.stack([O.reconstruct_stream(g["mu"][0, h, 1], g["refs"][0, h, 1], g["idx"][0, h, 1], g["codes"][0, h, 1],
                                         wd[2 + h].f64.T, cfg.stride, cfg.seq_len) for h in range(2)])
     ref = O.attend(q.f64[0], kh, vh, GH.default_scale(cfg))
-    assert np.abs(out.cpu().numpy()[0] - ref).max() <= GH.OUT_TOL["bf16"]
+    GH.check_same_cache(out.cpu().numpy()[0], ref, "bf16", "per-head matrices", codes=g["codes"])
 
 
 def test_handmade_ties_on_gpu():
@@ -241,3 +240,45 @@ def test_handmade_ties_on_gpu():
         assert np.array_equal(g["idx"][0, 0, kv][tie], r["idx"][tie])
         GH.check_stream(inp.k[0, 0], cfg.stride, inp.wdk.f64 if kv == 0 else inp.wdv.f64, "bf16",
                         {n: g[n][0, 0, kv] for n in g})
+
+
+@pytest.mark.parametrize("T,k,metric", [(1100, 1, "cos"), (2000, 1, "cos"), (1100, 2, "cos"), (1100, 4, "cos"),
+                                        (1500, 4, "l2")])
+def test_handmade_ties_across_chunks(T, k, metric):
+    """Exact ties spread over several search chunks (stride 4: 275 or more
+    references, so three or more 128-reference chunks of the top-1 search and
+    five or more 64-reference chunks of the top-k search): a later chunk wins
+    only with a strictly better score, and the merge of a token's lane groups
+    keeps the lower ordinal, so every tied set equals the oracle's exactly."""
+    cfg = BASE_BF16.replace(name="ties_x", seq_len=T, n_kv_heads=1, n_q_heads=4, stride=4)
+    rng = np.random.default_rng(5 + T + k)
+    d = cfg.head_dim
+    base = rng.integers(-3, 4, size=(6, d)).astype(np.float64)
+    x = base[rng.integers(0, 6, size=T)] + 5.0   # many exact duplicates, integer values
+    st = K.to_storage(x, "bf16")
+    inp = GH.Inputs(cfg)
+    inp.k_raw = st.raw[None, None].copy()
+    inp.v_raw = st.raw[None, None].copy()
+    inp.k = st.f64[None, None].copy()
+    inp.v = st.f64[None, None].copy()
+    lay = D.make_layout("bf16", d, cfg.code_dim, cfg.stride, 1, 1, T, top_k=k, metric=metric)
+    cache = D.Cache(lay)
+    ws = D.workspace(D.dkv_compress_workspace_bytes(lay))
+    D.deltakv_compress(lay, GH.dev(inp.k_raw), GH.dev(inp.v_raw), GH.dev(inp.wdk.raw), GH.dev(inp.wdv.raw), cache, ws)
+    torch.cuda.synchronize()
+    g = GH.cache_numpy(cache)
+    xt = O.center(inp.k[0, 0], O.shared_component(inp.k[0, 0], "bf16"), "bf16")
+    toks = O.nonref_positions(T, cfg.stride)
+    if k == 1 and metric == "cos":
+        idx_o, _, margin = O.search(xt, cfg.stride)
+        idx_o = idx_o[:, None]
+    else:
+        idx_o, _, margin = O.search_topk(xt, cfg.stride, k, metric)
+    tie = margin == 0.0
+    assert tie.sum() > 100, int(tie.sum())
+    for kv in (0, 1):
+        got = g["idx"][0, 0, kv].reshape(len(toks), k)
+        exact = tie | (margin > GH.MARGIN)
+        bad = np.any(got[exact] != idx_o[exact], axis=1)
+        assert not bad.any(), f"{int(bad.sum())} sets differ (first at t={toks[exact][bad][0]})"
+    GH.say(f"[gpu] ties across chunks T={T} k={k} {metric}: {int(tie.sum())} tied tokens, all sets exact")

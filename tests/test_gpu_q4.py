@@ -104,9 +104,7 @@ def test_q4_decode_matches_oracle(name, runs):
     q = inp.q(0)
     out = GH.gpu_decode(lay, cache, q.raw, inp)
     ref = GH.oracle_decode_on(gc, q.f64, inp)
-    err = float(np.abs(out - ref).max())
-    GH.say(f"[gpu] q4 decode {name}: max-abs {err:.3g}")
-    assert err <= GH.OUT_TOL[cfg.dtype]
+    GH.check_same_cache(out, ref, cfg.dtype, f"q4 decode {name}", codes=gc["codes"])
 
 
 @pytest.mark.parametrize("name", ["bf16_mfma_encode", "f32_dc32_s5"])
@@ -134,7 +132,7 @@ def test_q4_selective_matches_oracle(runs):
     D.deltakv_decode_attn_sel(lay, cache, GH.dev(q.raw), GH.dev(inp.wuk.raw), GH.dev(inp.wuv.raw), toks, out, ws)
     torch.cuda.synchronize()
     ref = O.decode_selected(gc, q.f64, inp.wuk.f64, inp.wuv.f64, cfg.stride, cfg.seq_len, sel)
-    assert np.abs(out.cpu().numpy() - ref).max() <= GH.OUT_TOL[cfg.dtype]
+    GH.check_same_cache(out.cpu().numpy(), ref, cfg.dtype, "q4 selective", codes=gc["codes"])
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -179,4 +177,4 @@ def test_q4_append(dtype):
     held = {n: (a[..., :O.n_refs(T, s), :] if n == "refs" else a[..., :T - O.n_refs(T, s), :] if n == "codes"
                 else a[..., :T - O.n_refs(T, s)] if n in ("idx", "scales") else a) for n, a in g.items() if n != "q"}
     ref = O.decode(held, inp.q(0).f64, inp.wuk.f64, inp.wuv.f64, s, T)
-    assert np.abs(out - ref).max() <= GH.OUT_TOL[cfg.dtype]
+    GH.check_same_cache(out, ref, cfg.dtype, "q4 append then decode", codes=held["codes"])

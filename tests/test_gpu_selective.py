@@ -89,6 +89,7 @@ def test_selective_matches_oracle(name, runs):
         GH.say(f"[gpu] selective {name} {lname} (n={sel.shape[1]}, splits "
                f"{D.dkv_decode_sel_auto_splits(lay, cfg.n_q_heads, sel.shape[1])}): max-abs {err:.3g}")
         assert err <= GH.OUT_TOL[cfg.dtype], lname
+        assert err <= GH.same_cache_bar(want, gc["codes"]), (lname, err)
 
 
 @pytest.mark.parametrize("splits", [1, 3, 64])
@@ -99,7 +100,7 @@ def test_selective_split_counts(splits, runs):
     q = inp.q(1)
     got = _gpu_sel(lay, cache, inp, q.raw, sel, n_splits=splits)
     want = O.decode_selected(gc, q.f64, inp.wuk.f64, inp.wuv.f64, cfg.stride, cfg.seq_len, sel)
-    assert np.abs(got - want).max() <= GH.OUT_TOL[cfg.dtype]
+    GH.check_same_cache(got, want, cfg.dtype, "selective", codes=gc["codes"])
 
 
 def test_selective_every_token_equals_full_decode(runs):
@@ -119,7 +120,7 @@ def test_selective_nothing_valid_gives_zeros(runs):
     got = _gpu_sel(lay, cache, inp, inp.q(0).raw, sel)
     assert np.all(got[0] == 0.0)
     want = O.decode_selected(gc, inp.q(0).f64, inp.wuk.f64, inp.wuv.f64, cfg.stride, T, sel)
-    assert np.abs(got[1] - want[1]).max() <= GH.OUT_TOL[cfg.dtype]
+    GH.check_same_cache(got[1], want[1], cfg.dtype, "selective seq 1", codes=gc["codes"])
 
 
 def test_selective_full_size_quarter_blocks():
@@ -140,3 +141,4 @@ def test_selective_full_size_quarter_blocks():
         err = float(np.abs(got - want).max())
         GH.say(f"[gpu] selective full size step {step}: {sel.shape[1]} tokens, max-abs {err:.3g}")
         assert err <= GH.OUT_TOL[cfg.dtype]
+        assert err <= GH.same_cache_bar(want, gc["codes"]), err

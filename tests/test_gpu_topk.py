@@ -143,7 +143,7 @@ def test_topk_decode_matches_oracle(name, runs):
     q = inp.q(0)
     out = GH.gpu_decode(lay, cache, q.raw, inp)
     ref = GH.oracle_decode_on(g, q.f64, inp)
-    err = float(np.abs(out - ref).max())
+    err = GH.check_same_cache(out, ref, cfg.dtype, "top-k decode", codes=g["codes"])
     GH.say(f"[gpu] top-k decode {name}: max-abs {err:.3g}")
     assert err <= GH.OUT_TOL[cfg.dtype]
 
@@ -171,7 +171,7 @@ def test_topk_selective(runs):
                               torch.from_numpy(sel.astype(np.int32)).cuda(), out, ws)
     torch.cuda.synchronize()
     ref = O.decode_selected(g, q.f64, inp.wuk.f64, inp.wuv.f64, cfg.stride, cfg.seq_len, sel)
-    assert np.abs(out.cpu().numpy() - ref).max() <= GH.OUT_TOL[cfg.dtype]
+    GH.check_same_cache(out.cpu().numpy(), ref, cfg.dtype, "top-k selective", codes=g["codes"])
 
 
 @pytest.mark.parametrize("k,metric,bits,dtype,d", [(3, "l2", 0, "bf16", 128), (2, "cos", 4, "bf16", 128),
@@ -223,4 +223,4 @@ def test_topk_append(k, metric, bits, dtype, d):
     R, N = O.n_refs(T, s), T - O.n_refs(T, s)
     held = {"mu": g["mu"], "refs": g["refs"][..., :R, :], "idx": g["idx"][..., :N, :], "codes": g["codes"][..., :N, :]}
     ref = O.decode(held, inp.q(0).f64, inp.wuk.f64, inp.wuv.f64, s, T)
-    assert np.abs(out - ref).max() <= GH.OUT_TOL[cfg.dtype]
+    GH.check_same_cache(out, ref, cfg.dtype, "top-k append then decode", codes=held["codes"])

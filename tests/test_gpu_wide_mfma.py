@@ -63,6 +63,7 @@ def test_wide_decode(wide):
     err = float(np.abs(out - ref).max())
     GH.say(f"[gpu] wide decode: max-abs {err:.3g}")
     assert err <= GH.OUT_TOL[CFG.dtype]
+    assert err <= GH.same_cache_bar(ref, gc["codes"]), err
 
 
 def test_wide_selective(wide):
@@ -83,6 +84,7 @@ def test_wide_selective(wide):
     err = float(np.abs(out.cpu().numpy() - ref).max())
     GH.say(f"[gpu] wide selective: max-abs {err:.3g}")
     assert err <= GH.OUT_TOL[CFG.dtype]
+    assert err <= GH.same_cache_bar(ref, gc["codes"]), err
 
 
 def test_wide_two_references(wide):
@@ -109,3 +111,4 @@ def test_wide_two_references(wide):
     err = float(np.abs(out - ref).max())
     GH.say(f"[gpu] wide k=2 decode: max-abs {err:.3g}")
     assert err <= GH.OUT_TOL[CFG.dtype]
+    assert err <= GH.same_cache_bar(ref, g["codes"]), err
