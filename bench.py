@@ -22,8 +22,13 @@ both W_up, the queries and the fp32 outputs, each counted once per decode
 step).  The oracle (fp64, CPU) is timed on a bounded sample afterwards as a
 baseline.
 
-Further operations are reported beside it (not part of `value`), each with
-stage events per kernel: selective decode (each step attends over a quarter
+With no --config the 32k layer is the headline line and three further
+workloads follow under "workloads", each with its own rooflines: the
+131072-token layer and the batch-16 layer (compress, then 256 graph-replayed
+decode steps) and the 32-layer 65536-token prefill (compress only).
+
+Further operations on the headline layer are reported beside it (not part
+of `value`), each with stage events per kernel: selective decode (each step attends over a quarter
 of the tokens, in random 64-token blocks, over the cache replicas in turn,
 whole steps timed by graph replay), the layer with 4-bit codes and the layer
 with 4 references per token by L2 distance (compress, and decode steps by
@@ -56,6 +61,9 @@ Q4_STEPS = 64
 VARIANT_STEPS = 64
 TOPK_K = 4
 MALL_BYTES = 256 << 20
+HEADLINE = "llama8b_32k"
+# Measured after the headline by the default run, each reported beside it.
+EXTRA_WORKLOADS = ("llama8b_131k", "llama8b_b16_32k", "prefill_32l_65k")
 
 
 def log(*a):
@@ -193,6 +201,21 @@ def search_flops_per_stream(cfg) -> int:
     return 2 * cfg.head_dim * pairs
 
 
+def host_info() -> dict:
+    """The host the oracle baseline runs on: CPU model and the CPUs this
+    process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "affinity_cpus": len(os.sched_getaffinity(0)), "os_cpu_count": os.cpu_count()}
+
+
 def cpu_baseline(cfg, budget_s: float = 20.0) -> dict:
     """Time the fp64 oracle on the host: compress of whole K and V streams of
     the first KV heads, and decode steps over the full layer cache it would
@@ -243,6 +266,7 @@ def cpu_baseline(cfg, budget_s: float = 20.0) -> dict:
         "decode_ms_per_step": per_step * 1e3,
         "decode_tokens_per_s": cfg.batch / per_step,
         "compress_tokens_per_s": comp_tok_s,
+        "host": host_info(),
     }
 
 
@@ -251,7 +275,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="llama8b_32k")
+    ap.add_argument("--config", default=None,
+                    help="measure only this workload (default: the 32k layer as the headline, then the others)")
     ap.add_argument("--splits", type=int, default=0, help="decode splits per head (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
@@ -271,12 +296,43 @@ def main():
     import kvsynth as K
     import residual_kv_cache_amd as D
 
-    cfg = K.CONFIGS[args.config]
-    if cfg.decode_steps == 0:
-        prefill(cfg, args, np, torch, K, D)
-        return
     torch.cuda.set_device(0)
     hip = Hip()
+    if args.config or args.profile:
+        cfg = K.CONFIGS[args.config or HEADLINE]
+        res = (prefill_workload(cfg, args, np, torch, K, D, hip) if cfg.decode_steps == 0 else
+               decode_workload(cfg, args, np, torch, K, D, hip, extras=True))
+        if res is None:   # profiling driver
+            return
+    else:
+        # Default run: the 32k layer is the headline line; the 131k layer,
+        # the batch-16 layer and the 32-layer prefill are measured after it
+        # and reported beside it, each with its own rooflines.
+        res = decode_workload(K.CONFIGS[HEADLINE], args, np, torch, K, D, hip, extras=True)
+        res["workloads"] = {}
+        for name in EXTRA_WORKLOADS:
+            torch.cuda.empty_cache()
+            cfg = K.CONFIGS[name]
+            sub = (prefill_workload(cfg, args, np, torch, K, D, hip) if cfg.decode_steps == 0 else
+                   decode_workload(cfg, args, np, torch, K, D, hip, extras=False))
+            for key in ("metric", "n_gpus", "steps", "warmup", "higher_is_better", "scaling", "vs_baseline", "data"):
+                sub.pop(key, None)
+            res["workloads"][name] = sub
+            log(f"[bench] {name} done")
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host")
+        cfg = K.CONFIGS[args.config or HEADLINE]
+        res["cpu_baseline"] = (cpu_baseline_prefill(cfg, args.cpu_budget) if cfg.decode_steps == 0 else
+                               cpu_baseline(cfg, args.cpu_budget))
+    print(json.dumps(res), flush=True)
+
+
+def decode_workload(cfg, args, np, torch, K, D, hip, extras: bool):
+    """One decode workload: compress its prefill into the cache replicas,
+    graph-replayed steps of compress + 256 decode steps, stage events for
+    the kernel times and rooflines; with ``extras`` also the selective
+    decode, the 4-bit and k-reference layouts and decode-time append.
+    Returns the result dict (None for the profiling driver)."""
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
 
     def dev(raw):
@@ -359,7 +415,7 @@ def main():
         log(f"[bench] profile driver: calibration copy of {CALIB_BYTES} bytes, {args.steps} decode steps, "
             f"splits {splits}, {nrep} cache replicas, {SEL_STEPS} selective decode steps, {Q4_STEPS} decode steps "
             f"with 4-bit codes, then {APPEND_TOKENS} appends")
-        return
+        return None
     D.deltakv_decode_attn(lay, caches[0], q_d[0], wuk_d, wuv_d, outs[0], ws_d, n_splits=splits)
     eager0 = outs[0].clone()
     D.deltakv_decode_attn(lay, caches[(nsteps - 1) % nrep], q_d[nsteps - 1], wuk_d, wuv_d, outs[nsteps - 1], ws_d,
@@ -430,150 +486,151 @@ def main():
     c_stage = np.mean(np.array(c_stage), axis=0)
     d_stage = np.array(d_stage)
 
-    # Selective decode: every step attends over a quarter of the tokens, in
-    # random 64-token blocks (a block-sparse attention mask), over the cache
-    # replicas in turn; stage events time its three kernels.
-    ev_s = [hip.events(6) for _ in range(SEL_STEPS)]
-    s_stage = []
-    for rep in range(2):
-        for i in range(SEL_STEPS):
-            D.deltakv_decode_attn_sel(lay, caches[i % nrep], q_d[i % nsteps], wuk_d, wuv_d, tok_d, outs[i % nsteps],
-                                      ws_d, stream=s_h, stage_events=ev_s[i])
-        hip.sync(s_h)
-        s_stage.extend([[hip.elapsed_ms(e[2 * j], e[2 * j + 1]) for j in range(3)] + [hip.elapsed_ms(e[0], e[5])]
-                        for e in ev_s])
-    s_stage = np.array(s_stage)
-    sel_split_us = float(s_stage[:, 1].mean()) * 1e3
-    # Whole selective steps, replayed from a graph like the decode steps.
-    hip.begin_capture(s_h)
-    try:
-        for i in range(SEL_STEPS):
-            D.deltakv_decode_attn_sel(lay, caches[i % nrep], q_d[i % nsteps], wuk_d, wuv_d, tok_d, outs[i % nsteps],
-                                      ws_d, stream=s_h)
-    finally:
-        _, g_sel = hip.end_capture(s_h)
-    hip.launch(g_sel, s_h)
-    hip.sync(s_h)
-    ev_g = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev_g[0].record(stream)
-    for _ in range(SEL_REPLAYS):
-        hip.launch(g_sel, s_h)
-    ev_g[1].record(stream)
-    hip.sync(s_h)
-    sel_step_us = ev_g[0].elapsed_time(ev_g[1]) * 1e3 / (SEL_REPLAYS * SEL_STEPS)
-    # Algorithmic bytes of one selective split launch: the list, each
-    # selected coded token's K and V codes and ordinals, and each distinct V
-    # reference row the selection uses, once.
-    elem = 2 if cfg.dtype == "bf16" else 4
-    idx_np = caches[0].arrays()["idx"].cpu().numpy()
-    idx_np = (idx_np.view(np.uint16) if idx_np.dtype == np.int16 else idx_np.view(np.uint32)).astype(np.int64)
-    sel_bytes = 0
-    for b in range(cfg.batch):
-        t = sel_np[b].astype(np.int64)
-        coded = t % cfg.stride != 0
-        slots = (t - t // cfg.stride - 1)[coded]
-        for h in range(cfg.n_kv_heads):
-            rv = np.unique(np.concatenate([idx_np[b, h, 1][slots], (t // cfg.stride)[~coded]]))
-            sel_bytes += n_sel * 4 + len(slots) * 2 * (cfg.code_dim * elem + lay.idx_bytes) + len(rv) * cfg.head_dim * elem
-
-    def variant(**kw):
-        """The same layer under another layout (4-bit codes, k references,
-        L2): compress into enough replicas to exceed the Infinity Cache,
-        decode steps replayed from a graph, stage events for the kernels."""
-        layv = D.make_layout(cfg.dtype, cfg.head_dim, cfg.code_dim, cfg.stride, cfg.n_kv_heads, cfg.batch,
-                             cfg.seq_len, **kw)
-        nbytes = D.dkv_cache_bytes(layv)
-        nrepv = max(1, math.ceil(2 * MALL_BYTES / nbytes))
-        cv = [D.Cache(layv) for _ in range(nrepv)]
-        ws_cv = D.workspace(D.dkv_compress_workspace_bytes(layv))
-        ev_cv = hip.events(8)
-        comp = []
-        for c in cv:
-            D.deltakv_compress(layv, k_d, v_d, wdk_d, wdv_d, c, ws_cv, stream=s_h, stage_events=ev_cv)
-            hip.sync(s_h)
-            comp.append([hip.elapsed_ms(ev_cv[2 * j], ev_cv[2 * j + 1]) for j in range(4)])
-        comp = np.mean(np.array(comp), axis=0)
-        ws_dv = D.workspace(D.dkv_decode_workspace_bytes(layv, cfg.n_q_heads))
-        ev_v = [hip.events(6) for _ in range(VARIANT_STEPS)]
-        stage = []
+    if extras:
+        # Selective decode: every step attends over a quarter of the tokens, in
+        # random 64-token blocks (a block-sparse attention mask), over the cache
+        # replicas in turn; stage events time its three kernels.
+        ev_s = [hip.events(6) for _ in range(SEL_STEPS)]
+        s_stage = []
         for rep in range(2):
-            for i in range(VARIANT_STEPS):
-                D.deltakv_decode_attn(layv, cv[i % nrepv], q_d[i % nsteps], wuk_d, wuv_d, outs[i % nsteps], ws_dv,
-                                      stream=s_h, stage_events=ev_v[i])
+            for i in range(SEL_STEPS):
+                D.deltakv_decode_attn_sel(lay, caches[i % nrep], q_d[i % nsteps], wuk_d, wuv_d, tok_d, outs[i % nsteps],
+                                          ws_d, stream=s_h, stage_events=ev_s[i])
             hip.sync(s_h)
-            stage.extend([[hip.elapsed_ms(e[2 * j], e[2 * j + 1]) for j in range(3)] for e in ev_v])
-        stage = np.array(stage)
+            s_stage.extend([[hip.elapsed_ms(e[2 * j], e[2 * j + 1]) for j in range(3)] + [hip.elapsed_ms(e[0], e[5])]
+                            for e in ev_s])
+        s_stage = np.array(s_stage)
+        sel_split_us = float(s_stage[:, 1].mean()) * 1e3
+        # Whole selective steps, replayed from a graph like the decode steps.
         hip.begin_capture(s_h)
         try:
-            for i in range(VARIANT_STEPS):
-                D.deltakv_decode_attn(layv, cv[i % nrepv], q_d[i % nsteps], wuk_d, wuv_d, outs[i % nsteps], ws_dv,
-                                      stream=s_h)
+            for i in range(SEL_STEPS):
+                D.deltakv_decode_attn_sel(lay, caches[i % nrep], q_d[i % nsteps], wuk_d, wuv_d, tok_d, outs[i % nsteps],
+                                          ws_d, stream=s_h)
         finally:
-            _, g_v = hip.end_capture(s_h)
-        hip.launch(g_v, s_h)
+            _, g_sel = hip.end_capture(s_h)
+        hip.launch(g_sel, s_h)
         hip.sync(s_h)
         ev_g = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         ev_g[0].record(stream)
         for _ in range(SEL_REPLAYS):
-            hip.launch(g_v, s_h)
+            hip.launch(g_sel, s_h)
         ev_g[1].record(stream)
         hip.sync(s_h)
-        step_us = ev_g[0].elapsed_time(ev_g[1]) * 1e3 / (SEL_REPLAYS * VARIANT_STEPS)
-        effv = effective_decode_bytes(cfg, code_bits=kw.get("code_bits", 0), top_k=kw.get("top_k", 1))
-        return {"layout": {k2: v2 for k2, v2 in kw.items()}, "cache_mb": round(nbytes / 1e6, 2),
-                "cache_replicas": nrepv, "splits": D.dkv_decode_auto_splits(layv, cfg.n_q_heads),
-                "compress_ms": round(float(comp.sum()), 4),
-                "compress_stage_ms": {"mean": round(comp[0], 4), "center": round(comp[1], 4),
-                                      "search": round(comp[2], 4), "encode": round(comp[3], 4)},
-                "decode_us_per_step": round(step_us, 3),
-                "decode_gbs_effective": round(effv / (step_us * 1e-6) / 1e9, 2),
-                "effective_bytes_per_step": effv,
-                "stage_us": {"refscore": round(float(stage[:, 0].mean()) * 1e3, 3),
-                             "split": round(float(stage[:, 1].mean()) * 1e3, 3),
-                             "combine": round(float(stage[:, 2].mean()) * 1e3, 3)}}
+        sel_step_us = ev_g[0].elapsed_time(ev_g[1]) * 1e3 / (SEL_REPLAYS * SEL_STEPS)
+        # Algorithmic bytes of one selective split launch: the list, each
+        # selected coded token's K and V codes and ordinals, and each distinct V
+        # reference row the selection uses, once.
+        elem = 2 if cfg.dtype == "bf16" else 4
+        idx_np = caches[0].arrays()["idx"].cpu().numpy()
+        idx_np = (idx_np.view(np.uint16) if idx_np.dtype == np.int16 else idx_np.view(np.uint32)).astype(np.int64)
+        sel_bytes = 0
+        for b in range(cfg.batch):
+            t = sel_np[b].astype(np.int64)
+            coded = t % cfg.stride != 0
+            slots = (t - t // cfg.stride - 1)[coded]
+            for h in range(cfg.n_kv_heads):
+                rv = np.unique(np.concatenate([idx_np[b, h, 1][slots], (t // cfg.stride)[~coded]]))
+                sel_bytes += n_sel * 4 + len(slots) * 2 * (cfg.code_dim * elem + lay.idx_bytes) + len(rv) * cfg.head_dim * elem
 
-    int4 = variant(code_bits=4)
-    topk = variant(top_k=TOPK_K, metric="l2")
-    topk["search_gflops_per_s"] = round(search_flops_per_stream(cfg) * cfg.batch * cfg.n_kv_heads * 2
-                                        / (topk["compress_stage_ms"]["search"] * 1e-3) / 1e9, 1)
+        def variant(**kw):
+            """The same layer under another layout (4-bit codes, k references,
+            L2): compress into enough replicas to exceed the Infinity Cache,
+            decode steps replayed from a graph, stage events for the kernels."""
+            layv = D.make_layout(cfg.dtype, cfg.head_dim, cfg.code_dim, cfg.stride, cfg.n_kv_heads, cfg.batch,
+                                 cfg.seq_len, **kw)
+            nbytes = D.dkv_cache_bytes(layv)
+            nrepv = max(1, math.ceil(2 * MALL_BYTES / nbytes))
+            cv = [D.Cache(layv) for _ in range(nrepv)]
+            ws_cv = D.workspace(D.dkv_compress_workspace_bytes(layv))
+            ev_cv = hip.events(8)
+            comp = []
+            for c in cv:
+                D.deltakv_compress(layv, k_d, v_d, wdk_d, wdv_d, c, ws_cv, stream=s_h, stage_events=ev_cv)
+                hip.sync(s_h)
+                comp.append([hip.elapsed_ms(ev_cv[2 * j], ev_cv[2 * j + 1]) for j in range(4)])
+            comp = np.mean(np.array(comp), axis=0)
+            ws_dv = D.workspace(D.dkv_decode_workspace_bytes(layv, cfg.n_q_heads))
+            ev_v = [hip.events(6) for _ in range(VARIANT_STEPS)]
+            stage = []
+            for rep in range(2):
+                for i in range(VARIANT_STEPS):
+                    D.deltakv_decode_attn(layv, cv[i % nrepv], q_d[i % nsteps], wuk_d, wuv_d, outs[i % nsteps], ws_dv,
+                                          stream=s_h, stage_events=ev_v[i])
+                hip.sync(s_h)
+                stage.extend([[hip.elapsed_ms(e[2 * j], e[2 * j + 1]) for j in range(3)] for e in ev_v])
+            stage = np.array(stage)
+            hip.begin_capture(s_h)
+            try:
+                for i in range(VARIANT_STEPS):
+                    D.deltakv_decode_attn(layv, cv[i % nrepv], q_d[i % nsteps], wuk_d, wuv_d, outs[i % nsteps], ws_dv,
+                                          stream=s_h)
+            finally:
+                _, g_v = hip.end_capture(s_h)
+            hip.launch(g_v, s_h)
+            hip.sync(s_h)
+            ev_g = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev_g[0].record(stream)
+            for _ in range(SEL_REPLAYS):
+                hip.launch(g_v, s_h)
+            ev_g[1].record(stream)
+            hip.sync(s_h)
+            step_us = ev_g[0].elapsed_time(ev_g[1]) * 1e3 / (SEL_REPLAYS * VARIANT_STEPS)
+            effv = effective_decode_bytes(cfg, code_bits=kw.get("code_bits", 0), top_k=kw.get("top_k", 1))
+            return {"layout": {k2: v2 for k2, v2 in kw.items()}, "cache_mb": round(nbytes / 1e6, 2),
+                    "cache_replicas": nrepv, "splits": D.dkv_decode_auto_splits(layv, cfg.n_q_heads),
+                    "compress_ms": round(float(comp.sum()), 4),
+                    "compress_stage_ms": {"mean": round(comp[0], 4), "center": round(comp[1], 4),
+                                          "search": round(comp[2], 4), "encode": round(comp[3], 4)},
+                    "decode_us_per_step": round(step_us, 3),
+                    "decode_gbs_effective": round(effv / (step_us * 1e-6) / 1e9, 2),
+                    "effective_bytes_per_step": effv,
+                    "stage_us": {"refscore": round(float(stage[:, 0].mean()) * 1e3, 3),
+                                 "split": round(float(stage[:, 1].mean()) * 1e3, 3),
+                                 "combine": round(float(stage[:, 2].mean()) * 1e3, 3)}}
 
-    # Decode-time append: a cache sized for APPEND_TOKENS more tokens takes
-    # them one at a time after the prefill (each new token of every stream is
-    # a copy of a prefill token, so it has the workload's statistics).  A
-    # copy twice the MALL's size runs between appends, so each append reads
-    # the references from HBM, as it would after the other layers' steps.
-    lay_a = D.make_layout(cfg.dtype, cfg.head_dim, cfg.code_dim, cfg.stride, cfg.n_kv_heads, cfg.batch,
-                          cfg.seq_len, capacity=cfg.seq_len + APPEND_TOKENS)
-    cache_a = D.Cache(lay_a)
-    ws_ca = D.workspace(D.dkv_compress_workspace_bytes(lay_a))
-    ws_a = D.workspace(D.dkv_append_workspace_bytes(lay_a))
-    D.deltakv_compress(lay_a, k_d, v_d, wdk_d, wdv_d, cache_a, ws_ca, stream=s_h)
-    new_k = [k_d[:, :, 1000 + i] for i in range(APPEND_TOKENS)]
-    new_v = [v_d[:, :, 1000 + i] for i in range(APPEND_TOKENS)]
-    ev_a = [hip.events(4) for _ in range(APPEND_TOKENS)]
-    flush_src = torch.ones(MALL_BYTES // 2, dtype=torch.float32, device="cuda")
-    flush_dst = torch.empty_like(flush_src)
-    a_search, a_total = [], []
-    for rep in range(2):
-        for i in range(APPEND_TOKENS):
-            with torch.cuda.stream(stream):
-                flush_dst.copy_(flush_src)
-            D.deltakv_append(D.with_seq_len(lay_a, cfg.seq_len + i), new_k[i], new_v[i], wdk_d, wdv_d, cache_a, ws_a,
-                             stream=s_h, stage_events=ev_a[i])
-        hip.sync(s_h)
-        for i in range(APPEND_TOKENS):
-            t = cfg.seq_len + i
-            a_total.append(hip.elapsed_ms(ev_a[i][0], ev_a[i][1]) + hip.elapsed_ms(ev_a[i][2], ev_a[i][3]))
-            if t % cfg.stride:
-                a_search.append((hip.elapsed_ms(ev_a[i][0], ev_a[i][1]), t // cfg.stride + 1))
-    append_us = float(np.mean(a_total)) * 1e3   # search + finish kernel times
-    search_us = float(np.mean([x[0] for x in a_search])) * 1e3
-    # Algorithmic bytes of one search launch: every candidate reference row
-    # of every stream once, plus the new token and the mean.
-    n_streams_a = cfg.batch * cfg.n_kv_heads * 2
-    elem = 2 if cfg.dtype == "bf16" else 4
-    append_bytes = float(np.mean([(x[1] + 2) * cfg.head_dim * elem * n_streams_a for x in a_search]))
-    del flush_src, flush_dst, cache_a
+        int4 = variant(code_bits=4)
+        topk = variant(top_k=TOPK_K, metric="l2")
+        topk["search_gflops_per_s"] = round(search_flops_per_stream(cfg) * cfg.batch * cfg.n_kv_heads * 2
+                                            / (topk["compress_stage_ms"]["search"] * 1e-3) / 1e9, 1)
+
+        # Decode-time append: a cache sized for APPEND_TOKENS more tokens takes
+        # them one at a time after the prefill (each new token of every stream is
+        # a copy of a prefill token, so it has the workload's statistics).  A
+        # copy twice the MALL's size runs between appends, so each append reads
+        # the references from HBM, as it would after the other layers' steps.
+        lay_a = D.make_layout(cfg.dtype, cfg.head_dim, cfg.code_dim, cfg.stride, cfg.n_kv_heads, cfg.batch,
+                              cfg.seq_len, capacity=cfg.seq_len + APPEND_TOKENS)
+        cache_a = D.Cache(lay_a)
+        ws_ca = D.workspace(D.dkv_compress_workspace_bytes(lay_a))
+        ws_a = D.workspace(D.dkv_append_workspace_bytes(lay_a))
+        D.deltakv_compress(lay_a, k_d, v_d, wdk_d, wdv_d, cache_a, ws_ca, stream=s_h)
+        new_k = [k_d[:, :, 1000 + i] for i in range(APPEND_TOKENS)]
+        new_v = [v_d[:, :, 1000 + i] for i in range(APPEND_TOKENS)]
+        ev_a = [hip.events(4) for _ in range(APPEND_TOKENS)]
+        flush_src = torch.ones(MALL_BYTES // 2, dtype=torch.float32, device="cuda")
+        flush_dst = torch.empty_like(flush_src)
+        a_search, a_total = [], []
+        for rep in range(2):
+            for i in range(APPEND_TOKENS):
+                with torch.cuda.stream(stream):
+                    flush_dst.copy_(flush_src)
+                D.deltakv_append(D.with_seq_len(lay_a, cfg.seq_len + i), new_k[i], new_v[i], wdk_d, wdv_d, cache_a, ws_a,
+                                 stream=s_h, stage_events=ev_a[i])
+            hip.sync(s_h)
+            for i in range(APPEND_TOKENS):
+                t = cfg.seq_len + i
+                a_total.append(hip.elapsed_ms(ev_a[i][0], ev_a[i][1]) + hip.elapsed_ms(ev_a[i][2], ev_a[i][3]))
+                if t % cfg.stride:
+                    a_search.append((hip.elapsed_ms(ev_a[i][0], ev_a[i][1]), t // cfg.stride + 1))
+        append_us = float(np.mean(a_total)) * 1e3   # search + finish kernel times
+        search_us = float(np.mean([x[0] for x in a_search])) * 1e3
+        # Algorithmic bytes of one search launch: every candidate reference row
+        # of every stream once, plus the new token and the mean.
+        n_streams_a = cfg.batch * cfg.n_kv_heads * 2
+        elem = 2 if cfg.dtype == "bf16" else 4
+        append_bytes = float(np.mean([(x[1] + 2) * cfg.head_dim * elem * n_streams_a for x in a_search]))
+        del flush_src, flush_dst, cache_a
 
     eff = effective_decode_bytes(cfg)
     value = nsteps * eff / (decode_window_ms * 1e-3) / 1e9
@@ -624,37 +681,40 @@ def main():
                      "unit": "GB/s", "frac": round(split_bytes / (split_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": stored_traffic(cfg.name, splits), "bytes_per_launch": split_bytes,
                      "launch_us": round(split_ms * 1e3, 3)},
-        "selective_decode": {"tokens_per_seq": n_sel, "selection": "a quarter of the tokens in random 64-token blocks",
-                             "us_per_step": round(sel_step_us, 3),
-                             "stage_us": {"refscore": round(float(s_stage[:, 0].mean()) * 1e3, 3),
-                                          "split": round(sel_split_us, 3),
-                                          "combine": round(float(s_stage[:, 2].mean()) * 1e3, 3)}},
-        "roofline_selective": {"kernel": "k_split_mfma (token list)" if mfma_shape and cfg.code_dim <= 32
-                               else "k_split_sel", "bound": "hbm",
-                               "achieved": round(sel_bytes / (sel_split_us * 1e-6) / 1e9, 2), "peak": HBM_PEAK_GBS,
-                               "unit": "GB/s",
-                               "frac": round(sel_bytes / (sel_split_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                               "bytes_per_launch": int(sel_bytes), "launch_us": round(sel_split_us, 3)},
-        "int4_codes": int4,
-        "topk_l2": topk,
-        "append_kernel_us_per_token": round(append_us, 3),
-        "roofline_append": {"kernel": "k_append_search", "bound": "hbm",
-                            "achieved": round(append_bytes / (search_us * 1e-6) / 1e9, 2), "peak": HBM_PEAK_GBS,
-                            "unit": "GB/s",
-                            "frac": round(append_bytes / (search_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                            "bytes_per_launch": round(append_bytes), "launch_us": round(search_us, 3),
-                            "tokens": APPEND_TOKENS},
         "roofline_search": {"kernel": "k_search_mfma", "bound": "mfma",
                             "achieved": round(search_flops / (c_stage[2] * 1e-3) / 1e12, 2),
                             "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                             "frac": round(search_flops / (c_stage[2] * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                             "flops_per_launch": search_flops},
+        "roofline_step": {"what": "whole decode step (every kernel of it, graph-replayed)", "bound": "hbm",
+                          "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(value / HBM_PEAK_GBS, 4), "bytes_per_step": eff},
     }
-    log(f"[bench] gpu done: {json.dumps(res)}")
-    if not args.no_cpu_baseline:
-        log("[bench] timing the oracle on the host")
-        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
-    print(json.dumps(res), flush=True)
+    if extras:
+        res.update({
+            "selective_decode": {"tokens_per_seq": n_sel, "selection": "a quarter of the tokens in random 64-token blocks",
+                                 "us_per_step": round(sel_step_us, 3),
+                                 "stage_us": {"refscore": round(float(s_stage[:, 0].mean()) * 1e3, 3),
+                                              "split": round(sel_split_us, 3),
+                                              "combine": round(float(s_stage[:, 2].mean()) * 1e3, 3)}},
+            "roofline_selective": {"kernel": "k_split_mfma (token list)" if mfma_shape and cfg.code_dim <= 32
+                                   else "k_split_sel", "bound": "hbm",
+                                   "achieved": round(sel_bytes / (sel_split_us * 1e-6) / 1e9, 2), "peak": HBM_PEAK_GBS,
+                                   "unit": "GB/s",
+                                   "frac": round(sel_bytes / (sel_split_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                   "bytes_per_launch": int(sel_bytes), "launch_us": round(sel_split_us, 3)},
+            "int4_codes": int4,
+            "topk_l2": topk,
+            "append_kernel_us_per_token": round(append_us, 3),
+            "roofline_append": {"kernel": "k_append_search", "bound": "hbm",
+                                "achieved": round(append_bytes / (search_us * 1e-6) / 1e9, 2), "peak": HBM_PEAK_GBS,
+                                "unit": "GB/s",
+                                "frac": round(append_bytes / (search_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                "bytes_per_launch": round(append_bytes), "launch_us": round(search_us, 3),
+                                "tokens": APPEND_TOKENS},
+        })
+    log(f"[bench] {cfg.name} gpu done: {json.dumps(res)}")
+    return res
 
 
 PREFILL_INPUT_LAYERS = 4   # distinct synthetic layers resident in HBM for the compress-only workload
@@ -695,17 +755,16 @@ def cpu_baseline_prefill(cfg, budget_s: float = 20.0) -> dict:
         "sample": (f"fp64 numpy oracle: compress of the first {tp} tokens of one K stream in {dt:.1f} s, "
                    f"scaled by causal (token, reference) pairs to a {cfg.seq_len}-token stream and over the "
                    f"{2 * cfg.n_kv_heads * cfg.batch} K and V streams of a layer"),
+        "host": host_info(),
     }
 
 
-def prefill(cfg, args, np, torch, K, D):
+def prefill_workload(cfg, args, np, torch, K, D, hip):
     """Compress-only workload (a prefill with no decode steps): one step is
     the compress of every layer of the configuration, graph-replayed over
     a few distinct resident synthetic layers in turn (each layer has the
     same shape and value distribution); stage events time the search
-    kernel for its MFMA roofline.  Prints one JSON line."""
-    torch.cuda.set_device(0)
-    hip = Hip()
+    kernel for its MFMA roofline.  Returns the result dict."""
 
     def dev(raw):
         return torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(torch.bfloat16).cuda()
@@ -786,11 +845,8 @@ def prefill(cfg, args, np, torch, K, D):
                      "unit": "TFLOP/s", "frac": round(search_flops / (st[2] * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                      "traffic": None, "flops_per_launch": search_flops},
     }
-    log(f"[bench] gpu done: {json.dumps(res)}")
-    if not args.no_cpu_baseline:
-        log("[bench] timing the oracle on the host")
-        res["cpu_baseline"] = cpu_baseline_prefill(cfg, args.cpu_budget)
-    print(json.dumps(res), flush=True)
+    log(f"[bench] {cfg.name} gpu done: {json.dumps(res)}")
+    return res
 
 
 if __name__ == "__main__":
