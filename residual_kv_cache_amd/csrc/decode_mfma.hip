@@ -848,29 +848,58 @@ __global__ __launch_bounds__(kThreads) void k_split_mfma(DecodeArgs a, Shape sh)
 // the additions and the output stays deterministic).  A dense pass over the
 // references then applies the weights with the token-tile split's
 // value-reference MFMAs.
+//
+// The score MFMA's 16 output columns hold each query head four times (the
+// four lanes of a quad).  Those four lanes split the chunk instead: lane e
+// of a quad takes tile e, so the S lookups, masks, exponentials and
+// histogram adds after the score MFMA run once per (token, query head).  The
+// value-code MFMA of tile k, which spreads the weights over the quad's
+// lanes, takes them from lane k of the quad by a DPP broadcast.
 // ---------------------------------------------------------------------------
 
-constexpr int kHistTiles = 4;   // tiles per wave per chunk
+constexpr int kHistTiles = 4;   // tiles per wave per chunk: one per lane of a quad
 
-// v[i] of a four-entry register array for a run-time i (selects, so that the
-// array stays in registers).
-__device__ __forceinline__ float pick4(const float (&v)[4], int i) {
-  return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
+// a where the bits of m are set, b elsewhere (one bitfield select, never a
+// branch).
+__device__ __forceinline__ float bsel(uint32_t m, float a, float b) {
+  return __uint_as_float((__float_as_uint(a) & m) | (__float_as_uint(b) & ~m));
+}
+
+// v[i] of a four-entry register array for a run-time i in 0..3, by bitfield
+// selects (the array stays in registers, and a lane-dependent i makes no
+// divergent branch).
+__device__ __forceinline__ float pick4(float v0, float v1, float v2, float v3, int i) {
+  const uint32_t m1 = 0u - (uint32_t)(i & 1), m2 = 0u - (uint32_t)((i >> 1) & 1);
+  return bsel(m2, bsel(m1, v3, v2), bsel(m1, v1, v0));
+}
+__device__ __forceinline__ float pick4(const float (&v)[4], int i) { return pick4(v[0], v[1], v[2], v[3], i); }
+
+// Lane K of each quad (four consecutive lanes), broadcast over the quad.
+template <int K>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, K * 0x55, 0xF, 0xF, true);
+}
+
+// Maximum over each quad (quad_perm 1,0,3,2 then 2,3,0,1).
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));
 }
 
 struct HChunk {
-  int ld[kHistTiles];     // loaded ordinal (coded tiles)
+  int ldk[4];             // K and V ordinal rows of tokens 4 q4 + i of the lane's own
+  int ldv[4];             //   tile (tile n16 & 3 of the chunk), as loaded
   Frag ck[kHistTiles];    // key-code A operand rows (zero rows for references)
   Frag cv[kHistTiles];    // value-code pieces, as Tile::cv
 };
 
-// p (0 <= p <= 2^kTau) as a fixed-point integer at scale 2^32, truncated,
-// in two exact 16-bit steps.
+// p (0 <= p <= 2^kTau) as a fixed-point integer at scale 2^32, truncated:
+// floor(p) in the high word and floor(fract(p) 2^32) in the low one (the
+// fraction and the power-of-two product are exact).
 __device__ __forceinline__ unsigned long long fix32(float p) {
-  const float t = p * 65536.f;
-  const uint32_t hi = (uint32_t)t;
-  const uint32_t lo = (uint32_t)((t - (float)hi) * 65536.f);
-  return ((unsigned long long)hi << 16) + lo;
+  const uint32_t hi = (uint32_t)p;
+  const uint32_t lo = (uint32_t)(__builtin_amdgcn_fractf(p) * 4294967296.0f);
+  return ((unsigned long long)hi << 32) | lo;
 }
 
 size_t hist_lds_bytes(const Shape& sh) {
@@ -892,7 +921,7 @@ __global__ __launch_bounds__(kThreads) void k_split_hist(DecodeArgs a, Shape sh)
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n16 = lane & 15, q4 = lane >> 4;
   const int G = a.G, dc = sh.dc, R = sh.R;
-  const int gl = n16 >> 2;
+  const int gl = n16 >> 2, e4 = n16 & 3;
 
   const int n0 = split_lo(sh.N, sp, a.splits, 16), n1 = split_lo(sh.N, sp + 1, a.splits, 16);
   const int r0 = split_lo(sh.R, sp, a.splits, 1), r1 = split_lo(sh.R, sp + 1, a.splits, 1);
@@ -929,9 +958,6 @@ __global__ __launch_bounds__(kThreads) void k_split_hist(DecodeArgs a, Shape sh)
       int tb, cnt;
       bool coded, live;
       tile_of(c, k, tb, cnt, coded, live);
-      const int ua = tb + min(q4 * 4 + (n16 & 3), cnt - 1);
-      const void* ip = coded ? (const void*)((const IdxT*)(n16 < 4 ? p.idxK : p.idxV) + ua) : (const void*)kZeroCodes;
-      L.ld[k] = (int)ldg<IdxT>(ip, 0u);
       const int ub = tb + min(n16, cnt - 1);
       const int cc = q4 * 8;
       L.ck[k] = ldg<Frag>(coded ? (const void*)p.codesK : (const void*)kZeroCodes,
@@ -942,6 +968,19 @@ __global__ __launch_bounds__(kThreads) void k_split_hist(DecodeArgs a, Shape sh)
       const bool in_code = col < dc;
       L.cv[k] = ldg<Frag>(in_code ? (coded ? (const void*)p.codesV : (const void*)kZeroCodes) : (const void*)kOnePair,
                           in_code && coded ? ((uint32_t)uc * dc + col) * 2u : 0u);
+    }
+    // The lane's own tile: the K and V ordinals of its four tokens (rows
+    // clamped into the tile).  A reference tile uses its positions instead;
+    // its rows, below R <= N, are read all the same, so the loads take no
+    // lane-dependent branch.
+    int tb, cnt;
+    bool coded, live;
+    tile_of(c, e4, tb, cnt, coded, live);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t row = (uint32_t)(tb + min(q4 * 4 + i, cnt - 1));
+      L.ldk[i] = (int)ldg<IdxT>(p.idxK, row * (uint32_t)sizeof(IdxT));
+      L.ldv[i] = (int)ldg<IdxT>(p.idxV, row * (uint32_t)sizeof(IdxT));
     }
   };
 
@@ -996,42 +1035,50 @@ __global__ __launch_bounds__(kThreads) void k_split_hist(DecodeArgs a, Shape sh)
   f32x4 accc = {0.f, 0.f, 0.f, 0.f};                         // value codes + weight sum, query head q4
 
   auto chunk = [&](int c, const HChunk& L, HChunk& Lnext) {
-    // ---- pass A: scores ----
-    float sc[kHistTiles][4];
-    int rw[kHistTiles];
-    float wmax = -INFINITY;
+    // ---- pass A: scores of the lane's own tile ----
+    f32x4 cs4[kHistTiles];
 #pragma unroll
     for (int k = 0; k < kHistTiles; ++k) {
-      int tb, cnt;
-      bool coded, live;
-      tile_of(c, k, tb, cnt, coded, live);
-      const int ua = tb + min(q4 * 4 + (n16 & 3), cnt - 1);
-      const int raw = coded ? L.ld[k] : ua;
-      rw[k] = raw;
       f32x4 cs = {0.f, 0.f, 0.f, 0.f};
       cs = mfma16(L.ck[k], qh[0], cs);
-      cs = mfma16(L.ck[k], ql[0], cs);
-      float sb[4];
-      sb[0] = s_tab[(uint32_t)min(row_bcast<0>(raw), R - 1) * 4 + gl];
-      sb[1] = s_tab[(uint32_t)min(row_bcast<1>(raw), R - 1) * 4 + gl];
-      sb[2] = s_tab[(uint32_t)min(row_bcast<2>(raw), R - 1) * 4 + gl];
-      sb[3] = s_tab[(uint32_t)min(row_bcast<3>(raw), R - 1) * 4 + gl];
-      const int vm = live ? cnt : 0;
+      cs4[k] = mfma16(L.ck[k], ql[0], cs);
+    }
+    int tb, cnt;
+    bool coded, live;
+    tile_of(c, e4, tb, cnt, coded, live);
+    const int vm = live ? cnt : 0;
+    float sc[4], sb[4];
+    int rv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float sv = q4 * 4 + i < vm ? sb[i] + cs[i] : -INFINITY;
-        sc[k][i] = sv;
-        wmax = fmaxf(wmax, sv);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int pos = tb + q4 * 4 + i;
+      const int rk = min(coded ? L.ldk[i] : pos, R - 1);
+      rv[i] = min(coded ? L.ldv[i] : pos, R - 1);
+      sb[i] = s_tab[(uint32_t)rk * 4 + gl];
+    }
+    float wmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float csi = pick4(cs4[0][i], cs4[1][i], cs4[2][i], cs4[3][i], e4);
+      // All ones when token 4 q4 + i is valid (a sign shift, so that no
+      // branch forms around the score).
+      const uint32_t valid = (uint32_t)((q4 * 4 + i - vm) >> 31);
+      const float sv = bsel(valid, sb[i] + csi, -INFINITY);
+      sc[i] = sv;
+      wmax = fmaxf(wmax, sv);
     }
     // The next chunk's loads fly through the barriers and pass B (issued
-    // once this chunk's ordinals and key codes are consumed).
-    if (c + 1 < nchunk) issue(c + 1, Lnext);
+    // once this chunk's ordinals and key codes are consumed).  They are
+    // issued after the last chunk too (its tiles clamped into the block):
+    // with the loads unconditional, the compiler can count exactly which are
+    // still in flight, so pass B waits only for this chunk's value codes.
+    issue(c + 1, Lnext);
+    wmax = quad_max(wmax);
     wmax = fmaxf(wmax, __shfl_xor(wmax, 16, 64));
     wmax = fmaxf(wmax, __shfl_xor(wmax, 32, 64));
     // Maxima slots alternate with the chunk's parity: a wave may write the
     // next chunk's while a slower one still reads these.
-    if (lane < 16 && (n16 & 3) == 0) chunk_m[c & 1][wave][gl] = wmax;
+    if (lane < 16 && e4 == 0) chunk_m[c & 1][wave][gl] = wmax;
     __syncthreads();
     // ---- block maxima and lazy rescale (the same decision in every thread) ----
     f32x4 mx4 = {M[0], M[1], M[2], M[3]};
@@ -1060,30 +1107,33 @@ __global__ __launch_bounds__(kThreads) void k_split_hist(DecodeArgs a, Shape sh)
       accc *= pick4(alpha, q4);
       __syncthreads();
     }
-    // ---- pass B: histogram weights and value-code MFMAs ----
+    // ---- pass B: histogram weights of the own tile, then each tile's
+    // value-code MFMAs with its weights from the quad's lane ----
     const float mg = pick4(M, gl);
+    float pw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pw[i] = __builtin_amdgcn_exp2f(sc[i] - mg);
+    // Every lane adds (the histogram has rows for all four query-head
+    // slots; the dense pass reads only those of real heads).
+    {
+      unsigned long long* hg = hist + (size_t)gl * R;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) atomicAdd(hg + rv[i], fix32(pw[i]));
+    }
+    const uint32_t h01 = pk_bf16(pw[0], pw[1]), h23 = pk_bf16(pw[2], pw[3]);
+    const uint32_t l01 = pk_bf16(pw[0] - __uint_as_float(h01 << 16), pw[1] - __uint_as_float(h01 & 0xFFFF0000u));
+    const uint32_t l23 = pk_bf16(pw[2] - __uint_as_float(h23 << 16), pw[3] - __uint_as_float(h23 & 0xFFFF0000u));
 #pragma unroll
     for (int k = 0; k < kHistTiles; ++k) {
-      float pw[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pw[i] = __builtin_amdgcn_exp2f(sc[k][i] - mg);
-      const int rv0 = min(row_bcast<4>(rw[k]), R - 1), rv1 = min(row_bcast<5>(rw[k]), R - 1);
-      const int rv2 = min(row_bcast<6>(rw[k]), R - 1), rv3 = min(row_bcast<7>(rw[k]), R - 1);
-      if ((n16 & 3) == 0 && gl < G) {   // one lane of the four that share (token, query head)
-        unsigned long long* hg = hist + (size_t)gl * R;
-        atomicAdd(hg + rv0, fix32(pw[0]));
-        atomicAdd(hg + rv1, fix32(pw[1]));
-        atomicAdd(hg + rv2, fix32(pw[2]));
-        atomicAdd(hg + rv3, fix32(pw[3]));
-      }
       Frag bc[2];
       value_code_operands(L.cv[k], n16, dc, bc);
-      const uint32_t h01 = pk_bf16(pw[0], pw[1]), h23 = pk_bf16(pw[2], pw[3]);
-      const uint32_t l01 = pk_bf16(pw[0] - __uint_as_float(h01 << 16), pw[1] - __uint_as_float(h01 & 0xFFFF0000u));
-      const uint32_t l23 = pk_bf16(pw[2] - __uint_as_float(h23 << 16), pw[3] - __uint_as_float(h23 & 0xFFFF0000u));
+      const uint32_t kh01 = k == 0 ? quad_bcast<0>(h01) : k == 1 ? quad_bcast<1>(h01) : k == 2 ? quad_bcast<2>(h01) : quad_bcast<3>(h01);
+      const uint32_t kh23 = k == 0 ? quad_bcast<0>(h23) : k == 1 ? quad_bcast<1>(h23) : k == 2 ? quad_bcast<2>(h23) : quad_bcast<3>(h23);
+      const uint32_t kl01 = k == 0 ? quad_bcast<0>(l01) : k == 1 ? quad_bcast<1>(l01) : k == 2 ? quad_bcast<2>(l01) : quad_bcast<3>(l01);
+      const uint32_t kl23 = k == 0 ? quad_bcast<0>(l23) : k == 1 ? quad_bcast<1>(l23) : k == 2 ? quad_bcast<2>(l23) : quad_bcast<3>(l23);
 #pragma unroll
       for (int g2 = 0; g2 < 2; ++g2) {
-        const uint32_t hp = g2 ? h23 : h01, lp = g2 ? l23 : l01;
+        const uint32_t hp = g2 ? kh23 : kh01, lp = g2 ? kl23 : kl01;
         const Frag ah = Frag{__builtin_amdgcn_perm(hp, hp, sel[0]), __builtin_amdgcn_perm(hp, hp, sel[1]),
                              __builtin_amdgcn_perm(hp, hp, sel[2]), __builtin_amdgcn_perm(hp, hp, sel[3])};
         const Frag al = Frag{__builtin_amdgcn_perm(lp, lp, sel[0]), __builtin_amdgcn_perm(lp, lp, sel[1]),

@@ -32,6 +32,10 @@ SMALL = {
     "bf16_g2_b3": BASE_BF16.replace(name="bf16_g2_b3", seq_len=777, n_kv_heads=2, n_q_heads=4, batch=3),
     "f32_ragged_g2": K.CONFIGS["tiny"].replace(name="f32_ragged_g2", seq_len=1234, n_kv_heads=2, n_q_heads=4,
                                                head_dim=128, code_dim=32, stride=5),
+    # one and three query heads per KV head, long enough for the histogram
+    # split at up to three splits per head
+    "bf16_g1_hist": BASE_BF16.replace(name="bf16_g1_hist", seq_len=2000, n_kv_heads=2, n_q_heads=2),
+    "bf16_g3_hist": BASE_BF16.replace(name="bf16_g3_hist", seq_len=1999, n_kv_heads=2, n_q_heads=6),
 }
 
 
@@ -116,6 +120,28 @@ def test_histogram_split_deterministic(small_runs):
     o = outs[0].cpu().numpy().astype(np.float64)
     GH.check_same_cache(o, GH.oracle_decode_on(gc, q.f64, inp), cfg.dtype, "histogram split", codes=gc["codes"])
     assert np.abs(o - GH.gpu_decode(lay, cache, q.raw, inp, n_splits=64)).max() <= 1e-5
+
+
+@pytest.mark.parametrize("name,splits", [("bf16_g1_hist", 1), ("bf16_g1_hist", 3), ("bf16_g2_b3", 2),
+                                         ("bf16_g3_hist", 1), ("bf16_g3_hist", 2), ("bf16_ragged", 3)])
+def test_histogram_split_query_groups(name, splits, small_runs):
+    """The histogram split with 1, 2, 3 or 4 query heads per KV head (its
+    tiles carry four query-head slots, the unused ones padded) and one to
+    three splits per head, so that split, chunk and reference-tile
+    boundaries fall at different places: identical bytes on a repeated call,
+    oracle parity on the GPU's cache, and agreement with the token-tile
+    form of the split at 64 splits."""
+    inp, lay, cache, gc = _run(name, small_runs)
+    cfg = inp.cfg
+    assert lay.n_codes >= 4 * lay.n_refs * splits   # the histogram form serves this split count
+    q = inp.q(2)
+    a = GH.gpu_decode(lay, cache, q.raw, inp, n_splits=splits)
+    b = GH.gpu_decode(lay, cache, q.raw, inp, n_splits=splits)
+    assert np.array_equal(a, b)
+    GH.check_same_cache(a, GH.oracle_decode_on(gc, q.f64, inp), cfg.dtype, f"histogram split {name}, {splits} splits",
+                        codes=gc["codes"], n_tokens=cfg.seq_len)
+    tiles = GH.gpu_decode(lay, cache, q.raw, inp, n_splits=64)
+    assert np.abs(a - tiles).max() <= GH.same_cache_bar(tiles, gc["codes"], cfg.seq_len)
 
 
 def test_softmax_scale_argument(small_runs):
