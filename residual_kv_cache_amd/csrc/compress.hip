@@ -231,10 +231,6 @@ __device__ __forceinline__ void centre8(uint4 x, uint4 m, uint32_t* w) {
                       __uint_as_float(xv[e] & 0xFFFF0000u) - __uint_as_float(mv[e] & 0xFFFF0000u));
 }
 
-// Word 3 of a raw buffer descriptor (gfx9 family): 32-bit data format, so
-// untyped loads return the bytes as stored; a load at or past the size in
-// word 2 (bytes, for stride 0) returns zeros.
-constexpr int kBufferRsrcWord3 = 0x00020000;
 // Buffer load of 16 bytes per lane straight into LDS: lane l's bytes land
 // at lds + 16 l; lds is wave-uniform and below 64 KB (the load takes its LDS
 // address from the low 16 bits of M0).

@@ -918,7 +918,8 @@ __global__ __launch_bounds__(kThreads) void k_split_hist(DecodeArgs a, Shape sh)
   const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
   const int bh = xcd + 8 * (kx / a.splits), sp = kx % a.splits;
   if (bh >= BH) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: tile bases stay scalar
   const int n16 = lane & 15, q4 = lane >> 4;
   const int G = a.G, dc = sh.dc, R = sh.R;
   const int gl = n16 >> 2, e4 = n16 & 3;
@@ -952,35 +953,52 @@ __global__ __launch_bounds__(kThreads) void k_split_hist(DecodeArgs a, Shape sh)
     tb = coded ? n0 + 16 * tc : r0 + 16 * (tc - nct);
     cnt = coded ? min(16, n1 - tb) : min(16, r1 - tb);
   };
+  // Loads through buffer descriptors whose range ends at the stream's last
+  // coded row, so that rows past it (capacity rows, whatever they hold) read
+  // as zeros without a clamp.  Per tile the base is a scalar; the lanes'
+  // offsets are the same for every tile.  A reference tile reads through an
+  // empty range: zero code rows.
+  const uint32_t row_bytes = (uint32_t)dc * 2u;
+  const int g2l = n16 >> 3, c7 = n16 & 7, colv = 4 * (c7 & ~1);
+  const uint32_t voff_ck = ((uint32_t)n16 * dc + (q4 * 8 < dc ? q4 * 8 : 0)) * 2u;
+  // Lanes past the code columns read nothing (their value-code operand is
+  // the constant weight-sum column, formed from no loaded data).
+  const uint32_t voff_cv = colv < dc ? ((uint32_t)(q4 * 4 + 2 * g2l + (c7 & 1)) * dc + colv) * 2u : 0x80000000u;
+  const __amdgpu_buffer_rsrc_t r_idxK = buffer_rsrc(p.idxK, (uint32_t)sh.N * sizeof(IdxT));
+  const __amdgpu_buffer_rsrc_t r_idxV = buffer_rsrc(p.idxV, (uint32_t)sh.N * sizeof(IdxT));
   auto issue = [&](int c, HChunk& L) {
 #pragma unroll
     for (int k = 0; k < kHistTiles; ++k) {
       int tb, cnt;
       bool coded, live;
       tile_of(c, k, tb, cnt, coded, live);
-      const int ub = tb + min(n16, cnt - 1);
-      const int cc = q4 * 8;
-      L.ck[k] = ldg<Frag>(coded ? (const void*)p.codesK : (const void*)kZeroCodes,
-                          coded ? ((uint32_t)ub * dc + (cc < dc ? cc : 0)) * 2u : 0u);
-      const int g2 = n16 >> 3, c7 = n16 & 7;
-      const int col = 4 * (c7 & ~1);
-      const int uc = tb + min(q4 * 4 + 2 * g2 + (c7 & 1), cnt - 1);
-      const bool in_code = col < dc;
-      L.cv[k] = ldg<Frag>(in_code ? (coded ? (const void*)p.codesV : (const void*)kZeroCodes) : (const void*)kOnePair,
-                          in_code && coded ? ((uint32_t)uc * dc + col) * 2u : 0u);
+      const uint32_t bytes = coded ? (uint32_t)(sh.N - tb) * row_bytes : 0u;
+      L.ck[k] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(
+                                             buffer_rsrc(p.codesK + (size_t)tb * dc, bytes), voff_ck, 0, 0));
+      L.cv[k] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(
+                                             buffer_rsrc(p.codesV + (size_t)tb * dc, bytes), voff_cv, 0, 0));
     }
-    // The lane's own tile: the K and V ordinals of its four tokens (rows
-    // clamped into the tile).  A reference tile uses its positions instead;
-    // its rows, below R <= N, are read all the same, so the loads take no
-    // lane-dependent branch.
+    // The lane's own tile: the K and V ordinals of its four tokens.  A
+    // reference tile uses its positions instead; its rows, below R <= N, are
+    // read all the same, so the loads take no lane-dependent branch.
     int tb, cnt;
     bool coded, live;
     tile_of(c, e4, tb, cnt, coded, live);
+    const uint32_t vo = (uint32_t)(tb + q4 * 4) * (uint32_t)sizeof(IdxT);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t row = (uint32_t)(tb + min(q4 * 4 + i, cnt - 1));
-      L.ldk[i] = (int)ldg<IdxT>(p.idxK, row * (uint32_t)sizeof(IdxT));
-      L.ldv[i] = (int)ldg<IdxT>(p.idxV, row * (uint32_t)sizeof(IdxT));
+      // Each ordinal its own load: an opaque offset keeps the compiler from
+      // merging neighbours into one wider load, whose unpacking it could
+      // then schedule ahead of the consuming chunk.
+      uint32_t o = vo + (uint32_t)sizeof(IdxT) * i;
+      asm("" : "+v"(o));
+      if constexpr (sizeof(IdxT) == 2) {
+        L.ldk[i] = (int)__builtin_amdgcn_raw_buffer_load_b16(r_idxK, o, 0, 0);
+        L.ldv[i] = (int)__builtin_amdgcn_raw_buffer_load_b16(r_idxV, o, 0, 0);
+      } else {
+        L.ldk[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(r_idxK, o, 0, 0);
+        L.ldv[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(r_idxV, o, 0, 0);
+      }
     }
   };
 
@@ -1034,7 +1052,15 @@ __global__ __launch_bounds__(kThreads) void k_split_hist(DecodeArgs a, Shape sh)
   float M[4] = {-3.0e38f, -3.0e38f, -3.0e38f, -3.0e38f};   // block maxima per query head (base 2)
   f32x4 accc = {0.f, 0.f, 0.f, 0.f};                         // value codes + weight sum, query head q4
 
-  auto chunk = [&](int c, const HChunk& L, HChunk& Lnext) {
+  auto chunk = [&](int c, HChunk& L, HChunk& Lnext) {
+    // This chunk's loaded registers become usable here, after the previous
+    // chunk's barrier (empty asm, ordered with the barrier): otherwise the
+    // scheduler may hoist their first uses into the previous chunk, whose
+    // wait would then also cover the loads it had just issued.
+#pragma unroll
+    for (int k = 0; k < kHistTiles; ++k) asm volatile("" : "+v"(L.ck[k]), "+v"(L.cv[k]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(L.ldk[i]), "+v"(L.ldv[i]));
     // ---- pass A: scores of the lane's own tile ----
     f32x4 cs4[kHistTiles];
 #pragma unroll

@@ -7,6 +7,17 @@
 
 namespace dkv {
 
+// Word 3 of a raw buffer descriptor (gfx9 family): 32-bit data format, so
+// untyped loads return the bytes as stored; a load whose offset (lane offset
+// plus immediate) is at or past the size in word 2 (bytes, for stride 0)
+// returns zeros.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+// Raw buffer descriptor over `bytes` bytes from base.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, kBufferRsrcWord3);
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
