@@ -675,7 +675,8 @@ __global__ __launch_bounds__(kThreads) void k_split_mfma(DecodeArgs a, Shape sh)
   const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
   const int bh = xcd + 8 * (kx / a.splits), sp = kx % a.splits;
   if (bh >= BH) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: tile ranges and bases stay scalar
   const int n16 = lane & 15, q4 = lane >> 4;
   const int G = a.G, dc = sh.dc;
 
