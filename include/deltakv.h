@@ -40,13 +40,17 @@
  *    HIP device; every other pointer is host memory and is only read during
  *    the call.  The caller owns all memory, including workspaces.  The
  *    library never allocates, frees or synchronises.
- *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
- *    and runs asynchronously; outputs are valid once the stream reaches it.
+ *  - Work is enqueued on `stream` (a hipStream_t, passed as void* so that
+ *    this header needs no HIP header; NULL = the null stream) and runs
+ *    asynchronously; outputs are valid once the stream reaches it.
  *  - Argument checks run on the host before anything is enqueued; on any
  *    error nothing is launched and outputs are untouched.  Launch failures
  *    are reported as DKV_ERR_DEVICE.  No C++ exception crosses this ABI.
- *  - The library holds no mutable global state; calls on different streams
- *    with disjoint outputs and workspaces may run concurrently.
+ *  - The library holds no mutable global state other than the per-GPU
+ *    scratch array of deltakv_decode_attn_noalloc (and the device address
+ *    of that array, looked up once per GPU); calls on different streams with
+ *    disjoint outputs and workspaces may run concurrently, except for that
+ *    entry point, whose calls on one GPU share the array.
  *  - Results are deterministic: the same inputs give the same bytes.
  */
 #ifndef DELTAKV_H
@@ -304,8 +308,11 @@ size_t dkv_decode_workspace_bytes(const dkv_layout* layout, uint32_t n_q_heads, 
  * Compresses one layer's prefill K and V into `cache` (all four arrays are
  * written whole).  `ws` is a device buffer of at least
  * dkv_compress_workspace_bytes(layout) bytes, 16-byte aligned; its contents
- * on entry do not matter.  Steps: shared component, centred references and
- * their norms, reference search, residual codes.
+ * on entry do not matter.  Steps: shared component (English page, Technical
+ * Summary §2 "Highly Shared Latent Components"), centred references at
+ * stride s and their norms, reference search (§3 "Strided Reference
+ * Selection"), residual codes (§3 "Residual Encoding"; French page,
+ * Méthodologie §2 "Architecture de compression").
  */
 dkv_status deltakv_compress(const dkv_layout* layout, const dkv_compress_in* in, const dkv_cache* cache,
                             void* ws, size_t ws_bytes, void* stream);
@@ -332,11 +339,13 @@ dkv_status deltakv_append(const dkv_layout* layout, const dkv_append_in* in, con
 
 /*
  * Decode attention of one query per sequence over a compressed cache, as if
- * every token were reconstructed and attended to; mathematically equal to
- * softmax(q K^T * scale) V^ over the reconstructed K^ and V^, computed
- * without materialising them (the shared key component shifts every score
- * equally and is not read).  `ws` as for deltakv_compress, of at least
- * dkv_decode_workspace_bytes(layout, n_q_heads, n_splits) bytes.
+ * every token were reconstructed and attended to (English page, Technical
+ * Summary §3 "Reconstruction": a token is its decoded code plus its
+ * reference); mathematically equal to softmax(q K^T * scale) V^ over the
+ * reconstructed K^ and V^, computed without materialising them (the shared
+ * key component shifts every score equally and is not read).  `ws` as for
+ * deltakv_compress, of at least dkv_decode_workspace_bytes(layout,
+ * n_q_heads, n_splits) bytes.
  */
 dkv_status deltakv_decode_attn(const dkv_layout* layout, const dkv_cache* cache, const dkv_decode_in* in,
                                void* ws, size_t ws_bytes, void* stream);
