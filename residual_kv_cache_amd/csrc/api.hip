@@ -291,6 +291,7 @@ dkv_status decode_setup(const dkv_layout* layout, const dkv_cache* cache, const 
   if (in->n_q_heads / sh->H > 16) return DKV_ERR_UNSUPPORTED;
   if (in->n_splits > 1024) return DKV_ERR_UNSUPPORTED;
   if (in->w_head_stride < 0) return DKV_ERR_SHAPE;
+  if (in->w_head_stride % 8) return DKV_ERR_ALIGN;
   if (in->w_head_stride != 0 && in->w_head_stride < (int64_t)sh->d * sh->dc) return DKV_ERR_SHAPE;
   if (!(in->softmax_scale >= 0.f) || isinf(in->softmax_scale)) return DKV_ERR_SHAPE;
   const int G = (int)(in->n_q_heads / sh->H);

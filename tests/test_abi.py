@@ -235,8 +235,8 @@ def test_compress_rejects_before_launch():
     assert _compress_status(lay2, P, P, P, P, cache) == 6
 
 
-def _decode_status(lay, q, wu, out, ws, cache, hq=32, splits=0, scale=0.0, ws_bytes=None, reserved=0):
-    a = D.dkv_decode_in(q, wu, wu, 0, hq, splits, scale, reserved, out, None)
+def _decode_status(lay, q, wu, out, ws, cache, hq=32, splits=0, scale=0.0, ws_bytes=None, reserved=0, whs=0):
+    a = D.dkv_decode_in(q, wu, wu, whs, hq, splits, scale, reserved, out, None)
     return D.lib().deltakv_decode_attn(ctypes.byref(lay), ctypes.byref(cache.c), ctypes.byref(a),
                                        ctypes.c_void_p(ws), ws_bytes if ws_bytes is not None else 1 << 30, None)
 
@@ -257,6 +257,9 @@ def test_decode_rejects_before_launch():
     assert _decode_status(lay, P, P, P, P, cache, scale=-1.0) == 2
     assert _decode_status(lay, P, P, P, P, cache, scale=float("nan")) == 2
     assert _decode_status(lay, P, P, P, P, cache, reserved=1) == 2
+    # per-head matrices: the stride is a multiple of 8 elements (16-byte rows) and covers one matrix
+    assert _decode_status(lay, P, P, P, P, cache, whs=128 * 32 + 4) == 4
+    assert _decode_status(lay, P, P, P, P, cache, whs=8) == 2
     assert _decode_status(lay, P, P, P, None, cache) == 5
     assert _decode_status(lay, P, P, P, P, cache, ws_bytes=need - 1) == 5
     bad = FakeCache(P)
