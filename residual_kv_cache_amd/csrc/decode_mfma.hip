@@ -77,6 +77,21 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
+// a where the bits of m are set, b elsewhere (one bitfield select, never a
+// branch).
+__device__ __forceinline__ float bsel(uint32_t m, float a, float b) {
+  return __uint_as_float((__float_as_uint(a) & m) | (__float_as_uint(b) & ~m));
+}
+
+// v[i] of a four-entry register array for a run-time i in 0..3, by bitfield
+// selects (the array stays in registers, and a lane-dependent i makes no
+// divergent branch).
+__device__ __forceinline__ float pick4(float v0, float v1, float v2, float v3, int i) {
+  const uint32_t m1 = 0u - (uint32_t)(i & 1), m2 = 0u - (uint32_t)((i >> 1) & 1);
+  return bsel(m2, bsel(m1, v3, v2), bsel(m1, v1, v0));
+}
+__device__ __forceinline__ float pick4(const float (&v)[4], int i) { return pick4(v[0], v[1], v[2], v[3], i); }
+
 // Global-memory load at a byte offset (the address space is explicit so that
 // selected base pointers still compile to global, not flat, loads).
 template <typename T>
@@ -91,9 +106,11 @@ __device__ const uint16_t kOnePair[8] __attribute__((aligned(16))) = {0x3F80u, 0
 // ---------------------------------------------------------------------------
 // refscore.  Block (bh, chunk) of 256 threads: S rows of kRsRefs references
 // (wave w: references chunk*64 + 16w + n16; A = q_g, B = reference rows, so
-// lane (n16, q4 = 0) ends with S[r][0..3]), and the q' outputs
-// o = chunk + chunks * (16 t + quarter) (16 lanes per output, 8 products
-// each, summed by a fixed butterfly).
+// lane (n16, q4 = 0) ends with S[r][0..3]); wave 0 also computes q' outputs
+// 4 (chunk + chunks m), m = 0, 1, ...: four consecutive code columns of one
+// query head, lane l taking rows l and l + 64 of W_up (8 contiguous bytes
+// each), summed over the wave by a fixed butterfly.  The first group's
+// loads go out with the S loads, so a block takes one round trip.
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(256) void k_refscore_mfma(DecodeArgs a, Shape sh, int chunks) {
@@ -101,7 +118,7 @@ __global__ __launch_bounds__(256) void k_refscore_mfma(DecodeArgs a, Shape sh, i
   const int bh = xcd + 8 * (kx / chunks), c = kx % chunks;
   if (bh >= sh.B * sh.H) return;
   const int b = bh / sh.H, h = bh % sh.H;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n16 = lane & 15, q4 = lane >> 4;
   const int G = a.G, dc = sh.dc;
   const float cs = a.scale * kLog2e;
@@ -110,6 +127,45 @@ __global__ __launch_bounds__(256) void k_refscore_mfma(DecodeArgs a, Shape sh, i
   const int r = c * kRsRefs + wave * 16 + n16;
   const uint32_t rr = (uint32_t)min(r, sh.R - 1);
   const uint16_t* refsK = (const uint16_t*)a.refs + (size_t)bh * 2 * sh.Rc * kD;
+  // q' group of this block (wave 0): outputs o0 .. o0 + 3 (clamped when the
+  // block has none; the stores are masked).
+  const int no = G * dc;
+  const uint16_t* wu = (const uint16_t*)a.wuk + (size_t)h * a.w_hs;
+  auto qp_loads = [&](int o0, U32x2 (&w)[2], uint16_t (&qx)[2]) {
+    const int oc = min(o0, no - 4);
+    const int g = oc / dc, j = oc % dc;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const uint32_t row = (uint32_t)(lane + 64 * hh);
+      w[hh] = ldg<U32x2>(wu, (row * dc + (uint32_t)j) * 2u);
+      qx[hh] = ldg<uint16_t>(q, ((uint32_t)g * kD + row) * 2u);
+    }
+  };
+  auto qp_out = [&](int o0, const U32x2 (&w)[2], const uint16_t (&qx)[2]) {
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const float qf = bf2f(qx[hh]);
+      v[0] = fmaf(qf, __uint_as_float(w[hh].x << 16), v[0]);
+      v[1] = fmaf(qf, __uint_as_float(w[hh].x & 0xFFFF0000u), v[1]);
+      v[2] = fmaf(qf, __uint_as_float(w[hh].y << 16), v[2]);
+      v[3] = fmaf(qf, __uint_as_float(w[hh].y & 0xFFFF0000u), v[3]);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += __shfl_xor(v[e], o, 64);
+    if (lane < 4 && o0 < no) {
+      const int g = o0 / dc, j = o0 % dc + lane;
+      a.qp[((size_t)bh * G + g) * dc + j] = pick4(v, lane) * cs;
+    }
+  };
+  // Every wave issues the first group's loads (a branch around them would
+  // make the compiler wait for them at its end); wave 0 uses them.
+  const bool qp_wave = wave == 0 && 4 * c < no;
+  U32x2 w0[2];
+  uint16_t q0[2];
+  qp_loads(4 * c, w0, q0);
   // The S part's loads are unconditional (query row clamped, heads past G
   // zeroed after the loads), so all eight are in flight at once.
   Frag aq[4], br[4];
@@ -127,26 +183,15 @@ __global__ __launch_bounds__(256) void k_refscore_mfma(DecodeArgs a, Shape sh, i
   }
   if (q4 == 0 && r < sh.R)
     *reinterpret_cast<f32x4*>(a.score + ((size_t)bh * sh.R + r) * 4) = acc * cs;
-
-  // q' outputs o = chunk + chunks * (16 t + quarter): 16 lanes per output, 8
-  // products each, summed by a fixed butterfly.
-  const int quarter = wave * 4 + q4;
-  const uint16_t* wu = (const uint16_t*)a.wuk + (size_t)h * a.w_hs;
-  for (int o = c + chunks * quarter; o < G * dc; o += chunks * 16) {
-    const int g = o / dc, j = o % dc;
-    const Frag qv = ldg<Frag>(q, ((uint32_t)g * kD + n16 * 8) * 2u);
-    float sacc = 0.f;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const uint32_t qw = qv[t >> 1];
-      const float qf = __uint_as_float((t & 1) ? (qw & 0xFFFF0000u) : (qw << 16));
-      sacc = fmaf(qf, bf2f(wu[(size_t)(n16 * 8 + t) * dc + j]), sacc);
+  if (qp_wave) {
+    qp_out(4 * c, w0, q0);
+    // Further groups of this block (only when G d_c > 4 chunks).
+    for (int o0 = 4 * (c + chunks); o0 < no; o0 += 4 * chunks) {
+      U32x2 w[2];
+      uint16_t qx[2];
+      qp_loads(o0, w, qx);
+      qp_out(o0, w, qx);
     }
-    sacc += __shfl_xor(sacc, 8, 64);
-    sacc += __shfl_xor(sacc, 4, 64);
-    sacc += __shfl_xor(sacc, 2, 64);
-    sacc += __shfl_xor(sacc, 1, 64);
-    if (n16 == 0) a.qp[((size_t)bh * G + g) * dc + j] = sacc * cs;
   }
 }
 
@@ -860,20 +905,6 @@ __global__ __launch_bounds__(kThreads) void k_split_mfma(DecodeArgs a, Shape sh)
 
 constexpr int kHistTiles = 4;   // tiles per wave per chunk: one per lane of a quad
 
-// a where the bits of m are set, b elsewhere (one bitfield select, never a
-// branch).
-__device__ __forceinline__ float bsel(uint32_t m, float a, float b) {
-  return __uint_as_float((__float_as_uint(a) & m) | (__float_as_uint(b) & ~m));
-}
-
-// v[i] of a four-entry register array for a run-time i in 0..3, by bitfield
-// selects (the array stays in registers, and a lane-dependent i makes no
-// divergent branch).
-__device__ __forceinline__ float pick4(float v0, float v1, float v2, float v3, int i) {
-  const uint32_t m1 = 0u - (uint32_t)(i & 1), m2 = 0u - (uint32_t)((i >> 1) & 1);
-  return bsel(m2, bsel(m1, v3, v2), bsel(m1, v1, v0));
-}
-__device__ __forceinline__ float pick4(const float (&v)[4], int i) { return pick4(v[0], v[1], v[2], v[3], i); }
 
 // Lane K of each quad (four consecutive lanes), broadcast over the quad.
 template <int K>
