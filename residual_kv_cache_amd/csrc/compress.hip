@@ -191,7 +191,6 @@ __global__ __launch_bounds__(256) void k_center_refs(CompressArgs a, Shape sh) {
 // token merge at the end (larger key, then lower ordinal).
 // ---------------------------------------------------------------------------
 
-constexpr int kSearchRefs = 64;   // references per LDS chunk (k references)
 constexpr int kTop1Refs = 128;    // references per LDS chunk (top-1 search)
 // Low key bits that hold a candidate's place in its top-1 chunk: each lane
 // sees 4 of every 16 references, kTop1Refs / 4 places.
@@ -577,23 +576,123 @@ __global__ __launch_bounds__(256) void k_search_f32(CompressArgs a, Shape sh) {
 // ---------------------------------------------------------------------------
 
 // bfloat16: the block and chunk structure of k_search_mfma (256 positions
-// per block, two 16-token MFMA tiles per wave, references staged through LDS
-// in double-buffered chunks of 64 with their norm terms), with a sorted list
-// of the best k per lane and token tile in place of the running maximum.
-// The norm term of a reference is 1 / ||r|| (cosine) or ||r||^2 (L2), written
-// by k_center_refs.  A candidate costs one multiply or FMA and a comparison
-// with the lane's k-th score (cached, refreshed after insertions; a tie passes
-// the test and the insertion applies the exact order); insertion runs, per
-// candidate slot, only when some lane of the wave has a candidate that
-// passes.  Lists hold KT >= k entries (4 or 8).  At the end the four lane
-// groups of a token merge their lists and lane group 0 writes the ordinals.
-template <int D, int KT, bool KFULL>
-__global__ __launch_bounds__(kSearchThreads) void k_search_topk_mfma(CompressArgs a, Shape sh) {
+// per block, two 16-token MFMA tiles per wave, 128-reference chunks loaded
+// straight into XOR-swizzled LDS, the norm terms through a register), with
+// lists of the KT best candidates in place of the running maximum, and no
+// data-dependent branches.  Candidates carry the selection key of
+// k_search_mfma: an unsigned integer that orders as the score (cosine:
+// dot / ||r|| offset by 2 ||x~_t||; L2: 2 dot - ||r||^2 in the usual
+// sign-flip integer order of floats), with its low 5 bits replaced by
+// 31 - (place in the chunk), so equal scores within a chunk order by
+// ordinal; the perturbation is below 2^-18 of the key (cosine: keys are at
+// most 3 ||x~_t||) or of |score| (L2), inside the 1e-4 margin.  Key 0 is
+// "no candidate".  Per chunk a lane keeps a descending
+// list of its KT best keys: each tile's four keys are sorted by a network
+// and merged in with a bitonic step.  At the end of the chunk the list
+// joins the lane's running list of (key, ordinal) under the total order
+// "key above the place bits, then lower ordinal", by the same bitonic
+// merge; at the end the four lane groups of a token merge their lists the
+// same way and lane group 0 writes the first min(k, refs before t)
+// ordinals in ascending order.  KT = 1, 4 or 8 >= k.
+// ---------------------------------------------------------------------------
+
+// a >= b afterwards.
+__device__ __forceinline__ void cswap_u(uint32_t& a, uint32_t& b) {
+  const uint32_t hi = max(a, b), lo = min(a, b);
+  a = hi;
+  b = lo;
+}
+
+// Sorts a bitonic sequence into descending order (half-cleaner stages).
+template <int N>
+__device__ __forceinline__ void bitonic_desc(uint32_t (&v)[N]) {
+#pragma unroll
+  for (int h = N / 2; h >= 1; h /= 2)
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+      if ((j & h) == 0) cswap_u(v[j], v[j + h]);
+}
+
+// The four keys of a tile into a descending list of the KT best keys.
+template <int KT>
+__device__ __forceinline__ void tile_into_list(uint32_t (&L)[KT], uint32_t c0, uint32_t c1, uint32_t c2,
+                                               uint32_t c3) {
+  if constexpr (KT == 1) {
+    L[0] = max(max(L[0], c0), max(max(c1, c2), c3));
+  } else {
+    uint32_t c[4] = {c0, c1, c2, c3};
+    cswap_u(c[0], c[1]);
+    cswap_u(c[2], c[3]);
+    cswap_u(c[0], c[2]);
+    cswap_u(c[1], c[3]);
+    cswap_u(c[1], c[2]);
+    // L descending and c ascending side by side: their elementwise maxima
+    // form a bitonic sequence holding the KT largest of both.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) L[KT - 4 + j] = max(L[KT - 4 + j], c[3 - j]);
+    bitonic_desc(L);
+  }
+}
+
+// Running lists: keys and ordinals, ordered by the key above the place bits
+// (descending), then by ordinal (ascending).
+template <int KT>
+struct SelList {
+  uint32_t k[KT];
+  int r[KT];
+};
+
+__device__ __forceinline__ bool sel_before(uint32_t ak, int ar, uint32_t bk, int br) {
+  const uint32_t at = ak & ~kPlaceMask, bt = bk & ~kPlaceMask;
+  return (at > bt) | ((at == bt) & (ar < br));
+}
+
+// G <- the KT first of G and (bk, br), both in list order.
+template <int KT>
+__device__ __forceinline__ void merge_sel(SelList<KT>& G, const uint32_t (&bk)[KT], const int (&br)[KT]) {
+#pragma unroll
+  for (int j = 0; j < KT; ++j) {
+    const int q = KT - 1 - j;
+    const bool take = sel_before(bk[q], br[q], G.k[j], G.r[j]);
+    G.k[j] = take ? bk[q] : G.k[j];
+    G.r[j] = take ? br[q] : G.r[j];
+  }
+#pragma unroll
+  for (int h = KT / 2; h >= 1; h /= 2)
+#pragma unroll
+    for (int j = 0; j < KT; ++j)
+      if ((j & h) == 0) {
+        const bool sw = sel_before(G.k[j + h], G.r[j + h], G.k[j], G.r[j]);
+        const uint32_t tk = G.k[j];
+        const int tr = G.r[j];
+        G.k[j] = sw ? G.k[j + h] : G.k[j];
+        G.r[j] = sw ? G.r[j + h] : G.r[j];
+        G.k[j + h] = sw ? tk : G.k[j + h];
+        G.r[j + h] = sw ? tr : G.r[j + h];
+      }
+}
+
+// Selection key of a candidate with accumulator acc and norm term n (off:
+// the token's cosine offset).
+template <bool L2>
+__device__ __forceinline__ uint32_t sel_key(float acc, float n, float off, uint32_t place) {
+  uint32_t u;
+  if constexpr (L2) {
+    const uint32_t b = __float_as_uint(fmaf(2.f, acc, -n));
+    u = b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
+  } else {
+    u = __float_as_uint(fmaf(acc, n, off));
+  }
+  return (u & ~kPlaceMask) | (kPlaceMask - place);
+}
+
+template <int D, int KT, bool L2>
+__global__ __launch_bounds__(kSearchThreads) __attribute__((amdgpu_waves_per_eu(KT > 4 ? 2 : 4))) void k_search_topk_mfma(
+    CompressArgs a, Shape sh) {
   constexpr int KS = D / 32;
-  constexpr int LDR = D + 8;
-  constexpr int PER = kSearchRefs * (D / 8) / kSearchThreads;
-  __shared__ __attribute__((aligned(16))) uint16_t lds_ref[2][kSearchRefs * LDR];
-  __shared__ float lds_nrm[2][kSearchRefs];
+  constexpr int MT = kTop1Refs / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t lds_ref0[kTop1Refs * D], lds_ref1[kTop1Refs * D];
+  __shared__ __attribute__((aligned(16))) float lds_n0[kTop1Refs], lds_n1[kTop1Refs];
 
   const XcdItem xi = xcd_item(sh.n_streams());
   if (xi.stream < 0) return;
@@ -602,8 +701,6 @@ __global__ __launch_bounds__(kSearchThreads) void k_search_topk_mfma(CompressArg
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lrow = lane & 15, lgrp = lane >> 4;
-  const int K = KFULL ? KT : sh.K;   // k equal to the list length: a compile-time constant
-  const bool l2 = sh.l2 != 0;
   const StreamId id = decode_stream(stream, sh.H);
   const uint16_t* src = stream_src<BF16>(a, id);
   const uint16_t* mu = (const uint16_t*)a.mu + (size_t)stream * D;
@@ -616,73 +713,123 @@ __global__ __launch_bounds__(kSearchThreads) void k_search_topk_mfma(CompressArg
   const int rend_b = (tmax_b + sh.s - 1) / sh.s;
   const int tmax_w = min(sh.T - 1, tw + 16 * kSearchNT - 1);
   const int rend_w = tw < sh.T ? (tmax_w + sh.s - 1) / sh.s : 0;
-  const int nchunks = (rend_b + kSearchRefs - 1) / kSearchRefs;
+  const int nchunks = (rend_b + kTop1Refs - 1) / kTop1Refs;
 
-  uint4 pre[PER];
+  // Chunk loads as in k_search_mfma.
+  constexpr int NI = kTop1Refs * D * 2 / (kSearchWaves * 1024);
   float pn = 0.f;
-  auto fetch = [&](int ch) {
-    const int rc = ch * kSearchRefs;
+  auto fetch = [&](int ch, uint16_t* dref) {
+    const int rc = ch * kTop1Refs;
+    const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(refs + (size_t)rc * D), (short)0, (rend_b - rc) * D * 2, kBufferRsrcWord3);
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int q = tid + j * kSearchThreads;
-      const int row = q / (D / 8), col = (q % (D / 8)) * 8;
-      pre[j] = rc + row < rend_b ? *reinterpret_cast<const uint4*>(refs + (size_t)(rc + row) * D + col)
-                                 : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < NI; ++j) {
+      const int q = (wave * NI + j) * 64 + lane;
+      load_to_lds16(rr, dref + (wave * NI + j) * 512, (uint32_t)chunk_off<D>(q / (D / 8), q % (D / 8)) * 2);
     }
-    if (tid < kSearchRefs) {
-      const float v = nrm[min(rc + tid, rend_b - 1)];
-      pn = rc + tid < rend_b ? v : 0.f;
+    if (tid < kTop1Refs) {
+      const __amdgpu_buffer_rsrc_t rn = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(nrm + rc), (short)0, (rend_b - rc) * 4, kBufferRsrcWord3);
+      pn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rn, tid * 4, 0, 0));
     }
   };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int q = tid + j * kSearchThreads;
-      const int row = q / (D / 8), col = (q % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(&lds_ref[buf][row * LDR + col]) = pre[j];
-    }
-    if (tid < kSearchRefs) lds_nrm[buf][tid] = pn;
+  auto stash = [&](float* dn) {
+    if (tid < kTop1Refs) dn[tid] = pn;
   };
-  if (nchunks > 0) fetch(0);
+  if (nchunks > 0) fetch(0, lds_ref0);
 
-  // B operands: the centred tokens rnd(x - mu), as in k_search_mfma.
+  // B operands (centred tokens rnd(x - mu)) and, for cosine, the key offset
+  // 2 ||x~_t|| of k_search_mfma.
   bf16x8 bt[kSearchNT][KS];
+  float off[kSearchNT] = {};
   {
     uint4 xr[kSearchNT][KS], mr[KS];
     load_tokens<D>(src, a.st, mu, tw, sh.T, lrow, lgrp, xr, mr);
+    float n2[kSearchNT] = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int nt = 0; nt < kSearchNT; ++nt) {
         uint32_t w[4];
         centre8(xr[nt][ks], mr[ks], w);
+        if (!L2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            n2[nt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[e]),
+                                                     __builtin_bit_cast(bf16x2_t, w[e]), n2[nt], false);
+        }
         bt[nt][ks] = __builtin_bit_cast(bf16x8, w);
       }
-  }
-
-  TopKN<KT> top[kSearchNT];
-  float ths[kSearchNT];
-  int thr[kSearchNT];
+    if (!L2) {
 #pragma unroll
-  for (int nt = 0; nt < kSearchNT; ++nt) {
-    top[nt].init();
-    top[nt].kth(K, ths[nt], thr[nt]);
+      for (int nt = 0; nt < kSearchNT; ++nt) {
+        float v = n2[nt];
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        off[nt] = 2.0f * sqrtf(v) + 1e-30f;
+      }
+    }
   }
 
-  if (nchunks > 0) stash(0);
+  SelList<KT> best[kSearchNT];
+#pragma unroll
+  for (int nt = 0; nt < kSearchNT; ++nt)
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      best[nt].k[j] = 0u;
+      best[nt].r[j] = 0x7FFFFFFF;
+    }
+
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  if (nchunks > 0) stash(lds_n0);
   __syncthreads();
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const int rc = ch * kSearchRefs;
-    const int buf = ch & 1;
-    if (ch + 1 < nchunks) fetch(ch + 1);
-    if (rc < rend_w) {
-      const int nmt = min(kSearchRefs / 16, (rend_w - rc + 15) / 16);
+  auto chunk = [&](int ch, const uint16_t* cref, const float* cn, uint16_t* nref, float* nn) {
+    const int rc = ch * kTop1Refs;
+    if (ch + 1 < nchunks) fetch(ch + 1, nref);
+    uint32_t L[kSearchNT][KT];
+#pragma unroll
+    for (int nt = 0; nt < kSearchNT; ++nt)
+#pragma unroll
+      for (int j = 0; j < KT; ++j) L[nt][j] = 0u;
+    const int nmt = min(MT, (rend_w - rc + 15) / 16);
+    if (rc < rend_w && nmt == MT && (rc + kTop1Refs - 1) * sh.s < tw) {
+      // Full chunk before the wave's first position: no causal mask.  The A
+      // fragments of tile mt + 1 are read from LDS while tile mt's MFMAs run.
+      bf16x8 ar[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        ar[ks] = *reinterpret_cast<const bf16x8*>(&cref[chunk_off<D>(lrow, ks * 4 + lgrp)]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 acc[kSearchNT];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+          for (int nt = 0; nt < kSearchNT; ++nt)
+            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar[ks], bt[nt][ks],
+                                                              ks ? acc[nt] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          if (mt + 1 < MT)
+            ar[ks] = *reinterpret_cast<const bf16x8*>(&cref[chunk_off<D>((mt + 1) * 16 + lrow, ks * 4 + lgrp)]);
+        }
+        const f32x4 n4 = *reinterpret_cast<const f32x4*>(&cn[mt * 16 + lgrp * 4]);
+#pragma unroll
+        for (int nt = 0; nt < kSearchNT; ++nt) {
+          uint32_t c[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) c[i] = sel_key<L2>(acc[nt][i], n4[i], off[nt], (uint32_t)(4 * mt + i));
+          tile_into_list<KT>(L[nt], c[0], c[1], c[2], c[3]);
+        }
+      }
+    } else if (rc < rend_w) {
+      // Partial or diagonal chunk, one tile at a time; a candidate needs
+      // r s < t.
+#pragma unroll 1
       for (int mt = 0; mt < nmt; ++mt) {
         const int rbase = rc + mt * 16;
         bf16x8 ar[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          ar[ks] = *reinterpret_cast<const bf16x8*>(&lds_ref[buf][(mt * 16 + lrow) * LDR + ks * 32 + lgrp * 8]);
+          ar[ks] = *reinterpret_cast<const bf16x8*>(&cref[chunk_off<D>(mt * 16 + lrow, ks * 4 + lgrp)]);
         f32x4 acc[kSearchNT];
 #pragma unroll
         for (int nt = 0; nt < kSearchNT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -691,57 +838,76 @@ __global__ __launch_bounds__(kSearchThreads) void k_search_topk_mfma(CompressArg
 #pragma unroll
           for (int nt = 0; nt < kSearchNT; ++nt)
             acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar[ks], bt[nt][ks], acc[nt], 0, 0, 0);
-        float nr[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) nr[i] = lds_nrm[buf][mt * 16 + lgrp * 4 + i];
+        const f32x4 n4 = *reinterpret_cast<const f32x4*>(&cn[mt * 16 + lgrp * 4]);
         const int r0 = rbase + lgrp * 4;
-        const bool masked = (rbase + 15) * sh.s >= tw;
 #pragma unroll
         for (int nt = 0; nt < kSearchNT; ++nt) {
           const int t = tw + nt * 16 + lrow;
-          float v[4];
-          bool want[4];
-          (void)thr;
+          uint32_t c[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            v[i] = l2 ? fmaf(2.f, acc[nt][i], -nr[i]) : acc[nt][i] * nr[i];
-            const bool ok = !masked | (((r0 + i) * sh.s < t) & (t < sh.T));
-            want[i] = ok & (v[i] >= ths[nt]);
+            const uint32_t k = sel_key<L2>(acc[nt][i], n4[i], off[nt], (uint32_t)(4 * mt + i));
+            c[i] = (r0 + i) * sh.s < t ? k : 0u;
           }
-          bool any = false;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (__ballot(want[i]) != 0ull) {
-              top[nt].insert(want[i] ? v[i] : -INFINITY, want[i] ? r0 + i : 0x7FFFFFFF, K);
-              any = true;
-            }
-          }
-          if (any) {
-            // Pass threshold: the largest k-th score of the token's four
-            // lane lists.  The token's k best over all references score at
-            // least that much, so a candidate below it can never be kept;
-            // ties pass and the insertion applies the exact order.
-            top[nt].kth(K, ths[nt], thr[nt]);
-            ths[nt] = fmaxf(ths[nt], __shfl_xor(ths[nt], 16, 64));
-            ths[nt] = fmaxf(ths[nt], __shfl_xor(ths[nt], 32, 64));
-          }
+          tile_into_list<KT>(L[nt], c[0], c[1], c[2], c[3]);
         }
       }
     }
-    if (ch + 1 < nchunks) stash(buf ^ 1);
+    if (rc < rend_w) {
+      // The chunk's lists join the running lists (ordinals from the place
+      // bits).
+#pragma unroll
+      for (int nt = 0; nt < kSearchNT; ++nt) {
+        int lr[KT];
+#pragma unroll
+        for (int j = 0; j < KT; ++j) {
+          const uint32_t q = kPlaceMask - (L[nt][j] & kPlaceMask);
+          lr[j] = rc + (int)(q >> 2) * 16 + lgrp * 4 + (int)(q & 3);
+        }
+        merge_sel<KT>(best[nt], L[nt], lr);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    if (ch + 1 < nchunks) stash(nn);
     __syncthreads();
+  };
+  for (int ch = 0; ch < nchunks; ch += 2) {
+    chunk(ch, lds_ref0, lds_n0, lds_ref1, lds_n1);
+    if (ch + 1 < nchunks) chunk(ch + 1, lds_ref1, lds_n1, lds_ref0, lds_n0);
   }
 
+  // The four lane groups of each token merge their lists; lane group 0
+  // writes the first min(k, refs before t) ordinals in ascending order.
+  const int K = sh.K;
 #pragma unroll
   for (int nt = 0; nt < kSearchNT; ++nt) {
-    top[nt].merge_xor(16, K);
-    top[nt].merge_xor(32, K);
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      uint32_t ok[KT];
+      int orr[KT];
+#pragma unroll
+      for (int j = 0; j < KT; ++j) {
+        ok[j] = (uint32_t)__shfl_xor((int)best[nt].k[j], o, 64);
+        orr[j] = __shfl_xor(best[nt].r[j], o, 64);
+      }
+      merge_sel<KT>(best[nt], ok, orr);
+    }
     const int t = tw + nt * 16 + lrow;
     if (lgrp == 0 && t < sh.T && t % sh.s != 0) {
-      int o[kTopMax];
-      top[nt].sorted_ordinals(min(K, t / sh.s + 1), o);
+      const int c = min(K, t / sh.s + 1);
+      int v[KT];
+#pragma unroll
+      for (int j = 0; j < KT; ++j) v[j] = j < c ? best[nt].r[j] : 0x7FFFFFFF;
+#pragma unroll
+      for (int i = 0; i < KT; ++i)
+#pragma unroll
+        for (int j = 0; j + 1 < KT - i; ++j) {
+          const int lo = min(v[j], v[j + 1]), hi = max(v[j], v[j + 1]);
+          v[j] = lo;
+          v[j + 1] = hi;
+        }
       const size_t base = ((size_t)stream * sh.Nc + pos_to_slot(t, sh.s)) * K;
-      for (int j = 0; j < K; ++j) store_idx(a.idx, base + j, sh.idx_bytes, (uint32_t)o[j]);
+      for (int j = 0; j < K; ++j) store_idx(a.idx, base + j, sh.idx_bytes, (uint32_t)(j < c ? v[j] : 0));
     }
   }
 }
@@ -1003,10 +1169,11 @@ hipError_t launch_compress_d(const Shape& sh, const CompressArgs& a, hipStream_t
     DKV_TRY(launch(k_center_refs<BF16>, g_ref, 256, st, ev_start(ev, 1), ev_stop(ev, 1), a, sh));
     if (sh.N > 0) {
       if (sh.topk_search()) {
-        auto kern = sh.K == 4   ? k_search_topk_mfma<D, 4, true>
-                    : sh.K < 4  ? k_search_topk_mfma<D, 4, false>
-                    : sh.K == 8 ? k_search_topk_mfma<D, 8, true>
-                                : k_search_topk_mfma<D, 8, false>;
+        // Lists of 1, 4 or 8 entries (at least k).
+        auto kern = sh.l2 ? (sh.K == 1 ? k_search_topk_mfma<D, 1, true>
+                             : sh.K <= 4 ? k_search_topk_mfma<D, 4, true>
+                                         : k_search_topk_mfma<D, 8, true>)
+                          : (sh.K <= 4 ? k_search_topk_mfma<D, 4, false> : k_search_topk_mfma<D, 8, false>);
         DKV_TRY(launch(kern, g_search, kSearchThreads, st, ev_start(ev, 2), ev_stop(ev, 2), a, sh));
       } else {
         DKV_TRY(launch(k_search_mfma<D>, g_search, kSearchThreads, st, ev_start(ev, 2), ev_stop(ev, 2), a, sh));
