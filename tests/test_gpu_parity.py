@@ -272,10 +272,10 @@ def test_handmade_ties_on_gpu():
                                         (1500, 4, "l2")])
 def test_handmade_ties_across_chunks(T, k, metric):
     """Exact ties spread over several search chunks (stride 4: 275 or more
-    references, so three or more 128-reference chunks of the top-1 search and
-    five or more 64-reference chunks of the top-k search): a later chunk wins
-    only with a strictly better score, and the merge of a token's lane groups
-    keeps the lower ordinal, so every tied set equals the oracle's exactly."""
+    references, so three or more 128-reference chunks of either search): a
+    later chunk wins only with a strictly better score, and the merge of a
+    token's lane groups keeps the lower ordinal, so every tied set equals the
+    oracle's exactly."""
     cfg = BASE_BF16.replace(name="ties_x", seq_len=T, n_kv_heads=1, n_q_heads=4, stride=4)
     rng = np.random.default_rng(5 + T + k)
     d = cfg.head_dim
