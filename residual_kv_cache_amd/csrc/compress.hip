@@ -147,31 +147,50 @@ __global__ __launch_bounds__(256) void k_mean_final(CompressArgs a, Shape sh, in
 }
 
 // ---------------------------------------------------------------------------
-// Centred references and their inverse norms.  grid (ceil(R/4), streams),
-// block 256: one wave per reference, lanes across the head dim.
+// Centred references and their inverse norms.  grid (ceil(R / (256 / (d/8))),
+// streams), block 256: d/8 lanes per reference, eight elements per lane (one
+// 16-byte load each of the row and of mu), the squared norm summed over the
+// lane group by a fixed butterfly.
 // ---------------------------------------------------------------------------
 
 template <class S>
 __global__ __launch_bounds__(256) void k_center_refs(CompressArgs a, Shape sh) {
   const int stream = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + wave;
+  const int lpr = sh.d / 8, rpb = 256 / lpr;   // lanes per reference, references per block
+  const int l = threadIdx.x % lpr;
+  const int r = blockIdx.x * rpb + threadIdx.x / lpr;
   if (r >= sh.R) return;
   const StreamId id = decode_stream(stream, sh.H);
-  const typename S::T* src = stream_src<S>(a, id) + (int64_t)r * sh.s * a.st;
-  const typename S::T* mu = (const typename S::T*)a.mu + (size_t)stream * sh.d;
-  typename S::T* dst = (typename S::T*)a.refs + ((size_t)stream * sh.Rc + r) * sh.d;
+  const typename S::T* src = stream_src<S>(a, id) + (int64_t)r * sh.s * a.st + l * 8;
+  const typename S::T* mu = (const typename S::T*)a.mu + (size_t)stream * sh.d + l * 8;
+  typename S::T* dst = (typename S::T*)a.refs + ((size_t)stream * sh.Rc + r) * sh.d + l * 8;
+  float x[8], m[8];
+  load8(src, x);
+  load8(mu, m);
+  typename S::T y[8];
   float n2 = 0.f;
-  for (int i = lane; i < sh.d; i += 64) {
-    typename S::T x = S::sub_rn(S::load(src[i]), S::load(mu[i]));
-    dst[i] = x;
-    float f = S::load(x);
-    n2 += f * f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    y[i] = S::sub_rn(x[i], m[i]);
+    const float f = S::load(y[i]);
+    n2 = fmaf(f, f, n2);
   }
-  n2 = wave_sum(n2);
+  if constexpr (sizeof(typename S::T) == 2) {
+    uint4 o;
+    o.x = (uint32_t)y[0] | ((uint32_t)y[1] << 16);
+    o.y = (uint32_t)y[2] | ((uint32_t)y[3] << 16);
+    o.z = (uint32_t)y[4] | ((uint32_t)y[5] << 16);
+    o.w = (uint32_t)y[6] | ((uint32_t)y[7] << 16);
+    *reinterpret_cast<uint4*>(dst) = o;
+  } else {
+    *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
+    *reinterpret_cast<float4*>(dst + 4) = make_float4(y[4], y[5], y[6], y[7]);
+  }
+  // The lane group (lpr consecutive lanes of one wave) sums its parts.
+  for (int o = 1; o < lpr; o <<= 1) n2 += __shfl_xor(n2, o, 64);
   // Norm term of the search: 1 / ||r|| (cosine; 0 for a zero reference) or
   // ||r||^2 (L2).
-  if (lane == 0) a.inv_n[(size_t)stream * sh.R + r] = sh.l2 ? n2 : n2 > 0.f ? 1.0f / sqrtf(n2) : 0.0f;
+  if (l == 0) a.inv_n[(size_t)stream * sh.R + r] = sh.l2 ? n2 : n2 > 0.f ? 1.0f / sqrtf(n2) : 0.0f;
 }
 
 // ---------------------------------------------------------------------------
@@ -1154,7 +1173,8 @@ template <int D>
 hipError_t launch_compress_d(const Shape& sh, const CompressArgs& a, hipStream_t st) {
   const int ns = sh.n_streams();
   const int chunks = mean_chunks(sh);
-  const dim3 g_mean(chunks, ns), g_ref((sh.R + 3) / 4, ns);
+  const int rpb = 256 / (D / 8);   // references per k_center_refs block
+  const dim3 g_mean(chunks, ns), g_ref((sh.R + rpb - 1) / rpb, ns);
   const dim3 g_search(xcd_grid(ns, (sh.T + kSearchTok - 1) / kSearchTok)), g_search32((sh.T + 255) / 256, ns);
   const dim3 g_enc(xcd_grid(ns, (sh.N + 63) / 64)), g_enc32((sh.N + 255) / 256, ns);
   void* const* ev = a.events;
