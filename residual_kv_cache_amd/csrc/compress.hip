@@ -32,6 +32,16 @@ namespace {
 // Loads of 8 consecutive storage elements (16-byte aligned) as floats.
 // ---------------------------------------------------------------------------
 
+// Eight packed bfloat16 values as floats.
+__device__ __forceinline__ void unpack8(uint4 u, float* out) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
 __device__ __forceinline__ void load8(const uint16_t* p, float* out) {
   uint4 u = *reinterpret_cast<const uint4*>(p);
   uint32_t w[4] = {u.x, u.y, u.z, u.w};
@@ -988,6 +998,8 @@ __global__ __launch_bounds__(256) void k_search_topk_f32(CompressArgs a, Shape s
   }
 }
 
+constexpr int kEncTiles = 4;   // 64-row tiles per encode block
+
 template <int D, bool Q4>
 __global__ __launch_bounds__(256) void k_encode_mfma(CompressArgs a, Shape sh) {
   constexpr int KS = D / 32;
@@ -1005,31 +1017,59 @@ __global__ __launch_bounds__(256) void k_encode_mfma(CompressArgs a, Shape sh) {
   const uint16_t* wd = (const uint16_t*)(id.kv ? a.wdv : a.wdk) + (size_t)id.h * a.w_hs;
   uint16_t* codes = (uint16_t*)a.codes + (size_t)stream * sh.Nc * sh.dc;
 
-  const int n = xi.item * 64 + wave * 16 + lrow;   // this lane's coded row
-  const bool valid = n < sh.N;
-  const int t = valid ? slot_to_pos(n, sh.s) : 0;
-  // The row's references: one ordinal, or (top_k > 1) the first
-  // c = min(k, floor(t / s) + 1) of its k, whose mean is the reference.
+  // Rows of tile j (kEncTiles tiles of 64 rows per block); loads use the
+  // row clamped to the last coded row, stores are masked.  The next tile's
+  // ordinal and token row are loaded while this tile's reference rows are in
+  // flight, so a tile costs about one memory round trip.
   const int K = sh.K;
-  const int cnt = valid ? min(K, t / sh.s + 1) : 1;
-  const size_t ibase = ((size_t)stream * sh.Nc + (valid ? n : 0)) * K;
-  const int r = valid ? min((int)load_idx(a.idx, ibase, sh.idx_bytes), sh.R - 1) : 0;
+  auto row_of = [&](int j) { return (xi.item * kEncTiles + j) * 64 + wave * 16 + lrow; };
+  uint32_t r_nx;
+  uint4 x_nx[KS];
+  auto prefetch = [&](int j) {
+    const int nc = min(row_of(j), sh.N - 1);
+    const int tc = slot_to_pos(nc, sh.s);
+    r_nx = load_idx(a.idx, ((size_t)stream * sh.Nc + nc) * K, sh.idx_bytes);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      x_nx[ks] = *reinterpret_cast<const uint4*>(src + (int64_t)tc * a.st + ks * 32 + lgrp * 8);
+  };
+  prefetch(0);
+  uint4 mr[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) mr[ks] = *reinterpret_cast<const uint4*>(mu + ks * 32 + lgrp * 8);
 
   for (int p = threadIdx.x; p < sh.dc * (D / 8); p += 256) {
     const int row = p / (D / 8), col = (p % (D / 8)) * 8;
     *reinterpret_cast<uint4*>(&w_lds[row * LDW + col]) = *reinterpret_cast<const uint4*>(wd + (size_t)row * D + col);
   }
 
-  bf16x8 bh[KS], bl[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const int c = ks * 32 + lgrp * 8;
-    uint32_t wh[4] = {0u, 0u, 0u, 0u}, wl[4] = {0u, 0u, 0u, 0u};
-    if (valid) {
+  for (int jt = 0; jt < kEncTiles; ++jt) {
+    const int n = row_of(jt);   // this lane's coded row
+    const bool valid = n < sh.N;
+    const int nc = min(n, sh.N - 1);
+    const int t = slot_to_pos(nc, sh.s);
+    // The row's references: one ordinal, or (top_k > 1) the first
+    // c = min(k, floor(t / s) + 1) of its k, whose mean is the reference.
+    const int cnt = min(K, t / sh.s + 1);
+    const size_t ibase = ((size_t)stream * sh.Nc + nc) * K;
+    const int r = min((int)r_nx, sh.R - 1);
+    uint4 xr[KS], rr[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      xr[ks] = x_nx[ks];
+      rr[ks] = *reinterpret_cast<const uint4*>(refs + (size_t)r * D + ks * 32 + lgrp * 8);
+    }
+    if (jt + 1 < kEncTiles) prefetch(jt + 1);
+
+    bf16x8 bh[KS], bl[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c = ks * 32 + lgrp * 8;
       float x[8], m[8], rf[8];
-      load8(src + (int64_t)t * a.st + c, x);
-      load8(mu + c, m);
-      load8(refs + (size_t)r * D + c, rf);
+      unpack8(xr[ks], x);
+      unpack8(mr[ks], m);
+      unpack8(rr[ks], rf);
       if (K > 1) {
         for (int j = 1; j < cnt; ++j) {
           float rj[8];
@@ -1041,6 +1081,7 @@ __global__ __launch_bounds__(256) void k_encode_mfma(CompressArgs a, Shape sh) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) rf[e] = cnt > 1 ? rf[e] * inv : rf[e];
       }
+      uint32_t wh[4], wl[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float d0 = (x[2 * e] - m[2 * e]) - rf[2 * e];
@@ -1048,64 +1089,64 @@ __global__ __launch_bounds__(256) void k_encode_mfma(CompressArgs a, Shape sh) {
         wh[e] = pk_bf16_rn(d0, d1);
         wl[e] = pk_bf16_rn(d0 - __uint_as_float(wh[e] << 16), d1 - __uint_as_float(wh[e] & 0xFFFF0000u));
       }
+      bh[ks] = __builtin_bit_cast(bf16x8, wh);
+      bl[ks] = __builtin_bit_cast(bf16x8, wl);
     }
-    bh[ks] = __builtin_bit_cast(bf16x8, wh);
-    bl[ks] = __builtin_bit_cast(bf16x8, wl);
-  }
-  __syncthreads();
+    if (jt == 0) __syncthreads();   // W_down staged
 
-  if constexpr (!Q4) {
-    for (int mt = 0; mt < sh.dc / 16; ++mt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 aw = *reinterpret_cast<const bf16x8*>(&w_lds[(mt * 16 + lrow) * LDW + ks * 32 + lgrp * 8]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bl[ks], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bh[ks], acc, 0, 0, 0);
-      }
-      // Lane l holds code elements mt*16 + 4*(l/16) + (0..3) of row l%16.
-      if (valid) {
-        uint2 o;
-        o.x = pk_bf16_rn(acc[0], acc[1]);
-        o.y = pk_bf16_rn(acc[2], acc[3]);
-        *reinterpret_cast<uint2*>(codes + (size_t)n * sh.dc + mt * 16 + lgrp * 4) = o;
-      }
-    }
-  } else {
-    // 4-bit codes: the whole row first (up to D / 16 tiles), then its
-    // maximum magnitude over the row's lanes l, l ^ 16, l ^ 32, l ^ 48, the
-    // scale and the nibbles.
-    const int nmt = sh.dc / 16;
-    f32x4 acc[D / 16];
-    float amax = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt) {
-      acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (mt < nmt) {
+    if constexpr (!Q4) {
+      for (int mt = 0; mt < sh.dc / 16; ++mt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const bf16x8 aw = *reinterpret_cast<const bf16x8*>(&w_lds[(mt * 16 + lrow) * LDW + ks * 32 + lgrp * 8]);
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bl[ks], acc[mt], 0, 0, 0);
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bh[ks], acc[mt], 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bl[ks], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bh[ks], acc, 0, 0, 0);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(acc[mt][i]));
+        // Lane l holds code elements mt*16 + 4*(l/16) + (0..3) of row l%16.
+        if (valid) {
+          uint2 o;
+          o.x = pk_bf16_rn(acc[0], acc[1]);
+          o.y = pk_bf16_rn(acc[2], acc[3]);
+          *reinterpret_cast<uint2*>(codes + (size_t)n * sh.dc + mt * 16 + lgrp * 4) = o;
+        }
       }
-    }
-    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-    const uint16_t sbits = f2bf(amax / 7.0f);
-    const float scale = bf2f(sbits);
-    uint8_t* qrow = (uint8_t*)a.codes + ((size_t)stream * sh.Nc + n) * (sh.dc / 2);
+    } else {
+      // 4-bit codes: the whole row first (up to D / 16 tiles), then its
+      // maximum magnitude over the row's lanes l, l ^ 16, l ^ 32, l ^ 48, the
+      // scale and the nibbles.
+      const int nmt = sh.dc / 16;
+      f32x4 acc[D / 16];
+      float amax = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt) {
-      if (mt < nmt && valid) {
-        const uint32_t q0 = (uint32_t)q4_quant(acc[mt][0], scale) & 15u, q1 = (uint32_t)q4_quant(acc[mt][1], scale) & 15u;
-        const uint32_t q2 = (uint32_t)q4_quant(acc[mt][2], scale) & 15u, q3 = (uint32_t)q4_quant(acc[mt][3], scale) & 15u;
-        *reinterpret_cast<uint16_t*>(qrow + mt * 8 + lgrp * 2) = (uint16_t)(q0 | (q1 << 4) | (q2 << 8) | (q3 << 12));
+      for (int mt = 0; mt < D / 16; ++mt) {
+        acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (mt < nmt) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 aw = *reinterpret_cast<const bf16x8*>(&w_lds[(mt * 16 + lrow) * LDW + ks * 32 + lgrp * 8]);
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bl[ks], acc[mt], 0, 0, 0);
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bh[ks], acc[mt], 0, 0, 0);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(acc[mt][i]));
+        }
       }
+      amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+      const uint16_t sbits = f2bf(amax / 7.0f);
+      const float scale = bf2f(sbits);
+      uint8_t* qrow = (uint8_t*)a.codes + ((size_t)stream * sh.Nc + n) * (sh.dc / 2);
+#pragma unroll
+      for (int mt = 0; mt < D / 16; ++mt) {
+        if (mt < nmt && valid) {
+          const uint32_t q0 = (uint32_t)q4_quant(acc[mt][0], scale) & 15u, q1 = (uint32_t)q4_quant(acc[mt][1], scale) & 15u;
+          const uint32_t q2 = (uint32_t)q4_quant(acc[mt][2], scale) & 15u, q3 = (uint32_t)q4_quant(acc[mt][3], scale) & 15u;
+          *reinterpret_cast<uint16_t*>(qrow + mt * 8 + lgrp * 2) = (uint16_t)(q0 | (q1 << 4) | (q2 << 8) | (q3 << 12));
+        }
+      }
+      if (valid && lgrp == 0) ((uint16_t*)a.scales)[(size_t)stream * sh.Nc + n] = sbits;
     }
-    if (valid && lgrp == 0) ((uint16_t*)a.scales)[(size_t)stream * sh.Nc + n] = sbits;
   }
 }
 
@@ -1176,7 +1217,7 @@ hipError_t launch_compress_d(const Shape& sh, const CompressArgs& a, hipStream_t
   const int rpb = 256 / (D / 8);   // references per k_center_refs block
   const dim3 g_mean(chunks, ns), g_ref((sh.R + rpb - 1) / rpb, ns);
   const dim3 g_search(xcd_grid(ns, (sh.T + kSearchTok - 1) / kSearchTok)), g_search32((sh.T + 255) / 256, ns);
-  const dim3 g_enc(xcd_grid(ns, (sh.N + 63) / 64)), g_enc32((sh.N + 255) / 256, ns);
+  const dim3 g_enc(xcd_grid(ns, (sh.N + 64 * kEncTiles - 1) / (64 * kEncTiles))), g_enc32((sh.N + 255) / 256, ns);
   void* const* ev = a.events;
   hipError_t e;
 #define DKV_TRY(x)                         \
