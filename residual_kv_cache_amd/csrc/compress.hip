@@ -89,37 +89,51 @@ __device__ __forceinline__ const typename S::T* stream_src(const CompressArgs& a
 
 // ---------------------------------------------------------------------------
 // Mean: stage 1, fp64 partial sums over kMeanChunk tokens.
-// grid (chunks, streams), block 256.
+// grid (chunks, streams), block 256: d/8 threads per token row, 16 bytes
+// each; kMeanRows rows per thread in flight at once (clamped to the chunk's
+// last row, the repeats adding nothing); the rows of a wave are summed by a
+// fixed butterfly, then the four waves in order.
 // ---------------------------------------------------------------------------
+
+constexpr int kMeanRows = 2;
 
 template <class S>
 __global__ __launch_bounds__(256) void k_mean_partial(CompressArgs a, Shape sh) {
-  __shared__ double red[256 / 8][128];
+  __shared__ double red[4][128];
   const int stream = blockIdx.y;
   const StreamId id = decode_stream(stream, sh.H);
   const typename S::T* src = stream_src<S>(a, id);
   const int tpr = sh.d / 8;           // threads per token row
   const int rows = 256 / tpr;         // rows per pass
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c0 = (tid % tpr) * 8;
   const int r0 = tid / tpr;
   const int t0 = blockIdx.x * kMeanChunk;
   const int t1 = min(sh.T, t0 + kMeanChunk);
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int t = t0 + r0; t < t1; t += rows) {
-    float x[8];
-    load8(src + (int64_t)t * a.st + c0, x);
+  for (int t = t0 + r0; t < t1; t += kMeanRows * rows) {
+    float x[kMeanRows][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += (double)x[e];
+    for (int u = 0; u < kMeanRows; ++u) load8(src + (int64_t)min(t + u * rows, t1 - 1) * a.st + c0, x[u]);
+#pragma unroll
+    for (int u = 0; u < kMeanRows; ++u) {
+      const bool in = t + u * rows < t1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += in ? (double)x[u][e] : 0.0;
+    }
   }
+  // Lanes tpr apart hold the same columns.
+  for (int o = tpr; o < 64; o <<= 1)
 #pragma unroll
-  for (int e = 0; e < 8; ++e) red[r0][c0 + e] = acc[e];
+    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
+  if (lane < tpr) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[wave][c0 + e] = acc[e];
+  }
   __syncthreads();
-  if (tid < sh.d) {
-    double s = 0.0;
-    for (int r = 0; r < rows; ++r) s += red[r][tid];
-    a.mean_part[((size_t)stream * gridDim.x + blockIdx.x) * sh.d + tid] = s;
-  }
+  if (tid < sh.d)
+    a.mean_part[((size_t)stream * gridDim.x + blockIdx.x) * sh.d + tid] =
+        ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
 }
 
 // Mean: stage 2, fixed-order total, divide, round once.  grid streams,
