@@ -105,8 +105,10 @@ __device__ const uint16_t kOnePair[8] __attribute__((aligned(16))) = {0x3F80u, 0
 
 // ---------------------------------------------------------------------------
 // refscore.  Block (bh, chunk) of 256 threads: S rows of kRsRefs references
-// (wave w: references chunk*64 + 16w + n16; A = q_g, B = reference rows, so
-// lane (n16, q4 = 0) ends with S[r][0..3]); wave 0 also computes q' outputs
+// (wave w: references chunk*64 + 16w + n16; A = q_g, B = reference rows read
+// from LDS, where the block's rows arrive by buffer loads straight into LDS,
+// one contiguous KB per wave instruction; lane (n16, q4 = 0) ends with
+// S[r][0..3]); wave 0 also computes q' outputs
 // 4 (chunk + chunks m), m = 0, 1, ...: four consecutive code columns of one
 // query head, lane l taking rows l and l + 64 of W_up (8 contiguous bytes
 // each), summed over the wave by a fixed butterfly.  The first group's
@@ -125,7 +127,6 @@ __global__ __launch_bounds__(256) void k_refscore_mfma(DecodeArgs a, Shape sh, i
   const uint16_t* q = (const uint16_t*)a.q + ((size_t)b * a.Hq + h * G) * kD;
 
   const int r = c * kRsRefs + wave * 16 + n16;
-  const uint32_t rr = (uint32_t)min(r, sh.R - 1);
   const uint16_t* refsK = (const uint16_t*)a.refs + (size_t)bh * 2 * sh.Rc * kD;
   // q' group of this block (wave 0): outputs o0 .. o0 + 3 (clamped when the
   // block has none; the stores are masked).
@@ -166,14 +167,38 @@ __global__ __launch_bounds__(256) void k_refscore_mfma(DecodeArgs a, Shape sh, i
   U32x2 w0[2];
   uint16_t q0[2];
   qp_loads(4 * c, w0, q0);
-  // The S part's loads are unconditional (query row clamped, heads past G
-  // zeroed after the loads), so all eight are in flight at once.
+  // The block's 64 reference rows go straight into LDS, each wave
+  // instruction one contiguous KB (rows past R read as zeros); piece p of row
+  // w lands at slot p ^ (w & 15), so the B-fragment reads below hit distinct
+  // banks.  The query rows come through registers.
+  __shared__ __attribute__((aligned(16))) uint16_t rl[kRsRefs * kD];
+  {
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(refsK + (size_t)c * kRsRefs * kD,
+                                                  (uint32_t)max(sh.R - c * kRsRefs, 0) * kD * 2u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int qi = (wave * 4 + j) * 64 + lane;   // 16-byte slot in LDS order
+      const int row = qi >> 4, slot = qi & 15;
+      const uint32_t voff = (uint32_t)(row * kD + ((slot ^ (row & 15)) << 3)) * 2u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(rl + (wave * 4 + j) * 512),
+                                               16, voff, 0, 0, 0);
+    }
+  }
   Frag aq[4], br[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const uint32_t col = ks * 32 + q4 * 8;
     aq[ks] = ldg<Frag>(q, ((uint32_t)min(n16, G - 1) * kD + col) * 2u);
-    br[ks] = ldg<Frag>(refsK, (rr * kD + col) * 2u);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the LDS rows have landed
+  __syncthreads();
+  {
+    const int row = wave * 16 + n16;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int piece = ks * 4 + q4;
+      br[ks] = *reinterpret_cast<const Frag*>(&rl[row * kD + ((piece ^ (row & 15)) << 3)]);
+    }
   }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
