@@ -629,9 +629,9 @@ __global__ __launch_bounds__(256) void k_search_f32(CompressArgs a, Shape sh) {
 // 31 - (place in the chunk), so equal scores within a chunk order by
 // ordinal; the perturbation is below 2^-18 of the key (cosine: keys are at
 // most 3 ||x~_t||) or of |score| (L2), inside the 1e-4 margin.  Key 0 is
-// "no candidate".  Per chunk a lane keeps a descending
-// list of its KT best keys: each tile's four keys are sorted by a network
-// and merged in with a bitonic step.  At the end of the chunk the list
+// "no candidate".  Per chunk a lane keeps a descending list of its KT best
+// keys: each tile's four keys are sorted by a network and merged in with a
+// bitonic step.  At the end of the chunk the list
 // joins the lane's running list of (key, ordinal) under the total order
 // "key above the place bits, then lower ordinal", by the same bitonic
 // merge; at the end the four lane groups of a token merge their lists the
