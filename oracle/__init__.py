@@ -6,6 +6,6 @@ from .deltakv_oracle import (  # noqa: F401
     cache_array_bytes, cache_bytes, dense_kv_bytes, decode_effective_bytes,
     shared_component, center, cosines, search, encode, compress_stream, compress, append_token,
     reconstruct_stream, attend, decode, decode_selected, quantize_q4, dequantize_q4, encode_exact,
-    search_topk, mean_refs, ref_count, ref_rows,
+    search_topk, mean_refs, ref_count, ref_rows, group_order, group_cache,
     ELEM_BYTES, ALIGN,
 )

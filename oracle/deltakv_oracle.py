@@ -43,6 +43,12 @@ seedable instance computed here is:
         references (by cosine, or by smallest ||x~_t - x~_r||), ties to the
         lower ordinal, all of them when fewer than k are earlier; O6 and O7
         use their mean in place of the single reference row
+  and one storage order of a compressed cache:
+    O13 grouped by value reference: the coded rows of a (sequence, KV head)
+        stored sorted by their V ordinal, rows of equal ordinal in position
+        order, the K and V rows of a token kept together (O8 sums over the
+        tokens, so every order of the rows gives the same attention; the
+        pages fix no storage order)
 
 ``rnd`` rounds to the storage dtype (nearest, ties to even).  Storage
 "f64" makes rnd the identity; the pins use it to test the mathematics
@@ -529,6 +535,33 @@ def attend(q, khat, vhat, scale) -> np.ndarray:
         sc = (khat[h] @ q[g]) * scale
         p = np.exp(sc - sc.max())
         out[g] = (p @ vhat[h]) / p.sum()
+    return out
+
+
+def group_order(idx_v) -> np.ndarray:
+    """O13: order[j] = the position row (0 .. N-1) that a grouped cache
+    stores in row j, for one (sequence, KV head) with V ordinals ``idx_v``
+    ([N], or [N][1] with one reference per row): rows sorted by V ordinal,
+    equal ordinals in position order (a stable sort)."""
+    v = np.asarray(idx_v, np.int64)
+    return np.argsort(v.reshape(len(v), -1)[:, 0], kind="stable")
+
+
+def group_cache(cache: dict) -> dict:
+    """O13 applied to a compressed layer cache (arrays [B][H][2][...] in
+    position order, as ``compress`` returns, top_k = 1): every per-row array
+    (ordinals, codes, 4-bit values and scales, margins) of each (b, h) is
+    reordered by group_order of that head's V ordinals, K and V alike; the
+    references and shared components do not move."""
+    B, H = cache["mu"].shape[:2]
+    rows = [n for n in ("idx", "codes", "q", "scales", "margin", "top1") if n in cache]
+    out = {n: np.array(a, copy=True) for n, a in cache.items()}
+    for b in range(B):
+        for h in range(H):
+            order = group_order(cache["idx"][b, h, 1])
+            for n in rows:
+                for kv in range(2):
+                    out[n][b, h, kv] = cache[n][b, h, kv][order]
     return out
 
 

@@ -53,6 +53,8 @@ PINS = [
     lambda: P.test_decode_effective_bytes_counts_the_arrays("bf16", 16, 3),
     P.test_decode_effective_bytes_llama8b_32k,
     lambda: P.test_topk_ordinal_bytes_count_the_arrays(4),
+    lambda: P.test_group_order_matches_counting_by_hand(0),
+    P.test_grouped_cache_keeps_tokens_and_decodes_the_same,
 ]
 
 
@@ -340,6 +342,45 @@ def _sb_one_ordinal(T, s, d, dc, storage, code_bits=16, top_k=1):
     return _ORIG_SB(T, s, d, dc, storage, code_bits, 1)
 
 
+def _group_reverse_ties(idx_v):
+    v = np.asarray(idx_v, np.int64)
+    return np.lexsort((-np.arange(len(v)), v))
+
+
+def _group_cache_by_key(cache):
+    out = {n: np.array(a, copy=True) for n, a in cache.items()}
+    for b in range(cache["mu"].shape[0]):
+        for h in range(cache["mu"].shape[1]):
+            order = OD.group_order(cache["idx"][b, h, 0])
+            for n in ("idx", "codes", "margin", "top1"):
+                if n in cache:
+                    for kv in range(2):
+                        out[n][b, h, kv] = cache[n][b, h, kv][order]
+    return out
+
+
+def _group_cache_each_half(cache):
+    out = {n: np.array(a, copy=True) for n, a in cache.items()}
+    for b in range(cache["mu"].shape[0]):
+        for h in range(cache["mu"].shape[1]):
+            for kv in range(2):
+                order = OD.group_order(cache["idx"][b, h, kv])
+                for n in ("idx", "codes", "margin", "top1"):
+                    if n in cache:
+                        out[n][b, h, kv] = cache[n][b, h, kv][order]
+    return out
+
+
+def _group_cache_codes_stay(cache):
+    out = {n: np.array(a, copy=True) for n, a in cache.items()}
+    for b in range(cache["mu"].shape[0]):
+        for h in range(cache["mu"].shape[1]):
+            order = OD.group_order(cache["idx"][b, h, 1])
+            for kv in range(2):
+                out["idx"][b, h, kv] = cache["idx"][b, h, kv][order]
+    return out
+
+
 MUTATIONS = {
     "search: also sees the next (later) reference": ("search", _search_factory(see_next=True)),
     "search: ties to highest ordinal": ("search", _search_factory(last_tie=True)),
@@ -385,6 +426,10 @@ MUTATIONS = {
     "decode bytes: one ordinal per row whatever k": ("decode_effective_bytes", _deb_one_ordinal),
     "array bytes: one ordinal per row whatever k": ("cache_array_bytes", _cab_one_ordinal),
     "stream bytes: one ordinal per row whatever k": ("stream_bytes", _sb_one_ordinal),
+    "grouping: equal ordinals in reverse position order": ("group_order", _group_reverse_ties),
+    "grouping: sorted by the K ordinal": ("group_cache", _group_cache_by_key),
+    "grouping: K and V halves sorted separately": ("group_cache", _group_cache_each_half),
+    "grouping: codes left in position order": ("group_cache", _group_cache_codes_stay),
 }
 
 

@@ -918,3 +918,49 @@ def test_topk_ordinal_bytes_count_the_arrays(top_k):
     assert sum(a.values()) == B * H * 2 * O.stream_bytes(T, s, d, dc, "f32", top_k=top_k)
     per_tok = (O.stream_bytes(32768, 16, 128, 32, "bf16", top_k=top_k) - 256) / 32768
     assert per_tok == 16 + 60 + top_k * 1.875
+
+
+# ---------------------------------------------------------------------------
+# O13: the cache grouped by value reference.
+# ---------------------------------------------------------------------------
+
+def _group_slots_by_hand(v):
+    """The row each position row takes in the grouped order, counted with
+    plain loops: the rows with a smaller V ordinal, plus the earlier rows
+    with the same one."""
+    v = [int(x) for x in v]
+    return [sum(1 for y in v if y < x) + sum(1 for m in range(n) if v[m] == x) for n, x in enumerate(v)]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_group_order_matches_counting_by_hand(seed):
+    assert O.group_order([2, 0, 2, 1, 0]).tolist() == [1, 4, 3, 0, 2]
+    rng = np.random.default_rng(40 + seed)
+    v = rng.integers(0, 5, size=37)
+    order = O.group_order(v)
+    slot = _group_slots_by_hand(v)
+    assert sorted(slot) == list(range(37))
+    for n in range(37):
+        assert order[slot[n]] == n
+
+
+def test_grouped_cache_keeps_tokens_and_decodes_the_same():
+    """The grouped cache holds the same tokens: V ordinals nondecreasing per
+    head, each row's K half (ordinal and code) from the same token as its V
+    half, and, since attention sums over the tokens, the same decode output
+    up to the order of the sums."""
+    k, v, w, cache, q = _small_cache()
+    T = k.shape[2]
+    g = O.group_cache(cache)
+    B, H = cache["mu"].shape[:2]
+    for b in range(B):
+        for h in range(H):
+            assert np.all(np.diff(g["idx"][b, h, 1]) >= 0)
+            slot = _group_slots_by_hand(cache["idx"][b, h, 1])
+            for n, j in enumerate(slot):
+                for kv in range(2):
+                    assert g["idx"][b, h, kv][j] == cache["idx"][b, h, kv][n]
+                    np.testing.assert_array_equal(g["codes"][b, h, kv][j], cache["codes"][b, h, kv][n])
+    np.testing.assert_array_equal(g["refs"], cache["refs"])
+    full = O.decode(cache, q, w, w, 3, T)
+    assert np.abs(O.decode(g, q, w, w, 3, T) - full).max() < 1e-12
