@@ -62,6 +62,11 @@ VARIANT_STEPS = 64
 TOPK_K = 4
 MALL_BYTES = 256 << 20
 HEADLINE = "llama8b_32k"
+# Storage order of the decode workloads' caches: code rows grouped by value
+# reference (the decode reads a shared value reference row once per run of
+# rows).  Selective decode looks rows up by position and takes caches in
+# position order; the headline also reports the position order as a variant.
+DECODE_ORDER = "value_ref"
 # Measured after the headline by the default run, each reported beside it.
 EXTRA_WORKLOADS = ("llama8b_131k", "llama8b_b16_32k", "prefill_32l_65k")
 
@@ -90,8 +95,8 @@ def sources_sha256(paths) -> str:
 def stored_traffic(cfg_name: str, splits: int):
     """HBM bytes per split-kernel launch from the committed counter summary
     (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None when the
-    summary is missing, was taken on another workload, or the kernel's
-    sources changed since."""
+    summary is missing, was taken on another workload or storage order, or
+    the kernel's sources changed since."""
     path = os.path.join(ROOT, TRAFFIC_FILE)
     if not os.path.exists(path):
         return None
@@ -102,7 +107,7 @@ def stored_traffic(cfg_name: str, splits: int):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
     if (kv.get("sources_sha256") != sources_sha256(SPLIT_SOURCES) or kv.get("workload") != cfg_name
-            or kv.get("splits") != str(splits)):
+            or kv.get("splits") != str(splits) or kv.get("order", "position") != DECODE_ORDER):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -285,7 +290,7 @@ def main():
                          "decode steps over the cache replicas; prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs the DeltaKV hot path on a single GPU (every "
+        print("bench.py measures one GPU only: the library runs the DeltaKV hot path on a single GPU (every "
               "(sequence, KV head) stream is independent, so more GPUs would each take their own share of "
               "sequences or heads). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
@@ -362,7 +367,8 @@ def decode_workload(cfg, args, np, torch, K, D, hip, extras: bool):
     tok_d = torch.from_numpy(sel_np).cuda()
     n_sel = sel_np.shape[1]
 
-    lay = D.make_layout(cfg.dtype, cfg.head_dim, cfg.code_dim, cfg.stride, cfg.n_kv_heads, cfg.batch, cfg.seq_len)
+    lay = D.make_layout(cfg.dtype, cfg.head_dim, cfg.code_dim, cfg.stride, cfg.n_kv_heads, cfg.batch, cfg.seq_len,
+                        order=DECODE_ORDER)
     cache_bytes = D.dkv_cache_bytes(lay)
     # Shapes the MFMA token-tile decode serves (bfloat16, d = 128, up to 4
     # query heads per KV head, code dim up to 48; token lists up to 32).
@@ -376,8 +382,13 @@ def decode_workload(cfg, args, np, torch, K, D, hip, extras: bool):
     outs = torch.empty((nsteps, cfg.batch, cfg.n_q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
 
     # Eager pass: fill every replica and keep reference outputs for steps 0 and 255.
-    for c in caches:
-        D.deltakv_compress(lay, k_d, v_d, wdk_d, wdv_d, c, ws_c)
+    # Stage events time each fill's kernels; their mean joins the timed runs'
+    # below, so the per-kernel figures average over every eager compress.
+    ev_fill = [hip.events(8) for _ in caches]
+    for c, ev in zip(caches, ev_fill):
+        D.deltakv_compress(lay, k_d, v_d, wdk_d, wdv_d, c, ws_c, stage_events=ev)
+    torch.cuda.synchronize()
+    fill_stage = [[hip.elapsed_ms(ev[2 * j], ev[2 * j + 1]) for j in range(4)] for ev in ev_fill]
     if args.profile:
         src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -387,11 +398,18 @@ def decode_workload(cfg, args, np, torch, K, D, hip, extras: bool):
         for i in range(args.steps):
             D.deltakv_decode_attn(lay, caches[i % nrep], q_d[i % nsteps], wuk_d, wuv_d, outs[i % nsteps], ws_d,
                                   n_splits=splits)
+        lay_p = D.make_layout(cfg.dtype, cfg.head_dim, cfg.code_dim, cfg.stride, cfg.n_kv_heads, cfg.batch,
+                              cfg.seq_len)
+        caches_p = [D.Cache(lay_p) for _ in range(nrep)]
+        ws_cp = D.workspace(D.dkv_compress_workspace_bytes(lay_p))
+        for c in caches_p:
+            D.deltakv_compress(lay_p, k_d, v_d, wdk_d, wdv_d, c, ws_cp)
         for i in range(SEL_STEPS):
-            D.deltakv_decode_attn_sel(lay, caches[i % nrep], q_d[i % nsteps], wuk_d, wuv_d, tok_d, outs[i % nsteps],
-                                      ws_d)
+            D.deltakv_decode_attn_sel(lay_p, caches_p[i % nrep], q_d[i % nsteps], wuk_d, wuv_d, tok_d,
+                                      outs[i % nsteps], ws_d)
+        del caches_p
         lay4 = D.make_layout(cfg.dtype, cfg.head_dim, cfg.code_dim, cfg.stride, cfg.n_kv_heads, cfg.batch,
-                             cfg.seq_len, code_bits=4)
+                             cfg.seq_len, code_bits=4, order=DECODE_ORDER)
         caches4 = [D.Cache(lay4) for _ in range(max(1, math.ceil(2 * MALL_BYTES / D.dkv_cache_bytes(lay4))))]
         ws_c4 = D.workspace(D.dkv_compress_workspace_bytes(lay4))
         for c4 in caches4:
@@ -483,19 +501,26 @@ def decode_workload(cfg, args, np, torch, K, D, hip, extras: bool):
         hip.sync(s_h)
         c_stage.append([hip.elapsed_ms(ev_c[2 * j], ev_c[2 * j + 1]) for j in range(4)])
         d_stage.extend([[hip.elapsed_ms(e[2 * j], e[2 * j + 1]) for j in range(3)] for e in ev_d])
-    c_stage = np.mean(np.array(c_stage), axis=0)
+    c_stage = np.mean(np.array(fill_stage + c_stage), axis=0)
     d_stage = np.array(d_stage)
 
     if extras:
         # Selective decode: every step attends over a quarter of the tokens, in
-        # random 64-token blocks (a block-sparse attention mask), over the cache
-        # replicas in turn; stage events time its three kernels.
+        # random 64-token blocks (a block-sparse attention mask), over replicas
+        # of the cache in position order (rows are looked up by position);
+        # stage events time its three kernels.
+        lay_p = D.make_layout(cfg.dtype, cfg.head_dim, cfg.code_dim, cfg.stride, cfg.n_kv_heads, cfg.batch,
+                              cfg.seq_len)
+        caches_p = [D.Cache(lay_p) for _ in range(nrep)]
+        ws_cp = D.workspace(D.dkv_compress_workspace_bytes(lay_p))
+        for c in caches_p:
+            D.deltakv_compress(lay_p, k_d, v_d, wdk_d, wdv_d, c, ws_cp)
         ev_s = [hip.events(6) for _ in range(SEL_STEPS)]
         s_stage = []
         for rep in range(2):
             for i in range(SEL_STEPS):
-                D.deltakv_decode_attn_sel(lay, caches[i % nrep], q_d[i % nsteps], wuk_d, wuv_d, tok_d, outs[i % nsteps],
-                                          ws_d, stream=s_h, stage_events=ev_s[i])
+                D.deltakv_decode_attn_sel(lay_p, caches_p[i % nrep], q_d[i % nsteps], wuk_d, wuv_d, tok_d,
+                                          outs[i % nsteps], ws_d, stream=s_h, stage_events=ev_s[i])
             hip.sync(s_h)
             s_stage.extend([[hip.elapsed_ms(e[2 * j], e[2 * j + 1]) for j in range(3)] + [hip.elapsed_ms(e[0], e[5])]
                             for e in ev_s])
@@ -505,8 +530,8 @@ def decode_workload(cfg, args, np, torch, K, D, hip, extras: bool):
         hip.begin_capture(s_h)
         try:
             for i in range(SEL_STEPS):
-                D.deltakv_decode_attn_sel(lay, caches[i % nrep], q_d[i % nsteps], wuk_d, wuv_d, tok_d, outs[i % nsteps],
-                                          ws_d, stream=s_h)
+                D.deltakv_decode_attn_sel(lay_p, caches_p[i % nrep], q_d[i % nsteps], wuk_d, wuv_d, tok_d,
+                                          outs[i % nsteps], ws_d, stream=s_h)
         finally:
             _, g_sel = hip.end_capture(s_h)
         hip.launch(g_sel, s_h)
@@ -522,7 +547,7 @@ def decode_workload(cfg, args, np, torch, K, D, hip, extras: bool):
         # selected coded token's K and V codes and ordinals, and each distinct V
         # reference row the selection uses, once.
         elem = 2 if cfg.dtype == "bf16" else 4
-        idx_np = caches[0].arrays()["idx"].cpu().numpy()
+        idx_np = caches_p[0].arrays()["idx"].cpu().numpy()
         idx_np = (idx_np.view(np.uint16) if idx_np.dtype == np.int16 else idx_np.view(np.uint32)).astype(np.int64)
         sel_bytes = 0
         for b in range(cfg.batch):
@@ -589,7 +614,8 @@ def decode_workload(cfg, args, np, torch, K, D, hip, extras: bool):
                                  "split": round(float(stage[:, 1].mean()) * 1e3, 3),
                                  "combine": round(float(stage[:, 2].mean()) * 1e3, 3)}}
 
-        int4 = variant(code_bits=4)
+        int4 = variant(code_bits=4, order=DECODE_ORDER)
+        position = variant(order="position")
         topk = variant(top_k=TOPK_K, metric="l2")
         topk["search_gflops_per_s"] = round(search_flops_per_stream(cfg) * cfg.batch * cfg.n_kv_heads * 2
                                             / (topk["compress_stage_ms"]["search"] * 1e-3) / 1e9, 1)
@@ -662,10 +688,10 @@ def decode_workload(cfg, args, np, torch, K, D, hip, extras: bool):
         "data": "synthetic (seeded generator: shared high-norm mean + Zipf-clustered tokens + noise; random "
                 "orthonormal W)",
         "config": {"workload": f"{cfg.name}: Llama-3-8B-shaped layer, compress {cfg.seq_len}-token prefill then "
-                               f"{nsteps} decode steps", "batch": cfg.batch, "n_kv_heads": cfg.n_kv_heads,
+                               f"{nsteps} decode steps (cache rows grouped by value reference)", "batch": cfg.batch, "n_kv_heads": cfg.n_kv_heads,
                    "n_q_heads": cfg.n_q_heads, "head_dim": cfg.head_dim, "seq_len": cfg.seq_len,
                    "stride": cfg.stride, "code_dim": cfg.code_dim, "decode_steps": nsteps, "splits": splits,
-                   "cache_replicas": nrep, "cache_mb": round(cache_bytes / 1e6, 2)},
+                   "cache_replicas": nrep, "cache_mb": round(cache_bytes / 1e6, 2), "order": DECODE_ORDER},
         "decode_tokens_per_s": round(cfg.batch * nsteps / (decode_window_ms * 1e-3), 1),
         "decode_us_per_step": round(decode_window_ms * 1e3 / nsteps, 3),
         "decode_hbm_frac": round(value / HBM_PEAK_GBS, 4),
@@ -704,6 +730,7 @@ def decode_workload(cfg, args, np, torch, K, D, hip, extras: bool):
                                    "frac": round(sel_bytes / (sel_split_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                                    "bytes_per_launch": int(sel_bytes), "launch_us": round(sel_split_us, 3)},
             "int4_codes": int4,
+            "position_order": position,
             "topk_l2": topk,
             "append_kernel_us_per_token": round(append_us, 3),
             "roofline_append": {"kernel": "k_append_search", "bound": "hbm",

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define DKV_ABI_VERSION 4u
+#define DKV_ABI_VERSION 5u
 
 typedef enum dkv_status {
   DKV_OK = 0,
@@ -114,6 +114,20 @@ typedef enum dkv_dtype {
  *                mean KV^R)
  *   metric       DKV_METRIC_COS (0): rank by cosine; DKV_METRIC_L2 (1): by
  *                smallest ||x~_t - refs[r]|| (the English page's L2 distance)
+ *   order        DKV_ORDER_POSITION (0): code rows in position order (see
+ *                dkv_cache); DKV_ORDER_BY_VALUE_REF (1): deltakv_compress
+ *                stores the coded tokens of each (sequence, KV head) grouped
+ *                by their value reference: the K and V rows (codes,
+ *                ordinals, scales) of the N coded tokens are ordered by
+ *                (V ordinal, position), so rows that share a value
+ *                reference row are adjacent and a decode reads that row
+ *                once per run instead of once per token.  Attention sums
+ *                over the cached tokens, so any order of the rows decodes to
+ *                the same result; the pages fix no storage order.  Requires
+ *                top_k <= 1 and R_cap <= 32768; selective decode (which looks
+ *                rows up by position) rejects such a cache.  Rows appended
+ *                after the compress stay in position order after the N
+ *                grouped rows.
  * Derived: R = ceil(T / s) references and N = T - R coded tokens per stream
  * are held; the arrays are laid out for R_cap = ceil(T_cap / s) and
  * N_cap = T_cap - R_cap (a cache's layout is fixed by T_cap, so a layout
@@ -133,10 +147,13 @@ typedef struct dkv_layout {
   uint32_t code_bits;
   uint32_t top_k;
   uint32_t metric;
+  uint32_t order;
 } dkv_layout;
 
 #define DKV_METRIC_COS 0u
 #define DKV_METRIC_L2 1u
+#define DKV_ORDER_POSITION 0u
+#define DKV_ORDER_BY_VALUE_REF 1u
 
 /*
  * Device pointers of a compressed cache.  All arrays are dense, row-major,
@@ -146,7 +163,10 @@ typedef struct dkv_layout {
  *   codes  [B][H][2][N_cap][d_c]  storage dtype: one row per non-reference
  *                                 token in position order; token t
  *                                 (t mod s != 0) sits in row
- *                                 t - floor(t / s) - 1 (rows 0 .. N-1 in use)
+ *                                 t - floor(t / s) - 1 (rows 0 .. N-1 in use;
+ *                                 with order = DKV_ORDER_BY_VALUE_REF rows
+ *                                 0 .. N-1 hold the same tokens grouped, see
+ *                                 dkv_layout)
  *                                 With code_bits = 4 a row is d_c / 2 bytes:
  *                                 element 2i in the low nibble of byte i,
  *                                 2i + 1 in the high nibble, two's complement
@@ -182,7 +202,8 @@ typedef struct dkv_cache {
  *              instead of computing the mean (NULL = compute)
  *   stage_events  optional host array of DKV_COMPRESS_EVENTS hipEvent_t
  *              handles (NULL = none): a (start, stop) pair per stage, in the
- *              order mean, center, search, encode.  Start is stamped when the
+ *              order mean, center, search, encode (with a grouped order the
+ *              encode stage begins with the grouping).  Start is stamped when the
  *              stage's first kernel starts executing and stop when its last
  *              kernel ends, so hipEventElapsedTime(start, stop) is the
  *              stage's device time.  Not allowed while `stream` is being
@@ -380,7 +401,9 @@ dkv_status deltakv_decode_attn_noalloc(const dkv_layout* layout, const dkv_cache
  * deltakv_decode_attn; in->n_splits = 0 takes
  * dkv_decode_sel_auto_splits, which never exceeds dkv_decode_auto_splits,
  * so a workspace of dkv_decode_workspace_bytes(layout, n_q_heads, 0) bytes
- * serves both calls.  stage_events as for deltakv_decode_attn.
+ * serves both calls.  stage_events as for deltakv_decode_attn.  A layout
+ * with order = DKV_ORDER_BY_VALUE_REF returns DKV_ERR_UNSUPPORTED (its rows
+ * are not found by position).
  */
 uint32_t dkv_decode_sel_auto_splits(const dkv_layout* layout, uint32_t n_q_heads, uint32_t n_sel);
 dkv_status deltakv_decode_attn_sel(const dkv_layout* layout, const dkv_cache* cache, const dkv_decode_in* in,

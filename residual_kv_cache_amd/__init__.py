@@ -17,7 +17,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdeltakv.so")
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 F32, BF16 = 0, 1
 STATUS = {0: "DKV_OK", 1: "DKV_ERR_NULL", 2: "DKV_ERR_SHAPE", 3: "DKV_ERR_DTYPE", 4: "DKV_ERR_ALIGN",
           5: "DKV_ERR_WORKSPACE", 6: "DKV_ERR_UNSUPPORTED", 7: "DKV_ERR_VERSION", 8: "DKV_ERR_DEVICE"}
@@ -37,7 +37,7 @@ class DeltaKVError(RuntimeError):
 class dkv_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint32) for n in ("abi_version", "dtype", "head_dim", "code_dim", "stride",
                                               "idx_bytes", "n_kv_heads", "batch", "seq_len", "capacity",
-                                              "code_bits", "top_k", "metric")]
+                                              "code_bits", "top_k", "metric", "order")]
 
     @property
     def n_refs(self) -> int:
@@ -142,20 +142,22 @@ def _check(status: int, what: str):
 # ---------------------------------------------------------------------------
 
 METRICS = {"cos": 0, "l2": 1}
+ORDERS = {"position": 0, "value_ref": 1}
 
 
 def make_layout(dtype: str, head_dim: int, code_dim: int, stride: int, n_kv_heads: int, batch: int,
                 seq_len: int, idx_bytes: int | None = None, capacity: int = 0, code_bits: int = 0, top_k: int = 1,
-                metric: str = "cos") -> dkv_layout:
+                metric: str = "cos", order: str = "position") -> dkv_layout:
     """capacity: tokens the cache arrays are sized for (0 = seq_len);
     code_bits: 0 = codes in the storage dtype, 4 = 4-bit codes with scales;
-    top_k: references per coded token; metric: "cos" or "l2"."""
+    top_k: references per coded token; metric: "cos" or "l2"; order:
+    "position" or "value_ref" (code rows grouped by value reference)."""
     cap = capacity or seq_len
     R = -(-cap // stride) if stride > 0 else 0
     if idx_bytes is None:
         idx_bytes = 2 if R <= 65536 else 4
     return dkv_layout(ABI_VERSION, {"f32": F32, "bf16": BF16}[dtype], head_dim, code_dim, stride, idx_bytes,
-                      n_kv_heads, batch, seq_len, capacity, code_bits, top_k, METRICS[metric])
+                      n_kv_heads, batch, seq_len, capacity, code_bits, top_k, METRICS[metric], ORDERS[order])
 
 
 def with_seq_len(layout: dkv_layout, seq_len: int) -> dkv_layout:
@@ -164,7 +166,7 @@ def with_seq_len(layout: dkv_layout, seq_len: int) -> dkv_layout:
     cap = layout.cap_tokens
     return dkv_layout(layout.abi_version, layout.dtype, layout.head_dim, layout.code_dim, layout.stride,
                       layout.idx_bytes, layout.n_kv_heads, layout.batch, seq_len, cap, layout.code_bits,
-                      layout.top_k, layout.metric)
+                      layout.top_k, layout.metric, layout.order)
 
 
 def dkv_layout_check(layout: dkv_layout) -> int:

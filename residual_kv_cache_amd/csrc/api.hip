@@ -30,7 +30,9 @@ dkv_status check_layout(const dkv_layout* L, Shape* out) {
   if (L->idx_bytes != 2 && L->idx_bytes != 4) return DKV_ERR_SHAPE;
   if (L->code_bits != 0 && L->code_bits != 4) return DKV_ERR_SHAPE;
   if (L->metric != DKV_METRIC_COS && L->metric != DKV_METRIC_L2) return DKV_ERR_SHAPE;
+  if (L->order != DKV_ORDER_POSITION && L->order != DKV_ORDER_BY_VALUE_REF) return DKV_ERR_SHAPE;
   if (L->top_k > 8) return DKV_ERR_UNSUPPORTED;
+  if (L->order == DKV_ORDER_BY_VALUE_REF && L->top_k > 1) return DKV_ERR_UNSUPPORTED;
   if (L->head_dim != 64 && L->head_dim != 128) return DKV_ERR_UNSUPPORTED;
   if (L->code_dim % 16 != 0) return DKV_ERR_UNSUPPORTED;
   // Strides up to 2^30 (one reference per 2^30 tokens) keep every
@@ -40,6 +42,7 @@ dkv_status check_layout(const dkv_layout* L, Shape* out) {
   const uint64_t R = ((uint64_t)L->seq_len + L->stride - 1) / L->stride;
   const uint64_t Rc = ((uint64_t)cap + L->stride - 1) / L->stride;
   if (L->idx_bytes == 2 && Rc > 65536) return DKV_ERR_UNSUPPORTED;
+  if (L->order == DKV_ORDER_BY_VALUE_REF && Rc > (uint64_t)dkv::kGroupMaxRefs) return DKV_ERR_UNSUPPORTED;
   const uint64_t streams = 2ull * L->batch * L->n_kv_heads;
   if (streams > 65535) return DKV_ERR_UNSUPPORTED;  // grid y limit of the stream axis
   if (out) {
@@ -58,6 +61,7 @@ dkv_status check_layout(const dkv_layout* L, Shape* out) {
     out->q4 = L->code_bits == 4;
     out->K = L->top_k ? (int)L->top_k : 1;
     out->l2 = L->metric == DKV_METRIC_L2;
+    out->grouped = L->order == DKV_ORDER_BY_VALUE_REF;
   }
   return DKV_OK;
 }
@@ -220,6 +224,19 @@ dkv_status deltakv_compress(const dkv_layout* layout, const dkv_compress_in* in,
   a.scales = sh.q4 ? cache->scales : nullptr;
   a.mean_part = (double*)((char*)ws + dkv::ws_mean_off(sh));
   a.inv_n = (float*)((char*)ws + dkv::ws_invn_off(sh));
+  a.idx_out = nullptr;
+  a.perm = nullptr;
+  a.gcnt = nullptr;
+  a.gtot = nullptr;
+  if (sh.grouped) {
+    // The search writes ordinals in position order to the workspace; the
+    // grouping places them (and the encode places the codes) in the cache.
+    a.idx_out = cache->idx;
+    a.idx = (char*)ws + dkv::ws_gidx_off(sh);
+    a.perm = (int*)((char*)ws + dkv::ws_perm_off(sh));
+    a.gcnt = (int*)((char*)ws + dkv::ws_gcnt_off(sh));
+    a.gtot = (int*)((char*)ws + dkv::ws_gtot_off(sh));
+  }
   a.events = in->stage_events;
   if ((st = check_events(a.events, stream)) != DKV_OK) return st;
   return from_hip(dkv::launch_compress(sh, a, (hipStream_t)stream));
@@ -420,6 +437,7 @@ dkv_status deltakv_decode_attn_sel(const dkv_layout* layout, const dkv_cache* ca
   Shape sh;
   const dkv_status lst = check_layout(layout, &sh);
   if (lst != DKV_OK) return lst;
+  if (sh.grouped) return DKV_ERR_UNSUPPORTED;
   const int G = in && in->n_q_heads && in->n_q_heads % sh.H == 0 ? (int)(in->n_q_heads / sh.H) : 1;
   dkv::DecodeArgs a;
   const dkv_status st =

@@ -1038,11 +1038,13 @@ __global__ __launch_bounds__(256) void k_encode_mfma(CompressArgs a, Shape sh) {
   const int K = sh.K;
   auto row_of = [&](int j) { return (xi.item * kEncTiles + j) * 64 + wave * 16 + lrow; };
   uint32_t r_nx;
+  int s_nx;   // row the code is stored in (the grouped row for grouped layouts)
   uint4 x_nx[KS];
   auto prefetch = [&](int j) {
     const int nc = min(row_of(j), sh.N - 1);
     const int tc = slot_to_pos(nc, sh.s);
     r_nx = load_idx(a.idx, ((size_t)stream * sh.Nc + nc) * K, sh.idx_bytes);
+    s_nx = a.perm ? a.perm[(size_t)(stream >> 1) * sh.Nc + nc] : nc;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       x_nx[ks] = *reinterpret_cast<const uint4*>(src + (int64_t)tc * a.st + ks * 32 + lgrp * 8);
@@ -1068,6 +1070,7 @@ __global__ __launch_bounds__(256) void k_encode_mfma(CompressArgs a, Shape sh) {
     const int cnt = min(K, t / sh.s + 1);
     const size_t ibase = ((size_t)stream * sh.Nc + nc) * K;
     const int r = min((int)r_nx, sh.R - 1);
+    const int slot = s_nx;
     uint4 xr[KS], rr[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -1122,7 +1125,7 @@ __global__ __launch_bounds__(256) void k_encode_mfma(CompressArgs a, Shape sh) {
           uint2 o;
           o.x = pk_bf16_rn(acc[0], acc[1]);
           o.y = pk_bf16_rn(acc[2], acc[3]);
-          *reinterpret_cast<uint2*>(codes + (size_t)n * sh.dc + mt * 16 + lgrp * 4) = o;
+          *reinterpret_cast<uint2*>(codes + (size_t)slot * sh.dc + mt * 16 + lgrp * 4) = o;
         }
       }
     } else {
@@ -1150,7 +1153,7 @@ __global__ __launch_bounds__(256) void k_encode_mfma(CompressArgs a, Shape sh) {
       amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
       const uint16_t sbits = f2bf(amax / 7.0f);
       const float scale = bf2f(sbits);
-      uint8_t* qrow = (uint8_t*)a.codes + ((size_t)stream * sh.Nc + n) * (sh.dc / 2);
+      uint8_t* qrow = (uint8_t*)a.codes + ((size_t)stream * sh.Nc + slot) * (sh.dc / 2);
 #pragma unroll
       for (int mt = 0; mt < D / 16; ++mt) {
         if (mt < nmt && valid) {
@@ -1159,7 +1162,7 @@ __global__ __launch_bounds__(256) void k_encode_mfma(CompressArgs a, Shape sh) {
           *reinterpret_cast<uint16_t*>(qrow + mt * 8 + lgrp * 2) = (uint16_t)(q0 | (q1 << 4) | (q2 << 8) | (q3 << 12));
         }
       }
-      if (valid && lgrp == 0) ((uint16_t*)a.scales)[(size_t)stream * sh.Nc + n] = sbits;
+      if (valid && lgrp == 0) ((uint16_t*)a.scales)[(size_t)stream * sh.Nc + slot] = sbits;
     }
   }
 }
@@ -1180,6 +1183,7 @@ __global__ __launch_bounds__(256) void k_encode_f32(CompressArgs a, Shape sh) {
   const int K = sh.K;
   const int cnt = min(K, t / sh.s + 1);
   const size_t ibase = ((size_t)stream * sh.Nc + n) * K;
+  const int slot = a.perm ? a.perm[(size_t)(stream >> 1) * sh.Nc + n] : n;   // row the code is stored in
   float dl[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) dl[i] = 0.f;
@@ -1192,7 +1196,7 @@ __global__ __launch_bounds__(256) void k_encode_f32(CompressArgs a, Shape sh) {
 #pragma unroll
   for (int i = 0; i < D; ++i) dl[i] = (src[(int64_t)t * a.st + i] - mu[i]) - (cnt > 1 ? dl[i] * inv : dl[i]);
   if (!sh.q4) {
-    float* codes = (float*)a.codes + ((size_t)stream * sh.Nc + n) * sh.dc;
+    float* codes = (float*)a.codes + ((size_t)stream * sh.Nc + slot) * sh.dc;
     for (int j = 0; j < sh.dc; ++j) {
       float c = 0.f;
 #pragma unroll
@@ -1211,7 +1215,7 @@ __global__ __launch_bounds__(256) void k_encode_f32(CompressArgs a, Shape sh) {
     amax = fmaxf(amax, fabsf(c));
   }
   const float scale = amax / 7.0f;
-  uint8_t* qrow = (uint8_t*)a.codes + ((size_t)stream * sh.Nc + n) * (sh.dc / 2);
+  uint8_t* qrow = (uint8_t*)a.codes + ((size_t)stream * sh.Nc + slot) * (sh.dc / 2);
   for (int j = 0; j < sh.dc; j += 2) {
     float c0 = 0.f, c1 = 0.f;
 #pragma unroll
@@ -1221,7 +1225,171 @@ __global__ __launch_bounds__(256) void k_encode_f32(CompressArgs a, Shape sh) {
     }
     qrow[j / 2] = (uint8_t)(((uint32_t)q4_quant(c0, scale) & 15u) | (((uint32_t)q4_quant(c1, scale) & 15u) << 4));
   }
-  ((float*)a.scales)[(size_t)stream * sh.Nc + n] = scale;
+  ((float*)a.scales)[(size_t)stream * sh.Nc + slot] = scale;
+}
+
+// ---------------------------------------------------------------------------
+// Grouping by value reference (layouts with order = by value reference).
+// The coded rows of head (b, h) are put in the order of (V ordinal,
+// position): a counting sort, stable in position, over pieces of
+// kGroupPiece position rows.  k_group_count counts each piece's V ordinals;
+// k_group_scan gives each piece the count of every ordinal in the pieces
+// before it, and the total per ordinal; k_group_place sorts the piece's
+// (ordinal, row) keys, gives each row its grouped slot (the rows of all
+// lower ordinals, then this ordinal's rows in earlier pieces, then its rank
+// among the piece's rows of that ordinal) and moves the K and V ordinals
+// there.  Integer work only: the order is deterministic.
+// ---------------------------------------------------------------------------
+
+// grid (pieces, B*H), block kGroupThreads, dynamic LDS R * 4 bytes.
+__global__ __launch_bounds__(kGroupThreads) void k_group_count(CompressArgs a, Shape sh) {
+  extern __shared__ int cnt[];
+  const int head = blockIdx.y, p = blockIdx.x;
+  const int n0 = p * kGroupPiece, len = min(kGroupPiece, sh.N - n0);
+  for (int r = threadIdx.x; r < sh.R; r += kGroupThreads) cnt[r] = 0;
+  __syncthreads();
+  const size_t vbase = (size_t)(2 * head + 1) * sh.Nc + n0;
+  for (int i = threadIdx.x; i < len; i += kGroupThreads)
+    atomicAdd(&cnt[min((int)load_idx(a.idx, vbase + i, sh.idx_bytes), sh.R - 1)], 1);
+  __syncthreads();
+  int* out = a.gcnt + ((size_t)head * gridDim.x + p) * sh.R;
+  for (int r = threadIdx.x; r < sh.R; r += kGroupThreads) out[r] = cnt[r];
+}
+
+// grid (ceil(R / 256), B*H), block 256: thread r walks the pieces, 16 loads
+// in flight at a time, leaving each piece's exclusive prefix and the total.
+__global__ __launch_bounds__(256) void k_group_scan(CompressArgs a, Shape sh, int P) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= sh.R) return;
+  const int head = blockIdx.y;
+  int* c = a.gcnt + (size_t)head * P * sh.R + r;
+  int run = 0;
+  for (int p0 = 0; p0 < P; p0 += 16) {
+    int v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = p0 + u < P ? c[(size_t)(p0 + u) * sh.R] : 0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      if (p0 + u < P) {
+        c[(size_t)(p0 + u) * sh.R] = run;
+        run += v[u];
+      }
+    }
+  }
+  a.gtot[(size_t)head * sh.R + r] = run;
+}
+
+// Bitonic compare-exchange from one element's side: it keeps the smaller
+// key when it is the lower index of the pair in an ascending run (or the
+// upper index in a descending one), else the larger.
+__device__ __forceinline__ uint32_t bitonic_keep(uint32_t x, uint32_t y, int i, int l, int kk) {
+  const bool keep_min = (i < l) == ((i & kk) == 0);
+  return keep_min ? min(x, y) : max(x, y);
+}
+
+// grid (pieces, B*H), block kGroupThreads, dynamic LDS R * 4 bytes (the first
+// grouped row of each ordinal).
+__global__ __launch_bounds__(kGroupThreads) void k_group_place(CompressArgs a, Shape sh) {
+  __shared__ uint32_t key[kGroupPiece];   // (V ordinal << 12) | row in piece
+  __shared__ int wsum[kGroupThreads / 64];
+  extern __shared__ int off[];
+  static_assert(kGroupPiece == 4 * kGroupThreads && kGroupPiece <= 4096, "4 keys a thread; 12-bit row field");
+  const int head = blockIdx.y, p = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n0 = p * kGroupPiece, len = min(kGroupPiece, sh.N - n0);
+  const size_t kstream = (size_t)(2 * head) * sh.Nc, vstream = kstream + sh.Nc;
+  // Thread t holds keys 4t .. 4t + 3 (past the piece: all ones, sorted last).
+  uint32_t k[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = 4 * tid + e;
+    k[e] = i < len ? ((uint32_t)min((int)load_idx(a.idx, vstream + n0 + i, sh.idx_bytes), sh.R - 1) << 12) |
+                         (uint32_t)i
+                   : 0xFFFFFFFFu;
+  }
+  // Rows per ordinal -> exclusive prefix (the grouped row of the ordinal's
+  // first row): thread t scans a contiguous segment, then the segment sums
+  // are scanned over the wave and the 16 waves.
+  const int* tot = a.gtot + (size_t)head * sh.R;
+  for (int r = tid; r < sh.R; r += kGroupThreads) off[r] = tot[r];
+  __syncthreads();
+  const int seg = (sh.R + kGroupThreads - 1) / kGroupThreads;
+  const int r0 = min(tid * seg, sh.R), r1 = min(r0 + seg, sh.R);
+  int sum = 0;
+  for (int r = r0; r < r1; ++r) sum += off[r];
+  int x = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  int run = x - sum;
+  for (int i = 0; i < w; ++i) run += wsum[i];
+  for (int r = r0; r < r1; ++r) {
+    const int v = off[r];
+    off[r] = run;
+    run += v;
+  }
+  // Bitonic sort, ascending: partners 1 and 2 apart are in the thread's own
+  // registers, 4 .. 128 apart in the same wave (shuffles), 256 and more
+  // apart in other waves (through LDS).
+  // From 4 apart on, a thread's four keys share their role (bits j and kk
+  // of 4t + e do not depend on e), decided once per step.
+  for (int kk = 2; kk <= kGroupPiece; kk <<= 1) {
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      if (j >= 256) {
+        const bool keep_min = ((4 * tid) & j) == 0 ? ((4 * tid) & kk) == 0 : ((4 * tid) & kk) != 0;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) key[4 * tid + e] = k[e];
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t y = key[(4 * tid + e) ^ j];
+          k[e] = keep_min ? min(k[e], y) : max(k[e], y);
+        }
+      } else if (j >= 4) {
+        const bool keep_min = ((4 * tid) & j) == 0 ? ((4 * tid) & kk) == 0 : ((4 * tid) & kk) != 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t y = (uint32_t)__shfl_xor((int)k[e], j >> 2, 64);
+          k[e] = keep_min ? min(k[e], y) : max(k[e], y);
+        }
+      } else {
+        uint32_t t[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t[e] = bitonic_keep(k[e], k[e ^ j], 4 * tid + e, 4 * tid + (e ^ j), kk);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) k[e] = t[e];
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 4; ++e) key[4 * tid + e] = k[e];
+  __syncthreads();
+  // Sorted entry i: its rank among the piece's rows of the same ordinal is
+  // i minus the ordinal's first sorted entry.
+  const int* before = a.gcnt + ((size_t)head * gridDim.x + p) * sh.R;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = 4 * tid + e;
+    if (i < len) {
+      const uint32_t o = k[e] >> 12;
+      const int row = (int)(k[e] & 4095u);
+      int lo = 0, hi = i;
+      while (lo < hi) {
+        const int m = (lo + hi) >> 1;
+        if ((key[m] >> 12) < o) lo = m + 1;
+        else hi = m;
+      }
+      const int slot = off[o] + before[o] + (i - lo);
+      a.perm[(size_t)head * sh.Nc + n0 + row] = slot;
+      store_idx(a.idx_out, kstream + slot, sh.idx_bytes, load_idx(a.idx, kstream + n0 + row, sh.idx_bytes));
+      store_idx(a.idx_out, vstream + slot, sh.idx_bytes, o);
+    }
+  }
 }
 
 template <int D>
@@ -1238,6 +1406,18 @@ hipError_t launch_compress_d(const Shape& sh, const CompressArgs& a, hipStream_t
   do {                                     \
     if ((e = (x)) != hipSuccess) return e; \
   } while (0)
+  // Grouped layouts: count, scan and place between the search and the
+  // encode (timed as the start of the encode stage).
+  const int heads = sh.B * sh.H, pieces = group_pieces(sh);
+  auto group = [&]() -> hipError_t {
+    DKV_TRY(launch_lds(k_group_count, dim3(pieces, heads), kGroupThreads, (size_t)sh.R * 4, st, ev_start(ev, 3),
+                       nullptr, a, sh));
+    DKV_TRY(launch(k_group_scan, dim3((sh.R + 255) / 256, heads), 256, st, nullptr, nullptr, a, sh, pieces));
+    DKV_TRY(launch_lds(k_group_place, dim3(pieces, heads), kGroupThreads, (size_t)sh.R * 4, st, nullptr, nullptr, a, sh));
+    return hipSuccess;
+  };
+  hipEvent_t enc_start = ev_start(ev, 3);
+  if (sh.grouped) enc_start = nullptr;
   if (sh.bf16) {
     DKV_TRY(launch(k_mean_partial<BF16>, g_mean, 256, st, ev_start(ev, 0), nullptr, a, sh));
     DKV_TRY(launch(k_mean_final<BF16>, ns, 256, st, nullptr, ev_stop(ev, 0), a, sh, chunks));
@@ -1253,11 +1433,12 @@ hipError_t launch_compress_d(const Shape& sh, const CompressArgs& a, hipStream_t
       } else {
         DKV_TRY(launch(k_search_mfma<D>, g_search, kSearchThreads, st, ev_start(ev, 2), ev_stop(ev, 2), a, sh));
       }
+      if (sh.grouped) DKV_TRY(group());
       if (sh.q4) {
-        DKV_TRY(launch_lds(k_encode_mfma<D, true>, g_enc, 256, (size_t)sh.dc * (D + 8) * 2, st, ev_start(ev, 3),
+        DKV_TRY(launch_lds(k_encode_mfma<D, true>, g_enc, 256, (size_t)sh.dc * (D + 8) * 2, st, enc_start,
                            ev_stop(ev, 3), a, sh));
       } else {
-        DKV_TRY(launch_lds(k_encode_mfma<D, false>, g_enc, 256, (size_t)sh.dc * (D + 8) * 2, st, ev_start(ev, 3),
+        DKV_TRY(launch_lds(k_encode_mfma<D, false>, g_enc, 256, (size_t)sh.dc * (D + 8) * 2, st, enc_start,
                            ev_stop(ev, 3), a, sh));
       }
     }
@@ -1272,7 +1453,8 @@ hipError_t launch_compress_d(const Shape& sh, const CompressArgs& a, hipStream_t
       } else {
         DKV_TRY(launch(k_search_f32<D>, g_search32, 256, st, ev_start(ev, 2), ev_stop(ev, 2), a, sh));
       }
-      DKV_TRY(launch(k_encode_f32<D>, g_enc32, 256, st, ev_start(ev, 3), ev_stop(ev, 3), a, sh));
+      if (sh.grouped) DKV_TRY(group());
+      DKV_TRY(launch(k_encode_f32<D>, g_enc32, 256, st, enc_start, ev_stop(ev, 3), a, sh));
     }
   }
   if (sh.N == 0 && ev) {

@@ -27,6 +27,7 @@ struct Shape {
   int q4;       // 1 = 4-bit codes with one scale per row
   int K;        // references per coded token (top_k)
   int l2;       // 1 = references ranked by L2 distance, 0 = by cosine
+  int grouped;  // 1 = coded rows of a head grouped by value reference
   // The fast paths (top-1 cosine search; token-tile decode) serve K = 1.
   __host__ __device__ bool topk_search() const { return K > 1 || l2; }
   __host__ __device__ int n_streams() const { return B * H * 2; }
@@ -66,7 +67,26 @@ inline size_t ws_mean_bytes(const Shape& sh) {
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline size_t ws_invn_off(const Shape& sh) { return align_up(ws_mean_bytes(sh), 256); }
 inline size_t ws_invn_bytes(const Shape& sh) { return (size_t)sh.n_streams() * sh.R * sizeof(float); }
-inline size_t compress_ws_bytes(const Shape& sh) { return align_up(ws_invn_off(sh) + ws_invn_bytes(sh), 256); }
+// Grouped layouts add: the ordinals in position order (written by the
+// search, read by the grouping and the encode), the grouped row of each
+// position row per head, and the per-piece reference counts per head.
+constexpr int kGroupPiece = 2048;    // coded rows per grouping block
+constexpr int kGroupThreads = kGroupPiece / 4;   // threads of a grouping block (4 rows each)
+constexpr int kGroupMaxRefs = 32768; // LDS counters of one grouping block
+inline int group_pieces(const Shape& sh) { return (sh.N + kGroupPiece - 1) / kGroupPiece; }
+inline size_t ws_gidx_off(const Shape& sh) { return align_up(ws_invn_off(sh) + ws_invn_bytes(sh), 256); }
+inline size_t ws_gidx_bytes(const Shape& sh) {
+  return sh.grouped ? (size_t)sh.n_streams() * sh.Nc * sh.idx_bytes : 0;
+}
+inline size_t ws_perm_off(const Shape& sh) { return align_up(ws_gidx_off(sh) + ws_gidx_bytes(sh), 256); }
+inline size_t ws_perm_bytes(const Shape& sh) { return sh.grouped ? (size_t)sh.B * sh.H * sh.Nc * 4 : 0; }
+inline size_t ws_gcnt_off(const Shape& sh) { return align_up(ws_perm_off(sh) + ws_perm_bytes(sh), 256); }
+inline size_t ws_gcnt_bytes(const Shape& sh) {
+  return sh.grouped ? (size_t)sh.B * sh.H * ((sh.Nc + kGroupPiece - 1) / kGroupPiece) * sh.Rc * 4 : 0;
+}
+inline size_t ws_gtot_off(const Shape& sh) { return align_up(ws_gcnt_off(sh) + ws_gcnt_bytes(sh), 256); }
+inline size_t ws_gtot_bytes(const Shape& sh) { return sh.grouped ? (size_t)sh.B * sh.H * sh.Rc * 4 : 0; }
+inline size_t compress_ws_bytes(const Shape& sh) { return align_up(ws_gtot_off(sh) + ws_gtot_bytes(sh), 256); }
 
 // Decode workspace: reference scores S [B][H][R][Gs] (Gs = G rounded up to
 // a multiple of 4, padding zero), projected queries q' [B][H][G][dc] and
@@ -111,6 +131,15 @@ struct CompressArgs {
   void* scales;              // 4-bit codes: per-row scales, else NULL
   double* mean_part;
   float* inv_n;
+  // Grouped layouts (else NULL): idx above is the position-order workspace
+  // copy; idx_out is the cache's array, perm the grouped row of each
+  // position row [B*H][N_cap], gcnt the per-piece counts [B*H][pieces][R]
+  // (then each piece's count of the ordinal in earlier pieces), gtot the
+  // rows per ordinal [B*H][R].
+  void* idx_out;
+  int* perm;
+  int* gcnt;
+  int* gtot;
   void* const* events;       // DKV_COMPRESS_EVENTS hipEvent_t or NULL
 };
 

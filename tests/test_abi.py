@@ -32,7 +32,7 @@ def test_header_declarations_are_exported():
 
 def test_abi_version_and_status_strings():
     lib = _lib()
-    assert lib.dkv_abi_version() == D.ABI_VERSION == 4
+    assert lib.dkv_abi_version() == D.ABI_VERSION == 5
     for code, name in D.STATUS.items():
         assert lib.dkv_status_str(code).decode().startswith(name)
 
@@ -392,3 +392,39 @@ def test_noalloc_decode_rejects_oversized_shapes_before_the_device():
     assert st == 5   # DKV_ERR_WORKSPACE
     lay.abi_version = 1
     assert D.lib().deltakv_decode_attn_noalloc(ctypes.byref(lay), ctypes.byref(cache), ctypes.byref(a), None) == 7
+
+
+def test_grouped_order_layout_checks():
+    """order: 0 (position) or 1 (grouped by value reference); grouping keeps
+    one ordinal per row and at most 32768 reference rows; the cache bytes do
+    not change, the compress workspace grows by the grouping's arrays."""
+    _lib()
+    g = L(order="value_ref")
+    assert g.order == 1 and D.dkv_layout_check(g) == 0
+    assert D.dkv_cache_bytes(g) == D.dkv_cache_bytes(L())
+    lay = L()
+    lay.order = 2
+    assert D.dkv_layout_check(lay) == 2
+    assert D.dkv_layout_check(L(order="value_ref", top_k=2)) == 6
+    assert D.dkv_layout_check(L(order="value_ref", top_k=1, metric="l2")) == 0
+    assert D.dkv_layout_check(L(order="value_ref", seq_len=32768 * 16)) == 0
+    assert D.dkv_layout_check(L(order="value_ref", seq_len=32768 * 16 + 1)) == 6
+    assert D.dkv_layout_check(L(order="value_ref", seq_len=1000, capacity=32768 * 16 + 1)) == 6
+    # Grouping arrays: position-order ordinals, the grouped row of each row
+    # per head, the per-piece counts (pieces of 2048 rows) and the rows per
+    # ordinal.
+    T, s, H = 32768, 16, 8
+    R = T // s
+    N = T - R
+    pieces = -(-N // 2048)
+    extra = 2 * H * N * 2 + H * N * 4 + H * pieces * R * 4 + H * R * 4
+    grow = D.dkv_compress_workspace_bytes(g) - D.dkv_compress_workspace_bytes(L())
+    assert extra <= grow <= extra + 4 * 256
+    assert D.with_seq_len(L(order="value_ref", capacity=40000), 33000).order == 1
+
+
+def test_grouped_layout_rejects_selective_decode():
+    _lib()
+    _no_device()
+    P = 1 << 30
+    assert _sel_status(L(order="value_ref"), D.dkv_token_sel(P, 8, 0), FakeCache(P)) == 6
