@@ -1288,31 +1288,43 @@ __device__ __forceinline__ uint32_t bitonic_keep(uint32_t x, uint32_t y, int i, 
 }
 
 // grid (pieces, B*H), block kGroupThreads, dynamic LDS R * 4 bytes (the first
-// grouped row of each ordinal).
+// grouped row of each ordinal).  Every global load is unconditional (clamped
+// indices, masked afterwards) and issued in batches, so the kernel waits on
+// few memory round trips.
+template <typename IdxT>
 __global__ __launch_bounds__(kGroupThreads) void k_group_place(CompressArgs a, Shape sh) {
   __shared__ uint32_t key[kGroupPiece];   // (V ordinal << 12) | row in piece
   __shared__ int wsum[kGroupThreads / 64];
   extern __shared__ int off[];
   static_assert(kGroupPiece == 4 * kGroupThreads && kGroupPiece <= 4096, "4 keys a thread; 12-bit row field");
+  constexpr int T = kGroupThreads;
   const int head = blockIdx.y, p = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n0 = p * kGroupPiece, len = min(kGroupPiece, sh.N - n0);
-  const size_t kstream = (size_t)(2 * head) * sh.Nc, vstream = kstream + sh.Nc;
+  const IdxT* kin = (const IdxT*)a.idx + (size_t)(2 * head) * sh.Nc + n0;
+  const IdxT* vin = kin + sh.Nc;
   // Thread t holds keys 4t .. 4t + 3 (past the piece: all ones, sorted last).
   uint32_t k[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int i = 4 * tid + e;
-    k[e] = i < len ? ((uint32_t)min((int)load_idx(a.idx, vstream + n0 + i, sh.idx_bytes), sh.R - 1) << 12) |
-                         (uint32_t)i
-                   : 0xFFFFFFFFu;
-  }
+  for (int e = 0; e < 4; ++e) k[e] = (uint32_t)vin[min(4 * tid + e, len - 1)];
   // Rows per ordinal -> exclusive prefix (the grouped row of the ordinal's
   // first row): thread t scans a contiguous segment, then the segment sums
-  // are scanned over the wave and the 16 waves.
+  // are scanned over the wave and over the waves.
   const int* tot = a.gtot + (size_t)head * sh.R;
-  for (int r = tid; r < sh.R; r += kGroupThreads) off[r] = tot[r];
+  for (int r0 = tid; r0 < sh.R; r0 += 8 * T) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = tot[min(r0 + u * T, sh.R - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (r0 + u * T < sh.R) off[r0 + u * T] = v[u];
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = 4 * tid + e;
+    k[e] = i < len ? (min(k[e], (uint32_t)sh.R - 1u) << 12) | (uint32_t)i : 0xFFFFFFFFu;
+  }
   __syncthreads();
-  const int seg = (sh.R + kGroupThreads - 1) / kGroupThreads;
+  const int seg = (sh.R + T - 1) / T;
   const int r0 = min(tid * seg, sh.R), r1 = min(r0 + seg, sh.R);
   int sum = 0;
   for (int r = r0; r < r1; ++r) sum += off[r];
@@ -1333,9 +1345,8 @@ __global__ __launch_bounds__(kGroupThreads) void k_group_place(CompressArgs a, S
   }
   // Bitonic sort, ascending: partners 1 and 2 apart are in the thread's own
   // registers, 4 .. 128 apart in the same wave (shuffles), 256 and more
-  // apart in other waves (through LDS).
-  // From 4 apart on, a thread's four keys share their role (bits j and kk
-  // of 4t + e do not depend on e), decided once per step.
+  // apart in other waves (through LDS).  From 4 apart on, a thread's four
+  // keys share their role (bits j and kk of 4t + e do not depend on e).
   for (int kk = 2; kk <= kGroupPiece; kk <<= 1) {
     for (int j = kk >> 1; j > 0; j >>= 1) {
       if (j >= 256) {
@@ -1370,24 +1381,42 @@ __global__ __launch_bounds__(kGroupThreads) void k_group_place(CompressArgs a, S
   for (int e = 0; e < 4; ++e) key[4 * tid + e] = k[e];
   __syncthreads();
   // Sorted entry i: its rank among the piece's rows of the same ordinal is
-  // i minus the ordinal's first sorted entry.
+  // i minus the ordinal's first sorted entry (binary search).  The searches
+  // run first, then every load, then the stores.
   const int* before = a.gcnt + ((size_t)head * gridDim.x + p) * sh.R;
+  int first[4];
+  uint32_t o[4];
+  int row[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = 4 * tid + e;
+    o[e] = min(k[e] >> 12, (uint32_t)sh.R - 1u);
+    row[e] = (int)(k[e] & 4095u);
+    int lo = 0, hi = min(i, len);
+    while (lo < hi) {
+      const int m = (lo + hi) >> 1;
+      if ((key[m] >> 12) < o[e]) lo = m + 1;
+      else hi = m;
+    }
+    first[e] = lo;
+  }
+  int bef[4];
+  IdxT kord[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    bef[e] = before[o[e]];
+    kord[e] = kin[min(row[e], len - 1)];
+  }
+  IdxT* kout = (IdxT*)a.idx_out + (size_t)(2 * head) * sh.Nc;
+  IdxT* vout = kout + sh.Nc;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int i = 4 * tid + e;
     if (i < len) {
-      const uint32_t o = k[e] >> 12;
-      const int row = (int)(k[e] & 4095u);
-      int lo = 0, hi = i;
-      while (lo < hi) {
-        const int m = (lo + hi) >> 1;
-        if ((key[m] >> 12) < o) lo = m + 1;
-        else hi = m;
-      }
-      const int slot = off[o] + before[o] + (i - lo);
-      a.perm[(size_t)head * sh.Nc + n0 + row] = slot;
-      store_idx(a.idx_out, kstream + slot, sh.idx_bytes, load_idx(a.idx, kstream + n0 + row, sh.idx_bytes));
-      store_idx(a.idx_out, vstream + slot, sh.idx_bytes, o);
+      const int slot = off[o[e]] + bef[e] + (i - first[e]);
+      a.perm[(size_t)head * sh.Nc + n0 + row[e]] = slot;
+      kout[slot] = kord[e];
+      vout[slot] = (IdxT)o[e];
     }
   }
 }
@@ -1413,7 +1442,8 @@ hipError_t launch_compress_d(const Shape& sh, const CompressArgs& a, hipStream_t
     DKV_TRY(launch_lds(k_group_count, dim3(pieces, heads), kGroupThreads, (size_t)sh.R * 4, st, ev_start(ev, 3),
                        nullptr, a, sh));
     DKV_TRY(launch(k_group_scan, dim3((sh.R + 255) / 256, heads), 256, st, nullptr, nullptr, a, sh, pieces));
-    DKV_TRY(launch_lds(k_group_place, dim3(pieces, heads), kGroupThreads, (size_t)sh.R * 4, st, nullptr, nullptr, a, sh));
+    DKV_TRY(launch_lds(sh.idx_bytes == 2 ? k_group_place<uint16_t> : k_group_place<uint32_t>, dim3(pieces, heads),
+                       kGroupThreads, (size_t)sh.R * 4, st, nullptr, nullptr, a, sh));
     return hipSuccess;
   };
   hipEvent_t enc_start = ev_start(ev, 3);
