@@ -382,8 +382,9 @@ def decode_workload(cfg, args, np, torch, K, D, hip, extras: bool):
     outs = torch.empty((nsteps, cfg.batch, cfg.n_q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
 
     # Eager pass: fill every replica and keep reference outputs for steps 0 and 255.
-    # Stage events time each fill's kernels; their mean joins the timed runs'
-    # below, so the per-kernel figures average over every eager compress.
+    # Stage events time each fill's kernels; with the timed runs below they
+    # give each compress stage's median over every eager compress (a search
+    # varies by a few percent from launch to launch with the clocks).
     ev_fill = [hip.events(8) for _ in caches]
     for c, ev in zip(caches, ev_fill):
         D.deltakv_compress(lay, k_d, v_d, wdk_d, wdv_d, c, ws_c, stage_events=ev)
@@ -501,7 +502,7 @@ def decode_workload(cfg, args, np, torch, K, D, hip, extras: bool):
         hip.sync(s_h)
         c_stage.append([hip.elapsed_ms(ev_c[2 * j], ev_c[2 * j + 1]) for j in range(4)])
         d_stage.extend([[hip.elapsed_ms(e[2 * j], e[2 * j + 1]) for j in range(3)] for e in ev_d])
-    c_stage = np.mean(np.array(fill_stage + c_stage), axis=0)
+    c_stage = np.median(np.array(fill_stage + c_stage), axis=0)
     d_stage = np.array(d_stage)
 
     if extras:
@@ -515,6 +516,7 @@ def decode_workload(cfg, args, np, torch, K, D, hip, extras: bool):
         ws_cp = D.workspace(D.dkv_compress_workspace_bytes(lay_p))
         for c in caches_p:
             D.deltakv_compress(lay_p, k_d, v_d, wdk_d, wdv_d, c, ws_cp)
+        torch.cuda.synchronize()   # the selective steps below run on another stream
         ev_s = [hip.events(6) for _ in range(SEL_STEPS)]
         s_stage = []
         for rep in range(2):

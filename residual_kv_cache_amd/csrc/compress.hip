@@ -1279,21 +1279,14 @@ __global__ __launch_bounds__(256) void k_group_scan(CompressArgs a, Shape sh, in
   a.gtot[(size_t)head * sh.R + r] = run;
 }
 
-// Bitonic compare-exchange from one element's side: it keeps the smaller
-// key when it is the lower index of the pair in an ascending run (or the
-// upper index in a descending one), else the larger.
-__device__ __forceinline__ uint32_t bitonic_keep(uint32_t x, uint32_t y, int i, int l, int kk) {
-  const bool keep_min = (i < l) == ((i & kk) == 0);
-  return keep_min ? min(x, y) : max(x, y);
-}
-
 // grid (pieces, B*H), block kGroupThreads, dynamic LDS R * 4 bytes (the first
 // grouped row of each ordinal).  Every global load is unconditional (clamped
 // indices, masked afterwards) and issued in batches, so the kernel waits on
 // few memory round trips.
 template <typename IdxT>
 __global__ __launch_bounds__(kGroupThreads) void k_group_place(CompressArgs a, Shape sh) {
-  __shared__ uint32_t key[kGroupPiece];   // (V ordinal << 12) | row in piece
+  __shared__ uint32_t keys[2][kGroupPiece];   // (V ordinal << 12) | row in piece, two buffers
+  __shared__ int wcnt[kGroupThreads / 64][256];
   __shared__ int wsum[kGroupThreads / 64];
   extern __shared__ int off[];
   static_assert(kGroupPiece == 4 * kGroupThreads && kGroupPiece <= 4096, "4 keys a thread; 12-bit row field");
@@ -1343,43 +1336,76 @@ __global__ __launch_bounds__(kGroupThreads) void k_group_place(CompressArgs a, S
     off[r] = run;
     run += v;
   }
-  // Bitonic sort, ascending: partners 1 and 2 apart are in the thread's own
-  // registers, 4 .. 128 apart in the same wave (shuffles), 256 and more
-  // apart in other waves (through LDS).  From 4 apart on, a thread's four
-  // keys share their role (bits j and kk of 4t + e do not depend on e).
-  for (int kk = 2; kk <= kGroupPiece; kk <<= 1) {
-    for (int j = kk >> 1; j > 0; j >>= 1) {
-      if (j >= 256) {
-        const bool keep_min = ((4 * tid) & j) == 0 ? ((4 * tid) & kk) == 0 : ((4 * tid) & kk) != 0;
-        __syncthreads();
+  // Stable LSD radix sort of the keys by ordinal, 8 bits a pass (two passes
+  // when R > 256).  Wave w takes keys 256w .. 256w + 255 in four rounds of
+  // 64, so equal ordinals keep their row order.  A key's rank among the
+  // round's keys of its digit comes from eight ballots (the lanes whose
+  // digit agrees bit by bit); the wave's running count per digit sits in
+  // LDS; one block-wide scan over (digit, wave), digit-major, gives each
+  // wave's first slot per digit.
+  constexpr int NW = kGroupThreads / 64;
+  static_assert(NW * 256 == 4 * kGroupThreads, "one scan entry per (digit, wave), four per thread");
+  const uint64_t lanes_below = (1ull << lane) - 1ull;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) key[4 * tid + e] = k[e];
-        __syncthreads();
+  for (int e = 0; e < 4; ++e) keys[0][4 * tid + e] = k[e];
+  const int passes = sh.R > 256 ? 2 : 1;
+  for (int pass = 0; pass < passes; ++pass) {
+    const uint32_t* src = keys[pass & 1];
+    uint32_t* dst = keys[(pass + 1) & 1];
+    const int shift = 12 + 8 * pass;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t y = key[(4 * tid + e) ^ j];
-          k[e] = keep_min ? min(k[e], y) : max(k[e], y);
-        }
-      } else if (j >= 4) {
-        const bool keep_min = ((4 * tid) & j) == 0 ? ((4 * tid) & kk) == 0 : ((4 * tid) & kk) != 0;
+    for (int e = 0; e < 4; ++e) (&wcnt[0][0])[4 * tid + e] = 0;
+    __syncthreads();
+    int dg[4], rk[4];
+    uint32_t kv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t y = (uint32_t)__shfl_xor((int)k[e], j >> 2, 64);
-          k[e] = keep_min ? min(k[e], y) : max(k[e], y);
-        }
-      } else {
-        uint32_t t[4];
+    for (int u = 0; u < 4; ++u) {
+      kv[u] = src[256 * w + 64 * u + lane];
+      const int d = (int)((kv[u] >> shift) & 255u);
+      uint64_t m = ~0ull;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) t[e] = bitonic_keep(k[e], k[e ^ j], 4 * tid + e, 4 * tid + (e ^ j), kk);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) k[e] = t[e];
+      for (int b = 0; b < 8; ++b) {
+        const uint64_t bal = __ballot((d >> b) & 1);
+        m &= ((d >> b) & 1) ? bal : ~bal;
       }
+      const int r = __popcll(m & lanes_below);
+      const int base = wcnt[w][d];
+      if (r == 0) wcnt[w][d] = base + __popcll(m);
+      dg[u] = d;
+      rk[u] = base + r;
     }
-  }
-  __syncthreads();
+    __syncthreads();
+    int c4[4], s4 = 0;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) key[4 * tid + e] = k[e];
-  __syncthreads();
+    for (int e = 0; e < 4; ++e) {
+      const int f = 4 * tid + e;
+      c4[e] = wcnt[f % NW][f / NW];
+      s4 += c4[e];
+    }
+    int xs = s4;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(xs, o, 64);
+      if (lane >= o) xs += y;
+    }
+    if (lane == 63) wsum[w] = xs;
+    __syncthreads();
+    int pre = xs - s4;
+    for (int i = 0; i < w; ++i) pre += wsum[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int f = 4 * tid + e;
+      wcnt[f % NW][f / NW] = pre;
+      pre += c4[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) dst[wcnt[w][dg[u]] + rk[u]] = kv[u];
+    __syncthreads();
+  }
+  const uint32_t* key = keys[passes & 1];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) k[e] = key[4 * tid + e];
   // Sorted entry i: its rank among the piece's rows of the same ordinal is
   // i minus the ordinal's first sorted entry (binary search).  The searches
   // run first, then every load, then the stores.
