@@ -19,8 +19,11 @@
 //             along the sequence; a 512-thread block (8 waves) owns one
 //             piece, each wave a contiguous run of 16-token tiles.  The
 //             head's S table sits in LDS, so a token's key reference costs
-//             one LDS read instead of a 256-byte row gather;
-//   combine   merges the splits of each query head and applies mu_V, W_up_V.
+//             one LDS read instead of a 256-byte row gather.  Each block
+//             applies W_up_V to its own value-code sums, so its record per
+//             query head is [max, sum, d output columns];
+//   combine   merges the splits of each query head and adds mu_V (one wave
+//             per 64 columns, no LDS, no barrier).
 //
 // Blocks of head bh run on XCD bh % 8 (workgroups are dispatched to the
 // eight XCDs round-robin), so the value reference rows a head gathers stay
@@ -727,6 +730,71 @@ __device__ __forceinline__ void run_tiles(const Args& p, const Shape& sh, const 
   }
 }
 
+// W_up_V row i = tid % d of head bh % H (the output column that thread tid
+// writes in store_partials), as 16-byte pieces; pieces past d_c repeat the
+// last one and are never used.
+__device__ __forceinline__ void load_wup_row(const DecodeArgs& a, const Shape& sh, int bh, int tid,
+                                             Frag (&wr)[kMaxDc / 8]) {
+  const int dc = sh.dc;
+  const uint16_t* row = (const uint16_t*)a.wuv + (size_t)(bh % sh.H) * a.w_hs + (size_t)(tid % kD) * dc;
+#pragma unroll
+  for (int j = 0; j < kMaxDc / 8; ++j) wr[j] = ldg<Frag>(row, (uint32_t)min(j * 8, dc - 8) * 2u);
+}
+
+// Partial record of each query head g of a split block: [max, sum, out[d]],
+// out = the block's value-reference sum plus W_up_V times its value-code
+// sums, both weighted against the block's maximum, so the combine only
+// merges splits.  red_acc [NW][4][d + 64] holds each wave's head-dim columns,
+// then its code columns and the weight-sum column (at d_c); threads
+// tid < G (d_c + 1) first sum the code columns over the waves into cs, then
+// thread (g, i) = (tid / d, tid % d) writes out[i] with its row wr of W_up_V
+// (load_wup_row).
+template <int NW>
+__device__ __forceinline__ void store_partials(const DecodeArgs& a, const Shape& sh, int bh, int sp, int tid,
+                                               const float (*red_m)[4], const float* red_acc, float* cs,
+                                               const Frag (&wr)[kMaxDc / 8]) {
+  const int G = a.G, dc = sh.dc;
+  if (tid < G * (dc + 1)) {
+    const int g = tid / (dc + 1), j = tid % (dc + 1);
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += red_acc[(w * 4 + g) * (kD + 64) + kD + j];
+    cs[g * (kMaxDc + 1) + j] = v;
+  }
+  __syncthreads();
+  if (tid < G * kD) {
+    const int g = tid / kD, i = tid % kD;
+    float r = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) r += red_acc[(w * 4 + g) * (kD + 64) + i];
+    const float* c = cs + g * (kMaxDc + 1);
+    float u = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxDc / 8; ++j) {
+      if (j * 8 < dc) {
+        const Frag w = wr[j];
+        u = fmaf(__uint_as_float(w.x << 16), c[8 * j + 0], u);
+        u = fmaf(__uint_as_float(w.x & 0xFFFF0000u), c[8 * j + 1], u);
+        u = fmaf(__uint_as_float(w.y << 16), c[8 * j + 2], u);
+        u = fmaf(__uint_as_float(w.y & 0xFFFF0000u), c[8 * j + 3], u);
+        u = fmaf(__uint_as_float(w.z << 16), c[8 * j + 4], u);
+        u = fmaf(__uint_as_float(w.z & 0xFFFF0000u), c[8 * j + 5], u);
+        u = fmaf(__uint_as_float(w.w << 16), c[8 * j + 6], u);
+        u = fmaf(__uint_as_float(w.w & 0xFFFF0000u), c[8 * j + 7], u);
+      }
+    }
+    float* part = a.part + (((size_t)bh * a.splits + sp) * G + g) * partial_rec(sh);
+    part[2 + i] = r + u;
+    if (i == 0) {
+      float mx = red_m[0][g];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) mx = fmaxf(mx, red_m[w][g]);
+      part[0] = mx;
+      part[1] = c[dc];
+    }
+  }
+}
+
 // Split boundaries (coded rows on 16-row boundaries).
 __device__ __forceinline__ int split_lo(int n, int sp, int splits, int align) {
   int64_t x = (int64_t)n * sp / splits;
@@ -740,6 +808,7 @@ template <int DCK, typename IdxT, bool SLDS, bool Q4, bool SEL, int KT = 1>
 __global__ __launch_bounds__(kThreads) void k_split_mfma(DecodeArgs a, Shape sh) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   __shared__ float red_m[kWaves][4];
+  __shared__ float csum[4 * (kMaxDc + 1)];
 
   const int BH = sh.B * sh.H;
   const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
@@ -856,6 +925,9 @@ __global__ __launch_bounds__(kThreads) void k_split_mfma(DecodeArgs a, Shape sh)
     run_tiles<false, DCK, IdxT, SLDS, Q4, false>(p, sh, lds, rt0, rt1, r0, r1, n16, q4, qh, ql, sel, ra, rb, st);
   }
 
+  Frag wr[kMaxDc / 8];
+  load_wup_row(a, sh, bh, tid, wr);
+
   // ---- merge the block's waves (fixed order) ----
   if (lane < 16 && (n16 & 3) == 0) red_m[wave][n16 >> 2] = st.m;
   __syncthreads();  // also: every wave is done with the S table
@@ -874,27 +946,7 @@ __global__ __launch_bounds__(kThreads) void k_split_mfma(DecodeArgs a, Shape sh)
   for (int i = 0; i < 4; ++i)
     if (n16 * 4 + i <= dc) mine_acc[kD + n16 * 4 + i] = st.accc[i] * wgt;
   __syncthreads();
-  // Partial record per query head: [max, sum, code acc[dc], reference acc[d]].
-  const int rec = partial_rec(sh);
-  float* part = a.part + ((size_t)bh * a.splits + sp) * G * rec;
-  for (int i = tid; i < G * rec; i += kThreads) {
-    const int g = i / rec, f = i % rec;
-    float v = 0.f;
-    if (f == 0) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) v = w == 0 ? red_m[0][g] : fmaxf(v, red_m[w][g]);
-    } else if (f == 1) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) v += red_acc[(w * 4 + g) * (kD + 64) + kD + dc];
-    } else if (f < 2 + dc) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) v += red_acc[(w * 4 + g) * (kD + 64) + kD + f - 2];
-    } else if (f < 2 + dc + kD) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) v += red_acc[(w * 4 + g) * (kD + 64) + f - 2 - dc];
-    }
-    part[i] = v;
-  }
+  store_partials<kWaves>(a, sh, bh, sp, tid, red_m, red_acc, csum, wr);
 }
 
 // ---------------------------------------------------------------------------
@@ -970,6 +1022,7 @@ __global__ __launch_bounds__(kThreads) void k_split_hist(DecodeArgs a, Shape sh)
   extern __shared__ __attribute__((aligned(16))) float lds[];
   __shared__ __attribute__((aligned(16))) float red_m[kWaves][4];
   __shared__ __attribute__((aligned(16))) float chunk_m[2][kWaves][4];   // by chunk parity
+  __shared__ float csum[4 * (kMaxDc + 1)];
 
   const int BH = sh.B * sh.H;
   const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
@@ -1287,6 +1340,9 @@ __global__ __launch_bounds__(kThreads) void k_split_hist(DecodeArgs a, Shape sh)
     }
   }
 
+  Frag wr[kMaxDc / 8];
+  load_wup_row(a, sh, bh, tid, wr);
+
   // ---- merge the block's waves: one maximum per query head, plain sums ----
   if (lane < 16 && (n16 & 3) == 0) red_m[wave][gl] = pick4(M, gl);
   __syncthreads();   // also: the S table is no longer read
@@ -1300,29 +1356,14 @@ __global__ __launch_bounds__(kThreads) void k_split_hist(DecodeArgs a, Shape sh)
   for (int i = 0; i < 4; ++i)
     if (n16 * 4 + i <= dc) mine_acc[kD + n16 * 4 + i] = accc[i];
   __syncthreads();
-  const int rec = partial_rec(sh);
-  float* part = a.part + ((size_t)bh * a.splits + sp) * G * rec;
-  for (int i = tid; i < G * rec; i += kThreads) {
-    const int g = i / rec, f = i % rec;
-    float v = 0.f;
-    if (f == 0) {
-      v = red_m[0][g];
-    } else if (f == 1) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) v += red_acc[(w * 4 + g) * (kD + 64) + kD + dc];
-    } else if (f < 2 + dc) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) v += red_acc[(w * 4 + g) * (kD + 64) + kD + f - 2];
-    } else if (f < 2 + dc + kD) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) v += red_acc[(w * 4 + g) * (kD + 64) + f - 2 - dc];
-    }
-    part[i] = v;
-  }
+  store_partials<kWaves>(a, sh, bh, sp, tid, red_m, red_acc, csum, wr);
 }
 
-// combine: merges the splits of one (b, query head) and applies mu_V and
-// W_up_V.  Block L (256 threads) runs on XCD L % 8, the XCD of its head's
+// combine of the general (VALU) split kernels, whose records hold
+// [max, sum, code acc[d_c], reference acc[d]]: merges the splits of one
+// (b, query head) and applies mu_V and W_up_V (the token-tile and histogram
+// splits apply W_up_V themselves; k_combine_out merges theirs).
+// Block L (256 threads) runs on XCD L % 8, the XCD of its head's
 // split blocks; thread t owns column t of the partial records (code columns,
 // then head-dim columns) and issues its loads of 32 splits at once, together
 // with the split maxima and sums, so the records arrive in few round trips.
@@ -1422,6 +1463,57 @@ __global__ __launch_bounds__(256) void k_combine(DecodeArgs a, Shape sh) {
     const uint32_t keep = 0u - (uint32_t)(red[0] > 0.f);
     a.out[((size_t)b * a.Hq + gq) * kD + i_out] = __uint_as_float(__float_as_uint(res) & keep);
   }
+}
+
+// combine of the token-tile and histogram splits, whose records hold
+// [max, sum, out[d]] (store_partials).  Block L is one wave on XCD L % 8, the
+// XCD of its head's split blocks, and owns 64 output columns of one
+// (b, query head).  Per batch of 32 splits, lane j loads the (max, sum) pair
+// of split j and every lane loads its column of each split at once; the
+// pairs reach every lane by readlane, so the merge needs no LDS and no
+// barrier.  Splits are merged in fixed order against a running maximum.
+__global__ __launch_bounds__(64) void k_combine_out(DecodeArgs a, Shape sh) {
+  const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
+  const int per = 2 * a.G;
+  const int bh = xcd + 8 * (kx / per), g = (kx % per) >> 1, half = kx & 1;
+  if (bh >= sh.B * sh.H) return;
+  const int b = bh / sh.H, h = bh % sh.H;
+  const int rec = partial_rec(sh), ns = a.splits;
+  const size_t pstride = (size_t)a.G * rec;
+  const float* part = a.part + (size_t)bh * ns * pstride + (size_t)g * rec;
+  const int lane = threadIdx.x, col = half * 64 + lane;
+  const float muv = bf2f(ldg<uint16_t>(a.mu, ((uint32_t)(bh * 2 + 1) * kD + (uint32_t)col) * 2u));
+  float M = -INFINITY, L = 0.f, acc = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += kCombineBatch) {
+    const f32x2 ml = *reinterpret_cast<const f32x2*>(part + (size_t)min(s0 + (lane & 31), ns - 1) * pstride);
+    float v[kCombineBatch];
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k) v[k] = part[(size_t)min(s0 + k, ns - 1) * pstride + 2 + col];
+    float mj[kCombineBatch];
+    float bm = M;
+#pragma unroll
+    for (int j = 0; j < kCombineBatch; ++j) {
+      const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml.x), j));
+      mj[j] = s0 + j < ns ? m : -INFINITY;
+      bm = fmaxf(bm, mj[j]);
+    }
+    // What is summed so far, to the new maximum (nothing when M = -inf;
+    // a factor of exactly 1 when the maximum stays).
+    const float r = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - bm);
+    acc *= r;
+    L *= r;
+    M = bm;
+#pragma unroll
+    for (int j = 0; j < kCombineBatch; ++j) {
+      const float w = mj[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mj[j] - M);
+      L = fmaf(w, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml.y), j)), L);
+      acc = fmaf(w, v[j], acc);
+    }
+  }
+  // L = 0 only when a selective decode attended no token: the output is 0.
+  const float res = muv + acc / L;
+  const uint32_t keep = 0u - (uint32_t)(L > 0.f);
+  a.out[((size_t)b * a.Hq + h * a.G + g) * kD + col] = __uint_as_float(__float_as_uint(res) & keep);
 }
 
 size_t split_lds_bytes(const Shape& sh, bool slds) {
@@ -1532,7 +1624,7 @@ hipError_t launch_decode_fused(const Shape& sh, const DecodeArgs& a, hipStream_t
   else
     e = i16 ? launch_split_s<2, uint16_t>(sh, a, st, grid) : launch_split_s<2, uint32_t>(sh, a, st, grid);
   if (e != hipSuccess) return e;
-  return launch(k_combine, dim3(BH8 * a.G), 256, st, ev_start(a.events, 2), ev_stop(a.events, 2), a, sh);
+  return launch(k_combine_out, dim3(BH8 * a.G * 2), 64, st, ev_start(a.events, 2), ev_stop(a.events, 2), a, sh);
 }
 
 hipError_t launch_decode_sel_fused(const Shape& sh, const DecodeArgs& a, hipStream_t st) {
@@ -1543,7 +1635,7 @@ hipError_t launch_decode_sel_fused(const Shape& sh, const DecodeArgs& a, hipStre
   e = sh.idx_bytes == 2 ? launch_split_s<1, uint16_t, true>(sh, a, st, grid)
                         : launch_split_s<1, uint32_t, true>(sh, a, st, grid);
   if (e != hipSuccess) return e;
-  return launch(k_combine, dim3(BH8 * a.G), 256, st, ev_start(a.events, 2), ev_stop(a.events, 2), a, sh);
+  return launch(k_combine_out, dim3(BH8 * a.G * 2), 64, st, ev_start(a.events, 2), ev_stop(a.events, 2), a, sh);
 }
 
 }  // namespace dkv
