@@ -183,17 +183,17 @@ def effective_decode_bytes(cfg, code_bits: int = 0, top_k: int = 1) -> int:
 def split_kernel_bytes_per_head(cfg, splits: int) -> int:
     """Algorithmic bytes of the split kernel per (sequence, KV head): K and V
     codes and ordinals, V references, the reference-score table (4 floats
-    per reference) and projected queries it reads, each once, and the split
-    partials it writes."""
+    per reference), the projected queries and W_up_V it reads, each once,
+    and the split records it writes (max, sum and d output columns per
+    query head)."""
     e = 2 if cfg.dtype == "bf16" else 4
     R = -(-cfg.seq_len // cfg.stride)
     N = cfg.seq_len - R
     ib = 2 if R <= 65536 else 4
     G = cfg.group
-    rec = (2 + cfg.code_dim + cfg.head_dim + 3) // 4 * 4
     gs = (G + 3) // 4 * 4
     return (2 * N * (cfg.code_dim * e + ib) + R * cfg.head_dim * e + R * gs * 4 + G * cfg.code_dim * 4
-            + splits * G * rec * 4)
+            + cfg.head_dim * cfg.code_dim * e + splits * G * (2 + cfg.head_dim) * 4)
 
 
 def search_flops_per_stream(cfg) -> int:
