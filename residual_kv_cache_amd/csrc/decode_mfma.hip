@@ -95,6 +95,28 @@ __device__ __forceinline__ float pick4(float v0, float v1, float v2, float v3, i
 }
 __device__ __forceinline__ float pick4(const float (&v)[4], int i) { return pick4(v[0], v[1], v[2], v[3], i); }
 
+// DPP move of a float with control C (every lane has a valid source).
+template <int C>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), C, 0xF, 0xF, true));
+}
+
+// Sum over the wave, the same value in every lane: quads (quad_perm 1,0,3,2
+// and 2,3,0,1), eights (row_half_mirror) and rows of 16 (row_mirror) by DPP,
+// each step adding two equal partial sums in either order, then the four
+// row sums by readlane, added in a fixed order.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dppf<0xB1>(v);
+  v += dppf<0x4E>(v);
+  v += dppf<0x141>(v);
+  v += dppf<0x140>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 // Global-memory load at a byte offset (the address space is explicit so that
 // selected base pointers still compile to global, not flat, loads).
 template <typename T>
@@ -114,7 +136,7 @@ __device__ const uint16_t kOnePair[8] __attribute__((aligned(16))) = {0x3F80u, 0
 // S[r][0..3]); wave 0 also computes q' outputs
 // 4 (chunk + chunks m), m = 0, 1, ...: four consecutive code columns of one
 // query head, lane l taking rows l and l + 64 of W_up (8 contiguous bytes
-// each), summed over the wave by a fixed butterfly.  The first group's
+// each), summed over the wave by wave_sum.  The first group's
 // loads go out with the S loads, so a block takes one round trip.
 // ---------------------------------------------------------------------------
 
@@ -156,9 +178,7 @@ __global__ __launch_bounds__(256) void k_refscore_mfma(DecodeArgs a, Shape sh, i
       v[3] = fmaf(qf, __uint_as_float(w[hh].y & 0xFFFF0000u), v[3]);
     }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] += __shfl_xor(v[e], o, 64);
+    for (int e = 0; e < 4; ++e) v[e] = wave_sum(v[e]);
     if (lane < 4 && o0 < no) {
       const int g = o0 / dc, j = o0 % dc + lane;
       a.qp[((size_t)bh * G + g) * dc + j] = pick4(v, lane) * cs;
@@ -255,7 +275,7 @@ struct Tile {
   Frag cv;         // d_c <= 32: the tile's value codes, one 16-byte load per lane
   uint32_t ckq;    // 4-bit codes: the key code nibbles of token n16 (columns 8 q4 ..)
   uint32_t cvq;    // 4-bit codes: the value code nibbles the lane would load as cv
-  uint32_t scl;    // 4-bit codes: bits of the key scale of token n16
+  uint32_t scl;    // 4-bit codes: bits of the key scale of token 4 q4 + n16 % 4 (token lists: n16)
   uint32_t sclv;   // 4-bit codes: bits of the value scale of the token of cvq
   int cnt;
   // k references per token (KT > 1): value ordinals 1 .. KT - 1 of the lane's
@@ -467,7 +487,9 @@ __device__ __forceinline__ void load_data(const Args& p, const Shape& sh, const 
     const uint32_t ua = ti.base + min(n16, cnt - 1);
     const int c = q4 * 8;
     td.ckq = ldg<uint32_t>(p.qK, ua * (uint32_t)(dc / 2) + (uint32_t)(c < dc ? c : 0) / 2u);
-    td.scl = ldg<uint16_t>(p.sclK, ua * 2u);
+    // Key scale of token 4 q4 + n16 % 4: compute_tile hands lane i's to the
+    // whole row by a DPP row broadcast.
+    td.scl = ldg<uint16_t>(p.sclK, (ti.base + (uint32_t)min(q4 * 4 + (n16 & 3), cnt - 1)) * 2u);
     const int g2 = n16 >> 3, cc = n16 & 7;
     const int col = 4 * (cc & ~1);
     const uint32_t u = ti.base + min(q4 * 4 + 2 * g2 + (cc & 1), cnt - 1);
@@ -583,8 +605,16 @@ __device__ __forceinline__ void compute_tile(const Tile& td, const Frag* qh, con
     f32x4 c = {0.f, 0.f, 0.f, 0.f};
     c = mfma16(ck, qh[0], c);
     c = mfma16(ck, ql[0], c);
+    if constexpr (SEL) {
+      // Token lists: the lane's scale is its key-code token's (n16).
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] += bf2f((uint16_t)__shfl((int)td.scl, 4 * q4 + i, 64)) * c[i];
+      for (int i = 0; i < 4; ++i) s[i] += bf2f((uint16_t)__shfl((int)td.scl, 4 * q4 + i, 64)) * c[i];
+    } else {
+      s[0] += bf2f((uint16_t)row_bcast<0>((int)td.scl)) * c[0];
+      s[1] += bf2f((uint16_t)row_bcast<1>((int)td.scl)) * c[1];
+      s[2] += bf2f((uint16_t)row_bcast<2>((int)td.scl)) * c[2];
+      s[3] += bf2f((uint16_t)row_bcast<3>((int)td.scl)) * c[3];
+    }
   } else if (CODED) {
     f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
