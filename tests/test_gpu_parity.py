@@ -88,8 +88,12 @@ def test_end_to_end_matches_oracle(name, small_runs):
     assert err <= GH.OUT_TOL[cfg.dtype]
 
 
-@pytest.mark.parametrize("splits", [1, 2, 3, 17, 64, 1024])
+@pytest.mark.parametrize("splits", [1, 2, 3, 17, 40, 64, 100, 256, 1024])
 def test_split_count_invariance(splits, small_runs):
+    """The same decode at several split counts: one split (the histogram
+    form), partial batches of 32 records in the merge (17, 40, 100), several
+    batches (64 to 256, the MFMA path's maximum) and the general kernels
+    (1024)."""
     inp, lay, cache, gc = _run("bf16_ragged", small_runs)
     q = inp.q(3)
     base = GH.gpu_decode(lay, cache, q.raw, inp, n_splits=1)
