@@ -261,7 +261,7 @@ __global__ __launch_bounds__(256) void k_split_valu(DecodeArgs a, Shape sh) {
       }
 #pragma unroll
       for (int g = 0; g < GP; ++g) {
-        if (g >= G) break;
+        if (g >= G) continue;   // continue, not break: a loop with a break is not unrolled
         const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p[g]), k));
 #pragma unroll
         for (int e = 0; e < RPL; ++e) accr[g][e] = fmaf(w, xr[e], accr[g][e]);
@@ -545,7 +545,7 @@ __global__ __launch_bounds__(256) void k_split_sel(DecodeArgs a, Shape sh) {
         const float v1 = ck && lane + 64 < dc ? c1[i] : 0.f;
 #pragma unroll
         for (int g = 0; g < GP; ++g) {
-          if (g >= G) break;
+          if (g >= G) continue;
           const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p[g]), k));
 #pragma unroll
           for (int e = 0; e < RPL; ++e) accr[g][e] = fmaf(w, xr[i][e], accr[g][e]);

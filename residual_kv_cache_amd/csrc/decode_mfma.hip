@@ -475,7 +475,7 @@ __device__ __forceinline__ void load_data(const Args& p, const Shape& sh, const 
     const bool kb = ti.rb >= 0;
     td.ck[0] = ldg<Frag>(kb ? (const void*)p.codesK : (const void*)kZeroCodes,
                          kb ? ((uint32_t)ti.rb * dc + (c < dc ? c : 0)) * 2u : 0u);
-    const int g2 = n16 >> 3, cc = n16 & 7;
+    const int cc = n16 & 7;
     const int col = 4 * (cc & ~1);
     const bool in_code = col < dc, vb = ti.rc >= 0;
     const void* vbase = in_code ? (vb ? (const void*)p.codesV : (const void*)kZeroCodes) : (const void*)kOnePair;
