@@ -117,6 +117,19 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
+// Maximum over the wave, the same value in every lane (as wave_sum).
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dppf<0xB1>(v));
+  v = fmaxf(v, dppf<0x4E>(v));
+  v = fmaxf(v, dppf<0x141>(v));
+  v = fmaxf(v, dppf<0x140>(v));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 // Global-memory load at a byte offset (the address space is explicit so that
 // selected base pointers still compile to global, not flat, loads).
 template <typename T>
@@ -1499,9 +1512,11 @@ __global__ __launch_bounds__(256) void k_combine(DecodeArgs a, Shape sh) {
 // [max, sum, out[d]] (store_partials).  Block L is one wave on XCD L % 8, the
 // XCD of its head's split blocks, and owns 64 output columns of one
 // (b, query head).  Per batch of 32 splits, lane j loads the (max, sum) pair
-// of split j and every lane loads its column of each split at once; the
-// pairs reach every lane by readlane, so the merge needs no LDS and no
-// barrier.  Splits are merged in fixed order against a running maximum.
+// of split j and every lane loads its column of each split at once; lane j
+// forms split j's weight against the running maximum (wave reductions give
+// the maximum and the weighted sum), and the weights reach every lane by
+// readlane, so the merge needs no LDS and no barrier.  Columns add the
+// splits in fixed order.
 __global__ __launch_bounds__(64) void k_combine_out(DecodeArgs a, Shape sh) {
   const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
   const int per = 2 * a.G;
@@ -1519,26 +1534,20 @@ __global__ __launch_bounds__(64) void k_combine_out(DecodeArgs a, Shape sh) {
     float v[kCombineBatch];
 #pragma unroll
     for (int k = 0; k < kCombineBatch; ++k) v[k] = part[(size_t)min(s0 + k, ns - 1) * pstride + 2 + col];
-    float mj[kCombineBatch];
-    float bm = M;
-#pragma unroll
-    for (int j = 0; j < kCombineBatch; ++j) {
-      const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml.x), j));
-      mj[j] = s0 + j < ns ? m : -INFINITY;
-      bm = fmaxf(bm, mj[j]);
-    }
+    // Lane j < 32: split s0 + j (lanes past the batch or the split count
+    // hold no split).
+    const float mj = lane < kCombineBatch && s0 + lane < ns ? ml.x : -INFINITY;
+    const float bm = fmaxf(M, wave_max(mj));
     // What is summed so far, to the new maximum (nothing when M = -inf;
     // a factor of exactly 1 when the maximum stays).
     const float r = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - bm);
-    acc *= r;
-    L *= r;
     M = bm;
+    const float w = mj == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mj - M);
+    L = fmaf(L, r, wave_sum(w * ml.y));
+    acc *= r;
 #pragma unroll
-    for (int j = 0; j < kCombineBatch; ++j) {
-      const float w = mj[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mj[j] - M);
-      L = fmaf(w, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml.y), j)), L);
-      acc = fmaf(w, v[j], acc);
-    }
+    for (int j = 0; j < kCombineBatch; ++j)
+      acc = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j)), v[j], acc);
   }
   // L = 0 only when a selective decode attended no token: the output is 0.
   const float res = muv + acc / L;
