@@ -81,6 +81,7 @@ SPLIT_SOURCES = ["residual_kv_cache_amd/csrc/decode_mfma.hip", "residual_kv_cach
                  "residual_kv_cache_amd/csrc/dkv_internal.h"]
 TRAFFIC_FILE = "profiles/decode_split_llama8b_32k_traffic.txt"
 CALIB_BYTES = 256 << 20
+STAGE_COMPRESSES = 16   # eager compresses whose stage times give the compress stages' medians
 
 
 def sources_sha256(paths) -> str:
@@ -382,14 +383,9 @@ def decode_workload(cfg, args, np, torch, K, D, hip, extras: bool):
     outs = torch.empty((nsteps, cfg.batch, cfg.n_q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
 
     # Eager pass: fill every replica and keep reference outputs for steps 0 and 255.
-    # Stage events time each fill's kernels; with the timed runs below they
-    # give each compress stage's median over every eager compress (a search
-    # varies by a few percent from launch to launch with the clocks).
-    ev_fill = [hip.events(8) for _ in caches]
-    for c, ev in zip(caches, ev_fill):
-        D.deltakv_compress(lay, k_d, v_d, wdk_d, wdv_d, c, ws_c, stage_events=ev)
+    for c in caches:
+        D.deltakv_compress(lay, k_d, v_d, wdk_d, wdv_d, c, ws_c)
     torch.cuda.synchronize()
-    fill_stage = [[hip.elapsed_ms(ev[2 * j], ev[2 * j + 1]) for j in range(4)] for ev in ev_fill]
     if args.profile:
         src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -490,19 +486,24 @@ def decode_workload(cfg, args, np, torch, K, D, hip, extras: bool):
     decode_window_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
 
     # Per-kernel device times: the same work launched eagerly with the
-    # library's stage events (stamped at kernel start and end).
-    ev_c = hip.events(8)
+    # library's stage events (stamped at kernel start and end), right after
+    # the timed replays, so at the clocks they ran at.  Compress stages: the
+    # median of STAGE_COMPRESSES compresses (a search varies by a few
+    # percent from launch to launch with the clocks).
+    ev_c = [hip.events(8) for _ in range(STAGE_COMPRESSES)]
     ev_d = [hip.events(6) for _ in range(nsteps)]
     c_stage, d_stage = [], []
+    for ev in ev_c:
+        D.deltakv_compress(lay, k_d, v_d, wdk_d, wdv_d, caches[0], ws_c, stream=s_h, stage_events=ev)
+    hip.sync(s_h)
+    c_stage = [[hip.elapsed_ms(ev[2 * j], ev[2 * j + 1]) for j in range(4)] for ev in ev_c]
     for rep in range(2):
-        D.deltakv_compress(lay, k_d, v_d, wdk_d, wdv_d, caches[0], ws_c, stream=s_h, stage_events=ev_c)
         for i in range(nsteps):
             D.deltakv_decode_attn(lay, caches[i % nrep], q_d[i], wuk_d, wuv_d, outs[i], ws_d, n_splits=splits,
                                   stream=s_h, stage_events=ev_d[i])
         hip.sync(s_h)
-        c_stage.append([hip.elapsed_ms(ev_c[2 * j], ev_c[2 * j + 1]) for j in range(4)])
         d_stage.extend([[hip.elapsed_ms(e[2 * j], e[2 * j + 1]) for j in range(3)] for e in ev_d])
-    c_stage = np.median(np.array(fill_stage + c_stage), axis=0)
+    c_stage = np.median(np.array(c_stage), axis=0)
     d_stage = np.array(d_stage)
 
     if extras:
